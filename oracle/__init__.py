@@ -1,0 +1,118 @@
+"""ctypes wrapper around the plain-C CPU oracle (bitnet_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+bench's CPU-baseline leg.  The GPU library never imports, links or calls it.
+All arrays are numpy arrays on the host.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "bitnet_oracle.c")
+_LIB = os.path.join(_HERE, "libbitnet_oracle.so")
+
+def build_cmd(out: str) -> list[str]:
+    return ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+            "-ffp-contract=off", "-fno-fast-math", _SRC, "-o", out, "-lm"]
+
+
+def build() -> str:
+    """Compile the oracle (always; cheap)."""
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(build_cmd(tmp))
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        L.oracle_weight_scale.argtypes = [P, I64, I64, P]
+        L.oracle_weight_scale.restype = ctypes.c_float
+        L.oracle_pack.argtypes = [P, I64, I64, ctypes.c_float, ctypes.c_float, P]
+        L.oracle_unpack.argtypes = [P, I64, I64, P]
+        L.oracle_quant_act.argtypes = [P, I64, I64, P, P]
+        L.oracle_linear.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, P, P]
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        L.oracle_get_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().oracle_get_threads())
+
+
+def weight_scale(w: np.ndarray) -> tuple[np.float32, np.ndarray]:
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    rows = np.empty(N, dtype=np.float64)
+    s = lib().oracle_weight_scale(_p(w), N, K, _p(rows))
+    return np.float32(s), rows
+
+
+def pack(w: np.ndarray, eps: float = 1e-5) -> tuple[np.ndarray, np.float32]:
+    """-> (packed uint8 [N][K/4], s_w)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    assert K % 4 == 0
+    s_w, _ = weight_scale(w)
+    out = np.empty((N, K // 4), dtype=np.uint8)
+    lib().oracle_pack(_p(w), N, K, ctypes.c_float(eps), ctypes.c_float(s_w), _p(out))
+    return out, s_w
+
+
+def unpack(packed: np.ndarray, K: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    N = packed.shape[0]
+    t = np.empty((N, K), dtype=np.int8)
+    lib().oracle_unpack(_p(packed), N, K, _p(t))
+    return t
+
+
+def quant_act(x_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """x_bits: uint16 [M][K] bf16 bit patterns -> (q int8 [M][K], s_x fp32 [M])."""
+    x_bits = np.ascontiguousarray(x_bits).view(np.uint16)
+    M, K = x_bits.shape
+    q = np.empty((M, K), dtype=np.int8)
+    s = np.empty(M, dtype=np.float32)
+    lib().oracle_quant_act(_p(x_bits), M, K, _p(q), _p(s))
+    return q, s
+
+
+def linear(q: np.ndarray, s_x: np.ndarray, packed: np.ndarray, s_w, K: int | None = None):
+    """-> (acc int32 [M][N], y fp32 [M][N])."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s_x = np.ascontiguousarray(s_x, dtype=np.float32)
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    M, Kq = q.shape
+    K = Kq if K is None else K
+    N = packed.shape[0]
+    assert packed.shape[1] * 4 == K and s_x.shape == (M,)
+    acc = np.empty((M, N), dtype=np.int32)
+    y = np.empty((M, N), dtype=np.float32)
+    lib().oracle_linear(_p(q), _p(s_x), _p(packed), ctypes.c_float(float(s_w)),
+                        M, N, K, _p(acc), _p(y))
+    return acc, y

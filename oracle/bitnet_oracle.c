@@ -1,0 +1,180 @@
+/*
+ * CPU oracle for the BitNet b1.58 BitLinear forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file: it is used by the tests, by the smoke check and by the
+ * bench's CPU-baseline leg, and by nothing else.  It shares no code, header,
+ * table or constant with the GPU library.
+ *
+ * It is written to be read against the pages, not to be fast: every function
+ * is the plain definition, step by step, with no blocking, fusion or
+ * reordering beyond what the definition states.  The only concession to speed
+ * is an OpenMP "parallel for" over independent output rows, which changes no
+ * arithmetic.
+ *
+ * Sources (page titles as printed on the pages):
+ *  [P1] "BitNet 深度拆解：当大模型被压到 1.58 bit……" (chenxutan.com),
+ *       sec. 2.2 (absmean / absmax quantization), sec. 2.3 (rescale with the
+ *       two scale factors), sec. 3.1 (BitLinear.forward), sec. 3.3 (INT2
+ *       packing, 4 weights per byte, code = w + 1, LSB first).
+ *  [P5] "1-bit推理框架bitnet.cpp实测……" (0539edu.com), sec. 2.1
+ *       (RoundClip(w / scale, -1, 1), scale = mean|w|).
+ *
+ * Readings where the pages are ambiguous (each is argued in the design notes):
+ *  - weight scale s_w = mean|W| over the whole tensor ([P5] 2.1); the mean is
+ *    formed in float64, row sums first (each row summed k = 0..K-1 in order),
+ *    then the row sums added n = 0..N-1 in order, then one rounding to fp32;
+ *  - ternary code: t = clamp(rint(w / (s_w + eps)), -1, 1) with s_w + eps and
+ *    the quotient each one IEEE binary32 operation (the pages' tensors are
+ *    fp32); rint is round-half-to-even, the rounding of torch.round in [P1];
+ *  - activation code: q = clamp(RNE(127 * x / max|x_row|), -127, 127) where the
+ *    quotient is the exact real number (computed in float64, which is exact
+ *    for bf16 inputs, see the tests); an all-zero row gives q = 0, s_x = 0;
+ *  - output y = acc * (s_x / 127) * s_w, the real number rounded once to fp32
+ *    (formed in float64); the /127 undoes the *127 of the activation code;
+ *  - a 2-bit field holding 3 (never written by the packer) decodes to +2.
+ *
+ * Parity pins for every function live in tests/test_oracle_pins.py.
+ * Build: gcc -O2 -std=c11 -fPIC -shared -fopenmp -ffp-contract=off.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* --- threads ------------------------------------------------------------ */
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int oracle_get_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* --- weights: absmean scale ([P1] 2.2 absmean_quantize, [P5] 2.1) -------- */
+
+/* rowsum[n] = sum_k |W[n][k]| in float64, k ascending; returns s_w = fp32 of
+ * (sum_n rowsum[n]) / (N*K), n ascending. */
+float oracle_weight_scale(const float *w, int64_t N, int64_t K, double *rowsum) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        double r = 0.0;
+        for (int64_t k = 0; k < K; ++k) r += fabs((double)w[n * K + k]);
+        rowsum[n] = r;
+    }
+    double total = 0.0;
+    for (int64_t n = 0; n < N; ++n) total += rowsum[n];
+    if (N * K == 0) return 0.0f;
+    return (float)(total / (double)(N * K));
+}
+
+/* --- weights: ternary code and 2-bit packing ([P1] 3.3 pack_ternary) ---- */
+
+/* t = clamp(rint(w / d), -1, 1) with d = fl32(s_w + eps). */
+static int ternary_of(float w, float d) {
+    float v = w / d;                 /* one binary32 division */
+    float r = rintf(v);              /* half to even */
+    if (r > 1.0f) r = 1.0f;
+    if (r < -1.0f) r = -1.0f;
+    return (int)r;
+}
+
+/* packed[n][j] holds weights (n, 4j .. 4j+3); weight 4j+i sits in bits
+ * 2i..2i+1 as code t + 1.  K must be a multiple of 4 (no padding). */
+void oracle_pack(const float *w, int64_t N, int64_t K, float eps,
+                 float s_w, uint8_t *packed) {
+    float d = s_w + eps;             /* one binary32 addition */
+    int64_t KB = K / 4;
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < KB; ++j) {
+            unsigned byte = 0;
+            for (int i = 0; i < 4; ++i) {
+                int t = ternary_of(w[n * K + 4 * j + i], d);
+                unsigned code = (unsigned)(t + 1);
+                byte |= code << (2 * i);
+            }
+            packed[n * KB + j] = (uint8_t)byte;
+        }
+    }
+}
+
+/* Decode one weight from the packed layout (code - 1; code 3 -> +2). */
+static int weight_at(const uint8_t *packed, int64_t KB, int64_t n, int64_t k) {
+    unsigned byte = packed[n * KB + k / 4];
+    unsigned code = (byte >> (2 * (k % 4))) & 3u;
+    return (int)code - 1;
+}
+
+void oracle_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *t) {
+    int64_t KB = K / 4;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            t[n * K + k] = (int8_t)weight_at(packed, KB, n, k);
+}
+
+/* --- activations: absmax int8 ([P1] 2.2 absmax_quantize) ---------------- */
+
+static float bf16_to_float(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+void oracle_quant_act(const uint16_t *x, int64_t M, int64_t K,
+                      int8_t *q, float *s_x) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *row = x + m * K;
+        float s = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(bf16_to_float(row[k]));
+            if (a > s) s = a;
+        }
+        s_x[m] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            if (s == 0.0f) { q[m * K + k] = 0; continue; }
+            double v = (127.0 * (double)bf16_to_float(row[k])) / (double)s;
+            double r = rint(v);      /* half to even */
+            if (r > 127.0) r = 127.0;
+            if (r < -127.0) r = -127.0;
+            q[m * K + k] = (int8_t)r;
+        }
+    }
+}
+
+/* --- contraction and rescale ([P1] 2.3, 3.1 BitLinear.forward) ---------- */
+
+/* acc[m][n] = sum_k q[m][k] * t[n][k]  (exact integer sum)
+ * y[m][n]   = fp32( acc * s_x[m] * s_w / 127 )   formed in float64.
+ * acc may be NULL. */
+void oracle_linear(const int8_t *q, const float *s_x, const uint8_t *packed,
+                   float s_w, int64_t M, int64_t N, int64_t K,
+                   int32_t *acc, float *y) {
+    int64_t KB = K / 4;
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            int64_t a = 0;
+            for (int64_t k = 0; k < K; ++k)
+                a += (int64_t)q[m * K + k] * (int64_t)weight_at(packed, KB, n, k);
+            if (acc) acc[m * N + n] = (int32_t)a;
+            double v = (double)a * (double)s_x[m];
+            v = v * (double)s_w;
+            v = v / 127.0;
+            y[m * N + n] = (float)v;
+        }
+    }
+}

@@ -1,0 +1,360 @@
+"""Pins for the CPU oracle: checks against values and facts that do not come
+from the oracle itself (hand-worked examples, exact rational arithmetic, brute
+force, closed forms, library routines and invariants).
+
+Definitions pinned (pages: "BitNet 深度拆解……" on chenxutan.com, sec. 2.2
+absmean/absmax quantization, sec. 2.3 rescale, sec. 3.1 BitLinear.forward,
+sec. 3.3 INT2 packing; "1-bit推理框架bitnet.cpp实测……" on 0539edu.com,
+sec. 2.1 RoundClip).
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- helpers
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Exact conversion for values already representable in bf16."""
+    a = np.asarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "value not exactly representable in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def round_fraction_to_f32(fr: Fraction) -> float:
+    """Correct round-to-nearest-even of an exact rational to binary32 (normal range)."""
+    if fr == 0:
+        return 0.0
+    sign = -1.0 if fr < 0 else 1.0
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length() - 23
+    while a / Fraction(2) ** e >= 2 ** 24:
+        e += 1
+    while a / Fraction(2) ** e < 2 ** 23:
+        e -= 1
+    m = a / Fraction(2) ** e
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * math.ldexp(float(fl), e)
+
+
+def rne_int(num: np.ndarray, den: np.ndarray) -> np.ndarray:
+    """Round-half-even of num/den for int64 arrays (den > 0), exact."""
+    fl = np.floor_divide(num, den)
+    rem = num - fl * den
+    twice = 2 * rem
+    up = (twice > den) | ((twice == den) & (fl % 2 != 0))
+    return fl + up.astype(np.int64)
+
+
+def decode_unpackbits(packed: np.ndarray, K: int) -> np.ndarray:
+    """Independent decoder of the byte layout: numpy little-endian bit order,
+    bit pairs (2i, 2i+1) -> code, weight = code - 1."""
+    bits = np.unpackbits(packed.reshape(-1, 1), axis=1, bitorder="little")  # [B][8]
+    codes = bits[:, 0::2].astype(np.int16) + 2 * bits[:, 1::2].astype(np.int16)  # [B][4]
+    return (codes.reshape(packed.shape[0], K) - 1).astype(np.int8)
+
+
+def parse_cases(name: str):
+    out = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            out.append([p.strip() for p in line.split("|")])
+    return out
+
+
+# ----------------------------------------------------------------- generator
+
+def test_splitmix64_published_first_output():
+    # SplitMix64 seeded with 0: first output 0xE220A8397B1DCDAF (Vigna's
+    # reference splitmix64.c), second 0x6E789E6AA1B965F4.
+    assert synth.splitmix64_py(0, 2) == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4]
+
+
+def test_generator_torch_matches_python():
+    key = synth.stream_key(7, 3)
+    ref = synth.splitmix64_py(key, 1000)
+    got = synth.raw64(key, 0, 1000).tolist()
+    assert [g & ((1 << 64) - 1) for g in got] == ref
+
+
+def test_generator_normal_moments():
+    z = synth.normal(synth.stream_key(1), 1 << 20)
+    assert abs(z.mean().item()) < 5e-3
+    assert abs(z.std().item() - 1.0) < 5e-3
+
+
+# ----------------------------------------------------------------- pack
+
+@pytest.mark.parametrize("case", parse_cases("pack_cases.txt"))
+def test_pack_golden(case):
+    eps = float(case[0])
+    w = np.array([float(v) for v in case[1].split()], dtype=np.float32)[None, :]
+    expect = np.array([int(b, 16) for b in case[2].split()], dtype=np.uint8)
+    packed, s_w = oracle.pack(w, eps)
+    assert packed[0].tolist() == expect.tolist()
+    assert s_w == np.float32(float(case[3]))
+
+
+def test_pack_layout_against_unpackbits():
+    key = synth.stream_key(11)
+    w = synth.density_weights(key, 37, 128, 0.6).numpy()
+    t_expect = np.rint(w / 0.02).astype(np.int8)
+    packed, _ = oracle.pack(w, 1e-5)
+    assert np.array_equal(decode_unpackbits(packed, 128), t_expect)
+    assert np.array_equal(oracle.unpack(packed, 128), t_expect)
+
+
+def test_pack_all_zero_tensor():
+    packed, s_w = oracle.pack(np.zeros((5, 64), np.float32), 1e-5)
+    assert s_w == 0.0 and np.all(packed == 0x55)
+
+
+def test_pack_sign_symmetry():
+    w = synth.latent_weights(synth.stream_key(3), 64, 256, 0.02).numpy()
+    p1, s1 = oracle.pack(w)
+    p2, s2 = oracle.pack(-w)
+    assert s1 == s2
+    t1 = decode_unpackbits(p1, 256)
+    t2 = decode_unpackbits(p2, 256)
+    assert np.array_equal(t1, -t2)
+
+
+def test_weight_scale_equals_exact_mean():
+    # s_w must be the correctly rounded binary32 value of the exact mean of |W|.
+    for seed in range(3):
+        w = synth.latent_weights(synth.stream_key(4, seed), 48, 320, 0.02).numpy()
+        s_w, rows = oracle.weight_scale(w)
+        exact = sum(Fraction(float(v)) for v in np.abs(w).ravel()) / w.size
+        assert s_w == np.float32(round_fraction_to_f32(exact))
+        # row sums agree with exact row sums to float64 accuracy
+        r0 = sum(Fraction(float(v)) for v in np.abs(w[0]))
+        assert abs(Fraction(rows[0]) - r0) <= abs(r0) * Fraction(1, 2 ** 45)
+
+
+def test_ternary_density_closed_form():
+    # For w ~ N(0, s): mean|w| = s*sqrt(2/pi); t != 0 iff |w| > mean|w|/2, so
+    # P(t != 0) = 2 * (1 - Phi(sqrt(2/pi)/2)) = 0.68996...
+    w = synth.latent_weights(synth.stream_key(5), 2560, 2560, 0.02).numpy()
+    packed, _ = oracle.pack(w, 1e-5)
+    t = decode_unpackbits(packed, 2560)
+    dens = float(np.count_nonzero(t)) / t.size
+    c = math.sqrt(2 / math.pi) / 2
+    expect = 2 * (1 - 0.5 * (1 + math.erf(c / math.sqrt(2))))
+    assert abs(expect - 0.68996) < 1e-4
+    assert abs(dens - expect) < 1.5e-3
+    # and the latent scale: s_w ~ 0.02*sqrt(2/pi)
+    s_w, _ = oracle.weight_scale(w)
+    assert abs(float(s_w) / (0.02 * math.sqrt(2 / math.pi)) - 1) < 2e-3
+
+
+def test_density_weights_round_trip():
+    for d in (0.3, 0.5, 0.7):
+        w = synth.density_weights(synth.stream_key(6, int(d * 10)), 64, 512, d).numpy()
+        packed, s_w = oracle.pack(w, 1e-5)
+        assert np.array_equal(decode_unpackbits(packed, 512), np.rint(w / 0.02).astype(np.int8))
+        nz = np.count_nonzero(w)
+        assert abs(float(s_w) - 0.02 * nz / w.size) < 1e-8
+
+
+# ----------------------------------------------------------------- quant_act
+
+@pytest.mark.parametrize("case", parse_cases("quant_act_cases.txt"))
+def test_quant_golden(case):
+    x = np.array([float(v) for v in case[0].split()], dtype=np.float32)[None, :]
+    q, s = oracle.quant_act(f32_to_bf16_bits(x))
+    assert q[0].tolist() == [int(v) for v in case[1].split()]
+    assert s[0] == np.float32(float(case[2]))
+
+
+def _exhaustive_rows(s_exp: int):
+    """One row per bf16 s in the binade [2^s_exp, 2^(s_exp+1)); the row holds s
+    followed by every bf16 x with |x| <= s over 13 binades below, both signs."""
+    rows = []
+    mant = np.arange(128, dtype=np.uint32)
+    xs = []
+    for e in range(s_exp - 12, s_exp + 1):
+        xs.append(((e + 127) << 7) | mant)
+    xs = np.concatenate(xs).astype(np.uint16)
+    for m in range(128):
+        s_bits = np.uint16(((s_exp + 127) << 7) | m)
+        xv = xs[xs <= s_bits]
+        row = np.concatenate([[s_bits], xv, xv | 0x8000]).astype(np.uint16)
+        rows.append(row)
+    width = max(len(r) for r in rows)
+    # pad with +0 (does not change the max)
+    out = np.zeros((len(rows), width), dtype=np.uint16)
+    for i, r in enumerate(rows):
+        out[i, :len(r)] = r
+    return out
+
+
+@pytest.mark.parametrize("s_exp", [0, -40, 50])
+def test_quant_exhaustive_against_exact_rne(s_exp):
+    x = _exhaustive_rows(s_exp)
+    q, s = oracle.quant_act(x)
+    # exact: x = mx * 2^ex, s = ms * 2^es (integers) -> 127*x/s rounded half-even
+    xb = x.astype(np.int64)
+    sign = np.where(xb & 0x8000, -1, 1)
+    ex_field = (xb >> 7) & 0xFF
+    mx = np.where(ex_field == 0, 0, (xb & 0x7F) | 0x80)
+    sb = xb[:, :1]
+    ms = (sb & 0x7F) | 0x80
+    sh = ex_field - ((sb >> 7) & 0xFF)  # in [-12, 0] for nonzero x
+    sh = np.where(mx == 0, 0, sh)
+    num = 127 * mx * (1 << (sh + 12))
+    den = ms * (1 << 12) * np.ones_like(num)
+    expect = sign * rne_int(num, den)
+    assert np.array_equal(q.astype(np.int64), expect)
+    assert np.array_equal(s, bf16_bits_to_f32(x[:, 0]))
+    # the same decision taken in binary32, (127*x)/s with one rounding each, is
+    # identical: 127*x is exact for bf16 x, so the quotient has one rounding and
+    # never lands on a tie it did not start on.
+    xf = bf16_bits_to_f32(x)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q32 = np.rint((np.float32(127.0) * xf) / xf[:, :1]).astype(np.int64)
+    assert np.array_equal(q32, expect)
+
+
+def test_quant_invariants():
+    x = synth.activations(synth.stream_key(8), 16, 512, outlier_frac=0.001)
+    bits = synth.bf16_bits(x).numpy().view(np.uint16)
+    q, s = oracle.quant_act(bits)
+    # every nonzero row reaches +-127 exactly
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    # x -> -x negates q and keeps s
+    qn, sn = oracle.quant_act(bits ^ np.uint16(0x8000))
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    # x -> 2^j x keeps q, scales s by 2^j (exact in bf16)
+    for j in (-7, 5):
+        xs = (x.float() * (2.0 ** j)).to(torch.bfloat16)
+        qj, sj = oracle.quant_act(synth.bf16_bits(xs).numpy().view(np.uint16))
+        assert np.array_equal(qj, q)
+        assert np.array_equal(sj, (s * np.float32(2.0 ** j)).astype(np.float32))
+
+
+# ----------------------------------------------------------------- linear
+
+def _brute_force(q, s_x, packed, s_w, K):
+    """int64 triple loop in plain Python over decoded weights."""
+    t = decode_unpackbits(packed, K).tolist()
+    M = q.shape[0]
+    N = packed.shape[0]
+    acc = [[sum(int(q[m, k]) * t[n][k] for k in range(K)) for n in range(N)] for m in range(M)]
+    return np.array(acc, dtype=np.int64)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 4), (3, 5, 8), (2, 7, 68), (5, 3, 132)])
+def test_linear_brute_force(M, N, K):
+    key = synth.stream_key(9, M, N, K)
+    x = synth.activations(key, M, K)
+    q, s = oracle.quant_act(synth.bf16_bits(x).numpy().view(np.uint16))
+    packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
+    acc, y = oracle.linear(q, s, packed, np.float32(0.0137))
+    assert np.array_equal(acc.astype(np.int64), _brute_force(q, s, packed, 0.0137, K))
+
+
+def test_linear_matches_float64_matmul():
+    key = synth.stream_key(10)
+    M, N, K = 9, 300, 640
+    x = synth.activations(key, M, K, outlier_frac=0.001)
+    q, s = oracle.quant_act(synth.bf16_bits(x).numpy().view(np.uint16))
+    w = synth.latent_weights(synth.stream_key(key, 5), N, K, 0.02).numpy()
+    packed, s_w = oracle.pack(w)
+    acc, y = oracle.linear(q, s, packed, s_w)
+    t = decode_unpackbits(packed, K).astype(np.float64)
+    ref = q.astype(np.float64) @ t.T
+    assert np.array_equal(acc.astype(np.float64), ref)
+    # and the rescale is a faithful approximation of the float model of the pages
+    yref = ref * (s.astype(np.float64)[:, None] / 127.0) * float(s_w)
+    assert np.allclose(y, yref, rtol=2 ** -23, atol=0)
+
+
+def test_linear_k_permutation_invariance():
+    key = synth.stream_key(12)
+    M, N, K = 4, 33, 256
+    x = synth.activations(key, M, K)
+    q, s = oracle.quant_act(synth.bf16_bits(x).numpy().view(np.uint16))
+    w = synth.density_weights(synth.stream_key(key, 1), N, K, 0.7).numpy()
+    packed, s_w = oracle.pack(w)
+    acc, y = oracle.linear(q, s, packed, s_w)
+    perm = np.random.default_rng(0).permutation(K)
+    packed_p, s_wp = oracle.pack(np.ascontiguousarray(w[:, perm]))
+    assert s_wp == s_w
+    acc_p, y_p = oracle.linear(np.ascontiguousarray(q[:, perm]), s, packed_p, s_w)
+    assert np.array_equal(acc, acc_p) and np.array_equal(y, y_p)
+
+
+def test_linear_negating_w_negates_outputs():
+    key = synth.stream_key(13)
+    M, N, K = 3, 50, 384
+    x = synth.activations(key, M, K, outlier_frac=0.01)
+    q, s = oracle.quant_act(synth.bf16_bits(x).numpy().view(np.uint16))
+    w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02).numpy()
+    p1, s1 = oracle.pack(w)
+    p2, s2 = oracle.pack(-w)
+    a1, y1 = oracle.linear(q, s, p1, s1)
+    a2, y2 = oracle.linear(q, s, p2, s2)
+    assert np.array_equal(a1, -a2) and np.array_equal(y1, -y2)
+
+
+def test_linear_all_plus_one_and_code3():
+    key = synth.stream_key(14)
+    M, N, K = 6, 4, 320
+    x = synth.activations(key, M, K)
+    q, s = oracle.quant_act(synth.bf16_bits(x).numpy().view(np.uint16))
+    plus = np.full((N, K // 4), 0xAA, np.uint8)       # every code 2 -> +1
+    acc, _ = oracle.linear(q, s, plus, np.float32(1.0))
+    assert np.array_equal(acc, np.repeat(q.astype(np.int32).sum(1, keepdims=True), N, 1))
+    three = np.full((N, K // 4), 0xFF, np.uint8)      # code 3 decodes to +2
+    acc3, _ = oracle.linear(q, s, three, np.float32(1.0))
+    assert np.array_equal(acc3, 2 * acc)
+    zero = np.full((N, K // 4), 0x55, np.uint8)
+    acc0, y0 = oracle.linear(q, s, zero, np.float32(0.5))
+    assert np.all(acc0 == 0) and np.all(y0 == 0)
+    # a constant positive row quantizes to 127 everywhere -> acc = 127 K
+    xc = np.full((1, K), 0.75, np.float32)
+    qc, sc = oracle.quant_act(f32_to_bf16_bits(xc))
+    accc, _ = oracle.linear(qc, sc, plus[:1], np.float32(1.0))
+    assert accc[0, 0] == 127 * K
+
+
+def test_epilogue_is_correctly_rounded():
+    key = synth.stream_key(15)
+    M, N, K = 4, 200, 512
+    x = synth.activations(key, M, K, row_scale=(0.1, 10.0))
+    q, s = oracle.quant_act(synth.bf16_bits(x).numpy().view(np.uint16))
+    w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02).numpy()
+    packed, s_w = oracle.pack(w)
+    acc, y = oracle.linear(q, s, packed, s_w)
+    for m in range(M):
+        for n in range(N):
+            exact = Fraction(int(acc[m, n])) * Fraction(float(s[m])) * Fraction(float(s_w)) / 127
+            assert y[m, n] == np.float32(round_fraction_to_f32(exact)), (m, n)
+    # extreme accumulators
+    qx = np.full((1, K), 127, np.int8)
+    acc_x, y_x = oracle.linear(qx, np.array([3.0e5], np.float32), np.full((1, K // 4), 0xAA, np.uint8),
+                               np.float32(7.77e-3))
+    exact = Fraction(127 * K) * Fraction(float(np.float32(3.0e5))) * Fraction(float(np.float32(7.77e-3))) / 127
+    assert y_x[0, 0] == np.float32(round_fraction_to_f32(exact))
