@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Bench: the BitNet b1.58 BitLinear forward on one MI355X.
+
+Headline workload (the `value`): one decode step over 30 distinct 2.4B-shaped
+transformer layers at M = 1 -- per layer q (2560->2560), k and v (2560->640),
+o (2560->2560), gate and up (2560->6912), down (6912->2560): 210 matrices,
+2,084,044,800 ternary weights, 521,011,200 packed bytes (about twice the
+256 MB on-chip cache).  A step is one pass of the whole hot path: per-token
+int8 quantization of the 120 activation vectors (one grouped launch) and the
+210 ternary GEMVs with their fp32 rescale (one grouped launch).  Weight
+ternarization / packing is the offline step and runs once before timing.
+Inputs are seeded synthetic tensors generated in HBM before the timed region.
+
+value = packed weight bytes per step / wall time per step (GB/s, 1 GB = 1e9 B).
+
+Also reported: the roofline of the dominant kernel (the grouped GEMV) from HIP
+events recorded on its stream inside the timed region, the prefill GEMM
+(M = 2048) in int8 TOPS against the dense int8 MFMA peak, the batched-decode
+sweep, and the CPU oracle timed on a bounded sample of the headline workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOPS
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "ternary_weight_token_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None
+    when the counters were taken on different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(f"{kernel}|{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling PMC byte counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    from synth import workloads as W
+    import ternary_weight_token_amd as tw
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    tw.lib()
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------ headline setup
+    t0 = time.time()
+    mats = W.decode_step_2p4b(30)
+    packed, sws = [], []
+    for m in mats:
+        w = W.weights(m, dev)
+        p, s = tw.pack_weights(w, 1e-5)
+        packed.append(p)
+        sws.append(s)
+        del w
+    xs = [W.decode_step_activations(l, dev) for l in range(30)]
+    qs = [[torch.empty((1, x.shape[1]), dtype=torch.int8, device=dev) for x in xl] for xl in xs]
+    sxs = [[torch.empty(1, dtype=torch.float32, device=dev) for _ in xl] for xl in xs]
+    ys = [torch.empty((1, m.N), dtype=torch.float32, device=dev) for m in mats]
+    qplan = tw.bitnet_grouped_plan_quant([(xs[l][s], qs[l][s], sxs[l][s]) for l in range(30) for s in range(4)])
+    lplan = tw.bitnet_grouped_plan_linear(
+        [(qs[m.layer][m.slot], sxs[m.layer][m.slot], packed[i], sws[i], ys[i], None) for i, m in enumerate(mats)])
+    torch.cuda.synchronize()
+    weight_bytes = sum(m.N * m.K // 4 for m in mats)
+    n_weights = sum(m.N * m.K for m in mats)
+    # algorithmic bytes of one grouped GEMV launch: 0.25 B per weight, 1 B per q
+    # element read, 4 B per output, 4 B per s_x read, 4 B per s_w read
+    gemv_bytes = weight_bytes + sum(m.K + 4 * m.N + 8 for m in mats)
+    log(f"decode step ready in {time.time() - t0:.1f}s: {len(mats)} matrices, {weight_bytes} packed bytes")
+
+    # ------------------------------------------------------------ timed region
+    for _ in range(args.warmup):
+        qplan.launch(stream)
+        lplan.launch(stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e_start.record(stream)
+    for i in range(args.steps):
+        qplan.launch(stream)
+        ev[i][0].record(stream)
+        lplan.launch(stream)
+        ev[i][1].record(stream)
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = wall * 1e3 / args.steps
+    ev_ms_per_step = e_start.elapsed_time(e_end) / args.steps
+    gemv_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    value = weight_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = gemv_bytes / (gemv_ms * 1e-3) / 1e9
+    log(f"step {ms_per_step * 1e3:.1f} us wall ({ev_ms_per_step * 1e3:.1f} us events), "
+        f"grouped GEMV {gemv_ms * 1e3:.1f} us -> {achieved:.0f} GB/s")
+    # sanity: outputs of the last step are finite
+    for y in ys:
+        assert torch.isfinite(y).all()
+
+    line = {
+        "metric": "BitLinear M=1 weight-stream GB/s (% HBM peak); int8 TOPS at M=2048",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded SplitMix64 inputs generated in HBM)",
+        "config": {
+            "workload": "decode step: 30 x 2.4B-shaped layers {q,k,v,o,gate,up,down}, M=1, "
+                        "grouped quant + grouped GEMV launch per step",
+            "matrices": len(mats), "weights": n_weights, "packed_bytes": weight_bytes,
+            "hbm_frac_of_value": round(value / HBM_PEAK_GBS, 4),
+            "weights_per_s": round(n_weights / (ms_per_step * 1e-3), 1),
+        },
+        "roofline": {
+            "kernel": "gemv_grouped_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": committed_traffic("gemv_grouped_kernel", "decode_step_2p4b"),
+            "algorithmic_bytes_per_launch": gemv_bytes,
+            "avg_launch_us": round(gemv_ms * 1e3, 2),
+        },
+    }
+
+    # ------------------------------------------------------------ secondary legs
+    if not args.no_secondary:
+        sec = {}
+        # prefill GEMM, M = 2048
+        reps = 50
+        for name in ("up", "down"):
+            for density in (None, 0.3, 0.5, 0.7):
+                x, w = W.prefill_inputs(name, density, dev)
+                p, s = tw.pack_weights(w, 1e-5)
+                del w
+                q, sx = tw.quant_act(x)
+                N, K = p.shape[0], q.shape[1]
+                y = torch.empty((2048, N), dtype=torch.float32, device=dev)
+                for _ in range(5):
+                    tw.bitnet_linear(q, sx, p, s, y)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(reps):
+                    tw.bitnet_linear(q, sx, p, s, y)
+                b.record(stream)
+                torch.cuda.synchronize()
+                us = a.elapsed_time(b) * 1e3 / reps
+                tops = 2.0 * 2048 * N * K / (us * 1e-6) / 1e12
+                key = f"prefill_{name}_M2048" + ("" if density is None else f"_density{int(density * 100)}")
+                sec[key] = {"us": round(us, 2), "int8_tops": round(tops, 1),
+                            "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+                log(f"{key}: {us:.1f} us, {tops:.0f} TOPS")
+        # batched-decode sweep K=2560 N=6912: both kernels at every M
+        p, s = tw.pack_weights(W.sweep_weights(dev), 1e-5)
+        sweep = {}
+        for M in (1, 2, 4, 8, 16, 32, 64):
+            q, sx = tw.quant_act(W.sweep_activations(M, dev))
+            y = torch.empty((M, p.shape[0]), dtype=torch.float32, device=dev)
+            row = {}
+            for kname, kid in (("gemv", 1), ("gemm", 2)):
+                for _ in range(5):
+                    tw.bitnet_linear_select(q, sx, p, s, y, None, kid)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(100):
+                    tw.bitnet_linear_select(q, sx, p, s, y, None, kid)
+                b.record(stream)
+                torch.cuda.synchronize()
+                us = a.elapsed_time(b) * 1e3 / 100
+                row[kname] = {"us": round(us, 2), "weight_GBs": round(p.numel() / (us * 1e-6) / 1e9, 1)}
+            sweep[f"M{M}"] = row
+        sec["sweep_K2560_N6912"] = sweep
+        log(f"sweep: {json.dumps(sweep)}")
+        line["secondary"] = sec
+
+    # ------------------------------------------------------------ CPU baseline
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        oracle.set_threads(threads)
+        layers = [0, 1, 2, 3]
+        sample = [i for i, m in enumerate(mats) if m.layer in layers]
+        host_inputs = []
+        for i in sample:
+            m = mats[i]
+            w = W.weights(m, dev).cpu().numpy()
+            p_ref, sw_ref = oracle.pack(w, 1e-5)
+            host_inputs.append((m, p_ref, sw_ref))
+        xs_host = {(l, s): synth.bf16_bits(xs[l][s].cpu()).numpy().view(np.uint16)
+                   for l in layers for s in range(4)}
+        done_bytes, reps = 0, 0
+        c0 = time.perf_counter()
+        while True:
+            qcache = {k: oracle.quant_act(v) for k, v in xs_host.items()}
+            for m, p_ref, sw_ref in host_inputs:
+                qv, sv = qcache[(m.layer, m.slot)]
+                oracle.linear(qv, sv, p_ref, sw_ref)
+                done_bytes += m.N * m.K // 4
+            reps += 1
+            if time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        cpu_s = time.perf_counter() - c0
+        line["cpu_baseline"] = {
+            "value": round(done_bytes / cpu_s / 1e9, 3),
+            "unit": "GB/s",
+            "cores": oracle.get_threads(),
+            "kind": "oracle",
+            "sample": f"layers 0-3 of the decode step (28 matrices, quant of 16 vectors + 28 ternary "
+                      f"GEMVs), repeated {reps}x over {cpu_s:.1f}s",
+        }
+        log(f"cpu oracle: {line['cpu_baseline']['value']} GB/s on {oracle.get_threads()} threads")
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device copies done")
+
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

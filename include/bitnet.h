@@ -1,0 +1,199 @@
+/*
+ * bitnet.h -- C ABI of the MI355X (gfx950) BitNet b1.58 BitLinear forward.
+ *
+ * The operation (pages: "BitNet 深度拆解……" on chenxutan.com, sec. 2.2
+ * absmean / absmax quantization, sec. 2.3 rescale, sec. 3.1 BitLinear.forward,
+ * sec. 3.3 INT2 packing; "1-bit推理框架bitnet.cpp实测……" on 0539edu.com,
+ * sec. 2.1 RoundClip):
+ *
+ *   s_w      = mean |W|                                   (per tensor)
+ *   t[n][k]  = clamp(round_half_even(W[n][k] / (s_w + eps)), -1, 1)
+ *   s_x[m]   = max_k |x[m][k]|                             (per token)
+ *   q[m][k]  = clamp(round_half_even(127 * x[m][k] / s_x[m]), -127, 127)
+ *   acc[m][n]= sum_k q[m][k] * t[n][k]                     (exact int32)
+ *   y[m][n]  = acc[m][n] * s_x[m] * s_w / 127               (fp32)
+ *
+ * Layouts (all row-major, K is the contiguous dimension):
+ *   W       fp32  [N][K]     (nn.Linear weight: out_features x in_features)
+ *   packed  uint8 [N][K/4]   byte (n, j) holds weights (n, 4j+i), i = 0..3, in
+ *                            bits 2i..2i+1 as code t + 1 (0, 1, 2); a code of 3
+ *                            is never written and is read as weight +2
+ *   x       bf16  [M][K]     raw bit patterns (uint16)
+ *   q       int8  [M][K],  s_x fp32 [M],  s_w fp32 [1]
+ *   y       fp32  [M][N],  acc int32 [M][N]
+ *
+ * Memory and execution
+ *   Every pointer argument marked (device) is device memory on the current HIP
+ *   device; scales stay on the device, so consecutive calls need no host
+ *   synchronisation.  The caller owns every buffer; the library allocates no
+ *   memory and keeps no state between calls.  Work is enqueued asynchronously
+ *   on `stream` (a hipStream_t, NULL = the default stream); buffers must stay
+ *   valid until that work has completed.  Calls on different streams may run
+ *   concurrently as long as their output buffers do not overlap.
+ *
+ * Errors
+ *   Arguments are checked on the host before anything is enqueued; a failed
+ *   check returns a status and enqueues nothing.  A launch failure reported by
+ *   the runtime returns BITNET_ERR_HIP (the runtime's message is available
+ *   from bitnet_last_error()).  Faults during execution surface at the
+ *   caller's next synchronisation.  Inputs are assumed finite (non-finite
+ *   inputs give unspecified values, never out-of-bounds accesses).
+ *
+ * Sizes: M, N, K are int64_t; K must be positive and a multiple of 4; M == 0 or
+ * N == 0 is a successful no-op.  Fast kernels are used when K % 64 == 0 and the
+ * q / packed / x base pointers are 16-byte aligned; other valid inputs take a
+ * slower general kernel with identical results.
+ */
+#ifndef BITNET_H
+#define BITNET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(BITNET_BUILD)
+#define BITNET_API __attribute__((visibility("default")))
+#else
+#define BITNET_API
+#endif
+
+typedef enum bitnet_status {
+    BITNET_OK = 0,
+    BITNET_ERR_NULL = 1,   /* a required pointer is NULL                      */
+    BITNET_ERR_SHAPE = 2,  /* negative size, K <= 0, K % 4 != 0, bad count    */
+    BITNET_ERR_ALIGN = 3,  /* a pointer the call requires aligned is not      */
+    BITNET_ERR_HIP = 4,    /* the HIP runtime reported an error               */
+    BITNET_ERR_ARG = 5     /* other invalid argument (workspace too small,
+                              plan not made by bitnet_grouped_plan, ...)       */
+} bitnet_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+BITNET_API const char *bitnet_status_str(int status);
+
+/* Message of the last BITNET_ERR_HIP / BITNET_ERR_ARG on the calling thread
+ * ("" if none). */
+BITNET_API const char *bitnet_last_error(void);
+
+/* ABI version (major * 100 + minor). */
+BITNET_API int bitnet_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Weight ternarization and packing (offline step).
+ * Pages: chenxutan.com sec. 2.2 (absmean_quantize) and sec. 3.3 (pack_ternary);
+ * 0539edu.com sec. 2.1 (scale = mean|w|, RoundClip to [-1, 1]).
+ *
+ *   w          (device) fp32 [N][K], 16-byte aligned
+ *   eps        added to s_w before dividing (the configurations use 1e-5)
+ *   packed     (device) uint8 [N][K/4], output
+ *   s_w        (device) fp32 [1], output: mean |W| rounded once to fp32
+ *   workspace  (device) at least bitnet_pack_workspace_bytes(N, K) bytes,
+ *              8-byte aligned; holds per-row float64 sums during the call
+ *
+ * s_w is formed in float64: each row summed in increasing k, the row sums
+ * added in increasing n, then one rounding to fp32; d = s_w + eps and w / d are
+ * single binary32 operations (round to nearest even), so the result is
+ * reproducible bit for bit.  N == 0 writes s_w = 0.
+ * ------------------------------------------------------------------------- */
+BITNET_API size_t bitnet_pack_workspace_bytes(int64_t N, int64_t K);
+BITNET_API int bitnet_pack_weights(const float *w, int64_t N, int64_t K, float eps,
+                                   uint8_t *packed, float *s_w,
+                                   void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Per-token absmax int8 activation quantization.
+ * Page: chenxutan.com sec. 2.2 (absmax_quantize, 8 bits -> qmax 127).
+ *
+ *   x    (device) bf16 bit patterns [M][K]
+ *   q    (device) int8 [M][K], output
+ *   s_x  (device) fp32 [M], output: max_k |x[m][k]| (exact)
+ *
+ * q = round_half_even((127 * x) / s_x) with 127 * x exact and one correctly
+ * rounded binary32 division, which equals the exact rounding of the real
+ * quotient for every bf16 input; a row of zeros gives s_x = 0 and q = 0.
+ * ------------------------------------------------------------------------- */
+BITNET_API int bitnet_quant_act(const uint16_t *x, int64_t M, int64_t K,
+                                int8_t *q, float *s_x, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Ternary contraction with the fp32 rescale (BitLinear forward after the two
+ * quantizations).  Pages: chenxutan.com sec. 2.3 (Y ~ (W_t . X_q) * act_scale *
+ * beta) and sec. 3.1 (BitLinear.forward); the ternary product is a sign-select
+ * add/subtract (chenxutan.com sec. 1).
+ *
+ *   q, s_x   (device) outputs of bitnet_quant_act
+ *   packed   (device) uint8 [N][K/4], s_w (device) fp32 [1]: outputs of
+ *            bitnet_pack_weights (any bytes are accepted; code 3 reads as +2)
+ *   y        (device) fp32 [M][N], output
+ *   acc      (device) int32 [M][N], output, or NULL to skip it
+ *
+ * acc is exact.  y is acc * s_x[m] * s_w / 127 evaluated as
+ * fp32(acc * c_m) with c_m = (s_x[m] * s_w) / 127 in float64, i.e. within one
+ * unit in the last place of the correctly rounded value.  M <= 16 runs the
+ * decode GEMV (v_dot4); larger M runs the int8 MFMA GEMM.
+ * ------------------------------------------------------------------------- */
+BITNET_API int bitnet_linear(const int8_t *q, const float *s_x, const uint8_t *packed,
+                             const float *s_w, int64_t M, int64_t N, int64_t K,
+                             float *y, int32_t *acc, void *stream);
+
+/* Same as bitnet_linear with the kernel chosen by the caller instead of by M
+ * (for measuring the GEMV / GEMM crossover): kernel 0 = automatic, 1 = decode
+ * GEMV (any M; M > 8 re-reads the weights once per 8 rows of q), 2 = MFMA GEMM,
+ * 3 = general kernel.  Kernels 1 and 2 need K % 64 == 0 and 16-byte aligned q /
+ * packed (else BITNET_ERR_ALIGN); other values give BITNET_ERR_ARG. */
+BITNET_API int bitnet_linear_select(const int8_t *q, const float *s_x, const uint8_t *packed,
+                                    const float *s_w, int64_t M, int64_t N, int64_t K,
+                                    float *y, int32_t *acc, int kernel, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Grouped decode calls: many independent quant_act or linear problems in one
+ * launch (a decode step has hundreds of small matrices; one launch each would
+ * be dominated by dispatch gaps).  Same definitions and results as the single
+ * calls, problem by problem.
+ *
+ * A plan is a byte image built on the host by bitnet_grouped_plan_*() from an
+ * array of descriptors, copied by the caller to device memory once (e.g. with
+ * hipMemcpy), and then launched any number of times.  The host image is needed
+ * at launch for the grid size; the device copy is what the kernel reads.  The
+ * pointers inside the descriptors are baked into the plan.
+ *
+ * Linear descriptors must have 1 <= M <= 16, K % 64 == 0 and 16-byte aligned
+ * q / packed; quant descriptors K % 8 == 0 and 16-byte aligned x / q.
+ * ------------------------------------------------------------------------- */
+typedef struct bitnet_linear_desc {
+    const int8_t *q;        /* (device) [M][K]   */
+    const float *s_x;       /* (device) [M]      */
+    const uint8_t *packed;  /* (device) [N][K/4] */
+    const float *s_w;       /* (device) [1]      */
+    float *y;               /* (device) [M][N]   */
+    int32_t *acc;           /* (device) [M][N] or NULL */
+    int64_t M, N, K;
+} bitnet_linear_desc;
+
+typedef struct bitnet_quant_desc {
+    const uint16_t *x;      /* (device) [M][K] bf16 bits */
+    int8_t *q;              /* (device) [M][K]  */
+    float *s_x;             /* (device) [M]     */
+    int64_t M, K;
+} bitnet_quant_desc;
+
+/* Size in bytes of the plan image for `count` descriptors. */
+BITNET_API size_t bitnet_grouped_plan_bytes(int count, int is_linear, const void *descs);
+/* Build a plan image into plan_host (plan_bytes >= bitnet_grouped_plan_bytes). */
+BITNET_API int bitnet_grouped_plan_linear(const bitnet_linear_desc *descs, int count,
+                                          void *plan_host, size_t plan_bytes);
+BITNET_API int bitnet_grouped_plan_quant(const bitnet_quant_desc *descs, int count,
+                                         void *plan_host, size_t plan_bytes);
+/* Launch a plan: plan_host (host image) and plan_dev (device copy, 16-byte
+ * aligned) must hold the same bytes. */
+BITNET_API int bitnet_linear_grouped(const void *plan_host, const void *plan_dev, void *stream);
+BITNET_API int bitnet_quant_act_grouped(const void *plan_host, const void *plan_dev, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITNET_H */

@@ -1,0 +1,231 @@
+"""Python binding of libbitnet.so, the gfx950 BitNet b1.58 BitLinear forward.
+
+Argument marshalling only: torch tensors (device memory) are turned into raw
+pointers and sizes, the current torch stream into a hipStream_t, and a nonzero
+status into an exception.  Every step of the computation runs in the library's
+HIP kernels; there is no fallback.  The function names are those of the C ABI
+(include/bitnet.h).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitnet.so")
+
+_lib = None
+
+
+class BitnetError(RuntimeError):
+    pass
+
+
+class _LinearDesc(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("s_x", ctypes.c_void_p), ("packed", ctypes.c_void_p),
+                ("s_w", ctypes.c_void_p), ("y", ctypes.c_void_p), ("acc", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class _QuantDesc(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("q", ctypes.c_void_p), ("s_x", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbitnet.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python ternary_weight_token_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.bitnet_status_str.argtypes = [I]
+        L.bitnet_status_str.restype = ctypes.c_char_p
+        L.bitnet_last_error.restype = ctypes.c_char_p
+        L.bitnet_version.restype = I
+        L.bitnet_pack_workspace_bytes.argtypes = [I64, I64]
+        L.bitnet_pack_workspace_bytes.restype = ctypes.c_size_t
+        L.bitnet_pack_weights.argtypes = [P, I64, I64, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
+        L.bitnet_quant_act.argtypes = [P, I64, I64, P, P, P]
+        L.bitnet_linear.argtypes = [P, P, P, P, I64, I64, I64, P, P, P]
+        L.bitnet_linear_select.argtypes = [P, P, P, P, I64, I64, I64, P, P, I, P]
+        L.bitnet_grouped_plan_bytes.argtypes = [I, I, P]
+        L.bitnet_grouped_plan_bytes.restype = ctypes.c_size_t
+        L.bitnet_grouped_plan_linear.argtypes = [P, I, P, ctypes.c_size_t]
+        L.bitnet_grouped_plan_quant.argtypes = [P, I, P, ctypes.c_size_t]
+        L.bitnet_linear_grouped.argtypes = [P, P, P]
+        L.bitnet_quant_act_grouped.argtypes = [P, P, P]
+        for f in ("bitnet_pack_weights", "bitnet_quant_act", "bitnet_linear", "bitnet_linear_select",
+                  "bitnet_grouped_plan_linear", "bitnet_grouped_plan_quant",
+                  "bitnet_linear_grouped", "bitnet_quant_act_grouped"):
+            getattr(L, f).restype = I
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = lib()
+        raise BitnetError(f"{L.bitnet_status_str(status).decode()} "
+                          f"({L.bitnet_last_error().decode()})")
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def bitnet_pack_workspace_bytes(N: int, K: int) -> int:
+    return int(lib().bitnet_pack_workspace_bytes(N, K))
+
+
+def bitnet_pack_weights(w: torch.Tensor, eps: float, packed: torch.Tensor, s_w: torch.Tensor,
+                        workspace: torch.Tensor, stream=None) -> None:
+    """w fp32 [N][K] -> packed uint8 [N][K/4], s_w fp32 [1]."""
+    _dev(w, torch.float32, "w"); _dev(packed, torch.uint8, "packed"); _dev(s_w, torch.float32, "s_w")
+    N, K = w.shape
+    if packed.shape != (N, K // 4) or s_w.numel() != 1:
+        raise ValueError("packed must be [N][K/4] and s_w [1]")
+    _check(lib().bitnet_pack_weights(_ptr(w), N, K, ctypes.c_float(eps), _ptr(packed), _ptr(s_w),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)))
+
+
+def bitnet_quant_act(x: torch.Tensor, q: torch.Tensor, s_x: torch.Tensor, stream=None) -> None:
+    """x bf16 [M][K] -> q int8 [M][K], s_x fp32 [M]."""
+    _dev(x, torch.bfloat16, "x"); _dev(q, torch.int8, "q"); _dev(s_x, torch.float32, "s_x")
+    M, K = x.shape
+    if q.shape != (M, K) or s_x.shape != (M,):
+        raise ValueError("q must be [M][K] and s_x [M]")
+    _check(lib().bitnet_quant_act(_ptr(x), M, K, _ptr(q), _ptr(s_x), _stream(stream)))
+
+
+def bitnet_linear(q: torch.Tensor, s_x: torch.Tensor, packed: torch.Tensor, s_w: torch.Tensor,
+                  y: torch.Tensor, acc: torch.Tensor | None = None, stream=None) -> None:
+    """q int8 [M][K], packed uint8 [N][K/4] -> y fp32 [M][N] (and acc int32 [M][N])."""
+    _dev(q, torch.int8, "q"); _dev(s_x, torch.float32, "s_x"); _dev(packed, torch.uint8, "packed")
+    _dev(s_w, torch.float32, "s_w"); _dev(y, torch.float32, "y")
+    M, K = q.shape
+    N = packed.shape[0]
+    if packed.shape != (N, K // 4) or s_x.shape != (M,) or y.shape != (M, N):
+        raise ValueError("shape mismatch")
+    if acc is not None:
+        _dev(acc, torch.int32, "acc")
+        if acc.shape != (M, N):
+            raise ValueError("acc must be [M][N]")
+    _check(lib().bitnet_linear(_ptr(q), _ptr(s_x), _ptr(packed), _ptr(s_w), M, N, K, _ptr(y),
+                               _ptr(acc), _stream(stream)))
+
+
+KERNEL_AUTO, KERNEL_GEMV, KERNEL_GEMM, KERNEL_GENERIC = 0, 1, 2, 3
+
+
+def bitnet_linear_select(q: torch.Tensor, s_x: torch.Tensor, packed: torch.Tensor, s_w: torch.Tensor,
+                         y: torch.Tensor, acc: torch.Tensor | None, kernel: int, stream=None) -> None:
+    """bitnet_linear with an explicit kernel choice (0 auto, 1 GEMV, 2 GEMM, 3 general)."""
+    _dev(q, torch.int8, "q"); _dev(s_x, torch.float32, "s_x"); _dev(packed, torch.uint8, "packed")
+    _dev(s_w, torch.float32, "s_w"); _dev(y, torch.float32, "y")
+    M, K = q.shape
+    N = packed.shape[0]
+    if packed.shape != (N, K // 4) or s_x.shape != (M,) or y.shape != (M, N):
+        raise ValueError("shape mismatch")
+    if acc is not None:
+        _dev(acc, torch.int32, "acc")
+    _check(lib().bitnet_linear_select(_ptr(q), _ptr(s_x), _ptr(packed), _ptr(s_w), M, N, K, _ptr(y),
+                                      _ptr(acc), int(kernel), _stream(stream)))
+
+
+class GroupedPlan:
+    """A grouped launch plan: host image + device copy (see bitnet_grouped_plan_*)."""
+
+    def __init__(self, host: bytes, dev: torch.Tensor, kind: str, refs: list):
+        self.host = ctypes.create_string_buffer(host, len(host))
+        self.dev = dev
+        self.kind = kind
+        self._refs = refs  # keep the described tensors alive
+
+    def launch(self, stream=None) -> None:
+        f = lib().bitnet_linear_grouped if self.kind == "linear" else lib().bitnet_quant_act_grouped
+        _check(f(ctypes.cast(self.host, ctypes.c_void_p), _ptr(self.dev), _stream(stream)))
+
+
+def bitnet_grouped_plan_linear(problems, device=None) -> GroupedPlan:
+    """problems: list of (q, s_x, packed, s_w, y, acc_or_None)."""
+    arr = (_LinearDesc * len(problems))()
+    refs = []
+    for i, (q, s_x, packed, s_w, y, acc) in enumerate(problems):
+        M, K = q.shape
+        arr[i] = _LinearDesc(q.data_ptr(), s_x.data_ptr(), packed.data_ptr(), s_w.data_ptr(),
+                             y.data_ptr(), 0 if acc is None else acc.data_ptr(), M, packed.shape[0], K)
+        refs.append((q, s_x, packed, s_w, y, acc))
+    n = lib().bitnet_grouped_plan_bytes(len(problems), 1, ctypes.cast(arr, ctypes.c_void_p))
+    buf = ctypes.create_string_buffer(n)
+    _check(lib().bitnet_grouped_plan_linear(ctypes.cast(arr, ctypes.c_void_p), len(problems),
+                                            ctypes.cast(buf, ctypes.c_void_p), n))
+    host = buf.raw
+    dev = torch.frombuffer(bytearray(host), dtype=torch.uint8).to(device or problems[0][0].device)
+    return GroupedPlan(host, dev, "linear", refs)
+
+
+def bitnet_grouped_plan_quant(problems, device=None) -> GroupedPlan:
+    """problems: list of (x, q, s_x)."""
+    arr = (_QuantDesc * len(problems))()
+    refs = []
+    for i, (x, q, s_x) in enumerate(problems):
+        M, K = x.shape
+        arr[i] = _QuantDesc(x.data_ptr(), q.data_ptr(), s_x.data_ptr(), M, K)
+        refs.append((x, q, s_x))
+    n = lib().bitnet_grouped_plan_bytes(len(problems), 0, ctypes.cast(arr, ctypes.c_void_p))
+    buf = ctypes.create_string_buffer(n)
+    _check(lib().bitnet_grouped_plan_quant(ctypes.cast(arr, ctypes.c_void_p), len(problems),
+                                           ctypes.cast(buf, ctypes.c_void_p), n))
+    host = buf.raw
+    dev = torch.frombuffer(bytearray(host), dtype=torch.uint8).to(device or problems[0][0].device)
+    return GroupedPlan(host, dev, "quant", refs)
+
+
+# ----------------------------------------------------------------- conveniences
+
+def pack_weights(w: torch.Tensor, eps: float = 1e-5, stream=None):
+    """Allocate outputs and run bitnet_pack_weights -> (packed, s_w)."""
+    N, K = w.shape
+    packed = torch.empty((N, K // 4), dtype=torch.uint8, device=w.device)
+    s_w = torch.empty(1, dtype=torch.float32, device=w.device)
+    ws = torch.empty(max(1, bitnet_pack_workspace_bytes(N, K) // 8), dtype=torch.float64, device=w.device)
+    bitnet_pack_weights(w, eps, packed, s_w, ws, stream)
+    return packed, s_w
+
+
+def quant_act(x: torch.Tensor, stream=None):
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    s_x = torch.empty(M, dtype=torch.float32, device=x.device)
+    bitnet_quant_act(x, q, s_x, stream)
+    return q, s_x
+
+
+def linear(q, s_x, packed, s_w, want_acc: bool = False, stream=None):
+    M, K = q.shape
+    N = packed.shape[0]
+    y = torch.empty((M, N), dtype=torch.float32, device=q.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=q.device) if want_acc else None
+    bitnet_linear(q, s_x, packed, s_w, y, acc, stream)
+    return (y, acc) if want_acc else y

@@ -1,0 +1,274 @@
+// C ABI of the library: argument checks on the host, then dispatch to the gfx950
+// kernels.  Checks never touch the GPU, so a failed check enqueues nothing.
+#define BITNET_BUILD 1
+#include "../../include/bitnet.h"
+
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+using namespace bitnet;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // kernels index rows and columns with int32
+constexpr int64_t kGemvMaxM = 16;
+
+int fail(int status, const char *msg) {
+    g_last_error = msg;
+    return status;
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return BITNET_OK;
+    g_last_error = hipGetErrorString(e);
+    return BITNET_ERR_HIP;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_dims(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K <= 0 || K % 4 != 0) return fail(BITNET_ERR_SHAPE, "bad M/N/K");
+    if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return fail(BITNET_ERR_SHAPE, "dimension too large");
+    if (M * K >= ((int64_t)1 << 40) || N * K >= ((int64_t)1 << 42) || M * N >= ((int64_t)1 << 40))
+        return fail(BITNET_ERR_SHAPE, "problem too large");
+    return BITNET_OK;
+}
+
+int check_linear(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
+                 int64_t M, int64_t N, int64_t K, const float *y, const int32_t *acc) {
+    int st = check_dims(M, N, K);
+    if (st) return st;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!q || !s_x || !packed || !s_w || !y) return fail(BITNET_ERR_NULL, "null pointer");
+    if (!aligned(s_x, 4) || !aligned(s_w, 4) || !aligned(y, 4) || (acc && !aligned(acc, 4)))
+        return fail(BITNET_ERR_ALIGN, "s_x, s_w, y and acc must be 4-byte aligned");
+    return BITNET_OK;
+}
+
+bool linear_fast(const int8_t *q, const uint8_t *packed, int64_t K) {
+    return K % 64 == 0 && aligned(q, 16) && aligned(packed, 16);
+}
+
+}  // namespace
+
+extern "C" {
+
+BITNET_API const char *bitnet_status_str(int s) {
+    switch (s) {
+        case BITNET_OK: return "BITNET_OK";
+        case BITNET_ERR_NULL: return "BITNET_ERR_NULL: a required pointer is NULL";
+        case BITNET_ERR_SHAPE: return "BITNET_ERR_SHAPE: invalid M, N, K or count";
+        case BITNET_ERR_ALIGN: return "BITNET_ERR_ALIGN: misaligned pointer";
+        case BITNET_ERR_HIP: return "BITNET_ERR_HIP: the HIP runtime reported an error";
+        case BITNET_ERR_ARG: return "BITNET_ERR_ARG: invalid argument";
+        default: return "unknown bitnet status";
+    }
+}
+
+BITNET_API const char *bitnet_last_error(void) { return g_last_error.c_str(); }
+
+BITNET_API int bitnet_version(void) { return 100; }
+
+BITNET_API size_t bitnet_pack_workspace_bytes(int64_t N, int64_t K) {
+    (void)K;
+    return N > 0 ? (size_t)N * sizeof(double) : 0;
+}
+
+BITNET_API int bitnet_pack_weights(const float *w, int64_t N, int64_t K, float eps, uint8_t *packed,
+                                   float *s_w, void *workspace, size_t workspace_bytes, void *stream) {
+    int st = check_dims(0, N, K);
+    if (st) return st;
+    if (!s_w) return fail(BITNET_ERR_NULL, "s_w is NULL");
+    if (N > 0 && (!w || !packed || !workspace)) return fail(BITNET_ERR_NULL, "null pointer");
+    if (!aligned(s_w, 4) || (w && !aligned(w, 4)) || (workspace && !aligned(workspace, 8)))
+        return fail(BITNET_ERR_ALIGN, "w, s_w must be 4-byte and workspace 8-byte aligned");
+    if (workspace_bytes < bitnet_pack_workspace_bytes(N, K))
+        return fail(BITNET_ERR_ARG, "workspace too small");
+    return hip_status(launch_pack(w, N, K, eps, packed, s_w, (double *)workspace, (hipStream_t)stream));
+}
+
+BITNET_API int bitnet_quant_act(const uint16_t *x, int64_t M, int64_t K, int8_t *q, float *s_x,
+                                void *stream) {
+    int st = check_dims(M, 1, K);
+    if (st) return st;
+    if (M == 0) return BITNET_OK;
+    if (!x || !q || !s_x) return fail(BITNET_ERR_NULL, "null pointer");
+    if (!aligned(x, 2) || !aligned(s_x, 4)) return fail(BITNET_ERR_ALIGN, "x must be 2-byte, s_x 4-byte aligned");
+    return hip_status(launch_quant_act(x, M, K, q, s_x, (hipStream_t)stream));
+}
+
+BITNET_API int bitnet_linear(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
+                             int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, void *stream) {
+    int st = check_linear(q, s_x, packed, s_w, M, N, K, y, acc);
+    if (st || M == 0 || N == 0) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (!linear_fast(q, packed, K)) return hip_status(launch_linear_generic(q, s_x, packed, s_w, M, N, K, y, acc, s));
+    if (M <= kGemvMaxM) return hip_status(launch_gemv(q, s_x, packed, s_w, M, N, K, y, acc, s));
+    return hip_status(launch_gemm(q, s_x, packed, s_w, M, N, K, y, acc, s));
+}
+
+BITNET_API int bitnet_linear_select(const int8_t *q, const float *s_x, const uint8_t *packed,
+                                    const float *s_w, int64_t M, int64_t N, int64_t K, float *y,
+                                    int32_t *acc, int kernel, void *stream) {
+    if (kernel == 0) return bitnet_linear(q, s_x, packed, s_w, M, N, K, y, acc, stream);
+    if (kernel < 0 || kernel > 3) return fail(BITNET_ERR_ARG, "kernel must be 0..3");
+    int st = check_linear(q, s_x, packed, s_w, M, N, K, y, acc);
+    if (st || M == 0 || N == 0) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (kernel == 3) return hip_status(launch_linear_generic(q, s_x, packed, s_w, M, N, K, y, acc, s));
+    if (!linear_fast(q, packed, K)) return fail(BITNET_ERR_ALIGN, "kernel needs K % 64 == 0 and 16-byte aligned q/packed");
+    if (kernel == 1) return hip_status(launch_gemv(q, s_x, packed, s_w, M, N, K, y, acc, s));
+    return hip_status(launch_gemm(q, s_x, packed, s_w, M, N, K, y, acc, s));
+}
+
+// ----------------------------------------------------------------- grouped plans
+
+static size_t plan_layout(int count, size_t desc_size, uint64_t blocks, uint64_t *desc_off,
+                          uint64_t *table_off) {
+    *desc_off = sizeof(PlanHeader);
+    *table_off = *desc_off + (uint64_t)count * desc_size;
+    *table_off = (*table_off + 15) & ~(uint64_t)15;
+    return (size_t)(*table_off + blocks * sizeof(BlockEntry));
+}
+
+static uint64_t linear_blocks(const bitnet_linear_desc &d) {
+    const uint64_t rows = gemv_grouped_rows_per_block();
+    return ((uint64_t)d.N + rows - 1) / rows * (uint64_t)d.M;
+}
+
+static int check_linear_desc(const bitnet_linear_desc &d) {
+    int st = check_linear(d.q, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, d.y, d.acc);
+    if (st) return st;
+    if (d.M < 1 || d.M > kGemvMaxM || d.N < 1) return fail(BITNET_ERR_SHAPE, "grouped linear needs 1 <= M <= 16, N >= 1");
+    if (!linear_fast(d.q, d.packed, d.K)) return fail(BITNET_ERR_ALIGN, "grouped linear needs K % 64 == 0 and 16-byte aligned q/packed");
+    return BITNET_OK;
+}
+
+static int check_quant_desc(const bitnet_quant_desc &d) {
+    int st = check_dims(d.M, 1, d.K);
+    if (st) return st;
+    if (d.M < 1) return fail(BITNET_ERR_SHAPE, "grouped quant needs M >= 1");
+    if (!d.x || !d.q || !d.s_x) return fail(BITNET_ERR_NULL, "null pointer");
+    if (d.K % 8 != 0 || !aligned(d.x, 16) || !aligned(d.q, 16) || !aligned(d.s_x, 4))
+        return fail(BITNET_ERR_ALIGN, "grouped quant needs K % 8 == 0 and 16-byte aligned x/q");
+    return BITNET_OK;
+}
+
+BITNET_API size_t bitnet_grouped_plan_bytes(int count, int is_linear, const void *descs) {
+    if (count <= 0 || !descs) return 0;
+    uint64_t blocks = 0, a, b;
+    if (is_linear) {
+        const bitnet_linear_desc *d = (const bitnet_linear_desc *)descs;
+        for (int i = 0; i < count; ++i) blocks += (d[i].M > 0 && d[i].N > 0) ? linear_blocks(d[i]) : 0;
+        return plan_layout(count, sizeof(LinearDescDev), blocks, &a, &b);
+    }
+    const bitnet_quant_desc *d = (const bitnet_quant_desc *)descs;
+    for (int i = 0; i < count; ++i) blocks += d[i].M > 0 ? (uint64_t)d[i].M : 0;
+    return plan_layout(count, sizeof(QuantDescDev), blocks, &a, &b);
+}
+
+BITNET_API int bitnet_grouped_plan_linear(const bitnet_linear_desc *descs, int count, void *plan_host,
+                                          size_t plan_bytes) {
+    if (!descs || !plan_host) return fail(BITNET_ERR_NULL, "null pointer");
+    if (count <= 0) return fail(BITNET_ERR_SHAPE, "count must be positive");
+    uint64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        int st = check_linear_desc(descs[i]);
+        if (st) return st;
+        blocks += linear_blocks(descs[i]);
+    }
+    if (blocks >= ((uint64_t)1 << 31)) return fail(BITNET_ERR_SHAPE, "too many blocks");
+    uint64_t doff, toff;
+    const size_t need = plan_layout(count, sizeof(LinearDescDev), blocks, &doff, &toff);
+    if (plan_bytes < need) return fail(BITNET_ERR_ARG, "plan buffer too small");
+    uint8_t *p = (uint8_t *)plan_host;
+    memset(p, 0, need);
+    PlanHeader *h = (PlanHeader *)p;
+    h->magic = kPlanMagic;
+    h->kind = kPlanLinear;
+    h->count = (uint32_t)count;
+    h->total_blocks = (uint32_t)blocks;
+    h->block_threads = gemv_grouped_threads();
+    h->rows_per_block = gemv_grouped_rows_per_block();
+    h->desc_offset = doff;
+    h->table_offset = toff;
+    h->total_bytes = need;
+    LinearDescDev *dd = (LinearDescDev *)(p + doff);
+    BlockEntry *tb = (BlockEntry *)(p + toff);
+    uint64_t b = 0;
+    for (int i = 0; i < count; ++i) {
+        const bitnet_linear_desc &d = descs[i];
+        dd[i] = LinearDescDev{d.q, d.s_x, d.packed, d.s_w, d.y, d.acc, (int32_t)d.M, (int32_t)d.N, (int32_t)d.K, 0};
+        const uint64_t nb = linear_blocks(d);
+        for (uint64_t j = 0; j < nb; ++j) tb[b++] = BlockEntry{(uint32_t)i, (uint32_t)j};
+    }
+    return BITNET_OK;
+}
+
+BITNET_API int bitnet_grouped_plan_quant(const bitnet_quant_desc *descs, int count, void *plan_host,
+                                         size_t plan_bytes) {
+    if (!descs || !plan_host) return fail(BITNET_ERR_NULL, "null pointer");
+    if (count <= 0) return fail(BITNET_ERR_SHAPE, "count must be positive");
+    uint64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        int st = check_quant_desc(descs[i]);
+        if (st) return st;
+        blocks += (uint64_t)descs[i].M;
+    }
+    if (blocks >= ((uint64_t)1 << 31)) return fail(BITNET_ERR_SHAPE, "too many blocks");
+    uint64_t doff, toff;
+    const size_t need = plan_layout(count, sizeof(QuantDescDev), blocks, &doff, &toff);
+    if (plan_bytes < need) return fail(BITNET_ERR_ARG, "plan buffer too small");
+    uint8_t *p = (uint8_t *)plan_host;
+    memset(p, 0, need);
+    PlanHeader *h = (PlanHeader *)p;
+    h->magic = kPlanMagic;
+    h->kind = kPlanQuant;
+    h->count = (uint32_t)count;
+    h->total_blocks = (uint32_t)blocks;
+    h->block_threads = 256;
+    h->desc_offset = doff;
+    h->table_offset = toff;
+    h->total_bytes = need;
+    QuantDescDev *dd = (QuantDescDev *)(p + doff);
+    BlockEntry *tb = (BlockEntry *)(p + toff);
+    uint64_t b = 0;
+    for (int i = 0; i < count; ++i) {
+        const bitnet_quant_desc &d = descs[i];
+        dd[i] = QuantDescDev{d.x, d.q, d.s_x, (int32_t)d.M, (int32_t)d.K};
+        for (int64_t j = 0; j < d.M; ++j) tb[b++] = BlockEntry{(uint32_t)i, (uint32_t)j};
+    }
+    return BITNET_OK;
+}
+
+static int check_plan(const void *plan_host, const void *plan_dev, uint32_t kind) {
+    if (!plan_host || !plan_dev) return fail(BITNET_ERR_NULL, "null plan");
+    if (!aligned(plan_dev, 16)) return fail(BITNET_ERR_ALIGN, "device plan must be 16-byte aligned");
+    const PlanHeader *h = (const PlanHeader *)plan_host;
+    if (h->magic != kPlanMagic || h->kind != kind) return fail(BITNET_ERR_ARG, "not a plan of this kind");
+    return BITNET_OK;
+}
+
+BITNET_API int bitnet_linear_grouped(const void *plan_host, const void *plan_dev, void *stream) {
+    int st = check_plan(plan_host, plan_dev, kPlanLinear);
+    if (st) return st;
+    const PlanHeader *h = (const PlanHeader *)plan_host;
+    if (h->total_blocks == 0) return BITNET_OK;
+    return hip_status(launch_gemv_grouped(plan_dev, h->total_blocks, (hipStream_t)stream));
+}
+
+BITNET_API int bitnet_quant_act_grouped(const void *plan_host, const void *plan_dev, void *stream) {
+    int st = check_plan(plan_host, plan_dev, kPlanQuant);
+    if (st) return st;
+    const PlanHeader *h = (const PlanHeader *)plan_host;
+    if (h->total_blocks == 0) return BITNET_OK;
+    return hip_status(launch_quant_act_grouped(plan_dev, h->total_blocks, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Device-side helpers shared by the gfx950 kernels of this library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitnet {
+
+// Four signed bytes of `a` dotted with four signed bytes of `b`, plus c
+// (v_dot4_i32_i8).
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// Codes of one packed dword (16 weights: byte b holds k = 4b + i in bits 2i..2i+1)
+// regrouped by i: lane i of the result holds, in byte b, the code of k = 4b + i.
+__device__ __forceinline__ uint32_t codes_i(uint32_t w, int i) {
+    return (w >> (2 * i)) & 0x03030303u;
+}
+
+// Ternary value (code - 1) of four codes held one per byte: v_perm_b32 used as
+// a 4-entry byte table {0xFF, 0x00, 0x01, 0x02}.
+__device__ __forceinline__ uint32_t codes_to_ternary(uint32_t c) {
+    return __builtin_amdgcn_perm(0u, 0x020100FFu, c);
+}
+
+// 4x4 byte transpose: given natural dwords Q0..Q3 (Qj byte b = element 4j + b)
+// return P0..P3 with Pi byte b = element 4b + i, the order codes_i() produces.
+__device__ __forceinline__ void transpose4x4(uint32_t q0, uint32_t q1, uint32_t q2, uint32_t q3,
+                                             uint32_t &p0, uint32_t &p1, uint32_t &p2, uint32_t &p3) {
+    // v_perm_b32(a, b, sel): selector 0..3 picks bytes of b, 4..7 bytes of a.
+    uint32_t t0 = __builtin_amdgcn_perm(q1, q0, 0x05010400u);  // q0.b0 q1.b0 q0.b1 q1.b1
+    uint32_t t1 = __builtin_amdgcn_perm(q3, q2, 0x05010400u);  // q2.b0 q3.b0 q2.b1 q3.b1
+    uint32_t t2 = __builtin_amdgcn_perm(q1, q0, 0x07030602u);  // q0.b2 q1.b2 q0.b3 q1.b3
+    uint32_t t3 = __builtin_amdgcn_perm(q3, q2, 0x07030602u);  // q2.b2 q3.b2 q2.b3 q3.b3
+    p0 = __builtin_amdgcn_perm(t1, t0, 0x05040100u);           // q0.b0 q1.b0 q2.b0 q3.b0
+    p1 = __builtin_amdgcn_perm(t1, t0, 0x07060302u);           // q0.b1 q1.b1 q2.b1 q3.b1
+    p2 = __builtin_amdgcn_perm(t3, t2, 0x05040100u);
+    p3 = __builtin_amdgcn_perm(t3, t2, 0x07060302u);
+}
+
+// Sum over the 8 lanes of each aligned lane octet (DPP: quad swaps, then the
+// half-row mirror, which pairs lane i with lane 7 - i of the octet).
+__device__ __forceinline__ int octet_sum(int v) {
+    v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+    v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true);  // row_half_mirror
+    return v;
+}
+
+// Full-wavefront max of non-negative ints (64 lanes).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    #pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        uint32_t u = (uint32_t)__shfl_xor((int)v, o, 64);
+        v = u > v ? u : v;
+    }
+    return v;
+}
+
+// y = fp32(acc * c) with c = (s_x * s_w) / 127 formed in float64.
+__device__ __forceinline__ double rescale_factor(float s_x, float s_w) {
+    return ((double)s_x * (double)s_w) / 127.0;
+}
+__device__ __forceinline__ float rescale(int acc, double c) {
+    return (float)((double)acc * c);
+}
+
+}  // namespace bitnet

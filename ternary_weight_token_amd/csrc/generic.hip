@@ -1,0 +1,38 @@
+// General contraction kernel for shapes the fast kernels do not take
+// (K % 64 != 0 or unaligned q / packed): one thread per output, byte loads.
+// Same definition and results as the fast kernels (pages: chenxutan.com
+// sec. 2.3 and sec. 3.1).
+#include "device_common.h"
+#include "internal.h"
+
+namespace bitnet {
+
+__global__ __launch_bounds__(256) void linear_generic_kernel(
+    const int8_t *__restrict__ q, const float *__restrict__ s_x, const uint8_t *__restrict__ packed,
+    const float *__restrict__ s_w, int64_t M, int64_t N, int64_t K, float *__restrict__ y,
+    int32_t *__restrict__ acc_out) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= M * N) return;
+    const int64_t m = idx / N, n = idx % N;
+    const int8_t *qr = q + m * K;
+    const uint8_t *pr = packed + n * (K / 4);
+    int s = 0;
+    for (int64_t j = 0; j < K / 4; ++j) {
+        const uint32_t b = pr[j];
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) s += (int)qr[4 * j + i] * ((int)((b >> (2 * i)) & 3u) - 1);
+    }
+    y[idx] = rescale(s, rescale_factor(s_x[m], *s_w));
+    if (acc_out) acc_out[idx] = s;
+}
+
+hipError_t launch_linear_generic(const int8_t *q, const float *s_x, const uint8_t *packed,
+                                 const float *s_w, int64_t M, int64_t N, int64_t K, float *y,
+                                 int32_t *acc, hipStream_t st) {
+    const int64_t total = M * N;
+    linear_generic_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st>>>(
+        q, s_x, packed, s_w, M, N, K, y, acc);
+    return hipGetLastError();
+}
+
+}  // namespace bitnet

@@ -1,0 +1,49 @@
+// Host-side declarations shared by the launchers and the C ABI (not exported).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bitnet {
+
+// Plan image for grouped launches.
+constexpr uint32_t kPlanMagic = 0xB17E7A01u;
+constexpr uint32_t kPlanLinear = 1, kPlanQuant = 2;
+
+struct PlanHeader {            // 64 bytes
+    uint32_t magic, kind, count, total_blocks;
+    uint32_t block_threads, rows_per_block, reserved0, reserved1;
+    uint64_t desc_offset, table_offset, total_bytes, reserved2;
+};
+
+struct LinearDescDev {         // 64 bytes, device layout
+    const int8_t *q; const float *s_x; const uint8_t *packed; const float *s_w;
+    float *y; int32_t *acc;
+    int32_t M, N, K, pad;
+};
+
+struct QuantDescDev {          // 32 bytes
+    const uint16_t *x; int8_t *q; float *s_x;
+    int32_t M, K;
+};
+
+struct BlockEntry { uint32_t desc, local; };
+
+// launchers (return hipError_t of the launch)
+hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int8_t *q, float *s_x,
+                            hipStream_t st);
+hipError_t launch_quant_act_grouped(const void *plan_dev, uint32_t blocks, hipStream_t st);
+hipError_t launch_pack(const float *w, int64_t N, int64_t K, float eps, uint8_t *packed,
+                       float *s_w, double *rowsum, hipStream_t st);
+hipError_t launch_gemv(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
+                       int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st);
+hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, hipStream_t st);
+uint32_t gemv_grouped_rows_per_block();
+uint32_t gemv_grouped_threads();
+hipError_t launch_gemm(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
+                       int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st);
+hipError_t launch_linear_generic(const int8_t *q, const float *s_x, const uint8_t *packed,
+                                 const float *s_w, int64_t M, int64_t N, int64_t K, float *y,
+                                 int32_t *acc, hipStream_t st);
+
+}  // namespace bitnet

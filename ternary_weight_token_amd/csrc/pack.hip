@@ -1,0 +1,79 @@
+// Absmean ternarization and 2-bit packing of a weight tensor (pages:
+// chenxutan.com sec. 2.2 absmean_quantize and sec. 3.3 pack_ternary;
+// 0539edu.com sec. 2.1 RoundClip with scale = mean|w|).  Offline step.
+//
+//  1. rowsum_kernel   : one thread per row, sum_k |w| in float64 in increasing k
+//                       (the order is part of the result, so it is fixed);
+//  2. combine_kernel  : one thread, sum_n rowsum in increasing n, one rounding of
+//                       the mean to fp32 -> s_w;
+//  3. code_kernel     : t = clamp(rint(w / (s_w + eps)), -1, 1) with binary32
+//                       ops, code t + 1, four codes per byte, LSB first; works on
+//                       the flat array (K % 4 == 0 keeps bytes inside rows).
+#include "device_common.h"
+#include "internal.h"
+
+namespace bitnet {
+
+__global__ __launch_bounds__(64) void rowsum_kernel(const float *__restrict__ w, int64_t N, int64_t K,
+                                                    double *__restrict__ rowsum) {
+    const int64_t n = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (n >= N) return;
+    const float *r = w + n * K;
+    double s = 0.0;
+    for (int64_t k = 0; k < K; ++k) s += fabs((double)r[k]);
+    rowsum[n] = s;
+}
+
+__global__ __launch_bounds__(64) void combine_kernel(const double *__restrict__ rowsum, int64_t N,
+                                                     int64_t K, float *__restrict__ s_w) {
+    if (threadIdx.x != 0) return;
+    double t = 0.0;
+    for (int64_t n = 0; n < N; ++n) t += rowsum[n];
+    *s_w = (N * K == 0) ? 0.0f : (float)(t / (double)(N * K));
+}
+
+__device__ __forceinline__ uint32_t code_of(float w, float d) {
+    float r = __builtin_rintf(w / d);
+    r = fminf(fmaxf(r, -1.0f), 1.0f);
+    return (uint32_t)((int)r + 1);
+}
+
+__global__ __launch_bounds__(256) void code_kernel(const float *__restrict__ w, int64_t nbytes,
+                                                   float eps, const float *__restrict__ s_w,
+                                                   uint8_t *__restrict__ packed) {
+    const int64_t j4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;  // first byte of this thread
+    if (j4 >= nbytes) return;
+    const float d = *s_w + eps;
+    const int nb = (int)min((int64_t)4, nbytes - j4);
+    uint32_t out = 0;
+    for (int b = 0; b < nb; ++b) {
+        const float *p = w + (j4 + b) * 4;
+        uint32_t byte = code_of(p[0], d) | code_of(p[1], d) << 2 | code_of(p[2], d) << 4 |
+                        code_of(p[3], d) << 6;
+        out |= byte << (8 * b);
+    }
+    if (nb == 4 && ((uintptr_t)(packed + j4) % 4 == 0)) {
+        *reinterpret_cast<uint32_t *>(packed + j4) = out;
+    } else {
+        for (int b = 0; b < nb; ++b) packed[j4 + b] = (uint8_t)(out >> (8 * b));
+    }
+}
+
+hipError_t launch_pack(const float *w, int64_t N, int64_t K, float eps, uint8_t *packed, float *s_w,
+                       double *rowsum, hipStream_t st) {
+    if (N > 0) {
+        rowsum_kernel<<<dim3((unsigned)((N + 63) / 64)), dim3(64), 0, st>>>(w, N, K, rowsum);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    combine_kernel<<<dim3(1), dim3(64), 0, st>>>(rowsum, N, K, s_w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || N == 0) return e;
+    const int64_t nbytes = N * K / 4;
+    const int64_t threads = (nbytes + 3) / 4;
+    code_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st>>>(w, nbytes, eps, s_w,
+                                                                               packed);
+    return hipGetLastError();
+}
+
+}  // namespace bitnet

@@ -1,0 +1,108 @@
+// Per-token absmax int8 activation quantization (page chenxutan.com, sec. 2.2,
+// absmax_quantize with 8 bits: qmax = 127).
+//
+// One workgroup per row: pass 1 takes max|x| over the row (an integer max of the
+// bf16 magnitude bits, exact and order-free; wavefront shuffles, then LDS across
+// the 4 waves), pass 2 re-reads the row (L2-resident) and writes
+// q = rint((127 * x) / s) as int8, 8 codes per 8-byte store.  127 * x is exact
+// in binary32 for bf16 x and the division is the correctly rounded IEEE one.
+#include "device_common.h"
+#include "internal.h"
+
+namespace bitnet {
+
+constexpr int kQThreads = 256;
+
+__device__ __forceinline__ float bf16f(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ int qcode(float x, float s) {
+    float v = (127.0f * x) / s;
+    float r = __builtin_rintf(v);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+template <bool VEC>
+__device__ __forceinline__ void quant_row(const uint16_t *__restrict__ x, int K,
+                                          int8_t *__restrict__ q, float *__restrict__ s_out) {
+    __shared__ uint32_t red[kQThreads / 64];
+    const int tid = threadIdx.x;
+    uint32_t mx = 0;
+    if (VEC) {
+        const uint4 *xv = reinterpret_cast<const uint4 *>(x);
+        for (int v = tid; v < (K >> 3); v += kQThreads) {
+            uint4 u = xv[v];
+            uint32_t a = max(u.x & 0x7FFFu, u.x >> 16 & 0x7FFFu);
+            uint32_t b = max(u.y & 0x7FFFu, u.y >> 16 & 0x7FFFu);
+            uint32_t c = max(u.z & 0x7FFFu, u.z >> 16 & 0x7FFFu);
+            uint32_t d = max(u.w & 0x7FFFu, u.w >> 16 & 0x7FFFu);
+            mx = max(mx, max(max(a, b), max(c, d)));
+        }
+    } else {
+        for (int k = tid; k < K; k += kQThreads) mx = max(mx, (uint32_t)(x[k] & 0x7FFFu));
+    }
+    mx = wave_max_u32(mx);
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    mx = max(max(red[0], red[1]), max(red[2], red[3]));
+    const float s = bf16f(mx);
+    if (tid == 0) *s_out = s;
+    if (VEC) {
+        const uint4 *xv = reinterpret_cast<const uint4 *>(x);
+        uint2 *qv = reinterpret_cast<uint2 *>(q);
+        for (int v = tid; v < (K >> 3); v += kQThreads) {
+            uint2 o = make_uint2(0u, 0u);
+            if (mx != 0) {
+                uint4 u = xv[v];
+                uint32_t w[4] = {u.x, u.y, u.z, u.w};
+                uint32_t b[8];
+                #pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    b[2 * j] = (uint32_t)qcode(bf16f(w[j] & 0xFFFFu), s) & 0xFFu;
+                    b[2 * j + 1] = (uint32_t)qcode(bf16f(w[j] >> 16), s) & 0xFFu;
+                }
+                o.x = b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24;
+                o.y = b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24;
+            }
+            qv[v] = o;
+        }
+    } else {
+        for (int k = tid; k < K; k += kQThreads)
+            q[k] = (mx != 0) ? (int8_t)qcode(bf16f(x[k]), s) : (int8_t)0;
+    }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kQThreads) void quant_act_kernel(const uint16_t *__restrict__ x, int K,
+                                                              int8_t *__restrict__ q,
+                                                              float *__restrict__ s_x) {
+    const size_t m = blockIdx.x;
+    quant_row<VEC>(x + m * K, K, q + m * K, s_x + m);
+}
+
+__global__ __launch_bounds__(kQThreads) void quant_act_grouped_kernel(const uint8_t *__restrict__ plan) {
+    const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
+    const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[blockIdx.x];
+    const QuantDescDev d = reinterpret_cast<const QuantDescDev *>(plan + h->desc_offset)[e.desc];
+    const size_t m = e.local;
+    quant_row<true>(d.x + m * d.K, d.K, d.q + m * d.K, d.s_x + m);
+}
+
+hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int8_t *q, float *s_x,
+                            hipStream_t st) {
+    const bool vec = (K % 8 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)q % 16 == 0);
+    dim3 grid((unsigned)M), block(kQThreads);
+    if (vec)
+        quant_act_kernel<true><<<grid, block, 0, st>>>(x, (int)K, q, s_x);
+    else
+        quant_act_kernel<false><<<grid, block, 0, st>>>(x, (int)K, q, s_x);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_grouped(const void *plan_dev, uint32_t blocks, hipStream_t st) {
+    quant_act_grouped_kernel<<<dim3(blocks), dim3(kQThreads), 0, st>>>(
+        reinterpret_cast<const uint8_t *>(plan_dev));
+    return hipGetLastError();
+}
+
+}  // namespace bitnet

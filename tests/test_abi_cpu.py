@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/bitnet.h declares, and rejects invalid arguments
+before enqueuing anything (no kernel is launched by any call in this file)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import ternary_weight_token_amd as tw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitnet.h")
+
+OK, NULL, SHAPE, ALIGN, HIP, ARG = range(6)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"BITNET_API\s+[\w\s\*]+?\b(bitnet_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tw.LIB_PATH):
+        from ternary_weight_token_amd import build
+        build.build()
+    return tw.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) == 13, names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in range(6):
+        assert L.bitnet_status_str(s).decode().startswith("BITNET_")
+    assert L.bitnet_version() == 100
+
+
+def test_linear_rejects_bad_arguments(L):
+    p = ctypes.c_void_p(256)  # never dereferenced: every call below fails its checks
+    z = None
+    # NULL pointers
+    assert L.bitnet_linear(z, p, p, p, 1, 1, 64, p, z, z) == NULL
+    assert L.bitnet_linear(p, p, p, p, 1, 1, 64, z, z, z) == NULL
+    # shapes
+    assert L.bitnet_linear(p, p, p, p, 1, 1, 6, p, z, z) == SHAPE
+    assert L.bitnet_linear(p, p, p, p, 1, 1, 0, p, z, z) == SHAPE
+    assert L.bitnet_linear(p, p, p, p, -1, 1, 64, p, z, z) == SHAPE
+    assert L.bitnet_linear(p, p, p, p, 1, -5, 64, p, z, z) == SHAPE
+    assert L.bitnet_linear(p, p, p, p, 1 << 31, 1, 64, p, z, z) == SHAPE
+    # alignment of the fp32 / int32 arrays
+    assert L.bitnet_linear(p, ctypes.c_void_p(257), p, p, 1, 1, 64, p, z, z) == ALIGN
+    assert L.bitnet_linear(p, p, p, p, 1, 1, 64, ctypes.c_void_p(258), z, z) == ALIGN
+    assert L.bitnet_linear(p, p, p, p, 1, 1, 64, p, ctypes.c_void_p(2), z) == ALIGN
+    # empty problems are successful no-ops, even with NULL pointers
+    assert L.bitnet_linear(z, z, z, z, 0, 5, 64, z, z, z) == OK
+    assert L.bitnet_linear(z, z, z, z, 3, 0, 64, z, z, z) == OK
+
+
+def test_quant_and_pack_reject_bad_arguments(L):
+    p = ctypes.c_void_p(256)
+    z = None
+    assert L.bitnet_quant_act(z, 1, 64, p, p, z) == NULL
+    assert L.bitnet_quant_act(p, 1, 66, p, p, z) == SHAPE
+    assert L.bitnet_quant_act(ctypes.c_void_p(257), 1, 64, p, p, z) == ALIGN
+    assert L.bitnet_quant_act(z, 0, 64, z, z, z) == OK
+    assert L.bitnet_pack_workspace_bytes(10, 64) == 80
+    assert L.bitnet_pack_weights(z, 2, 64, ctypes.c_float(1e-5), p, p, p, 16, z) == NULL
+    assert L.bitnet_pack_weights(p, 2, 62, ctypes.c_float(1e-5), p, p, p, 16, z) == SHAPE
+    assert L.bitnet_pack_weights(p, 2, 64, ctypes.c_float(1e-5), p, p, p, 8, z) == ARG
+    assert L.bitnet_pack_weights(p, 2, 64, ctypes.c_float(1e-5), p, p, ctypes.c_void_p(260), 16, z) == ALIGN
+
+
+def test_grouped_plan_checks(L):
+    D = tw._LinearDesc
+    a16 = 4096
+    good = D(a16, a16, a16, a16, a16, 0, 1, 100, 2560)
+    arr = (D * 2)(good, D(a16, a16, a16, a16, a16, 0, 17, 100, 2560))
+    n = L.bitnet_grouped_plan_bytes(2, 1, ctypes.cast(arr, ctypes.c_void_p))
+    buf = ctypes.create_string_buffer(n)
+    # M = 17 is beyond the grouped decode path
+    assert L.bitnet_grouped_plan_linear(ctypes.cast(arr, ctypes.c_void_p), 2,
+                                        ctypes.cast(buf, ctypes.c_void_p), n) == SHAPE
+    arr2 = (D * 1)(D(a16 + 4, a16, a16, a16, a16, 0, 1, 100, 2560))
+    assert L.bitnet_grouped_plan_linear(ctypes.cast(arr2, ctypes.c_void_p), 1,
+                                        ctypes.cast(buf, ctypes.c_void_p), n) == ALIGN
+    arr3 = (D * 1)(good)
+    n3 = L.bitnet_grouped_plan_bytes(1, 1, ctypes.cast(arr3, ctypes.c_void_p))
+    assert L.bitnet_grouped_plan_linear(ctypes.cast(arr3, ctypes.c_void_p), 1,
+                                        ctypes.cast(buf, ctypes.c_void_p), n3 - 1) == ARG
+    assert L.bitnet_grouped_plan_linear(ctypes.cast(arr3, ctypes.c_void_p), 1,
+                                        ctypes.cast(buf, ctypes.c_void_p), n3) == OK
+    # a linear plan is not a quant plan; a random buffer is not a plan
+    dev = ctypes.c_void_p(4096)
+    assert L.bitnet_quant_act_grouped(ctypes.cast(buf, ctypes.c_void_p), dev, None) == ARG
+    junk = ctypes.create_string_buffer(128)
+    assert L.bitnet_linear_grouped(ctypes.cast(junk, ctypes.c_void_p), dev, None) == ARG
+    assert L.bitnet_linear_grouped(ctypes.cast(buf, ctypes.c_void_p), ctypes.c_void_p(4100), None) == ALIGN
+    # 13 row sets of 8 * 4 rows for N = 100 ... the block count is in the header
+    hdr = (ctypes.c_uint32 * 4).from_buffer_copy(buf.raw[:16])
+    assert hdr[3] == (100 + 31) // 32
+
+
+def test_python_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    q = torch.zeros((1, 64), dtype=torch.int8)
+    with pytest.raises(ValueError):
+        tw.bitnet_linear(q, torch.zeros(1), torch.zeros((4, 16), dtype=torch.uint8),
+                         torch.zeros(1), torch.zeros((1, 4)))

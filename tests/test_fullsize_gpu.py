@@ -1,0 +1,131 @@
+"""Full-size workloads on the GPU, in the launch configuration the bench times,
+checked against the CPU oracle on sampled matrices / rows / columns.
+
+* decode step: 30 layers x {q, k, v, o, gate, up, down} of the 2.4B shape,
+  M = 1, one grouped quant launch + one grouped GEMV launch (layers 0 and 29
+  compared in full, every matrix's y checked for finiteness);
+* prefill: M = 2048 on up (2560 -> 6912) and down (6912 -> 2560), natural
+  density and 30 / 50 / 70 % nonzero codes, 160 sampled output columns;
+* 100B-scale FFN: gate (8192 -> 28672) and down (28672 -> 8192) of layer 0 at
+  M = 1 and M = 8, compared in full.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import workloads as W
+import ternary_weight_token_amd as tw
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+REL = 2.0 ** -23
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    tw.lib()
+    oracle.set_threads(min(16, max(1, len(os.sched_getaffinity(0)))))
+
+
+def bits_np(x):
+    return synth.bf16_bits(x.contiguous().cpu()).numpy().view(np.uint16)
+
+
+def assert_y(y, y_ref):
+    d = np.abs(y.astype(np.float64) - y_ref.astype(np.float64))
+    assert np.all(d <= REL * np.abs(y_ref.astype(np.float64)))
+
+
+def test_decode_step_grouped():
+    mats = W.decode_step_2p4b(30)
+    sample = {0, 29}
+    packed, sws, host_w = [], [], {}
+    for i, m in enumerate(mats):
+        w = W.weights(m, DEV)
+        p, s = tw.pack_weights(w, 1e-5)
+        packed.append(p)
+        sws.append(s)
+        if m.layer in sample:
+            host_w[i] = w.cpu()
+        del w
+    xs = [W.decode_step_activations(l, DEV) for l in range(30)]
+    qs = [[torch.empty((1, x.shape[1]), dtype=torch.int8, device=DEV) for x in xl] for xl in xs]
+    sxs = [[torch.empty(1, dtype=torch.float32, device=DEV) for _ in xl] for xl in xs]
+    qplan = tw.bitnet_grouped_plan_quant(
+        [(xs[l][s], qs[l][s], sxs[l][s]) for l in range(30) for s in range(4)])
+    ys, accs, probs = [], [], []
+    for i, m in enumerate(mats):
+        y = torch.full((1, m.N), float("nan"), dtype=torch.float32, device=DEV)
+        acc = torch.empty((1, m.N), dtype=torch.int32, device=DEV) if m.layer in sample else None
+        ys.append(y)
+        accs.append(acc)
+        probs.append((qs[m.layer][m.slot], sxs[m.layer][m.slot], packed[i], sws[i], y, acc))
+    lplan = tw.bitnet_grouped_plan_linear(probs)
+    qplan.launch()
+    lplan.launch()
+    torch.cuda.synchronize()
+    for y in ys:
+        assert torch.isfinite(y).all()
+    for l in sorted(sample):
+        for s in range(4):
+            q_ref, sx_ref = oracle.quant_act(bits_np(xs[l][s]))
+            assert np.array_equal(qs[l][s].cpu().numpy(), q_ref)
+            assert np.array_equal(sxs[l][s].cpu().numpy(), sx_ref)
+    for i, m in enumerate(mats):
+        if m.layer not in sample:
+            continue
+        p_ref, sw_ref = oracle.pack(host_w[i].numpy(), 1e-5)
+        assert sws[i].item() == sw_ref
+        assert np.array_equal(packed[i].cpu().numpy(), p_ref)
+        q_ref, sx_ref = oracle.quant_act(bits_np(xs[m.layer][m.slot]))
+        acc_ref, y_ref = oracle.linear(q_ref, sx_ref, p_ref, sw_ref)
+        assert np.array_equal(accs[i].cpu().numpy(), acc_ref), (m.layer, m.name)
+        assert_y(ys[i].cpu().numpy(), y_ref)
+
+
+@pytest.mark.parametrize("name", ["up", "down"])
+@pytest.mark.parametrize("density", [None, 0.3, 0.5, 0.7])
+def test_prefill_sampled(name, density):
+    x, w = W.prefill_inputs(name, density)
+    N, K = w.shape
+    p_ref, sw_ref = oracle.pack(w.numpy(), 1e-5)
+    q_ref, sx_ref = oracle.quant_act(bits_np(x))
+    p, sw = tw.pack_weights(w.to(DEV), 1e-5)
+    q, sx = tw.quant_act(x.to(DEV))
+    y, acc = tw.linear(q, sx, p, sw, want_acc=True)
+    torch.cuda.synchronize()
+    assert sw.item() == sw_ref and np.array_equal(p.cpu().numpy(), p_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref) and np.array_equal(sx.cpu().numpy(), sx_ref)
+    cols = np.sort(np.random.default_rng(7).choice(N, 160, replace=False))
+    cols[-1] = N - 1
+    acc_ref, y_ref = oracle.linear(q_ref, sx_ref, np.ascontiguousarray(p_ref[cols]), sw_ref)
+    assert np.array_equal(acc.cpu().numpy()[:, cols], acc_ref)
+    assert_y(y.cpu().numpy()[:, cols], y_ref)
+
+
+@pytest.mark.parametrize("which", [0, 2])  # gate (8192 -> 28672), down (28672 -> 8192)
+def test_ffn_100b_layer0(which):
+    m = W.ffn_100b(1)[which]
+    w = W.weights(m, DEV)
+    p, sw = tw.pack_weights(w, 1e-5)
+    w_host = w.cpu().numpy()
+    del w
+    p_ref, sw_ref = oracle.pack(w_host, 1e-5)
+    assert sw.item() == sw_ref
+    assert np.array_equal(p.cpu().numpy(), p_ref)
+    for M in (1, 8):
+        x = W.ffn_100b_activations(0, M)[m.slot]
+        q, sx = tw.quant_act(x.to(DEV))
+        y, acc = tw.linear(q, sx, p, sw, want_acc=True)
+        q_ref, sx_ref = oracle.quant_act(bits_np(x))
+        acc_ref, y_ref = oracle.linear(q_ref, sx_ref, p_ref, sw_ref)
+        assert np.array_equal(acc.cpu().numpy(), acc_ref)
+        assert_y(y.cpu().numpy(), y_ref)
