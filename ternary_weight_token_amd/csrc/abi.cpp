@@ -1,10 +1,11 @@
 // C ABI of the library: argument checks on the host, then dispatch to the gfx950
 // kernels.  Checks never touch the GPU, so a failed check enqueues nothing.
 #define BITNET_BUILD 1
-#include "../../include/bitnet.h"
+#include "bitnet.h"
 
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -147,6 +148,7 @@ static int check_linear_desc(const bitnet_linear_desc &d) {
     if (st) return st;
     if (d.M < 1 || d.M > kGemvMaxM || d.N < 1) return fail(BITNET_ERR_SHAPE, "grouped linear needs 1 <= M <= 16, N >= 1");
     if (!linear_fast(d.q, d.packed, d.K)) return fail(BITNET_ERR_ALIGN, "grouped linear needs K % 64 == 0 and 16-byte aligned q/packed");
+    if (gemv_grouped_lds_bytes(d.K) > 64 * 1024) return fail(BITNET_ERR_SHAPE, "grouped linear needs K <= 52416");
     return BITNET_OK;
 }
 
@@ -196,16 +198,24 @@ BITNET_API int bitnet_grouped_plan_linear(const bitnet_linear_desc *descs, int c
     h->total_blocks = (uint32_t)blocks;
     h->block_threads = gemv_grouped_threads();
     h->rows_per_block = gemv_grouped_rows_per_block();
+    for (int i = 0; i < count; ++i) h->lds_bytes = std::max(h->lds_bytes, gemv_grouped_lds_bytes(descs[i].K));
     h->desc_offset = doff;
     h->table_offset = toff;
     h->total_bytes = need;
     LinearDescDev *dd = (LinearDescDev *)(p + doff);
     BlockEntry *tb = (BlockEntry *)(p + toff);
-    uint64_t b = 0;
     for (int i = 0; i < count; ++i) {
         const bitnet_linear_desc &d = descs[i];
         dd[i] = LinearDescDev{d.q, d.s_x, d.packed, d.s_w, d.y, d.acc, (int32_t)d.M, (int32_t)d.N, (int32_t)d.K, 0};
-        const uint64_t nb = linear_blocks(d);
+    }
+    // Workgroups are dispatched roughly in table order: put the longest ones (largest
+    // K, i.e. most bytes per row) first so that the short ones fill the tail.
+    std::vector<int> order(count);
+    for (int i = 0; i < count; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return descs[a].K > descs[b].K; });
+    uint64_t b = 0;
+    for (int i : order) {
+        const uint64_t nb = linear_blocks(descs[i]);
         for (uint64_t j = 0; j < nb; ++j) tb[b++] = BlockEntry{(uint32_t)i, (uint32_t)j};
     }
     return BITNET_OK;
@@ -260,7 +270,7 @@ BITNET_API int bitnet_linear_grouped(const void *plan_host, const void *plan_dev
     if (st) return st;
     const PlanHeader *h = (const PlanHeader *)plan_host;
     if (h->total_blocks == 0) return BITNET_OK;
-    return hip_status(launch_gemv_grouped(plan_dev, h->total_blocks, (hipStream_t)stream));
+    return hip_status(launch_gemv_grouped(plan_dev, h->total_blocks, h->lds_bytes, (hipStream_t)stream));
 }
 
 BITNET_API int bitnet_quant_act_grouped(const void *plan_host, const void *plan_dev, void *stream) {

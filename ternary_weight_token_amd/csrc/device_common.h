@@ -38,6 +38,37 @@ __device__ __forceinline__ void transpose4x4(uint32_t q0, uint32_t q1, uint32_t 
     p3 = __builtin_amdgcn_perm(t3, t2, 0x07060302u);
 }
 
+// Eight unsigned / signed 4-bit products summed, plus c (v_dot8_u32_u4 /
+// v_dot8_i32_i4).
+__device__ __forceinline__ uint32_t udot8(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_udot8(a, b, c, false);
+}
+__device__ __forceinline__ int sdot8(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot8((int)a, (int)b, c, false);
+}
+
+// Nibble form of 16 int8 activations q_0..q_15 (natural dwords Q0..Q3, Qj byte b
+// = q_{4j+b}) for a product with the 16 two-bit codes of one packed dword.
+// Write q = 16 h + l with l = q & 15 (unsigned) and h = q >> 4 (signed 4-bit).
+// Codes split as u0 = w & 0x33333333 (nibble j = code of element 2j) and
+// u1 = (w >> 2) & 0x33333333 (nibble j = code of element 2j + 1); the matching
+// activation nibbles are
+//   le / he : nibble j = l_{2j} / h_{2j},   lo / ho : nibble j = l_{2j+1} / h_{2j+1}
+// so that  sum_k q_k c_k = 16 (sdot8(u0, he) + sdot8(u1, ho)) + udot8(u0, le) + udot8(u1, lo).
+struct QNib { uint32_t le, he, lo, ho; };
+
+__device__ __forceinline__ QNib nibble_form(uint32_t q0, uint32_t q1, uint32_t q2, uint32_t q3) {
+    uint32_t p0, p1, p2, p3;  // p_i byte b = q_{4b+i}
+    transpose4x4(q0, q1, q2, q3, p0, p1, p2, p3);
+    const uint32_t m = 0x0F0F0F0Fu;
+    QNib r;
+    r.le = (p0 & m) | ((p2 << 4) & ~m);   // byte b: l_{4b} | l_{4b+2} << 4
+    r.he = ((p0 >> 4) & m) | (p2 & ~m);   // byte b: h_{4b} | h_{4b+2} << 4
+    r.lo = (p1 & m) | ((p3 << 4) & ~m);
+    r.ho = ((p1 >> 4) & m) | (p3 & ~m);
+    return r;
+}
+
 // Sum over the 8 lanes of each aligned lane octet (DPP: quad swaps, then the
 // half-row mirror, which pairs lane i with lane 7 - i of the octet).
 __device__ __forceinline__ int octet_sum(int v) {

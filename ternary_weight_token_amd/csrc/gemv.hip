@@ -6,24 +6,57 @@
 //  * a wavefront owns RG row groups of 8 rows; the 8 lanes of an octet walk one
 //    row, lane l8 taking 16-byte chunks l8, l8 + 8, ... (one chunk = 64 weights),
 //    so one load instruction reads 8 rows x 128 contiguous bytes;
-//  * the 2-bit codes c = t + 1 are regrouped in registers with shift+mask
-//    (codes_i) and fed to v_dot4_i32_i8 unshifted; sum_k q * t is then
-//    sum_k q * c - sum_k q, the second term costing 16 dot4 per chunk and row of q
-//    instead of one subtraction per weight;
-//  * the 64 q bytes of a chunk are loaded once per chunk (L2/L1-resident) and
-//    byte-transposed to the order codes_i produces; they are reused by every row
-//    group of the wavefront;
+//  * the 2-bit codes c = t + 1 are used unshifted: sum_k q t = sum_k q c - sum_k q,
+//    the second term costing a few dot products per chunk and row of q instead of
+//    one subtraction per weight;
+//  * DOT8 = false: codes regrouped by shift + mask into bytes (codes_i) and fed to
+//    v_dot4_i32_i8 against byte-transposed q (7 + 4 VALU ops per 16 weights);
+//    DOT8 = true: codes kept as nibbles (2 masks, 1 shift) and fed to the 4-bit
+//    dot products against q split into its signed high and unsigned low nibbles
+//    (3 + 4 ops per 16 weights);
+//  * the 64 q bytes of a chunk are loaded once per chunk (L1/L2-resident),
+//    rearranged once and reused by every row group of the wavefront;
 //  * partial sums are reduced across the octet with DPP; when the workgroup has
 //    several wavefronts they split K and combine their partials through LDS;
 //  * epilogue: y = fp32(acc * c_m), c_m = (s_x[m] * s_w) / 127 in float64.
 #include "device_common.h"
 #include "internal.h"
 
+#ifndef BITNET_GROUPED_RG
+#define BITNET_GROUPED_RG 2
+#endif
+#ifndef BITNET_GROUPED_DOT8
+#define BITNET_GROUPED_DOT8 1
+#endif
+#ifndef BITNET_GEMV_NT
+#define BITNET_GEMV_NT 1
+#endif
+
 namespace bitnet {
 
 constexpr int kMaxKSplit = 8;
 
-template <int MT, int RG>
+// Weight loads go through the global address space explicitly: pointers read
+// from a plan descriptor are otherwise generic (FLAT) accesses, which also count
+// against the LDS wait counter and would serialise them with the LDS reads.
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const v4u gv4u;
+
+__device__ __forceinline__ uint4 gload16(const void *p) {
+    const v4u v = *(gv4u *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <bool NT>
+__device__ __forceinline__ uint4 load_weights(const uint8_t *p) {
+    if (NT) {
+        const v4u v = __builtin_nontemporal_load((gv4u *)p);
+        return make_uint4(v.x, v.y, v.z, v.w);
+    }
+    return gload16(p);
+}
+
+template <int MT, int RG, bool DOT8, bool NT>
 __device__ __forceinline__ void gemv_tile(const int8_t *__restrict__ q, const float *__restrict__ s_x,
                                           const uint8_t *__restrict__ packed,
                                           const float *__restrict__ s_w, int M, int N, int K,
@@ -53,32 +86,56 @@ __device__ __forceinline__ void gemv_tile(const int8_t *__restrict__ q, const fl
     for (int c = cb + l8; c < ce; c += 8) {
         uint4 wv[RG];
         #pragma unroll
-        for (int g = 0; g < RG; ++g) wv[g] = *reinterpret_cast<const uint4 *>(prow[g] + 16 * c);
+        for (int g = 0; g < RG; ++g) wv[g] = load_weights<NT>(prow[g] + 16 * c);
         #pragma unroll
         for (int m = 0; m < MT; ++m) {
             if (m < mcount) {
                 const uint4 *qp = reinterpret_cast<const uint4 *>(qrow + (size_t)m * K + 64 * c);
-                uint4 a[4] = {qp[0], qp[1], qp[2], qp[3]};
-                uint32_t P[4][4];
+                const uint4 a[4] = {qp[0], qp[1], qp[2], qp[3]};
                 int sq = 0;
                 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
-                    transpose4x4(a[d].x, a[d].y, a[d].z, a[d].w, P[d][0], P[d][1], P[d][2], P[d][3]);
                     sq = dot4(a[d].x, 0x01010101u, sq);
                     sq = dot4(a[d].y, 0x01010101u, sq);
                     sq = dot4(a[d].z, 0x01010101u, sq);
                     sq = dot4(a[d].w, 0x01010101u, sq);
                 }
-                #pragma unroll
-                for (int g = 0; g < RG; ++g) {
-                    const uint32_t wd[4] = {wv[g].x, wv[g].y, wv[g].z, wv[g].w};
-                    int s = acc[g][m] - sq;
+                if (DOT8) {
+                    QNib nb[4];
                     #pragma unroll
-                    for (int d = 0; d < 4; ++d) {
+                    for (int d = 0; d < 4; ++d) nb[d] = nibble_form(a[d].x, a[d].y, a[d].z, a[d].w);
+                    #pragma unroll
+                    for (int g = 0; g < RG; ++g) {
+                        const uint32_t wd[4] = {wv[g].x, wv[g].y, wv[g].z, wv[g].w};
+                        int hi = 0;
+                        uint32_t lo = 0;
                         #pragma unroll
-                        for (int i = 0; i < 4; ++i) s = dot4(codes_i(wd[d], i), P[d][i], s);
+                        for (int d = 0; d < 4; ++d) {
+                            const uint32_t u0 = wd[d] & 0x33333333u;
+                            const uint32_t u1 = (wd[d] >> 2) & 0x33333333u;
+                            hi = sdot8(u0, nb[d].he, hi);
+                            hi = sdot8(u1, nb[d].ho, hi);
+                            lo = udot8(u0, nb[d].le, lo);
+                            lo = udot8(u1, nb[d].lo, lo);
+                        }
+                        acc[g][m] += 16 * hi + (int)lo - sq;
                     }
-                    acc[g][m] = s;
+                } else {
+                    uint32_t P[4][4];
+                    #pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        transpose4x4(a[d].x, a[d].y, a[d].z, a[d].w, P[d][0], P[d][1], P[d][2], P[d][3]);
+                    #pragma unroll
+                    for (int g = 0; g < RG; ++g) {
+                        const uint32_t wd[4] = {wv[g].x, wv[g].y, wv[g].z, wv[g].w};
+                        int s = acc[g][m] - sq;
+                        #pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            #pragma unroll
+                            for (int i = 0; i < 4; ++i) s = dot4(codes_i(wd[d], i), P[d][i], s);
+                        }
+                        acc[g][m] = s;
+                    }
                 }
             }
         }
@@ -93,14 +150,15 @@ __device__ __forceinline__ void gemv_tile(const int8_t *__restrict__ q, const fl
     const float sw = *s_w;
     if (kslices == 1) {
         #pragma unroll
-        for (int g = 0; g < RG; ++g) {
-            const int r = row0 + 8 * g + rs;
-            if (r >= N) continue;
+        for (int m = 0; m < MT; ++m) {
+            if (m >= mcount) continue;
+            const double cm = rescale_factor(s_x[m0 + m], sw);
             #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                if (m < mcount && l8 == (m & 7)) {
+            for (int g = 0; g < RG; ++g) {
+                const int r = row0 + 8 * g + rs;
+                if (r < N && l8 == (m & 7)) {
                     const size_t o = (size_t)(m0 + m) * N + r;
-                    y[o] = rescale(acc[g][m], rescale_factor(s_x[m0 + m], sw));
+                    y[o] = rescale(acc[g][m], cm);
                     if (acc_out) acc_out[o] = acc[g][m];
                 }
             }
@@ -129,36 +187,256 @@ __device__ __forceinline__ void gemv_tile(const int8_t *__restrict__ q, const fl
     }
 }
 
-template <int MT, int RG>
+// ---------------------------------------------------------------------------
+// LDS-staged variant (used whenever MT x K fits the LDS budget).  A workgroup of
+// 4 wavefronts shares one M tile of q: the prologue loads it once, rearranges each
+// 16-byte piece (nibble form for the 4-bit dot products, byte transpose for
+// v_dot4), stores it in LDS (80 bytes per 64-weight chunk, which keeps the 8
+// chunks an instruction reads on distinct banks) and forms sum_k q per row of q.
+// The main loop then issues only weight loads to memory, prefetching the next
+// chunk's weights before working on the current one.
+constexpr int kLdsChunkDw = 20;           // dwords per staged chunk (64 bytes + pad)
+constexpr int kLdsBudget = 64 * 1024;     // bytes of staged q per workgroup
+
+template <bool DOT8>
+__device__ __forceinline__ uint4 prep16(uint4 a) {
+    uint4 r;
+    if (DOT8) {
+        const QNib n = nibble_form(a.x, a.y, a.z, a.w);
+        r = make_uint4(n.le, n.he, n.lo, n.ho);
+    } else {
+        transpose4x4(a.x, a.y, a.z, a.w, r.x, r.y, r.z, r.w);
+    }
+    return r;
+}
+
+// 16 weights (one packed dword) against their 16 prepared activations.
+template <bool DOT8>
+__device__ __forceinline__ void mac16(uint32_t w, uint4 pq, int &hi, uint32_t &lo) {
+    if (DOT8) {
+        const uint32_t u0 = w & 0x33333333u;
+        const uint32_t u1 = (w >> 2) & 0x33333333u;
+        hi = sdot8(u0, pq.y, hi);
+        hi = sdot8(u1, pq.w, hi);
+        lo = udot8(u0, pq.x, lo);
+        lo = udot8(u1, pq.z, lo);
+    } else {
+        hi = dot4(codes_i(w, 0), pq.x, hi);
+        hi = dot4(codes_i(w, 1), pq.y, hi);
+        hi = dot4(codes_i(w, 2), pq.z, hi);
+        hi = dot4(codes_i(w, 3), pq.w, hi);
+    }
+}
+
+template <int MT, int RG, bool DOT8, bool NT>
+__device__ __forceinline__ void gemv_lds_tile(const int8_t *__restrict__ q, const float *__restrict__ s_x,
+                                              const uint8_t *__restrict__ packed,
+                                              const float *__restrict__ s_w, int M, int N, int K,
+                                              float *__restrict__ y, int32_t *__restrict__ acc_out,
+                                              int row_base, int m0, int kslices, uint32_t *qs,
+                                              int *sq, int *red) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l8 = lane & 7, rs = lane >> 3;
+    const int C = K >> 6;
+    const int KB = K >> 2;
+    const int mcount = min(MT, M - m0);
+
+    // ---- wave -> (row set, K slice); the first weight loads go out before the
+    // prologue so that their latency overlaps the staging of q
+    const int rowset = wave / kslices, slice = wave - rowset * kslices;
+    const int row0 = row_base + rowset * 8 * RG;
+    const int cb = (int)(((int64_t)C * slice) / kslices);
+    const int ce = (int)(((int64_t)C * (slice + 1)) / kslices);
+
+    int hi[RG][MT];
+    uint32_t lo[RG][MT];
+    const uint8_t *prow[RG];
+    #pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        const int r = row0 + 8 * g + rs;
+        prow[g] = packed + (size_t)(r < N ? r : 0) * KB;   // rows past N read row 0, discarded
+        #pragma unroll
+        for (int m = 0; m < MT; ++m) { hi[g][m] = 0; lo[g][m] = 0u; }
+    }
+
+    // Chunk t of this lane is c = cb + l8 + 8 t, t < T (T uniform across the
+    // wavefront; lanes past the slice end load a clamped in-range chunk and use
+    // all-zero codes, which add nothing).  Two register buffers alternate so that
+    // the loads of chunk t + 1 are in flight while chunk t is being consumed.
+    // (ce > cb always: every slice holds at least one chunk.)
+    const int T = (ce - cb + 7) >> 3;
+    const int clast = ce - 1;
+    uint4 bufA[RG], bufB[RG];
+    auto issue = [&](uint4 (&b)[RG], int t) {
+        const int cc = min(cb + l8 + 8 * t, clast);
+        #pragma unroll
+        for (int g = 0; g < RG; ++g) b[g] = load_weights<NT>(prow[g] + 16 * cc);
+    };
+    auto consume = [&](const uint4 (&b)[RG], int t) {
+        const int craw = cb + l8 + 8 * t;
+        const bool valid = craw < ce;
+        const int cc = min(craw, clast);
+        #pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            if (m < mcount) {
+                const uint32_t *qc = qs + (m * C + cc) * kLdsChunkDw;
+                #pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint4 pq = *reinterpret_cast<const uint4 *>(qc + 4 * d);
+                    #pragma unroll
+                    for (int g = 0; g < RG; ++g) {
+                        uint32_t wd = d == 0 ? b[g].x : d == 1 ? b[g].y : d == 2 ? b[g].z : b[g].w;
+                        wd = valid ? wd : 0u;
+                        mac16<DOT8>(wd, pq, hi[g][m], lo[g][m]);
+                    }
+                }
+            }
+        }
+    };
+    if (T > 0) issue(bufA, 0);
+
+    // ---- prologue: stage the M tile of q, rearranged, and its row sums
+    if (tid < MT) sq[tid] = 0;
+    __syncthreads();
+    {
+        int part[MT];
+        #pragma unroll
+        for (int m = 0; m < MT; ++m) part[m] = 0;
+        const int pieces = C * 4;  // 16-byte pieces per row of q
+        for (int idx = tid; idx < mcount * pieces; idx += blockDim.x) {
+            const int m = idx / pieces, r = idx - m * pieces;
+            const uint4 a = gload16(q + (size_t)(m0 + m) * K + 16 * r);
+            const int c = r >> 2, d = r & 3;
+            *reinterpret_cast<uint4 *>(qs + (m * C + c) * kLdsChunkDw + 4 * d) = prep16<DOT8>(a);
+            int s = dot4(a.x, 0x01010101u, 0);
+            s = dot4(a.y, 0x01010101u, s);
+            s = dot4(a.z, 0x01010101u, s);
+            s = dot4(a.w, 0x01010101u, s);
+            #pragma unroll
+            for (int mm = 0; mm < MT; ++mm) part[mm] += (mm == m) ? s : 0;
+        }
+        #pragma unroll
+        for (int m = 0; m < MT; ++m)
+            if (m < mcount && part[m] != 0) atomicAdd(&sq[m], part[m]);
+    }
+    __syncthreads();
+
+    // The chunk count is padded to even (a padded chunk is a clamped in-range load
+    // with zero codes) so the loop body has no branches: the compiler can then wait
+    // for exactly the older buffer's loads.
+    if (T > 0) {
+        const int T2 = (T + 1) & ~1;
+        for (int t = 0; t < T2 - 2; t += 2) {
+            issue(bufB, t + 1);
+            consume(bufA, t);
+            issue(bufA, t + 2);
+            consume(bufB, t + 1);
+        }
+        issue(bufB, T2 - 1);
+        consume(bufA, T2 - 2);
+        consume(bufB, T2 - 1);
+    }
+
+    int acc[RG][MT];
+    #pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        #pragma unroll
+        for (int m = 0; m < MT; ++m)
+            acc[g][m] = octet_sum(DOT8 ? 16 * hi[g][m] + (int)lo[g][m] : hi[g][m]);
+    }
+
+    const float sw = *s_w;
+    if (kslices == 1) {
+        #pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            if (m >= mcount) continue;
+            const double cm = rescale_factor(s_x[m0 + m], sw);
+            const int sqm = sq[m];
+            #pragma unroll
+            for (int g = 0; g < RG; ++g) {
+                const int r = row0 + 8 * g + rs;
+                if (r < N && l8 == (m & 7)) {
+                    const size_t o = (size_t)(m0 + m) * N + r;
+                    const int a = acc[g][m] - sqm;
+                    y[o] = rescale(a, cm);
+                    if (acc_out) acc_out[o] = a;
+                }
+            }
+        }
+        return;
+    }
+    constexpr int R = 8 * RG;
+    if (l8 == 0) {
+        #pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            #pragma unroll
+            for (int m = 0; m < MT; ++m) red[(wave * R + 8 * g + rs) * MT + m] = acc[g][m];
+        }
+    }
+    __syncthreads();
+    const int rowsets = 4 / kslices;
+    for (int idx = tid; idx < rowsets * R * MT; idx += blockDim.x) {
+        const int rsi = idx / (R * MT), rem = idx - rsi * R * MT;
+        const int rr = rem / MT, m = rem - rr * MT;
+        const int r = row_base + rsi * R + rr;
+        if (r >= N || m >= mcount) continue;
+        int s = -sq[m];
+        for (int w = 0; w < kslices; ++w) s += red[((rsi * kslices + w) * R + rr) * MT + m];
+        const size_t o = (size_t)(m0 + m) * N + r;
+        y[o] = rescale(s, rescale_factor(s_x[m0 + m], sw));
+        if (acc_out) acc_out[o] = s;
+    }
+}
+
+template <int MT, int RG, bool DOT8>
+__global__ __launch_bounds__(256) void gemv_lds_kernel(
+    const int8_t *__restrict__ q, const float *__restrict__ s_x, const uint8_t *__restrict__ packed,
+    const float *__restrict__ s_w, int M, int N, int K, float *__restrict__ y,
+    int32_t *__restrict__ acc_out, int kslices) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+    __shared__ int sq[MT];
+    __shared__ int red[4 * 8 * RG * MT];
+    const int rows_per_block = (4 / kslices) * 8 * RG;
+    gemv_lds_tile<MT, RG, DOT8, BITNET_GEMV_NT != 0>(q, s_x, packed, s_w, M, N, K, y, acc_out,
+                                                     blockIdx.x * rows_per_block, blockIdx.y * MT, kslices,
+                                                     dyn, sq, red);
+}
+
+template <int MT, int RG, bool DOT8>
 __global__ __launch_bounds__(64 * kMaxKSplit) void gemv_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s_x, const uint8_t *__restrict__ packed,
     const float *__restrict__ s_w, int M, int N, int K, float *__restrict__ y,
     int32_t *__restrict__ acc_out, int kslices) {
     __shared__ int lds[kMaxKSplit * 8 * RG * MT];
-    gemv_tile<MT, RG>(q, s_x, packed, s_w, M, N, K, y, acc_out, blockIdx.x * 8 * RG, blockIdx.y * MT,
-                      kslices, lds);
+    gemv_tile<MT, RG, DOT8, BITNET_GEMV_NT != 0>(q, s_x, packed, s_w, M, N, K, y, acc_out,
+                                                 blockIdx.x * 8 * RG, blockIdx.y * MT, kslices, lds);
 }
 
-// Grouped decode: one wavefront per block, block -> (descriptor, row set, M tile)
-// through the plan's block table.
-constexpr int kGroupedRG = 4;
+// Grouped decode: 4 wavefronts per block, block -> (descriptor, row block, M tile)
+// through the plan's block table; staged-q LDS size comes from the plan header.
+constexpr int kGroupedRG = BITNET_GROUPED_RG;
 constexpr int kGroupedMT = 1;
 
-__global__ __launch_bounds__(64) void gemv_grouped_kernel(const uint8_t *__restrict__ plan) {
+__global__ __launch_bounds__(256) void gemv_grouped_kernel(const uint8_t *__restrict__ plan) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+    __shared__ int sq[kGroupedMT];
+    __shared__ int red[4 * 8 * kGroupedRG * kGroupedMT];
     const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
     const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[blockIdx.x];
     const LinearDescDev d = reinterpret_cast<const LinearDescDev *>(plan + h->desc_offset)[e.desc];
-    const int rowsets = (d.N + 8 * kGroupedRG - 1) / (8 * kGroupedRG);
-    const int rs = (int)(e.local % rowsets), mt = (int)(e.local / rowsets);
-    gemv_tile<kGroupedMT, kGroupedRG>(d.q, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, d.y, d.acc,
-                                      rs * 8 * kGroupedRG, mt * kGroupedMT, 1, nullptr);
+    const int rows = 4 * 8 * kGroupedRG;
+    const int rowblocks = (d.N + rows - 1) / rows;
+    const int rb = (int)(e.local % rowblocks), mt = (int)(e.local / rowblocks);
+    gemv_lds_tile<kGroupedMT, kGroupedRG, BITNET_GROUPED_DOT8 != 0, BITNET_GEMV_NT != 0>(
+        d.q, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, d.y, d.acc, rb * rows, mt * kGroupedMT, 1, dyn, sq, red);
 }
 
-uint32_t gemv_grouped_rows_per_block() { return 8 * kGroupedRG; }
-uint32_t gemv_grouped_threads() { return 64; }
-uint32_t gemv_grouped_mtile() { return kGroupedMT; }
+uint32_t gemv_grouped_rows_per_block() { return 4 * 8 * kGroupedRG; }
+uint32_t gemv_grouped_threads() { return 256; }
+uint32_t gemv_grouped_lds_bytes(int64_t K) { return (uint32_t)(kGroupedMT * (K / 64) * kLdsChunkDw * 4); }
 
-template <int MT, int RG>
+template <int MT, int RG, bool DOT8>
 static hipError_t launch_t(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                            int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
     const int rows = 8 * RG;
@@ -169,21 +447,49 @@ static hipError_t launch_t(const int8_t *q, const float *s_x, const uint8_t *pac
     // at least 4 chunk iterations per lane.
     int ks = 1;
     while (ks < kMaxKSplit && (int64_t)gx * gy * ks < 2048 && C / (16 * ks) >= 4) ks *= 2;
-    gemv_kernel<MT, RG><<<dim3(gx, gy), dim3(64 * ks), 0, st>>>(q, s_x, packed, s_w, (int)M, (int)N,
-                                                                (int)K, y, acc, ks);
+    gemv_kernel<MT, RG, DOT8><<<dim3(gx, gy), dim3(64 * ks), 0, st>>>(q, s_x, packed, s_w, (int)M, (int)N,
+                                                                      (int)K, y, acc, ks);
+    return hipGetLastError();
+}
+
+template <int MT, int RG, bool DOT8>
+static hipError_t launch_lds(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
+                             int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
+    const int C = (int)(K / 64);
+    const unsigned gy = (unsigned)((M + MT - 1) / MT);
+    // more K slices per row set until the launch has >= 2 workgroups per CU,
+    // keeping at least 2 chunk iterations per lane
+    int ks = 1;
+    auto blocks = [&](int k) { return (int64_t)((N + (4 / k) * 8 * RG - 1) / ((4 / k) * 8 * RG)) * gy; };
+    while (ks < 4 && blocks(ks) < 512 && C / (8 * ks * 2) >= 2) ks *= 2;
+    const unsigned gx = (unsigned)((N + (4 / ks) * 8 * RG - 1) / ((4 / ks) * 8 * RG));
+    const size_t lds = (size_t)MT * C * kLdsChunkDw * 4;
+    gemv_lds_kernel<MT, RG, DOT8><<<dim3(gx, gy), dim3(256), lds, st>>>(q, s_x, packed, s_w, (int)M, (int)N,
+                                                                        (int)K, y, acc, ks);
     return hipGetLastError();
 }
 
 hipError_t launch_gemv(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                        int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
-    if (M == 1) return launch_t<1, 4>(q, s_x, packed, s_w, M, N, K, y, acc, st);
-    if (M == 2) return launch_t<2, 4>(q, s_x, packed, s_w, M, N, K, y, acc, st);
-    if (M <= 4) return launch_t<4, 2>(q, s_x, packed, s_w, M, N, K, y, acc, st);
-    return launch_t<8, 2>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    const int64_t C = K / 64;
+    const bool d8 = BITNET_GROUPED_DOT8 != 0;
+    if (M == 1 && C * kLdsChunkDw * 4 <= kLdsBudget)
+        return launch_lds<1, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    if (M == 2 && 2 * C * kLdsChunkDw * 4 <= kLdsBudget)
+        return launch_lds<2, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    if (M <= 4 && 4 * C * kLdsChunkDw * 4 <= kLdsBudget)
+        return launch_lds<4, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    if (8 * C * kLdsChunkDw * 4 <= kLdsBudget)
+        return launch_lds<8, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    // q tile too large for LDS: rearrange q in registers per chunk
+    if (M == 1) return launch_t<1, 4, true>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    if (M == 2) return launch_t<2, 4, true>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    if (M <= 4) return launch_t<4, 2, true>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    return launch_t<8, 2, true>(q, s_x, packed, s_w, M, N, K, y, acc, st);
 }
 
-hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, hipStream_t st) {
-    gemv_grouped_kernel<<<dim3(blocks), dim3(64), 0, st>>>(reinterpret_cast<const uint8_t *>(plan_dev));
+hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st) {
+    gemv_grouped_kernel<<<dim3(blocks), dim3(256), lds_bytes, st>>>(reinterpret_cast<const uint8_t *>(plan_dev));
     return hipGetLastError();
 }
 

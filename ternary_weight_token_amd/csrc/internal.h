@@ -12,7 +12,7 @@ constexpr uint32_t kPlanLinear = 1, kPlanQuant = 2;
 
 struct PlanHeader {            // 64 bytes
     uint32_t magic, kind, count, total_blocks;
-    uint32_t block_threads, rows_per_block, reserved0, reserved1;
+    uint32_t block_threads, rows_per_block, lds_bytes, reserved1;
     uint64_t desc_offset, table_offset, total_bytes, reserved2;
 };
 
@@ -37,7 +37,8 @@ hipError_t launch_pack(const float *w, int64_t N, int64_t K, float eps, uint8_t 
                        float *s_w, double *rowsum, hipStream_t st);
 hipError_t launch_gemv(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                        int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st);
-hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, hipStream_t st);
+hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st);
+uint32_t gemv_grouped_lds_bytes(int64_t K);
 uint32_t gemv_grouped_rows_per_block();
 uint32_t gemv_grouped_threads();
 hipError_t launch_gemm(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,

