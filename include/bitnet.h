@@ -85,7 +85,7 @@ BITNET_API int bitnet_version(void);
  * Pages: chenxutan.com sec. 2.2 (absmean_quantize) and sec. 3.3 (pack_ternary);
  * 0539edu.com sec. 2.1 (scale = mean|w|, RoundClip to [-1, 1]).
  *
- *   w          (device) fp32 [N][K], 16-byte aligned
+ *   w          (device) fp32 [N][K], 4-byte aligned
  *   eps        added to s_w before dividing (the configurations use 1e-5)
  *   packed     (device) uint8 [N][K/4], output
  *   s_w        (device) fp32 [1], output: mean |W| rounded once to fp32
@@ -133,7 +133,7 @@ BITNET_API int bitnet_quant_act(const uint16_t *x, int64_t M, int64_t K,
  * acc is exact.  y is acc * s_x[m] * s_w / 127 evaluated as
  * fp32(acc * c_m) with c_m = (s_x[m] * s_w) / 127 in float64, i.e. within one
  * unit in the last place of the correctly rounded value.  M <= 16 runs the
- * decode GEMV (v_dot4); larger M runs the int8 MFMA GEMM.
+ * decode GEMV (4-bit / 8-bit dot products); larger M runs the int8 MFMA GEMM.
  * ------------------------------------------------------------------------- */
 BITNET_API int bitnet_linear(const int8_t *q, const float *s_x, const uint8_t *packed,
                              const float *s_w, int64_t M, int64_t N, int64_t K,
@@ -142,8 +142,10 @@ BITNET_API int bitnet_linear(const int8_t *q, const float *s_x, const uint8_t *p
 /* Same as bitnet_linear with the kernel chosen by the caller instead of by M
  * (for measuring the GEMV / GEMM crossover): kernel 0 = automatic, 1 = decode
  * GEMV (any M; M > 8 re-reads the weights once per 8 rows of q), 2 = MFMA GEMM,
- * 3 = general kernel.  Kernels 1 and 2 need K % 64 == 0 and 16-byte aligned q /
- * packed (else BITNET_ERR_ALIGN); other values give BITNET_ERR_ARG. */
+ * 3 = general kernel, 16 + i = MFMA GEMM with tile configuration i (0: 256 x 224,
+ * 1: 256 x 80, 2: 256 x 128, 3: 128 x 128, 4: 64 x 128 rows x columns of y).
+ * Kernels other than 0 and 3 need K % 64 == 0 and 16-byte aligned q / packed
+ * (else BITNET_ERR_ALIGN); other values give BITNET_ERR_ARG. */
 BITNET_API int bitnet_linear_select(const int8_t *q, const float *s_x, const uint8_t *packed,
                                     const float *s_w, int64_t M, int64_t N, int64_t K,
                                     float *y, int32_t *acc, int kernel, void *stream);

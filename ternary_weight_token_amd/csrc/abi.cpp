@@ -118,13 +118,15 @@ BITNET_API int bitnet_linear_select(const int8_t *q, const float *s_x, const uin
                                     const float *s_w, int64_t M, int64_t N, int64_t K, float *y,
                                     int32_t *acc, int kernel, void *stream) {
     if (kernel == 0) return bitnet_linear(q, s_x, packed, s_w, M, N, K, y, acc, stream);
-    if (kernel < 0 || kernel > 3) return fail(BITNET_ERR_ARG, "kernel must be 0..3");
+    const bool forced_tile = kernel >= 16 && kernel < 16 + gemm_config_count();
+    if ((kernel < 0 || kernel > 3) && !forced_tile) return fail(BITNET_ERR_ARG, "unknown kernel id");
     int st = check_linear(q, s_x, packed, s_w, M, N, K, y, acc);
     if (st || M == 0 || N == 0) return st;
     hipStream_t s = (hipStream_t)stream;
     if (kernel == 3) return hip_status(launch_linear_generic(q, s_x, packed, s_w, M, N, K, y, acc, s));
     if (!linear_fast(q, packed, K)) return fail(BITNET_ERR_ALIGN, "kernel needs K % 64 == 0 and 16-byte aligned q/packed");
     if (kernel == 1) return hip_status(launch_gemv(q, s_x, packed, s_w, M, N, K, y, acc, s));
+    if (forced_tile) return hip_status(launch_gemm_cfg(kernel - 16, q, s_x, packed, s_w, M, N, K, y, acc, s));
     return hip_status(launch_gemm(q, s_x, packed, s_w, M, N, K, y, acc, s));
 }
 

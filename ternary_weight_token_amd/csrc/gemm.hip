@@ -1,125 +1,232 @@
 // Prefill GEMM (M > 16): the same contraction and rescale as the GEMV, as a dense
-// int8 x ternary -> int32 product on the matrix cores (v_mfma_i32_32x32x32_i8).
+// int8 x ternary -> int32 product on the matrix cores (v_mfma_i32_16x16x64_i8).
+// Pages: chenxutan.com sec. 2.3 (rescale) and sec. 3.1 (BitLinear.forward).
 //
-// Tiles: 128 x 128 outputs per 256-thread workgroup, K in steps of 64; each of
-// the 4 wavefronts owns a 64 x 64 quadrant = 2 x 2 MFMA 32x32 tiles.
-//  * A (q) tile 128 x 64 int8 is staged in LDS with each 16-byte chunk
-//    byte-transposed into the order the weight expansion produces;
-//  * B tile stays packed in LDS (128 rows x 16 bytes); each wavefront expands
-//    the 2-bit codes of its fragments to int8 ternary values in registers
-//    (shift + mask, then v_perm_b32 as the table {-1, 0, +1, +2}) right before the
-//    MFMA, so LDS holds and moves 4x fewer bytes for B;
+// Workgroup = WM x WN wavefronts; a wavefront owns TM x TN MFMA tiles of 16 x 16,
+// so the block tile is BM = 16 WM TM rows by BN = 16 WN TN columns, chosen per
+// shape so that the tile count matches the 256 compute units (e.g. 256 x 224 for
+// N = 6912, 256 x 80 for N = 2560).  K advances 64 per step:
+//  * the A (q) tile BM x 64 int8 is staged in LDS with each 16-byte piece
+//    byte-transposed into the order the code expansion produces;
+//  * the B tile is loaded packed (16 bytes per row and step) and expanded once per
+//    workgroup to int8 codes c = t + 1 in LDS (shift + mask, 7 VALU ops per 16
+//    weights); sum_k q t = sum_k q c - sum_k q, where sum_k q is accumulated per
+//    row while staging A;
+//  * LDS is double-buffered: the global loads of step s + 1 are in flight while
+//    the MFMAs of step s run; one barrier per step;
 //  * both operands assign the same k to the same (lane, byte) position, which is
 //    all the MFMA needs: the sum over k is order-free in integers;
 //  * epilogue: y = fp32(acc * c_m), c_m = (s_x[m] * s_w) / 127 in float64.
-// Pages: chenxutan.com sec. 2.3 and sec. 3.1 (BitLinear.forward).
 #include "device_common.h"
 #include "internal.h"
 
 namespace bitnet {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned int v4u_g __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const v4u_g gv4u_g;
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int A_STRIDE = 20;  // dwords per A row in LDS (64 bytes + 16 pad)
-constexpr int B_STRIDE = 5;   // dwords per B row in LDS (16 bytes + 4 pad)
+#ifndef BITNET_GEMM_GROUP_M
+#define BITNET_GEMM_GROUP_M 8
+#endif
+// tile configurations 0 (256 x 224) and 1 (256 x 80): waves M, waves N, MFMA
+// tiles per wave in M and N, 64-k substeps per barrier step
+#ifndef BITNET_GEMM_CFG0
+#define BITNET_GEMM_CFG0 4, 2, 4, 7, 2
+#define BITNET_GEMM_CFG0_K64 4, 2, 4, 7, 1
+#endif
+#ifndef BITNET_GEMM_CFG1
+#define BITNET_GEMM_CFG1 8, 1, 2, 5, 2
+#define BITNET_GEMM_CFG1_K64 8, 1, 2, 5, 1
+#endif
 
-__global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ q,
-                                                   const float *__restrict__ s_x,
-                                                   const uint8_t *__restrict__ packed,
-                                                   const float *__restrict__ s_w, int M, int N, int K,
-                                                   float *__restrict__ y, int32_t *__restrict__ acc_out,
-                                                   int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint32_t As[BM * A_STRIDE];
-    __shared__ uint32_t Bs[BN * B_STRIDE];
+constexpr int kStrideB = 80;   // bytes per LDS row (64 data + 16 pad: conflict-free b128 reads)
+
+__device__ __forceinline__ uint4 gld16(const void *p) {
+    const v4u_g v = *(gv4u_g *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int WM, int WN, int TM, int TN, int KS, bool BPACK>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__restrict__ q,
+                                                           const float *__restrict__ s_x,
+                                                           const uint8_t *__restrict__ packed,
+                                                           const float *__restrict__ s_w, int M, int N,
+                                                           int K, float *__restrict__ y,
+                                                           int32_t *__restrict__ acc_out, int tiles_m,
+                                                           int tiles_n) {
+    constexpr int NT = 64 * WM * WN;          // threads
+    constexpr int BM = 16 * WM * TM, BN = 16 * WN * TN;
+    constexpr int BK = 64 * KS;               // k per barrier step
+    constexpr int RS = BK + 16;               // LDS row stride (bytes): +16 keeps b128 reads conflict-free
+    constexpr int CPR = BK / 16;              // 16-byte pieces per A row and step
+    constexpr int A_PIECES = BM * CPR;
+    constexpr int A_PER_T = (A_PIECES + NT - 1) / NT;
+    constexpr int B_PIECES = BN * KS;         // 16-byte packed pieces per step
+    constexpr int B_PER_T = (B_PIECES + NT - 1) / NT;
+    // B in LDS: expanded int8 codes (row stride RS) or packed 2-bit codes (row
+    // stride 16 KS + 4 bytes: 16 lanes reading one dword each hit distinct banks)
+    constexpr int RSB = BPACK ? 16 * KS + 4 : RS;
+    __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * RS];
+    __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * RSB];
+    __shared__ int rowsum[BM];
+    __shared__ double rowscale[BM];
 
     // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; give each
-    // XCD a contiguous range of tiles, walked column-major in groups of 8 M-tiles
-    // so that neighbouring workgroups share A rows and B columns in that XCD's L2.
+    // XCD a contiguous range of tiles, column-major in groups of GM M tiles, so that
+    // workgroups sharing A rows and B columns share that XCD's L2.
     const int nt = tiles_m * tiles_n;
     const int bid = blockIdx.x;
     const int q8 = nt / 8, r8 = nt % 8, x = bid % 8;
-    const int t = x * q8 + min(x, r8) + bid / 8;  // XCD x owns tiles [x*q8 + min(x,r8), +q8 + (x<r8))
-    const int GM = 8;
+    const int t = x * q8 + min(x, r8) + bid / 8;
+    const int GM = BITNET_GEMM_GROUP_M;
     const int group = t / (GM * tiles_n);
     const int first_m = group * GM;
     const int gsize = min(GM, tiles_m - first_m);
     const int tm = first_m + (t % (GM * tiles_n)) % gsize;
     const int tn = (t % (GM * tiles_n)) / gsize;
+    const int m_base = tm * BM, n_base = tn * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave % WM, wn = wave / WM;
     const int KB = K >> 2;
+    const int steps = K / BK;                 // K % BK == 0 (checked by the launcher)
 
-    v16i acc[2][2];
+    // staging: A piece p = tid + NT * i -> row p / CPR, piece p % CPR (CPR
+    // consecutive threads cover a row's BK bytes); B piece p -> row p / KS, part p % KS.
+    int a_sum[A_PER_T];
     #pragma unroll
-    for (int i = 0; i < 2; ++i)
-        #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = v16i{};
+    for (int i = 0; i < A_PER_T; ++i) a_sum[i] = 0;
 
-    for (int k0 = 0; k0 < K; k0 += BK) {
-        // stage A: 128 rows x 4 chunks of 16 bytes, two chunks per thread
+    uint4 ra[A_PER_T], rb[B_PER_T];
+    auto load_step = [&](int s) {
+        const int k0 = s * BK;
         #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int c = tid + 256 * r;
-            const int row = c >> 2, ch = c & 3;
-            const int gm = tm * BM + row;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (gm < M) v = *reinterpret_cast<const uint4 *>(q + (size_t)gm * K + k0 + 16 * ch);
-            uint4 p;
-            transpose4x4(v.x, v.y, v.z, v.w, p.x, p.y, p.z, p.w);
-            *reinterpret_cast<uint4 *>(&As[row * A_STRIDE + 4 * ch]) = p;
+        for (int i = 0; i < A_PER_T; ++i) {
+            const int p = tid + NT * i;
+            const int row = p / CPR, ch = p % CPR;
+            const int gm = m_base + row;
+            ra[i] = (p < A_PIECES && gm < M) ? gld16(q + (size_t)gm * K + k0 + 16 * ch) : make_uint4(0u, 0u, 0u, 0u);
         }
-        // stage B: 128 packed rows x 16 bytes
-        if (tid < BN) {
-            const int gn = tn * BN + tid;
-            uint4 v = make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
-            if (gn < N) v = *reinterpret_cast<const uint4 *>(packed + (size_t)gn * KB + (k0 >> 2));
-            Bs[tid * B_STRIDE + 0] = v.x;
-            Bs[tid * B_STRIDE + 1] = v.y;
-            Bs[tid * B_STRIDE + 2] = v.z;
-            Bs[tid * B_STRIDE + 3] = v.w;
-        }
-        __syncthreads();
-        const int g = lane >> 5, l32 = lane & 31;
         #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            v4i b[2];
+        for (int i = 0; i < B_PER_T; ++i) {
+            const int p = tid + NT * i;
+            const int r = p / KS, part = p % KS;
+            const int gn = n_base + r;
+            rb[i] = (p < B_PIECES && gn < N) ? gld16(packed + (size_t)gn * KB + (k0 >> 2) + 16 * part)
+                                             : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto store_step = [&](int buf) {
+        #pragma unroll
+        for (int i = 0; i < A_PER_T; ++i) {
+            const int p = tid + NT * i;
+            if (p < A_PIECES) {
+                const int row = p / CPR, ch = p % CPR;
+                const uint4 v = ra[i];
+                uint4 o;
+                transpose4x4(v.x, v.y, v.z, v.w, o.x, o.y, o.z, o.w);
+                *reinterpret_cast<uint4 *>(&As[buf][row * RS + 16 * ch]) = o;
+                int sm = dot4(v.x, 0x01010101u, a_sum[i]);
+                sm = dot4(v.y, 0x01010101u, sm);
+                sm = dot4(v.z, 0x01010101u, sm);
+                a_sum[i] = dot4(v.w, 0x01010101u, sm);
+            }
+        }
+        #pragma unroll
+        for (int i = 0; i < B_PER_T; ++i) {
+            const int p = tid + NT * i;
+            if (p < B_PIECES) {
+                const int r = p / KS, part = p % KS;
+                const uint32_t w[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
+                if (BPACK) {
+                    uint32_t *dst = reinterpret_cast<uint32_t *>(&Bs[buf][r * RSB + 16 * part]);
+                    dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2]; dst[3] = w[3];
+                } else {
+                    #pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const uint4 o = make_uint4(codes_i(w[d], 0), codes_i(w[d], 1), codes_i(w[d], 2),
+                                                   codes_i(w[d], 3));
+                        *reinterpret_cast<uint4 *>(&Bs[buf][r * RS + 64 * part + 16 * d]) = o;
+                    }
+                }
+            }
+        }
+    };
+
+    v4i acc[TM][TN];
+    #pragma unroll
+    for (int i = 0; i < TM; ++i)
+        #pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+    const int l16 = lane & 15, g = lane >> 4;
+    load_step(0);
+    store_step(0);
+    __syncthreads();
+    for (int s = 0; s < steps; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < steps) load_step(s + 1);
+        #pragma unroll
+        for (int u = 0; u < KS; ++u) {
+            v4i a[TM], b[TN];
             #pragma unroll
-            for (int jn = 0; jn < 2; ++jn) {
-                const uint32_t w = Bs[(wn * 64 + jn * 32 + l32) * B_STRIDE + 2 * s + g];
-                b[jn] = v4i{(int)codes_to_ternary(codes_i(w, 0)), (int)codes_to_ternary(codes_i(w, 1)),
-                            (int)codes_to_ternary(codes_i(w, 2)), (int)codes_to_ternary(codes_i(w, 3))};
+            for (int i = 0; i < TM; ++i)
+                a[i] = *reinterpret_cast<const v4i *>(&As[buf][(wm * TM * 16 + i * 16 + l16) * RS + 64 * u + 16 * g]);
+            #pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                if (BPACK) {
+                    const uint32_t w = *reinterpret_cast<const uint32_t *>(
+                        &Bs[buf][(wn * TN * 16 + j * 16 + l16) * RSB + 16 * u + 4 * g]);
+                    b[j] = v4i{(int)codes_i(w, 0), (int)codes_i(w, 1), (int)codes_i(w, 2), (int)codes_i(w, 3)};
+                } else {
+                    b[j] = *reinterpret_cast<const v4i *>(&Bs[buf][(wn * TN * 16 + j * 16 + l16) * RS + 64 * u + 16 * g]);
+                }
             }
             #pragma unroll
-            for (int im = 0; im < 2; ++im) {
-                const v4i a = *reinterpret_cast<const v4i *>(
-                    &As[(wm * 64 + im * 32 + l32) * A_STRIDE + 8 * s + 4 * g]);
+            for (int i = 0; i < TM; ++i)
                 #pragma unroll
-                for (int jn = 0; jn < 2; ++jn)
-                    acc[im][jn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[jn], acc[im][jn], 0, 0, 0);
-            }
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
         }
+        if (s + 1 < steps) store_step(buf ^ 1);
         __syncthreads();
     }
 
-    // 32x32 accumulator layout: lane -> column l32; register r -> row
-    // 8 * (r / 4) + 4 * (lane / 32) + r % 4.
+    // row sums of q (CPR threads per row) and per-row rescale factors
     const float sw = *s_w;
-    const int l32 = lane & 31, hi = lane >> 5;
     #pragma unroll
-    for (int im = 0; im < 2; ++im) {
+    for (int i = 0; i < A_PER_T; ++i) {
+        int v = a_sum[i];
         #pragma unroll
-        for (int jn = 0; jn < 2; ++jn) {
-            const int col = tn * BN + wn * 64 + jn * 32 + l32;
+        for (int o = 1; o < CPR; o <<= 1) v += __shfl_xor(v, o, 64);
+        const int p = tid + NT * i;
+        if (p < A_PIECES && (p % CPR) == 0) {
+            const int row = p / CPR;
+            rowsum[row] = v;
+            const int gm = m_base + row;
+            rowscale[row] = gm < M ? rescale_factor(s_x[gm], sw) : 0.0;
+        }
+    }
+    __syncthreads();
+
+    // 16x16 accumulator layout: lane -> column l16; register r -> row 4 * (lane / 16) + r.
+    #pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int lr = wm * TM * 16 + i * 16 + 4 * g + r;
+            const int row = m_base + lr;
+            if (row >= M) continue;
+            const int sq = rowsum[lr];
+            const double cm = rowscale[lr];
             #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = tm * BM + wm * 64 + im * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                if (row < M && col < N) {
+            for (int j = 0; j < TN; ++j) {
+                const int col = n_base + wn * TN * 16 + j * 16 + l16;
+                if (col < N) {
                     const size_t o = (size_t)row * N + col;
-                    const int v = acc[im][jn][r];
-                    y[o] = rescale(v, rescale_factor(s_x[row], sw));
+                    const int v = acc[i][j][r] - sq;
+                    y[o] = rescale(v, cm);
                     if (acc_out) acc_out[o] = v;
                 }
             }
@@ -127,12 +234,51 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ q,
     }
 }
 
-hipError_t launch_gemm(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
-                       int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
+struct GemmCfg { int wm, wn, tm, tn; };
+
+template <int WM, int WN, int TM, int TN, int KS, bool BPACK = false>
+static hipError_t launch_cfg(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
+                             int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
+    constexpr int BM = 16 * WM * TM, BN = 16 * WN * TN;
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-    gemm_kernel<<<dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, st>>>(
+    gemm_kernel<WM, WN, TM, TN, KS, BPACK><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * WM * WN), 0, st>>>(
         q, s_x, packed, s_w, (int)M, (int)N, (int)K, y, acc, tiles_m, tiles_n);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
+                       int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
+    // Tile configurations (id: BM x BN): 0: 256 x 224, 1: 256 x 80, 2: 256 x 128,
+    // 3: 128 x 128, 4: 64 x 128.  Pick the tile whose busiest compute unit does the least work, assuming one
+    // workgroup per CU at a time: cost = ceil(tiles / 256) * BM * BN.
+    struct Cand { int bm, bn, id; };
+    const Cand cands[] = {{256, 224, 0}, {256, 80, 1}, {256, 128, 2}, {128, 128, 3}, {64, 128, 4}};
+    int best = 3;
+    int64_t best_cost = -1;
+    for (const Cand &c : cands) {
+        const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+        const int64_t cost = ((tiles + 255) / 256) * (int64_t)c.bm * c.bn;
+        if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = c.id; }
+    }
+    return launch_gemm_cfg(best, q, s_x, packed, s_w, M, N, K, y, acc, st);
+}
+
+int gemm_config_count() { return 5; }
+
+hipError_t launch_gemm_cfg(int cfg, const int8_t *q, const float *s_x, const uint8_t *packed,
+                           const float *s_w, int64_t M, int64_t N, int64_t K, float *y, int32_t *acc,
+                           hipStream_t st) {
+    // a configuration needing K % 128 == 0 falls back to its single-step twin
+    const bool k128 = (K % 128) == 0;
+    switch (cfg) {
+        case 0: return k128 ? launch_cfg<BITNET_GEMM_CFG0>(q, s_x, packed, s_w, M, N, K, y, acc, st)
+                            : launch_cfg<BITNET_GEMM_CFG0_K64>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+        case 1: return k128 ? launch_cfg<BITNET_GEMM_CFG1>(q, s_x, packed, s_w, M, N, K, y, acc, st)
+                            : launch_cfg<BITNET_GEMM_CFG1_K64>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+        case 2: return launch_cfg<2, 2, 8, 4, 1>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+        case 3: return launch_cfg<2, 2, 4, 4, 1>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+        default: return launch_cfg<1, 4, 4, 2, 1>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    }
 }
 
 }  // namespace bitnet

@@ -43,6 +43,10 @@ uint32_t gemv_grouped_rows_per_block();
 uint32_t gemv_grouped_threads();
 hipError_t launch_gemm(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                        int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st);
+hipError_t launch_gemm_cfg(int cfg, const int8_t *q, const float *s_x, const uint8_t *packed,
+                           const float *s_w, int64_t M, int64_t N, int64_t K, float *y, int32_t *acc,
+                           hipStream_t st);
+int gemm_config_count();
 hipError_t launch_linear_generic(const int8_t *q, const float *s_x, const uint8_t *packed,
                                  const float *s_w, int64_t M, int64_t N, int64_t K, float *y,
                                  int32_t *acc, hipStream_t st);

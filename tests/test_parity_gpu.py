@@ -174,6 +174,23 @@ def test_gemm_parity(M, N, K):
     check_linear(q, s, packed, np.float32(0.0071))
 
 
+@pytest.mark.parametrize("cfg", range(5))
+@pytest.mark.parametrize("M,N,K", [(300, 500, 640), (17, 33, 64), (257, 225, 6912 - 64)])
+def test_gemm_tile_configs(cfg, M, N, K):
+    """Every MFMA tile configuration, forced, on ragged M and N."""
+    key = synth.stream_key(307, M, N, K)
+    x, q, s = quantized_inputs(key, M, K, row_scale=(0.1, 10.0))
+    packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
+    acc_ref, y_ref = oracle.linear(q, s, packed, np.float32(0.0093))
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    tw.bitnet_linear_select(torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV),
+                            torch.from_numpy(packed).to(DEV), torch.tensor([0.0093], device=DEV),
+                            y, acc, 16 + cfg)
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    assert_y(y.cpu().numpy(), y_ref)
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 5, 4), (3, 9, 68), (20, 33, 132), (2, 70, 2560 + 4)])
 def test_generic_path_parity(M, N, K):
     key = synth.stream_key(303, M, N, K)
