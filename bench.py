@@ -266,12 +266,13 @@ def main() -> int:
         log(f"cpu oracle: {line['cpu_baseline']['value']} GB/s on {oracle.get_threads()} threads")
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # a plain elementwise kernel of known traffic: reads 1 GiB, writes 1 GiB
+        src = torch.ones(1 << 28, dtype=torch.int32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        log("copy calibration: 3 x 1 GiB device copies done")
+        log("copy calibration: 3 x (read 1 GiB + write 1 GiB) elementwise kernels done")
 
     print(json.dumps(line), flush=True)
     return 0

@@ -23,7 +23,7 @@
 #include "internal.h"
 
 #ifndef BITNET_GROUPED_RG
-#define BITNET_GROUPED_RG 2
+#define BITNET_GROUPED_RG 4
 #endif
 #ifndef BITNET_GROUPED_DOT8
 #define BITNET_GROUPED_DOT8 1
@@ -322,9 +322,9 @@ __device__ __forceinline__ void gemv_lds_tile(const int8_t *__restrict__ q, cons
     }
     __syncthreads();
 
-    // The chunk count is padded to even (a padded chunk is a clamped in-range load
-    // with zero codes) so the loop body has no branches: the compiler can then wait
-    // for exactly the older buffer's loads.
+    // Pairs of chunks with no branch inside the loop body, so that the compiler
+    // waits for exactly the older buffer's loads; the last one or two chunks are
+    // peeled (a uniform branch outside the loop).
     if (T > 0) {
         const int T2 = (T + 1) & ~1;
         for (int t = 0; t < T2 - 2; t += 2) {
@@ -333,9 +333,13 @@ __device__ __forceinline__ void gemv_lds_tile(const int8_t *__restrict__ q, cons
             issue(bufA, t + 2);
             consume(bufB, t + 1);
         }
-        issue(bufB, T2 - 1);
-        consume(bufA, T2 - 2);
-        consume(bufB, T2 - 1);
+        if (T2 == T) {
+            issue(bufB, T - 1);
+            consume(bufA, T - 2);
+            consume(bufB, T - 1);
+        } else {
+            consume(bufA, T - 1);
+        }
     }
 
     int acc[RG][MT];
