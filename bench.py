@@ -226,6 +226,58 @@ def main() -> int:
             sweep[f"M{M}"] = row
         sec["sweep_K2560_N6912"] = sweep
         log(f"sweep: {json.dumps(sweep)}")
+
+        # 100B-scale FFN stream: 8 layers x {gate, up 8192->28672; down 28672->8192},
+        # 1,409,286,144 packed bytes (5.5x the on-chip cache)
+        fmats = W.ffn_100b(8)
+        fpacked, fsw = [], []
+        for m in fmats:
+            p_, s_ = tw.pack_weights(W.weights(m, dev), 1e-5)
+            fpacked.append(p_)
+            fsw.append(s_)
+        fbytes = sum(p_.numel() for p_ in fpacked)
+        for M in (1, 8):
+            xs8 = [W.ffn_100b_activations(l, M, dev) for l in range(8)]
+            qx = [[tw.quant_act(x) for x in xl] for xl in xs8]
+            fys = [torch.empty((M, m.N), dtype=torch.float32, device=dev) for m in fmats]
+            if M == 1:
+                plan = tw.bitnet_grouped_plan_linear(
+                    [(qx[m.layer][m.slot][0], qx[m.layer][m.slot][1], fpacked[i], fsw[i], fys[i], None)
+                     for i, m in enumerate(fmats)])
+                run = lambda: plan.launch(stream)
+            else:
+                def run():
+                    for i, m in enumerate(fmats):
+                        qq, ss = qx[m.layer][m.slot]
+                        tw.bitnet_linear(qq, ss, fpacked[i], fsw[i], fys[i])
+            for _ in range(3):
+                run()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(20):
+                run()
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / 20
+            key = f"ffn100b_8layers_M{M}"
+            sec[key] = {"us": round(us, 1), "weight_GBs": round(fbytes / (us * 1e-6) / 1e9, 1),
+                        "launches": 1 if M == 1 else len(fmats)}
+            log(f"{key}: {us:.1f} us, {sec[key]['weight_GBs']} GB/s")
+        # one GPU's share of an 8-way column split of the 100B gate matrix (K=8192, N=3584)
+        shard = fpacked[0][:3584].contiguous()
+        q1, s1 = tw.quant_act(W.ffn_100b_activations(0, 1, dev)[0])
+        y1 = torch.empty((1, 3584), dtype=torch.float32, device=dev)
+        for _ in range(5):
+            tw.bitnet_linear(q1, s1, shard, fsw[0], y1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(100):
+            tw.bitnet_linear(q1, s1, shard, fsw[0], y1)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / 100
+        sec["colsplit8_gate_shard_M1"] = {"us": round(us, 2), "weight_GBs": round(shard.numel() / (us * 1e-6) / 1e9, 1)}
+        del fpacked
         line["secondary"] = sec
 
     # ------------------------------------------------------------ CPU baseline
