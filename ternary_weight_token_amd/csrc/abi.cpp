@@ -150,7 +150,6 @@ static int check_linear_desc(const bitnet_linear_desc &d) {
     if (st) return st;
     if (d.M < 1 || d.M > kGemvMaxM || d.N < 1) return fail(BITNET_ERR_SHAPE, "grouped linear needs 1 <= M <= 16, N >= 1");
     if (!linear_fast(d.q, d.packed, d.K)) return fail(BITNET_ERR_ALIGN, "grouped linear needs K % 64 == 0 and 16-byte aligned q/packed");
-    if (gemv_grouped_lds_bytes(d.K) > 64 * 1024) return fail(BITNET_ERR_SHAPE, "grouped linear needs K <= 52416");
     return BITNET_OK;
 }
 

@@ -34,8 +34,6 @@
 
 namespace bitnet {
 
-constexpr int kMaxKSplit = 8;
-
 // Weight loads go through the global address space explicitly: pointers read
 // from a plan descriptor are otherwise generic (FLAT) accesses, which also count
 // against the LDS wait counter and would serialise them with the LDS reads.
@@ -54,137 +52,6 @@ __device__ __forceinline__ uint4 load_weights(const uint8_t *p) {
         return make_uint4(v.x, v.y, v.z, v.w);
     }
     return gload16(p);
-}
-
-template <int MT, int RG, bool DOT8, bool NT>
-__device__ __forceinline__ void gemv_tile(const int8_t *__restrict__ q, const float *__restrict__ s_x,
-                                          const uint8_t *__restrict__ packed,
-                                          const float *__restrict__ s_w, int M, int N, int K,
-                                          float *__restrict__ y, int32_t *__restrict__ acc_out,
-                                          int row0, int m0, int kslices, int *lds) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int l8 = lane & 7;
-    const int rs = lane >> 3;
-    const int C = K >> 6;     // 16-byte chunks per packed row
-    const int KB = K >> 2;    // bytes per packed row
-    const int cb = (int)(((int64_t)C * wave) / kslices);
-    const int ce = (int)(((int64_t)C * (wave + 1)) / kslices);
-    const int mcount = min(MT, M - m0);
-
-    int acc[RG][MT];
-    const uint8_t *prow[RG];
-    #pragma unroll
-    for (int g = 0; g < RG; ++g) {
-        const int r = row0 + 8 * g + rs;
-        prow[g] = packed + (size_t)(r < N ? r : 0) * KB;   // rows past N read row 0, discarded
-        #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[g][m] = 0;
-    }
-    const int8_t *qrow = q + (size_t)m0 * K;
-
-    for (int c = cb + l8; c < ce; c += 8) {
-        uint4 wv[RG];
-        #pragma unroll
-        for (int g = 0; g < RG; ++g) wv[g] = load_weights<NT>(prow[g] + 16 * c);
-        #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            if (m < mcount) {
-                const uint4 *qp = reinterpret_cast<const uint4 *>(qrow + (size_t)m * K + 64 * c);
-                const uint4 a[4] = {qp[0], qp[1], qp[2], qp[3]};
-                int sq = 0;
-                #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    sq = dot4(a[d].x, 0x01010101u, sq);
-                    sq = dot4(a[d].y, 0x01010101u, sq);
-                    sq = dot4(a[d].z, 0x01010101u, sq);
-                    sq = dot4(a[d].w, 0x01010101u, sq);
-                }
-                if (DOT8) {
-                    QNib nb[4];
-                    #pragma unroll
-                    for (int d = 0; d < 4; ++d) nb[d] = nibble_form(a[d].x, a[d].y, a[d].z, a[d].w);
-                    #pragma unroll
-                    for (int g = 0; g < RG; ++g) {
-                        const uint32_t wd[4] = {wv[g].x, wv[g].y, wv[g].z, wv[g].w};
-                        int hi = 0;
-                        uint32_t lo = 0;
-                        #pragma unroll
-                        for (int d = 0; d < 4; ++d) {
-                            const uint32_t u0 = wd[d] & 0x33333333u;
-                            const uint32_t u1 = (wd[d] >> 2) & 0x33333333u;
-                            hi = sdot8(u0, nb[d].he, hi);
-                            hi = sdot8(u1, nb[d].ho, hi);
-                            lo = udot8(u0, nb[d].le, lo);
-                            lo = udot8(u1, nb[d].lo, lo);
-                        }
-                        acc[g][m] += 16 * hi + (int)lo - sq;
-                    }
-                } else {
-                    uint32_t P[4][4];
-                    #pragma unroll
-                    for (int d = 0; d < 4; ++d)
-                        transpose4x4(a[d].x, a[d].y, a[d].z, a[d].w, P[d][0], P[d][1], P[d][2], P[d][3]);
-                    #pragma unroll
-                    for (int g = 0; g < RG; ++g) {
-                        const uint32_t wd[4] = {wv[g].x, wv[g].y, wv[g].z, wv[g].w};
-                        int s = acc[g][m] - sq;
-                        #pragma unroll
-                        for (int d = 0; d < 4; ++d) {
-                            #pragma unroll
-                            for (int i = 0; i < 4; ++i) s = dot4(codes_i(wd[d], i), P[d][i], s);
-                        }
-                        acc[g][m] = s;
-                    }
-                }
-            }
-        }
-    }
-
-    #pragma unroll
-    for (int g = 0; g < RG; ++g) {
-        #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[g][m] = octet_sum(acc[g][m]);
-    }
-
-    const float sw = *s_w;
-    if (kslices == 1) {
-        #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            if (m >= mcount) continue;
-            const double cm = rescale_factor(s_x[m0 + m], sw);
-            #pragma unroll
-            for (int g = 0; g < RG; ++g) {
-                const int r = row0 + 8 * g + rs;
-                if (r < N && l8 == (m & 7)) {
-                    const size_t o = (size_t)(m0 + m) * N + r;
-                    y[o] = rescale(acc[g][m], cm);
-                    if (acc_out) acc_out[o] = acc[g][m];
-                }
-            }
-        }
-        return;
-    }
-    // K split across the workgroup's wavefronts: combine through LDS.
-    constexpr int R = 8 * RG;
-    if (l8 == 0) {
-        #pragma unroll
-        for (int g = 0; g < RG; ++g) {
-            #pragma unroll
-            for (int m = 0; m < MT; ++m) lds[(wave * R + 8 * g + rs) * MT + m] = acc[g][m];
-        }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < R * MT; idx += blockDim.x) {
-        const int rr = idx / MT, m = idx % MT;
-        const int r = row0 + rr;
-        if (r >= N || m >= mcount) continue;
-        int s = 0;
-        for (int w = 0; w < kslices; ++w) s += lds[(w * R + rr) * MT + m];
-        const size_t o = (size_t)(m0 + m) * N + r;
-        y[o] = rescale(s, rescale_factor(s_x[m0 + m], sw));
-        if (acc_out) acc_out[o] = s;
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -233,8 +100,8 @@ __device__ __forceinline__ void gemv_lds_tile(const int8_t *__restrict__ q, cons
                                               const uint8_t *__restrict__ packed,
                                               const float *__restrict__ s_w, int M, int N, int K,
                                               float *__restrict__ y, int32_t *__restrict__ acc_out,
-                                              int row_base, int m0, int kslices, uint32_t *qs,
-                                              int *sq, int *red) {
+                                              int row_base, int m0, int kslices, int seg_chunks,
+                                              uint32_t *qs, int *sq, int *red) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l8 = lane & 7, rs = lane >> 3;
@@ -242,12 +109,9 @@ __device__ __forceinline__ void gemv_lds_tile(const int8_t *__restrict__ q, cons
     const int KB = K >> 2;
     const int mcount = min(MT, M - m0);
 
-    // ---- wave -> (row set, K slice); the first weight loads go out before the
-    // prologue so that their latency overlaps the staging of q
+    // wave -> (row set, K slice of every segment)
     const int rowset = wave / kslices, slice = wave - rowset * kslices;
     const int row0 = row_base + rowset * 8 * RG;
-    const int cb = (int)(((int64_t)C * slice) / kslices);
-    const int ce = (int)(((int64_t)C * (slice + 1)) / kslices);
 
     int hi[RG][MT];
     uint32_t lo[RG][MT];
@@ -259,86 +123,95 @@ __device__ __forceinline__ void gemv_lds_tile(const int8_t *__restrict__ q, cons
         #pragma unroll
         for (int m = 0; m < MT; ++m) { hi[g][m] = 0; lo[g][m] = 0u; }
     }
+    if (tid < MT) sq[tid] = 0;
 
-    // Chunk t of this lane is c = cb + l8 + 8 t, t < T (T uniform across the
-    // wavefront; lanes past the slice end load a clamped in-range chunk and use
-    // all-zero codes, which add nothing).  Two register buffers alternate so that
-    // the loads of chunk t + 1 are in flight while chunk t is being consumed.
-    // (ce > cb always: every slice holds at least one chunk.)
-    const int T = (ce - cb + 7) >> 3;
-    const int clast = ce - 1;
-    uint4 bufA[RG], bufB[RG];
-    auto issue = [&](uint4 (&b)[RG], int t) {
-        const int cc = min(cb + l8 + 8 * t, clast);
-        #pragma unroll
-        for (int g = 0; g < RG; ++g) b[g] = load_weights<NT>(prow[g] + 16 * cc);
-    };
-    auto consume = [&](const uint4 (&b)[RG], int t) {
-        const int craw = cb + l8 + 8 * t;
-        const bool valid = craw < ce;
-        const int cc = min(craw, clast);
-        #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            if (m < mcount) {
-                const uint32_t *qc = qs + (m * C + cc) * kLdsChunkDw;
-                #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const uint4 pq = *reinterpret_cast<const uint4 *>(qc + 4 * d);
+    // K is walked in segments of seg_chunks 64-weight chunks; the q tile of a segment
+    // (MT rows) is what LDS holds, so any K and M tile fit the LDS budget.
+    for (int s0 = 0; s0 < C; s0 += seg_chunks) {
+        const int sc = min(seg_chunks, C - s0);
+        const int cb = s0 + (int)(((int64_t)sc * slice) / kslices);
+        const int ce = s0 + (int)(((int64_t)sc * (slice + 1)) / kslices);
+
+        // Chunk t of this lane is c = cb + l8 + 8 t, t < T (T uniform across the
+        // wavefront; lanes past the slice end load a clamped in-range chunk and use
+        // all-zero codes, which add nothing).  Two register buffers alternate so that
+        // the loads of chunk t + 1 are in flight while chunk t is being consumed.
+        const int T = (ce - cb + 7) >> 3;
+        const int clast = max(ce - 1, cb);
+        uint4 bufA[RG], bufB[RG];
+        auto issue = [&](uint4 (&b)[RG], int t) {
+            const int cc = min(cb + l8 + 8 * t, clast);
+            #pragma unroll
+            for (int g = 0; g < RG; ++g) b[g] = load_weights<NT>(prow[g] + 16 * cc);
+        };
+        auto consume = [&](const uint4 (&b)[RG], int t) {
+            const int craw = cb + l8 + 8 * t;
+            const bool valid = craw < ce;
+            const int cc = min(craw, clast) - s0;
+            #pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                if (m < mcount) {
+                    const uint32_t *qc = qs + (m * seg_chunks + cc) * kLdsChunkDw;
                     #pragma unroll
-                    for (int g = 0; g < RG; ++g) {
-                        uint32_t wd = d == 0 ? b[g].x : d == 1 ? b[g].y : d == 2 ? b[g].z : b[g].w;
-                        wd = valid ? wd : 0u;
-                        mac16<DOT8>(wd, pq, hi[g][m], lo[g][m]);
+                    for (int d = 0; d < 4; ++d) {
+                        const uint4 pq = *reinterpret_cast<const uint4 *>(qc + 4 * d);
+                        #pragma unroll
+                        for (int g = 0; g < RG; ++g) {
+                            uint32_t wd = d == 0 ? b[g].x : d == 1 ? b[g].y : d == 2 ? b[g].z : b[g].w;
+                            wd = valid ? wd : 0u;
+                            mac16<DOT8>(wd, pq, hi[g][m], lo[g][m]);
+                        }
                     }
                 }
             }
-        }
-    };
-    if (T > 0) issue(bufA, 0);
+        };
+        // the segment's first weight loads go out before the staging of q, so that
+        // their latency overlaps it
+        if (T > 0) issue(bufA, 0);
 
-    // ---- prologue: stage the M tile of q, rearranged, and its row sums
-    if (tid < MT) sq[tid] = 0;
-    __syncthreads();
-    {
-        int part[MT];
-        #pragma unroll
-        for (int m = 0; m < MT; ++m) part[m] = 0;
-        const int pieces = C * 4;  // 16-byte pieces per row of q
-        for (int idx = tid; idx < mcount * pieces; idx += blockDim.x) {
-            const int m = idx / pieces, r = idx - m * pieces;
-            const uint4 a = gload16(q + (size_t)(m0 + m) * K + 16 * r);
-            const int c = r >> 2, d = r & 3;
-            *reinterpret_cast<uint4 *>(qs + (m * C + c) * kLdsChunkDw + 4 * d) = prep16<DOT8>(a);
-            int s = dot4(a.x, 0x01010101u, 0);
-            s = dot4(a.y, 0x01010101u, s);
-            s = dot4(a.z, 0x01010101u, s);
-            s = dot4(a.w, 0x01010101u, s);
+        // ---- stage the segment of the M tile of q, rearranged, and its row sums
+        __syncthreads();   // previous segment's LDS reads done; sq initialised
+        {
+            int part[MT];
             #pragma unroll
-            for (int mm = 0; mm < MT; ++mm) part[mm] += (mm == m) ? s : 0;
+            for (int m = 0; m < MT; ++m) part[m] = 0;
+            const int pieces = sc * 4;  // 16-byte pieces per row of q in this segment
+            for (int idx = tid; idx < mcount * pieces; idx += blockDim.x) {
+                const int m = idx / pieces, r = idx - m * pieces;
+                const uint4 a = gload16(q + (size_t)(m0 + m) * K + 64 * s0 + 16 * r);
+                const int c = r >> 2, d = r & 3;
+                *reinterpret_cast<uint4 *>(qs + (m * seg_chunks + c) * kLdsChunkDw + 4 * d) = prep16<DOT8>(a);
+                int sm = dot4(a.x, 0x01010101u, 0);
+                sm = dot4(a.y, 0x01010101u, sm);
+                sm = dot4(a.z, 0x01010101u, sm);
+                sm = dot4(a.w, 0x01010101u, sm);
+                #pragma unroll
+                for (int mm = 0; mm < MT; ++mm) part[mm] += (mm == m) ? sm : 0;
+            }
+            #pragma unroll
+            for (int m = 0; m < MT; ++m)
+                if (m < mcount && part[m] != 0) atomicAdd(&sq[m], part[m]);
         }
-        #pragma unroll
-        for (int m = 0; m < MT; ++m)
-            if (m < mcount && part[m] != 0) atomicAdd(&sq[m], part[m]);
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // Pairs of chunks with no branch inside the loop body, so that the compiler
-    // waits for exactly the older buffer's loads; the last one or two chunks are
-    // peeled (a uniform branch outside the loop).
-    if (T > 0) {
-        const int T2 = (T + 1) & ~1;
-        for (int t = 0; t < T2 - 2; t += 2) {
-            issue(bufB, t + 1);
-            consume(bufA, t);
-            issue(bufA, t + 2);
-            consume(bufB, t + 1);
-        }
-        if (T2 == T) {
-            issue(bufB, T - 1);
-            consume(bufA, T - 2);
-            consume(bufB, T - 1);
-        } else {
-            consume(bufA, T - 1);
+        // Pairs of chunks with no branch inside the loop body, so that the compiler
+        // waits for exactly the older buffer's loads; the last one or two chunks are
+        // peeled (a uniform branch outside the loop).
+        if (T > 0) {
+            const int T2 = (T + 1) & ~1;
+            for (int t = 0; t < T2 - 2; t += 2) {
+                issue(bufB, t + 1);
+                consume(bufA, t);
+                issue(bufA, t + 2);
+                consume(bufB, t + 1);
+            }
+            if (T2 == T) {
+                issue(bufB, T - 1);
+                consume(bufA, T - 2);
+                consume(bufB, T - 1);
+            } else {
+                consume(bufA, T - 1);
+            }
         }
     }
 
@@ -397,24 +270,24 @@ template <int MT, int RG, bool DOT8>
 __global__ __launch_bounds__(256) void gemv_lds_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s_x, const uint8_t *__restrict__ packed,
     const float *__restrict__ s_w, int M, int N, int K, float *__restrict__ y,
-    int32_t *__restrict__ acc_out, int kslices) {
+    int32_t *__restrict__ acc_out, int kslices, int seg_chunks) {
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
     __shared__ int sq[MT];
     __shared__ int red[4 * 8 * RG * MT];
     const int rows_per_block = (4 / kslices) * 8 * RG;
     gemv_lds_tile<MT, RG, DOT8, BITNET_GEMV_NT != 0>(q, s_x, packed, s_w, M, N, K, y, acc_out,
                                                      blockIdx.x * rows_per_block, blockIdx.y * MT, kslices,
-                                                     dyn, sq, red);
+                                                     seg_chunks, dyn, sq, red);
 }
 
-template <int MT, int RG, bool DOT8>
-__global__ __launch_bounds__(64 * kMaxKSplit) void gemv_kernel(
-    const int8_t *__restrict__ q, const float *__restrict__ s_x, const uint8_t *__restrict__ packed,
-    const float *__restrict__ s_w, int M, int N, int K, float *__restrict__ y,
-    int32_t *__restrict__ acc_out, int kslices) {
-    __shared__ int lds[kMaxKSplit * 8 * RG * MT];
-    gemv_tile<MT, RG, DOT8, BITNET_GEMV_NT != 0>(q, s_x, packed, s_w, M, N, K, y, acc_out,
-                                                 blockIdx.x * 8 * RG, blockIdx.y * MT, kslices, lds);
+// K segment length in 64-weight chunks for an M tile of mt rows: the whole of K when
+// its staged q fits the LDS budget, else the fewest segments of equal size, each a
+// multiple of 8 chunks (one per lane of an octet).
+__host__ __device__ __forceinline__ int segment_chunks(int C, int mt) {
+    const int max_seg = (kLdsBudget / (mt * kLdsChunkDw * 4)) & ~7;
+    if (C <= max_seg) return C;
+    const int nseg = (C + max_seg - 1) / max_seg;
+    return (((C + nseg - 1) / nseg) + 7) & ~7;
 }
 
 // Grouped decode: 4 wavefronts per block, block -> (descriptor, row block, M tile)
@@ -433,27 +306,14 @@ __global__ __launch_bounds__(256) void gemv_grouped_kernel(const uint8_t *__rest
     const int rowblocks = (d.N + rows - 1) / rows;
     const int rb = (int)(e.local % rowblocks), mt = (int)(e.local / rowblocks);
     gemv_lds_tile<kGroupedMT, kGroupedRG, BITNET_GROUPED_DOT8 != 0, BITNET_GEMV_NT != 0>(
-        d.q, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, d.y, d.acc, rb * rows, mt * kGroupedMT, 1, dyn, sq, red);
+        d.q, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, d.y, d.acc, rb * rows, mt * kGroupedMT, 1, segment_chunks(d.K >> 6, kGroupedMT), dyn,
+        sq, red);
 }
 
 uint32_t gemv_grouped_rows_per_block() { return 4 * 8 * kGroupedRG; }
 uint32_t gemv_grouped_threads() { return 256; }
-uint32_t gemv_grouped_lds_bytes(int64_t K) { return (uint32_t)(kGroupedMT * (K / 64) * kLdsChunkDw * 4); }
-
-template <int MT, int RG, bool DOT8>
-static hipError_t launch_t(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
-                           int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
-    const int rows = 8 * RG;
-    const unsigned gx = (unsigned)((N + rows - 1) / rows);
-    const unsigned gy = (unsigned)((M + MT - 1) / MT);
-    const int C = (int)(K / 64);
-    // split K across wavefronts until the launch has ~8 wavefronts per CU, keeping
-    // at least 4 chunk iterations per lane.
-    int ks = 1;
-    while (ks < kMaxKSplit && (int64_t)gx * gy * ks < 2048 && C / (16 * ks) >= 4) ks *= 2;
-    gemv_kernel<MT, RG, DOT8><<<dim3(gx, gy), dim3(64 * ks), 0, st>>>(q, s_x, packed, s_w, (int)M, (int)N,
-                                                                      (int)K, y, acc, ks);
-    return hipGetLastError();
+uint32_t gemv_grouped_lds_bytes(int64_t K) {
+    return (uint32_t)(kGroupedMT * segment_chunks((int)(K / 64), kGroupedMT) * kLdsChunkDw * 4);
 }
 
 template <int MT, int RG, bool DOT8>
@@ -467,29 +327,20 @@ static hipError_t launch_lds(const int8_t *q, const float *s_x, const uint8_t *p
     auto blocks = [&](int k) { return (int64_t)((N + (4 / k) * 8 * RG - 1) / ((4 / k) * 8 * RG)) * gy; };
     while (ks < 4 && blocks(ks) < 512 && C / (8 * ks * 2) >= 2) ks *= 2;
     const unsigned gx = (unsigned)((N + (4 / ks) * 8 * RG - 1) / ((4 / ks) * 8 * RG));
-    const size_t lds = (size_t)MT * C * kLdsChunkDw * 4;
+    const int seg = segment_chunks(C, MT);
+    const size_t lds = (size_t)MT * seg * kLdsChunkDw * 4;
     gemv_lds_kernel<MT, RG, DOT8><<<dim3(gx, gy), dim3(256), lds, st>>>(q, s_x, packed, s_w, (int)M, (int)N,
-                                                                        (int)K, y, acc, ks);
+                                                                        (int)K, y, acc, ks, seg);
     return hipGetLastError();
 }
 
 hipError_t launch_gemv(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                        int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
-    const int64_t C = K / 64;
     const bool d8 = BITNET_GROUPED_DOT8 != 0;
-    if (M == 1 && C * kLdsChunkDw * 4 <= kLdsBudget)
-        return launch_lds<1, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
-    if (M == 2 && 2 * C * kLdsChunkDw * 4 <= kLdsBudget)
-        return launch_lds<2, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
-    if (M <= 4 && 4 * C * kLdsChunkDw * 4 <= kLdsBudget)
-        return launch_lds<4, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
-    if (8 * C * kLdsChunkDw * 4 <= kLdsBudget)
-        return launch_lds<8, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
-    // q tile too large for LDS: rearrange q in registers per chunk
-    if (M == 1) return launch_t<1, 4, true>(q, s_x, packed, s_w, M, N, K, y, acc, st);
-    if (M == 2) return launch_t<2, 4, true>(q, s_x, packed, s_w, M, N, K, y, acc, st);
-    if (M <= 4) return launch_t<4, 2, true>(q, s_x, packed, s_w, M, N, K, y, acc, st);
-    return launch_t<8, 2, true>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    if (M == 1) return launch_lds<1, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    if (M == 2) return launch_lds<2, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    if (M <= 4) return launch_lds<4, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    return launch_lds<8, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
 }
 
 hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st) {

@@ -106,6 +106,15 @@ def test_grouped_plan_checks(L):
     # the header records the block count: ceil(N / rows_per_block) * M
     hdr = (ctypes.c_uint32 * 8).from_buffer_copy(buf.raw[:32])
     assert hdr[5] > 0 and hdr[3] == (100 + hdr[5] - 1) // hdr[5]
+    # a K whose staged q exceeds the LDS budget is walked in segments: accepted,
+    # and the recorded LDS size stays within 64 KiB
+    arr4 = (D * 1)(D(a16, a16, a16, a16, a16, 0, 1, 100, 64 * 1000))
+    n4 = L.bitnet_grouped_plan_bytes(1, 1, ctypes.cast(arr4, ctypes.c_void_p))
+    buf4 = ctypes.create_string_buffer(n4)
+    assert L.bitnet_grouped_plan_linear(ctypes.cast(arr4, ctypes.c_void_p), 1,
+                                        ctypes.cast(buf4, ctypes.c_void_p), n4) == OK
+    hdr4 = (ctypes.c_uint32 * 8).from_buffer_copy(buf4.raw[:32])
+    assert 0 < hdr4[6] <= 64 * 1024
 
 
 def test_python_binding_fails_loudly_without_gpu_tensors():

@@ -165,6 +165,41 @@ def test_gemv_parity_shapes(M, N, K):
     check_linear(q, s, packed, s_w)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 200, 53312), (2, 70, 26176), (3, 200, 16704), (8, 200, 16704),
+                                   (13, 130, 8192), (16, 65, 28672)])
+def test_gemv_parity_k_segments(M, N, K):
+    # K long enough that the staged q tile of the M tile exceeds the LDS budget, so
+    # the GEMV walks K in segments (uneven last segment, ragged N).
+    key = synth.stream_key(302, M, N, K)
+    x, q, s = quantized_inputs(key, M, K)
+    w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02)
+    packed, s_w = oracle.pack(w.numpy())
+    check_linear(q, s, packed, s_w)
+
+
+def test_grouped_linear_mixed_k():
+    """One grouped GEMV launch over problems with different M, N and K, one of
+    whose K needs two LDS segments; every output is compared."""
+    shapes = [(1, 300, 2560), (3, 129, 53312), (1, 64, 64), (16, 97, 6912), (2, 700, 640)]
+    probs, refs = [], []
+    for i, (M, N, K) in enumerate(shapes):
+        key = synth.stream_key(303, i)
+        x, q, s = quantized_inputs(key, M, K)
+        packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
+        s_w = np.float32(0.0071 * (i + 1))
+        refs.append(oracle.linear(q, s, packed, s_w))
+        y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+        acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+        probs.append((torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV), torch.from_numpy(packed).to(DEV),
+                      torch.tensor([s_w], dtype=torch.float32, device=DEV), y, acc))
+    plan = tw.bitnet_grouped_plan_linear(probs)
+    plan.launch()
+    torch.cuda.synchronize()
+    for (acc_ref, y_ref), pr in zip(refs, probs):
+        assert np.array_equal(pr[5].cpu().numpy(), acc_ref)
+        assert_y(pr[4].cpu().numpy(), y_ref)
+
+
 @pytest.mark.parametrize("M,N,K", [(17, 129, 256), (32, 300, 2560), (64, 6912, 2560), (130, 257, 640),
                                    (200, 96, 6912), (2048, 384, 2560)])
 def test_gemm_parity(M, N, K):
