@@ -60,6 +60,29 @@ def committed_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def graph_us(torch, fn, reps: int = 20, replays: int = 5) -> float:
+    """Device time per call of fn(): reps calls captured in one HIP graph, replayed
+    (removes the host cost of one launch per call from the figure)."""
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * replays)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,27 +228,47 @@ def main() -> int:
                 sec[key] = {"us": round(us, 2), "int8_tops": round(tops, 1),
                             "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
                 log(f"{key}: {us:.1f} us, {tops:.0f} TOPS")
-        # batched-decode sweep K=2560 N=6912: both kernels at every M
+        # batched-decode sweep K=2560 N=6912: every kernel at every M, one launch
+        # per call, device time (graph-captured)
         p, s = tw.pack_weights(W.sweep_weights(dev), 1e-5)
         sweep = {}
         for M in (1, 2, 4, 8, 16, 32, 64):
             q, sx = tw.quant_act(W.sweep_activations(M, dev))
             y = torch.empty((M, p.shape[0]), dtype=torch.float32, device=dev)
             row = {}
-            for kname, kid in (("gemv", 1), ("gemm", 2)):
-                for _ in range(5):
-                    tw.bitnet_linear_select(q, sx, p, s, y, None, kid)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                for _ in range(100):
-                    tw.bitnet_linear_select(q, sx, p, s, y, None, kid)
-                b.record(stream)
-                torch.cuda.synchronize()
-                us = a.elapsed_time(b) * 1e3 / 100
+            for kname, kid in (("gemv", 1), ("mfma_decode", 4), ("gemm", 2)):
+                us = graph_us(torch, lambda: tw.bitnet_linear_select(q, sx, p, s, y, None, kid))
                 row[kname] = {"us": round(us, 2), "weight_GBs": round(p.numel() / (us * 1e-6) / 1e9, 1)}
             sweep[f"M{M}"] = row
         sec["sweep_K2560_N6912"] = sweep
         log(f"sweep: {json.dumps(sweep)}")
+
+        # batched decode step: the same 210 matrices with 8 sequences decoding together
+        # (grouped quant + grouped linear, which runs the MFMA decode kernel)
+        M8 = 8
+        xs8 = [W.decode_step_activations(l, dev, M8) for l in range(30)]
+        qs8 = [[torch.empty((M8, x.shape[1]), dtype=torch.int8, device=dev) for x in xl] for xl in xs8]
+        sxs8 = [[torch.empty(M8, dtype=torch.float32, device=dev) for _ in xl] for xl in xs8]
+        ys8 = [torch.empty((M8, m.N), dtype=torch.float32, device=dev) for m in mats]
+        qplan8 = tw.bitnet_grouped_plan_quant([(xs8[l][j], qs8[l][j], sxs8[l][j]) for l in range(30) for j in range(4)])
+        lplan8 = tw.bitnet_grouped_plan_linear(
+            [(qs8[m.layer][m.slot], sxs8[m.layer][m.slot], packed[i], sws[i], ys8[i], None)
+             for i, m in enumerate(mats)])
+        for _ in range(10):
+            qplan8.launch(stream)
+            lplan8.launch(stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(100):
+            qplan8.launch(stream)
+            lplan8.launch(stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / 100
+        sec["decode_step_2p4b_M8"] = {"us": round(us, 1), "weight_GBs": round(weight_bytes / (us * 1e-6) / 1e9, 1),
+                                      "tokens_per_s": round(M8 / (us * 1e-6), 1), "launches": 2}
+        log(f"decode step M=8: {us:.1f} us, {sec['decode_step_2p4b_M8']['weight_GBs']} GB/s")
+        del xs8, qs8, sxs8, ys8, qplan8, lplan8
 
         # 100B-scale FFN stream: 8 layers x {gate, up 8192->28672; down 28672->8192},
         # 1,409,286,144 packed bytes (5.5x the on-chip cache)
@@ -240,16 +283,10 @@ def main() -> int:
             xs8 = [W.ffn_100b_activations(l, M, dev) for l in range(8)]
             qx = [[tw.quant_act(x) for x in xl] for xl in xs8]
             fys = [torch.empty((M, m.N), dtype=torch.float32, device=dev) for m in fmats]
-            if M == 1:
-                plan = tw.bitnet_grouped_plan_linear(
-                    [(qx[m.layer][m.slot][0], qx[m.layer][m.slot][1], fpacked[i], fsw[i], fys[i], None)
-                     for i, m in enumerate(fmats)])
-                run = lambda: plan.launch(stream)
-            else:
-                def run():
-                    for i, m in enumerate(fmats):
-                        qq, ss = qx[m.layer][m.slot]
-                        tw.bitnet_linear(qq, ss, fpacked[i], fsw[i], fys[i])
+            plan = tw.bitnet_grouped_plan_linear(
+                [(qx[m.layer][m.slot][0], qx[m.layer][m.slot][1], fpacked[i], fsw[i], fys[i], None)
+                 for i, m in enumerate(fmats)])
+            run = lambda: plan.launch(stream)
             for _ in range(3):
                 run()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -261,21 +298,13 @@ def main() -> int:
             us = a.elapsed_time(b) * 1e3 / 20
             key = f"ffn100b_8layers_M{M}"
             sec[key] = {"us": round(us, 1), "weight_GBs": round(fbytes / (us * 1e-6) / 1e9, 1),
-                        "launches": 1 if M == 1 else len(fmats)}
+                        "launches": 1, "kernel": "gemv_grouped_kernel" if M == 1 else "skinny_grouped_kernel"}
             log(f"{key}: {us:.1f} us, {sec[key]['weight_GBs']} GB/s")
         # one GPU's share of an 8-way column split of the 100B gate matrix (K=8192, N=3584)
         shard = fpacked[0][:3584].contiguous()
         q1, s1 = tw.quant_act(W.ffn_100b_activations(0, 1, dev)[0])
         y1 = torch.empty((1, 3584), dtype=torch.float32, device=dev)
-        for _ in range(5):
-            tw.bitnet_linear(q1, s1, shard, fsw[0], y1)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(100):
-            tw.bitnet_linear(q1, s1, shard, fsw[0], y1)
-        b.record(stream)
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / 100
+        us = graph_us(torch, lambda: tw.bitnet_linear(q1, s1, shard, fsw[0], y1), reps=50)
         sec["colsplit8_gate_shard_M1"] = {"us": round(us, 2), "weight_GBs": round(shard.numel() / (us * 1e-6) / 1e9, 1)}
         del fpacked
         line["secondary"] = sec

@@ -132,8 +132,9 @@ BITNET_API int bitnet_quant_act(const uint16_t *x, int64_t M, int64_t K,
  *
  * acc is exact.  y is acc * s_x[m] * s_w / 127 evaluated as
  * fp32(acc * c_m) with c_m = (s_x[m] * s_w) / 127 in float64, i.e. within one
- * unit in the last place of the correctly rounded value.  M <= 16 runs the
- * decode GEMV (4-bit / 8-bit dot products); larger M runs the int8 MFMA GEMM.
+ * unit in the last place of the correctly rounded value.  M = 1 runs the
+ * decode GEMV (4-bit dot products), 2 <= M <= 16 the MFMA decode kernel (int8
+ * MFMA, all tokens in one pass over the weights), larger M the int8 MFMA GEMM.
  * ------------------------------------------------------------------------- */
 BITNET_API int bitnet_linear(const int8_t *q, const float *s_x, const uint8_t *packed,
                              const float *s_w, int64_t M, int64_t N, int64_t K,
@@ -142,7 +143,8 @@ BITNET_API int bitnet_linear(const int8_t *q, const float *s_x, const uint8_t *p
 /* Same as bitnet_linear with the kernel chosen by the caller instead of by M
  * (for measuring the GEMV / GEMM crossover): kernel 0 = automatic, 1 = decode
  * GEMV (any M; M > 8 re-reads the weights once per 8 rows of q), 2 = MFMA GEMM,
- * 3 = general kernel, 16 + i = MFMA GEMM with tile configuration i (0: 256 x 224,
+ * 3 = general kernel, 4 = MFMA decode kernel (any M; the weights are read once
+ * per 16 rows of q), 16 + i = MFMA GEMM with tile configuration i (0: 256 x 224,
  * 1: 256 x 80, 2: 256 x 128, 3: 128 x 128, 4: 64 x 128 rows x columns of y).
  * Kernels other than 0 and 3 need K % 64 == 0 and 16-byte aligned q / packed
  * (else BITNET_ERR_ALIGN); other values give BITNET_ERR_ARG. */
@@ -163,7 +165,10 @@ BITNET_API int bitnet_linear_select(const int8_t *q, const float *s_x, const uin
  * pointers inside the descriptors are baked into the plan.
  *
  * Linear descriptors must have 1 <= M <= 16, K % 64 == 0 and 16-byte aligned
- * q / packed; quant descriptors K % 8 == 0 and 16-byte aligned x / q.
+ * q / packed; quant descriptors K % 8 == 0 and 16-byte aligned x / q.  A linear
+ * plan whose descriptors all have M = 1 runs the decode GEMV; if any has M > 1,
+ * the whole plan runs the MFMA decode kernel (each weight read once for all M
+ * tokens of its problem).
  * ------------------------------------------------------------------------- */
 typedef struct bitnet_linear_desc {
     const int8_t *q;        /* (device) [M][K]   */

@@ -48,9 +48,10 @@ def decode_step_2p4b(layers: int = 30):
     return out
 
 
-def decode_step_activations(layer: int, device="cpu"):
-    """The 4 bf16 [1][K] activation vectors of one layer (no outliers)."""
-    return [activations(stream_key(CFG_DECODE, layer, 100 + s), 1, K, device=device)
+def decode_step_activations(layer: int, device="cpu", M: int = 1):
+    """The 4 bf16 [M][K] activations of one layer (no outliers); M > 1 is a batch of
+    M sequences decoding together."""
+    return [activations(stream_key(CFG_DECODE, layer, 100 + s, *((M,) if M > 1 else ())), M, K, device=device)
             for s, K in enumerate(SLOT_K_2P4B)]
 
 

@@ -110,7 +110,8 @@ BITNET_API int bitnet_linear(const int8_t *q, const float *s_x, const uint8_t *p
     if (st || M == 0 || N == 0) return st;
     hipStream_t s = (hipStream_t)stream;
     if (!linear_fast(q, packed, K)) return hip_status(launch_linear_generic(q, s_x, packed, s_w, M, N, K, y, acc, s));
-    if (M <= kGemvMaxM) return hip_status(launch_gemv(q, s_x, packed, s_w, M, N, K, y, acc, s));
+    if (M == 1) return hip_status(launch_gemv(q, s_x, packed, s_w, M, N, K, y, acc, s));
+    if (M <= kGemvMaxM) return hip_status(launch_skinny(q, s_x, packed, s_w, M, N, K, y, acc, s));
     return hip_status(launch_gemm(q, s_x, packed, s_w, M, N, K, y, acc, s));
 }
 
@@ -119,13 +120,14 @@ BITNET_API int bitnet_linear_select(const int8_t *q, const float *s_x, const uin
                                     int32_t *acc, int kernel, void *stream) {
     if (kernel == 0) return bitnet_linear(q, s_x, packed, s_w, M, N, K, y, acc, stream);
     const bool forced_tile = kernel >= 16 && kernel < 16 + gemm_config_count();
-    if ((kernel < 0 || kernel > 3) && !forced_tile) return fail(BITNET_ERR_ARG, "unknown kernel id");
+    if ((kernel < 0 || kernel > 4) && !forced_tile) return fail(BITNET_ERR_ARG, "unknown kernel id");
     int st = check_linear(q, s_x, packed, s_w, M, N, K, y, acc);
     if (st || M == 0 || N == 0) return st;
     hipStream_t s = (hipStream_t)stream;
     if (kernel == 3) return hip_status(launch_linear_generic(q, s_x, packed, s_w, M, N, K, y, acc, s));
     if (!linear_fast(q, packed, K)) return fail(BITNET_ERR_ALIGN, "kernel needs K % 64 == 0 and 16-byte aligned q/packed");
     if (kernel == 1) return hip_status(launch_gemv(q, s_x, packed, s_w, M, N, K, y, acc, s));
+    if (kernel == 4) return hip_status(launch_skinny(q, s_x, packed, s_w, M, N, K, y, acc, s));
     if (forced_tile) return hip_status(launch_gemm_cfg(kernel - 16, q, s_x, packed, s_w, M, N, K, y, acc, s));
     return hip_status(launch_gemm(q, s_x, packed, s_w, M, N, K, y, acc, s));
 }
@@ -140,7 +142,19 @@ static size_t plan_layout(int count, size_t desc_size, uint64_t blocks, uint64_t
     return (size_t)(*table_off + blocks * sizeof(BlockEntry));
 }
 
-static uint64_t linear_blocks(const bitnet_linear_desc &d) {
+// A plan whose problems all have M == 1 runs the GEMV (q staged in LDS); any M > 1
+// makes it run the MFMA decode kernel, which reads each weight once for all M tokens.
+static uint32_t linear_variant(const bitnet_linear_desc *d, int count) {
+    for (int i = 0; i < count; ++i)
+        if (d[i].M > 1) return kVariantMfma;
+    return kVariantGemv;
+}
+
+static uint64_t linear_blocks(const bitnet_linear_desc &d, uint32_t variant) {
+    if (variant == kVariantMfma) {
+        const uint64_t rows = skinny_grouped_rows_per_block();
+        return ((uint64_t)d.N + rows - 1) / rows;
+    }
     const uint64_t rows = gemv_grouped_rows_per_block();
     return ((uint64_t)d.N + rows - 1) / rows * (uint64_t)d.M;
 }
@@ -168,7 +182,8 @@ BITNET_API size_t bitnet_grouped_plan_bytes(int count, int is_linear, const void
     uint64_t blocks = 0, a, b;
     if (is_linear) {
         const bitnet_linear_desc *d = (const bitnet_linear_desc *)descs;
-        for (int i = 0; i < count; ++i) blocks += (d[i].M > 0 && d[i].N > 0) ? linear_blocks(d[i]) : 0;
+        const uint32_t variant = linear_variant(d, count);
+        for (int i = 0; i < count; ++i) blocks += (d[i].M > 0 && d[i].N > 0) ? linear_blocks(d[i], variant) : 0;
         return plan_layout(count, sizeof(LinearDescDev), blocks, &a, &b);
     }
     const bitnet_quant_desc *d = (const bitnet_quant_desc *)descs;
@@ -184,8 +199,9 @@ BITNET_API int bitnet_grouped_plan_linear(const bitnet_linear_desc *descs, int c
     for (int i = 0; i < count; ++i) {
         int st = check_linear_desc(descs[i]);
         if (st) return st;
-        blocks += linear_blocks(descs[i]);
     }
+    const uint32_t variant = linear_variant(descs, count);
+    for (int i = 0; i < count; ++i) blocks += linear_blocks(descs[i], variant);
     if (blocks >= ((uint64_t)1 << 31)) return fail(BITNET_ERR_SHAPE, "too many blocks");
     uint64_t doff, toff;
     const size_t need = plan_layout(count, sizeof(LinearDescDev), blocks, &doff, &toff);
@@ -198,8 +214,14 @@ BITNET_API int bitnet_grouped_plan_linear(const bitnet_linear_desc *descs, int c
     h->count = (uint32_t)count;
     h->total_blocks = (uint32_t)blocks;
     h->block_threads = gemv_grouped_threads();
-    h->rows_per_block = gemv_grouped_rows_per_block();
-    for (int i = 0; i < count; ++i) h->lds_bytes = std::max(h->lds_bytes, gemv_grouped_lds_bytes(descs[i].K));
+    h->variant = variant;
+    if (variant == kVariantMfma) {
+        h->rows_per_block = skinny_grouped_rows_per_block();
+        for (int i = 0; i < count; ++i) h->lds_bytes = std::max(h->lds_bytes, skinny_grouped_lds_bytes(descs[i].M));
+    } else {
+        h->rows_per_block = gemv_grouped_rows_per_block();
+        for (int i = 0; i < count; ++i) h->lds_bytes = std::max(h->lds_bytes, gemv_grouped_lds_bytes(descs[i].K));
+    }
     h->desc_offset = doff;
     h->table_offset = toff;
     h->total_bytes = need;
@@ -216,7 +238,7 @@ BITNET_API int bitnet_grouped_plan_linear(const bitnet_linear_desc *descs, int c
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return descs[a].K > descs[b].K; });
     uint64_t b = 0;
     for (int i : order) {
-        const uint64_t nb = linear_blocks(descs[i]);
+        const uint64_t nb = linear_blocks(descs[i], variant);
         for (uint64_t j = 0; j < nb; ++j) tb[b++] = BlockEntry{(uint32_t)i, (uint32_t)j};
     }
     return BITNET_OK;
@@ -271,6 +293,9 @@ BITNET_API int bitnet_linear_grouped(const void *plan_host, const void *plan_dev
     if (st) return st;
     const PlanHeader *h = (const PlanHeader *)plan_host;
     if (h->total_blocks == 0) return BITNET_OK;
+    if (h->variant == kVariantMfma)
+        return hip_status(launch_skinny_grouped(plan_dev, h->total_blocks, h->lds_bytes, (hipStream_t)stream));
+    if (h->variant != kVariantGemv) return fail(BITNET_ERR_ARG, "not a plan of this kind");
     return hip_status(launch_gemv_grouped(plan_dev, h->total_blocks, h->lds_bytes, (hipStream_t)stream));
 }
 

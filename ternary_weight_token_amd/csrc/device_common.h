@@ -5,6 +5,27 @@
 
 namespace bitnet {
 
+// Global loads go through the global address space explicitly: pointers read
+// from a plan descriptor are otherwise generic (FLAT) accesses, which also count
+// against the LDS wait counter and would serialise them with the LDS reads.
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const v4u gv4u;
+
+__device__ __forceinline__ uint4 gload16(const void *p) {
+    const v4u v = *(gv4u *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Weight loads: nontemporal when NT (each packed byte is read once per launch).
+template <bool NT>
+__device__ __forceinline__ uint4 load_weights(const uint8_t *p) {
+    if (NT) {
+        const v4u v = __builtin_nontemporal_load((gv4u *)p);
+        return make_uint4(v.x, v.y, v.z, v.w);
+    }
+    return gload16(p);
+}
+
 // Four signed bytes of `a` dotted with four signed bytes of `b`, plus c
 // (v_dot4_i32_i8).
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {

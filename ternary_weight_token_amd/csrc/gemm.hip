@@ -40,8 +40,6 @@ typedef __attribute__((address_space(1))) const v4u_g gv4u_g;
 #define BITNET_GEMM_CFG1_K64 8, 1, 2, 5, 1
 #endif
 
-constexpr int kStrideB = 80;   // bytes per LDS row (64 data + 16 pad: conflict-free b128 reads)
-
 __device__ __forceinline__ uint4 gld16(const void *p) {
     const v4u_g v = *(gv4u_g *)p;
     return make_uint4(v.x, v.y, v.z, v.w);

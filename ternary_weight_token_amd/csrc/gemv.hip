@@ -34,26 +34,6 @@
 
 namespace bitnet {
 
-// Weight loads go through the global address space explicitly: pointers read
-// from a plan descriptor are otherwise generic (FLAT) accesses, which also count
-// against the LDS wait counter and would serialise them with the LDS reads.
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(1))) const v4u gv4u;
-
-__device__ __forceinline__ uint4 gload16(const void *p) {
-    const v4u v = *(gv4u *)p;
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-template <bool NT>
-__device__ __forceinline__ uint4 load_weights(const uint8_t *p) {
-    if (NT) {
-        const v4u v = __builtin_nontemporal_load((gv4u *)p);
-        return make_uint4(v.x, v.y, v.z, v.w);
-    }
-    return gload16(p);
-}
-
 // ---------------------------------------------------------------------------
 // LDS-staged variant (used whenever MT x K fits the LDS budget).  A workgroup of
 // 4 wavefronts shares one M tile of q: the prologue loads it once, rearranges each

@@ -10,9 +10,13 @@ namespace bitnet {
 constexpr uint32_t kPlanMagic = 0xB17E7A01u;
 constexpr uint32_t kPlanLinear = 1, kPlanQuant = 2;
 
+// Linear plan variants: one block per (row block, token) running the GEMV, or one
+// block per row block running the MFMA decode kernel for all tokens at once.
+constexpr uint32_t kVariantGemv = 0, kVariantMfma = 1;
+
 struct PlanHeader {            // 64 bytes
     uint32_t magic, kind, count, total_blocks;
-    uint32_t block_threads, rows_per_block, lds_bytes, reserved1;
+    uint32_t block_threads, rows_per_block, lds_bytes, variant;
     uint64_t desc_offset, table_offset, total_bytes, reserved2;
 };
 
@@ -41,6 +45,11 @@ hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t l
 uint32_t gemv_grouped_lds_bytes(int64_t K);
 uint32_t gemv_grouped_rows_per_block();
 uint32_t gemv_grouped_threads();
+hipError_t launch_skinny(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
+                         int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st);
+hipError_t launch_skinny_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st);
+uint32_t skinny_grouped_rows_per_block();
+uint32_t skinny_grouped_lds_bytes(int64_t M);
 hipError_t launch_gemm(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                        int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st);
 hipError_t launch_gemm_cfg(int cfg, const int8_t *q, const float *s_x, const uint8_t *packed,

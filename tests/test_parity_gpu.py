@@ -165,6 +165,25 @@ def test_gemv_parity_shapes(M, N, K):
     check_linear(q, s, packed, s_w)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 300, 2624), (2, 70, 26176), (3, 200, 64), (5, 33, 8192),
+                                   (8, 1000, 6912), (11, 129, 2560), (16, 65, 28672), (17, 97, 640),
+                                   (40, 300, 1024)])
+def test_mfma_decode_kernel(M, N, K):
+    """The MFMA decode kernel, forced: ragged N, K slices with ragged tails, M below
+    and above one 16-token tile."""
+    key = synth.stream_key(308, M, N, K)
+    x, q, s = quantized_inputs(key, M, K, row_scale=(0.1, 10.0))
+    packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
+    acc_ref, y_ref = oracle.linear(q, s, packed, np.float32(0.0117))
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    tw.bitnet_linear_select(torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV),
+                            torch.from_numpy(packed).to(DEV), torch.tensor([0.0117], device=DEV),
+                            y, acc, 4)
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    assert_y(y.cpu().numpy(), y_ref)
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 200, 53312), (2, 70, 26176), (3, 200, 16704), (8, 200, 16704),
                                    (13, 130, 8192), (16, 65, 28672)])
 def test_gemv_parity_k_segments(M, N, K):
@@ -177,10 +196,15 @@ def test_gemv_parity_k_segments(M, N, K):
     check_linear(q, s, packed, s_w)
 
 
-def test_grouped_linear_mixed_k():
-    """One grouped GEMV launch over problems with different M, N and K, one of
-    whose K needs two LDS segments; every output is compared."""
-    shapes = [(1, 300, 2560), (3, 129, 53312), (1, 64, 64), (16, 97, 6912), (2, 700, 640)]
+@pytest.mark.parametrize("shapes", [
+    # M = 1 everywhere: the GEMV variant; one K needs two LDS segments
+    [(1, 300, 2560), (1, 129, 53312), (1, 64, 64), (1, 97, 6912), (1, 700, 640)],
+    # some M > 1: the MFMA variant for every problem, M = 1 included
+    [(1, 300, 2560), (3, 129, 53312), (1, 64, 64), (16, 97, 6912), (2, 700, 640)],
+])
+def test_grouped_linear_mixed_k(shapes):
+    """One grouped launch over problems with different M, N and K; every output is
+    compared."""
     probs, refs = [], []
     for i, (M, N, K) in enumerate(shapes):
         key = synth.stream_key(303, i)
