@@ -104,6 +104,9 @@ __device__ __forceinline__ void gemv_lds_tile(const int8_t *__restrict__ q, cons
         for (int m = 0; m < MT; ++m) { hi[g][m] = 0; lo[g][m] = 0u; }
     }
     if (tid < MT) sq[tid] = 0;
+    // chunk offset of this lane's rows within their 128-byte line (the same for all
+    // RG groups: their rows differ by multiples of 8)
+    const int line_off = (int)((((uint32_t)(row0 + rs) & 7u) * ((uint32_t)(KB >> 4) & 7u)) & 7u);
 
     // K is walked in segments of seg_chunks 64-weight chunks; the q tile of a segment
     // (MT rows) is what LDS holds, so any K and M tile fit the LDS budget.
@@ -112,22 +115,27 @@ __device__ __forceinline__ void gemv_lds_tile(const int8_t *__restrict__ q, cons
         const int cb = s0 + (int)(((int64_t)sc * slice) / kslices);
         const int ce = s0 + (int)(((int64_t)sc * (slice + 1)) / kslices);
 
-        // Chunk t of this lane is c = cb + l8 + 8 t, t < T (T uniform across the
-        // wavefront; lanes past the slice end load a clamped in-range chunk and use
-        // all-zero codes, which add nothing).  Two register buffers alternate so that
-        // the loads of chunk t + 1 are in flight while chunk t is being consumed.
-        const int T = (ce - cb + 7) >> 3;
+        // Step t of the octet reads one aligned 128-byte line of its row: lane l8 takes
+        // 16-byte slot l8 of line t, i.e. chunk c0 + 8 t + l8 with c0 = the chunk at
+        // the start of the line holding chunk cb (rows may start mid-line: for
+        // K = 6912 odd rows start 64 bytes into a line).  Lanes whose chunk falls
+        // outside [cb, ce) load a clamped in-range chunk and use all-zero codes, which
+        // add nothing; an unaligned start costs one more step.  Two register buffers
+        // alternate so that the loads of step t + 1 are in flight during step t.
+        const int c0 = ((line_off + cb) & ~7) - line_off;
+        const bool aligned = ((KB >> 4) & 7) == 0 && (cb & 7) == 0;
+        const int T = ((ce - cb + 7) >> 3) + (aligned ? 0 : 1);
         const int clast = max(ce - 1, cb);
         uint4 bufA[RG], bufB[RG];
         auto issue = [&](uint4 (&b)[RG], int t) {
-            const int cc = min(cb + l8 + 8 * t, clast);
+            const int cc = min(max(c0 + l8 + 8 * t, cb), clast);
             #pragma unroll
             for (int g = 0; g < RG; ++g) b[g] = load_weights<NT>(prow[g] + 16 * cc);
         };
         auto consume = [&](const uint4 (&b)[RG], int t) {
-            const int craw = cb + l8 + 8 * t;
-            const bool valid = craw < ce;
-            const int cc = min(craw, clast) - s0;
+            const int craw = c0 + l8 + 8 * t;
+            const bool valid = craw >= cb && craw < ce;
+            const int cc = min(max(craw, cb), clast) - s0;
             #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 if (m < mcount) {
