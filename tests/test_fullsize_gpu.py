@@ -70,6 +70,11 @@ def test_decode_step_grouped():
         probs.append((qs[m.layer][m.slot], sxs[m.layer][m.slot], packed[i], sws[i], y, acc))
     lplan = tw.bitnet_grouped_plan_linear(probs)
     qplan.launch()
+    for _ in range(4):   # repeated launches of one plan (the work counters reset each time)
+        lplan.launch()
+    torch.cuda.synchronize()
+    for y in ys:
+        y.fill_(float("nan"))
     lplan.launch()
     torch.cuda.synchronize()
     for y in ys:

@@ -217,11 +217,17 @@ def test_grouped_linear_mixed_k(shapes):
         probs.append((torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV), torch.from_numpy(packed).to(DEV),
                       torch.tensor([s_w], dtype=torch.float32, device=DEV), y, acc))
     plan = tw.bitnet_grouped_plan_linear(probs)
-    plan.launch()
-    torch.cuda.synchronize()
-    for (acc_ref, y_ref), pr in zip(refs, probs):
-        assert np.array_equal(pr[5].cpu().numpy(), acc_ref)
-        assert_y(pr[4].cpu().numpy(), y_ref)
+    # several launches of one plan in stream order (the GEMV variant's work counters
+    # must be back at zero after each launch), outputs cleared in between
+    for _ in range(3):
+        for pr in probs:
+            pr[4].fill_(float("nan"))
+            pr[5].fill_(-1)
+        plan.launch()
+        torch.cuda.synchronize()
+        for (acc_ref, y_ref), pr in zip(refs, probs):
+            assert np.array_equal(pr[5].cpu().numpy(), acc_ref)
+            assert_y(pr[4].cpu().numpy(), y_ref)
 
 
 @pytest.mark.parametrize("M,N,K", [(17, 129, 256), (32, 300, 2560), (64, 6912, 2560), (130, 257, 640),
