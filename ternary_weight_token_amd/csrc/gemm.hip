@@ -33,10 +33,14 @@ typedef __attribute__((address_space(1))) const v4u_g gv4u_g;
 // tiles per wave in M and N, 64-k substeps per barrier step
 #ifndef BITNET_GEMM_CFG0
 #define BITNET_GEMM_CFG0 4, 2, 4, 7, 2
+#endif
+#ifndef BITNET_GEMM_CFG0_K64
 #define BITNET_GEMM_CFG0_K64 4, 2, 4, 7, 1
 #endif
 #ifndef BITNET_GEMM_CFG1
 #define BITNET_GEMM_CFG1 8, 1, 2, 5, 2
+#endif
+#ifndef BITNET_GEMM_CFG1_K64
 #define BITNET_GEMM_CFG1_K64 8, 1, 2, 5, 1
 #endif
 
