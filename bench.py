@@ -125,24 +125,21 @@ def main() -> int:
         sws.append(s)
         del w
     xs = [W.decode_step_activations(l, dev) for l in range(30)]
-    qs = [[torch.empty((1, x.shape[1]), dtype=torch.int8, device=dev) for x in xl] for xl in xs]
-    sxs = [[torch.empty(1, dtype=torch.float32, device=dev) for _ in xl] for xl in xs]
     ys = [torch.empty((1, m.N), dtype=torch.float32, device=dev) for m in mats]
-    qplan = tw.bitnet_grouped_plan_quant([(xs[l][s], qs[l][s], sxs[l][s]) for l in range(30) for s in range(4)])
-    lplan = tw.bitnet_grouped_plan_linear(
-        [(qs[m.layer][m.slot], sxs[m.layer][m.slot], packed[i], sws[i], ys[i], None) for i, m in enumerate(mats)])
+    # the step: one fused launch (activation quantization inside the GEMV workgroups)
+    fplan = tw.bitnet_grouped_plan_fused(
+        [(xs[m.layer][m.slot], packed[i], sws[i], ys[i], None, None, None) for i, m in enumerate(mats)])
     torch.cuda.synchronize()
     weight_bytes = sum(m.N * m.K // 4 for m in mats)
     n_weights = sum(m.N * m.K for m in mats)
-    # algorithmic bytes of one grouped GEMV launch: 0.25 B per weight, 1 B per q
-    # element read, 4 B per output, 4 B per s_x read, 4 B per s_w read
-    gemv_bytes = weight_bytes + sum(m.K + 4 * m.N + 8 for m in mats)
+    # algorithmic bytes of one fused launch: 0.25 B per weight, 2 B per x element read
+    # (once per matrix), 4 B per output, 4 B per s_w read
+    fused_bytes = weight_bytes + sum(2 * m.K + 4 * m.N + 4 for m in mats)
     log(f"decode step ready in {time.time() - t0:.1f}s: {len(mats)} matrices, {weight_bytes} packed bytes")
 
     # ------------------------------------------------------------ timed region
     for _ in range(args.warmup):
-        qplan.launch(stream)
-        lplan.launch(stream)
+        fplan.launch(stream)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -150,20 +147,19 @@ def main() -> int:
     w0 = time.perf_counter()
     e_start.record(stream)
     for i in range(args.steps):
-        qplan.launch(stream)
         ev[i][0].record(stream)
-        lplan.launch(stream)
+        fplan.launch(stream)
         ev[i][1].record(stream)
     e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_per_step = wall * 1e3 / args.steps
     ev_ms_per_step = e_start.elapsed_time(e_end) / args.steps
-    gemv_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     value = weight_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = gemv_bytes / (gemv_ms * 1e-3) / 1e9
+    achieved = fused_bytes / (kern_ms * 1e-3) / 1e9
     log(f"step {ms_per_step * 1e3:.1f} us wall ({ev_ms_per_step * 1e3:.1f} us events), "
-        f"grouped GEMV {gemv_ms * 1e3:.1f} us -> {achieved:.0f} GB/s")
+        f"fused quant + GEMV launch {kern_ms * 1e3:.1f} us -> {achieved:.0f} GB/s")
     # sanity: outputs of the last step are finite
     for y in ys:
         assert torch.isfinite(y).all()
@@ -183,27 +179,56 @@ def main() -> int:
         "data": "synthetic (seeded SplitMix64 inputs generated in HBM)",
         "config": {
             "workload": "decode step: 30 x 2.4B-shaped layers {q,k,v,o,gate,up,down}, M=1, "
-                        "grouped quant + grouped GEMV launch per step",
+                        "one fused launch per step (activation quantization + ternary GEMV + rescale)",
             "matrices": len(mats), "weights": n_weights, "packed_bytes": weight_bytes,
             "hbm_frac_of_value": round(value / HBM_PEAK_GBS, 4),
             "weights_per_s": round(n_weights / (ms_per_step * 1e-3), 1),
         },
         "roofline": {
-            "kernel": "gemv_grouped_kernel",
+            "kernel": "gemv_fused_grouped_kernel",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": committed_traffic("gemv_grouped_kernel", "decode_step_2p4b"),
-            "algorithmic_bytes_per_launch": gemv_bytes,
-            "avg_launch_us": round(gemv_ms * 1e3, 2),
+            "traffic": committed_traffic("gemv_fused_grouped_kernel", "decode_step_2p4b"),
+            "algorithmic_bytes_per_launch": fused_bytes,
+            "avg_launch_us": round(kern_ms * 1e3, 2),
         },
     }
 
     # ------------------------------------------------------------ secondary legs
     if not args.no_secondary:
         sec = {}
+        # the same step as two launches: grouped quantization, then grouped GEMV on q
+        qs = [[torch.empty((1, x.shape[1]), dtype=torch.int8, device=dev) for x in xl] for xl in xs]
+        sxs = [[torch.empty(1, dtype=torch.float32, device=dev) for _ in xl] for xl in xs]
+        qplan = tw.bitnet_grouped_plan_quant([(xs[l][j], qs[l][j], sxs[l][j]) for l in range(30) for j in range(4)])
+        lplan = tw.bitnet_grouped_plan_linear(
+            [(qs[m.layer][m.slot], sxs[m.layer][m.slot], packed[i], sws[i], ys[i], None) for i, m in enumerate(mats)])
+        gemv_bytes = weight_bytes + sum(m.K + 4 * m.N + 8 for m in mats)
+        for _ in range(10):
+            qplan.launch(stream)
+            lplan.launch(stream)
+        torch.cuda.synchronize()
+        evq = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(100)]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(100):
+            qplan.launch(stream)
+            evq[i][0].record(stream)
+            lplan.launch(stream)
+            evq[i][1].record(stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        step_us = a.elapsed_time(b) * 1e3 / 100
+        g_us = float(np.mean([x.elapsed_time(y) for x, y in evq])) * 1e3
+        sec["decode_step_2p4b_two_launches"] = {
+            "us": round(step_us, 1), "weight_GBs": round(weight_bytes / (step_us * 1e-6) / 1e9, 1),
+            "gemv_grouped_kernel_us": round(g_us, 2),
+            "gemv_grouped_kernel_GBs": round(gemv_bytes / (g_us * 1e-6) / 1e9, 1)}
+        log(f"two-launch step: {step_us:.1f} us (grouped GEMV {g_us:.1f} us)")
+        del qs, sxs, qplan, lplan
         # prefill GEMM, M = 2048
         reps = 50
         for name in ("up", "down"):

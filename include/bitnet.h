@@ -199,6 +199,36 @@ BITNET_API int bitnet_grouped_plan_quant(const bitnet_quant_desc *descs, int cou
 BITNET_API int bitnet_linear_grouped(const void *plan_host, const void *plan_dev, void *stream);
 BITNET_API int bitnet_quant_act_grouped(const void *plan_host, const void *plan_dev, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Fused decode step: activation quantization and linear in one grouped launch
+ * (pages: chenxutan.com sec. 2.2 absmax_quantize and sec. 3.1 BitLinear.forward,
+ * whose forward quantizes the input on entry; sec. 5.3 item 4 on fusing the
+ * steps around the product).  For every descriptor (one token, M = 1) the result
+ * is bit-identical to bitnet_quant_act(x) followed by bitnet_linear(q, s_x, ...):
+ * every workgroup of the problem quantizes the row itself while staging it, so no
+ * q round trip through memory and no second launch are needed.  q and s_x are
+ * optional outputs (written once, by one workgroup).
+ *
+ * Descriptors: M = 1, K % 64 == 0, K <= 52224 (the row's q fits one LDS
+ * segment), x / packed / q 16-byte aligned.  Plans are built and launched like
+ * the other grouped plans (host image + device copy).
+ * ------------------------------------------------------------------------- */
+typedef struct bitnet_fused_desc {
+    const uint16_t *x;      /* (device) [M][K] bf16 bits */
+    const uint8_t *packed;  /* (device) [N][K/4] */
+    const float *s_w;       /* (device) [1] */
+    float *y;               /* (device) [M][N] */
+    int32_t *acc;           /* (device) [M][N] or NULL */
+    int8_t *q;              /* (device) [M][K] or NULL */
+    float *s_x;             /* (device) [M] or NULL */
+    int64_t M, N, K;
+} bitnet_fused_desc;
+
+BITNET_API size_t bitnet_grouped_plan_fused_bytes(int count, const bitnet_fused_desc *descs);
+BITNET_API int bitnet_grouped_plan_fused(const bitnet_fused_desc *descs, int count,
+                                         void *plan_host, size_t plan_bytes);
+BITNET_API int bitnet_linear_fused_grouped(const void *plan_host, const void *plan_dev, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,6 +29,12 @@ class _LinearDesc(ctypes.Structure):
                 ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
+class _FusedDesc(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("packed", ctypes.c_void_p), ("s_w", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("acc", ctypes.c_void_p), ("q", ctypes.c_void_p),
+                ("s_x", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
 class _QuantDesc(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("q", ctypes.c_void_p), ("s_x", ctypes.c_void_p),
                 ("M", ctypes.c_int64), ("K", ctypes.c_int64)]
@@ -59,9 +65,13 @@ def lib() -> ctypes.CDLL:
         L.bitnet_grouped_plan_quant.argtypes = [P, I, P, ctypes.c_size_t]
         L.bitnet_linear_grouped.argtypes = [P, P, P]
         L.bitnet_quant_act_grouped.argtypes = [P, P, P]
+        L.bitnet_grouped_plan_fused_bytes.argtypes = [I, P]
+        L.bitnet_grouped_plan_fused_bytes.restype = ctypes.c_size_t
+        L.bitnet_grouped_plan_fused.argtypes = [P, I, P, ctypes.c_size_t]
+        L.bitnet_linear_fused_grouped.argtypes = [P, P, P]
         for f in ("bitnet_pack_weights", "bitnet_quant_act", "bitnet_linear", "bitnet_linear_select",
-                  "bitnet_grouped_plan_linear", "bitnet_grouped_plan_quant",
-                  "bitnet_linear_grouped", "bitnet_quant_act_grouped"):
+                  "bitnet_grouped_plan_linear", "bitnet_grouped_plan_quant", "bitnet_grouped_plan_fused",
+                  "bitnet_linear_grouped", "bitnet_quant_act_grouped", "bitnet_linear_fused_grouped"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -163,7 +173,8 @@ class GroupedPlan:
         self._refs = refs  # keep the described tensors alive
 
     def launch(self, stream=None) -> None:
-        f = lib().bitnet_linear_grouped if self.kind == "linear" else lib().bitnet_quant_act_grouped
+        f = {"linear": lib().bitnet_linear_grouped, "quant": lib().bitnet_quant_act_grouped,
+             "fused": lib().bitnet_linear_fused_grouped}[self.kind]
         _check(f(ctypes.cast(self.host, ctypes.c_void_p), _ptr(self.dev), _stream(stream)))
 
 
@@ -200,6 +211,27 @@ def bitnet_grouped_plan_quant(problems, device=None) -> GroupedPlan:
     host = buf.raw
     dev = torch.frombuffer(bytearray(host), dtype=torch.uint8).to(device or problems[0][0].device)
     return GroupedPlan(host, dev, "quant", refs)
+
+
+def bitnet_grouped_plan_fused(problems, device=None) -> GroupedPlan:
+    """problems: list of (x, packed, s_w, y, acc_or_None, q_or_None, s_x_or_None); x is
+    bf16 [1][K] (quantized inside the launch)."""
+    arr = (_FusedDesc * len(problems))()
+    refs = []
+    for i, (x, packed, s_w, y, acc, q, s_x) in enumerate(problems):
+        _dev(x, torch.bfloat16, "x")
+        M, K = x.shape
+        arr[i] = _FusedDesc(x.data_ptr(), packed.data_ptr(), s_w.data_ptr(), y.data_ptr(),
+                            0 if acc is None else acc.data_ptr(), 0 if q is None else q.data_ptr(),
+                            0 if s_x is None else s_x.data_ptr(), M, packed.shape[0], K)
+        refs.append((x, packed, s_w, y, acc, q, s_x))
+    n = lib().bitnet_grouped_plan_fused_bytes(len(problems), ctypes.cast(arr, ctypes.c_void_p))
+    buf = ctypes.create_string_buffer(n)
+    _check(lib().bitnet_grouped_plan_fused(ctypes.cast(arr, ctypes.c_void_p), len(problems),
+                                           ctypes.cast(buf, ctypes.c_void_p), n))
+    host = buf.raw
+    dev = torch.frombuffer(bytearray(host), dtype=torch.uint8).to(device or problems[0][0].device)
+    return GroupedPlan(host, dev, "fused", refs)
 
 
 # ----------------------------------------------------------------- conveniences

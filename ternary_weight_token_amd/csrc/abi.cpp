@@ -167,6 +167,19 @@ static int check_linear_desc(const bitnet_linear_desc &d) {
     return BITNET_OK;
 }
 
+static int check_fused_desc(const bitnet_fused_desc &d) {
+    int st = check_dims(d.M, d.N, d.K);
+    if (st) return st;
+    if (d.M != 1 || d.N < 1) return fail(BITNET_ERR_SHAPE, "fused linear needs M == 1, N >= 1");
+    if (!d.x || !d.packed || !d.s_w || !d.y) return fail(BITNET_ERR_NULL, "null pointer");
+    if (d.K > gemv_fused_max_k()) return fail(BITNET_ERR_SHAPE, "fused linear needs K <= 52224");
+    if (d.K % 64 != 0 || !aligned(d.x, 16) || !aligned(d.packed, 16) || (d.q && !aligned(d.q, 16)))
+        return fail(BITNET_ERR_ALIGN, "fused linear needs K % 64 == 0 and 16-byte aligned x, packed and q");
+    if (!aligned(d.s_w, 4) || !aligned(d.y, 4) || (d.acc && !aligned(d.acc, 4)) || (d.s_x && !aligned(d.s_x, 4)))
+        return fail(BITNET_ERR_ALIGN, "s_w, y, acc and s_x must be 4-byte aligned");
+    return BITNET_OK;
+}
+
 static int check_quant_desc(const bitnet_quant_desc &d) {
     int st = check_dims(d.M, 1, d.K);
     if (st) return st;
@@ -280,6 +293,63 @@ BITNET_API int bitnet_grouped_plan_quant(const bitnet_quant_desc *descs, int cou
     return BITNET_OK;
 }
 
+static uint64_t fused_blocks(const bitnet_fused_desc &d) {
+    const uint64_t rows = gemv_grouped_rows_per_block();
+    return ((uint64_t)d.N + rows - 1) / rows;
+}
+
+BITNET_API size_t bitnet_grouped_plan_fused_bytes(int count, const bitnet_fused_desc *descs) {
+    if (count <= 0 || !descs) return 0;
+    uint64_t blocks = 0, a, b;
+    for (int i = 0; i < count; ++i) blocks += descs[i].N > 0 ? fused_blocks(descs[i]) : 0;
+    return plan_layout(count, sizeof(FusedDescDev), blocks, &a, &b);
+}
+
+BITNET_API int bitnet_grouped_plan_fused(const bitnet_fused_desc *descs, int count, void *plan_host,
+                                         size_t plan_bytes) {
+    if (!descs || !plan_host) return fail(BITNET_ERR_NULL, "null pointer");
+    if (count <= 0) return fail(BITNET_ERR_SHAPE, "count must be positive");
+    uint64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        int st = check_fused_desc(descs[i]);
+        if (st) return st;
+        blocks += fused_blocks(descs[i]);
+    }
+    if (blocks >= ((uint64_t)1 << 31)) return fail(BITNET_ERR_SHAPE, "too many blocks");
+    uint64_t doff, toff;
+    const size_t need = plan_layout(count, sizeof(FusedDescDev), blocks, &doff, &toff);
+    if (plan_bytes < need) return fail(BITNET_ERR_ARG, "plan buffer too small");
+    uint8_t *p = (uint8_t *)plan_host;
+    memset(p, 0, need);
+    PlanHeader *h = (PlanHeader *)p;
+    h->magic = kPlanMagic;
+    h->kind = kPlanFused;
+    h->count = (uint32_t)count;
+    h->total_blocks = (uint32_t)blocks;
+    h->block_threads = gemv_grouped_threads();
+    h->rows_per_block = gemv_grouped_rows_per_block();
+    for (int i = 0; i < count; ++i) h->lds_bytes = std::max(h->lds_bytes, gemv_grouped_lds_bytes(descs[i].K));
+    h->desc_offset = doff;
+    h->table_offset = toff;
+    h->total_bytes = need;
+    FusedDescDev *dd = (FusedDescDev *)(p + doff);
+    BlockEntry *tb = (BlockEntry *)(p + toff);
+    for (int i = 0; i < count; ++i) {
+        const bitnet_fused_desc &d = descs[i];
+        dd[i] = FusedDescDev{d.x, d.packed, d.s_w, d.y, d.acc, d.q, d.s_x, (int32_t)d.M, (int32_t)d.N, (int32_t)d.K, 0};
+    }
+    // longest rows first, as for linear plans
+    std::vector<int> order(count);
+    for (int i = 0; i < count; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return descs[a].K > descs[b].K; });
+    uint64_t b = 0;
+    for (int i : order) {
+        const uint64_t nb = fused_blocks(descs[i]);
+        for (uint64_t j = 0; j < nb; ++j) tb[b++] = BlockEntry{(uint32_t)i, (uint32_t)j};
+    }
+    return BITNET_OK;
+}
+
 static int check_plan(const void *plan_host, const void *plan_dev, uint32_t kind) {
     if (!plan_host || !plan_dev) return fail(BITNET_ERR_NULL, "null plan");
     if (!aligned(plan_dev, 16)) return fail(BITNET_ERR_ALIGN, "device plan must be 16-byte aligned");
@@ -297,6 +367,14 @@ BITNET_API int bitnet_linear_grouped(const void *plan_host, const void *plan_dev
         return hip_status(launch_skinny_grouped(plan_dev, h->total_blocks, h->lds_bytes, (hipStream_t)stream));
     if (h->variant != kVariantGemv) return fail(BITNET_ERR_ARG, "not a plan of this kind");
     return hip_status(launch_gemv_grouped(plan_dev, h->total_blocks, h->lds_bytes, (hipStream_t)stream));
+}
+
+BITNET_API int bitnet_linear_fused_grouped(const void *plan_host, const void *plan_dev, void *stream) {
+    int st = check_plan(plan_host, plan_dev, kPlanFused);
+    if (st) return st;
+    const PlanHeader *h = (const PlanHeader *)plan_host;
+    if (h->total_blocks == 0) return BITNET_OK;
+    return hip_status(launch_gemv_fused_grouped(plan_dev, h->total_blocks, h->lds_bytes, (hipStream_t)stream));
 }
 
 BITNET_API int bitnet_quant_act_grouped(const void *plan_host, const void *plan_dev, void *stream) {

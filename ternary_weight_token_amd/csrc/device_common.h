@@ -109,6 +109,58 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
+// bf16 bits -> float (exact).
+__device__ __forceinline__ float bf16f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Activation code of x for the row scale s = max|x| > 0 (page chenxutan.com sec. 2.2,
+// absmax_quantize, 8 bits): rint((127 x) / s) clamped to [-127, 127].  127 x is exact
+// in binary32 for bf16 x and the division is the correctly rounded IEEE one.
+__device__ __forceinline__ int qcode(float x, float s) {
+    float v = (127.0f * x) / s;
+    float r = __builtin_rintf(v);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+// Largest bf16 magnitude bits (|x| with the sign cleared) among the 8 values of a
+// 16-byte vector: an integer max, exact and order-free.
+__device__ __forceinline__ uint32_t absmax8(uint4 u) {
+    const uint32_t a = max(u.x & 0x7FFFu, u.x >> 16 & 0x7FFFu);
+    const uint32_t b = max(u.y & 0x7FFFu, u.y >> 16 & 0x7FFFu);
+    const uint32_t c = max(u.z & 0x7FFFu, u.z >> 16 & 0x7FFFu);
+    const uint32_t d = max(u.w & 0x7FFFu, u.w >> 16 & 0x7FFFu);
+    return max(max(a, b), max(c, d));
+}
+
+// The same code with inv = 1 / s (correctly rounded) computed once per row: the
+// product (127 x) * inv lies within 1.6e-5 of the exact quotient (|quotient| <= 127,
+// two roundings of 2^-24 relative each), so its nearest integer is the exact one
+// whenever it is at least 4e-5 away from a half-integer -- and then the binary32
+// quotient, within 4e-6 of the exact one, rounds to that integer too.  Otherwise
+// (about one code in a thousand, and never for an overflowing or non-finite
+// product) the correctly rounded division decides.  An exhaustive test over all
+// bf16 inputs checks the result against the plain definition.
+__device__ __forceinline__ int qcode_inv(float x, float s, float inv) {
+    const float a = 127.0f * x;
+    const float t = a * inv;
+    float r = __builtin_rintf(t);
+    if (!(fabsf(t - r) < 0.49996f)) r = __builtin_rintf(a / s);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+// Codes of 8 bf16 values (one 16-byte vector) packed into 8 bytes; inv = 1 / s.
+__device__ __forceinline__ uint2 qcode8(uint4 u, float s, float inv) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    uint32_t b[8];
+    #pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        b[2 * j] = (uint32_t)qcode_inv(bf16f(w[j] & 0xFFFFu), s, inv) & 0xFFu;
+        b[2 * j + 1] = (uint32_t)qcode_inv(bf16f(w[j] >> 16), s, inv) & 0xFFu;
+    }
+    return make_uint2(b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24, b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24);
+}
+
 // y = fp32(acc * c) with c = (s_x * s_w) / 127 formed in float64.
 __device__ __forceinline__ double rescale_factor(float s_x, float s_w) {
     return ((double)s_x * (double)s_w) / 127.0;

@@ -75,8 +75,104 @@ __device__ __forceinline__ void mac16(uint32_t w, uint4 pq, int &hi, uint32_t &l
     }
 }
 
-template <int MT, int RG, bool DOT8, bool NT>
-__device__ __forceinline__ void gemv_lds_tile(const int8_t *__restrict__ q, const float *__restrict__ s_x,
+// q staging for one K segment (chunks s0 .. s0 + sc - 1) of an M tile (rows m0 ..
+// m0 + mcount - 1): each 16-byte piece rearranged for the dot products into LDS
+// (qs, 80 bytes per 64-value chunk) and sum_k q per row added to sq.  Called by
+// every thread of the workgroup between two barriers.
+
+// From int8 q in global memory.
+template <int MT, bool DOT8>
+struct StageQ {
+    const int8_t *q;
+    int K;
+    __device__ __forceinline__ void operator()(int s0, int sc, int m0, int mcount, int seg_chunks, uint32_t *qs,
+                                               int *sq) const {
+        const int tid = threadIdx.x;
+        int part[MT];
+        #pragma unroll
+        for (int m = 0; m < MT; ++m) part[m] = 0;
+        const int pieces = sc * 4;  // 16-byte pieces per row of q in this segment
+        for (int idx = tid; idx < mcount * pieces; idx += blockDim.x) {
+            const int m = idx / pieces, r = idx - m * pieces;
+            const uint4 a = gload16(q + (size_t)(m0 + m) * K + 64 * s0 + 16 * r);
+            const int c = r >> 2, d = r & 3;
+            *reinterpret_cast<uint4 *>(qs + (m * seg_chunks + c) * kLdsChunkDw + 4 * d) = prep16<DOT8>(a);
+            int sm = dot4(a.x, 0x01010101u, 0);
+            sm = dot4(a.y, 0x01010101u, sm);
+            sm = dot4(a.z, 0x01010101u, sm);
+            sm = dot4(a.w, 0x01010101u, sm);
+            #pragma unroll
+            for (int mm = 0; mm < MT; ++mm) part[mm] += (mm == m) ? sm : 0;
+        }
+        #pragma unroll
+        for (int m = 0; m < MT; ++m)
+            if (m < mcount && part[m] != 0) atomicAdd(&sq[m], part[m]);
+    }
+};
+
+// From the bf16 activation row itself (one token, K in one segment): the
+// quantization of bitnet_quant_act done in the workgroup (page chenxutan.com
+// sec. 2.2, absmax_quantize): s = max|x| (integer max of the bf16 magnitude bits),
+// q = rint((127 x) / s), all zero for an all-zero row.  The row scale goes to LDS
+// (*s_lds) for the epilogue; q and s are also written out when q_out / s_out are set.
+template <bool DOT8>
+struct StageQuantize {
+    const uint16_t *x;   // [K] bf16 bits, 16-byte aligned
+    int8_t *q_out;       // [K] or nullptr
+    float *s_out;        // or nullptr
+    float *s_lds;        // LDS
+    uint32_t *red;       // LDS, one word per wavefront (4)
+    __device__ __forceinline__ void operator()(int, int sc, int, int, int, uint32_t *qs, int *sq) const {
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int pieces = sc * 4;  // pieces of 16 values (32 bytes of x)
+        // the first two pieces of each thread stay in registers (K <= 8192)
+        uint4 xr[2][2];
+        uint32_t mx = 0;
+        #pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = min(tid + 256 * j, pieces - 1);   // clamped duplicates leave the max as it is
+            xr[j][0] = gload16(x + 16 * r);
+            xr[j][1] = gload16(x + 16 * r + 8);
+            mx = max(mx, max(absmax8(xr[j][0]), absmax8(xr[j][1])));
+        }
+        for (int r = tid + 512; r < pieces; r += 256)
+            mx = max(mx, max(absmax8(gload16(x + 16 * r)), absmax8(gload16(x + 16 * r + 8))));
+        mx = wave_max_u32(mx);
+        if (lane == 0) red[wave] = mx;
+        __syncthreads();
+        mx = max(max(red[0], red[1]), max(red[2], red[3]));
+        const float s = bf16f(mx);
+        const float inv = 1.0f / s;
+        if (tid == 0) {
+            *s_lds = s;
+            if (s_out) *s_out = s;
+        }
+        int part = 0;
+        auto emit = [&](int r, uint4 u0, uint4 u1) {
+            uint4 a = make_uint4(0u, 0u, 0u, 0u);
+            if (mx != 0) {
+                const uint2 lo = qcode8(u0, s, inv), hi = qcode8(u1, s, inv);
+                a = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+            if (q_out) *reinterpret_cast<uint4 *>(q_out + 16 * r) = a;
+            *reinterpret_cast<uint4 *>(qs + (r >> 2) * kLdsChunkDw + 4 * (r & 3)) = prep16<DOT8>(a);
+            int sm = dot4(a.x, 0x01010101u, 0);
+            sm = dot4(a.y, 0x01010101u, sm);
+            sm = dot4(a.z, 0x01010101u, sm);
+            part += dot4(a.w, 0x01010101u, sm);
+        };
+        #pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = tid + 256 * j;
+            if (r < pieces) emit(r, xr[j][0], xr[j][1]);
+        }
+        for (int r = tid + 512; r < pieces; r += 256) emit(r, gload16(x + 16 * r), gload16(x + 16 * r + 8));
+        if (part != 0) atomicAdd(&sq[0], part);
+    }
+};
+
+template <int MT, int RG, bool DOT8, bool NT, class Stage>
+__device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *__restrict__ s_x,
                                               const uint8_t *__restrict__ packed,
                                               const float *__restrict__ s_w, int M, int N, int K,
                                               float *__restrict__ y, int32_t *__restrict__ acc_out,
@@ -159,27 +255,7 @@ __device__ __forceinline__ void gemv_lds_tile(const int8_t *__restrict__ q, cons
 
         // ---- stage the segment of the M tile of q, rearranged, and its row sums
         __syncthreads();   // previous segment's LDS reads done; sq initialised
-        {
-            int part[MT];
-            #pragma unroll
-            for (int m = 0; m < MT; ++m) part[m] = 0;
-            const int pieces = sc * 4;  // 16-byte pieces per row of q in this segment
-            for (int idx = tid; idx < mcount * pieces; idx += blockDim.x) {
-                const int m = idx / pieces, r = idx - m * pieces;
-                const uint4 a = gload16(q + (size_t)(m0 + m) * K + 64 * s0 + 16 * r);
-                const int c = r >> 2, d = r & 3;
-                *reinterpret_cast<uint4 *>(qs + (m * seg_chunks + c) * kLdsChunkDw + 4 * d) = prep16<DOT8>(a);
-                int sm = dot4(a.x, 0x01010101u, 0);
-                sm = dot4(a.y, 0x01010101u, sm);
-                sm = dot4(a.z, 0x01010101u, sm);
-                sm = dot4(a.w, 0x01010101u, sm);
-                #pragma unroll
-                for (int mm = 0; mm < MT; ++mm) part[mm] += (mm == m) ? sm : 0;
-            }
-            #pragma unroll
-            for (int m = 0; m < MT; ++m)
-                if (m < mcount && part[m] != 0) atomicAdd(&sq[m], part[m]);
-        }
+        stage(s0, sc, m0, mcount, seg_chunks, qs, sq);
         __syncthreads();
 
         // Pairs of chunks with no branch inside the loop body, so that the compiler
@@ -263,7 +339,7 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(
     __shared__ int sq[MT];
     __shared__ int red[4 * 8 * RG * MT];
     const int rows_per_block = (4 / kslices) * 8 * RG;
-    gemv_lds_tile<MT, RG, DOT8, BITNET_GEMV_NT != 0>(q, s_x, packed, s_w, M, N, K, y, acc_out,
+    gemv_lds_tile<MT, RG, DOT8, BITNET_GEMV_NT != 0>(StageQ<MT, DOT8>{q, K}, s_x, packed, s_w, M, N, K, y, acc_out,
                                                      blockIdx.x * rows_per_block, blockIdx.y * MT, kslices,
                                                      seg_chunks, dyn, sq, red);
 }
@@ -294,8 +370,37 @@ __global__ __launch_bounds__(256) void gemv_grouped_kernel(const uint8_t *__rest
     const int rowblocks = (d.N + rows - 1) / rows;
     const int rb = (int)(e.local % rowblocks), mt = (int)(e.local / rowblocks);
     gemv_lds_tile<kGroupedMT, kGroupedRG, BITNET_GROUPED_DOT8 != 0, BITNET_GEMV_NT != 0>(
-        d.q, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, d.y, d.acc, rb * rows, mt * kGroupedMT, 1, segment_chunks(d.K >> 6, kGroupedMT), dyn,
+        StageQ<kGroupedMT, BITNET_GROUPED_DOT8 != 0>{d.q, d.K}, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, d.y, d.acc, rb * rows, mt * kGroupedMT, 1, segment_chunks(d.K >> 6, kGroupedMT), dyn,
         sq, red);
+}
+
+// Fused grouped decode: the same work items, with the activation quantization of
+// each problem's token row done by every workgroup of that problem in its q
+// staging step (one segment, so the row max covers the whole row).  The workgroup of
+// row block 0 also writes q and s_x out when the descriptor asks for them.
+__global__ __launch_bounds__(256) void gemv_fused_grouped_kernel(const uint8_t *__restrict__ plan) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+    __shared__ int sq[1];
+    __shared__ int red[4 * 8 * kGroupedRG];
+    __shared__ uint32_t qred[4];
+    __shared__ float s_lds;
+    const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
+    const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[blockIdx.x];
+    const FusedDescDev d = reinterpret_cast<const FusedDescDev *>(plan + h->desc_offset)[e.desc];
+    const int rows = 4 * 8 * kGroupedRG;
+    const bool first = e.local == 0;
+    const StageQuantize<BITNET_GROUPED_DOT8 != 0> stage{d.x, first ? d.q : nullptr, first ? d.s_x : nullptr,
+                                                         &s_lds, qred};
+    gemv_lds_tile<1, kGroupedRG, BITNET_GROUPED_DOT8 != 0, BITNET_GEMV_NT != 0>(
+        stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K, d.y, d.acc, (int)e.local * rows, 0, 1, d.K >> 6, dyn, sq, red);
+}
+
+// Longest K whose q fits one LDS segment of the grouped GEMV.
+int64_t gemv_fused_max_k() { return 64 * (int64_t)((kLdsBudget / (kLdsChunkDw * 4)) & ~7); }
+
+hipError_t launch_gemv_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st) {
+    gemv_fused_grouped_kernel<<<dim3(blocks), dim3(256), lds_bytes, st>>>(reinterpret_cast<const uint8_t *>(plan_dev));
+    return hipGetLastError();
 }
 
 uint32_t gemv_grouped_rows_per_block() { return 4 * 8 * kGroupedRG; }

@@ -8,7 +8,7 @@ namespace bitnet {
 
 // Plan image for grouped launches.
 constexpr uint32_t kPlanMagic = 0xB17E7A01u;
-constexpr uint32_t kPlanLinear = 1, kPlanQuant = 2;
+constexpr uint32_t kPlanLinear = 1, kPlanQuant = 2, kPlanFused = 3;
 
 // Linear plan variants: one block per (row block, token) running the GEMV, or one
 // block per row block running the MFMA decode kernel for all tokens at once.
@@ -31,6 +31,12 @@ struct QuantDescDev {          // 32 bytes
     int32_t M, K;
 };
 
+struct FusedDescDev {          // 72 bytes: quantization + linear of one token row
+    const uint16_t *x; const uint8_t *packed; const float *s_w;
+    float *y; int32_t *acc; int8_t *q; float *s_x;
+    int32_t M, N, K, pad;
+};
+
 struct BlockEntry { uint32_t desc, local; };
 
 // launchers (return hipError_t of the launch)
@@ -43,6 +49,8 @@ hipError_t launch_gemv(const int8_t *q, const float *s_x, const uint8_t *packed,
                        int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st);
 hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st);
 uint32_t gemv_grouped_lds_bytes(int64_t K);
+hipError_t launch_gemv_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st);
+int64_t gemv_fused_max_k();
 uint32_t gemv_grouped_rows_per_block();
 uint32_t gemv_grouped_threads();
 hipError_t launch_skinny(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,

@@ -5,22 +5,14 @@
 // bf16 magnitude bits, exact and order-free; wavefront shuffles, then LDS across
 // the 4 waves), pass 2 re-reads the row (L2-resident) and writes
 // q = rint((127 * x) / s) as int8, 8 codes per 8-byte store.  127 * x is exact
-// in binary32 for bf16 x and the division is the correctly rounded IEEE one.
+// in binary32 for bf16 x and the quotient is the correctly rounded IEEE one (the
+// vector path multiplies by 1 / s and divides only near a rounding boundary).
 #include "device_common.h"
 #include "internal.h"
 
 namespace bitnet {
 
 constexpr int kQThreads = 256;
-
-__device__ __forceinline__ float bf16f(uint32_t b) { return __uint_as_float(b << 16); }
-
-__device__ __forceinline__ int qcode(float x, float s) {
-    float v = (127.0f * x) / s;
-    float r = __builtin_rintf(v);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
-}
 
 template <bool VEC>
 __device__ __forceinline__ void quant_row(const uint16_t *__restrict__ x, int K,
@@ -30,14 +22,7 @@ __device__ __forceinline__ void quant_row(const uint16_t *__restrict__ x, int K,
     uint32_t mx = 0;
     if (VEC) {
         const uint4 *xv = reinterpret_cast<const uint4 *>(x);
-        for (int v = tid; v < (K >> 3); v += kQThreads) {
-            uint4 u = xv[v];
-            uint32_t a = max(u.x & 0x7FFFu, u.x >> 16 & 0x7FFFu);
-            uint32_t b = max(u.y & 0x7FFFu, u.y >> 16 & 0x7FFFu);
-            uint32_t c = max(u.z & 0x7FFFu, u.z >> 16 & 0x7FFFu);
-            uint32_t d = max(u.w & 0x7FFFu, u.w >> 16 & 0x7FFFu);
-            mx = max(mx, max(max(a, b), max(c, d)));
-        }
+        for (int v = tid; v < (K >> 3); v += kQThreads) mx = max(mx, absmax8(xv[v]));
     } else {
         for (int k = tid; k < K; k += kQThreads) mx = max(mx, (uint32_t)(x[k] & 0x7FFFu));
     }
@@ -46,25 +31,13 @@ __device__ __forceinline__ void quant_row(const uint16_t *__restrict__ x, int K,
     __syncthreads();
     mx = max(max(red[0], red[1]), max(red[2], red[3]));
     const float s = bf16f(mx);
+    const float inv = 1.0f / s;
     if (tid == 0) *s_out = s;
     if (VEC) {
         const uint4 *xv = reinterpret_cast<const uint4 *>(x);
         uint2 *qv = reinterpret_cast<uint2 *>(q);
         for (int v = tid; v < (K >> 3); v += kQThreads) {
-            uint2 o = make_uint2(0u, 0u);
-            if (mx != 0) {
-                uint4 u = xv[v];
-                uint32_t w[4] = {u.x, u.y, u.z, u.w};
-                uint32_t b[8];
-                #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    b[2 * j] = (uint32_t)qcode(bf16f(w[j] & 0xFFFFu), s) & 0xFFu;
-                    b[2 * j + 1] = (uint32_t)qcode(bf16f(w[j] >> 16), s) & 0xFFu;
-                }
-                o.x = b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24;
-                o.y = b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24;
-            }
-            qv[v] = o;
+            qv[v] = mx != 0 ? qcode8(xv[v], s, inv) : make_uint2(0u, 0u);
         }
     } else {
         for (int k = tid; k < K; k += kQThreads)

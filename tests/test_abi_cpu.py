@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -132,3 +132,32 @@ def test_python_binding_fails_loudly_without_gpu_tensors():
     with pytest.raises(ValueError):
         tw.bitnet_linear(q, torch.zeros(1), torch.zeros((4, 16), dtype=torch.uint8),
                          torch.zeros(1), torch.zeros((1, 4)))
+
+
+def test_fused_plan_checks(L):
+    F = tw._FusedDesc
+    a16 = 4096
+    good = F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560)
+    arr = (F * 1)(good)
+    n = L.bitnet_grouped_plan_fused_bytes(1, ctypes.cast(arr, ctypes.c_void_p))
+    buf = ctypes.create_string_buffer(n)
+    assert L.bitnet_grouped_plan_fused(ctypes.cast(arr, ctypes.c_void_p), 1, ctypes.cast(buf, ctypes.c_void_p), n) == OK
+    hdr = (ctypes.c_uint32 * 8).from_buffer_copy(buf.raw[:32])
+    assert hdr[1] == 3 and hdr[3] == (300 + 127) // 128 and hdr[5] == 128
+    assert L.bitnet_grouped_plan_fused(ctypes.cast(arr, ctypes.c_void_p), 1, ctypes.cast(buf, ctypes.c_void_p), n - 1) == ARG
+    bad = [
+        (F(a16, a16, a16, a16, 0, 0, 0, 2, 300, 2560), SHAPE),      # one token per problem
+        (F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 52224 + 64), SHAPE),  # q must fit one LDS segment
+        (F(a16 + 2, a16, a16, a16, 0, 0, 0, 1, 300, 2560), ALIGN),    # x 16-byte aligned
+        (F(a16, a16, a16, a16, 0, a16 + 8, 0, 1, 300, 2560), ALIGN),  # q 16-byte aligned
+        (F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2528), ALIGN),        # K % 64
+        (F(0, a16, a16, a16, 0, 0, 0, 1, 300, 2560), NULL),
+    ]
+    for d, want in bad:
+        one = (F * 1)(d)
+        assert L.bitnet_grouped_plan_fused(ctypes.cast(one, ctypes.c_void_p), 1, ctypes.cast(buf, ctypes.c_void_p),
+                                           n) == want, (d.M, d.K, want)
+    # a fused plan is not a linear or quant plan
+    dev = ctypes.c_void_p(4096)
+    assert L.bitnet_linear_grouped(ctypes.cast(buf, ctypes.c_void_p), dev, None) == ARG
+    assert L.bitnet_quant_act_grouped(ctypes.cast(buf, ctypes.c_void_p), dev, None) == ARG

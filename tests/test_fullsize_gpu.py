@@ -96,6 +96,41 @@ def test_decode_step_grouped():
         assert_y(ys[i].cpu().numpy(), y_ref)
 
 
+def test_decode_step_fused():
+    """The 30-layer decode step as one fused launch (quantization inside the GEMV):
+    layers 0 and 29 compared in full (q, s_x, acc, y), every other output finite."""
+    mats = W.decode_step_2p4b(30)
+    sample = {0, 29}
+    xs = [W.decode_step_activations(l, DEV) for l in range(30)]
+    probs, host = [], {}
+    for i, m in enumerate(mats):
+        w = W.weights(m, DEV)
+        p, s = tw.pack_weights(w, 1e-5)
+        if m.layer in sample:
+            host[i] = w.cpu()
+        del w
+        y = torch.full((1, m.N), float("nan"), dtype=torch.float32, device=DEV)
+        acc = torch.empty((1, m.N), dtype=torch.int32, device=DEV) if m.layer in sample else None
+        q = torch.empty((1, m.K), dtype=torch.int8, device=DEV) if m.layer in sample else None
+        sx = torch.empty(1, dtype=torch.float32, device=DEV) if m.layer in sample else None
+        probs.append((xs[m.layer][m.slot], p, s, y, acc, q, sx))
+    plan = tw.bitnet_grouped_plan_fused(probs)
+    plan.launch()
+    torch.cuda.synchronize()
+    for pr in probs:
+        assert torch.isfinite(pr[3]).all()
+    for i, m in enumerate(mats):
+        if m.layer not in sample:
+            continue
+        p_ref, sw_ref = oracle.pack(host[i].numpy(), 1e-5)
+        q_ref, sx_ref = oracle.quant_act(bits_np(xs[m.layer][m.slot]))
+        acc_ref, y_ref = oracle.linear(q_ref, sx_ref, p_ref, sw_ref)
+        x, p, s, y, acc, q, sx = probs[i]
+        assert np.array_equal(q.cpu().numpy(), q_ref) and np.array_equal(sx.cpu().numpy(), sx_ref)
+        assert np.array_equal(acc.cpu().numpy(), acc_ref), (m.layer, m.name)
+        assert_y(y.cpu().numpy(), y_ref)
+
+
 @pytest.mark.parametrize("name", ["up", "down"])
 @pytest.mark.parametrize("density", [None, 0.3, 0.5, 0.7])
 def test_prefill_sampled(name, density):

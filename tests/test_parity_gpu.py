@@ -96,6 +96,39 @@ def test_quant_act_parity(M, K, kw):
     assert np.array_equal(s, s_ref)
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_quant_act_exhaustive_bf16(fused):
+    """Every finite bf16 value x with |x| <= s, for scales s across the whole range
+    (subnormal, tiny, ordinary, large), quantized on the GPU (bitnet_quant_act, or
+    inside the fused launch) against the oracle's exact rounding of 127 x / s."""
+    pos = np.arange(0, 0x7F80, dtype=np.uint32)              # +0 .. largest finite
+    vals = (pos << 16).view(np.float32)
+    scales = [np.uint16(b) for b in (0x0001, 0x0080, 0x0D80, 0x3A00, 0x3F80, 0x4040, 0x42FE, 0x4B00, 0x5F00, 0x7A00)]
+    for sb in scales:
+        s = np.array([np.uint32(sb) << 16], dtype=np.uint32).view(np.float32)[0]
+        xb = pos[vals <= s].astype(np.uint16)
+        row = np.concatenate([xb, xb | np.uint16(0x8000)])          # both signs, contains s itself
+        K = 52224 if fused else -(-len(row) // 64) * 64
+        reps = -(-K // len(row))
+        row = np.tile(row, reps)[:K] if len(row) < K else row[:K]
+        if not np.any((row & 0x7FFF) == sb):                     # keep the row max at s
+            row[0] = sb
+        x_bits = row.reshape(1, K).view(np.uint16)
+        q_ref, s_ref = oracle.quant_act(x_bits)
+        x = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).to(DEV)
+        if not fused:
+            q, sx = tw.quant_act(x)
+        else:
+            packed = torch.full((64, K // 4), 0x55, dtype=torch.uint8, device=DEV)
+            y = torch.empty((1, 64), dtype=torch.float32, device=DEV)
+            q = torch.empty((1, K), dtype=torch.int8, device=DEV)
+            sx = torch.empty(1, dtype=torch.float32, device=DEV)
+            tw.bitnet_grouped_plan_fused([(x, packed, torch.ones(1, device=DEV), y, None, q, sx)]).launch()
+        torch.cuda.synchronize()
+        assert np.array_equal(sx.cpu().numpy(), s_ref), hex(int(sb))
+        assert np.array_equal(q.cpu().numpy(), q_ref), hex(int(sb))
+
+
 def test_quant_act_zero_rows_and_unaligned():
     x = synth.activations(synth.stream_key(101), 6, 512)
     x[2] = 0
@@ -182,6 +215,42 @@ def test_mfma_decode_kernel(M, N, K):
                             y, acc, 4)
     assert np.array_equal(acc.cpu().numpy(), acc_ref)
     assert_y(y.cpu().numpy(), y_ref)
+
+
+@pytest.mark.parametrize("with_outputs", [True, False])
+def test_fused_quant_linear_grouped(with_outputs):
+    """One fused grouped launch (quantization inside the GEMV workgroups) against the
+    oracle's quant_act + linear, problem by problem: ragged N, K from one chunk to the
+    longest single-segment K, an all-zero row, outliers, rows of every scale."""
+    shapes = [(300, 2560, {}), (129, 52224, {"outlier_frac": 0.001}), (64, 64, {}), (97, 6912, {"row_scale": (1e-3, 1e-3)}),
+              (700, 640, {"outlier_frac": 0.01}), (33, 2560, "zero")]
+    probs, refs = [], []
+    for i, (N, K, kw) in enumerate(shapes):
+        key = synth.stream_key(309, i)
+        x = torch.zeros((1, K), dtype=torch.bfloat16) if kw == "zero" else synth.activations(key, 1, K, **kw)
+        packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
+        s_w = np.float32(0.0093 * (i + 1))
+        q_ref, sx_ref = oracle.quant_act(bits_np(x))
+        acc_ref, y_ref = oracle.linear(q_ref, sx_ref, packed, s_w)
+        refs.append((q_ref, sx_ref, acc_ref, y_ref))
+        y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+        acc = torch.empty((1, N), dtype=torch.int32, device=DEV)
+        q = torch.full((1, K), 99, dtype=torch.int8, device=DEV) if with_outputs else None
+        sx = torch.full((1,), -1.0, dtype=torch.float32, device=DEV) if with_outputs else None
+        probs.append((x.to(DEV), torch.from_numpy(packed).to(DEV), torch.tensor([s_w], device=DEV), y, acc, q, sx))
+    plan = tw.bitnet_grouped_plan_fused(probs)
+    for _ in range(2):
+        for pr in probs:
+            pr[3].fill_(float("nan"))
+            pr[4].fill_(-1)
+        plan.launch()
+        torch.cuda.synchronize()
+        for (q_ref, sx_ref, acc_ref, y_ref), pr in zip(refs, probs):
+            assert np.array_equal(pr[4].cpu().numpy(), acc_ref)
+            assert_y(pr[3].cpu().numpy(), y_ref)
+            if with_outputs:
+                assert np.array_equal(pr[5].cpu().numpy(), q_ref)
+                assert np.array_equal(pr[6].cpu().numpy(), sx_ref)
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 200, 53312), (2, 70, 26176), (3, 200, 16704), (8, 200, 16704),
