@@ -90,6 +90,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--legs", default="two_launch,prefill,sweep,decode_m8,ffn100b",
+                    help="secondary legs to run (comma-separated subset of the default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling PMC byte counters)")
@@ -200,138 +202,144 @@ def main() -> int:
     # ------------------------------------------------------------ secondary legs
     if not args.no_secondary:
         sec = {}
-        # the same step as two launches: grouped quantization, then grouped GEMV on q
-        qs = [[torch.empty((1, x.shape[1]), dtype=torch.int8, device=dev) for x in xl] for xl in xs]
-        sxs = [[torch.empty(1, dtype=torch.float32, device=dev) for _ in xl] for xl in xs]
-        qplan = tw.bitnet_grouped_plan_quant([(xs[l][j], qs[l][j], sxs[l][j]) for l in range(30) for j in range(4)])
-        lplan = tw.bitnet_grouped_plan_linear(
-            [(qs[m.layer][m.slot], sxs[m.layer][m.slot], packed[i], sws[i], ys[i], None) for i, m in enumerate(mats)])
-        gemv_bytes = weight_bytes + sum(m.K + 4 * m.N + 8 for m in mats)
-        for _ in range(10):
-            qplan.launch(stream)
-            lplan.launch(stream)
-        torch.cuda.synchronize()
-        evq = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(100)]
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(100):
-            qplan.launch(stream)
-            evq[i][0].record(stream)
-            lplan.launch(stream)
-            evq[i][1].record(stream)
-        b.record(stream)
-        torch.cuda.synchronize()
-        step_us = a.elapsed_time(b) * 1e3 / 100
-        g_us = float(np.mean([x.elapsed_time(y) for x, y in evq])) * 1e3
-        sec["decode_step_2p4b_two_launches"] = {
-            "us": round(step_us, 1), "weight_GBs": round(weight_bytes / (step_us * 1e-6) / 1e9, 1),
-            "gemv_grouped_kernel_us": round(g_us, 2),
-            "gemv_grouped_kernel_GBs": round(gemv_bytes / (g_us * 1e-6) / 1e9, 1)}
-        log(f"two-launch step: {step_us:.1f} us (grouped GEMV {g_us:.1f} us)")
-        del qs, sxs, qplan, lplan
-        # prefill GEMM, M = 2048
-        reps = 50
-        for name in ("up", "down"):
-            for density in (None, 0.3, 0.5, 0.7):
-                x, w = W.prefill_inputs(name, density, dev)
-                p, s = tw.pack_weights(w, 1e-5)
-                del w
-                q, sx = tw.quant_act(x)
-                N, K = p.shape[0], q.shape[1]
-                y = torch.empty((2048, N), dtype=torch.float32, device=dev)
-                for _ in range(5):
-                    tw.bitnet_linear(q, sx, p, s, y)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                for _ in range(reps):
-                    tw.bitnet_linear(q, sx, p, s, y)
-                b.record(stream)
-                torch.cuda.synchronize()
-                us = a.elapsed_time(b) * 1e3 / reps
-                tops = 2.0 * 2048 * N * K / (us * 1e-6) / 1e12
-                key = f"prefill_{name}_M2048" + ("" if density is None else f"_density{int(density * 100)}")
-                sec[key] = {"us": round(us, 2), "int8_tops": round(tops, 1),
-                            "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
-                log(f"{key}: {us:.1f} us, {tops:.0f} TOPS")
-        # batched-decode sweep K=2560 N=6912: every kernel at every M, one launch
-        # per call, device time (graph-captured)
-        p, s = tw.pack_weights(W.sweep_weights(dev), 1e-5)
-        sweep = {}
-        for M in (1, 2, 4, 8, 16, 32, 64):
-            q, sx = tw.quant_act(W.sweep_activations(M, dev))
-            y = torch.empty((M, p.shape[0]), dtype=torch.float32, device=dev)
-            row = {}
-            for kname, kid in (("gemv", 1), ("mfma_decode", 4), ("gemm", 2)):
-                us = graph_us(torch, lambda: tw.bitnet_linear_select(q, sx, p, s, y, None, kid))
-                row[kname] = {"us": round(us, 2), "weight_GBs": round(p.numel() / (us * 1e-6) / 1e9, 1)}
-            sweep[f"M{M}"] = row
-        sec["sweep_K2560_N6912"] = sweep
-        log(f"sweep: {json.dumps(sweep)}")
-
-        # batched decode step: the same 210 matrices with 8 sequences decoding together
-        # (grouped quant + grouped linear, which runs the MFMA decode kernel)
-        M8 = 8
-        xs8 = [W.decode_step_activations(l, dev, M8) for l in range(30)]
-        qs8 = [[torch.empty((M8, x.shape[1]), dtype=torch.int8, device=dev) for x in xl] for xl in xs8]
-        sxs8 = [[torch.empty(M8, dtype=torch.float32, device=dev) for _ in xl] for xl in xs8]
-        ys8 = [torch.empty((M8, m.N), dtype=torch.float32, device=dev) for m in mats]
-        qplan8 = tw.bitnet_grouped_plan_quant([(xs8[l][j], qs8[l][j], sxs8[l][j]) for l in range(30) for j in range(4)])
-        lplan8 = tw.bitnet_grouped_plan_linear(
-            [(qs8[m.layer][m.slot], sxs8[m.layer][m.slot], packed[i], sws[i], ys8[i], None)
-             for i, m in enumerate(mats)])
-        for _ in range(10):
-            qplan8.launch(stream)
-            lplan8.launch(stream)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(100):
-            qplan8.launch(stream)
-            lplan8.launch(stream)
-        b.record(stream)
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / 100
-        sec["decode_step_2p4b_M8"] = {"us": round(us, 1), "weight_GBs": round(weight_bytes / (us * 1e-6) / 1e9, 1),
-                                      "tokens_per_s": round(M8 / (us * 1e-6), 1), "launches": 2}
-        log(f"decode step M=8: {us:.1f} us, {sec['decode_step_2p4b_M8']['weight_GBs']} GB/s")
-        del xs8, qs8, sxs8, ys8, qplan8, lplan8
-
-        # 100B-scale FFN stream: 8 layers x {gate, up 8192->28672; down 28672->8192},
-        # 1,409,286,144 packed bytes (5.5x the on-chip cache)
-        fmats = W.ffn_100b(8)
-        fpacked, fsw = [], []
-        for m in fmats:
-            p_, s_ = tw.pack_weights(W.weights(m, dev), 1e-5)
-            fpacked.append(p_)
-            fsw.append(s_)
-        fbytes = sum(p_.numel() for p_ in fpacked)
-        for M in (1, 8):
-            xs8 = [W.ffn_100b_activations(l, M, dev) for l in range(8)]
-            qx = [[tw.quant_act(x) for x in xl] for xl in xs8]
-            fys = [torch.empty((M, m.N), dtype=torch.float32, device=dev) for m in fmats]
-            plan = tw.bitnet_grouped_plan_linear(
-                [(qx[m.layer][m.slot][0], qx[m.layer][m.slot][1], fpacked[i], fsw[i], fys[i], None)
-                 for i, m in enumerate(fmats)])
-            run = lambda: plan.launch(stream)
-            for _ in range(3):
-                run()
+        legs = set(args.legs.split(","))
+        if "two_launch" in legs:
+            # the same step as two launches: grouped quantization, then grouped GEMV on q
+            qs = [[torch.empty((1, x.shape[1]), dtype=torch.int8, device=dev) for x in xl] for xl in xs]
+            sxs = [[torch.empty(1, dtype=torch.float32, device=dev) for _ in xl] for xl in xs]
+            qplan = tw.bitnet_grouped_plan_quant([(xs[l][j], qs[l][j], sxs[l][j]) for l in range(30) for j in range(4)])
+            lplan = tw.bitnet_grouped_plan_linear(
+                [(qs[m.layer][m.slot], sxs[m.layer][m.slot], packed[i], sws[i], ys[i], None) for i, m in enumerate(mats)])
+            gemv_bytes = weight_bytes + sum(m.K + 4 * m.N + 8 for m in mats)
+            for _ in range(10):
+                qplan.launch(stream)
+                lplan.launch(stream)
+            torch.cuda.synchronize()
+            evq = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(100)]
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            for _ in range(20):
-                run()
+            for i in range(100):
+                qplan.launch(stream)
+                evq[i][0].record(stream)
+                lplan.launch(stream)
+                evq[i][1].record(stream)
             b.record(stream)
             torch.cuda.synchronize()
-            us = a.elapsed_time(b) * 1e3 / 20
-            key = f"ffn100b_8layers_M{M}"
-            sec[key] = {"us": round(us, 1), "weight_GBs": round(fbytes / (us * 1e-6) / 1e9, 1),
-                        "launches": 1, "kernel": "gemv_grouped_kernel" if M == 1 else "skinny_grouped_kernel"}
-            log(f"{key}: {us:.1f} us, {sec[key]['weight_GBs']} GB/s")
-        # one GPU's share of an 8-way column split of the 100B gate matrix (K=8192, N=3584)
-        shard = fpacked[0][:3584].contiguous()
-        q1, s1 = tw.quant_act(W.ffn_100b_activations(0, 1, dev)[0])
-        y1 = torch.empty((1, 3584), dtype=torch.float32, device=dev)
-        us = graph_us(torch, lambda: tw.bitnet_linear(q1, s1, shard, fsw[0], y1), reps=50)
-        sec["colsplit8_gate_shard_M1"] = {"us": round(us, 2), "weight_GBs": round(shard.numel() / (us * 1e-6) / 1e9, 1)}
-        del fpacked
+            step_us = a.elapsed_time(b) * 1e3 / 100
+            g_us = float(np.mean([x.elapsed_time(y) for x, y in evq])) * 1e3
+            sec["decode_step_2p4b_two_launches"] = {
+                "us": round(step_us, 1), "weight_GBs": round(weight_bytes / (step_us * 1e-6) / 1e9, 1),
+                "gemv_grouped_kernel_us": round(g_us, 2),
+                "gemv_grouped_kernel_GBs": round(gemv_bytes / (g_us * 1e-6) / 1e9, 1)}
+            log(f"two-launch step: {step_us:.1f} us (grouped GEMV {g_us:.1f} us)")
+            del qs, sxs, qplan, lplan
+        if "prefill" in legs:
+            # prefill GEMM, M = 2048
+            reps = 50
+            for name in ("up", "down"):
+                for density in (None, 0.3, 0.5, 0.7):
+                    x, w = W.prefill_inputs(name, density, dev)
+                    p, s = tw.pack_weights(w, 1e-5)
+                    del w
+                    q, sx = tw.quant_act(x)
+                    N, K = p.shape[0], q.shape[1]
+                    y = torch.empty((2048, N), dtype=torch.float32, device=dev)
+                    for _ in range(5):
+                        tw.bitnet_linear(q, sx, p, s, y)
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    for _ in range(reps):
+                        tw.bitnet_linear(q, sx, p, s, y)
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    us = a.elapsed_time(b) * 1e3 / reps
+                    tops = 2.0 * 2048 * N * K / (us * 1e-6) / 1e12
+                    key = f"prefill_{name}_M2048" + ("" if density is None else f"_density{int(density * 100)}")
+                    sec[key] = {"us": round(us, 2), "int8_tops": round(tops, 1),
+                                "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+                    log(f"{key}: {us:.1f} us, {tops:.0f} TOPS")
+        if "sweep" in legs:
+            # batched-decode sweep K=2560 N=6912: every kernel at every M, one launch
+            # per call, device time (graph-captured)
+            p, s = tw.pack_weights(W.sweep_weights(dev), 1e-5)
+            sweep = {}
+            for M in (1, 2, 4, 8, 16, 32, 64):
+                q, sx = tw.quant_act(W.sweep_activations(M, dev))
+                y = torch.empty((M, p.shape[0]), dtype=torch.float32, device=dev)
+                row = {}
+                for kname, kid in (("gemv", 1), ("mfma_decode", 4), ("gemm", 2)):
+                    us = graph_us(torch, lambda: tw.bitnet_linear_select(q, sx, p, s, y, None, kid))
+                    row[kname] = {"us": round(us, 2), "weight_GBs": round(p.numel() / (us * 1e-6) / 1e9, 1)}
+                sweep[f"M{M}"] = row
+            sec["sweep_K2560_N6912"] = sweep
+            log(f"sweep: {json.dumps(sweep)}")
+
+        if "decode_m8" in legs:
+            # batched decode step: the same 210 matrices with 8 sequences decoding together
+            # (grouped quant + grouped linear, which runs the MFMA decode kernel)
+            M8 = 8
+            xs8 = [W.decode_step_activations(l, dev, M8) for l in range(30)]
+            qs8 = [[torch.empty((M8, x.shape[1]), dtype=torch.int8, device=dev) for x in xl] for xl in xs8]
+            sxs8 = [[torch.empty(M8, dtype=torch.float32, device=dev) for _ in xl] for xl in xs8]
+            ys8 = [torch.empty((M8, m.N), dtype=torch.float32, device=dev) for m in mats]
+            qplan8 = tw.bitnet_grouped_plan_quant([(xs8[l][j], qs8[l][j], sxs8[l][j]) for l in range(30) for j in range(4)])
+            lplan8 = tw.bitnet_grouped_plan_linear(
+                [(qs8[m.layer][m.slot], sxs8[m.layer][m.slot], packed[i], sws[i], ys8[i], None)
+                 for i, m in enumerate(mats)])
+            for _ in range(10):
+                qplan8.launch(stream)
+                lplan8.launch(stream)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(100):
+                qplan8.launch(stream)
+                lplan8.launch(stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / 100
+            sec["decode_step_2p4b_M8"] = {"us": round(us, 1), "weight_GBs": round(weight_bytes / (us * 1e-6) / 1e9, 1),
+                                          "tokens_per_s": round(M8 / (us * 1e-6), 1), "launches": 2}
+            log(f"decode step M=8: {us:.1f} us, {sec['decode_step_2p4b_M8']['weight_GBs']} GB/s")
+            del xs8, qs8, sxs8, ys8, qplan8, lplan8
+
+        if "ffn100b" in legs:
+            # 100B-scale FFN stream: 8 layers x {gate, up 8192->28672; down 28672->8192},
+            # 1,409,286,144 packed bytes (5.5x the on-chip cache)
+            fmats = W.ffn_100b(8)
+            fpacked, fsw = [], []
+            for m in fmats:
+                p_, s_ = tw.pack_weights(W.weights(m, dev), 1e-5)
+                fpacked.append(p_)
+                fsw.append(s_)
+            fbytes = sum(p_.numel() for p_ in fpacked)
+            for M in (1, 8):
+                xs8 = [W.ffn_100b_activations(l, M, dev) for l in range(8)]
+                qx = [[tw.quant_act(x) for x in xl] for xl in xs8]
+                fys = [torch.empty((M, m.N), dtype=torch.float32, device=dev) for m in fmats]
+                plan = tw.bitnet_grouped_plan_linear(
+                    [(qx[m.layer][m.slot][0], qx[m.layer][m.slot][1], fpacked[i], fsw[i], fys[i], None)
+                     for i, m in enumerate(fmats)])
+                run = lambda: plan.launch(stream)
+                for _ in range(3):
+                    run()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(20):
+                    run()
+                b.record(stream)
+                torch.cuda.synchronize()
+                us = a.elapsed_time(b) * 1e3 / 20
+                key = f"ffn100b_8layers_M{M}"
+                sec[key] = {"us": round(us, 1), "weight_GBs": round(fbytes / (us * 1e-6) / 1e9, 1),
+                            "launches": 1, "kernel": "gemv_grouped_kernel" if M == 1 else "skinny_grouped_kernel"}
+                log(f"{key}: {us:.1f} us, {sec[key]['weight_GBs']} GB/s")
+            # one GPU's share of an 8-way column split of the 100B gate matrix (K=8192, N=3584)
+            shard = fpacked[0][:3584].contiguous()
+            q1, s1 = tw.quant_act(W.ffn_100b_activations(0, 1, dev)[0])
+            y1 = torch.empty((1, 3584), dtype=torch.float32, device=dev)
+            us = graph_us(torch, lambda: tw.bitnet_linear(q1, s1, shard, fsw[0], y1), reps=50)
+            sec["colsplit8_gate_shard_M1"] = {"us": round(us, 2), "weight_GBs": round(shard.numel() / (us * 1e-6) / 1e9, 1)}
+            del fpacked
         line["secondary"] = sec
 
     # ------------------------------------------------------------ CPU baseline
