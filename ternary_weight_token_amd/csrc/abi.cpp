@@ -230,7 +230,7 @@ BITNET_API int bitnet_grouped_plan_linear(const bitnet_linear_desc *descs, int c
     h->variant = variant;
     if (variant == kVariantMfma) {
         h->rows_per_block = skinny_grouped_rows_per_block();
-        for (int i = 0; i < count; ++i) h->lds_bytes = std::max(h->lds_bytes, skinny_grouped_lds_bytes(descs[i].M));
+        for (int i = 0; i < count; ++i) h->lds_bytes = std::max(h->lds_bytes, skinny_grouped_lds_bytes(descs[i].M, descs[i].K));
     } else {
         h->rows_per_block = gemv_grouped_rows_per_block();
         for (int i = 0; i < count; ++i) h->lds_bytes = std::max(h->lds_bytes, gemv_grouped_lds_bytes(descs[i].K));

@@ -57,7 +57,7 @@ hipError_t launch_skinny(const int8_t *q, const float *s_x, const uint8_t *packe
                          int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st);
 hipError_t launch_skinny_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st);
 uint32_t skinny_grouped_rows_per_block();
-uint32_t skinny_grouped_lds_bytes(int64_t M);
+uint32_t skinny_grouped_lds_bytes(int64_t M, int64_t K);
 hipError_t launch_gemm(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                        int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st);
 hipError_t launch_gemm_cfg(int cfg, const int8_t *q, const float *s_x, const uint8_t *packed,

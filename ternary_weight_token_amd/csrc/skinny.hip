@@ -40,7 +40,14 @@ namespace bitnet {
 typedef int v4i_sk __attribute__((ext_vector_type(4)));
 
 constexpr int kSkinnyNW = 8;          // wavefronts per workgroup (single launches)
-constexpr int kGroupedSkRG = 2;       // grouped launches: 4 wavefronts x 2 groups of 16 rows
+#ifndef BITNET_GROUPED_SK_RG
+#define BITNET_GROUPED_SK_RG 2
+#endif
+#ifndef BITNET_GROUPED_SK_NW
+#define BITNET_GROUPED_SK_NW 8
+#endif
+constexpr int kGroupedSkRG = BITNET_GROUPED_SK_RG;   // grouped launches: row groups of 16 per wavefront
+constexpr int kGroupedSkNW = BITNET_GROUPED_SK_NW;   // wavefronts per workgroup
 #ifndef BITNET_GROUPED_SK_UN
 #define BITNET_GROUPED_SK_UN 2
 #endif
@@ -228,17 +235,25 @@ hipError_t launch_skinny(const int8_t *q, const float *s_x, const uint8_t *packe
 }
 
 // ---------------------------------------------------------------------------
-// LDS-staged variant (grouped launches): the 4 wavefronts of a workgroup walk the
-// whole K of 4 x 16 RG rows in lockstep segments of kSegChunks chunks.  The q of a
-// segment (all tokens) is loaded once per workgroup, byte-transposed once and kept
-// in LDS in MFMA B-operand order, so the main loop issues only weight loads and
-// reads its B operands from LDS; sum_k q is formed while staging.  Two segment
-// buffers: segment s + 1 is written while nobody reads its buffer any more, and its
-// global loads were issued a whole segment earlier; one barrier per segment.
-constexpr int kSegChunks = 16;   // 4 steps of 4 chunks
+// LDS-staged variant (grouped launches): the NW wavefronts of a workgroup walk the
+// whole K of NW x 16 RG rows (8 x 32 = 256: measured against 4 x 32, 16 x 32 and
+// 8 x 64, it stages each q for the most rows without starving the grid).  The q of a
+// K segment (all tokens) is loaded once per
+// workgroup, byte-transposed once and kept in LDS in MFMA B-operand order (chunk,
+// vector i, token: 16 bytes each), so the main loop issues only weight loads and
+// reads its B operands from LDS; sum_k q is formed while staging.  A segment is as
+// long as the LDS budget allows for the problem's M tokens: the whole K for every
+// decode-step shape up to 12 tokens; one barrier pair per segment.
+constexpr int kSkLdsBudget = 64 * 1024;
 
-// LDS bytes of the two segment buffers for an M-token tile: chunk x vector x token x 16 B
-__host__ __device__ constexpr int seg_buffer_dw(int m) { return kSegChunks * 4 * m * 4; }
+// Segment length in 64-weight chunks for M tokens: all of K if its staged q fits the
+// budget, else the fewest equal segments, each a multiple of 8 chunks (one step).
+__host__ __device__ __forceinline__ int sk_segment_chunks(int C, int M) {
+    const int max_seg = (kSkLdsBudget / (64 * M)) & ~7;
+    if (C <= max_seg) return C;
+    const int nseg = (C + max_seg - 1) / max_seg;
+    return (((C + nseg - 1) / nseg) + 7) & ~7;
+}
 
 template <int RG, int UN, bool NT>
 __device__ __forceinline__ void skinny_lds_tile(const int8_t *__restrict__ q, const float *__restrict__ s_x,
@@ -253,8 +268,7 @@ __device__ __forceinline__ void skinny_lds_tile(const int8_t *__restrict__ q, co
     const int KB = K >> 2;
     const int row0 = row_base + wave * 16 * RG;
     const int tok = min(l16, M - 1);
-    const int nseg = (C + kSegChunks - 1) / kSegChunks;
-    const int seg_dw = seg_buffer_dw(M);   // token stride M: the buffers hold M tokens
+    const int seg_chunks = sk_segment_chunks(C, M);
 
     const uint8_t *prow[RG];
     #pragma unroll
@@ -263,111 +277,98 @@ __device__ __forceinline__ void skinny_lds_tile(const int8_t *__restrict__ q, co
         prow[rg] = packed + (size_t)(r < N ? r : 0) * KB;   // rows past N read row 0, dropped
     }
 
-    // staging role: thread -> (token st_m, chunk st_c of the segment), 16 threads per
-    // token reading its 1 KB of the segment contiguously
-    const int st_m = tid >> 4, st_c = tid & 15;
-    const bool stager = st_m < M;
-    const int8_t *st_row = q + (size_t)(stager ? st_m : 0) * K;
-    uint4 sreg[4];
-    int st_sum = 0;
-    auto stage_load = [&](int seg) {
-        const int c = min(seg * kSegChunks + st_c, C - 1);
-        #pragma unroll
-        for (int d = 0; d < 4; ++d) sreg[d] = gload16(st_row + 64 * c + 16 * d);
-    };
-    auto stage_store = [&](int seg) {
-        const bool ok = stager && seg * kSegChunks + st_c < C;
-        uint32_t P[4][4];
-        #pragma unroll
-        for (int d = 0; d < 4; ++d)
-            transpose4x4(sreg[d].x, sreg[d].y, sreg[d].z, sreg[d].w, P[0][d], P[1][d], P[2][d], P[3][d]);
-        int sm = 0;
-        #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            sm = dot4(sreg[d].x, 0x01010101u, sm);
-            sm = dot4(sreg[d].y, 0x01010101u, sm);
-            sm = dot4(sreg[d].z, 0x01010101u, sm);
-            sm = dot4(sreg[d].w, 0x01010101u, sm);
-        }
-        st_sum += ok ? sm : 0;
-        if (ok) {
-            uint32_t *dst = qs + (seg & 1) * seg_dw;
-            #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<uint4 *>(dst + ((st_c * 4 + i) * M + st_m) * 4) =
-                    make_uint4(P[i][0], P[i][1], P[i][2], P[i][3]);
-        }
-    };
-
     v4i_sk acc[RG];
     #pragma unroll
     for (int rg = 0; rg < RG; ++rg) acc[rg] = v4i_sk{0, 0, 0, 0};
+    if (tid < 16) sq[tid] = 0;
 
-    // step t: lane group g takes chunks 4 UN t + 4 u + g, u < UN (so the UN loads of
-    // a row group are back to back and cover 64 UN contiguous bytes of each row);
-    // steps run to a whole number of segments, chunks past K clamped to an
-    // in-range load and zeroed
-    constexpr int SPS = kSegChunks / (4 * UN);   // steps per segment (even)
-    static_assert(SPS % 2 == 0, "two register buffers alternate within a segment");
-    uint4 wA[UN][RG], wB[UN][RG];
-    auto issue = [&](uint4 (&w)[UN][RG], int t) {
-        #pragma unroll
-        for (int u = 0; u < UN; ++u) {
-            const int cc = min(4 * UN * t + 4 * u + g, C - 1);
+    for (int s0 = 0; s0 < C; s0 += seg_chunks) {
+        const int sc = min(seg_chunks, C - s0);
+        // step t: lane group g takes local chunks 4 UN t + 4 u + g, u < UN (the UN loads
+        // of a row group are back to back: 64 UN contiguous bytes of each row); chunks
+        // past the segment are clamped to an in-range load and zeroed
+        const int T = (sc + 4 * UN - 1) / (4 * UN);
+        uint4 wA[UN][RG], wB[UN][RG];
+        auto issue = [&](uint4 (&w)[UN][RG], int t) {
             #pragma unroll
-            for (int rg = 0; rg < RG; ++rg) w[u][rg] = load_weights<NT>(prow[rg] + 16 * cc);
-        }
-    };
-    auto consume = [&](const uint4 (&w)[UN][RG], int t) {
-        #pragma unroll
-        for (int u = 0; u < UN; ++u) {
-            const bool valid = 4 * UN * t + 4 * u + g < C;
-            const int cl = 4 * UN * (t % SPS) + 4 * u + g;
-            const uint32_t *src = qs + ((t / SPS) & 1) * seg_dw + ((cl * 4) * M + tok) * 4;
-            uint32_t wm[RG][4];
-            #pragma unroll
-            for (int rg = 0; rg < RG; ++rg) {
-                wm[rg][0] = valid ? w[u][rg].x : 0u;
-                wm[rg][1] = valid ? w[u][rg].y : 0u;
-                wm[rg][2] = valid ? w[u][rg].z : 0u;
-                wm[rg][3] = valid ? w[u][rg].w : 0u;
+            for (int u = 0; u < UN; ++u) {
+                const int cc = s0 + min(4 * UN * t + 4 * u + g, sc - 1);
+                #pragma unroll
+                for (int rg = 0; rg < RG; ++rg) w[u][rg] = load_weights<NT>(prow[rg] + 16 * cc);
             }
+        };
+        auto consume = [&](const uint4 (&w)[UN][RG], int t) {
             #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const v4i_sk b = *reinterpret_cast<const v4i_sk *>(src + i * M * 4);
+            for (int u = 0; u < UN; ++u) {
+                const int cl = 4 * UN * t + 4 * u + g;
+                const bool valid = cl < sc;
+                const uint32_t *src = qs + ((min(cl, sc - 1) * 4) * M + tok) * 4;
+                uint32_t wm[RG][4];
                 #pragma unroll
                 for (int rg = 0; rg < RG; ++rg) {
-                    const v4i_sk a = v4i_sk{(int)codes_i(wm[rg][0], i), (int)codes_i(wm[rg][1], i),
-                                            (int)codes_i(wm[rg][2], i), (int)codes_i(wm[rg][3], i)};
-                    acc[rg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[rg], 0, 0, 0);
+                    wm[rg][0] = valid ? w[u][rg].x : 0u;
+                    wm[rg][1] = valid ? w[u][rg].y : 0u;
+                    wm[rg][2] = valid ? w[u][rg].z : 0u;
+                    wm[rg][3] = valid ? w[u][rg].w : 0u;
+                }
+                #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const v4i_sk b = *reinterpret_cast<const v4i_sk *>(src + i * M * 4);
+                    #pragma unroll
+                    for (int rg = 0; rg < RG; ++rg) {
+                        const v4i_sk a = v4i_sk{(int)codes_i(wm[rg][0], i), (int)codes_i(wm[rg][1], i),
+                                                (int)codes_i(wm[rg][2], i), (int)codes_i(wm[rg][3], i)};
+                        acc[rg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[rg], 0, 0, 0);
+                    }
                 }
             }
-        }
-    };
+        };
+        // the segment's first weight loads go out before the staging of q
+        if (T > 0) issue(wA, 0);
 
-    if (tid < 16) sq[tid] = 0;
-    stage_load(0);
-    issue(wA, 0);
-    stage_store(0);
-    if (nseg > 1) stage_load(1);
-    __syncthreads();
-    for (int seg = 0; seg < nseg; ++seg) {
-        #pragma unroll
-        for (int j = 0; j < SPS; j += 2) {
-            const int t = seg * SPS + j;
-            issue(wB, t + 1);
-            consume(wA, t);
-            issue(wA, t + 2);
-            consume(wB, t + 1);
+        // ---- stage the segment's q: (token m, chunk c) per thread, 64 contiguous bytes
+        __syncthreads();   // previous segment's LDS reads done; sq initialised
+        for (int idx = tid; idx < M * sc; idx += blockDim.x) {
+            const int m = idx / sc, c = idx - m * sc;
+            const int8_t *src = q + (size_t)m * K + 64 * (s0 + c);
+            uint4 v[4];
+            #pragma unroll
+            for (int d = 0; d < 4; ++d) v[d] = gload16(src + 16 * d);
+            uint32_t P[4][4];   // P[i][d]: byte b = q of k = 16 d + 4 b + i
+            int sm = 0;
+            #pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                transpose4x4(v[d].x, v[d].y, v[d].z, v[d].w, P[0][d], P[1][d], P[2][d], P[3][d]);
+                sm = dot4(v[d].x, 0x01010101u, sm);
+                sm = dot4(v[d].y, 0x01010101u, sm);
+                sm = dot4(v[d].z, 0x01010101u, sm);
+                sm = dot4(v[d].w, 0x01010101u, sm);
+            }
+            #pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<uint4 *>(qs + ((c * 4 + i) * M + m) * 4) = make_uint4(P[i][0], P[i][1], P[i][2], P[i][3]);
+            if (sm != 0) atomicAdd(&sq[m], sm);
         }
-        // segment seg + 1 into the other buffer (last read in segment seg - 1), and
-        // the loads of segment seg + 2
-        stage_store(seg + 1);
-        if (seg + 2 < nseg) stage_load(seg + 2);
         __syncthreads();
+
+        // pairs of steps, no branch in the loop body; the last one or two peeled
+        if (T > 0) {
+            const int T2 = (T + 1) & ~1;
+            for (int t = 0; t < T2 - 2; t += 2) {
+                issue(wB, t + 1);
+                consume(wA, t);
+                issue(wA, t + 2);
+                consume(wB, t + 1);
+            }
+            if (T2 == T) {
+                issue(wB, T - 1);
+                consume(wA, T - 2);
+                consume(wB, T - 1);
+            } else {
+                consume(wA, T - 1);
+            }
+        }
     }
-    if (stager) atomicAdd(&sq[st_m], st_sum);
-    __syncthreads();
 
     // 16 x 16 accumulator layout: lane -> token l16; register r -> row 4 g + r
     if (l16 < M) {
@@ -390,23 +391,25 @@ __device__ __forceinline__ void skinny_lds_tile(const int8_t *__restrict__ q, co
     }
 }
 
-// Grouped decode on the matrix cores: block -> (descriptor, row block of 4 x 16 RG
+// Grouped decode on the matrix cores: block -> (descriptor, row block of NW x 16 RG
 // rows) through the plan's block table; every descriptor has M <= 16.
-__global__ __launch_bounds__(256) void skinny_grouped_kernel(const uint8_t *__restrict__ plan) {
-    extern __shared__ __attribute__((aligned(16))) uint32_t qs[];   // 2 x seg_buffer_dw(max M) dwords
+__global__ __launch_bounds__(64 * kGroupedSkNW) void skinny_grouped_kernel(const uint8_t *__restrict__ plan) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t qs[];   // staged q of one segment
     __shared__ int sq[16];
     const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
     const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[blockIdx.x];
     const LinearDescDev d = reinterpret_cast<const LinearDescDev *>(plan + h->desc_offset)[e.desc];
     skinny_lds_tile<kGroupedSkRG, kGroupedSkUN, BITNET_GROUPED_SK_NT != 0>(d.q, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, d.y, d.acc,
-                                                         (int)e.local * 4 * 16 * kGroupedSkRG, qs, sq);
+                                                         (int)e.local * kGroupedSkNW * 16 * kGroupedSkRG, qs, sq);
 }
 
-uint32_t skinny_grouped_rows_per_block() { return 4 * 16 * kGroupedSkRG; }
-uint32_t skinny_grouped_lds_bytes(int64_t M) { return (uint32_t)(2 * seg_buffer_dw((int)M) * 4); }
+uint32_t skinny_grouped_rows_per_block() { return kGroupedSkNW * 16 * kGroupedSkRG; }
+uint32_t skinny_grouped_lds_bytes(int64_t M, int64_t K) {
+    return (uint32_t)(sk_segment_chunks((int)(K / 64), (int)M) * 64 * M);
+}
 
 hipError_t launch_skinny_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st) {
-    skinny_grouped_kernel<<<dim3(blocks), dim3(256), lds_bytes, st>>>(reinterpret_cast<const uint8_t *>(plan_dev));
+    skinny_grouped_kernel<<<dim3(blocks), dim3(64 * kGroupedSkNW), lds_bytes, st>>>(reinterpret_cast<const uint8_t *>(plan_dev));
     return hipGetLastError();
 }
 

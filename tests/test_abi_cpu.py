@@ -115,14 +115,14 @@ def test_grouped_plan_checks(L):
                                         ctypes.cast(buf4, ctypes.c_void_p), n4) == OK
     hdr4 = (ctypes.c_uint32 * 8).from_buffer_copy(buf4.raw[:32])
     assert 0 < hdr4[6] <= 64 * 1024
-    # any M > 1 selects the MFMA variant: one block per 128 rows for all M tokens
+    # any M > 1 selects the MFMA variant: one block per 256 rows for all M tokens
     arr5 = (D * 2)(D(a16, a16, a16, a16, a16, 0, 1, 300, 2560), D(a16, a16, a16, a16, a16, 0, 5, 200, 2560))
     n5 = L.bitnet_grouped_plan_bytes(2, 1, ctypes.cast(arr5, ctypes.c_void_p))
     buf5 = ctypes.create_string_buffer(n5)
     assert L.bitnet_grouped_plan_linear(ctypes.cast(arr5, ctypes.c_void_p), 2,
                                         ctypes.cast(buf5, ctypes.c_void_p), n5) == OK
     hdr5 = (ctypes.c_uint32 * 8).from_buffer_copy(buf5.raw[:32])
-    assert hdr5[7] == 1 and hdr5[5] == 128 and hdr5[3] == 3 + 2
+    assert hdr5[7] == 1 and hdr5[5] == 256 and hdr5[3] == 2 + 1
     assert hdr[7] == 0
 
 
