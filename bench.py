@@ -259,6 +259,23 @@ def main() -> int:
                     sec[key] = {"us": round(us, 2), "int8_tops": round(tops, 1),
                                 "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
                     log(f"{key}: {us:.1f} us, {tops:.0f} TOPS")
+                    if density is None:
+                        # the same GEMM with the layer bias and a bf16 output
+                        bias = torch.linspace(-1.0, 1.0, N, dtype=torch.float32, device=dev)
+                        yb = torch.empty((2048, N), dtype=torch.bfloat16, device=dev)
+                        for _ in range(5):
+                            tw.bitnet_linear_ex(q, sx, p, s, bias, yb)
+                        a.record(stream)
+                        for _ in range(reps):
+                            tw.bitnet_linear_ex(q, sx, p, s, bias, yb)
+                        b.record(stream)
+                        torch.cuda.synchronize()
+                        us = a.elapsed_time(b) * 1e3 / reps
+                        tops = 2.0 * 2048 * N * K / (us * 1e-6) / 1e12
+                        sec[key + "_bias_bf16"] = {"us": round(us, 2), "int8_tops": round(tops, 1),
+                                                   "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+                        log(f"{key}_bias_bf16: {us:.1f} us, {tops:.0f} TOPS")
+                        del yb, bias
         if "sweep" in legs:
             # batched-decode sweep K=2560 N=6912: every kernel at every M, one launch
             # per call, device time (graph-captured)

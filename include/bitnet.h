@@ -152,6 +152,32 @@ BITNET_API int bitnet_linear_select(const int8_t *q, const float *s_x, const uin
                                     const float *s_w, int64_t M, int64_t N, int64_t K,
                                     float *y, int32_t *acc, int kernel, void *stream);
 
+/* Output element types of bitnet_linear_ex. */
+enum bitnet_dtype {
+    BITNET_F32 = 0,   /* IEEE binary32                                     */
+    BITNET_BF16 = 1   /* bfloat16 (upper half of binary32), uint16 storage */
+};
+
+/* bitnet_linear_select with the two epilogue options of the BitLinear forward
+ * (chenxutan.com sec. 3.1 adds the layer's bias after the rescale; sec. 2.3 and
+ * the bf16 activations of sec. 2.2 motivate a bf16 output for the next layer):
+ *
+ *   bias     (device) fp32 [N], added to every row of y, or NULL for none
+ *   y        (device) [M][N] of y_dtype: BITNET_F32 or BITNET_BF16
+ *   kernel   as for bitnet_linear_select (0 = automatic)
+ *
+ * y[m][n] = fp32(acc * c_m + bias[n]) with c_m = (s_x[m] * s_w) / 127, the
+ * product and the sum taken in float64 and rounded once to fp32; a bf16 y is
+ * that fp32 value rounded to nearest, ties to even (finite inputs only).  acc
+ * is unchanged by the options.  bias must be 4-byte aligned, y aligned to its
+ * element size (else BITNET_ERR_ALIGN); an unknown y_dtype or kernel gives
+ * BITNET_ERR_ARG.  bitnet_linear and bitnet_linear_select are this call with
+ * bias = NULL and y_dtype = BITNET_F32. */
+BITNET_API int bitnet_linear_ex(const int8_t *q, const float *s_x, const uint8_t *packed,
+                                const float *s_w, int64_t M, int64_t N, int64_t K,
+                                const float *bias, void *y, int y_dtype, int32_t *acc,
+                                int kernel, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Grouped decode calls: many independent quant_act or linear problems in one
  * launch (a decode step has hundreds of small matrices; one launch each would

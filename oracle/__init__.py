@@ -46,6 +46,8 @@ def lib():
         L.oracle_unpack.argtypes = [P, I64, I64, P]
         L.oracle_quant_act.argtypes = [P, I64, I64, P, P]
         L.oracle_linear.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, P, P]
+        L.oracle_linear_bias.argtypes = [P, P, P, ctypes.c_float, P, I64, I64, I64, P, P]
+        L.oracle_to_bf16.argtypes = [P, I64, P]
         L.oracle_set_threads.argtypes = [ctypes.c_int]
         L.oracle_get_threads.restype = ctypes.c_int
         _lib = L
@@ -102,8 +104,9 @@ def quant_act(x_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return q, s
 
 
-def linear(q: np.ndarray, s_x: np.ndarray, packed: np.ndarray, s_w, K: int | None = None):
-    """-> (acc int32 [M][N], y fp32 [M][N])."""
+def linear(q: np.ndarray, s_x: np.ndarray, packed: np.ndarray, s_w, K: int | None = None,
+           bias: np.ndarray | None = None):
+    """-> (acc int32 [M][N], y fp32 [M][N]); bias: fp32 [N] added after the rescale."""
     q = np.ascontiguousarray(q, dtype=np.int8)
     s_x = np.ascontiguousarray(s_x, dtype=np.float32)
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
@@ -113,6 +116,20 @@ def linear(q: np.ndarray, s_x: np.ndarray, packed: np.ndarray, s_w, K: int | Non
     assert packed.shape[1] * 4 == K and s_x.shape == (M,)
     acc = np.empty((M, N), dtype=np.int32)
     y = np.empty((M, N), dtype=np.float32)
-    lib().oracle_linear(_p(q), _p(s_x), _p(packed), ctypes.c_float(float(s_w)),
-                        M, N, K, _p(acc), _p(y))
+    if bias is None:
+        lib().oracle_linear(_p(q), _p(s_x), _p(packed), ctypes.c_float(float(s_w)),
+                            M, N, K, _p(acc), _p(y))
+    else:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        assert bias.shape == (N,)
+        lib().oracle_linear_bias(_p(q), _p(s_x), _p(packed), ctypes.c_float(float(s_w)), _p(bias),
+                                 M, N, K, _p(acc), _p(y))
     return acc, y
+
+
+def to_bf16(y: np.ndarray) -> np.ndarray:
+    """fp32 values -> bf16 bit patterns (uint16), nearest, ties to even."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, dtype=np.uint16)
+    lib().oracle_to_bf16(_p(y), y.size, _p(out))
+    return out

@@ -32,7 +32,10 @@
  *    for bf16 inputs, see the tests); an all-zero row gives q = 0, s_x = 0;
  *  - output y = acc * (s_x / 127) * s_w, the real number rounded once to fp32
  *    (formed in float64); the /127 undoes the *127 of the activation code;
- *  - a 2-bit field holding 3 (never written by the packer) decodes to +2.
+ *  - a 2-bit field holding 3 (never written by the packer) decodes to +2;
+ *  - the optional bias ([P1] 3.1 adds it after the rescale) joins the float64
+ *    value before its one rounding to fp32; a bf16 output is that fp32 value
+ *    rounded again, to nearest bf16, ties to even.
  *
  * Parity pins for every function live in tests/test_oracle_pins.py.
  * Build: gcc -O2 -std=c11 -fPIC -shared -fopenmp -ffp-contract=off.
@@ -158,11 +161,13 @@ void oracle_quant_act(const uint16_t *x, int64_t M, int64_t K,
 /* --- contraction and rescale ([P1] 2.3, 3.1 BitLinear.forward) ---------- */
 
 /* acc[m][n] = sum_k q[m][k] * t[n][k]  (exact integer sum)
- * y[m][n]   = fp32( acc * s_x[m] * s_w / 127 )   formed in float64.
- * acc may be NULL. */
-void oracle_linear(const int8_t *q, const float *s_x, const uint8_t *packed,
-                   float s_w, int64_t M, int64_t N, int64_t K,
-                   int32_t *acc, float *y) {
+ * y[m][n]   = fp32( acc * s_x[m] * s_w / 127 + bias[n] )   formed in float64;
+ * the bias is the layer's own bias, added after the rescale ([P1] 3.1, where
+ * BitLinear.forward adds self.bias to the dequantized product).
+ * acc and bias may be NULL (no bias: the sum has no second term). */
+void oracle_linear_bias(const int8_t *q, const float *s_x, const uint8_t *packed,
+                        float s_w, const float *bias, int64_t M, int64_t N, int64_t K,
+                        int32_t *acc, float *y) {
     int64_t KB = K / 4;
     #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n) {
@@ -174,7 +179,39 @@ void oracle_linear(const int8_t *q, const float *s_x, const uint8_t *packed,
             double v = (double)a * (double)s_x[m];
             v = v * (double)s_w;
             v = v / 127.0;
+            if (bias) v = v + (double)bias[n];
             y[m * N + n] = (float)v;
         }
+    }
+}
+
+void oracle_linear(const int8_t *q, const float *s_x, const uint8_t *packed,
+                   float s_w, int64_t M, int64_t N, int64_t K,
+                   int32_t *acc, float *y) {
+    oracle_linear_bias(q, s_x, packed, s_w, NULL, M, N, K, acc, y);
+}
+
+/* --- bf16 output ---------------------------------------------------------- */
+
+/* Each finite fp32 value rounded to the nearest bfloat16 (8 significand bits,
+ * the exponent range of fp32), ties to the even significand: IEEE 754
+ * round-to-nearest-even into that format.  Written from the definition: the
+ * two bf16 neighbours of |f| are its truncation `lo` and lo plus one unit in
+ * its last place; the nearer one wins, a tie goes to the one whose last
+ * significand bit is 0.  Above the largest finite bf16 the upper neighbour is
+ * 2^128, i.e. the result is infinity, as IEEE overflow under this rounding. */
+void oracle_to_bf16(const float *y, int64_t n, uint16_t *out) {
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t u;
+        memcpy(&u, &y[i], sizeof u);
+        const uint16_t lo = (uint16_t)(u >> 16);          /* sign kept, |value| <= |f| */
+        const double a = fabs((double)y[i]);
+        const double a_lo = fabs((double)bf16_to_float(lo));
+        if (a == a_lo) { out[i] = lo; continue; }
+        const int e = (lo >> 7) & 0xFF;                    /* biased exponent of lo */
+        const double ulp = ldexp(1.0, (e == 0 ? 1 : e) - 127 - 7);
+        const double d_lo = a - a_lo, d_hi = (a_lo + ulp) - a;   /* both exact in float64 */
+        if (d_lo < d_hi || (d_lo == d_hi && (lo & 1) == 0)) out[i] = lo;
+        else out[i] = (uint16_t)(lo + 1);
     }
 }

@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
         L.bitnet_quant_act.argtypes = [P, I64, I64, P, P, P]
         L.bitnet_linear.argtypes = [P, P, P, P, I64, I64, I64, P, P, P]
         L.bitnet_linear_select.argtypes = [P, P, P, P, I64, I64, I64, P, P, I, P]
+        L.bitnet_linear_ex.argtypes = [P, P, P, P, I64, I64, I64, P, P, I, P, I, P]
         L.bitnet_grouped_plan_bytes.argtypes = [I, I, P]
         L.bitnet_grouped_plan_bytes.restype = ctypes.c_size_t
         L.bitnet_grouped_plan_linear.argtypes = [P, I, P, ctypes.c_size_t]
@@ -69,7 +70,7 @@ def lib() -> ctypes.CDLL:
         L.bitnet_grouped_plan_fused_bytes.restype = ctypes.c_size_t
         L.bitnet_grouped_plan_fused.argtypes = [P, I, P, ctypes.c_size_t]
         L.bitnet_linear_fused_grouped.argtypes = [P, P, P]
-        for f in ("bitnet_pack_weights", "bitnet_quant_act", "bitnet_linear", "bitnet_linear_select",
+        for f in ("bitnet_pack_weights", "bitnet_quant_act", "bitnet_linear", "bitnet_linear_select", "bitnet_linear_ex",
                   "bitnet_grouped_plan_linear", "bitnet_grouped_plan_quant", "bitnet_grouped_plan_fused",
                   "bitnet_linear_grouped", "bitnet_quant_act_grouped", "bitnet_linear_fused_grouped"):
             getattr(L, f).restype = I
@@ -159,8 +160,39 @@ def bitnet_linear_select(q: torch.Tensor, s_x: torch.Tensor, packed: torch.Tenso
         raise ValueError("shape mismatch")
     if acc is not None:
         _dev(acc, torch.int32, "acc")
+        if acc.shape != (M, N):
+            raise ValueError("acc must be [M][N]")
     _check(lib().bitnet_linear_select(_ptr(q), _ptr(s_x), _ptr(packed), _ptr(s_w), M, N, K, _ptr(y),
                                       _ptr(acc), int(kernel), _stream(stream)))
+
+
+BITNET_F32, BITNET_BF16 = 0, 1
+_OUT_DTYPES = {torch.float32: BITNET_F32, torch.bfloat16: BITNET_BF16}
+
+
+def bitnet_linear_ex(q: torch.Tensor, s_x: torch.Tensor, packed: torch.Tensor, s_w: torch.Tensor,
+                     bias: torch.Tensor | None, y: torch.Tensor, acc: torch.Tensor | None = None,
+                     kernel: int = 0, stream=None) -> None:
+    """bitnet_linear_select with an optional fp32 bias [N] and y in fp32 or bf16 [M][N]."""
+    _dev(q, torch.int8, "q"); _dev(s_x, torch.float32, "s_x"); _dev(packed, torch.uint8, "packed")
+    _dev(s_w, torch.float32, "s_w")
+    if y.dtype not in _OUT_DTYPES:
+        raise ValueError(f"y must be float32 or bfloat16, got {y.dtype}")
+    _dev(y, y.dtype, "y")
+    M, K = q.shape
+    N = packed.shape[0]
+    if packed.shape != (N, K // 4) or s_x.shape != (M,) or y.shape != (M, N):
+        raise ValueError("shape mismatch")
+    if bias is not None:
+        _dev(bias, torch.float32, "bias")
+        if bias.shape != (N,):
+            raise ValueError("bias must be [N]")
+    if acc is not None:
+        _dev(acc, torch.int32, "acc")
+        if acc.shape != (M, N):
+            raise ValueError("acc must be [M][N]")
+    _check(lib().bitnet_linear_ex(_ptr(q), _ptr(s_x), _ptr(packed), _ptr(s_w), M, N, K, _ptr(bias),
+                                  _ptr(y), _OUT_DTYPES[y.dtype], _ptr(acc), int(kernel), _stream(stream)))
 
 
 class GroupedPlan:
@@ -254,10 +286,14 @@ def quant_act(x: torch.Tensor, stream=None):
     return q, s_x
 
 
-def linear(q, s_x, packed, s_w, want_acc: bool = False, stream=None):
+def linear(q, s_x, packed, s_w, want_acc: bool = False, stream=None, bias=None,
+           out_dtype=torch.float32, kernel: int = 0):
     M, K = q.shape
     N = packed.shape[0]
-    y = torch.empty((M, N), dtype=torch.float32, device=q.device)
+    y = torch.empty((M, N), dtype=out_dtype, device=q.device)
     acc = torch.empty((M, N), dtype=torch.int32, device=q.device) if want_acc else None
-    bitnet_linear(q, s_x, packed, s_w, y, acc, stream)
+    if bias is None and out_dtype == torch.float32 and kernel == 0:
+        bitnet_linear(q, s_x, packed, s_w, y, acc, stream)
+    else:
+        bitnet_linear_ex(q, s_x, packed, s_w, bias, y, acc, kernel, stream)
     return (y, acc) if want_acc else y

@@ -104,32 +104,41 @@ BITNET_API int bitnet_quant_act(const uint16_t *x, int64_t M, int64_t K, int8_t 
     return hip_status(launch_quant_act(x, M, K, q, s_x, (hipStream_t)stream));
 }
 
+BITNET_API int bitnet_linear_ex(const int8_t *q, const float *s_x, const uint8_t *packed,
+                                const float *s_w, int64_t M, int64_t N, int64_t K, const float *bias,
+                                void *y, int y_dtype, int32_t *acc, int kernel, void *stream) {
+    const bool forced_tile = kernel >= 16 && kernel < 16 + gemm_config_count();
+    if ((kernel < 0 || kernel > 4) && !forced_tile) return fail(BITNET_ERR_ARG, "unknown kernel id");
+    if (y_dtype != BITNET_F32 && y_dtype != BITNET_BF16) return fail(BITNET_ERR_ARG, "unknown output dtype");
+    int st = check_dims(M, N, K);
+    if (st || M == 0 || N == 0) return st;
+    if (!q || !s_x || !packed || !s_w || !y) return fail(BITNET_ERR_NULL, "null pointer");
+    if (!aligned(s_x, 4) || !aligned(s_w, 4) || (acc && !aligned(acc, 4)) || (bias && !aligned(bias, 4)))
+        return fail(BITNET_ERR_ALIGN, "s_x, s_w, bias and acc must be 4-byte aligned");
+    if (!aligned(y, y_dtype == BITNET_BF16 ? 2 : 4))
+        return fail(BITNET_ERR_ALIGN, "y must be aligned to its element size");
+    const OutSpec out{y, bias, y_dtype == BITNET_BF16 ? 1 : 0};
+    hipStream_t s = (hipStream_t)stream;
+    const bool fast = linear_fast(q, packed, K);
+    if (kernel == 3 || (kernel == 0 && !fast))
+        return hip_status(launch_linear_generic(q, s_x, packed, s_w, M, N, K, out, acc, s));
+    if (!fast) return fail(BITNET_ERR_ALIGN, "kernel needs K % 64 == 0 and 16-byte aligned q/packed");
+    if (kernel == 0) kernel = M == 1 ? 1 : (M <= kGemvMaxM ? 4 : 2);
+    if (kernel == 1) return hip_status(launch_gemv(q, s_x, packed, s_w, M, N, K, out, acc, s));
+    if (kernel == 4) return hip_status(launch_skinny(q, s_x, packed, s_w, M, N, K, out, acc, s));
+    if (forced_tile) return hip_status(launch_gemm_cfg(kernel - 16, q, s_x, packed, s_w, M, N, K, out, acc, s));
+    return hip_status(launch_gemm(q, s_x, packed, s_w, M, N, K, out, acc, s));
+}
+
 BITNET_API int bitnet_linear(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                              int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, void *stream) {
-    int st = check_linear(q, s_x, packed, s_w, M, N, K, y, acc);
-    if (st || M == 0 || N == 0) return st;
-    hipStream_t s = (hipStream_t)stream;
-    if (!linear_fast(q, packed, K)) return hip_status(launch_linear_generic(q, s_x, packed, s_w, M, N, K, y, acc, s));
-    if (M == 1) return hip_status(launch_gemv(q, s_x, packed, s_w, M, N, K, y, acc, s));
-    if (M <= kGemvMaxM) return hip_status(launch_skinny(q, s_x, packed, s_w, M, N, K, y, acc, s));
-    return hip_status(launch_gemm(q, s_x, packed, s_w, M, N, K, y, acc, s));
+    return bitnet_linear_ex(q, s_x, packed, s_w, M, N, K, nullptr, y, BITNET_F32, acc, 0, stream);
 }
 
 BITNET_API int bitnet_linear_select(const int8_t *q, const float *s_x, const uint8_t *packed,
                                     const float *s_w, int64_t M, int64_t N, int64_t K, float *y,
                                     int32_t *acc, int kernel, void *stream) {
-    if (kernel == 0) return bitnet_linear(q, s_x, packed, s_w, M, N, K, y, acc, stream);
-    const bool forced_tile = kernel >= 16 && kernel < 16 + gemm_config_count();
-    if ((kernel < 0 || kernel > 4) && !forced_tile) return fail(BITNET_ERR_ARG, "unknown kernel id");
-    int st = check_linear(q, s_x, packed, s_w, M, N, K, y, acc);
-    if (st || M == 0 || N == 0) return st;
-    hipStream_t s = (hipStream_t)stream;
-    if (kernel == 3) return hip_status(launch_linear_generic(q, s_x, packed, s_w, M, N, K, y, acc, s));
-    if (!linear_fast(q, packed, K)) return fail(BITNET_ERR_ALIGN, "kernel needs K % 64 == 0 and 16-byte aligned q/packed");
-    if (kernel == 1) return hip_status(launch_gemv(q, s_x, packed, s_w, M, N, K, y, acc, s));
-    if (kernel == 4) return hip_status(launch_skinny(q, s_x, packed, s_w, M, N, K, y, acc, s));
-    if (forced_tile) return hip_status(launch_gemm_cfg(kernel - 16, q, s_x, packed, s_w, M, N, K, y, acc, s));
-    return hip_status(launch_gemm(q, s_x, packed, s_w, M, N, K, y, acc, s));
+    return bitnet_linear_ex(q, s_x, packed, s_w, M, N, K, nullptr, y, BITNET_F32, acc, kernel, stream);
 }
 
 // ----------------------------------------------------------------- grouped plans

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.h"
+
 namespace bitnet {
 
 // Global loads go through the global address space explicitly: pointers read
@@ -167,6 +169,26 @@ __device__ __forceinline__ double rescale_factor(float s_x, float s_w) {
 }
 __device__ __forceinline__ float rescale(int acc, double c) {
     return (float)((double)acc * c);
+}
+
+// bf16 nearest-even rounding of a finite fp32 value.
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Round the float64 output value once to fp32 and store it (as bf16 if asked).
+__device__ __forceinline__ void store_y(const OutSpec &out, size_t o, double v) {
+    const float f = (float)v;
+    if (out.bf16) reinterpret_cast<uint16_t *>(out.y)[o] = bf16_rne(f);
+    else reinterpret_cast<float *>(out.y)[o] = f;
+}
+
+// Store output element o (column n) from acc and c = c_m; see OutSpec.
+__device__ __forceinline__ void put_y(const OutSpec &out, size_t o, int n, int acc, double c) {
+    double v = (double)acc * c;
+    if (out.bias) v += (double)out.bias[n];
+    store_y(out, o, v);
 }
 
 }  // namespace bitnet

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
                                                            const float *__restrict__ s_x,
                                                            const uint8_t *__restrict__ packed,
                                                            const float *__restrict__ s_w, int M, int N,
-                                                           int K, float *__restrict__ y,
+                                                           int K, const OutSpec out,
                                                            int32_t *__restrict__ acc_out, int tiles_m,
                                                            int tiles_n) {
     constexpr int NT = 64 * WM * WN;          // threads
@@ -213,6 +213,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
     __syncthreads();
 
     // 16x16 accumulator layout: lane -> column l16; register r -> row 4 * (lane / 16) + r.
+    // The bias of the lane's TN columns is loaded once, before any store.
+    float bcol[TN];
+    #pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int col = n_base + wn * TN * 16 + j * 16 + l16;
+        bcol[j] = (out.bias && col < N) ? out.bias[col] : 0.0f;
+    }
     #pragma unroll
     for (int i = 0; i < TM; ++i) {
         #pragma unroll
@@ -228,7 +235,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
                 if (col < N) {
                     const size_t o = (size_t)row * N + col;
                     const int v = acc[i][j][r] - sq;
-                    y[o] = rescale(v, cm);
+                    double yv = (double)v * cm;
+                    if (out.bias) yv += (double)bcol[j];
+                    store_y(out, o, yv);
                     if (acc_out) acc_out[o] = v;
                 }
             }
@@ -240,7 +249,7 @@ struct GemmCfg { int wm, wn, tm, tn; };
 
 template <int WM, int WN, int TM, int TN, int KS, bool BPACK = false>
 static hipError_t launch_cfg(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
-                             int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
+                             int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st) {
     constexpr int BM = 16 * WM * TM, BN = 16 * WN * TN;
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
     gemm_kernel<WM, WN, TM, TN, KS, BPACK><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * WM * WN), 0, st>>>(
@@ -249,7 +258,7 @@ static hipError_t launch_cfg(const int8_t *q, const float *s_x, const uint8_t *p
 }
 
 hipError_t launch_gemm(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
-                       int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
+                       int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st) {
     // Tile configurations (id: BM x BN): 0: 256 x 224, 1: 256 x 80, 2: 256 x 128,
     // 3: 128 x 128, 4: 64 x 128.  Pick the tile whose busiest compute unit does the least work, assuming one
     // workgroup per CU at a time: cost = ceil(tiles / 256) * BM * BN.
@@ -268,7 +277,7 @@ hipError_t launch_gemm(const int8_t *q, const float *s_x, const uint8_t *packed,
 int gemm_config_count() { return 5; }
 
 hipError_t launch_gemm_cfg(int cfg, const int8_t *q, const float *s_x, const uint8_t *packed,
-                           const float *s_w, int64_t M, int64_t N, int64_t K, float *y, int32_t *acc,
+                           const float *s_w, int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc,
                            hipStream_t st) {
     // a configuration needing K % 128 == 0 falls back to its single-step twin
     const bool k128 = (K % 128) == 0;

@@ -175,7 +175,7 @@ template <int MT, int RG, bool DOT8, bool NT, class Stage>
 __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *__restrict__ s_x,
                                               const uint8_t *__restrict__ packed,
                                               const float *__restrict__ s_w, int M, int N, int K,
-                                              float *__restrict__ y, int32_t *__restrict__ acc_out,
+                                              const OutSpec &out, int32_t *__restrict__ acc_out,
                                               int row_base, int m0, int kslices, int seg_chunks,
                                               uint32_t *qs, int *sq, int *red) {
     const int tid = threadIdx.x;
@@ -300,7 +300,7 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *_
                 if (r < N && l8 == (m & 7)) {
                     const size_t o = (size_t)(m0 + m) * N + r;
                     const int a = acc[g][m] - sqm;
-                    y[o] = rescale(a, cm);
+                    put_y(out, o, r, a, cm);
                     if (acc_out) acc_out[o] = a;
                 }
             }
@@ -325,7 +325,7 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *_
         int s = -sq[m];
         for (int w = 0; w < kslices; ++w) s += red[((rsi * kslices + w) * R + rr) * MT + m];
         const size_t o = (size_t)(m0 + m) * N + r;
-        y[o] = rescale(s, rescale_factor(s_x[m0 + m], sw));
+        put_y(out, o, r, s, rescale_factor(s_x[m0 + m], sw));
         if (acc_out) acc_out[o] = s;
     }
 }
@@ -333,13 +333,13 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *_
 template <int MT, int RG, bool DOT8>
 __global__ __launch_bounds__(256) void gemv_lds_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s_x, const uint8_t *__restrict__ packed,
-    const float *__restrict__ s_w, int M, int N, int K, float *__restrict__ y,
+    const float *__restrict__ s_w, int M, int N, int K, const OutSpec out,
     int32_t *__restrict__ acc_out, int kslices, int seg_chunks) {
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
     __shared__ int sq[MT];
     __shared__ int red[4 * 8 * RG * MT];
     const int rows_per_block = (4 / kslices) * 8 * RG;
-    gemv_lds_tile<MT, RG, DOT8, BITNET_GEMV_NT != 0>(StageQ<MT, DOT8>{q, K}, s_x, packed, s_w, M, N, K, y, acc_out,
+    gemv_lds_tile<MT, RG, DOT8, BITNET_GEMV_NT != 0>(StageQ<MT, DOT8>{q, K}, s_x, packed, s_w, M, N, K, out, acc_out,
                                                      blockIdx.x * rows_per_block, blockIdx.y * MT, kslices,
                                                      seg_chunks, dyn, sq, red);
 }
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(256) void gemv_grouped_kernel(const uint8_t *__rest
     const int rowblocks = (d.N + rows - 1) / rows;
     const int rb = (int)(e.local % rowblocks), mt = (int)(e.local / rowblocks);
     gemv_lds_tile<kGroupedMT, kGroupedRG, BITNET_GROUPED_DOT8 != 0, BITNET_GEMV_NT != 0>(
-        StageQ<kGroupedMT, BITNET_GROUPED_DOT8 != 0>{d.q, d.K}, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, d.y, d.acc, rb * rows, mt * kGroupedMT, 1, segment_chunks(d.K >> 6, kGroupedMT), dyn,
+        StageQ<kGroupedMT, BITNET_GROUPED_DOT8 != 0>{d.q, d.K}, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, OutSpec{d.y, nullptr, 0}, d.acc, rb * rows, mt * kGroupedMT, 1, segment_chunks(d.K >> 6, kGroupedMT), dyn,
         sq, red);
 }
 
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(256) void gemv_fused_grouped_kernel(const uint8_t *
     const StageQuantize<BITNET_GROUPED_DOT8 != 0> stage{d.x, first ? d.q : nullptr, first ? d.s_x : nullptr,
                                                          &s_lds, qred};
     gemv_lds_tile<1, kGroupedRG, BITNET_GROUPED_DOT8 != 0, BITNET_GEMV_NT != 0>(
-        stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K, d.y, d.acc, (int)e.local * rows, 0, 1, d.K >> 6, dyn, sq, red);
+        stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K, OutSpec{d.y, nullptr, 0}, d.acc, (int)e.local * rows, 0, 1, d.K >> 6, dyn, sq, red);
 }
 
 // Longest K whose q fits one LDS segment of the grouped GEMV.
@@ -411,7 +411,7 @@ uint32_t gemv_grouped_lds_bytes(int64_t K) {
 
 template <int MT, int RG, bool DOT8>
 static hipError_t launch_lds(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
-                             int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
+                             int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st) {
     const int C = (int)(K / 64);
     const unsigned gy = (unsigned)((M + MT - 1) / MT);
     // more K slices per row set until the launch has >= 2 workgroups per CU,
@@ -428,7 +428,7 @@ static hipError_t launch_lds(const int8_t *q, const float *s_x, const uint8_t *p
 }
 
 hipError_t launch_gemv(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
-                       int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
+                       int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st) {
     const bool d8 = BITNET_GROUPED_DOT8 != 0;
     if (M == 1) return launch_lds<1, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
     if (M == 2) return launch_lds<2, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);

@@ -9,7 +9,7 @@ namespace bitnet {
 
 __global__ __launch_bounds__(256) void linear_generic_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s_x, const uint8_t *__restrict__ packed,
-    const float *__restrict__ s_w, int64_t M, int64_t N, int64_t K, float *__restrict__ y,
+    const float *__restrict__ s_w, int64_t M, int64_t N, int64_t K, const OutSpec out,
     int32_t *__restrict__ acc_out) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= M * N) return;
@@ -22,12 +22,12 @@ __global__ __launch_bounds__(256) void linear_generic_kernel(
         #pragma unroll
         for (int i = 0; i < 4; ++i) s += (int)qr[4 * j + i] * ((int)((b >> (2 * i)) & 3u) - 1);
     }
-    y[idx] = rescale(s, rescale_factor(s_x[m], *s_w));
+    put_y(out, idx, (int)n, s, rescale_factor(s_x[m], *s_w));
     if (acc_out) acc_out[idx] = s;
 }
 
 hipError_t launch_linear_generic(const int8_t *q, const float *s_x, const uint8_t *packed,
-                                 const float *s_w, int64_t M, int64_t N, int64_t K, float *y,
+                                 const float *s_w, int64_t M, int64_t N, int64_t K, const OutSpec &y,
                                  int32_t *acc, hipStream_t st) {
     const int64_t total = M * N;
     linear_generic_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st>>>(

@@ -6,6 +6,21 @@
 
 namespace bitnet {
 
+// Output of the rescale epilogue (pages: chenxutan.com sec. 2.3 rescale, sec. 3.1
+// forward with its optional bias): y = acc * c_m (+ bias[n]), c_m = (s_x * s_w) / 127,
+// formed in float64 and rounded once to fp32; a bf16 output is that fp32 value
+// rounded to nearest even.
+struct OutSpec {
+    void *y;             // fp32 or bf16, [M][N]
+    const float *bias;   // [N] or nullptr
+    int bf16;
+};
+
+// The same output advanced by `elems` elements (a later row block of y).
+__host__ __device__ inline OutSpec out_offset(const OutSpec &o, size_t elems) {
+    return OutSpec{static_cast<char *>(o.y) + elems * (o.bf16 ? 2 : 4), o.bias, o.bf16};
+}
+
 // Plan image for grouped launches.
 constexpr uint32_t kPlanMagic = 0xB17E7A01u;
 constexpr uint32_t kPlanLinear = 1, kPlanQuant = 2, kPlanFused = 3;
@@ -46,7 +61,7 @@ hipError_t launch_quant_act_grouped(const void *plan_dev, uint32_t blocks, hipSt
 hipError_t launch_pack(const float *w, int64_t N, int64_t K, float eps, uint8_t *packed,
                        float *s_w, double *rowsum, hipStream_t st);
 hipError_t launch_gemv(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
-                       int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st);
+                       int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st);
 hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st);
 uint32_t gemv_grouped_lds_bytes(int64_t K);
 hipError_t launch_gemv_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st);
@@ -54,18 +69,18 @@ int64_t gemv_fused_max_k();
 uint32_t gemv_grouped_rows_per_block();
 uint32_t gemv_grouped_threads();
 hipError_t launch_skinny(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
-                         int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st);
+                         int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st);
 hipError_t launch_skinny_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st);
 uint32_t skinny_grouped_rows_per_block();
 uint32_t skinny_grouped_lds_bytes(int64_t M, int64_t K);
 hipError_t launch_gemm(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
-                       int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st);
+                       int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st);
 hipError_t launch_gemm_cfg(int cfg, const int8_t *q, const float *s_x, const uint8_t *packed,
-                           const float *s_w, int64_t M, int64_t N, int64_t K, float *y, int32_t *acc,
+                           const float *s_w, int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc,
                            hipStream_t st);
 int gemm_config_count();
 hipError_t launch_linear_generic(const int8_t *q, const float *s_x, const uint8_t *packed,
-                                 const float *s_w, int64_t M, int64_t N, int64_t K, float *y,
+                                 const float *s_w, int64_t M, int64_t N, int64_t K, const OutSpec &y,
                                  int32_t *acc, hipStream_t st);
 
 }  // namespace bitnet

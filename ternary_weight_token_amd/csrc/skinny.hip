@@ -60,7 +60,7 @@ template <int RG, bool NT>
 __device__ __forceinline__ void skinny_tile(const int8_t *__restrict__ q, const float *__restrict__ s_x,
                                             const uint8_t *__restrict__ packed,
                                             const float *__restrict__ s_w, int M, int N, int K,
-                                            float *__restrict__ y, int32_t *__restrict__ acc_out,
+                                            const OutSpec &out, int32_t *__restrict__ acc_out,
                                             int row_base, int nwaves, int kslices, int *red) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -157,7 +157,7 @@ __device__ __forceinline__ void skinny_tile(const int8_t *__restrict__ q, const 
                     if (row < N) {
                         const size_t o = (size_t)l16 * N + row;
                         const int v = acc[rg][r] - accq[r];
-                        y[o] = rescale(v, cm);
+                        put_y(out, o, row, v, cm);
                         if (acc_out) acc_out[o] = v;
                     }
                 }
@@ -181,7 +181,7 @@ __device__ __forceinline__ void skinny_tile(const int8_t *__restrict__ q, const 
         int s = 0;
         for (int w = 0; w < kslices; ++w) s += red[(((rsi * kslices + w) * RG + rg) * 4 + r) * 64 + ln];
         const size_t o = (size_t)tok * N + row;
-        y[o] = rescale(s, rescale_factor(s_x[tok], sw));
+        put_y(out, o, row, s, rescale_factor(s_x[tok], sw));
         if (acc_out) acc_out[o] = s;
     }
 }
@@ -191,19 +191,19 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(const int8_t *__restric
                                                          const float *__restrict__ s_x,
                                                          const uint8_t *__restrict__ packed,
                                                          const float *__restrict__ s_w, int M, int N, int K,
-                                                         float *__restrict__ y, int32_t *__restrict__ acc_out,
+                                                         const OutSpec out, int32_t *__restrict__ acc_out,
                                                          int kslices) {
     __shared__ int red[NW * RG * 256];
     const int rows_per_block = (NW / kslices) * 16 * RG;
     const int m0 = blockIdx.y * 16;   // tiles of 16 tokens (one for M <= 16)
     skinny_tile<RG, BITNET_SKINNY_NT != 0>(q + (size_t)m0 * K, s_x + m0, packed, s_w, min(16, M - m0), N, K,
-                                           y + (size_t)m0 * N, acc_out ? acc_out + (size_t)m0 * N : nullptr,
+                                           out_offset(out, (size_t)m0 * N), acc_out ? acc_out + (size_t)m0 * N : nullptr,
                                            blockIdx.x * rows_per_block, NW, kslices, red);
 }
 
 template <int RG>
 static void launch_rg(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w, int64_t M,
-                      int64_t N, int64_t K, float *y, int32_t *acc, int ks, hipStream_t st) {
+                      int64_t N, int64_t K, const OutSpec &y, int32_t *acc, int ks, hipStream_t st) {
     constexpr int NW = kSkinnyNW;
     const int rows_per_block = (NW / ks) * 16 * RG;
     const unsigned blocks = (unsigned)((N + rows_per_block - 1) / rows_per_block);
@@ -213,7 +213,7 @@ static void launch_rg(const int8_t *q, const float *s_x, const uint8_t *packed, 
 }
 
 hipError_t launch_skinny(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
-                         int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
+                         int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st) {
     // Rows per wavefront (16 RG) against parallelism: the largest RG whose launch,
     // with K split over up to 8 wavefronts of a workgroup (at least 8 chunks per
     // slice), still reaches 2048 wavefronts (one workgroup per CU); more row groups
@@ -259,7 +259,7 @@ template <int RG, int UN, bool NT>
 __device__ __forceinline__ void skinny_lds_tile(const int8_t *__restrict__ q, const float *__restrict__ s_x,
                                                 const uint8_t *__restrict__ packed,
                                                 const float *__restrict__ s_w, int M, int N, int K,
-                                                float *__restrict__ y, int32_t *__restrict__ acc_out,
+                                                const OutSpec &out, int32_t *__restrict__ acc_out,
                                                 int row_base, uint32_t *qs, int *sq) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -383,7 +383,7 @@ __device__ __forceinline__ void skinny_lds_tile(const int8_t *__restrict__ q, co
                 if (row < N) {
                     const size_t o = (size_t)l16 * N + row;
                     const int v = acc[rg][r] - sqm;
-                    y[o] = rescale(v, cm);
+                    put_y(out, o, row, v, cm);
                     if (acc_out) acc_out[o] = v;
                 }
             }
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(64 * kGroupedSkNW) void skinny_grouped_kernel(const
     const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
     const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[blockIdx.x];
     const LinearDescDev d = reinterpret_cast<const LinearDescDev *>(plan + h->desc_offset)[e.desc];
-    skinny_lds_tile<kGroupedSkRG, kGroupedSkUN, BITNET_GROUPED_SK_NT != 0>(d.q, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, d.y, d.acc,
+    skinny_lds_tile<kGroupedSkRG, kGroupedSkUN, BITNET_GROUPED_SK_NT != 0>(d.q, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, OutSpec{d.y, nullptr, 0}, d.acc,
                                                          (int)e.local * kGroupedSkNW * 16 * kGroupedSkRG, qs, sq);
 }
 

@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -62,6 +62,22 @@ def test_linear_rejects_bad_arguments(L):
     # empty problems are successful no-ops, even with NULL pointers
     assert L.bitnet_linear(z, z, z, z, 0, 5, 64, z, z, z) == OK
     assert L.bitnet_linear(z, z, z, z, 3, 0, 64, z, z, z) == OK
+
+
+def test_linear_ex_rejects_bad_arguments(L):
+    p = ctypes.c_void_p(256)  # never dereferenced: every call below fails its checks
+    z = None
+    F32, BF16 = 0, 1
+    assert L.bitnet_linear_ex(p, p, p, p, 1, 1, 64, z, p, 2, z, 0, z) == ARG       # unknown dtype
+    assert L.bitnet_linear_ex(p, p, p, p, 1, 1, 64, z, p, F32, z, 7, z) == ARG     # unknown kernel
+    assert L.bitnet_linear_ex(p, p, p, p, 1, 1, 64, ctypes.c_void_p(258), p, F32, z, 0, z) == ALIGN
+    assert L.bitnet_linear_ex(p, p, p, p, 1, 1, 64, z, ctypes.c_void_p(258), F32, z, 0, z) == ALIGN
+    assert L.bitnet_linear_ex(p, p, p, p, 1, 1, 64, z, ctypes.c_void_p(257), BF16, z, 0, z) == ALIGN
+    assert L.bitnet_linear_ex(p, p, p, p, 1, 1, 64, p, z, BF16, z, 0, z) == NULL
+    assert L.bitnet_linear_ex(p, p, p, p, 1, 1, 6, p, p, BF16, z, 0, z) == SHAPE
+    # fast kernels need K % 64 == 0 (the general kernel, id 3, does not)
+    assert L.bitnet_linear_ex(p, p, p, p, 1, 1, 68, z, p, BF16, z, 1, z) == ALIGN
+    assert L.bitnet_linear_ex(z, z, z, z, 0, 5, 64, z, z, BF16, z, 0, z) == OK
 
 
 def test_quant_and_pack_reject_bad_arguments(L):

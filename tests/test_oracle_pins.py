@@ -358,3 +358,90 @@ def test_epilogue_is_correctly_rounded():
                                np.float32(7.77e-3))
     exact = Fraction(127 * K) * Fraction(float(np.float32(3.0e5))) * Fraction(float(np.float32(7.77e-3))) / 127
     assert y_x[0, 0] == np.float32(round_fraction_to_f32(exact))
+
+
+# ----------------------------------------------------------------- epilogue options
+
+def _f32(bits: int) -> np.float32:
+    return np.array([bits], np.uint32).view(np.float32)[0]
+
+
+def test_to_bf16_hand_cases():
+    # bf16 keeps 7 fraction bits: one unit in the last place at 1.0 is 2^-7
+    cases = [
+        (1.0, 0x3F80),
+        (1.0 + 2.0 ** -8, 0x3F80),                 # tie, lower neighbour even
+        (1.0 + 3 * 2.0 ** -8, 0x3F82),             # tie, lower neighbour odd -> up
+        (1.0 + 2.0 ** -8 + 2.0 ** -20, 0x3F81),    # just above the tie
+        (-(1.0 + 3 * 2.0 ** -8), 0xBF82),
+        (0.0, 0x0000),
+        (-0.0, 0x8000),
+        (2.0 ** -133, 0x0001),                     # smallest bf16 subnormal
+        (1.5 * 2.0 ** -133, 0x0002),               # tie between 1 (odd) and 2
+        (2.0 ** -134, 0x0000),                     # tie between 0 (even) and 1
+        (2.0 ** -149, 0x0000),                     # far below half the smallest
+        (3.0e38, 0x7F62),                          # bf16 nearest to 3e38 below max
+    ]
+    vals = np.array([c[0] for c in cases], np.float32)
+    got = oracle.to_bf16(vals)
+    for (v, want), g in zip(cases, got):
+        assert int(g) == want, (v, hex(int(g)), hex(want))
+    # the largest finite fp32 lies above the midpoint to 2^128: overflow to +inf
+    assert int(oracle.to_bf16(np.array([_f32(0x7F7FFFFF)]))[0]) == 0x7F80
+
+
+def test_to_bf16_matches_torch_rounding():
+    """The library conversion fp32 -> bfloat16 of torch (CPU) rounds to nearest even."""
+    rng = np.random.default_rng(2024)
+    hi = rng.integers(0, 1 << 16, size=1 << 18, dtype=np.uint32)
+    parts = [rng.integers(0, 1 << 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)]
+    for low in (0x8000, 0x7FFF, 0x8001, 0x0000, 0xFFFF):   # ties and their neighbours
+        parts.append((hi << 16) | np.uint32(low))
+    bits = np.concatenate(parts)
+    bits = bits[((bits >> 23) & 0xFF) != 0xFF]             # finite inputs only
+    f = bits.view(np.float32)
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.to_bf16(f), want)
+
+
+def test_to_bf16_is_nearest():
+    """Every result is a bf16 value at distance <= half a unit from the input."""
+    rng = np.random.default_rng(7)
+    f = (rng.standard_normal(1 << 16) * np.exp2(rng.integers(-60, 60, 1 << 16))).astype(np.float32)
+    b = oracle.to_bf16(f)
+    back = bf16_bits_to_f32(b).astype(np.float64)
+    e = np.floor(np.log2(np.maximum(np.abs(back), 1e-300)))
+    half_ulp = np.exp2(e - 8)
+    assert np.all(np.abs(back - f.astype(np.float64)) <= half_ulp * (1 + 1e-12))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 3, 4), (3, 5, 8), (4, 7, 132)])
+def test_linear_bias_exact(M, N, K):
+    key = synth.stream_key(16, M, N, K)
+    x = synth.activations(key, M, K, row_scale=(0.1, 10.0))
+    q, s = oracle.quant_act(synth.bf16_bits(x).numpy().view(np.uint16))
+    w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02).numpy()
+    packed, s_w = oracle.pack(w)
+    bias = (np.arange(N, dtype=np.float32) - N / 2) * np.float32(0.37) + np.float32(0.011)
+    acc, y = oracle.linear(q, s, packed, s_w, bias=bias)
+    acc0, _ = oracle.linear(q, s, packed, s_w)
+    assert np.array_equal(acc, acc0)                 # the bias leaves acc alone
+    acc_bf = _brute_force(q, s, packed, s_w, K)
+    for m in range(M):
+        for n in range(N):
+            exact = (Fraction(int(acc_bf[m, n])) * Fraction(float(s[m])) * Fraction(float(s_w)) / 127
+                     + Fraction(float(bias[n])))
+            assert y[m, n] == np.float32(round_fraction_to_f32(exact)), (m, n)
+
+
+def test_linear_bias_broadcast_over_tokens():
+    """A zero token row gives acc = 0, so every output of that row is the bias itself."""
+    N, K = 9, 64
+    q = np.zeros((3, K), np.int8)
+    q[1] = 5
+    s = np.array([0.0, 2.0, 0.0], np.float32)
+    packed = synth.random_bytes(synth.stream_key(17), N * K // 4).numpy().reshape(N, K // 4)
+    bias = np.linspace(-3, 3, N).astype(np.float32)
+    _, y = oracle.linear(q, s, packed, np.float32(0.5), bias=bias)
+    assert np.array_equal(y[0], bias) and np.array_equal(y[2], bias)
+    assert not np.array_equal(y[1], bias)

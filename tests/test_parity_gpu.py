@@ -325,6 +325,84 @@ def test_gemm_tile_configs(cfg, M, N, K):
     assert_y(y.cpu().numpy(), y_ref)
 
 
+# ----------------------------------------------------------------- epilogue options
+
+def _epilogue_tolerance(acc_ref, s, s_w, bias):
+    """Absolute bound for the fp32 y with a bias: the library forms
+    acc * ((s_x s_w) / 127) + b in float64, the oracle ((acc s_x) s_w) / 127 + b;
+    the two float64 values differ by a few units of 2^-52 (|P| + |b|), and each
+    is rounded once to fp32 (one unit in the last place apart at most)."""
+    P = np.abs(acc_ref.astype(np.float64) * s.astype(np.float64)[:, None] * float(s_w) / 127.0)
+    b = 0.0 if bias is None else np.abs(bias.astype(np.float64))[None, :]
+    return 2.0 ** -45 * (P + b)
+
+
+@pytest.mark.parametrize("kernel,M,N,K", [
+    (1, 1, 300, 2560), (1, 3, 70, 6912), (1, 9, 33, 640),             # decode GEMV
+    (4, 2, 300, 2624), (4, 16, 129, 2560), (4, 20, 70, 640),           # MFMA decode
+    (2, 17, 129, 256), (2, 130, 257, 640),                             # MFMA GEMM, automatic tile
+    (16, 257, 225, 640), (17, 257, 225, 640), (18, 257, 225, 640),     # each forced tile
+    (19, 257, 225, 640), (20, 257, 225, 640),
+    (3, 3, 9, 68), (3, 20, 33, 132),                                   # general kernel
+    (0, 1, 640, 2560), (0, 8, 300, 2560), (0, 40, 300, 2560),          # automatic choice
+])
+@pytest.mark.parametrize("with_bias,out_dtype", [(True, torch.float32), (False, torch.bfloat16),
+                                                 (True, torch.bfloat16)])
+def test_linear_epilogue_options(kernel, M, N, K, with_bias, out_dtype):
+    """bitnet_linear_ex: the bias added after the rescale and the bf16 output,
+    on every kernel; acc is unchanged by either option."""
+    key = synth.stream_key(311, kernel, M, N, K)
+    x, q, s = quantized_inputs(key, M, K, row_scale=(0.1, 10.0))
+    w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02).numpy()
+    packed, s_w = oracle.pack(w)
+    bias = None
+    if with_bias:
+        bias = synth.activations(synth.stream_key(key, 2), 1, N).float().numpy()[0] * np.float32(3.0)
+    acc_ref, y_ref = oracle.linear(q, s, packed, s_w, bias=bias)
+    y = torch.empty((M, N), dtype=out_dtype, device=DEV)
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    tw.bitnet_linear_ex(torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV),
+                        torch.from_numpy(packed).to(DEV), torch.tensor([s_w], device=DEV),
+                        None if bias is None else torch.from_numpy(bias).to(DEV), y, acc, kernel)
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    slack = _epilogue_tolerance(acc_ref, s, s_w, bias)
+    if out_dtype == torch.float32:
+        d = np.abs(y.cpu().numpy().astype(np.float64) - y_ref.astype(np.float64))
+        bad = d > REL * np.abs(y_ref.astype(np.float64)) + slack
+        assert not bad.any(), f"{bad.sum()} fp32 outputs outside the bound"
+        return
+    # bf16: the oracle's fp32 y rounded to nearest even; the library's fp32 value may
+    # sit one fp32 unit away, which moves its bf16 rounding by one bf16 unit at most
+    yb = y.cpu().view(torch.int16).numpy().view(np.uint16)
+    want = oracle.to_bf16(y_ref)
+    got_f = (yb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    want_f = (want.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    bad = np.abs(got_f - want_f) > 2.0 ** -7 * np.abs(want_f) + slack
+    assert not bad.any(), f"{bad.sum()} bf16 outputs more than one unit away"
+    assert (yb != want).mean() < 1e-3, "bf16 outputs differ from the oracle far more often than rounding allows"
+    # and the bf16 output is exactly the library's own fp32 result rounded to nearest even
+    y32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    tw.bitnet_linear_ex(torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV),
+                        torch.from_numpy(packed).to(DEV), torch.tensor([s_w], device=DEV),
+                        None if bias is None else torch.from_numpy(bias).to(DEV), y32, None, kernel)
+    rne = y32.cpu().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(yb, rne)
+
+
+def test_linear_ex_without_options_matches_linear():
+    """bias = NULL and fp32 output: bit-identical to bitnet_linear."""
+    M, N, K = 5, 300, 2560
+    key = synth.stream_key(312)
+    x, q, s = quantized_inputs(key, M, K)
+    packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
+    args = (torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV), torch.from_numpy(packed).to(DEV),
+            torch.tensor([0.011], device=DEV))
+    y1 = tw.linear(*args)
+    y2 = torch.empty_like(y1)
+    tw.bitnet_linear_ex(*args, None, y2, None, 0)
+    assert torch.equal(y1, y2)
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 5, 4), (3, 9, 68), (20, 33, 132), (2, 70, 2560 + 4)])
 def test_generic_path_parity(M, N, K):
     key = synth.stream_key(303, M, N, K)
