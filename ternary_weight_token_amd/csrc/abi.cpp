@@ -303,7 +303,7 @@ BITNET_API int bitnet_grouped_plan_quant(const bitnet_quant_desc *descs, int cou
 }
 
 static uint64_t fused_blocks(const bitnet_fused_desc &d) {
-    const uint64_t rows = gemv_grouped_rows_per_block();
+    const uint64_t rows = gemv_fused_rows_per_block();
     return ((uint64_t)d.N + rows - 1) / rows;
 }
 
@@ -335,8 +335,8 @@ BITNET_API int bitnet_grouped_plan_fused(const bitnet_fused_desc *descs, int cou
     h->kind = kPlanFused;
     h->count = (uint32_t)count;
     h->total_blocks = (uint32_t)blocks;
-    h->block_threads = gemv_grouped_threads();
-    h->rows_per_block = gemv_grouped_rows_per_block();
+    h->block_threads = gemv_fused_threads();
+    h->rows_per_block = gemv_fused_rows_per_block();
     for (int i = 0; i < count; ++i) h->lds_bytes = std::max(h->lds_bytes, gemv_grouped_lds_bytes(descs[i].K));
     h->desc_offset = doff;
     h->table_offset = toff;

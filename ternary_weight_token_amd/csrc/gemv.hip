@@ -19,6 +19,8 @@
 //  * partial sums are reduced across the octet with DPP; when the workgroup has
 //    several wavefronts they split K and combine their partials through LDS;
 //  * epilogue: y = fp32(acc * c_m), c_m = (s_x[m] * s_w) / 127 in float64.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -30,6 +32,15 @@
 #endif
 #ifndef BITNET_GEMV_NT
 #define BITNET_GEMV_NT 1
+#endif
+#ifndef BITNET_FUSED_NW
+#define BITNET_FUSED_NW 4        // wavefronts per workgroup of the fused grouped launch (4 or 8)
+#endif
+#ifndef BITNET_FUSED_PERSIST
+#define BITNET_FUSED_PERSIST 0   // > 0: the fused grouped launch uses at most this many workgroups
+#endif
+#ifndef BITNET_GEMV_PREISSUE
+#define BITNET_GEMV_PREISSUE 1   // weight steps issued before the q staging (1 or 2)
 #endif
 
 namespace bitnet {
@@ -81,12 +92,16 @@ __device__ __forceinline__ void mac16(uint32_t w, uint4 pq, int &hi, uint32_t &l
 // every thread of the workgroup between two barriers.
 
 // From int8 q in global memory.
+// Each stager has a load phase, issued before the segment's first weight loads (so
+// that waiting for its data does not wait for theirs), and the staging itself.
 template <int MT, bool DOT8>
 struct StageQ {
     const int8_t *q;
     int K;
-    __device__ __forceinline__ void operator()(int s0, int sc, int m0, int mcount, int seg_chunks, uint32_t *qs,
-                                               int *sq) const {
+    struct Pre {};
+    __device__ __forceinline__ Pre load(int, int) const { return Pre{}; }
+    __device__ __forceinline__ void operator()(const Pre &, int s0, int sc, int m0, int mcount, int seg_chunks,
+                                               uint32_t *qs, int *sq) const {
         const int tid = threadIdx.x;
         int part[MT];
         #pragma unroll
@@ -115,32 +130,43 @@ struct StageQ {
 // sec. 2.2, absmax_quantize): s = max|x| (integer max of the bf16 magnitude bits),
 // q = rint((127 x) / s), all zero for an all-zero row.  The row scale goes to LDS
 // (*s_lds) for the epilogue; q and s are also written out when q_out / s_out are set.
-template <bool DOT8>
+template <bool DOT8, int NW>
 struct StageQuantize {
+    static constexpr int kThreads = 64 * NW;
+    static constexpr int kPre = 512 / kThreads;   // pieces per thread held in registers (K <= 8192)
     const uint16_t *x;   // [K] bf16 bits, 16-byte aligned
     int8_t *q_out;       // [K] or nullptr
     float *s_out;        // or nullptr
     float *s_lds;        // LDS
-    uint32_t *red;       // LDS, one word per wavefront (4)
-    __device__ __forceinline__ void operator()(int, int sc, int, int, int, uint32_t *qs, int *sq) const {
+    uint32_t *red;       // LDS, one word per wavefront (NW)
+    // the first kPre pieces of 16 values of each thread
+    struct Pre { uint4 xr[kPre][2]; };
+    __device__ __forceinline__ Pre load(int, int sc) const {
+        const int pieces = sc * 4;
+        Pre p;
+        #pragma unroll
+        for (int j = 0; j < kPre; ++j) {
+            const int r = min((int)threadIdx.x + kThreads * j, pieces - 1);   // clamped duplicates leave the max as it is
+            p.xr[j][0] = gload16(x + 16 * r);
+            p.xr[j][1] = gload16(x + 16 * r + 8);
+        }
+        return p;
+    }
+    __device__ __forceinline__ void operator()(const Pre &pre, int, int sc, int, int, int, uint32_t *qs,
+                                               int *sq) const {
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
         const int pieces = sc * 4;  // pieces of 16 values (32 bytes of x)
-        // the first two pieces of each thread stay in registers (K <= 8192)
-        uint4 xr[2][2];
         uint32_t mx = 0;
         #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r = min(tid + 256 * j, pieces - 1);   // clamped duplicates leave the max as it is
-            xr[j][0] = gload16(x + 16 * r);
-            xr[j][1] = gload16(x + 16 * r + 8);
-            mx = max(mx, max(absmax8(xr[j][0]), absmax8(xr[j][1])));
-        }
-        for (int r = tid + 512; r < pieces; r += 256)
+        for (int j = 0; j < kPre; ++j) mx = max(mx, max(absmax8(pre.xr[j][0]), absmax8(pre.xr[j][1])));
+        for (int r = tid + 512; r < pieces; r += kThreads)
             mx = max(mx, max(absmax8(gload16(x + 16 * r)), absmax8(gload16(x + 16 * r + 8))));
         mx = wave_max_u32(mx);
         if (lane == 0) red[wave] = mx;
         __syncthreads();
-        mx = max(max(red[0], red[1]), max(red[2], red[3]));
+        mx = red[0];
+        #pragma unroll
+        for (int w = 1; w < NW; ++w) mx = max(mx, red[w]);
         const float s = bf16f(mx);
         const float inv = 1.0f / s;
         if (tid == 0) {
@@ -162,16 +188,16 @@ struct StageQuantize {
             part += dot4(a.w, 0x01010101u, sm);
         };
         #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r = tid + 256 * j;
-            if (r < pieces) emit(r, xr[j][0], xr[j][1]);
+        for (int j = 0; j < kPre; ++j) {
+            const int r = tid + kThreads * j;
+            if (r < pieces) emit(r, pre.xr[j][0], pre.xr[j][1]);
         }
-        for (int r = tid + 512; r < pieces; r += 256) emit(r, gload16(x + 16 * r), gload16(x + 16 * r + 8));
+        for (int r = tid + 512; r < pieces; r += kThreads) emit(r, gload16(x + 16 * r), gload16(x + 16 * r + 8));
         if (part != 0) atomicAdd(&sq[0], part);
     }
 };
 
-template <int MT, int RG, bool DOT8, bool NT, class Stage>
+template <int MT, int RG, bool DOT8, bool NT, int NW, class Stage>
 __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *__restrict__ s_x,
                                               const uint8_t *__restrict__ packed,
                                               const float *__restrict__ s_w, int M, int N, int K,
@@ -220,8 +246,9 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *_
         // alternate so that the loads of step t + 1 are in flight during step t.
         const int c0 = ((line_off + cb) & ~7) - line_off;
         const bool aligned = ((KB >> 4) & 7) == 0 && (cb & 7) == 0;
-        const int T = ((ce - cb + 7) >> 3) + (aligned ? 0 : 1);
-        const int clast = max(ce - 1, cb);
+        // a wave whose rows all lie past N loads (clamped, unused) but computes nothing
+        const int T = row0 < N ? ((ce - cb + 7) >> 3) + (aligned ? 0 : 1) : 0;
+        const int clast = min(max(ce - 1, cb), C - 1);   // in range even for an empty slice
         uint4 bufA[RG], bufB[RG];
         auto issue = [&](uint4 (&b)[RG], int t) {
             const int cc = min(max(c0 + l8 + 8 * t, cb), clast);
@@ -249,13 +276,18 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *_
                 }
             }
         };
-        // the segment's first weight loads go out before the staging of q, so that
-        // their latency overlaps it
-        if (T > 0) issue(bufA, 0);
+        // The stager's loads go out first, then the segment's first weight loads, so
+        // that the staging waits only for its own data while the weights are in flight.
+        // Both issues are unconditional (a step past the last reads a clamped in-range
+        // chunk and is never consumed): a branch here would make the compiler's wait
+        // for the stager's data also wait for these loads.
+        const typename Stage::Pre pre = stage.load(s0, sc);
+        issue(bufA, 0);
+        if (BITNET_GEMV_PREISSUE > 1) issue(bufB, 1);
 
         // ---- stage the segment of the M tile of q, rearranged, and its row sums
         __syncthreads();   // previous segment's LDS reads done; sq initialised
-        stage(s0, sc, m0, mcount, seg_chunks, qs, sq);
+        stage(pre, s0, sc, m0, mcount, seg_chunks, qs, sq);
         __syncthreads();
 
         // Pairs of chunks with no branch inside the loop body, so that the compiler
@@ -263,18 +295,40 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *_
         // peeled (a uniform branch outside the loop).
         if (T > 0) {
             const int T2 = (T + 1) & ~1;
-            for (int t = 0; t < T2 - 2; t += 2) {
-                issue(bufB, t + 1);
-                consume(bufA, t);
-                issue(bufA, t + 2);
-                consume(bufB, t + 1);
-            }
-            if (T2 == T) {
-                issue(bufB, T - 1);
-                consume(bufA, T - 2);
-                consume(bufB, T - 1);
+            if (BITNET_GEMV_PREISSUE > 1) {
+                // steps t and t + 1 are in flight at the top of every iteration
+                int t = 0;
+                for (; t + 3 < T; t += 2) {
+                    consume(bufA, t);
+                    issue(bufA, t + 2);
+                    consume(bufB, t + 1);
+                    issue(bufB, t + 3);
+                }
+                if (T - t == 3) {
+                    consume(bufA, t);
+                    issue(bufA, t + 2);
+                    consume(bufB, t + 1);
+                    consume(bufA, t + 2);
+                } else if (T - t == 2) {
+                    consume(bufA, t);
+                    consume(bufB, t + 1);
+                } else {
+                    consume(bufA, t);
+                }
             } else {
-                consume(bufA, T - 1);
+                for (int t = 0; t < T2 - 2; t += 2) {
+                    issue(bufB, t + 1);
+                    consume(bufA, t);
+                    issue(bufA, t + 2);
+                    consume(bufB, t + 1);
+                }
+                if (T2 == T) {
+                    issue(bufB, T - 1);
+                    consume(bufA, T - 2);
+                    consume(bufB, T - 1);
+                } else {
+                    consume(bufA, T - 1);
+                }
             }
         }
     }
@@ -316,7 +370,7 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *_
         }
     }
     __syncthreads();
-    const int rowsets = 4 / kslices;
+    const int rowsets = NW / kslices;
     for (int idx = tid; idx < rowsets * R * MT; idx += blockDim.x) {
         const int rsi = idx / (R * MT), rem = idx - rsi * R * MT;
         const int rr = rem / MT, m = rem - rr * MT;
@@ -339,7 +393,7 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(
     __shared__ int sq[MT];
     __shared__ int red[4 * 8 * RG * MT];
     const int rows_per_block = (4 / kslices) * 8 * RG;
-    gemv_lds_tile<MT, RG, DOT8, BITNET_GEMV_NT != 0>(StageQ<MT, DOT8>{q, K}, s_x, packed, s_w, M, N, K, out, acc_out,
+    gemv_lds_tile<MT, RG, DOT8, BITNET_GEMV_NT != 0, 4>(StageQ<MT, DOT8>{q, K}, s_x, packed, s_w, M, N, K, out, acc_out,
                                                      blockIdx.x * rows_per_block, blockIdx.y * MT, kslices,
                                                      seg_chunks, dyn, sq, red);
 }
@@ -369,7 +423,7 @@ __global__ __launch_bounds__(256) void gemv_grouped_kernel(const uint8_t *__rest
     const int rows = 4 * 8 * kGroupedRG;
     const int rowblocks = (d.N + rows - 1) / rows;
     const int rb = (int)(e.local % rowblocks), mt = (int)(e.local / rowblocks);
-    gemv_lds_tile<kGroupedMT, kGroupedRG, BITNET_GROUPED_DOT8 != 0, BITNET_GEMV_NT != 0>(
+    gemv_lds_tile<kGroupedMT, kGroupedRG, BITNET_GROUPED_DOT8 != 0, BITNET_GEMV_NT != 0, 4>(
         StageQ<kGroupedMT, BITNET_GROUPED_DOT8 != 0>{d.q, d.K}, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, OutSpec{d.y, nullptr, 0}, d.acc, rb * rows, mt * kGroupedMT, 1, segment_chunks(d.K >> 6, kGroupedMT), dyn,
         sq, red);
 }
@@ -378,32 +432,52 @@ __global__ __launch_bounds__(256) void gemv_grouped_kernel(const uint8_t *__rest
 // each problem's token row done by every workgroup of that problem in its q
 // staging step (one segment, so the row max covers the whole row).  The workgroup of
 // row block 0 also writes q and s_x out when the descriptor asks for them.
-__global__ __launch_bounds__(256) void gemv_fused_grouped_kernel(const uint8_t *__restrict__ plan) {
+constexpr int kFusedNW = BITNET_FUSED_NW;
+
+__global__ __launch_bounds__(64 * kFusedNW) void gemv_fused_grouped_kernel(const uint8_t *__restrict__ plan) {
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
     __shared__ int sq[1];
-    __shared__ int red[4 * 8 * kGroupedRG];
-    __shared__ uint32_t qred[4];
+    __shared__ int red[kFusedNW * 8 * kGroupedRG];
+    __shared__ uint32_t qred[kFusedNW];
     __shared__ float s_lds;
     const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
-    const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[blockIdx.x];
-    const FusedDescDev d = reinterpret_cast<const FusedDescDev *>(plan + h->desc_offset)[e.desc];
-    const int rows = 4 * 8 * kGroupedRG;
-    const bool first = e.local == 0;
-    const StageQuantize<BITNET_GROUPED_DOT8 != 0> stage{d.x, first ? d.q : nullptr, first ? d.s_x : nullptr,
-                                                         &s_lds, qred};
-    gemv_lds_tile<1, kGroupedRG, BITNET_GROUPED_DOT8 != 0, BITNET_GEMV_NT != 0>(
-        stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K, OutSpec{d.y, nullptr, 0}, d.acc, (int)e.local * rows, 0, 1, d.K >> 6, dyn, sq, red);
+    auto entry = [&](uint32_t b) {
+        const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[b];
+        const FusedDescDev d = reinterpret_cast<const FusedDescDev *>(plan + h->desc_offset)[e.desc];
+        const int rows = kFusedNW * 8 * kGroupedRG;
+        const bool first = e.local == 0;
+        const StageQuantize<BITNET_GROUPED_DOT8 != 0, kFusedNW> stage{d.x, first ? d.q : nullptr, first ? d.s_x : nullptr,
+                                                             &s_lds, qred};
+        gemv_lds_tile<1, kGroupedRG, BITNET_GROUPED_DOT8 != 0, BITNET_GEMV_NT != 0, kFusedNW>(
+            stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K, OutSpec{d.y, nullptr, 0}, d.acc, (int)e.local * rows, 0, 1,
+            d.K >> 6, dyn, sq, red);
+    };
+    if (BITNET_FUSED_PERSIST == 0) {
+        // one entry per workgroup and no loop: with memory operations of a previous
+        // entry pending at a loop head, the compiler's waits in the staging become
+        // waits for everything, weight loads included
+        entry(blockIdx.x);
+    } else {
+        for (uint32_t b = blockIdx.x; b < h->total_blocks; b += gridDim.x) {
+            entry(b);
+            __builtin_amdgcn_s_waitcnt(0);   // nothing pending at the loop head
+            __syncthreads();                  // LDS of this entry read by all before the next
+        }
+    }
 }
 
 // Longest K whose q fits one LDS segment of the grouped GEMV.
 int64_t gemv_fused_max_k() { return 64 * (int64_t)((kLdsBudget / (kLdsChunkDw * 4)) & ~7); }
 
 hipError_t launch_gemv_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st) {
-    gemv_fused_grouped_kernel<<<dim3(blocks), dim3(256), lds_bytes, st>>>(reinterpret_cast<const uint8_t *>(plan_dev));
+    if (BITNET_FUSED_PERSIST > 0) blocks = std::min<uint32_t>(blocks, BITNET_FUSED_PERSIST);
+    gemv_fused_grouped_kernel<<<dim3(blocks), dim3(64 * kFusedNW), lds_bytes, st>>>(reinterpret_cast<const uint8_t *>(plan_dev));
     return hipGetLastError();
 }
 
 uint32_t gemv_grouped_rows_per_block() { return 4 * 8 * kGroupedRG; }
+uint32_t gemv_fused_rows_per_block() { return kFusedNW * 8 * kGroupedRG; }
+uint32_t gemv_fused_threads() { return 64 * kFusedNW; }
 uint32_t gemv_grouped_threads() { return 256; }
 uint32_t gemv_grouped_lds_bytes(int64_t K) {
     return (uint32_t)(kGroupedMT * segment_chunks((int)(K / 64), kGroupedMT) * kLdsChunkDw * 4);
