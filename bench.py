@@ -90,7 +90,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--legs", default="two_launch,prefill,sweep,decode_m8,ffn100b",
+    ap.add_argument("--legs", default="two_launch,rmsnorm,prefill,sweep,decode_m8,ffn100b",
                     help="secondary legs to run (comma-separated subset of the default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -234,6 +234,33 @@ def main() -> int:
                 "gemv_grouped_kernel_GBs": round(gemv_bytes / (g_us * 1e-6) / 1e9, 1)}
             log(f"two-launch step: {step_us:.1f} us (grouped GEMV {g_us:.1f} us)")
             del qs, sxs, qplan, lplan
+        if "rmsnorm" in legs:
+            # the same fused step with the RMSNorm of the attention and FFN inputs folded
+            # into the q / k / v and gate / up problems (their workgroups normalize the
+            # token row with the layer's gain before quantizing it)
+            gains = [W.decode_step_gains(l, dev) for l in range(30)]
+            nys = [torch.empty_like(y) for y in ys]
+            nplan = tw.bitnet_grouped_plan_fused(
+                [(xs[m.layer][m.slot], packed[i], sws[i], nys[i], None, None, None,
+                  gains[m.layer].get(m.slot), 1e-6) for i, m in enumerate(mats)])
+            for _ in range(200):
+                nplan.launch(stream)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(200):
+                nplan.launch(stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            n_us = a.elapsed_time(b) * 1e3 / 200
+            for y in nys:
+                assert torch.isfinite(y).all()
+            sec["decode_step_2p4b_rmsnorm_fused"] = {
+                "us": round(n_us, 1), "weight_GBs": round(weight_bytes / (n_us * 1e-6) / 1e9, 1),
+                "normed_matrices": sum(1 for m in mats if m.slot in W.NORMED_SLOTS_2P4B),
+                "vs_plain_fused_us": round(n_us - kern_ms * 1e3, 1)}
+            log(f"fused step with RMSNorm: {n_us:.1f} us ({n_us - kern_ms * 1e3:+.1f} us vs without)")
+            del nplan, nys, gains
         if "prefill" in legs:
             # prefill GEMM, M = 2048
             reps = 50

@@ -119,6 +119,31 @@ BITNET_API int bitnet_quant_act(const uint16_t *x, int64_t M, int64_t K,
                                 int8_t *q, float *s_x, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * RMSNorm of each token row followed by the same absmax int8 quantization of the
+ * normalized row.  Page: chenxutan.com sec. 3.1 (the block normalizes the token
+ * row with an RMSNorm kept in full precision before every projection; the linear
+ * layer quantizes its input, sec. 2.2).
+ *
+ *   x     (device) bf16 bit patterns [M][K]
+ *   gain  (device) fp32 [K], the norm's elementwise gain g
+ *   eps   added to the mean square (finite, >= 0)
+ *   q     (device) int8 [M][K], output;  s_x (device) fp32 [M], output
+ *
+ * The normalized value is the real number h = x g r, r = 1 / sqrt(mean_k x^2 +
+ * eps).  Its codes are q = round_half_even(127 h / max|h|) = round_half_even(127
+ * z / max|z|) with z = x g (r cancels), decided exactly (z and 127 z are exact in
+ * float64 and the quotient is never rounded onto or across a half-integer); its
+ * scale is s_x = max|h| = max|z| r, formed in float64 and rounded once to fp32
+ * (the sum of squares in float64, in an order of the kernel's choosing).  A row
+ * of zeros gives q = 0 and s_x = 0.  bitnet_linear then rescales with this s_x
+ * as with any activation row.  Needs K % 8 == 0 and 16-byte aligned x, q and gain
+ * (BITNET_ERR_SHAPE / BITNET_ERR_ALIGN).
+ * ------------------------------------------------------------------------- */
+BITNET_API int bitnet_rmsnorm_quant_act(const uint16_t *x, const float *gain, float eps,
+                                        int64_t M, int64_t K, int8_t *q, float *s_x,
+                                        void *stream);
+
+/* ---------------------------------------------------------------------------
  * Ternary contraction with the fp32 rescale (BitLinear forward after the two
  * quantizations).  Pages: chenxutan.com sec. 2.3 (Y ~ (W_t . X_q) * act_scale *
  * beta) and sec. 3.1 (BitLinear.forward); the ternary product is a sign-select
@@ -237,7 +262,11 @@ BITNET_API int bitnet_quant_act_grouped(const void *plan_host, const void *plan_
  *
  * Descriptors: M = 1, K % 64 == 0, K <= 52224 (the row's q fits one LDS
  * segment), x / packed / q 16-byte aligned.  Plans are built and launched like
- * the other grouped plans (host image + device copy).
+ * the other grouped plans (host image + device copy).  A descriptor with
+ * norm_gain set is bit-identical to bitnet_rmsnorm_quant_act(x, norm_gain,
+ * norm_eps) followed by bitnet_linear instead (the RMSNorm before each projection
+ * of chenxutan.com sec. 3.1, fused the same way; problems sharing a token row and
+ * gain, such as q / k / v, each normalize it in their own workgroups).
  * ------------------------------------------------------------------------- */
 typedef struct bitnet_fused_desc {
     const uint16_t *x;      /* (device) [M][K] bf16 bits */
@@ -248,6 +277,9 @@ typedef struct bitnet_fused_desc {
     int8_t *q;              /* (device) [M][K] or NULL */
     float *s_x;             /* (device) [M] or NULL */
     int64_t M, N, K;
+    const float *norm_gain; /* (device) [K] fp32, 16-byte aligned, or NULL: when set, the
+                               row is RMSNorm-ed first (bitnet_rmsnorm_quant_act) */
+    float norm_eps;         /* the norm's eps (finite, >= 0); ignored without norm_gain */
 } bitnet_fused_desc;
 
 BITNET_API size_t bitnet_grouped_plan_fused_bytes(int count, const bitnet_fused_desc *descs);

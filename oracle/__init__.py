@@ -48,6 +48,7 @@ def lib():
         L.oracle_linear.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, P, P]
         L.oracle_linear_bias.argtypes = [P, P, P, ctypes.c_float, P, I64, I64, I64, P, P]
         L.oracle_to_bf16.argtypes = [P, I64, P]
+        L.oracle_rmsnorm_quant.argtypes = [P, P, ctypes.c_float, I64, I64, P, P]
         L.oracle_set_threads.argtypes = [ctypes.c_int]
         L.oracle_get_threads.restype = ctypes.c_int
         _lib = L
@@ -101,6 +102,19 @@ def quant_act(x_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     q = np.empty((M, K), dtype=np.int8)
     s = np.empty(M, dtype=np.float32)
     lib().oracle_quant_act(_p(x_bits), M, K, _p(q), _p(s))
+    return q, s
+
+
+def rmsnorm_quant(x_bits: np.ndarray, gain: np.ndarray, eps: float) -> tuple[np.ndarray, np.ndarray]:
+    """RMSNorm (gain g, eps) then absmax int8 of the normalized row:
+    x_bits uint16 [M][K] bf16 patterns, gain fp32 [K] -> (q int8 [M][K], s_x fp32 [M])."""
+    x_bits = np.ascontiguousarray(x_bits).view(np.uint16)
+    gain = np.ascontiguousarray(gain, dtype=np.float32)
+    M, K = x_bits.shape
+    assert gain.shape == (K,)
+    q = np.empty((M, K), dtype=np.int8)
+    s = np.empty(M, dtype=np.float32)
+    lib().oracle_rmsnorm_quant(_p(x_bits), _p(gain), ctypes.c_float(eps), M, K, _p(q), _p(s))
     return q, s
 
 

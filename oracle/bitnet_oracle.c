@@ -158,6 +158,51 @@ void oracle_quant_act(const uint16_t *x, int64_t M, int64_t K,
     }
 }
 
+/* --- RMSNorm before the activation quantization ([P1] 3.1) -------------- */
+
+/* The block of [P1] 3.1 feeds its projections from an RMSNorm of the token row;
+ * [P1] keeps the norm in full precision and quantizes its output inside the
+ * linear layer (absmax, [P1] 2.2).  Here the norm's value is the real number
+ *     h_k = x_k g_k r,   r = 1 / sqrt(mean_k(x_k^2) + eps),
+ * and it is quantized like any activation row:
+ *     s = max_k |h_k| = r max_k |x_k g_k|,   q_k = RNE(127 h_k / s).
+ * r cancels in q_k = RNE(127 z_k / max|z|) with z_k = x_k g_k, which float64
+ * holds exactly (8 + 24 significant bits); 127 z_k too, and the one rounding of
+ * the quotient cannot create or cross a half-integer (127 z / max|z| is a ratio
+ * of integers below 2^40 times powers of two, so it is either a tie exactly or
+ * at least 2^-41 relatively away from one).  The scale s_x = fp32(max|z| r) is
+ * formed in float64 with the sum of squares taken k = 0 .. K-1 in order.  An
+ * all-zero row (max|z| = 0) gives q = 0 and s_x = 0.
+ *   x: bf16 bits [M][K]; g: fp32 [K]; outputs q int8 [M][K], s_x fp32 [M]. */
+void oracle_rmsnorm_quant(const uint16_t *x, const float *g, float eps, int64_t M, int64_t K,
+                          int8_t *q, float *s_x) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *row = x + m * K;
+        double mz = 0.0, ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double xv = (double)bf16_to_float(row[k]);
+            const double z = xv * (double)g[k];
+            if (fabs(z) > mz) mz = fabs(z);
+            ss += xv * xv;
+        }
+        if (mz == 0.0) {
+            s_x[m] = 0.0f;
+            for (int64_t k = 0; k < K; ++k) q[m * K + k] = 0;
+            continue;
+        }
+        const double r = 1.0 / sqrt(ss / (double)K + (double)eps);
+        s_x[m] = (float)(mz * r);
+        for (int64_t k = 0; k < K; ++k) {
+            const double z = (double)bf16_to_float(row[k]) * (double)g[k];
+            double v = rint((127.0 * z) / mz);
+            if (v > 127.0) v = 127.0;
+            if (v < -127.0) v = -127.0;
+            q[m * K + k] = (int8_t)v;
+        }
+    }
+}
+
 /* --- contraction and rescale ([P1] 2.3, 3.1 BitLinear.forward) ---------- */
 
 /* acc[m][n] = sum_k q[m][k] * t[n][k]  (exact integer sum)

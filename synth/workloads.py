@@ -55,6 +55,24 @@ def decode_step_activations(layer: int, device="cpu", M: int = 1):
             for s, K in enumerate(SLOT_K_2P4B)]
 
 
+# activation slots that an RMSNorm precedes (the attention input and the FFN input
+# of chenxutan.com sec. 3.1's block); the other two read the attention output and
+# the FFN hidden state
+NORMED_SLOTS_2P4B = (0, 2)
+
+
+def decode_step_gains(layer: int, device="cpu"):
+    """fp32 RMSNorm gains of one layer, {slot: [K]}: 1 + 0.1 N(0, 1), seeded per
+    layer and slot (random-init stand-ins for the trained gains)."""
+    from . import normal
+    out = {}
+    for s in NORMED_SLOTS_2P4B:
+        K = SLOT_K_2P4B[s]
+        g = 1.0 + 0.1 * normal(stream_key(CFG_DECODE, layer, 200 + s), K, device).to(torch.float64)
+        out[s] = g.to(torch.float32)
+    return out
+
+
 def ffn_100b(layers: int = 8):
     out = []
     for l in range(layers):

@@ -32,7 +32,8 @@ class _LinearDesc(ctypes.Structure):
 class _FusedDesc(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("packed", ctypes.c_void_p), ("s_w", ctypes.c_void_p),
                 ("y", ctypes.c_void_p), ("acc", ctypes.c_void_p), ("q", ctypes.c_void_p),
-                ("s_x", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+                ("s_x", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("norm_gain", ctypes.c_void_p), ("norm_eps", ctypes.c_float)]
 
 
 class _QuantDesc(ctypes.Structure):
@@ -57,6 +58,7 @@ def lib() -> ctypes.CDLL:
         L.bitnet_pack_workspace_bytes.restype = ctypes.c_size_t
         L.bitnet_pack_weights.argtypes = [P, I64, I64, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
         L.bitnet_quant_act.argtypes = [P, I64, I64, P, P, P]
+        L.bitnet_rmsnorm_quant_act.argtypes = [P, P, ctypes.c_float, I64, I64, P, P, P]
         L.bitnet_linear.argtypes = [P, P, P, P, I64, I64, I64, P, P, P]
         L.bitnet_linear_select.argtypes = [P, P, P, P, I64, I64, I64, P, P, I, P]
         L.bitnet_linear_ex.argtypes = [P, P, P, P, I64, I64, I64, P, P, I, P, I, P]
@@ -70,7 +72,7 @@ def lib() -> ctypes.CDLL:
         L.bitnet_grouped_plan_fused_bytes.restype = ctypes.c_size_t
         L.bitnet_grouped_plan_fused.argtypes = [P, I, P, ctypes.c_size_t]
         L.bitnet_linear_fused_grouped.argtypes = [P, P, P]
-        for f in ("bitnet_pack_weights", "bitnet_quant_act", "bitnet_linear", "bitnet_linear_select", "bitnet_linear_ex",
+        for f in ("bitnet_pack_weights", "bitnet_quant_act", "bitnet_rmsnorm_quant_act", "bitnet_linear", "bitnet_linear_select", "bitnet_linear_ex",
                   "bitnet_grouped_plan_linear", "bitnet_grouped_plan_quant", "bitnet_grouped_plan_fused",
                   "bitnet_linear_grouped", "bitnet_quant_act_grouped", "bitnet_linear_fused_grouped"):
             getattr(L, f).restype = I
@@ -127,6 +129,18 @@ def bitnet_quant_act(x: torch.Tensor, q: torch.Tensor, s_x: torch.Tensor, stream
     if q.shape != (M, K) or s_x.shape != (M,):
         raise ValueError("q must be [M][K] and s_x [M]")
     _check(lib().bitnet_quant_act(_ptr(x), M, K, _ptr(q), _ptr(s_x), _stream(stream)))
+
+
+def bitnet_rmsnorm_quant_act(x: torch.Tensor, gain: torch.Tensor, eps: float, q: torch.Tensor,
+                             s_x: torch.Tensor, stream=None) -> None:
+    """x bf16 [M][K], gain fp32 [K] -> q int8 [M][K], s_x fp32 [M] of the RMSNorm-ed rows."""
+    _dev(x, torch.bfloat16, "x"); _dev(gain, torch.float32, "gain")
+    _dev(q, torch.int8, "q"); _dev(s_x, torch.float32, "s_x")
+    M, K = x.shape
+    if gain.shape != (K,) or q.shape != (M, K) or s_x.shape != (M,):
+        raise ValueError("gain must be [K], q [M][K] and s_x [M]")
+    _check(lib().bitnet_rmsnorm_quant_act(_ptr(x), _ptr(gain), ctypes.c_float(eps), M, K, _ptr(q), _ptr(s_x),
+                                          _stream(stream)))
 
 
 def bitnet_linear(q: torch.Tensor, s_x: torch.Tensor, packed: torch.Tensor, s_w: torch.Tensor,
@@ -246,17 +260,25 @@ def bitnet_grouped_plan_quant(problems, device=None) -> GroupedPlan:
 
 
 def bitnet_grouped_plan_fused(problems, device=None) -> GroupedPlan:
-    """problems: list of (x, packed, s_w, y, acc_or_None, q_or_None, s_x_or_None); x is
-    bf16 [1][K] (quantized inside the launch)."""
+    """problems: list of (x, packed, s_w, y, acc_or_None, q_or_None, s_x_or_None
+    [, norm_gain, norm_eps]); x is bf16 [1][K] (quantized inside the launch, after an
+    RMSNorm with the fp32 gain [K] when one is given)."""
     arr = (_FusedDesc * len(problems))()
     refs = []
-    for i, (x, packed, s_w, y, acc, q, s_x) in enumerate(problems):
+    for i, prob in enumerate(problems):
+        x, packed, s_w, y, acc, q, s_x = prob[:7]
+        gain, eps = (prob[7], float(prob[8])) if len(prob) > 7 and prob[7] is not None else (None, 0.0)
         _dev(x, torch.bfloat16, "x")
         M, K = x.shape
+        if gain is not None:
+            _dev(gain, torch.float32, "norm_gain")
+            if gain.shape != (K,):
+                raise ValueError("norm_gain must be [K]")
         arr[i] = _FusedDesc(x.data_ptr(), packed.data_ptr(), s_w.data_ptr(), y.data_ptr(),
                             0 if acc is None else acc.data_ptr(), 0 if q is None else q.data_ptr(),
-                            0 if s_x is None else s_x.data_ptr(), M, packed.shape[0], K)
-        refs.append((x, packed, s_w, y, acc, q, s_x))
+                            0 if s_x is None else s_x.data_ptr(), M, packed.shape[0], K,
+                            0 if gain is None else gain.data_ptr(), eps)
+        refs.append((x, packed, s_w, y, acc, q, s_x, gain))
     n = lib().bitnet_grouped_plan_fused_bytes(len(problems), ctypes.cast(arr, ctypes.c_void_p))
     buf = ctypes.create_string_buffer(n)
     _check(lib().bitnet_grouped_plan_fused(ctypes.cast(arr, ctypes.c_void_p), len(problems),
@@ -276,6 +298,14 @@ def pack_weights(w: torch.Tensor, eps: float = 1e-5, stream=None):
     ws = torch.empty(max(1, bitnet_pack_workspace_bytes(N, K) // 8), dtype=torch.float64, device=w.device)
     bitnet_pack_weights(w, eps, packed, s_w, ws, stream)
     return packed, s_w
+
+
+def rmsnorm_quant(x: torch.Tensor, gain: torch.Tensor, eps: float, stream=None):
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    s_x = torch.empty(M, dtype=torch.float32, device=x.device)
+    bitnet_rmsnorm_quant_act(x, gain, eps, q, s_x, stream)
+    return q, s_x
 
 
 def quant_act(x: torch.Tensor, stream=None):

@@ -104,6 +104,19 @@ BITNET_API int bitnet_quant_act(const uint16_t *x, int64_t M, int64_t K, int8_t 
     return hip_status(launch_quant_act(x, M, K, q, s_x, (hipStream_t)stream));
 }
 
+BITNET_API int bitnet_rmsnorm_quant_act(const uint16_t *x, const float *gain, float eps, int64_t M, int64_t K,
+                                        int8_t *q, float *s_x, void *stream) {
+    int st = check_dims(M, 1, K);
+    if (st) return st;
+    if (M == 0) return BITNET_OK;
+    if (!x || !gain || !q || !s_x) return fail(BITNET_ERR_NULL, "null pointer");
+    if (K % 8 != 0) return fail(BITNET_ERR_SHAPE, "K must be a multiple of 8");
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(gain, 16) || !aligned(s_x, 4) || (K * 2) % 16 != 0)
+        return fail(BITNET_ERR_ALIGN, "x, q and gain must be 16-byte aligned (rows too), s_x 4-byte");
+    if (!(eps >= 0.0f) || eps > 3.4e38f) return fail(BITNET_ERR_ARG, "eps must be finite and >= 0");
+    return hip_status(launch_rmsnorm_quant(x, gain, eps, M, K, q, s_x, (hipStream_t)stream));
+}
+
 BITNET_API int bitnet_linear_ex(const int8_t *q, const float *s_x, const uint8_t *packed,
                                 const float *s_w, int64_t M, int64_t N, int64_t K, const float *bias,
                                 void *y, int y_dtype, int32_t *acc, int kernel, void *stream) {
@@ -186,6 +199,10 @@ static int check_fused_desc(const bitnet_fused_desc &d) {
         return fail(BITNET_ERR_ALIGN, "fused linear needs K % 64 == 0 and 16-byte aligned x, packed and q");
     if (!aligned(d.s_w, 4) || !aligned(d.y, 4) || (d.acc && !aligned(d.acc, 4)) || (d.s_x && !aligned(d.s_x, 4)))
         return fail(BITNET_ERR_ALIGN, "s_w, y, acc and s_x must be 4-byte aligned");
+    if (d.norm_gain) {
+        if (!aligned(d.norm_gain, 16)) return fail(BITNET_ERR_ALIGN, "norm_gain must be 16-byte aligned");
+        if (!(d.norm_eps >= 0.0f) || d.norm_eps > 3.4e38f) return fail(BITNET_ERR_ARG, "norm_eps must be finite and >= 0");
+    }
     return BITNET_OK;
 }
 
@@ -337,6 +354,9 @@ BITNET_API int bitnet_grouped_plan_fused(const bitnet_fused_desc *descs, int cou
     h->total_blocks = (uint32_t)blocks;
     h->block_threads = gemv_fused_threads();
     h->rows_per_block = gemv_fused_rows_per_block();
+    h->variant = kVariantFused;
+    for (int i = 0; i < count; ++i)
+        if (descs[i].norm_gain) h->variant = kVariantFusedNorm;
     for (int i = 0; i < count; ++i) h->lds_bytes = std::max(h->lds_bytes, gemv_grouped_lds_bytes(descs[i].K));
     h->desc_offset = doff;
     h->table_offset = toff;
@@ -345,7 +365,8 @@ BITNET_API int bitnet_grouped_plan_fused(const bitnet_fused_desc *descs, int cou
     BlockEntry *tb = (BlockEntry *)(p + toff);
     for (int i = 0; i < count; ++i) {
         const bitnet_fused_desc &d = descs[i];
-        dd[i] = FusedDescDev{d.x, d.packed, d.s_w, d.y, d.acc, d.q, d.s_x, (int32_t)d.M, (int32_t)d.N, (int32_t)d.K, 0};
+        dd[i] = FusedDescDev{d.x, d.packed, d.s_w, d.y, d.acc, d.q, d.s_x, (int32_t)d.M, (int32_t)d.N, (int32_t)d.K, 0,
+                             d.norm_gain, d.norm_gain ? d.norm_eps : 0.0f, 0};
     }
     // longest rows first, as for linear plans
     std::vector<int> order(count);
@@ -383,7 +404,9 @@ BITNET_API int bitnet_linear_fused_grouped(const void *plan_host, const void *pl
     if (st) return st;
     const PlanHeader *h = (const PlanHeader *)plan_host;
     if (h->total_blocks == 0) return BITNET_OK;
-    return hip_status(launch_gemv_fused_grouped(plan_dev, h->total_blocks, h->lds_bytes, (hipStream_t)stream));
+    if (h->variant != kVariantFused && h->variant != kVariantFusedNorm) return fail(BITNET_ERR_ARG, "not a plan of this kind");
+    return hip_status(launch_gemv_fused_grouped(plan_dev, h->total_blocks, h->lds_bytes,
+                                                h->variant == kVariantFusedNorm, (hipStream_t)stream));
 }
 
 BITNET_API int bitnet_quant_act_grouped(const void *plan_host, const void *plan_dev, void *stream) {

@@ -163,6 +163,68 @@ __device__ __forceinline__ uint2 qcode8(uint4 u, float s, float inv) {
     return make_uint2(b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24, b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24);
 }
 
+// ---- RMSNorm before the quantization (page chenxutan.com sec. 3.1: the block
+// normalizes the token row in full precision; the linear layer quantizes the
+// result, sec. 2.2).  The normalized value is the real x g r, r = 1 / sqrt(mean(x^2)
+// + eps); its absmax codes are rint(127 z / max|z|) with z = x g (r cancels) and
+// its scale is max|z| r.  z is exact in float64 (bf16 x, fp32 g), and so is 127 z.
+
+__device__ __forceinline__ double wave_max_f64(double v) {
+    #pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    #pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Code of z for mz = max|z| > 0, with c = 127 / mz: t = z c is within 2^-51 |t| of
+// 127 z / mz, and a ratio of that form is either exactly a half-integer or at least
+// 2^-41 relatively away from one, so rint(t) is the exact rounding unless t lies
+// within 2^-45 |t| of a half-integer; there the correctly rounded division decides
+// (it keeps an exact tie exact).
+__device__ __forceinline__ int rms_code(double z, double c, double mz) {
+    const double t = z * c;
+    double r = rint(t);
+    if (fabs(fabs(t - r) - 0.5) <= 0x1p-45 * fabs(t)) r = rint((127.0 * z) / mz);
+    r = fmin(fmax(r, -127.0), 127.0);
+    return (int)r;
+}
+
+// Codes of 8 values (bf16 x in u, fp32 gains in g0 / g1) as 8 int8 bytes.
+__device__ __forceinline__ uint2 rms_code8(uint4 u, float4 g0, float4 g1, double c, double mz) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    uint32_t b[8];
+    #pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        b[2 * j] = (uint32_t)rms_code((double)bf16f(w[j] & 0xFFFFu) * (double)g[2 * j], c, mz) & 0xFFu;
+        b[2 * j + 1] = (uint32_t)rms_code((double)bf16f(w[j] >> 16) * (double)g[2 * j + 1], c, mz) & 0xFFu;
+    }
+    return make_uint2(b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24, b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24);
+}
+
+// max|x g| and sum x^2 over 8 values.
+__device__ __forceinline__ void rms_acc8(uint4 u, float4 g0, float4 g1, double &mz, double &ss) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    #pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float xf = bf16f(j & 1 ? w[j >> 1] >> 16 : w[j >> 1] & 0xFFFFu);
+        mz = fmax(mz, fabs((double)xf * (double)g[j]));
+        ss += (double)(xf * xf);   // x^2 is exact in fp32 for bf16 x
+    }
+}
+
+// Scale of the normalized row: max|z| / sqrt(mean(x^2) + eps), in float64.
+__device__ __forceinline__ float rms_scale(double mz, double ss, int K, float eps) {
+    if (mz == 0.0) return 0.0f;
+    const double r = 1.0 / sqrt(ss / (double)K + (double)eps);
+    return (float)(mz * r);
+}
+
 // y = fp32(acc * c) with c = (s_x * s_w) / 127 formed in float64.
 __device__ __forceinline__ double rescale_factor(float s_x, float s_w) {
     return ((double)s_x * (double)s_w) / 127.0;

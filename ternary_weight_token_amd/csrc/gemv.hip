@@ -197,8 +197,91 @@ struct StageQuantize {
     }
 };
 
+// From the bf16 activation row with an RMSNorm first (page chenxutan.com sec. 3.1):
+// the codes and scale of the normalized row (device_common.h, rms_*), computed in
+// the workgroup from x and the gain; otherwise as StageQuantize.  The load phase
+// holds one piece of 16 values (x and gain) per thread (all of K <= 64 NW 16).
+template <bool DOT8, int NW>
+struct StageRmsQuantize {
+    static constexpr int kThreads = 64 * NW;
+    const uint16_t *x;   // [K] bf16 bits, 16-byte aligned
+    const float *gain;   // [K], 16-byte aligned
+    float eps;
+    int8_t *q_out;       // [K] or nullptr
+    float *s_out;        // or nullptr
+    float *s_lds;        // LDS
+    double *red;         // LDS, 2 NW doubles
+    struct Pre { uint4 x0, x1; float4 g0, g1, g2, g3; };
+    __device__ __forceinline__ Pre load(int, int sc) const {
+        const int r = min((int)threadIdx.x, sc * 4 - 1);
+        Pre p;
+        p.x0 = gload16(x + 16 * r);
+        p.x1 = gload16(x + 16 * r + 8);
+        const float4 *g = reinterpret_cast<const float4 *>(gain + 16 * r);
+        p.g0 = g[0]; p.g1 = g[1]; p.g2 = g[2]; p.g3 = g[3];
+        return p;
+    }
+    __device__ __forceinline__ void operator()(const Pre &pre, int, int sc, int, int, int, uint32_t *qs,
+                                               int *sq) const {
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int pieces = sc * 4;
+        auto gain4 = [&](int r, float4 (&g)[4]) {
+            const float4 *gp = reinterpret_cast<const float4 *>(gain + 16 * r);
+            g[0] = gp[0]; g[1] = gp[1]; g[2] = gp[2]; g[3] = gp[3];
+        };
+        double mz = 0.0, ss = 0.0;
+        if (tid < pieces) {
+            rms_acc8(pre.x0, pre.g0, pre.g1, mz, ss);
+            rms_acc8(pre.x1, pre.g2, pre.g3, mz, ss);
+        }
+        for (int r = tid + kThreads; r < pieces; r += kThreads) {
+            float4 g[4];
+            gain4(r, g);
+            rms_acc8(gload16(x + 16 * r), g[0], g[1], mz, ss);
+            rms_acc8(gload16(x + 16 * r + 8), g[2], g[3], mz, ss);
+        }
+        mz = wave_max_f64(mz);
+        ss = wave_sum_f64(ss);
+        if (lane == 0) { red[wave] = mz; red[NW + wave] = ss; }
+        __syncthreads();
+        mz = red[0];
+        ss = red[NW];
+        #pragma unroll
+        for (int w = 1; w < NW; ++w) { mz = fmax(mz, red[w]); ss += red[NW + w]; }
+        const float s = rms_scale(mz, ss, 64 * sc, eps);
+        const double c = mz > 0.0 ? 127.0 / mz : 0.0;
+        if (tid == 0) {
+            *s_lds = s;
+            if (s_out) *s_out = s;
+        }
+        int part = 0;
+        auto emit = [&](int r, uint4 u0, uint4 u1, float4 g0, float4 g1, float4 g2, float4 g3) {
+            uint4 a = make_uint4(0u, 0u, 0u, 0u);
+            if (mz > 0.0) {
+                const uint2 lo = rms_code8(u0, g0, g1, c, mz), hi = rms_code8(u1, g2, g3, c, mz);
+                a = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+            if (q_out) *reinterpret_cast<uint4 *>(q_out + 16 * r) = a;
+            *reinterpret_cast<uint4 *>(qs + (r >> 2) * kLdsChunkDw + 4 * (r & 3)) = prep16<DOT8>(a);
+            int sm = dot4(a.x, 0x01010101u, 0);
+            sm = dot4(a.y, 0x01010101u, sm);
+            sm = dot4(a.z, 0x01010101u, sm);
+            part += dot4(a.w, 0x01010101u, sm);
+        };
+        if (tid < pieces) emit(tid, pre.x0, pre.x1, pre.g0, pre.g1, pre.g2, pre.g3);
+        for (int r = tid + kThreads; r < pieces; r += kThreads) {
+            float4 g[4];
+            gain4(r, g);
+            emit(r, gload16(x + 16 * r), gload16(x + 16 * r + 8), g[0], g[1], g[2], g[3]);
+        }
+        if (part != 0) atomicAdd(&sq[0], part);
+    }
+};
+
 template <int MT, int RG, bool DOT8, bool NT, int NW, class Stage>
-__device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *__restrict__ s_x,
+// s_x is not restrict-qualified: in the fused kernels it is the LDS word the stager
+// writes through its own pointer, and its reads must stay after the staging.
+__device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s_x,
                                               const uint8_t *__restrict__ packed,
                                               const float *__restrict__ s_w, int M, int N, int K,
                                               const OutSpec &out, int32_t *__restrict__ acc_out,
@@ -434,11 +517,16 @@ __global__ __launch_bounds__(256) void gemv_grouped_kernel(const uint8_t *__rest
 // row block 0 also writes q and s_x out when the descriptor asks for them.
 constexpr int kFusedNW = BITNET_FUSED_NW;
 
+// NORM: the plan has problems with an RMSNorm (each problem then takes the stager
+// its descriptor asks for); plans without one use the kernel without that path,
+// which needs fewer registers.
+template <bool NORM>
 __global__ __launch_bounds__(64 * kFusedNW) void gemv_fused_grouped_kernel(const uint8_t *__restrict__ plan) {
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
     __shared__ int sq[1];
     __shared__ int red[kFusedNW * 8 * kGroupedRG];
     __shared__ uint32_t qred[kFusedNW];
+    __shared__ double dred[2 * kFusedNW];
     __shared__ float s_lds;
     const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
     auto entry = [&](uint32_t b) {
@@ -446,11 +534,19 @@ __global__ __launch_bounds__(64 * kFusedNW) void gemv_fused_grouped_kernel(const
         const FusedDescDev d = reinterpret_cast<const FusedDescDev *>(plan + h->desc_offset)[e.desc];
         const int rows = kFusedNW * 8 * kGroupedRG;
         const bool first = e.local == 0;
-        const StageQuantize<BITNET_GROUPED_DOT8 != 0, kFusedNW> stage{d.x, first ? d.q : nullptr, first ? d.s_x : nullptr,
-                                                             &s_lds, qred};
-        gemv_lds_tile<1, kGroupedRG, BITNET_GROUPED_DOT8 != 0, BITNET_GEMV_NT != 0, kFusedNW>(
-            stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K, OutSpec{d.y, nullptr, 0}, d.acc, (int)e.local * rows, 0, 1,
-            d.K >> 6, dyn, sq, red);
+        if (NORM && d.gain) {
+            const StageRmsQuantize<BITNET_GROUPED_DOT8 != 0, kFusedNW> stage{
+                d.x, d.gain, d.eps, first ? d.q : nullptr, first ? d.s_x : nullptr, &s_lds, dred};
+            gemv_lds_tile<1, kGroupedRG, BITNET_GROUPED_DOT8 != 0, BITNET_GEMV_NT != 0, kFusedNW>(
+                stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K, OutSpec{d.y, nullptr, 0}, d.acc, (int)e.local * rows, 0,
+                1, d.K >> 6, dyn, sq, red);
+        } else {
+            const StageQuantize<BITNET_GROUPED_DOT8 != 0, kFusedNW> stage{d.x, first ? d.q : nullptr,
+                                                                          first ? d.s_x : nullptr, &s_lds, qred};
+            gemv_lds_tile<1, kGroupedRG, BITNET_GROUPED_DOT8 != 0, BITNET_GEMV_NT != 0, kFusedNW>(
+                stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K, OutSpec{d.y, nullptr, 0}, d.acc, (int)e.local * rows, 0,
+                1, d.K >> 6, dyn, sq, red);
+        }
     };
     if (BITNET_FUSED_PERSIST == 0) {
         // one entry per workgroup and no loop: with memory operations of a previous
@@ -469,9 +565,14 @@ __global__ __launch_bounds__(64 * kFusedNW) void gemv_fused_grouped_kernel(const
 // Longest K whose q fits one LDS segment of the grouped GEMV.
 int64_t gemv_fused_max_k() { return 64 * (int64_t)((kLdsBudget / (kLdsChunkDw * 4)) & ~7); }
 
-hipError_t launch_gemv_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st) {
+hipError_t launch_gemv_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, bool norm,
+                                     hipStream_t st) {
     if (BITNET_FUSED_PERSIST > 0) blocks = std::min<uint32_t>(blocks, BITNET_FUSED_PERSIST);
-    gemv_fused_grouped_kernel<<<dim3(blocks), dim3(64 * kFusedNW), lds_bytes, st>>>(reinterpret_cast<const uint8_t *>(plan_dev));
+    const uint8_t *p = reinterpret_cast<const uint8_t *>(plan_dev);
+    if (norm)
+        gemv_fused_grouped_kernel<true><<<dim3(blocks), dim3(64 * kFusedNW), lds_bytes, st>>>(p);
+    else
+        gemv_fused_grouped_kernel<false><<<dim3(blocks), dim3(64 * kFusedNW), lds_bytes, st>>>(p);
     return hipGetLastError();
 }
 

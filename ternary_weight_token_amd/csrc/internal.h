@@ -28,6 +28,8 @@ constexpr uint32_t kPlanLinear = 1, kPlanQuant = 2, kPlanFused = 3;
 // Linear plan variants: one block per (row block, token) running the GEMV, or one
 // block per row block running the MFMA decode kernel for all tokens at once.
 constexpr uint32_t kVariantGemv = 0, kVariantMfma = 1;
+// Fused plan variants: no problem with an RMSNorm, or some.
+constexpr uint32_t kVariantFused = 0, kVariantFusedNorm = 1;
 
 struct PlanHeader {            // 64 bytes
     uint32_t magic, kind, count, total_blocks;
@@ -46,10 +48,11 @@ struct QuantDescDev {          // 32 bytes
     int32_t M, K;
 };
 
-struct FusedDescDev {          // 72 bytes: quantization + linear of one token row
+struct FusedDescDev {          // 88 bytes: (RMSNorm +) quantization + linear of one token row
     const uint16_t *x; const uint8_t *packed; const float *s_w;
     float *y; int32_t *acc; int8_t *q; float *s_x;
     int32_t M, N, K, pad;
+    const float *gain; float eps; int32_t pad2;
 };
 
 struct BlockEntry { uint32_t desc, local; };
@@ -58,13 +61,16 @@ struct BlockEntry { uint32_t desc, local; };
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int8_t *q, float *s_x,
                             hipStream_t st);
 hipError_t launch_quant_act_grouped(const void *plan_dev, uint32_t blocks, hipStream_t st);
+hipError_t launch_rmsnorm_quant(const uint16_t *x, const float *g, float eps, int64_t M, int64_t K, int8_t *q,
+                                float *s_x, hipStream_t st);
 hipError_t launch_pack(const float *w, int64_t N, int64_t K, float eps, uint8_t *packed,
                        float *s_w, double *rowsum, hipStream_t st);
 hipError_t launch_gemv(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                        int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st);
 hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st);
 uint32_t gemv_grouped_lds_bytes(int64_t K);
-hipError_t launch_gemv_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st);
+hipError_t launch_gemv_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, bool norm,
+                                     hipStream_t st);
 int64_t gemv_fused_max_k();
 uint32_t gemv_grouped_rows_per_block();
 uint32_t gemv_fused_rows_per_block();

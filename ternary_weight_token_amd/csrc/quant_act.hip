@@ -61,6 +61,44 @@ __global__ __launch_bounds__(kQThreads) void quant_act_grouped_kernel(const uint
     quant_row<true>(d.x + m * d.K, d.K, d.q + m * d.K, d.s_x + m);
 }
 
+// RMSNorm of the row with gain g, then the same quantization of the normalized row
+// (device_common.h, rms_*): pass 1 takes max|x g| (float64, exact) and sum x^2
+// (float64), reduced over the workgroup; pass 2 re-reads the row and writes the codes.
+// Vector path: K % 8 == 0, x and q 16-byte aligned, g 16-byte aligned.
+__global__ __launch_bounds__(kQThreads) void rmsnorm_quant_kernel(const uint16_t *__restrict__ x,
+                                                                  const float *__restrict__ g, float eps,
+                                                                  int K, int8_t *__restrict__ q,
+                                                                  float *__restrict__ s_x) {
+    __shared__ double red[2][kQThreads / 64];
+    const size_t m = blockIdx.x;
+    const uint16_t *xr = x + m * K;
+    int8_t *qr = q + m * K;
+    const int tid = threadIdx.x;
+    const uint4 *xv = reinterpret_cast<const uint4 *>(xr);
+    const float4 *gv = reinterpret_cast<const float4 *>(g);
+    double mz = 0.0, ss = 0.0;
+    for (int v = tid; v < (K >> 3); v += kQThreads) rms_acc8(xv[v], gv[2 * v], gv[2 * v + 1], mz, ss);
+    mz = wave_max_f64(mz);
+    ss = wave_sum_f64(ss);
+    if ((tid & 63) == 0) { red[0][tid >> 6] = mz; red[1][tid >> 6] = ss; }
+    __syncthreads();
+    mz = red[0][0];
+    ss = red[1][0];
+    #pragma unroll
+    for (int w = 1; w < kQThreads / 64; ++w) { mz = fmax(mz, red[0][w]); ss += red[1][w]; }
+    if (tid == 0) s_x[m] = rms_scale(mz, ss, K, eps);
+    const double c = mz > 0.0 ? 127.0 / mz : 0.0;
+    uint2 *qv = reinterpret_cast<uint2 *>(qr);
+    for (int v = tid; v < (K >> 3); v += kQThreads)
+        qv[v] = mz > 0.0 ? rms_code8(xv[v], gv[2 * v], gv[2 * v + 1], c, mz) : make_uint2(0u, 0u);
+}
+
+hipError_t launch_rmsnorm_quant(const uint16_t *x, const float *g, float eps, int64_t M, int64_t K, int8_t *q,
+                                float *s_x, hipStream_t st) {
+    rmsnorm_quant_kernel<<<dim3((unsigned)M), dim3(kQThreads), 0, st>>>(x, g, eps, (int)K, q, s_x);
+    return hipGetLastError();
+}
+
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int8_t *q, float *s_x,
                             hipStream_t st) {
     const bool vec = (K % 8 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)q % 16 == 0);

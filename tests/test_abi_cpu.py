@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -177,3 +177,38 @@ def test_fused_plan_checks(L):
     dev = ctypes.c_void_p(4096)
     assert L.bitnet_linear_grouped(ctypes.cast(buf, ctypes.c_void_p), dev, None) == ARG
     assert L.bitnet_quant_act_grouped(ctypes.cast(buf, ctypes.c_void_p), dev, None) == ARG
+
+
+def test_rmsnorm_quant_rejects_bad_arguments(L):
+    p = ctypes.c_void_p(256)  # never dereferenced: every call below fails its checks
+    z = None
+    f = ctypes.c_float
+    assert L.bitnet_rmsnorm_quant_act(p, z, f(1e-6), 1, 64, p, p, z) == NULL
+    assert L.bitnet_rmsnorm_quant_act(p, p, f(1e-6), 1, 60, p, p, z) == SHAPE    # K % 8
+    assert L.bitnet_rmsnorm_quant_act(ctypes.c_void_p(264), p, f(1e-6), 1, 64, p, p, z) == ALIGN
+    assert L.bitnet_rmsnorm_quant_act(p, ctypes.c_void_p(260), f(1e-6), 1, 64, p, p, z) == ALIGN
+    assert L.bitnet_rmsnorm_quant_act(p, p, f(-1.0), 1, 64, p, p, z) == ARG
+    assert L.bitnet_rmsnorm_quant_act(p, p, f(float("nan")), 1, 64, p, p, z) == ARG
+    assert L.bitnet_rmsnorm_quant_act(z, z, f(0.0), 0, 64, z, z, z) == OK
+
+
+def test_fused_plan_norm_checks_and_variant(L):
+    F = tw._FusedDesc
+    a16 = 4096
+    n = ctypes.c_float
+    good = F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, a16, n(1e-6))
+    arr = (F * 2)(good, F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, 0, n(0.0)))
+    nb = L.bitnet_grouped_plan_fused_bytes(2, arr)
+    buf = ctypes.create_string_buffer(nb)
+    assert L.bitnet_grouped_plan_fused(arr, 2, buf, nb) == OK
+    hdr = (ctypes.c_uint32 * 8).from_buffer_copy(buf.raw[:32])
+    assert hdr[1] == 3 and hdr[7] == 1          # fused plan, variant with RMSNorm
+    arr1 = (F * 1)(F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, 0, n(0.0)))
+    nb1 = L.bitnet_grouped_plan_fused_bytes(1, arr1)
+    buf1 = ctypes.create_string_buffer(nb1)
+    assert L.bitnet_grouped_plan_fused(arr1, 1, buf1, nb1) == OK
+    assert (ctypes.c_uint32 * 8).from_buffer_copy(buf1.raw[:32])[7] == 0
+    for d, want in ((F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, a16 + 4, n(1e-6)), ALIGN),
+                    (F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, a16, n(-1.0)), ARG)):
+        one = (F * 1)(d)
+        assert L.bitnet_grouped_plan_fused(one, 1, buf, nb) == want

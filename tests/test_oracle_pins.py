@@ -445,3 +445,82 @@ def test_linear_bias_broadcast_over_tokens():
     _, y = oracle.linear(q, s, packed, np.float32(0.5), bias=bias)
     assert np.array_equal(y[0], bias) and np.array_equal(y[2], bias)
     assert not np.array_equal(y[1], bias)
+
+
+# ----------------------------------------------------------------- RMSNorm + quantization
+
+def _rms_scale_exact(z_max: Fraction, xs, eps: float) -> float:
+    """fp32 of z_max / sqrt(mean(x^2) + eps), the square root to 60 digits."""
+    import decimal
+    ctx = decimal.Context(prec=60)
+    ms = sum(Fraction(float(v)) ** 2 for v in xs) / len(xs) + Fraction(float(np.float32(eps)))
+    d = ctx.sqrt(ctx.divide(decimal.Decimal(ms.numerator), decimal.Decimal(ms.denominator)))
+    val = ctx.divide(decimal.Decimal(z_max.numerator), decimal.Decimal(z_max.denominator))
+    return round_fraction_to_f32(Fraction(ctx.divide(val, d)))
+
+
+def test_rmsnorm_quant_hand_case():
+    x = f32_to_bf16_bits(np.array([[1.0, 2.0, 0.0, -1.0]], np.float32))
+    q, s = oracle.rmsnorm_quant(x, np.ones(4, np.float32), 1e-6)
+    # 127 z / max|z| = 63.5, 127, 0, -63.5: the halves go to the even neighbour
+    assert q.tolist() == [[64, 127, 0, -64]]
+    assert s[0] == np.float32(_rms_scale_exact(Fraction(2), [1.0, 2.0, 0.0, -1.0], 1e-6))
+
+
+def test_rmsnorm_quant_unit_gain_is_plain_quantization():
+    """With g = 1 the codes are those of the row itself (r cancels) and the scale is
+    max|x| r."""
+    key = synth.stream_key(20)
+    x = synth.activations(key, 6, 640, outlier_frac=0.01, row_scale=(0.1, 10.0))
+    bits = synth.bf16_bits(x).numpy().view(np.uint16)
+    q0, s0 = oracle.quant_act(bits)
+    q1, s1 = oracle.rmsnorm_quant(bits, np.ones(640, np.float32), 1e-5)
+    assert np.array_equal(q0, q1)
+    xf = bf16_bits_to_f32(bits)
+    for m in range(6):
+        assert s1[m] == np.float32(_rms_scale_exact(Fraction(float(s0[m])), xf[m].tolist(), 1e-5))
+
+
+@pytest.mark.parametrize("K", [4, 68, 256])
+def test_rmsnorm_quant_exact(K):
+    """Codes against exact rational RNE of 127 x g / max|x g|; scale against the
+    60-digit value of max|x g| / sqrt(mean(x^2) + eps)."""
+    key = synth.stream_key(21, K)
+    x = synth.activations(key, 5, K, outlier_frac=0.02)
+    bits = synth.bf16_bits(x).numpy().view(np.uint16)
+    g = (1.0 + 0.3 * synth.normal(synth.stream_key(key, 7), K).float().numpy()).astype(np.float32)
+    g[::7] = -g[::7]
+    eps = 1e-6
+    q, s = oracle.rmsnorm_quant(bits, g, eps)
+    xf = bf16_bits_to_f32(bits)
+    for m in range(5):
+        z = [Fraction(float(xf[m, k])) * Fraction(float(g[k])) for k in range(K)]
+        zmax = max(abs(v) for v in z)
+        for k in range(K):
+            v = 127 * z[k] / zmax
+            fl = v.numerator // v.denominator
+            rem = v - fl
+            r = fl + (1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2) else 0)
+            assert q[m, k] == r, (m, k)
+        assert s[m] == np.float32(_rms_scale_exact(zmax, xf[m].tolist(), eps)), m
+
+
+def test_rmsnorm_quant_invariants():
+    key = synth.stream_key(22)
+    K = 512
+    x = synth.activations(key, 4, K)
+    bits = synth.bf16_bits(x).numpy().view(np.uint16)
+    g = (0.5 + synth.uniform(synth.stream_key(key, 3), K, 0).float().numpy()).astype(np.float32)
+    q, s = oracle.rmsnorm_quant(bits, g, 0.0)
+    # x -> 2x (exact in bf16) with eps = 0 changes nothing, bit for bit
+    x2 = f32_to_bf16_bits(bf16_bits_to_f32(bits) * np.float32(2.0))
+    q2, s2 = oracle.rmsnorm_quant(x2, g, 0.0)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+    # x -> -x negates the codes
+    qn, sn = oracle.rmsnorm_quant(bits ^ np.uint16(0x8000), g, 0.0)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    # every row reaches 127 in magnitude
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    # an all-zero row
+    qz, sz = oracle.rmsnorm_quant(np.zeros((1, K), np.uint16), g, 1e-6)
+    assert not qz.any() and sz[0] == 0.0

@@ -253,6 +253,81 @@ def test_fused_quant_linear_grouped(with_outputs):
                 assert np.array_equal(pr[6].cpu().numpy(), sx_ref)
 
 
+# ----------------------------------------------------------------- RMSNorm + quantization
+
+def _gain(key, K):
+    g = (1.0 + 0.25 * synth.normal(synth.stream_key(key, 11), K).float().numpy()).astype(np.float32)
+    g[::5] = -g[::5]
+    return g
+
+
+def assert_scale(s_gpu, s_ref):
+    """The scale of a normalized row: within one fp32 unit (the sum of squares is
+    taken in float64 in another order than the oracle's)."""
+    s_gpu = s_gpu.astype(np.float64)
+    s_ref = s_ref.astype(np.float64)
+    assert np.all(np.abs(s_gpu - s_ref) <= 2.0 ** -23 * np.abs(s_ref)), "scale more than one unit away"
+
+
+@pytest.mark.parametrize("M,K,kw,eps", [(1, 2560, {}, 1e-6), (5, 6912, {"outlier_frac": 0.001}, 1e-5),
+                                        (3, 64, {}, 0.0), (17, 640, {"row_scale": (1e-3, 1e3)}, 1e-6),
+                                        (2, 52224, {"outlier_frac": 0.01}, 1e-6)])
+def test_rmsnorm_quant_parity(M, K, kw, eps):
+    key = synth.stream_key(320, M, K)
+    x = synth.activations(key, M, K, **kw)
+    if M > 2:
+        x[1].zero_()
+    g = _gain(key, K)
+    q_ref, s_ref = oracle.rmsnorm_quant(bits_np(x), g, eps)
+    q, s = tw.rmsnorm_quant(x.to(DEV), torch.from_numpy(g).to(DEV), eps)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert_scale(s.cpu().numpy(), s_ref)
+
+
+@pytest.mark.parametrize("with_outputs", [True, False])
+def test_fused_rmsnorm_linear_grouped(with_outputs):
+    """One fused launch mixing problems with and without an RMSNorm: codes and acc
+    exact, the scale within one fp32 unit, y within 2^-22 (the scale's unit plus the
+    rescale's rounding) of the oracle's rmsnorm_quant + linear."""
+    shapes = [(300, 2560, True), (640, 2560, True), (97, 6912, False), (129, 12288, True), (64, 64, True),
+              (200, 2560, False), (33, 2560, "zero")]
+    probs, refs = [], []
+    for i, (N, K, norm) in enumerate(shapes):
+        key = synth.stream_key(321, i)
+        x = torch.zeros((1, K), dtype=torch.bfloat16) if norm == "zero" else synth.activations(key, 1, K, outlier_frac=0.002)
+        packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
+        s_w = np.float32(0.0071 * (i + 1))
+        if norm:
+            g = _gain(key, K)
+            q_ref, sx_ref = oracle.rmsnorm_quant(bits_np(x), g, 1e-6)
+        else:
+            g = None
+            q_ref, sx_ref = oracle.quant_act(bits_np(x))
+        acc_ref, y_ref = oracle.linear(q_ref, sx_ref, packed, s_w)
+        refs.append((q_ref, sx_ref, acc_ref, y_ref, bool(norm)))
+        y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+        acc = torch.empty((1, N), dtype=torch.int32, device=DEV)
+        q = torch.full((1, K), 99, dtype=torch.int8, device=DEV) if with_outputs else None
+        sx = torch.full((1,), -1.0, dtype=torch.float32, device=DEV) if with_outputs else None
+        probs.append((x.to(DEV), torch.from_numpy(packed).to(DEV), torch.tensor([s_w], device=DEV), y, acc, q, sx,
+                      None if g is None else torch.from_numpy(g).to(DEV), 1e-6))
+    plan = tw.bitnet_grouped_plan_fused(probs)
+    for _ in range(2):
+        for pr in probs:
+            pr[3].fill_(float("nan"))
+            pr[4].fill_(-1)
+        plan.launch()
+        torch.cuda.synchronize()
+        for (q_ref, sx_ref, acc_ref, y_ref, norm), pr in zip(refs, probs):
+            assert np.array_equal(pr[4].cpu().numpy(), acc_ref)
+            yd = np.abs(pr[3].cpu().numpy().astype(np.float64) - y_ref.astype(np.float64))
+            assert np.all(yd <= (2.0 ** -22 if norm else 2.0 ** -23) * np.abs(y_ref.astype(np.float64)))
+            if with_outputs:
+                assert np.array_equal(pr[5].cpu().numpy(), q_ref)
+                assert_scale(pr[6].cpu().numpy(), sx_ref)
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 200, 53312), (2, 70, 26176), (3, 200, 16704), (8, 200, 16704),
                                    (13, 130, 8192), (16, 65, 28672)])
 def test_gemv_parity_k_segments(M, N, K):
