@@ -49,6 +49,8 @@ def lib():
         L.oracle_linear_bias.argtypes = [P, P, P, ctypes.c_float, P, I64, I64, I64, P, P]
         L.oracle_to_bf16.argtypes = [P, I64, P]
         L.oracle_rmsnorm_quant.argtypes = [P, P, ctypes.c_float, I64, I64, P, P]
+        L.oracle_pack_grouped.argtypes = [P, I64, I64, I64, ctypes.c_float, P, P]
+        L.oracle_linear_grouped.argtypes = [P, P, P, P, I64, P, I64, I64, I64, P, P]
         L.oracle_set_threads.argtypes = [ctypes.c_int]
         L.oracle_get_threads.restype = ctypes.c_int
         _lib = L
@@ -85,6 +87,37 @@ def pack(w: np.ndarray, eps: float = 1e-5) -> tuple[np.ndarray, np.float32]:
     out = np.empty((N, K // 4), dtype=np.uint8)
     lib().oracle_pack(_p(w), N, K, ctypes.c_float(eps), ctypes.c_float(s_w), _p(out))
     return out, s_w
+
+
+def pack_grouped(w: np.ndarray, group: int, eps: float = 1e-5) -> tuple[np.ndarray, np.ndarray]:
+    """Group-wise absmean scales (group = K: one per output channel) ->
+    (packed uint8 [N][K/4], s_w fp32 [N][K/group])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    assert group > 0 and K % group == 0 and group % 4 == 0
+    packed = np.empty((N, K // 4), dtype=np.uint8)
+    s_w = np.empty((N, K // group), dtype=np.float32)
+    lib().oracle_pack_grouped(_p(w), N, K, group, ctypes.c_float(eps), _p(s_w), _p(packed))
+    return packed, s_w
+
+
+def linear_grouped(q: np.ndarray, s_x: np.ndarray, packed: np.ndarray, s_w: np.ndarray, group: int,
+                   bias: np.ndarray | None = None):
+    """-> (acc int32 [M][N] (whole-row sums), y fp32 [M][N]) with group-wise scales."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s_x = np.ascontiguousarray(s_x, dtype=np.float32)
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    s_w = np.ascontiguousarray(s_w, dtype=np.float32)
+    M, K = q.shape
+    N = packed.shape[0]
+    assert packed.shape[1] * 4 == K and s_w.shape == (N, K // group)
+    acc = np.empty((M, N), dtype=np.int32)
+    y = np.empty((M, N), dtype=np.float32)
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+    lib().oracle_linear_grouped(_p(q), _p(s_x), _p(packed), _p(s_w), group,
+                                None if bias is None else _p(bias), M, N, K, _p(acc), _p(y))
+    return acc, y
 
 
 def unpack(packed: np.ndarray, K: int) -> np.ndarray:

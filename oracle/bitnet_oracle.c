@@ -113,7 +113,36 @@ void oracle_pack(const float *w, int64_t N, int64_t K, float eps,
     }
 }
 
-/* Decode one weight from the packed layout (code - 1; code 3 -> +2). */
+/* Group-wise scales ([P1] 3.1: a weight_scale per output channel; [P1] 4.3:
+ * groups of group_size consecutive weights, each with its own scale; [P5] 2.1:
+ * scales per channel): row n is cut into K / G groups of G consecutive k; group g
+ * gets s = fp32(mean |w| over the group) (float64 sum, k ascending) and its codes
+ * t = clamp(rint(w / fl32(s + eps)), -1, 1) as in oracle_pack.  G = K is one scale
+ * per output channel.  s_w: [N][K / G]. */
+void oracle_pack_grouped(const float *w, int64_t N, int64_t K, int64_t G, float eps,
+                         float *s_w, uint8_t *packed) {
+    const int64_t ng = K / G, KB = K / 4;
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < ng; ++g) {
+            double sum = 0.0;
+            for (int64_t k = g * G; k < (g + 1) * G; ++k) sum += fabs((double)w[n * K + k]);
+            s_w[n * ng + g] = (float)(sum / (double)G);
+        }
+        for (int64_t j = 0; j < KB; ++j) {
+            unsigned byte = 0;
+            for (int i = 0; i < 4; ++i) {
+                const int64_t k = 4 * j + i;
+                const float d = s_w[n * ng + k / G] + eps;
+                const int t = ternary_of(w[n * K + k], d);
+                byte |= (unsigned)(t + 1) << (2 * i);
+            }
+            packed[n * KB + j] = (uint8_t)byte;
+        }
+    }
+}
+
+/* Decode one weight from the packed layout (code - 1; code 3 -> +2). *//* Decode one weight from the packed layout (code - 1; code 3 -> +2). */
 static int weight_at(const uint8_t *packed, int64_t KB, int64_t n, int64_t k) {
     unsigned byte = packed[n * KB + k / 4];
     unsigned code = (byte >> (2 * (k % 4))) & 3u;
@@ -223,6 +252,35 @@ void oracle_linear_bias(const int8_t *q, const float *s_x, const uint8_t *packed
             if (acc) acc[m * N + n] = (int32_t)a;
             double v = (double)a * (double)s_x[m];
             v = v * (double)s_w;
+            v = v / 127.0;
+            if (bias) v = v + (double)bias[n];
+            y[m * N + n] = (float)v;
+        }
+    }
+}
+
+/* Group-wise scales: acc_g[m][n] = sum over group g of q t (exact integer), and
+ * y[m][n] = fp32( (sum_g acc_g s_w[n][g]) * s_x[m] / 127 (+ bias[n]) ), the sum
+ * over g ascending, all in float64; acc[m][n] = sum_g acc_g (the whole-row
+ * integer sum, for inspection).  acc and bias may be NULL. */
+void oracle_linear_grouped(const int8_t *q, const float *s_x, const uint8_t *packed,
+                           const float *s_w, int64_t G, const float *bias, int64_t M, int64_t N,
+                           int64_t K, int32_t *acc, float *y) {
+    const int64_t KB = K / 4, ng = K / G;
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            int64_t total = 0;
+            double v = 0.0;
+            for (int64_t g = 0; g < ng; ++g) {
+                int64_t a = 0;
+                for (int64_t k = g * G; k < (g + 1) * G; ++k)
+                    a += (int64_t)q[m * K + k] * (int64_t)weight_at(packed, KB, n, k);
+                total += a;
+                v += (double)a * (double)s_w[n * ng + g];
+            }
+            if (acc) acc[m * N + n] = (int32_t)total;
+            v = v * (double)s_x[m];
             v = v / 127.0;
             if (bias) v = v + (double)bias[n];
             y[m * N + n] = (float)v;

@@ -524,3 +524,82 @@ def test_rmsnorm_quant_invariants():
     # an all-zero row
     qz, sz = oracle.rmsnorm_quant(np.zeros((1, K), np.uint16), g, 1e-6)
     assert not qz.any() and sz[0] == 0.0
+
+
+# ----------------------------------------------------------------- group-wise weight scales
+
+def test_pack_grouped_hand_case():
+    """Two groups of 4 in one row (eps = 0): group 0 = [0.5, -0.25, 0.1, 0] has
+    mean |w| = 0.2125 and w / s = [2.35, -1.18, 0.47, 0] -> t = [1, -1, 0, 0] ->
+    codes [2, 0, 1, 1] -> byte 0x52; group 1 = [2, 0.5, -0.5, 1] has mean 1 and
+    w / s = [2, 0.5, -0.5, 1] -> t = [1, 0, 0, 1] (halves to even) -> byte 0x96."""
+    w = np.array([[0.5, -0.25, 0.1, 0.0, 2.0, 0.5, -0.5, 1.0]], np.float32)
+    packed, s_w = oracle.pack_grouped(w, 4, 0.0)
+    assert packed.tolist() == [[0x52, 0x96]]
+    assert s_w[0, 0] == np.float32(round_fraction_to_f32(
+        (Fraction(0.5) + Fraction(0.25) + Fraction(float(np.float32(0.1)))) / 4))
+    assert s_w[0, 1] == 1.0
+
+
+def test_pack_per_channel_is_per_tensor_of_each_row():
+    key = synth.stream_key(23)
+    N, K = 7, 640
+    w = synth.latent_weights(key, N, K, 0.02).numpy()
+    w[3] *= 5.0
+    packed, s_w = oracle.pack_grouped(w, K, 1e-5)
+    for n in range(N):
+        p_row, s_row = oracle.pack(np.ascontiguousarray(w[n:n + 1]), 1e-5)
+        assert np.array_equal(packed[n:n + 1], p_row) and s_w[n, 0] == s_row
+
+
+@pytest.mark.parametrize("G", [4, 128, 640])
+def test_pack_grouped_scales_exact(G):
+    key = synth.stream_key(24, G)
+    N, K = 5, 640
+    w = synth.latent_weights(key, N, K, 0.02).numpy()
+    packed, s_w = oracle.pack_grouped(w, G, 1e-5)
+    for n in range(N):
+        for g in range(K // G):
+            exact = sum(Fraction(float(abs(v))) for v in w[n, g * G:(g + 1) * G]) / G
+            assert s_w[n, g] == np.float32(round_fraction_to_f32(exact))
+    # each group's codes are the per-tensor codes of that group alone
+    for n in (0, 4):
+        for g in (0, K // G - 1):
+            p_g, s_g = oracle.pack(np.ascontiguousarray(w[n:n + 1, g * G:(g + 1) * G]), 1e-5)
+            assert s_g == s_w[n, g] and np.array_equal(p_g[0], packed[n, g * G // 4:(g + 1) * G // 4])
+
+
+@pytest.mark.parametrize("M,N,K,G", [(1, 3, 256, 64), (3, 5, 512, 128), (2, 4, 384, 384)])
+def test_linear_grouped_exact(M, N, K, G):
+    key = synth.stream_key(25, M, N, K, G)
+    x = synth.activations(key, M, K, row_scale=(0.1, 10.0))
+    q, s = oracle.quant_act(synth.bf16_bits(x).numpy().view(np.uint16))
+    w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02).numpy()
+    w[:, :G] *= 7.0                      # groups with very different scales
+    packed, s_w = oracle.pack_grouped(w, G, 1e-5)
+    bias = np.linspace(-1, 1, N).astype(np.float32)
+    acc, y = oracle.linear_grouped(q, s, packed, s_w, G, bias=bias)
+    t = decode_unpackbits(packed, K).astype(np.int64)
+    for m in range(M):
+        for n in range(N):
+            groups = [int(np.dot(q[m, g * G:(g + 1) * G].astype(np.int64), t[n, g * G:(g + 1) * G]))
+                      for g in range(K // G)]
+            assert acc[m, n] == sum(groups)
+            exact = (sum(Fraction(a) * Fraction(float(s_w[n, g])) for g, a in enumerate(groups))
+                     * Fraction(float(s[m])) / 127 + Fraction(float(bias[n])))
+            assert y[m, n] == np.float32(round_fraction_to_f32(exact)), (m, n)
+
+
+def test_linear_grouped_uniform_scales_match_per_tensor():
+    """Every group with the same scale s: within one fp32 unit of the per-tensor form
+    (the two associate the float64 products differently)."""
+    key = synth.stream_key(26)
+    M, N, K, G = 3, 9, 512, 128
+    x = synth.activations(key, M, K)
+    q, s = oracle.quant_act(synth.bf16_bits(x).numpy().view(np.uint16))
+    packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
+    s_w = np.full((N, K // G), 0.0137, np.float32)
+    acc_g, y_g = oracle.linear_grouped(q, s, packed, s_w, G)
+    acc_t, y_t = oracle.linear(q, s, packed, np.float32(0.0137))
+    assert np.array_equal(acc_g, acc_t)
+    assert np.all(np.abs(y_g.astype(np.float64) - y_t) <= 2.0 ** -23 * np.abs(y_t.astype(np.float64)))
