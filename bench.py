@@ -90,7 +90,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--legs", default="two_launch,rmsnorm,prefill,sweep,decode_m8,ffn100b",
+    ap.add_argument("--legs", default="two_launch,rmsnorm,prefill,sweep,decode_m8,ffn100b,scales",
                     help="secondary legs to run (comma-separated subset of the default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -385,6 +385,36 @@ def main() -> int:
             us = graph_us(torch, lambda: tw.bitnet_linear(q1, s1, shard, fsw[0], y1), reps=50)
             sec["colsplit8_gate_shard_M1"] = {"us": round(us, 2), "weight_GBs": round(shard.numel() / (us * 1e-6) / 1e9, 1)}
             del fpacked
+        if "scales" in legs:
+            # weight-scale granularity on the 100B-scale FFN stream at M = 1 (HBM-bound):
+            # one scale per tensor, per output channel, per group of 128 weights; 24
+            # GEMV launches per stream, captured in one graph
+            fmats = W.ffn_100b(8)
+            variants = {"per_tensor": 0, "per_channel": -1, "group128": 128}
+            packs = {v: [] for v in variants}
+            for m in fmats:
+                w = W.weights(m, dev)
+                packs["per_tensor"].append(tw.pack_weights(w, 1e-5))
+                packs["per_channel"].append(tw.pack_weights_grouped(w, m.K, 1e-5))
+                packs["group128"].append(tw.pack_weights_grouped(w, 128, 1e-5))
+                del w
+            xq = [[tw.quant_act(x) for x in W.ffn_100b_activations(l, 1, dev)] for l in range(8)]
+            fys = [torch.empty((1, m.N), dtype=torch.float32, device=dev) for m in fmats]
+            wbytes = sum(m.N * m.K // 4 for m in fmats)
+            res = {}
+            for v, g in variants.items():
+                def stream_fn(v=v, g=g):
+                    for i, m in enumerate(fmats):
+                        q_, s_ = xq[m.layer][m.slot]
+                        p_, sw_ = packs[v][i]
+                        tw.bitnet_linear_ex(q_, s_, p_, sw_, None, fys[i], None, 0, w_group=(m.K if g < 0 else g))
+                us = graph_us(torch, stream_fn, reps=2, replays=5)
+                sbytes = sum(p_[1].numel() * 4 for p_ in packs[v])
+                res[v] = {"us": round(us, 1), "weight_GBs": round(wbytes / (us * 1e-6) / 1e9, 1),
+                          "scale_bytes": sbytes, "launches": len(fmats)}
+                log(f"ffn100b M=1 scales {v}: {us:.1f} us, {res[v]['weight_GBs']} GB/s")
+            sec["ffn100b_8layers_M1_weight_scales"] = res
+            del packs
         line["secondary"] = sec
 
     # ------------------------------------------------------------ CPU baseline

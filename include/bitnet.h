@@ -183,13 +183,44 @@ enum bitnet_dtype {
     BITNET_BF16 = 1   /* bfloat16 (upper half of binary32), uint16 storage */
 };
 
+/* ---------------------------------------------------------------------------
+ * Weights with group-wise scales.  Pages: chenxutan.com sec. 3.1 (a weight_scale
+ * per output channel), sec. 4.3 (group-wise quantization, groups of group_size
+ * consecutive weights, commonly 128, each with its own scale); 0539edu.com sec.
+ * 2.1 (scales per layer and per channel).
+ *
+ *   w       (device) fp32 [N][K]
+ *   group   G: a multiple of 4 dividing K; G = K is one scale per output channel
+ *   packed  (device) uint8 [N][K/4], output (the same 2-bit format)
+ *   s_w     (device) fp32 [N][K/G], output
+ *
+ * Group g of row n (k = g G .. g G + G - 1) gets s_w[n][g] = fp32(mean |w|) (sum
+ * in float64, k ascending) and codes clamp(rint(w / fl32(s_w[n][g] + eps)), -1, 1)
+ * with binary32 operations, as bitnet_pack_weights does for the whole tensor.
+ * ------------------------------------------------------------------------- */
+BITNET_API int bitnet_pack_weights_grouped(const float *w, int64_t N, int64_t K, int64_t group,
+                                           float eps, uint8_t *packed, float *s_w, void *stream);
+
 /* bitnet_linear_select with the two epilogue options of the BitLinear forward
  * (chenxutan.com sec. 3.1 adds the layer's bias after the rescale; sec. 2.3 and
  * the bf16 activations of sec. 2.2 motivate a bf16 output for the next layer):
  *
+ *   w_group  0: s_w is the tensor's one scale ([1]); else G with s_w [N][K/G]
+ *            from bitnet_pack_weights_grouped (G = K: one scale per output channel)
  *   bias     (device) fp32 [N], added to every row of y, or NULL for none
  *   y        (device) [M][N] of y_dtype: BITNET_F32 or BITNET_BF16
  *   kernel   as for bitnet_linear_select (0 = automatic)
+ *
+ * With G = K: y[m][n] = fp32(acc * c_mn (+ bias[n])), c_mn = (s_x[m] s_w[n]) / 127
+ * in float64, on every kernel.  With G < K: y[m][n] = fp32((sum_g acc_g s_w[n][g])
+ * s_x[m] / 127 (+ bias[n])), acc_g the exact integer sum of group g and the sum over
+ * groups in float64 (any order; the result is within 2^-23 |y| plus 2^-45 times
+ * the sum of the terms' magnitudes of the ordered sum); acc is then sum_g acc_g.
+ * Group-wise scales (G < K) run on the decode GEMV (kernel 1; needs G % 64 == 0
+ * besides its usual conditions) or the general kernel (3); kernel 0 picks the
+ * GEMV when it can, at any M (it re-reads the weights once per 8 rows of q);
+ * other kernel ids give BITNET_ERR_ARG.  A w_group that is not 0 or a multiple of
+ * 4 dividing K gives BITNET_ERR_SHAPE.
  *
  * y[m][n] = fp32(acc * c_m + bias[n]) with c_m = (s_x[m] * s_w) / 127, the
  * product and the sum taken in float64 and rounded once to fp32; a bf16 y is
@@ -197,9 +228,9 @@ enum bitnet_dtype {
  * is unchanged by the options.  bias must be 4-byte aligned, y aligned to its
  * element size (else BITNET_ERR_ALIGN); an unknown y_dtype or kernel gives
  * BITNET_ERR_ARG.  bitnet_linear and bitnet_linear_select are this call with
- * bias = NULL and y_dtype = BITNET_F32. */
+ * w_group = 0, bias = NULL and y_dtype = BITNET_F32. */
 BITNET_API int bitnet_linear_ex(const int8_t *q, const float *s_x, const uint8_t *packed,
-                                const float *s_w, int64_t M, int64_t N, int64_t K,
+                                const float *s_w, int64_t w_group, int64_t M, int64_t N, int64_t K,
                                 const float *bias, void *y, int y_dtype, int32_t *acc,
                                 int kernel, void *stream);
 

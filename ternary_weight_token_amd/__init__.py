@@ -61,7 +61,8 @@ def lib() -> ctypes.CDLL:
         L.bitnet_rmsnorm_quant_act.argtypes = [P, P, ctypes.c_float, I64, I64, P, P, P]
         L.bitnet_linear.argtypes = [P, P, P, P, I64, I64, I64, P, P, P]
         L.bitnet_linear_select.argtypes = [P, P, P, P, I64, I64, I64, P, P, I, P]
-        L.bitnet_linear_ex.argtypes = [P, P, P, P, I64, I64, I64, P, P, I, P, I, P]
+        L.bitnet_linear_ex.argtypes = [P, P, P, P, I64, I64, I64, I64, P, P, I, P, I, P]
+        L.bitnet_pack_weights_grouped.argtypes = [P, I64, I64, I64, ctypes.c_float, P, P, P]
         L.bitnet_grouped_plan_bytes.argtypes = [I, I, P]
         L.bitnet_grouped_plan_bytes.restype = ctypes.c_size_t
         L.bitnet_grouped_plan_linear.argtypes = [P, I, P, ctypes.c_size_t]
@@ -72,7 +73,7 @@ def lib() -> ctypes.CDLL:
         L.bitnet_grouped_plan_fused_bytes.restype = ctypes.c_size_t
         L.bitnet_grouped_plan_fused.argtypes = [P, I, P, ctypes.c_size_t]
         L.bitnet_linear_fused_grouped.argtypes = [P, P, P]
-        for f in ("bitnet_pack_weights", "bitnet_quant_act", "bitnet_rmsnorm_quant_act", "bitnet_linear", "bitnet_linear_select", "bitnet_linear_ex",
+        for f in ("bitnet_pack_weights", "bitnet_pack_weights_grouped", "bitnet_quant_act", "bitnet_rmsnorm_quant_act", "bitnet_linear", "bitnet_linear_select", "bitnet_linear_ex",
                   "bitnet_grouped_plan_linear", "bitnet_grouped_plan_quant", "bitnet_grouped_plan_fused",
                   "bitnet_linear_grouped", "bitnet_quant_act_grouped", "bitnet_linear_fused_grouped"):
             getattr(L, f).restype = I
@@ -186,10 +187,14 @@ _OUT_DTYPES = {torch.float32: BITNET_F32, torch.bfloat16: BITNET_BF16}
 
 def bitnet_linear_ex(q: torch.Tensor, s_x: torch.Tensor, packed: torch.Tensor, s_w: torch.Tensor,
                      bias: torch.Tensor | None, y: torch.Tensor, acc: torch.Tensor | None = None,
-                     kernel: int = 0, stream=None) -> None:
-    """bitnet_linear_select with an optional fp32 bias [N] and y in fp32 or bf16 [M][N]."""
+                     kernel: int = 0, stream=None, w_group: int = 0) -> None:
+    """bitnet_linear_select with an optional fp32 bias [N], y in fp32 or bf16 [M][N], and
+    weight scales per tensor (w_group = 0, s_w [1]) or per group of w_group weights
+    (s_w [N][K / w_group]; w_group = K: per output channel)."""
     _dev(q, torch.int8, "q"); _dev(s_x, torch.float32, "s_x"); _dev(packed, torch.uint8, "packed")
     _dev(s_w, torch.float32, "s_w")
+    if w_group and s_w.numel() != packed.shape[0] * (q.shape[1] // w_group):
+        raise ValueError("s_w must hold N * K / w_group scales")
     if y.dtype not in _OUT_DTYPES:
         raise ValueError(f"y must be float32 or bfloat16, got {y.dtype}")
     _dev(y, y.dtype, "y")
@@ -205,7 +210,7 @@ def bitnet_linear_ex(q: torch.Tensor, s_x: torch.Tensor, packed: torch.Tensor, s
         _dev(acc, torch.int32, "acc")
         if acc.shape != (M, N):
             raise ValueError("acc must be [M][N]")
-    _check(lib().bitnet_linear_ex(_ptr(q), _ptr(s_x), _ptr(packed), _ptr(s_w), M, N, K, _ptr(bias),
+    _check(lib().bitnet_linear_ex(_ptr(q), _ptr(s_x), _ptr(packed), _ptr(s_w), int(w_group), M, N, K, _ptr(bias),
                                   _ptr(y), _OUT_DTYPES[y.dtype], _ptr(acc), int(kernel), _stream(stream)))
 
 
@@ -308,6 +313,17 @@ def rmsnorm_quant(x: torch.Tensor, gain: torch.Tensor, eps: float, stream=None):
     return q, s_x
 
 
+def pack_weights_grouped(w: torch.Tensor, group: int, eps: float = 1e-5, stream=None):
+    """Group-wise absmean packing -> (packed uint8 [N][K/4], s_w fp32 [N][K/group])."""
+    _dev(w, torch.float32, "w")
+    N, K = w.shape
+    packed = torch.empty((N, K // 4), dtype=torch.uint8, device=w.device)
+    s_w = torch.empty((N, K // group if group else 0), dtype=torch.float32, device=w.device)
+    _check(lib().bitnet_pack_weights_grouped(_ptr(w), N, K, int(group), ctypes.c_float(eps), _ptr(packed),
+                                             _ptr(s_w), _stream(stream)))
+    return packed, s_w
+
+
 def quant_act(x: torch.Tensor, stream=None):
     M, K = x.shape
     q = torch.empty((M, K), dtype=torch.int8, device=x.device)
@@ -317,13 +333,13 @@ def quant_act(x: torch.Tensor, stream=None):
 
 
 def linear(q, s_x, packed, s_w, want_acc: bool = False, stream=None, bias=None,
-           out_dtype=torch.float32, kernel: int = 0):
+           out_dtype=torch.float32, kernel: int = 0, w_group: int = 0):
     M, K = q.shape
     N = packed.shape[0]
     y = torch.empty((M, N), dtype=out_dtype, device=q.device)
     acc = torch.empty((M, N), dtype=torch.int32, device=q.device) if want_acc else None
-    if bias is None and out_dtype == torch.float32 and kernel == 0:
+    if bias is None and out_dtype == torch.float32 and kernel == 0 and w_group == 0:
         bitnet_linear(q, s_x, packed, s_w, y, acc, stream)
     else:
-        bitnet_linear_ex(q, s_x, packed, s_w, bias, y, acc, kernel, stream)
+        bitnet_linear_ex(q, s_x, packed, s_w, bias, y, acc, kernel, stream, w_group)
     return (y, acc) if want_acc else y

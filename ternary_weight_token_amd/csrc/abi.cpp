@@ -94,6 +94,18 @@ BITNET_API int bitnet_pack_weights(const float *w, int64_t N, int64_t K, float e
     return hip_status(launch_pack(w, N, K, eps, packed, s_w, (double *)workspace, (hipStream_t)stream));
 }
 
+BITNET_API int bitnet_pack_weights_grouped(const float *w, int64_t N, int64_t K, int64_t group, float eps,
+                                           uint8_t *packed, float *s_w, void *stream) {
+    int st = check_dims(0, N, K);
+    if (st) return st;
+    if (group <= 0 || K % group != 0 || group % 4 != 0)
+        return fail(BITNET_ERR_SHAPE, "group must be a positive multiple of 4 dividing K");
+    if (N == 0) return BITNET_OK;
+    if (!w || !packed || !s_w) return fail(BITNET_ERR_NULL, "null pointer");
+    if (!aligned(w, 4) || !aligned(s_w, 4)) return fail(BITNET_ERR_ALIGN, "w and s_w must be 4-byte aligned");
+    return hip_status(launch_pack_grouped(w, N, K, group, eps, packed, s_w, (hipStream_t)stream));
+}
+
 BITNET_API int bitnet_quant_act(const uint16_t *x, int64_t M, int64_t K, int8_t *q, float *s_x,
                                 void *stream) {
     int st = check_dims(M, 1, K);
@@ -118,25 +130,34 @@ BITNET_API int bitnet_rmsnorm_quant_act(const uint16_t *x, const float *gain, fl
 }
 
 BITNET_API int bitnet_linear_ex(const int8_t *q, const float *s_x, const uint8_t *packed,
-                                const float *s_w, int64_t M, int64_t N, int64_t K, const float *bias,
-                                void *y, int y_dtype, int32_t *acc, int kernel, void *stream) {
+                                const float *s_w, int64_t w_group, int64_t M, int64_t N, int64_t K,
+                                const float *bias, void *y, int y_dtype, int32_t *acc, int kernel,
+                                void *stream) {
     const bool forced_tile = kernel >= 16 && kernel < 16 + gemm_config_count();
     if ((kernel < 0 || kernel > 4) && !forced_tile) return fail(BITNET_ERR_ARG, "unknown kernel id");
     if (y_dtype != BITNET_F32 && y_dtype != BITNET_BF16) return fail(BITNET_ERR_ARG, "unknown output dtype");
     int st = check_dims(M, N, K);
-    if (st || M == 0 || N == 0) return st;
+    if (st) return st;
+    if (w_group < 0 || (w_group > 0 && (K % w_group != 0 || w_group % 4 != 0)))
+        return fail(BITNET_ERR_SHAPE, "w_group must be 0 or a multiple of 4 dividing K");
+    // group-wise scales below the row length: decode GEMV or general kernel only
+    const bool groups = w_group > 0 && w_group < K;
+    if (groups && kernel != 0 && kernel != 1 && kernel != 3)
+        return fail(BITNET_ERR_ARG, "group-wise weight scales need kernel 0, 1 or 3");
+    if (M == 0 || N == 0) return BITNET_OK;
     if (!q || !s_x || !packed || !s_w || !y) return fail(BITNET_ERR_NULL, "null pointer");
     if (!aligned(s_x, 4) || !aligned(s_w, 4) || (acc && !aligned(acc, 4)) || (bias && !aligned(bias, 4)))
         return fail(BITNET_ERR_ALIGN, "s_x, s_w, bias and acc must be 4-byte aligned");
     if (!aligned(y, y_dtype == BITNET_BF16 ? 2 : 4))
         return fail(BITNET_ERR_ALIGN, "y must be aligned to its element size");
-    const OutSpec out{y, bias, y_dtype == BITNET_BF16 ? 1 : 0};
+    const OutSpec out{y, bias, y_dtype == BITNET_BF16 ? 1 : 0, (int)w_group};
     hipStream_t s = (hipStream_t)stream;
-    const bool fast = linear_fast(q, packed, K);
+    const bool fast = linear_fast(q, packed, K) && (!groups || w_group % 64 == 0);
     if (kernel == 3 || (kernel == 0 && !fast))
         return hip_status(launch_linear_generic(q, s_x, packed, s_w, M, N, K, out, acc, s));
-    if (!fast) return fail(BITNET_ERR_ALIGN, "kernel needs K % 64 == 0 and 16-byte aligned q/packed");
-    if (kernel == 0) kernel = M == 1 ? 1 : (M <= kGemvMaxM ? 4 : 2);
+    if (!fast)
+        return fail(BITNET_ERR_ALIGN, "kernel needs K % 64 == 0, 16-byte aligned q/packed (and w_group % 64 == 0)");
+    if (kernel == 0) kernel = (M == 1 || groups) ? 1 : (M <= kGemvMaxM ? 4 : 2);
     if (kernel == 1) return hip_status(launch_gemv(q, s_x, packed, s_w, M, N, K, out, acc, s));
     if (kernel == 4) return hip_status(launch_skinny(q, s_x, packed, s_w, M, N, K, out, acc, s));
     if (forced_tile) return hip_status(launch_gemm_cfg(kernel - 16, q, s_x, packed, s_w, M, N, K, out, acc, s));
@@ -145,13 +166,13 @@ BITNET_API int bitnet_linear_ex(const int8_t *q, const float *s_x, const uint8_t
 
 BITNET_API int bitnet_linear(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                              int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, void *stream) {
-    return bitnet_linear_ex(q, s_x, packed, s_w, M, N, K, nullptr, y, BITNET_F32, acc, 0, stream);
+    return bitnet_linear_ex(q, s_x, packed, s_w, 0, M, N, K, nullptr, y, BITNET_F32, acc, 0, stream);
 }
 
 BITNET_API int bitnet_linear_select(const int8_t *q, const float *s_x, const uint8_t *packed,
                                     const float *s_w, int64_t M, int64_t N, int64_t K, float *y,
                                     int32_t *acc, int kernel, void *stream) {
-    return bitnet_linear_ex(q, s_x, packed, s_w, M, N, K, nullptr, y, BITNET_F32, acc, kernel, stream);
+    return bitnet_linear_ex(q, s_x, packed, s_w, 0, M, N, K, nullptr, y, BITNET_F32, acc, kernel, stream);
 }
 
 // ----------------------------------------------------------------- grouped plans

@@ -101,6 +101,14 @@ __device__ __forceinline__ int octet_sum(int v) {
     return v;
 }
 
+// Sum over the 8 lanes of an octet, float64 (shuffles within the octet).
+__device__ __forceinline__ double octet_sum_f64(double v) {
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    return v;
+}
+
 // Full-wavefront max of non-negative ints (64 lanes).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     #pragma unroll
@@ -244,6 +252,12 @@ __device__ __forceinline__ void store_y(const OutSpec &out, size_t o, double v) 
     const float f = (float)v;
     if (out.bf16) reinterpret_cast<uint16_t *>(out.y)[o] = bf16_rne(f);
     else reinterpret_cast<float *>(out.y)[o] = f;
+}
+
+// Rescale factor of output column n: the per-tensor c_m when the weights have one
+// scale, else (s_x[m] * s_w[n]) / 127 with the column's own scale (w_group = K).
+__device__ __forceinline__ double col_factor(const OutSpec &out, const float *s_w, int n, float sxm, double cm) {
+    return out.w_group ? rescale_factor(sxm, s_w[n]) : cm;
 }
 
 // Store output element o (column n) from acc and c = c_m; see OutSpec.

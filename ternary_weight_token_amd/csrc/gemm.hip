@@ -229,13 +229,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
             if (row >= M) continue;
             const int sq = rowsum[lr];
             const double cm = rowscale[lr];
+            const float sxr = out.w_group ? s_x[row] : 0.0f;
             #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int col = n_base + wn * TN * 16 + j * 16 + l16;
                 if (col < N) {
                     const size_t o = (size_t)row * N + col;
                     const int v = acc[i][j][r] - sq;
-                    double yv = (double)v * cm;
+                    double yv = (double)v * col_factor(out, s_w, col, sxr, cm);
                     if (out.bias) yv += (double)bcol[j];
                     store_y(out, o, yv);
                     if (acc_out) acc_out[o] = v;

@@ -33,6 +33,9 @@
 #ifndef BITNET_GEMV_NT
 #define BITNET_GEMV_NT 1
 #endif
+#ifndef BITNET_GEMV1_RG
+#define BITNET_GEMV1_RG 2        // row groups of 8 per wavefront, single-token launches
+#endif
 #ifndef BITNET_FUSED_NW
 #define BITNET_FUSED_NW 4        // wavefronts per workgroup of the fused grouped launch (4 or 8)
 #endif
@@ -122,6 +125,36 @@ struct StageQ {
         #pragma unroll
         for (int m = 0; m < MT; ++m)
             if (m < mcount && part[m] != 0) atomicAdd(&sq[m], part[m]);
+    }
+};
+
+// From int8 q, chunk by chunk, for weights with group-wise scales: also the sum of
+// q over each 64-value chunk (sqc[m][c], plain stores), which the grouped product
+// subtracts chunk by chunk (sum_k q t = sum_k q c - sum_k q within every group).
+template <int MT, bool DOT8>
+struct StageQChunks {
+    const int8_t *q;
+    int K;
+    int *sqc;            // LDS, [MT][seg_chunks]
+    struct Pre {};
+    __device__ __forceinline__ Pre load(int, int) const { return Pre{}; }
+    __device__ __forceinline__ void operator()(const Pre &, int s0, int sc, int m0, int mcount, int seg_chunks,
+                                               uint32_t *qs, int *) const {
+        for (int idx = threadIdx.x; idx < mcount * sc; idx += blockDim.x) {
+            const int m = idx / sc, c = idx - m * sc;
+            const int8_t *src = q + (size_t)(m0 + m) * K + 64 * (s0 + c);
+            int sm = 0;
+            #pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint4 a = gload16(src + 16 * d);
+                *reinterpret_cast<uint4 *>(qs + (m * seg_chunks + c) * kLdsChunkDw + 4 * d) = prep16<DOT8>(a);
+                sm = dot4(a.x, 0x01010101u, sm);
+                sm = dot4(a.y, 0x01010101u, sm);
+                sm = dot4(a.z, 0x01010101u, sm);
+                sm = dot4(a.w, 0x01010101u, sm);
+            }
+            sqc[m * seg_chunks + c] = sm;
+        }
     }
 };
 
@@ -278,15 +311,18 @@ struct StageRmsQuantize {
     }
 };
 
-template <int MT, int RG, bool DOT8, bool NT, int NW, class Stage>
 // s_x is not restrict-qualified: in the fused kernels it is the LDS word the stager
 // writes through its own pointer, and its reads must stay after the staging.
+// GRP: the weights have group-wise scales (out.w_group = G, a multiple of 64 below K):
+// each chunk's integer partial, less its sum of q (sqc), is scaled by its group's
+// s_w[row][k / G] and summed in float64 (kslices == 1 only).
+template <int MT, int RG, bool DOT8, bool NT, int NW, class Stage, bool GRP = false>
 __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s_x,
                                               const uint8_t *__restrict__ packed,
                                               const float *__restrict__ s_w, int M, int N, int K,
                                               const OutSpec &out, int32_t *__restrict__ acc_out,
                                               int row_base, int m0, int kslices, int seg_chunks,
-                                              uint32_t *qs, int *sq, int *red) {
+                                              uint32_t *qs, int *sq, int *red, const int *sqc = nullptr) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l8 = lane & 7, rs = lane >> 3;
@@ -300,13 +336,17 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s
 
     int hi[RG][MT];
     uint32_t lo[RG][MT];
+    double facc[RG][MT];       // GRP: sum over chunks of partial x group scale
     const uint8_t *prow[RG];
+    const float *srow[RG];     // GRP: the row's group scales
+    const int G = GRP ? out.w_group : 1, ng = GRP ? K / G : 1;
     #pragma unroll
     for (int g = 0; g < RG; ++g) {
         const int r = row0 + 8 * g + rs;
         prow[g] = packed + (size_t)(r < N ? r : 0) * KB;   // rows past N read row 0, discarded
+        srow[g] = s_w + (size_t)(r < N ? r : 0) * ng;
         #pragma unroll
-        for (int m = 0; m < MT; ++m) { hi[g][m] = 0; lo[g][m] = 0u; }
+        for (int m = 0; m < MT; ++m) { hi[g][m] = 0; lo[g][m] = 0u; facc[g][m] = 0.0; }
     }
     if (tid < MT) sq[tid] = 0;
     // chunk offset of this lane's rows within their 128-byte line (the same for all
@@ -332,13 +372,18 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s
         // a wave whose rows all lie past N loads (clamped, unused) but computes nothing
         const int T = row0 < N ? ((ce - cb + 7) >> 3) + (aligned ? 0 : 1) : 0;
         const int clast = min(max(ce - 1, cb), C - 1);   // in range even for an empty slice
-        uint4 bufA[RG], bufB[RG];
-        auto issue = [&](uint4 (&b)[RG], int t) {
+        struct WBuf { uint4 w[RG]; float s[RG]; };   // s: GRP group scales of the chunk
+        WBuf bufA, bufB;
+        auto issue = [&](WBuf &b, int t) {
             const int cc = min(max(c0 + l8 + 8 * t, cb), clast);
             #pragma unroll
-            for (int g = 0; g < RG; ++g) b[g] = load_weights<NT>(prow[g] + 16 * cc);
+            for (int g = 0; g < RG; ++g) b.w[g] = load_weights<NT>(prow[g] + 16 * cc);
+            if (GRP) {
+                #pragma unroll
+                for (int g = 0; g < RG; ++g) b.s[g] = srow[g][(64 * cc) / G];
+            }
         };
-        auto consume = [&](const uint4 (&b)[RG], int t) {
+        auto consume = [&](const WBuf &b, int t) {
             const int craw = c0 + l8 + 8 * t;
             const bool valid = craw >= cb && craw < ce;
             const int cc = min(max(craw, cb), clast) - s0;
@@ -346,14 +391,28 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s
             for (int m = 0; m < MT; ++m) {
                 if (m < mcount) {
                     const uint32_t *qc = qs + (m * seg_chunks + cc) * kLdsChunkDw;
+                    int hc[RG];
+                    uint32_t lc[RG];
+                    #pragma unroll
+                    for (int g = 0; g < RG; ++g) { hc[g] = 0; lc[g] = 0u; }
                     #pragma unroll
                     for (int d = 0; d < 4; ++d) {
                         const uint4 pq = *reinterpret_cast<const uint4 *>(qc + 4 * d);
                         #pragma unroll
                         for (int g = 0; g < RG; ++g) {
-                            uint32_t wd = d == 0 ? b[g].x : d == 1 ? b[g].y : d == 2 ? b[g].z : b[g].w;
+                            uint32_t wd = d == 0 ? b.w[g].x : d == 1 ? b.w[g].y : d == 2 ? b.w[g].z : b.w[g].w;
                             wd = valid ? wd : 0u;
-                            mac16<DOT8>(wd, pq, hi[g][m], lo[g][m]);
+                            if (GRP) mac16<DOT8>(wd, pq, hc[g], lc[g]);
+                            else mac16<DOT8>(wd, pq, hi[g][m], lo[g][m]);
+                        }
+                    }
+                    if (GRP) {
+                        const int sqv = valid ? sqc[m * seg_chunks + cc] : 0;
+                        #pragma unroll
+                        for (int g = 0; g < RG; ++g) {
+                            const int p = (DOT8 ? 16 * hc[g] + (int)lc[g] : hc[g]) - sqv;   // |p| <= 64 * 127
+                            hi[g][m] += p;
+                            facc[g][m] += (double)p * (double)b.s[g];
                         }
                     }
                 }
@@ -416,6 +475,27 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s
         }
     }
 
+    if (GRP) {
+        // hi holds the exact integer sum (sq already subtracted chunk by chunk); facc
+        // the scaled sum: y = fp32((sum_g acc_g s_g) s_x / 127 (+ bias))
+        #pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            #pragma unroll
+            for (int g = 0; g < RG; ++g) {
+                const int a = octet_sum(hi[g][m]);
+                const double f = octet_sum_f64(facc[g][m]);
+                const int r = row0 + 8 * g + rs;
+                if (m < mcount && r < N && l8 == (m & 7)) {
+                    const size_t o = (size_t)(m0 + m) * N + r;
+                    double v = (f * (double)s_x[m0 + m]) / 127.0;
+                    if (out.bias) v += (double)out.bias[r];
+                    store_y(out, o, v);
+                    if (acc_out) acc_out[o] = a;
+                }
+            }
+        }
+        return;
+    }
     int acc[RG][MT];
     #pragma unroll
     for (int g = 0; g < RG; ++g) {
@@ -437,7 +517,7 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s
                 if (r < N && l8 == (m & 7)) {
                     const size_t o = (size_t)(m0 + m) * N + r;
                     const int a = acc[g][m] - sqm;
-                    put_y(out, o, r, a, cm);
+                    put_y(out, o, r, a, col_factor(out, s_w, r, s_x[m0 + m], cm));
                     if (acc_out) acc_out[o] = a;
                 }
             }
@@ -462,12 +542,12 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s
         int s = -sq[m];
         for (int w = 0; w < kslices; ++w) s += red[((rsi * kslices + w) * R + rr) * MT + m];
         const size_t o = (size_t)(m0 + m) * N + r;
-        put_y(out, o, r, s, rescale_factor(s_x[m0 + m], sw));
+        put_y(out, o, r, s, col_factor(out, s_w, r, s_x[m0 + m], rescale_factor(s_x[m0 + m], sw)));
         if (acc_out) acc_out[o] = s;
     }
 }
 
-template <int MT, int RG, bool DOT8>
+template <int MT, int RG, bool DOT8, bool GRP>
 __global__ __launch_bounds__(256) void gemv_lds_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s_x, const uint8_t *__restrict__ packed,
     const float *__restrict__ s_w, int M, int N, int K, const OutSpec out,
@@ -476,9 +556,17 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(
     __shared__ int sq[MT];
     __shared__ int red[4 * 8 * RG * MT];
     const int rows_per_block = (4 / kslices) * 8 * RG;
-    gemv_lds_tile<MT, RG, DOT8, BITNET_GEMV_NT != 0, 4>(StageQ<MT, DOT8>{q, K}, s_x, packed, s_w, M, N, K, out, acc_out,
-                                                     blockIdx.x * rows_per_block, blockIdx.y * MT, kslices,
-                                                     seg_chunks, dyn, sq, red);
+    if (GRP) {
+        // the chunk sums of q follow the staged q in the dynamic LDS
+        int *sqc = reinterpret_cast<int *>(dyn + MT * seg_chunks * kLdsChunkDw);
+        gemv_lds_tile<MT, RG, DOT8, BITNET_GEMV_NT != 0, 4, StageQChunks<MT, DOT8>, true>(
+            StageQChunks<MT, DOT8>{q, K, sqc}, s_x, packed, s_w, M, N, K, out, acc_out, blockIdx.x * rows_per_block,
+            blockIdx.y * MT, 1, seg_chunks, dyn, sq, red, sqc);
+    } else {
+        gemv_lds_tile<MT, RG, DOT8, BITNET_GEMV_NT != 0, 4>(StageQ<MT, DOT8>{q, K}, s_x, packed, s_w, M, N, K, out,
+                                                         acc_out, blockIdx.x * rows_per_block, blockIdx.y * MT,
+                                                         kslices, seg_chunks, dyn, sq, red);
+    }
 }
 
 // K segment length in 64-weight chunks for an M tile of mt rows: the whole of K when
@@ -584,31 +672,47 @@ uint32_t gemv_grouped_lds_bytes(int64_t K) {
     return (uint32_t)(kGroupedMT * segment_chunks((int)(K / 64), kGroupedMT) * kLdsChunkDw * 4);
 }
 
-template <int MT, int RG, bool DOT8>
+template <int MT, int RG, bool DOT8, bool GRP>
 static hipError_t launch_lds(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                              int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st) {
     const int C = (int)(K / 64);
     const unsigned gy = (unsigned)((M + MT - 1) / MT);
     // more K slices per row set until the launch has >= 2 workgroups per CU,
-    // keeping at least 2 chunk iterations per lane
+    // keeping at least 2 chunk iterations per lane (one slice with group scales)
     int ks = 1;
     auto blocks = [&](int k) { return (int64_t)((N + (4 / k) * 8 * RG - 1) / ((4 / k) * 8 * RG)) * gy; };
-    while (ks < 4 && blocks(ks) < 512 && C / (8 * ks * 2) >= 2) ks *= 2;
+    while (!GRP && ks < 4 && blocks(ks) < 512 && C / (8 * ks * 2) >= 2) ks *= 2;
     const unsigned gx = (unsigned)((N + (4 / ks) * 8 * RG - 1) / ((4 / ks) * 8 * RG));
-    const int seg = segment_chunks(C, MT);
-    const size_t lds = (size_t)MT * seg * kLdsChunkDw * 4;
-    gemv_lds_kernel<MT, RG, DOT8><<<dim3(gx, gy), dim3(256), lds, st>>>(q, s_x, packed, s_w, (int)M, (int)N,
-                                                                        (int)K, y, acc, ks, seg);
+    // with group scales each staged chunk also keeps its sum of q (one more dword)
+    const int per_chunk_dw = kLdsChunkDw + (GRP ? 1 : 0);
+    int seg = C;
+    const int max_seg = (kLdsBudget / (MT * per_chunk_dw * 4)) & ~7;
+    if (C > max_seg) {
+        const int nseg = (C + max_seg - 1) / max_seg;
+        seg = (((C + nseg - 1) / nseg) + 7) & ~7;
+    }
+    const size_t lds = (size_t)MT * seg * per_chunk_dw * 4;
+    gemv_lds_kernel<MT, RG, DOT8, GRP><<<dim3(gx, gy), dim3(256), lds, st>>>(q, s_x, packed, s_w, (int)M, (int)N,
+                                                                             (int)K, y, acc, ks, seg);
     return hipGetLastError();
+}
+
+template <bool GRP>
+static hipError_t launch_gemv_mt(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
+                                 int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st) {
+    const bool d8 = BITNET_GROUPED_DOT8 != 0;
+    if (M == 1) return launch_lds<1, BITNET_GEMV1_RG, d8, GRP>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    if (M == 2) return launch_lds<2, 2, d8, GRP>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    if (M <= 4) return launch_lds<4, 2, d8, GRP>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    return launch_lds<8, 2, d8, GRP>(q, s_x, packed, s_w, M, N, K, y, acc, st);
 }
 
 hipError_t launch_gemv(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                        int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st) {
-    const bool d8 = BITNET_GROUPED_DOT8 != 0;
-    if (M == 1) return launch_lds<1, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
-    if (M == 2) return launch_lds<2, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
-    if (M <= 4) return launch_lds<4, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
-    return launch_lds<8, 2, d8>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    // group-wise weight scales (a group smaller than the row) take the grouped path;
+    // one scale per tensor or per output channel only changes the epilogue
+    if (y.w_group > 0 && y.w_group < K) return launch_gemv_mt<true>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+    return launch_gemv_mt<false>(q, s_x, packed, s_w, M, N, K, y, acc, st);
 }
 
 hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st) {

@@ -16,14 +16,36 @@ __global__ __launch_bounds__(256) void linear_generic_kernel(
     const int64_t m = idx / N, n = idx % N;
     const int8_t *qr = q + m * K;
     const uint8_t *pr = packed + n * (K / 4);
-    int s = 0;
-    for (int64_t j = 0; j < K / 4; ++j) {
-        const uint32_t b = pr[j];
-        #pragma unroll
-        for (int i = 0; i < 4; ++i) s += (int)qr[4 * j + i] * ((int)((b >> (2 * i)) & 3u) - 1);
+    if (out.w_group == 0) {
+        int s = 0;
+        for (int64_t j = 0; j < K / 4; ++j) {
+            const uint32_t b = pr[j];
+            #pragma unroll
+            for (int i = 0; i < 4; ++i) s += (int)qr[4 * j + i] * ((int)((b >> (2 * i)) & 3u) - 1);
+        }
+        put_y(out, idx, (int)n, s, rescale_factor(s_x[m], *s_w));
+        if (acc_out) acc_out[idx] = s;
+        return;
     }
-    put_y(out, idx, (int)n, s, rescale_factor(s_x[m], *s_w));
-    if (acc_out) acc_out[idx] = s;
+    // weight scales per group of G = w_group weights of the row (G = K: per output
+    // channel): y = fp32((sum_g acc_g s_w[n][g]) s_x / 127), the sum in float64
+    const int64_t G = out.w_group, ng = K / G;
+    int total = 0;
+    double v = 0.0;
+    for (int64_t g = 0; g < ng; ++g) {
+        int a = 0;
+        for (int64_t j = g * G / 4; j < (g + 1) * G / 4; ++j) {
+            const uint32_t b = pr[j];
+            #pragma unroll
+            for (int i = 0; i < 4; ++i) a += (int)qr[4 * j + i] * ((int)((b >> (2 * i)) & 3u) - 1);
+        }
+        total += a;
+        v += (double)a * (double)s_w[n * ng + g];
+    }
+    v = (v * (double)s_x[m]) / 127.0;
+    if (out.bias) v += (double)out.bias[n];
+    store_y(out, idx, v);
+    if (acc_out) acc_out[idx] = total;
 }
 
 hipError_t launch_linear_generic(const int8_t *q, const float *s_x, const uint8_t *packed,

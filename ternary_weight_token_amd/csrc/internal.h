@@ -9,16 +9,20 @@ namespace bitnet {
 // Output of the rescale epilogue (pages: chenxutan.com sec. 2.3 rescale, sec. 3.1
 // forward with its optional bias): y = acc * c_m (+ bias[n]), c_m = (s_x * s_w) / 127,
 // formed in float64 and rounded once to fp32; a bf16 output is that fp32 value
-// rounded to nearest even.
+// rounded to nearest even.  w_group: granularity of the weight scales s_w (sec. 3.1
+// weight_scale per output channel, sec. 4.3 groups): 0 = one scale for the tensor,
+// K = one per output channel (s_w[n]), G = one per G consecutive weights of a row
+// (s_w[n][k / G]).
 struct OutSpec {
     void *y;             // fp32 or bf16, [M][N]
     const float *bias;   // [N] or nullptr
     int bf16;
+    int w_group;
 };
 
 // The same output advanced by `elems` elements (a later row block of y).
 __host__ __device__ inline OutSpec out_offset(const OutSpec &o, size_t elems) {
-    return OutSpec{static_cast<char *>(o.y) + elems * (o.bf16 ? 2 : 4), o.bias, o.bf16};
+    return OutSpec{static_cast<char *>(o.y) + elems * (o.bf16 ? 2 : 4), o.bias, o.bf16, o.w_group};
 }
 
 // Plan image for grouped launches.
@@ -65,6 +69,8 @@ hipError_t launch_rmsnorm_quant(const uint16_t *x, const float *g, float eps, in
                                 float *s_x, hipStream_t st);
 hipError_t launch_pack(const float *w, int64_t N, int64_t K, float eps, uint8_t *packed,
                        float *s_w, double *rowsum, hipStream_t st);
+hipError_t launch_pack_grouped(const float *w, int64_t N, int64_t K, int64_t G, float eps, uint8_t *packed,
+                               float *s_w, hipStream_t st);
 hipError_t launch_gemv(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                        int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st);
 hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st);

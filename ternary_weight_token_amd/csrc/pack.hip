@@ -59,6 +59,46 @@ __global__ __launch_bounds__(256) void code_kernel(const float *__restrict__ w, 
     }
 }
 
+// Group-wise scales (pages: chenxutan.com sec. 3.1 weight_scale per output channel,
+// sec. 4.3 group-wise quantization; 0539edu.com sec. 2.1 scales per channel): row n
+// is cut into K / G groups of G consecutive weights; each gets its own absmean scale
+// s = fp32(mean |w|) (float64 sum, k ascending) and its codes rint(w / (s + eps))
+// clamped to [-1, 1].  s_w is [N][K / G]; G = K is one scale per output channel.
+__global__ __launch_bounds__(64) void group_scale_kernel(const float *__restrict__ w, int64_t N, int64_t K,
+                                                         int64_t G, float *__restrict__ s_w) {
+    const int64_t ng = K / G;
+    const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;   // (n, g)
+    if (i >= N * ng) return;
+    const int64_t n = i / ng, g = i - n * ng;
+    const float *r = w + n * K + g * G;
+    double s = 0.0;
+    for (int64_t k = 0; k < G; ++k) s += fabs((double)r[k]);
+    s_w[i] = (float)(s / (double)G);
+}
+
+__global__ __launch_bounds__(256) void code_grouped_kernel(const float *__restrict__ w, int64_t N, int64_t K,
+                                                           int64_t G, float eps, const float *__restrict__ s_w,
+                                                           uint8_t *__restrict__ packed) {
+    const int64_t KB = K / 4, ng = K / G;
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;   // byte index
+    if (j >= N * KB) return;
+    const int64_t n = j / KB, k = 4 * (j - n * KB);               // G % 4 == 0: one group per byte
+    const float d = s_w[n * ng + k / G] + eps;
+    const float *p = w + n * K + k;
+    packed[j] = (uint8_t)(code_of(p[0], d) | code_of(p[1], d) << 2 | code_of(p[2], d) << 4 | code_of(p[3], d) << 6);
+}
+
+hipError_t launch_pack_grouped(const float *w, int64_t N, int64_t K, int64_t G, float eps, uint8_t *packed,
+                               float *s_w, hipStream_t st) {
+    const int64_t pairs = N * (K / G);
+    group_scale_kernel<<<dim3((unsigned)((pairs + 63) / 64)), dim3(64), 0, st>>>(w, N, K, G, s_w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nbytes = N * K / 4;
+    code_grouped_kernel<<<dim3((unsigned)((nbytes + 255) / 256)), dim3(256), 0, st>>>(w, N, K, G, eps, s_w, packed);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack(const float *w, int64_t N, int64_t K, float eps, uint8_t *packed, float *s_w,
                        double *rowsum, hipStream_t st) {
     if (N > 0) {

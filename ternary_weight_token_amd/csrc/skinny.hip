@@ -157,7 +157,7 @@ __device__ __forceinline__ void skinny_tile(const int8_t *__restrict__ q, const 
                     if (row < N) {
                         const size_t o = (size_t)l16 * N + row;
                         const int v = acc[rg][r] - accq[r];
-                        put_y(out, o, row, v, cm);
+                        put_y(out, o, row, v, col_factor(out, s_w, row, s_x[l16], cm));
                         if (acc_out) acc_out[o] = v;
                     }
                 }
@@ -181,7 +181,7 @@ __device__ __forceinline__ void skinny_tile(const int8_t *__restrict__ q, const 
         int s = 0;
         for (int w = 0; w < kslices; ++w) s += red[(((rsi * kslices + w) * RG + rg) * 4 + r) * 64 + ln];
         const size_t o = (size_t)tok * N + row;
-        put_y(out, o, row, s, rescale_factor(s_x[tok], sw));
+        put_y(out, o, row, s, col_factor(out, s_w, row, s_x[tok], rescale_factor(s_x[tok], sw)));
         if (acc_out) acc_out[o] = s;
     }
 }
@@ -383,7 +383,7 @@ __device__ __forceinline__ void skinny_lds_tile(const int8_t *__restrict__ q, co
                 if (row < N) {
                     const size_t o = (size_t)l16 * N + row;
                     const int v = acc[rg][r] - sqm;
-                    put_y(out, o, row, v, cm);
+                    put_y(out, o, row, v, col_factor(out, s_w, row, s_x[l16], cm));
                     if (acc_out) acc_out[o] = v;
                 }
             }

@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -68,16 +68,36 @@ def test_linear_ex_rejects_bad_arguments(L):
     p = ctypes.c_void_p(256)  # never dereferenced: every call below fails its checks
     z = None
     F32, BF16 = 0, 1
-    assert L.bitnet_linear_ex(p, p, p, p, 1, 1, 64, z, p, 2, z, 0, z) == ARG       # unknown dtype
-    assert L.bitnet_linear_ex(p, p, p, p, 1, 1, 64, z, p, F32, z, 7, z) == ARG     # unknown kernel
-    assert L.bitnet_linear_ex(p, p, p, p, 1, 1, 64, ctypes.c_void_p(258), p, F32, z, 0, z) == ALIGN
-    assert L.bitnet_linear_ex(p, p, p, p, 1, 1, 64, z, ctypes.c_void_p(258), F32, z, 0, z) == ALIGN
-    assert L.bitnet_linear_ex(p, p, p, p, 1, 1, 64, z, ctypes.c_void_p(257), BF16, z, 0, z) == ALIGN
-    assert L.bitnet_linear_ex(p, p, p, p, 1, 1, 64, p, z, BF16, z, 0, z) == NULL
-    assert L.bitnet_linear_ex(p, p, p, p, 1, 1, 6, p, p, BF16, z, 0, z) == SHAPE
+    assert L.bitnet_linear_ex(p, p, p, p, 0, 1, 1, 64, z, p, 2, z, 0, z) == ARG       # unknown dtype
+    assert L.bitnet_linear_ex(p, p, p, p, 0, 1, 1, 64, z, p, F32, z, 7, z) == ARG     # unknown kernel
+    assert L.bitnet_linear_ex(p, p, p, p, 0, 1, 1, 64, ctypes.c_void_p(258), p, F32, z, 0, z) == ALIGN
+    assert L.bitnet_linear_ex(p, p, p, p, 0, 1, 1, 64, z, ctypes.c_void_p(258), F32, z, 0, z) == ALIGN
+    assert L.bitnet_linear_ex(p, p, p, p, 0, 1, 1, 64, z, ctypes.c_void_p(257), BF16, z, 0, z) == ALIGN
+    assert L.bitnet_linear_ex(p, p, p, p, 0, 1, 1, 64, p, z, BF16, z, 0, z) == NULL
+    assert L.bitnet_linear_ex(p, p, p, p, 0, 1, 1, 6, p, p, BF16, z, 0, z) == SHAPE
     # fast kernels need K % 64 == 0 (the general kernel, id 3, does not)
-    assert L.bitnet_linear_ex(p, p, p, p, 1, 1, 68, z, p, BF16, z, 1, z) == ALIGN
-    assert L.bitnet_linear_ex(z, z, z, z, 0, 5, 64, z, z, BF16, z, 0, z) == OK
+    assert L.bitnet_linear_ex(p, p, p, p, 0, 1, 1, 68, z, p, BF16, z, 1, z) == ALIGN
+    assert L.bitnet_linear_ex(z, z, z, z, 0, 0, 5, 64, z, z, BF16, z, 0, z) == OK
+    # weight-scale groups: a multiple of 4 dividing K; below K only kernels 0, 1, 3;
+    # the GEMV also needs a multiple of 64
+    assert L.bitnet_linear_ex(p, p, p, p, 6, 1, 1, 64, z, p, F32, z, 0, z) == SHAPE
+    assert L.bitnet_linear_ex(p, p, p, p, 48, 1, 1, 128, z, p, F32, z, 0, z) == SHAPE
+    assert L.bitnet_linear_ex(p, p, p, p, -4, 1, 1, 64, z, p, F32, z, 0, z) == SHAPE
+    for kern in (2, 4, 16):
+        assert L.bitnet_linear_ex(p, p, p, p, 64, 1, 1, 128, z, p, F32, z, kern, z) == ARG
+    assert L.bitnet_linear_ex(p, p, p, p, 32, 1, 1, 128, z, p, F32, z, 1, z) == ALIGN
+
+
+def test_pack_grouped_rejects_bad_arguments(L):
+    p = ctypes.c_void_p(256)
+    z = None
+    f = ctypes.c_float(1e-5)
+    assert L.bitnet_pack_weights_grouped(p, 2, 64, 0, f, p, p, z) == SHAPE
+    assert L.bitnet_pack_weights_grouped(p, 2, 64, 6, f, p, p, z) == SHAPE
+    assert L.bitnet_pack_weights_grouped(p, 2, 64, 48, f, p, p, z) == SHAPE
+    assert L.bitnet_pack_weights_grouped(z, 2, 64, 32, f, p, p, z) == NULL
+    assert L.bitnet_pack_weights_grouped(p, 2, 64, 32, f, p, ctypes.c_void_p(258), z) == ALIGN
+    assert L.bitnet_pack_weights_grouped(z, 0, 64, 32, f, z, z, z) == OK
 
 
 def test_quant_and_pack_reject_bad_arguments(L):

@@ -253,6 +253,66 @@ def test_fused_quant_linear_grouped(with_outputs):
                 assert np.array_equal(pr[6].cpu().numpy(), sx_ref)
 
 
+# ----------------------------------------------------------------- group-wise weight scales
+
+@pytest.mark.parametrize("N,K,G", [(300, 2560, 128), (33, 6912, 6912), (70, 640, 64), (5, 68, 4), (129, 512, 512)])
+def test_pack_grouped_parity(N, K, G):
+    key = synth.stream_key(330, N, K, G)
+    w = synth.latent_weights(key, N, K, 0.02)
+    w[:, :G] *= 4.0
+    p_ref, s_ref = oracle.pack_grouped(w.numpy(), G, 1e-5)
+    p, sw = tw.pack_weights_grouped(w.to(DEV), G, 1e-5)
+    torch.cuda.synchronize()
+    assert np.array_equal(p.cpu().numpy(), p_ref) and np.array_equal(sw.cpu().numpy(), s_ref)
+
+
+def _grouped_bound(q, s_x, packed, s_w, G, K):
+    """2^-44 (s_x / 127) sum_g |acc_g s_g| per output: the float64 sum over groups is
+    taken in another order than the oracle's."""
+    t = oracle.unpack(packed, K).astype(np.float64)
+    sg = np.repeat(s_w.astype(np.float64), G, axis=1)
+    mag = np.abs(q.astype(np.float64)) @ (np.abs(t) * sg).T
+    return 2.0 ** -44 * mag * (s_x.astype(np.float64)[:, None] / 127.0)
+
+
+@pytest.mark.parametrize("kernel,M,N,K,G", [
+    (1, 1, 300, 2560, 2560), (4, 8, 300, 2560, 2560), (2, 40, 257, 640, 640), (3, 3, 33, 132, 132),
+    (16, 257, 225, 640, 640), (17, 257, 225, 640, 640), (18, 257, 225, 640, 640), (19, 257, 225, 640, 640),
+    (20, 257, 225, 640, 640), (0, 1, 640, 2560, 2560), (0, 20, 300, 2560, 2560),      # per output channel
+    (1, 1, 300, 2560, 128), (1, 3, 70, 6912, 128), (1, 9, 33, 640, 64), (0, 1, 640, 2560, 128),
+    (0, 20, 129, 2560, 256), (3, 4, 33, 132, 44), (0, 2, 50, 2560 + 4, 4),             # group-wise
+    (1, 1, 200, 53312, 64), (1, 2, 100, 53248, 128),                                   # K in segments
+])
+@pytest.mark.parametrize("opts", ["plain", "bias_bf16"])
+def test_linear_weight_scale_groups(kernel, M, N, K, G, opts):
+    key = synth.stream_key(331, kernel, M, N, K, G)
+    x, q, s = quantized_inputs(key, M, K, row_scale=(0.1, 10.0))
+    w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02).numpy()
+    w[: N // 2, : max(G, 4)] *= 6.0
+    packed, s_w = oracle.pack_grouped(w, G, 1e-5)
+    bias = (np.linspace(-2, 2, N).astype(np.float32) if opts == "bias_bf16" else None)
+    acc_ref, y_ref = oracle.linear_grouped(q, s, packed, s_w, G, bias=bias)
+    out_dtype = torch.bfloat16 if opts == "bias_bf16" else torch.float32
+    y = torch.empty((M, N), dtype=out_dtype, device=DEV)
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    tw.bitnet_linear_ex(torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV),
+                        torch.from_numpy(packed).to(DEV), torch.from_numpy(s_w).to(DEV),
+                        None if bias is None else torch.from_numpy(bias).to(DEV), y, acc, kernel, w_group=G)
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    slack = _grouped_bound(q, s, packed, s_w, G, K)
+    if bias is not None:
+        slack = slack + 2.0 ** -45 * np.abs(bias.astype(np.float64))[None, :]
+    if out_dtype == torch.float32:
+        d = np.abs(y.cpu().numpy().astype(np.float64) - y_ref.astype(np.float64))
+        bad = d > REL * np.abs(y_ref.astype(np.float64)) + slack
+    else:
+        got = (y.cpu().view(torch.int16).numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+        want = (oracle.to_bf16(y_ref).astype(np.uint32) << 16).view(np.float32)
+        d = np.abs(got.astype(np.float64) - want.astype(np.float64))
+        bad = d > 2.0 ** -7 * np.abs(want.astype(np.float64)) + slack
+    assert not bad.any(), f"{bad.sum()} outputs outside the bound"
+
+
 # ----------------------------------------------------------------- RMSNorm + quantization
 
 def _gain(key, K):
