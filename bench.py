@@ -415,6 +415,40 @@ def main() -> int:
                 log(f"ffn100b M=1 scales {v}: {us:.1f} us, {res[v]['weight_GBs']} GB/s")
             sec["ffn100b_8layers_M1_weight_scales"] = res
             del packs
+            # the decode step as two launches (grouped quantization, grouped GEMV), with
+            # one scale per tensor and with group-128 scales
+            qs2 = [[torch.empty((1, x.shape[1]), dtype=torch.int8, device=dev) for x in xl] for xl in xs]
+            sx2 = [[torch.empty(1, dtype=torch.float32, device=dev) for _ in xl] for xl in xs]
+            qplan2 = tw.bitnet_grouped_plan_quant([(xs[l][j], qs2[l][j], sx2[l][j]) for l in range(30) for j in range(4)])
+            gpk = []
+            for m in mats:
+                w = W.weights(m, dev)
+                gpk.append(tw.pack_weights_grouped(w, 128, 1e-5))
+                del w
+            dres = {}
+            for v, plan_probs in (
+                    ("per_tensor", [(qs2[m.layer][m.slot], sx2[m.layer][m.slot], packed[i], sws[i], ys[i], None)
+                                    for i, m in enumerate(mats)]),
+                    ("group128", [(qs2[m.layer][m.slot], sx2[m.layer][m.slot], gpk[i][0], gpk[i][1], ys[i], None, 128)
+                                  for i, m in enumerate(mats)])):
+                lp = tw.bitnet_grouped_plan_linear(plan_probs)
+                for _ in range(50):
+                    qplan2.launch(stream)
+                    lp.launch(stream)
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(100):
+                    qplan2.launch(stream)
+                    lp.launch(stream)
+                b.record(stream)
+                torch.cuda.synchronize()
+                us = a.elapsed_time(b) * 1e3 / 100
+                dres[v] = {"us": round(us, 1), "weight_GBs": round(weight_bytes / (us * 1e-6) / 1e9, 1),
+                           "scale_bytes": (4 if v == "per_tensor" else sum(p_[1].numel() * 4 for p_ in gpk))}
+                log(f"decode step two launches, scales {v}: {us:.1f} us")
+            sec["decode_step_2p4b_weight_scales"] = dres
+            del gpk
         line["secondary"] = sec
 
     # ------------------------------------------------------------ CPU baseline

@@ -256,10 +256,13 @@ typedef struct bitnet_linear_desc {
     const int8_t *q;        /* (device) [M][K]   */
     const float *s_x;       /* (device) [M]      */
     const uint8_t *packed;  /* (device) [N][K/4] */
-    const float *s_w;       /* (device) [1]      */
+    const float *s_w;       /* (device) [1], or [N][K/w_group] */
     float *y;               /* (device) [M][N]   */
     int32_t *acc;           /* (device) [M][N] or NULL */
     int64_t M, N, K;
+    int64_t w_group;        /* weight-scale granularity as in bitnet_linear_ex: 0, K, or
+                               a multiple of 64 dividing K (a plan holding any of the
+                               latter runs the decode GEMV for all its problems) */
 } bitnet_linear_desc;
 
 typedef struct bitnet_quant_desc {

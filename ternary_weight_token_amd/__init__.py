@@ -26,7 +26,7 @@ class BitnetError(RuntimeError):
 class _LinearDesc(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("s_x", ctypes.c_void_p), ("packed", ctypes.c_void_p),
                 ("s_w", ctypes.c_void_p), ("y", ctypes.c_void_p), ("acc", ctypes.c_void_p),
-                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("w_group", ctypes.c_int64)]
 
 
 class _FusedDesc(ctypes.Structure):
@@ -230,13 +230,16 @@ class GroupedPlan:
 
 
 def bitnet_grouped_plan_linear(problems, device=None) -> GroupedPlan:
-    """problems: list of (q, s_x, packed, s_w, y, acc_or_None)."""
+    """problems: list of (q, s_x, packed, s_w, y, acc_or_None[, w_group]); w_group as
+    in bitnet_linear_ex (s_w [N][K / w_group] when it is nonzero)."""
     arr = (_LinearDesc * len(problems))()
     refs = []
-    for i, (q, s_x, packed, s_w, y, acc) in enumerate(problems):
+    for i, prob in enumerate(problems):
+        q, s_x, packed, s_w, y, acc = prob[:6]
+        w_group = int(prob[6]) if len(prob) > 6 else 0
         M, K = q.shape
         arr[i] = _LinearDesc(q.data_ptr(), s_x.data_ptr(), packed.data_ptr(), s_w.data_ptr(),
-                             y.data_ptr(), 0 if acc is None else acc.data_ptr(), M, packed.shape[0], K)
+                             y.data_ptr(), 0 if acc is None else acc.data_ptr(), M, packed.shape[0], K, w_group)
         refs.append((q, s_x, packed, s_w, y, acc))
     n = lib().bitnet_grouped_plan_bytes(len(problems), 1, ctypes.cast(arr, ctypes.c_void_p))
     buf = ctypes.create_string_buffer(n)

@@ -187,7 +187,13 @@ static size_t plan_layout(int count, size_t desc_size, uint64_t blocks, uint64_t
 
 // A plan whose problems all have M == 1 runs the GEMV (q staged in LDS); any M > 1
 // makes it run the MFMA decode kernel, which reads each weight once for all M tokens.
+// Problems with group-wise weight scales (w_group below K) make the whole plan run
+// the GEMV with its grouped path (the MFMA decode kernel has one).
+static bool desc_groups(const bitnet_linear_desc &d) { return d.w_group > 0 && d.w_group < d.K; }
+
 static uint32_t linear_variant(const bitnet_linear_desc *d, int count) {
+    for (int i = 0; i < count; ++i)
+        if (desc_groups(d[i])) return kVariantGemvGroups;
     for (int i = 0; i < count; ++i)
         if (d[i].M > 1) return kVariantMfma;
     return kVariantGemv;
@@ -207,6 +213,8 @@ static int check_linear_desc(const bitnet_linear_desc &d) {
     if (st) return st;
     if (d.M < 1 || d.M > kGemvMaxM || d.N < 1) return fail(BITNET_ERR_SHAPE, "grouped linear needs 1 <= M <= 16, N >= 1");
     if (!linear_fast(d.q, d.packed, d.K)) return fail(BITNET_ERR_ALIGN, "grouped linear needs K % 64 == 0 and 16-byte aligned q/packed");
+    if (d.w_group < 0 || (d.w_group > 0 && (d.K % d.w_group != 0 || (desc_groups(d) && d.w_group % 64 != 0))))
+        return fail(BITNET_ERR_SHAPE, "w_group must be 0, K, or a multiple of 64 dividing K");
     return BITNET_OK;
 }
 
@@ -280,7 +288,8 @@ BITNET_API int bitnet_grouped_plan_linear(const bitnet_linear_desc *descs, int c
         for (int i = 0; i < count; ++i) h->lds_bytes = std::max(h->lds_bytes, skinny_grouped_lds_bytes(descs[i].M, descs[i].K));
     } else {
         h->rows_per_block = gemv_grouped_rows_per_block();
-        for (int i = 0; i < count; ++i) h->lds_bytes = std::max(h->lds_bytes, gemv_grouped_lds_bytes(descs[i].K));
+        for (int i = 0; i < count; ++i)
+            h->lds_bytes = std::max(h->lds_bytes, gemv_grouped_lds_bytes(descs[i].K, variant == kVariantGemvGroups));
     }
     h->desc_offset = doff;
     h->table_offset = toff;
@@ -289,7 +298,8 @@ BITNET_API int bitnet_grouped_plan_linear(const bitnet_linear_desc *descs, int c
     BlockEntry *tb = (BlockEntry *)(p + toff);
     for (int i = 0; i < count; ++i) {
         const bitnet_linear_desc &d = descs[i];
-        dd[i] = LinearDescDev{d.q, d.s_x, d.packed, d.s_w, d.y, d.acc, (int32_t)d.M, (int32_t)d.N, (int32_t)d.K, 0};
+        dd[i] = LinearDescDev{d.q, d.s_x, d.packed, d.s_w, d.y, d.acc, (int32_t)d.M, (int32_t)d.N, (int32_t)d.K,
+                              (int32_t)d.w_group};
     }
     // Workgroups are dispatched roughly in table order: put the longest ones (largest
     // K, i.e. most bytes per row) first so that the short ones fill the tail.
@@ -416,8 +426,9 @@ BITNET_API int bitnet_linear_grouped(const void *plan_host, const void *plan_dev
     if (h->total_blocks == 0) return BITNET_OK;
     if (h->variant == kVariantMfma)
         return hip_status(launch_skinny_grouped(plan_dev, h->total_blocks, h->lds_bytes, (hipStream_t)stream));
-    if (h->variant != kVariantGemv) return fail(BITNET_ERR_ARG, "not a plan of this kind");
-    return hip_status(launch_gemv_grouped(plan_dev, h->total_blocks, h->lds_bytes, (hipStream_t)stream));
+    if (h->variant != kVariantGemv && h->variant != kVariantGemvGroups) return fail(BITNET_ERR_ARG, "not a plan of this kind");
+    return hip_status(launch_gemv_grouped(plan_dev, h->total_blocks, h->lds_bytes, h->variant == kVariantGemvGroups,
+                                          (hipStream_t)stream));
 }
 
 BITNET_API int bitnet_linear_fused_grouped(const void *plan_host, const void *plan_dev, void *stream) {

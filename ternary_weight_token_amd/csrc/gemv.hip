@@ -572,8 +572,10 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(
 // K segment length in 64-weight chunks for an M tile of mt rows: the whole of K when
 // its staged q fits the LDS budget, else the fewest segments of equal size, each a
 // multiple of 8 chunks (one per lane of an octet).
-__host__ __device__ __forceinline__ int segment_chunks(int C, int mt) {
-    const int max_seg = (kLdsBudget / (mt * kLdsChunkDw * 4)) & ~7;
+// dw: LDS dwords per staged chunk (kLdsChunkDw, or one more with group-wise scales,
+// which also keep each chunk's sum of q).
+__host__ __device__ __forceinline__ int segment_chunks(int C, int mt, int dw = kLdsChunkDw) {
+    const int max_seg = (kLdsBudget / (mt * dw * 4)) & ~7;
     if (C <= max_seg) return C;
     const int nseg = (C + max_seg - 1) / max_seg;
     return (((C + nseg - 1) / nseg) + 7) & ~7;
@@ -584,6 +586,9 @@ __host__ __device__ __forceinline__ int segment_chunks(int C, int mt) {
 constexpr int kGroupedRG = BITNET_GROUPED_RG;
 constexpr int kGroupedMT = 1;
 
+// GRP: the plan has problems with group-wise weight scales (descriptor w_group below
+// K), which take the grouped tile; plans without them use the kernel without it.
+template <bool GRP>
 __global__ __launch_bounds__(256) void gemv_grouped_kernel(const uint8_t *__restrict__ plan) {
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
     __shared__ int sq[kGroupedMT];
@@ -594,9 +599,19 @@ __global__ __launch_bounds__(256) void gemv_grouped_kernel(const uint8_t *__rest
     const int rows = 4 * 8 * kGroupedRG;
     const int rowblocks = (d.N + rows - 1) / rows;
     const int rb = (int)(e.local % rowblocks), mt = (int)(e.local / rowblocks);
-    gemv_lds_tile<kGroupedMT, kGroupedRG, BITNET_GROUPED_DOT8 != 0, BITNET_GEMV_NT != 0, 4>(
-        StageQ<kGroupedMT, BITNET_GROUPED_DOT8 != 0>{d.q, d.K}, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, OutSpec{d.y, nullptr, 0}, d.acc, rb * rows, mt * kGroupedMT, 1, segment_chunks(d.K >> 6, kGroupedMT), dyn,
-        sq, red);
+    const OutSpec out{d.y, nullptr, 0, d.w_group};
+    constexpr bool D8 = BITNET_GROUPED_DOT8 != 0, NTL = BITNET_GEMV_NT != 0;
+    if (GRP && d.w_group > 0 && d.w_group < d.K) {
+        const int seg = segment_chunks(d.K >> 6, kGroupedMT, kLdsChunkDw + 1);
+        int *sqc = reinterpret_cast<int *>(dyn + kGroupedMT * seg * kLdsChunkDw);
+        gemv_lds_tile<kGroupedMT, kGroupedRG, D8, NTL, 4, StageQChunks<kGroupedMT, D8>, true>(
+            StageQChunks<kGroupedMT, D8>{d.q, d.K, sqc}, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, out, d.acc, rb * rows,
+            mt * kGroupedMT, 1, seg, dyn, sq, red, sqc);
+    } else {
+        gemv_lds_tile<kGroupedMT, kGroupedRG, D8, NTL, 4>(
+            StageQ<kGroupedMT, D8>{d.q, d.K}, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, out, d.acc, rb * rows,
+            mt * kGroupedMT, 1, segment_chunks(d.K >> 6, kGroupedMT), dyn, sq, red);
+    }
 }
 
 // Fused grouped decode: the same work items, with the activation quantization of
@@ -668,8 +683,9 @@ uint32_t gemv_grouped_rows_per_block() { return 4 * 8 * kGroupedRG; }
 uint32_t gemv_fused_rows_per_block() { return kFusedNW * 8 * kGroupedRG; }
 uint32_t gemv_fused_threads() { return 64 * kFusedNW; }
 uint32_t gemv_grouped_threads() { return 256; }
-uint32_t gemv_grouped_lds_bytes(int64_t K) {
-    return (uint32_t)(kGroupedMT * segment_chunks((int)(K / 64), kGroupedMT) * kLdsChunkDw * 4);
+uint32_t gemv_grouped_lds_bytes(int64_t K, bool grp) {
+    const int dw = kLdsChunkDw + (grp ? 1 : 0);
+    return (uint32_t)(kGroupedMT * segment_chunks((int)(K / 64), kGroupedMT, dw) * dw * 4);
 }
 
 template <int MT, int RG, bool DOT8, bool GRP>
@@ -715,8 +731,13 @@ hipError_t launch_gemv(const int8_t *q, const float *s_x, const uint8_t *packed,
     return launch_gemv_mt<false>(q, s_x, packed, s_w, M, N, K, y, acc, st);
 }
 
-hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st) {
-    gemv_grouped_kernel<<<dim3(blocks), dim3(256), lds_bytes, st>>>(reinterpret_cast<const uint8_t *>(plan_dev));
+hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, bool grp,
+                               hipStream_t st) {
+    const uint8_t *p = reinterpret_cast<const uint8_t *>(plan_dev);
+    if (grp)
+        gemv_grouped_kernel<true><<<dim3(blocks), dim3(256), lds_bytes, st>>>(p);
+    else
+        gemv_grouped_kernel<false><<<dim3(blocks), dim3(256), lds_bytes, st>>>(p);
     return hipGetLastError();
 }
 

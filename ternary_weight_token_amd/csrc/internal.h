@@ -32,6 +32,8 @@ constexpr uint32_t kPlanLinear = 1, kPlanQuant = 2, kPlanFused = 3;
 // Linear plan variants: one block per (row block, token) running the GEMV, or one
 // block per row block running the MFMA decode kernel for all tokens at once.
 constexpr uint32_t kVariantGemv = 0, kVariantMfma = 1;
+// ... and the GEMV with the group-wise-scale path, for plans with such weights.
+constexpr uint32_t kVariantGemvGroups = 2;
 // Fused plan variants: no problem with an RMSNorm, or some.
 constexpr uint32_t kVariantFused = 0, kVariantFusedNorm = 1;
 
@@ -44,7 +46,7 @@ struct PlanHeader {            // 64 bytes
 struct LinearDescDev {         // 64 bytes, device layout
     const int8_t *q; const float *s_x; const uint8_t *packed; const float *s_w;
     float *y; int32_t *acc;
-    int32_t M, N, K, pad;
+    int32_t M, N, K, w_group;  // w_group as OutSpec::w_group
 };
 
 struct QuantDescDev {          // 32 bytes
@@ -73,8 +75,9 @@ hipError_t launch_pack_grouped(const float *w, int64_t N, int64_t K, int64_t G, 
                                float *s_w, hipStream_t st);
 hipError_t launch_gemv(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                        int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st);
-hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st);
-uint32_t gemv_grouped_lds_bytes(int64_t K);
+hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, bool grp,
+                               hipStream_t st);
+uint32_t gemv_grouped_lds_bytes(int64_t K, bool grp = false);
 hipError_t launch_gemv_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, bool norm,
                                      hipStream_t st);
 int64_t gemv_fused_max_k();

@@ -232,3 +232,21 @@ def test_fused_plan_norm_checks_and_variant(L):
                     (F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, a16, n(-1.0)), ARG)):
         one = (F * 1)(d)
         assert L.bitnet_grouped_plan_fused(one, 1, buf, nb) == want
+
+
+def test_linear_plan_weight_groups(L):
+    D = tw._LinearDesc
+    a16 = 4096
+    arr = (D * 2)(D(a16, a16, a16, a16, a16, 0, 1, 300, 2560, 0), D(a16, a16, a16, a16, a16, 0, 3, 200, 2560, 128))
+    nb = L.bitnet_grouped_plan_bytes(2, 1, arr)
+    buf = ctypes.create_string_buffer(nb)
+    assert L.bitnet_grouped_plan_linear(arr, 2, buf, nb) == OK
+    hdr = (ctypes.c_uint32 * 8).from_buffer_copy(buf.raw[:32])
+    assert hdr[7] == 2                          # GEMV with the group-wise path, even with M = 3
+    assert hdr[3] == 3 + 2 * 3                  # GEMV blocks: one per 128 rows and token
+    for w_group in (96, 32, -64):               # not dividing K / not a multiple of 64
+        bad = (D * 1)(D(a16, a16, a16, a16, a16, 0, 1, 300, 2560, w_group))
+        assert L.bitnet_grouped_plan_linear(bad, 1, buf, nb) == SHAPE
+    ok = (D * 1)(D(a16, a16, a16, a16, a16, 0, 2, 300, 2560, 2560))     # per channel: MFMA variant stays
+    assert L.bitnet_grouped_plan_linear(ok, 1, buf, nb) == OK
+    assert (ctypes.c_uint32 * 8).from_buffer_copy(buf.raw[:32])[7] == 1

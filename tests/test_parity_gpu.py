@@ -313,6 +313,42 @@ def test_linear_weight_scale_groups(kernel, M, N, K, G, opts):
     assert not bad.any(), f"{bad.sum()} outputs outside the bound"
 
 
+@pytest.mark.parametrize("mixed_m", [False, True])
+def test_grouped_plan_weight_scales(mixed_m):
+    """One grouped linear launch over problems with one scale per tensor, per output
+    channel and per group of 128 / 64 weights (and, mixed_m, M up to 5)."""
+    shapes = [(300, 2560, 0), (129, 2560, 2560), (200, 6912, 128), (70, 640, 64), (640, 2560, 128)]
+    probs, refs = [], []
+    for i, (N, K, G) in enumerate(shapes):
+        M = (1 + i % 5) if mixed_m else 1
+        key = synth.stream_key(332, i, M)
+        x, q, s = quantized_inputs(key, M, K)
+        w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02).numpy()
+        w[:, : max(G, 64)] *= 5.0
+        if G:
+            packed, s_w = oracle.pack_grouped(w, G, 1e-5)
+            acc_ref, y_ref = oracle.linear_grouped(q, s, packed, s_w, G)
+            slack = _grouped_bound(q, s, packed, s_w, G, K)
+        else:
+            packed, s_w = oracle.pack(w, 1e-5)
+            acc_ref, y_ref = oracle.linear(q, s, packed, s_w)
+            s_w = np.array([s_w], np.float32)
+            slack = 0.0
+        refs.append((acc_ref, y_ref, slack))
+        y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+        acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+        probs.append((torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV), torch.from_numpy(packed).to(DEV),
+                      torch.from_numpy(s_w).to(DEV), y, acc, G))
+    plan = tw.bitnet_grouped_plan_linear(probs)
+    for _ in range(2):
+        plan.launch()
+        torch.cuda.synchronize()
+        for (acc_ref, y_ref, slack), pr in zip(refs, probs):
+            assert np.array_equal(pr[5].cpu().numpy(), acc_ref)
+            d = np.abs(pr[4].cpu().numpy().astype(np.float64) - y_ref.astype(np.float64))
+            assert np.all(d <= REL * np.abs(y_ref.astype(np.float64)) + slack)
+
+
 # ----------------------------------------------------------------- RMSNorm + quantization
 
 def _gain(key, K):
