@@ -50,6 +50,7 @@ def lib():
         L.oracle_to_bf16.argtypes = [P, I64, P]
         L.oracle_rmsnorm_quant.argtypes = [P, P, ctypes.c_float, I64, I64, P, P]
         L.oracle_pack_grouped.argtypes = [P, I64, I64, I64, ctypes.c_float, P, P]
+        L.oracle_swiglu_quant.argtypes = [P, P, I64, I64, P, P, P]
         L.oracle_linear_grouped.argtypes = [P, P, P, P, I64, P, I64, I64, I64, P, P]
         L.oracle_set_threads.argtypes = [ctypes.c_int]
         L.oracle_get_threads.restype = ctypes.c_int
@@ -149,6 +150,20 @@ def rmsnorm_quant(x_bits: np.ndarray, gain: np.ndarray, eps: float) -> tuple[np.
     s = np.empty(M, dtype=np.float32)
     lib().oracle_rmsnorm_quant(_p(x_bits), _p(gain), ctypes.c_float(eps), M, K, _p(q), _p(s))
     return q, s
+
+
+def swiglu_quant(g: np.ndarray, u: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """a = fp32(silu(g) u), then absmax int8 of a: g, u fp32 [M][K] ->
+    (a fp32 [M][K], q int8 [M][K], s_x fp32 [M])."""
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    M, K = g.shape
+    assert u.shape == (M, K)
+    a = np.empty((M, K), dtype=np.float32)
+    q = np.empty((M, K), dtype=np.int8)
+    s = np.empty(M, dtype=np.float32)
+    lib().oracle_swiglu_quant(_p(g), _p(u), M, K, _p(a), _p(q), _p(s))
+    return a, q, s
 
 
 def linear(q: np.ndarray, s_x: np.ndarray, packed: np.ndarray, s_w, K: int | None = None,

@@ -35,7 +35,9 @@
  *  - a 2-bit field holding 3 (never written by the packer) decodes to +2;
  *  - the optional bias ([P1] 3.1 adds it after the rescale) joins the float64
  *    value before its one rounding to fp32; a bf16 output is that fp32 value
- *    rounded again, to nearest bf16, ties to even.
+ *    rounded again, to nearest bf16, ties to even;
+ *  - RMSNorm before quantization, group-wise weight scales and SwiGLU before the
+ *    down projection: see the comments of their functions below.
  *
  * Parity pins for every function live in tests/test_oracle_pins.py.
  * Build: gcc -O2 -std=c11 -fPIC -shared -fopenmp -ffp-contract=off.
@@ -228,6 +230,45 @@ void oracle_rmsnorm_quant(const uint16_t *x, const float *g, float eps, int64_t 
             if (v > 127.0) v = 127.0;
             if (v < -127.0) v = -127.0;
             q[m * K + k] = (int8_t)v;
+        }
+    }
+}
+
+/* --- SwiGLU before the down projection's quantization ([P1] 3.1) -------- */
+
+/* [P1] 3.1's block feeds its down projection with silu(gate(h)) * up(h): the
+ * activation row of down is a_k = silu(g_k) u_k, g and u the fp32 outputs of the
+ * gate and up projections, silu(v) = v / (1 + exp(-v)).  Here a_k is that real
+ * value rounded once to fp32 (evaluated in float64 with the C library's exp), and
+ * the row is quantized like any activation row: s = max_k |a_k| (exact), q_k =
+ * RNE(127 a_k / s).  127 a_k is exact in float64 and the correctly rounded quotient
+ * cannot create or cross a half-integer (the ratio of two fp32 values times 127
+ * is either exactly one or at least 2^-32 relatively away), so the codes are the
+ * exact rounding.  A row of zeros gives q = 0 and s_x = 0.
+ *   g, u: fp32 [M][K]; outputs a fp32 [M][K] (or NULL), q int8 [M][K], s_x [M]. */
+static float silu_mul(float g, float u) {
+    const double gd = (double)g;
+    return (float)((gd / (1.0 + exp(-gd))) * (double)u);
+}
+
+void oracle_swiglu_quant(const float *g, const float *u, int64_t M, int64_t K, float *a, int8_t *q,
+                         float *s_x) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float s = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            const float v = silu_mul(g[m * K + k], u[m * K + k]);
+            if (a) a[m * K + k] = v;
+            if (fabsf(v) > s) s = fabsf(v);
+        }
+        s_x[m] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            if (s == 0.0f) { q[m * K + k] = 0; continue; }
+            const double v = (double)silu_mul(g[m * K + k], u[m * K + k]);
+            double r = rint((127.0 * v) / (double)s);
+            if (r > 127.0) r = 127.0;
+            if (r < -127.0) r = -127.0;
+            q[m * K + k] = (int8_t)r;
         }
     }
 }

@@ -603,3 +603,76 @@ def test_linear_grouped_uniform_scales_match_per_tensor():
     acc_t, y_t = oracle.linear(q, s, packed, np.float32(0.0137))
     assert np.array_equal(acc_g, acc_t)
     assert np.all(np.abs(y_g.astype(np.float64) - y_t) <= 2.0 ** -23 * np.abs(y_t.astype(np.float64)))
+
+
+# ----------------------------------------------------------------- SwiGLU before down
+
+def _silu_mul_exact_f32(g: float, u: float) -> float:
+    """fp32 rounding of g u / (1 + e^-g), e^-g to 50 digits (decimal module)."""
+    import decimal
+    ctx = decimal.Context(prec=50)
+    gd = decimal.Decimal(g)
+    den = ctx.add(decimal.Decimal(1), ctx.exp(ctx.minus(gd)))
+    val = ctx.divide(ctx.multiply(gd, decimal.Decimal(u)), den)
+    return round_fraction_to_f32(Fraction(val))
+
+
+def test_swiglu_quant_hand_case():
+    """silu(0) = 0; silu(20) u rounds to 20 u (the factor 1 - 2e-9 is below half
+    an fp32 unit); silu(1) 2 = 2 / (1 + 1/e) = 1.46211716..."""
+    g = np.array([[0.0, 1.0, -1.0, 20.0]], np.float32)
+    u = np.array([[3.0, 2.0, 2.0, 1.0]], np.float32)
+    a, q, s = oracle.swiglu_quant(g, u)
+    assert a[0, 0] == 0.0 and a[0, 3] == 20.0
+    assert a[0, 1] == np.float32(2.0 / (1.0 + math.exp(-1.0)))
+    assert a[0, 2] == np.float32(-2.0 / (1.0 + math.exp(1.0)))
+    assert s[0] == 20.0
+    # 127 a / 20 = 0, 9.284..., -3.415..., 127
+    assert q.tolist() == [[0, 9, -3, 127]]
+
+
+@pytest.mark.parametrize("K", [64, 300])
+def test_swiglu_quant_exact(K):
+    """a against the correctly rounded fp32 of g u / (1 + e^-g) (50-digit exp); codes
+    against exact rational RNE of 127 a / max|a|."""
+    key = synth.stream_key(27, K)
+    M = 3
+    g = (4.0 * synth.normal(key, M * K).float().numpy()).astype(np.float32).reshape(M, K)
+    u = synth.normal(synth.stream_key(key, 1), M * K).float().numpy().astype(np.float32).reshape(M, K)
+    a, q, s = oracle.swiglu_quant(g, u)
+    for m in range(M):
+        for k in range(K):
+            assert a[m, k] == np.float32(_silu_mul_exact_f32(float(g[m, k]), float(u[m, k]))), (m, k)
+        assert s[m] == np.abs(a[m]).max()
+        for k in range(K):
+            v = 127 * Fraction(float(a[m, k])) / Fraction(float(s[m]))
+            fl = v.numerator // v.denominator
+            rem = v - fl
+            r = fl + (1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2) else 0)
+            assert q[m, k] == r, (m, k)
+
+
+def test_swiglu_quant_invariants():
+    key = synth.stream_key(28)
+    M, K = 4, 512
+    g = (3.0 * synth.normal(key, M * K).float().numpy()).astype(np.float32).reshape(M, K)
+    u = synth.normal(synth.stream_key(key, 1), M * K).float().numpy().astype(np.float32).reshape(M, K)
+    a, q, s = oracle.swiglu_quant(g, u)
+    # up -> -up negates a and the codes
+    an, qn, sn = oracle.swiglu_quant(g, -u)
+    assert np.array_equal(an, -a) and np.array_equal(qn, -q) and np.array_equal(sn, s)
+    # up -> 2 up (exact) doubles a and s and keeps the codes
+    a2, q2, s2 = oracle.swiglu_quant(g, 2 * u)
+    assert np.array_equal(a2, 2 * a) and np.array_equal(q2, q) and np.array_equal(s2, 2 * s)
+    # silu(g) > 0 for g > 0 and < 0 for g < 0, so with up = 1 the signs follow g
+    a1, _, _ = oracle.swiglu_quant(g, np.ones_like(u))
+    assert np.array_equal(np.sign(a1), np.sign(g))
+    # silu(g) - silu(-g) = g: the two values of a differ by g to within rounding
+    am, _, _ = oracle.swiglu_quant(-g, np.ones_like(u))
+    assert np.all(np.abs((a1.astype(np.float64) - am) - g) <= 2.0 ** -23 * (np.abs(a1) + np.abs(am)))
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    # a row with up = 0
+    uz = u.copy()
+    uz[1] = 0.0
+    _, qz, sz = oracle.swiglu_quant(g, uz)
+    assert not qz[1].any() and sz[1] == 0.0
