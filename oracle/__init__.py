@@ -51,6 +51,7 @@ def lib():
         L.oracle_rmsnorm_quant.argtypes = [P, P, ctypes.c_float, I64, I64, P, P]
         L.oracle_pack_grouped.argtypes = [P, I64, I64, I64, ctypes.c_float, P, P]
         L.oracle_swiglu_quant.argtypes = [P, P, I64, I64, P, P, P]
+        L.oracle_quant_act_f32.argtypes = [P, I64, I64, P, P]
         L.oracle_linear_grouped.argtypes = [P, P, P, P, I64, P, I64, I64, I64, P, P]
         L.oracle_set_threads.argtypes = [ctypes.c_int]
         L.oracle_get_threads.restype = ctypes.c_int
@@ -149,6 +150,16 @@ def rmsnorm_quant(x_bits: np.ndarray, gain: np.ndarray, eps: float) -> tuple[np.
     q = np.empty((M, K), dtype=np.int8)
     s = np.empty(M, dtype=np.float32)
     lib().oracle_rmsnorm_quant(_p(x_bits), _p(gain), ctypes.c_float(eps), M, K, _p(q), _p(s))
+    return q, s
+
+
+def quant_act_f32(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """absmax int8 of fp32 rows: x [M][K] -> (q int8 [M][K], s_x fp32 [M])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    M, K = x.shape
+    q = np.empty((M, K), dtype=np.int8)
+    s = np.empty(M, dtype=np.float32)
+    lib().oracle_quant_act_f32(_p(x), M, K, _p(q), _p(s))
     return q, s
 
 

@@ -189,6 +189,29 @@ void oracle_quant_act(const uint16_t *x, int64_t M, int64_t K,
     }
 }
 
+/* The same absmax quantization ([P1] 2.2) of fp32 rows (the SwiGLU output that
+ * feeds a down projection is fp32): s = max|x| (exact), q = RNE(127 x / s) with the
+ * real quotient.  127 x is exact in float64 and the correctly rounded float64
+ * quotient cannot create or cross a half-integer (see oracle_swiglu_quant), so the
+ * codes are the exact rounding.  x: fp32 [M][K]. */
+void oracle_quant_act_f32(const float *x, int64_t M, int64_t K, int8_t *q, float *s_x) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const float *row = x + m * K;
+        float s = 0.0f;
+        for (int64_t k = 0; k < K; ++k)
+            if (fabsf(row[k]) > s) s = fabsf(row[k]);
+        s_x[m] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            if (s == 0.0f) { q[m * K + k] = 0; continue; }
+            double r = rint((127.0 * (double)row[k]) / (double)s);
+            if (r > 127.0) r = 127.0;
+            if (r < -127.0) r = -127.0;
+            q[m * K + k] = (int8_t)r;
+        }
+    }
+}
+
 /* --- RMSNorm before the activation quantization ([P1] 3.1) -------------- */
 
 /* The block of [P1] 3.1 feeds its projections from an RMSNorm of the token row;

@@ -676,3 +676,51 @@ def test_swiglu_quant_invariants():
     uz[1] = 0.0
     _, qz, sz = oracle.swiglu_quant(g, uz)
     assert not qz[1].any() and sz[1] == 0.0
+
+
+# ----------------------------------------------------------------- fp32 rows
+
+def _rne_fraction(v: Fraction) -> int:
+    fl = v.numerator // v.denominator
+    rem = v - fl
+    return fl + (1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2) else 0)
+
+
+def test_quant_act_f32_hand_case():
+    q, s = oracle.quant_act_f32(np.array([[1.0, 2.0, 0.0, -1.0], [0.0, 0.0, 0.0, 0.0]], np.float32))
+    assert q.tolist() == [[64, 127, 0, -64], [0, 0, 0, 0]] and s.tolist() == [2.0, 0.0]
+
+
+def test_quant_act_f32_near_ties_exact():
+    """x = fp32((2j + 1) / 254) with s = 1: 127 x lies within an fp32 rounding of
+    j + 1/2, so only the exact quotient decides (binary32 arithmetic would not)."""
+    j = np.arange(0, 127)
+    x = np.concatenate([((2 * j + 1) / 254.0).astype(np.float32), [np.float32(1.0)]])
+    x = np.stack([x, -x])
+    q, s = oracle.quant_act_f32(x)
+    assert s.tolist() == [1.0, 1.0]
+    for m in range(2):
+        for k in range(x.shape[1]):
+            assert q[m, k] == _rne_fraction(127 * Fraction(float(x[m, k]))), (m, k)
+
+
+def test_quant_act_f32_exact_random():
+    key = synth.stream_key(29)
+    M, K = 4, 700
+    x = synth.normal(key, M * K).float().numpy().astype(np.float32).reshape(M, K)
+    x[1] *= 1e-30
+    x[2] *= 1e30
+    q, s = oracle.quant_act_f32(x)
+    for m in range(M):
+        assert s[m] == np.abs(x[m]).max()
+        for k in range(K):
+            assert q[m, k] == _rne_fraction(127 * Fraction(float(x[m, k])) / Fraction(float(s[m]))), (m, k)
+
+
+def test_swiglu_quant_codes_are_those_of_its_fp32_row():
+    key = synth.stream_key(30)
+    g = (3.0 * synth.normal(key, 3 * 640).float().numpy()).astype(np.float32).reshape(3, 640)
+    u = synth.normal(synth.stream_key(key, 1), 3 * 640).float().numpy().astype(np.float32).reshape(3, 640)
+    a, q, s = oracle.swiglu_quant(g, u)
+    q2, s2 = oracle.quant_act_f32(a)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
