@@ -260,7 +260,42 @@ def main() -> int:
                 "normed_matrices": sum(1 for m in mats if m.slot in W.NORMED_SLOTS_2P4B),
                 "vs_plain_fused_us": round(n_us - kern_ms * 1e3, 1)}
             log(f"fused step with RMSNorm: {n_us:.1f} us ({n_us - kern_ms * 1e3:+.1f} us vs without)")
-            del nplan, nys, gains
+            # and SwiGLU at both ends: each layer's gate / up as one pair problem whose
+            # epilogue writes silu(y_gate) y_up (RMSNorm-ed input), and the down
+            # projection taking an fp32 row (the SwiGLU output) as its input
+            hidden = [W.decode_step_ffn_hidden(l, dev) for l in range(30)]
+            sprobs = []
+            for i, m in enumerate(mats):
+                if m.name == "up":
+                    continue
+                if m.name == "gate":
+                    iu = next(j for j, o in enumerate(mats) if o.layer == m.layer and o.name == "up")
+                    sprobs.append((xs[m.layer][m.slot], (packed[i], packed[iu]), (sws[i], sws[iu]), nys[i], None,
+                                   None, None, gains[m.layer].get(m.slot), 1e-6))
+                elif m.slot == W.SWIGLU_SLOT_2P4B:
+                    sprobs.append((hidden[m.layer], packed[i], sws[i], nys[i], None, None, None))
+                else:
+                    sprobs.append((xs[m.layer][m.slot], packed[i], sws[i], nys[i], None, None, None,
+                                   gains[m.layer].get(m.slot), 1e-6))
+            splan = tw.bitnet_grouped_plan_fused(sprobs)
+            for _ in range(200):
+                splan.launch(stream)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(200):
+                splan.launch(stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            s_us = a.elapsed_time(b) * 1e3 / 200
+            for y in nys:
+                assert torch.isfinite(y).all()
+            sec["decode_step_2p4b_rmsnorm_swiglu_fused"] = {
+                "us": round(s_us, 1), "weight_GBs": round(weight_bytes / (s_us * 1e-6) / 1e9, 1),
+                "gate_up_pairs": sum(1 for m in mats if m.name == "gate"),
+                "fp32_input_matrices": sum(1 for m in mats if m.slot == W.SWIGLU_SLOT_2P4B),
+                "vs_rmsnorm_fused_us": round(s_us - n_us, 1)}
+            log(f"fused step with RMSNorm and SwiGLU: {s_us:.1f} us ({s_us - n_us:+.1f} us vs RMSNorm only)")
+            del nplan, splan, nys, gains, hidden
         if "prefill" in legs:
             # prefill GEMM, M = 2048
             reps = 50

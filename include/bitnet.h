@@ -144,6 +144,28 @@ BITNET_API int bitnet_rmsnorm_quant_act(const uint16_t *x, const float *gain, fl
                                         void *stream);
 
 /* ---------------------------------------------------------------------------
+ * SwiGLU of the gate and up projections' outputs followed by the absmax int8
+ * quantization of the result: the input row of the down projection.  Page:
+ * chenxutan.com sec. 3.1 (the block's feed-forward part passes silu(gate(h)) *
+ * up(h) to its down projection, silu(v) = v / (1 + e^-v); the down projection
+ * quantizes its input on entry, sec. 2.2).
+ *
+ *   gate  (device) fp32 [M][K], the gate projection's output g
+ *   up    (device) fp32 [M][K], the up projection's output u
+ *   q     (device) int8 [M][K], output;  s_x (device) fp32 [M], output
+ *
+ * a = g u / (1 + e^-g) is evaluated in float64 and rounded once to fp32 (e^-g
+ * with the device math library's float64 exp; a host float64 exp may differ in
+ * its last bit, which moves a only where the float64 value lies within about
+ * 2^-29 of an fp32 rounding boundary).  Then s_x = max|a| over the row and q =
+ * round_half_even(127 a / s_x), decided exactly; a row of zeros gives q = 0 and
+ * s_x = 0.  Inputs must give finite a.  Needs K % 8 == 0 and 16-byte aligned
+ * gate, up and q (BITNET_ERR_SHAPE / BITNET_ERR_ALIGN).
+ * ------------------------------------------------------------------------- */
+BITNET_API int bitnet_swiglu_quant_act(const float *gate, const float *up, int64_t M, int64_t K,
+                                       int8_t *q, float *s_x, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Ternary contraction with the fp32 rescale (BitLinear forward after the two
  * quantizations).  Pages: chenxutan.com sec. 2.3 (Y ~ (W_t . X_q) * act_scale *
  * beta) and sec. 3.1 (BitLinear.forward); the ternary product is a sign-select
@@ -301,6 +323,18 @@ BITNET_API int bitnet_quant_act_grouped(const void *plan_host, const void *plan_
  * norm_eps) followed by bitnet_linear instead (the RMSNorm before each projection
  * of chenxutan.com sec. 3.1, fused the same way; problems sharing a token row and
  * gain, such as q / k / v, each normalize it in their own workgroups).
+ *
+ * The two ends of the SwiGLU feed-forward part of chenxutan.com sec. 3.1
+ * (down(silu(gate(h)) * up(h))):
+ *  - a gate / up pair (packed_up and s_w_up set) computes both projections of the
+ *    row in the same workgroups and writes y[n] = fp32(silu(y_gate[n]) y_up[n]),
+ *    where y_gate / y_up are bitnet_linear's fp32 outputs of the two matrices (one
+ *    rounding each) and the SwiGLU is evaluated in float64 and rounded once, as in
+ *    bitnet_swiglu_quant_act; the pair takes x with or without norm_gain;
+ *  - a descriptor with x_f32 quantizes that fp32 row like bitnet_quant_act does a
+ *    bf16 row (s_x = max|x|, q = round_half_even(127 x / s_x) decided exactly), so
+ *    bitnet_swiglu_quant_act(g, u) followed by bitnet_linear equals the pair's
+ *    output fed through an x_f32 descriptor.
  * ------------------------------------------------------------------------- */
 typedef struct bitnet_fused_desc {
     const uint16_t *x;      /* (device) [M][K] bf16 bits */
@@ -314,6 +348,13 @@ typedef struct bitnet_fused_desc {
     const float *norm_gain; /* (device) [K] fp32, 16-byte aligned, or NULL: when set, the
                                row is RMSNorm-ed first (bitnet_rmsnorm_quant_act) */
     float norm_eps;         /* the norm's eps (finite, >= 0); ignored without norm_gain */
+    const float *x_f32;     /* (device) [M][K] fp32, 16-byte aligned, or NULL: the input row
+                               in fp32 instead of x (x and norm_gain NULL), such as the
+                               SwiGLU output feeding a down projection */
+    const uint8_t *packed_up; /* (device) [N][K/4], 16-byte aligned, or NULL: with s_w_up,
+                               the problem is the gate (packed, s_w) / up (packed_up,
+                               s_w_up) pair of a SwiGLU feed-forward part; acc must be NULL */
+    const float *s_w_up;    /* (device) [1] */
 } bitnet_fused_desc;
 
 BITNET_API size_t bitnet_grouped_plan_fused_bytes(int count, const bitnet_fused_desc *descs);

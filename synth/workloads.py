@@ -73,6 +73,19 @@ def decode_step_gains(layer: int, device="cpu"):
     return out
 
 
+# activation slot whose row is the SwiGLU output, fp32 (the down projection's input
+# in chenxutan.com sec. 3.1's block)
+SWIGLU_SLOT_2P4B = 3
+
+
+def decode_step_ffn_hidden(layer: int, device="cpu"):
+    """fp32 [1][6912] row of one layer standing in for the SwiGLU output that feeds
+    the down projection: N(0, 1), seeded per layer (synthetic)."""
+    from . import normal
+    K = SLOT_K_2P4B[SWIGLU_SLOT_2P4B]
+    return normal(stream_key(CFG_DECODE, layer, 300), K, device).to(torch.float32).reshape(1, K).contiguous()
+
+
 def ffn_100b(layers: int = 8):
     out = []
     for l in range(layers):

@@ -33,7 +33,8 @@ class _FusedDesc(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("packed", ctypes.c_void_p), ("s_w", ctypes.c_void_p),
                 ("y", ctypes.c_void_p), ("acc", ctypes.c_void_p), ("q", ctypes.c_void_p),
                 ("s_x", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
-                ("norm_gain", ctypes.c_void_p), ("norm_eps", ctypes.c_float)]
+                ("norm_gain", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
+                ("x_f32", ctypes.c_void_p), ("packed_up", ctypes.c_void_p), ("s_w_up", ctypes.c_void_p)]
 
 
 class _QuantDesc(ctypes.Structure):
@@ -59,6 +60,7 @@ def lib() -> ctypes.CDLL:
         L.bitnet_pack_weights.argtypes = [P, I64, I64, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
         L.bitnet_quant_act.argtypes = [P, I64, I64, P, P, P]
         L.bitnet_rmsnorm_quant_act.argtypes = [P, P, ctypes.c_float, I64, I64, P, P, P]
+        L.bitnet_swiglu_quant_act.argtypes = [P, P, I64, I64, P, P, P]
         L.bitnet_linear.argtypes = [P, P, P, P, I64, I64, I64, P, P, P]
         L.bitnet_linear_select.argtypes = [P, P, P, P, I64, I64, I64, P, P, I, P]
         L.bitnet_linear_ex.argtypes = [P, P, P, P, I64, I64, I64, I64, P, P, I, P, I, P]
@@ -73,7 +75,7 @@ def lib() -> ctypes.CDLL:
         L.bitnet_grouped_plan_fused_bytes.restype = ctypes.c_size_t
         L.bitnet_grouped_plan_fused.argtypes = [P, I, P, ctypes.c_size_t]
         L.bitnet_linear_fused_grouped.argtypes = [P, P, P]
-        for f in ("bitnet_pack_weights", "bitnet_pack_weights_grouped", "bitnet_quant_act", "bitnet_rmsnorm_quant_act", "bitnet_linear", "bitnet_linear_select", "bitnet_linear_ex",
+        for f in ("bitnet_pack_weights", "bitnet_pack_weights_grouped", "bitnet_quant_act", "bitnet_rmsnorm_quant_act", "bitnet_swiglu_quant_act", "bitnet_linear", "bitnet_linear_select", "bitnet_linear_ex",
                   "bitnet_grouped_plan_linear", "bitnet_grouped_plan_quant", "bitnet_grouped_plan_fused",
                   "bitnet_linear_grouped", "bitnet_quant_act_grouped", "bitnet_linear_fused_grouped"):
             getattr(L, f).restype = I
@@ -142,6 +144,17 @@ def bitnet_rmsnorm_quant_act(x: torch.Tensor, gain: torch.Tensor, eps: float, q:
         raise ValueError("gain must be [K], q [M][K] and s_x [M]")
     _check(lib().bitnet_rmsnorm_quant_act(_ptr(x), _ptr(gain), ctypes.c_float(eps), M, K, _ptr(q), _ptr(s_x),
                                           _stream(stream)))
+
+
+def bitnet_swiglu_quant_act(gate: torch.Tensor, up: torch.Tensor, q: torch.Tensor, s_x: torch.Tensor,
+                            stream=None) -> None:
+    """gate, up fp32 [M][K] -> q int8 [M][K], s_x fp32 [M] of a = silu(gate) up."""
+    _dev(gate, torch.float32, "gate"); _dev(up, torch.float32, "up")
+    _dev(q, torch.int8, "q"); _dev(s_x, torch.float32, "s_x")
+    M, K = gate.shape
+    if up.shape != (M, K) or q.shape != (M, K) or s_x.shape != (M,):
+        raise ValueError("up and q must be [M][K] like gate, s_x [M]")
+    _check(lib().bitnet_swiglu_quant_act(_ptr(gate), _ptr(up), M, K, _ptr(q), _ptr(s_x), _stream(stream)))
 
 
 def bitnet_linear(q: torch.Tensor, s_x: torch.Tensor, packed: torch.Tensor, s_w: torch.Tensor,
@@ -269,23 +282,38 @@ def bitnet_grouped_plan_quant(problems, device=None) -> GroupedPlan:
 
 def bitnet_grouped_plan_fused(problems, device=None) -> GroupedPlan:
     """problems: list of (x, packed, s_w, y, acc_or_None, q_or_None, s_x_or_None
-    [, norm_gain, norm_eps]); x is bf16 [1][K] (quantized inside the launch, after an
-    RMSNorm with the fp32 gain [K] when one is given)."""
+    [, norm_gain, norm_eps]).  x is a bf16 [1][K] row (quantized inside the launch,
+    after an RMSNorm with the fp32 gain [K] when one is given) or an fp32 [1][K] row
+    (quantized the same way, no norm).  packed and s_w are one matrix, or the pairs
+    (packed_gate, packed_up) and (s_w_gate, s_w_up) of a SwiGLU feed-forward part,
+    whose y gets fp32(silu(y_gate) y_up)."""
     arr = (_FusedDesc * len(problems))()
     refs = []
     for i, prob in enumerate(problems):
         x, packed, s_w, y, acc, q, s_x = prob[:7]
         gain, eps = (prob[7], float(prob[8])) if len(prob) > 7 and prob[7] is not None else (None, 0.0)
-        _dev(x, torch.bfloat16, "x")
+        if not isinstance(x, torch.Tensor) or x.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("x must be a bf16 or fp32 tensor")
+        _dev(x, x.dtype, "x")
         M, K = x.shape
+        xp, xf = (x.data_ptr(), 0) if x.dtype == torch.bfloat16 else (0, x.data_ptr())
+        pu = su = 0
+        if isinstance(packed, (tuple, list)):
+            packed, packed_up = packed
+            s_w, s_w_up = s_w
+            _dev(packed_up, torch.uint8, "packed_up"); _dev(s_w_up, torch.float32, "s_w_up")
+            if packed_up.shape != packed.shape:
+                raise ValueError("gate and up weights must have one shape")
+            pu, su = packed_up.data_ptr(), s_w_up.data_ptr()
+            refs.append((packed_up, s_w_up))
         if gain is not None:
             _dev(gain, torch.float32, "norm_gain")
             if gain.shape != (K,):
                 raise ValueError("norm_gain must be [K]")
-        arr[i] = _FusedDesc(x.data_ptr(), packed.data_ptr(), s_w.data_ptr(), y.data_ptr(),
+        arr[i] = _FusedDesc(xp, packed.data_ptr(), s_w.data_ptr(), y.data_ptr(),
                             0 if acc is None else acc.data_ptr(), 0 if q is None else q.data_ptr(),
                             0 if s_x is None else s_x.data_ptr(), M, packed.shape[0], K,
-                            0 if gain is None else gain.data_ptr(), eps)
+                            0 if gain is None else gain.data_ptr(), eps, xf, pu, su)
         refs.append((x, packed, s_w, y, acc, q, s_x, gain))
     n = lib().bitnet_grouped_plan_fused_bytes(len(problems), ctypes.cast(arr, ctypes.c_void_p))
     buf = ctypes.create_string_buffer(n)
@@ -313,6 +341,14 @@ def rmsnorm_quant(x: torch.Tensor, gain: torch.Tensor, eps: float, stream=None):
     q = torch.empty((M, K), dtype=torch.int8, device=x.device)
     s_x = torch.empty(M, dtype=torch.float32, device=x.device)
     bitnet_rmsnorm_quant_act(x, gain, eps, q, s_x, stream)
+    return q, s_x
+
+
+def swiglu_quant(gate: torch.Tensor, up: torch.Tensor, stream=None):
+    M, K = gate.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=gate.device)
+    s_x = torch.empty(M, dtype=torch.float32, device=gate.device)
+    bitnet_swiglu_quant_act(gate, up, q, s_x, stream)
     return q, s_x
 
 

@@ -129,6 +129,18 @@ BITNET_API int bitnet_rmsnorm_quant_act(const uint16_t *x, const float *gain, fl
     return hip_status(launch_rmsnorm_quant(x, gain, eps, M, K, q, s_x, (hipStream_t)stream));
 }
 
+BITNET_API int bitnet_swiglu_quant_act(const float *gate, const float *up, int64_t M, int64_t K, int8_t *q,
+                                       float *s_x, void *stream) {
+    int st = check_dims(M, 1, K);
+    if (st) return st;
+    if (M == 0) return BITNET_OK;
+    if (!gate || !up || !q || !s_x) return fail(BITNET_ERR_NULL, "null pointer");
+    if (K % 8 != 0) return fail(BITNET_ERR_SHAPE, "K must be a multiple of 8");
+    if (!aligned(gate, 16) || !aligned(up, 16) || !aligned(q, 16) || !aligned(s_x, 4))
+        return fail(BITNET_ERR_ALIGN, "gate, up and q must be 16-byte aligned, s_x 4-byte");
+    return hip_status(launch_swiglu_quant(gate, up, M, K, q, s_x, (hipStream_t)stream));
+}
+
 BITNET_API int bitnet_linear_ex(const int8_t *q, const float *s_x, const uint8_t *packed,
                                 const float *s_w, int64_t w_group, int64_t M, int64_t N, int64_t K,
                                 const float *bias, void *y, int y_dtype, int32_t *acc, int kernel,
@@ -222,7 +234,19 @@ static int check_fused_desc(const bitnet_fused_desc &d) {
     int st = check_dims(d.M, d.N, d.K);
     if (st) return st;
     if (d.M != 1 || d.N < 1) return fail(BITNET_ERR_SHAPE, "fused linear needs M == 1, N >= 1");
-    if (!d.x || !d.packed || !d.s_w || !d.y) return fail(BITNET_ERR_NULL, "null pointer");
+    if (d.x_f32) {
+        if (d.x || d.norm_gain) return fail(BITNET_ERR_ARG, "an fp32 row takes no x and no norm_gain");
+        if (!aligned(d.x_f32, 16)) return fail(BITNET_ERR_ALIGN, "x_f32 must be 16-byte aligned");
+    } else if (!d.x) {
+        return fail(BITNET_ERR_NULL, "null pointer");
+    }
+    if (d.packed_up || d.s_w_up) {
+        if (!d.packed_up || !d.s_w_up) return fail(BITNET_ERR_NULL, "packed_up and s_w_up go together");
+        if (d.x_f32 || d.acc) return fail(BITNET_ERR_ARG, "a gate / up pair takes x (bf16) and no acc");
+        if (!aligned(d.packed_up, 16) || !aligned(d.s_w_up, 4))
+            return fail(BITNET_ERR_ALIGN, "packed_up must be 16-byte aligned, s_w_up 4-byte");
+    }
+    if (!d.packed || !d.s_w || !d.y) return fail(BITNET_ERR_NULL, "null pointer");
     if (d.K > gemv_fused_max_k()) return fail(BITNET_ERR_SHAPE, "fused linear needs K <= 52224");
     if (d.K % 64 != 0 || !aligned(d.x, 16) || !aligned(d.packed, 16) || (d.q && !aligned(d.q, 16)))
         return fail(BITNET_ERR_ALIGN, "fused linear needs K % 64 == 0 and 16-byte aligned x, packed and q");
@@ -351,7 +375,8 @@ BITNET_API int bitnet_grouped_plan_quant(const bitnet_quant_desc *descs, int cou
 }
 
 static uint64_t fused_blocks(const bitnet_fused_desc &d) {
-    const uint64_t rows = gemv_fused_rows_per_block();
+    // a gate / up pair takes both matrices' rows in each block: half the rows of each
+    const uint64_t rows = gemv_fused_rows_per_block() / (d.packed_up ? 2 : 1);
     return ((uint64_t)d.N + rows - 1) / rows;
 }
 
@@ -385,9 +410,11 @@ BITNET_API int bitnet_grouped_plan_fused(const bitnet_fused_desc *descs, int cou
     h->total_blocks = (uint32_t)blocks;
     h->block_threads = gemv_fused_threads();
     h->rows_per_block = gemv_fused_rows_per_block();
-    h->variant = kVariantFused;
-    for (int i = 0; i < count; ++i)
-        if (descs[i].norm_gain) h->variant = kVariantFusedNorm;
+    h->variant = 0;   // mask of the prologues in use
+    for (int i = 0; i < count; ++i) {
+        if (descs[i].norm_gain) h->variant |= kFusedProNorm;
+        if (descs[i].x_f32 || descs[i].packed_up) h->variant |= kFusedProSwiglu;
+    }
     for (int i = 0; i < count; ++i) h->lds_bytes = std::max(h->lds_bytes, gemv_grouped_lds_bytes(descs[i].K));
     h->desc_offset = doff;
     h->table_offset = toff;
@@ -397,7 +424,7 @@ BITNET_API int bitnet_grouped_plan_fused(const bitnet_fused_desc *descs, int cou
     for (int i = 0; i < count; ++i) {
         const bitnet_fused_desc &d = descs[i];
         dd[i] = FusedDescDev{d.x, d.packed, d.s_w, d.y, d.acc, d.q, d.s_x, (int32_t)d.M, (int32_t)d.N, (int32_t)d.K, 0,
-                             d.norm_gain, d.norm_gain ? d.norm_eps : 0.0f, 0};
+                             d.norm_gain, d.norm_gain ? d.norm_eps : 0.0f, 0, d.x_f32, d.packed_up, d.s_w_up};
     }
     // longest rows first, as for linear plans
     std::vector<int> order(count);
@@ -436,9 +463,9 @@ BITNET_API int bitnet_linear_fused_grouped(const void *plan_host, const void *pl
     if (st) return st;
     const PlanHeader *h = (const PlanHeader *)plan_host;
     if (h->total_blocks == 0) return BITNET_OK;
-    if (h->variant != kVariantFused && h->variant != kVariantFusedNorm) return fail(BITNET_ERR_ARG, "not a plan of this kind");
-    return hip_status(launch_gemv_fused_grouped(plan_dev, h->total_blocks, h->lds_bytes,
-                                                h->variant == kVariantFusedNorm, (hipStream_t)stream));
+    if (h->variant > kFusedProMask) return fail(BITNET_ERR_ARG, "not a plan of this kind");
+    return hip_status(launch_gemv_fused_grouped(plan_dev, h->total_blocks, h->lds_bytes, h->variant,
+                                                (hipStream_t)stream));
 }
 
 BITNET_API int bitnet_quant_act_grouped(const void *plan_host, const void *plan_dev, void *stream) {

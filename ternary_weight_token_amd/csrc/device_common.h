@@ -233,6 +233,63 @@ __device__ __forceinline__ float rms_scale(double mz, double ss, int K, float ep
     return (float)(mz * r);
 }
 
+// ---- SwiGLU before the down projection (page chenxutan.com sec. 3.1: the block
+// feeds its down projection with silu(gate(h)) * up(h), g and u the fp32 outputs of
+// gate and up).  a = g u / (1 + e^-g) is evaluated in float64 and rounded once to
+// fp32; the row is then quantized like any other fp32 row (scale max|a|, codes
+// rint(127 a / max|a|), qcode_f32).
+__device__ __forceinline__ float swiglu_value(float g, float u) {
+    const double gd = (double)g;
+    return (float)((gd / (1.0 + exp(-gd))) * (double)u);
+}
+
+// a of 8 values (g and u as two float4 each); returns the largest |a| bits (|a| as
+// an unsigned integer orders like |a| for finite values).
+__device__ __forceinline__ uint32_t swiglu8(float4 g0, float4 g1, float4 u0, float4 u1, float (&a)[8]) {
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    uint32_t mx = 0;
+    #pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        a[j] = swiglu_value(g[j], u[j]);
+        mx = max(mx, __float_as_uint(a[j]) & 0x7FFFFFFFu);
+    }
+    return mx;
+}
+
+// Code of an fp32 value x for the row scale s = max|x| > 0, inv = 1 / s (correctly
+// rounded): rint(127 x / s) of the real quotient.  t = fl(fl(127 x) inv) is within
+// 3.0001 2^-24 |127 x / s| <= 2.3e-5 of the quotient (three roundings; 127 x is exact
+// when it is subnormal), so when t is at least 4e-5 inside a half-integer interval
+// its nearest integer is the quotient's; otherwise (or for a non-finite t: inv
+// overflows for a subnormal s) float64 decides, where 127 x is exact and the
+// correctly rounded quotient never meets or crosses a half-integer it is not on.
+__device__ __forceinline__ int qcode_f32(float x, float s, float inv) {
+    const float t = (127.0f * x) * inv;
+    float r = __builtin_rintf(t);
+    if (!(fabsf(t - r) < 0.49996f)) r = (float)rint((127.0 * (double)x) / (double)s);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+// Codes of 8 fp32 values as 8 int8 bytes.
+__device__ __forceinline__ uint2 qcode8_f32(const float (&a)[8], float s, float inv) {
+    uint32_t b[8];
+    #pragma unroll
+    for (int j = 0; j < 8; ++j) b[j] = (uint32_t)qcode_f32(a[j], s, inv) & 0xFFu;
+    return make_uint2(b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24, b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24);
+}
+
+// Largest |x| bits among 8 fp32 values (|x| as an unsigned integer orders like |x|).
+__device__ __forceinline__ uint32_t absmax8_f32(float4 a, float4 b) {
+    const uint32_t m = 0x7FFFFFFFu;
+    const uint32_t u0 = max(__float_as_uint(a.x) & m, __float_as_uint(a.y) & m);
+    const uint32_t u1 = max(__float_as_uint(a.z) & m, __float_as_uint(a.w) & m);
+    const uint32_t u2 = max(__float_as_uint(b.x) & m, __float_as_uint(b.y) & m);
+    const uint32_t u3 = max(__float_as_uint(b.z) & m, __float_as_uint(b.w) & m);
+    return max(max(u0, u1), max(u2, u3));
+}
+
 // y = fp32(acc * c) with c = (s_x * s_w) / 127 formed in float64.
 __device__ __forceinline__ double rescale_factor(float s_x, float s_w) {
     return ((double)s_x * (double)s_w) / 127.0;

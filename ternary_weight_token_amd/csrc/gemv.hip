@@ -20,6 +20,7 @@
 //    several wavefronts they split K and combine their partials through LDS;
 //  * epilogue: y = fp32(acc * c_m), c_m = (s_x[m] * s_w) / 127 in float64.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -311,18 +312,100 @@ struct StageRmsQuantize {
     }
 };
 
+// From an fp32 activation row (such as the SwiGLU output that feeds a down
+// projection, page chenxutan.com sec. 3.1): the same absmax quantization (sec. 2.2)
+// of fp32 values, s = max|x| (integer max of the magnitude bits), codes by
+// qcode_f32; otherwise as StageQuantize.  The load phase holds one piece of 16
+// values per thread; the thread's second piece is held from the max to the codes,
+// later pieces (K > 64 NW 32) are read again.
+template <bool DOT8, int NW>
+struct StageQuantizeF32 {
+    static constexpr int kThreads = 64 * NW;
+    const float *x;      // [K] fp32, 16-byte aligned
+    int8_t *q_out;       // [K] or nullptr
+    float *s_out;        // or nullptr
+    float *s_lds;        // LDS
+    uint32_t *red;       // LDS, one word per wavefront (NW)
+    struct Pre { float4 v[4]; };
+    __device__ __forceinline__ Pre load(int, int sc) const {
+        const int r = min((int)threadIdx.x, sc * 4 - 1);   // a clamped duplicate leaves the max as it is
+        const float4 *p = reinterpret_cast<const float4 *>(x + 16 * r);
+        Pre pre;
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) pre.v[i] = p[i];
+        return pre;
+    }
+    __device__ __forceinline__ void operator()(const Pre &pre, int, int sc, int, int, int, uint32_t *qs,
+                                               int *sq) const {
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int pieces = sc * 4;
+        const float4 *xv = reinterpret_cast<const float4 *>(x);
+        const int r1 = tid + kThreads;
+        float4 v1[4];
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) v1[i] = xv[4 * min(r1, pieces - 1) + i];
+        uint32_t mx = max(absmax8_f32(pre.v[0], pre.v[1]), absmax8_f32(pre.v[2], pre.v[3]));
+        mx = max(mx, max(absmax8_f32(v1[0], v1[1]), absmax8_f32(v1[2], v1[3])));
+        for (int r = tid + 2 * kThreads; r < pieces; r += kThreads)
+            mx = max(mx, max(absmax8_f32(xv[4 * r], xv[4 * r + 1]), absmax8_f32(xv[4 * r + 2], xv[4 * r + 3])));
+        mx = wave_max_u32(mx);
+        if (lane == 0) red[wave] = mx;
+        __syncthreads();
+        mx = red[0];
+        #pragma unroll
+        for (int w = 1; w < NW; ++w) mx = max(mx, red[w]);
+        const float s = __uint_as_float(mx);
+        const float inv = 1.0f / s;
+        if (tid == 0) {
+            *s_lds = s;
+            if (s_out) *s_out = s;
+        }
+        int part = 0;
+        auto emit = [&](int r, const float4 (&v)[4]) {
+            uint4 b = make_uint4(0u, 0u, 0u, 0u);
+            if (mx != 0) {
+                const float lo[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
+                const float hi[8] = {v[2].x, v[2].y, v[2].z, v[2].w, v[3].x, v[3].y, v[3].z, v[3].w};
+                const uint2 cl = qcode8_f32(lo, s, inv), ch = qcode8_f32(hi, s, inv);
+                b = make_uint4(cl.x, cl.y, ch.x, ch.y);
+            }
+            if (q_out) *reinterpret_cast<uint4 *>(q_out + 16 * r) = b;
+            *reinterpret_cast<uint4 *>(qs + (r >> 2) * kLdsChunkDw + 4 * (r & 3)) = prep16<DOT8>(b);
+            int sm = dot4(b.x, 0x01010101u, 0);
+            sm = dot4(b.y, 0x01010101u, sm);
+            sm = dot4(b.z, 0x01010101u, sm);
+            part += dot4(b.w, 0x01010101u, sm);
+        };
+        if (tid < pieces) emit(tid, pre.v);
+        if (r1 < pieces) emit(r1, v1);
+        for (int r = tid + 2 * kThreads; r < pieces; r += kThreads) {
+            const float4 v[4] = {xv[4 * r], xv[4 * r + 1], xv[4 * r + 2], xv[4 * r + 3]};
+            emit(r, v);
+        }
+        if (part != 0) atomicAdd(&sq[0], part);
+    }
+};
+
 // s_x is not restrict-qualified: in the fused kernels it is the LDS word the stager
 // writes through its own pointer, and its reads must stay after the staging.
 // GRP: the weights have group-wise scales (out.w_group = G, a multiple of 64 below K):
 // each chunk's integer partial, less its sum of q (sqc), is scaled by its group's
 // s_w[row][k / G] and summed in float64 (kslices == 1 only).
-template <int MT, int RG, bool DOT8, bool NT, int NW, class Stage, bool GRP = false>
+// PAIR: the gate (packed, s_w) and up (packed2, s_w2) projections of a SwiGLU
+// feed-forward part (page chenxutan.com sec. 3.1) against the same row of q
+// (kslices == 1, MT == 1): the first NW / 2 waves take rows [row_base, row_base +
+// 4 NW RG) of gate, the others the same rows of up; the epilogue meets the two fp32
+// outputs of each row in LDS (ypair, 8 NW RG floats) and writes
+// a = fp32(silu(y_gate) y_up) (device_common.h, swiglu_value) to out.y.
+template <int MT, int RG, bool DOT8, bool NT, int NW, class Stage, bool GRP = false, bool PAIR = false>
 __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s_x,
                                               const uint8_t *__restrict__ packed,
                                               const float *__restrict__ s_w, int M, int N, int K,
                                               const OutSpec &out, int32_t *__restrict__ acc_out,
                                               int row_base, int m0, int kslices, int seg_chunks,
-                                              uint32_t *qs, int *sq, int *red, const int *sqc = nullptr) {
+                                              uint32_t *qs, int *sq, int *red, const int *sqc = nullptr,
+                                              const uint8_t *__restrict__ packed2 = nullptr,
+                                              const float *__restrict__ s_w2 = nullptr, float *ypair = nullptr) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l8 = lane & 7, rs = lane >> 3;
@@ -330,9 +413,15 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s
     const int KB = K >> 2;
     const int mcount = min(MT, M - m0);
 
-    // wave -> (row set, K slice of every segment)
-    const int rowset = wave / kslices, slice = wave - rowset * kslices;
+    // wave -> (row set, K slice of every segment); PAIR: wave -> (matrix, row set)
+    const int half = PAIR && wave >= NW / 2 ? 1 : 0;
+    const int rowset = PAIR ? wave - half * (NW / 2) : wave / kslices;
+    const int slice = PAIR ? 0 : wave - rowset * kslices;
     const int row0 = row_base + rowset * 8 * RG;
+    if (PAIR && half) {
+        packed = packed2;
+        s_w = s_w2;
+    }
 
     int hi[RG][MT];
     uint32_t lo[RG][MT];
@@ -505,6 +594,19 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s
     }
 
     const float sw = *s_w;
+    if (PAIR) {
+        constexpr int kHalfRows = (NW / 2) * 8 * RG;
+        const double cm = rescale_factor(s_x[m0], sw);
+        if (l8 == 0) {
+            #pragma unroll
+            for (int g = 0; g < RG; ++g)
+                ypair[half * kHalfRows + rowset * 8 * RG + 8 * g + rs] = rescale(acc[g][0] - sq[0], cm);
+        }
+        __syncthreads();
+        const int r = row_base + tid;
+        if (tid < kHalfRows && r < N) store_y(out, (size_t)m0 * N + r, (double)swiglu_value(ypair[tid], ypair[kHalfRows + tid]));
+        return;
+    }
     if (kslices == 1) {
         #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -620,36 +722,53 @@ __global__ __launch_bounds__(256) void gemv_grouped_kernel(const uint8_t *__rest
 // row block 0 also writes q and s_x out when the descriptor asks for them.
 constexpr int kFusedNW = BITNET_FUSED_NW;
 
-// NORM: the plan has problems with an RMSNorm (each problem then takes the stager
-// its descriptor asks for); plans without one use the kernel without that path,
-// which needs fewer registers.
-template <bool NORM>
-__global__ __launch_bounds__(64 * kFusedNW) void gemv_fused_grouped_kernel(const uint8_t *__restrict__ plan) {
+// PRO: the mask of paths the plan's problems use (kFusedProNorm: an RMSNorm;
+// kFusedProSwiglu: fp32 input rows and gate / up pairs with the SwiGLU epilogue);
+// each problem takes the stager and epilogue its descriptor asks for, and a kernel
+// holds only the paths of its mask (fewer registers without them).  At least 4
+// waves per SIMD: the kernels with the extra paths would otherwise settle just
+// above 128 registers, one wave fewer.  (The output spec is built in each call, not
+// kept in a named local, which costs registers here.)
+template <int PRO>
+__global__ __launch_bounds__(64 * kFusedNW) __attribute__((amdgpu_waves_per_eu(4)))
+void gemv_fused_grouped_kernel(const uint8_t *__restrict__ plan) {
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
     __shared__ int sq[1];
     __shared__ int red[kFusedNW * 8 * kGroupedRG];
     __shared__ uint32_t qred[kFusedNW];
     __shared__ double dred[2 * kFusedNW];
     __shared__ float s_lds;
+    __shared__ float ypair[(PRO & kFusedProSwiglu) ? kFusedNW * 8 * kGroupedRG : 1];
     const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
     auto entry = [&](uint32_t b) {
         const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[b];
         const FusedDescDev d = reinterpret_cast<const FusedDescDev *>(plan + h->desc_offset)[e.desc];
         const int rows = kFusedNW * 8 * kGroupedRG;
         const bool first = e.local == 0;
-        if (NORM && d.gain) {
-            const StageRmsQuantize<BITNET_GROUPED_DOT8 != 0, kFusedNW> stage{
-                d.x, d.gain, d.eps, first ? d.q : nullptr, first ? d.s_x : nullptr, &s_lds, dred};
-            gemv_lds_tile<1, kGroupedRG, BITNET_GROUPED_DOT8 != 0, BITNET_GEMV_NT != 0, kFusedNW>(
-                stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K, OutSpec{d.y, nullptr, 0}, d.acc, (int)e.local * rows, 0,
-                1, d.K >> 6, dyn, sq, red);
-        } else {
-            const StageQuantize<BITNET_GROUPED_DOT8 != 0, kFusedNW> stage{d.x, first ? d.q : nullptr,
-                                                                          first ? d.s_x : nullptr, &s_lds, qred};
-            gemv_lds_tile<1, kGroupedRG, BITNET_GROUPED_DOT8 != 0, BITNET_GEMV_NT != 0, kFusedNW>(
-                stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K, OutSpec{d.y, nullptr, 0}, d.acc, (int)e.local * rows, 0,
-                1, d.K >> 6, dyn, sq, red);
-        }
+        constexpr bool D8 = BITNET_GROUPED_DOT8 != 0, NTL = BITNET_GEMV_NT != 0;
+        // a gate / up pair covers half the rows per workgroup (each row twice)
+        const bool pair = (PRO & kFusedProSwiglu) && d.packed2;
+        const int row_base = (int)e.local * (pair ? rows / 2 : rows);
+        // the tile for a stager: a gate / up pair (SwiGLU epilogue) or one matrix
+        auto tile = [&](const auto &stage, bool as_pair) {
+            using S = std::decay_t<decltype(stage)>;
+            if ((PRO & kFusedProSwiglu) && as_pair)
+                gemv_lds_tile<1, kGroupedRG, D8, NTL, kFusedNW, S, false, true>(
+                    stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K, OutSpec{d.y, nullptr, 0}, nullptr, row_base, 0, 1,
+                    d.K >> 6, dyn, sq, red, nullptr, d.packed2, d.s_w2, ypair);
+            else
+                gemv_lds_tile<1, kGroupedRG, D8, NTL, kFusedNW>(stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K,
+                                                                 OutSpec{d.y, nullptr, 0}, d.acc, row_base, 0, 1,
+                                                                 d.K >> 6, dyn, sq, red);
+        };
+        int8_t *q_out = first ? d.q : nullptr;
+        float *s_out = first ? d.s_x : nullptr;
+        if ((PRO & kFusedProNorm) && d.gain)
+            tile(StageRmsQuantize<D8, kFusedNW>{d.x, d.gain, d.eps, q_out, s_out, &s_lds, dred}, pair);
+        else if ((PRO & kFusedProSwiglu) && d.xf)
+            tile(StageQuantizeF32<D8, kFusedNW>{d.xf, q_out, s_out, &s_lds, qred}, false);
+        else
+            tile(StageQuantize<D8, kFusedNW>{d.x, q_out, s_out, &s_lds, qred}, pair);
     };
     if (BITNET_FUSED_PERSIST == 0) {
         // one entry per workgroup and no loop: with memory operations of a previous
@@ -668,14 +787,18 @@ __global__ __launch_bounds__(64 * kFusedNW) void gemv_fused_grouped_kernel(const
 // Longest K whose q fits one LDS segment of the grouped GEMV.
 int64_t gemv_fused_max_k() { return 64 * (int64_t)((kLdsBudget / (kLdsChunkDw * 4)) & ~7); }
 
-hipError_t launch_gemv_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, bool norm,
+hipError_t launch_gemv_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, uint32_t pro,
                                      hipStream_t st) {
     if (BITNET_FUSED_PERSIST > 0) blocks = std::min<uint32_t>(blocks, BITNET_FUSED_PERSIST);
     const uint8_t *p = reinterpret_cast<const uint8_t *>(plan_dev);
-    if (norm)
-        gemv_fused_grouped_kernel<true><<<dim3(blocks), dim3(64 * kFusedNW), lds_bytes, st>>>(p);
-    else
-        gemv_fused_grouped_kernel<false><<<dim3(blocks), dim3(64 * kFusedNW), lds_bytes, st>>>(p);
+    const dim3 grid(blocks), block(64 * kFusedNW);
+    switch (pro) {
+        case 0: gemv_fused_grouped_kernel<0><<<grid, block, lds_bytes, st>>>(p); break;
+        case kFusedProNorm: gemv_fused_grouped_kernel<kFusedProNorm><<<grid, block, lds_bytes, st>>>(p); break;
+        case kFusedProSwiglu: gemv_fused_grouped_kernel<kFusedProSwiglu><<<grid, block, lds_bytes, st>>>(p); break;
+        case kFusedProMask: gemv_fused_grouped_kernel<kFusedProMask><<<grid, block, lds_bytes, st>>>(p); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -34,8 +34,10 @@ constexpr uint32_t kPlanLinear = 1, kPlanQuant = 2, kPlanFused = 3;
 constexpr uint32_t kVariantGemv = 0, kVariantMfma = 1;
 // ... and the GEMV with the group-wise-scale path, for plans with such weights.
 constexpr uint32_t kVariantGemvGroups = 2;
-// Fused plan variants: no problem with an RMSNorm, or some.
-constexpr uint32_t kVariantFused = 0, kVariantFusedNorm = 1;
+// Fused plan variants: a mask of what its problems use beyond the plain path (an
+// RMSNorm; fp32 input rows or gate / up pairs, the two ends of SwiGLU); each mask
+// has its own kernel, so a plan without them takes the kernel without that code.
+constexpr uint32_t kFusedProNorm = 1, kFusedProSwiglu = 2, kFusedProMask = 3;
 
 struct PlanHeader {            // 64 bytes
     uint32_t magic, kind, count, total_blocks;
@@ -54,11 +56,14 @@ struct QuantDescDev {          // 32 bytes
     int32_t M, K;
 };
 
-struct FusedDescDev {          // 88 bytes: (RMSNorm +) quantization + linear of one token row
+struct FusedDescDev {          // 112 bytes: (RMSNorm +) quantization + linear of one token row
     const uint16_t *x; const uint8_t *packed; const float *s_w;
     float *y; int32_t *acc; int8_t *q; float *s_x;
     int32_t M, N, K, pad;
     const float *gain; float eps; int32_t pad2;
+    const float *xf;           // fp32 input row instead of x, or null
+    const uint8_t *packed2;    // up projection of a gate / up pair (SwiGLU epilogue), or null
+    const float *s_w2;
 };
 
 struct BlockEntry { uint32_t desc, local; };
@@ -67,6 +72,8 @@ struct BlockEntry { uint32_t desc, local; };
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int8_t *q, float *s_x,
                             hipStream_t st);
 hipError_t launch_quant_act_grouped(const void *plan_dev, uint32_t blocks, hipStream_t st);
+hipError_t launch_swiglu_quant(const float *g, const float *u, int64_t M, int64_t K, int8_t *q, float *s_x,
+                               hipStream_t st);
 hipError_t launch_rmsnorm_quant(const uint16_t *x, const float *g, float eps, int64_t M, int64_t K, int8_t *q,
                                 float *s_x, hipStream_t st);
 hipError_t launch_pack(const float *w, int64_t N, int64_t K, float eps, uint8_t *packed,
@@ -78,7 +85,7 @@ hipError_t launch_gemv(const int8_t *q, const float *s_x, const uint8_t *packed,
 hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, bool grp,
                                hipStream_t st);
 uint32_t gemv_grouped_lds_bytes(int64_t K, bool grp = false);
-hipError_t launch_gemv_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, bool norm,
+hipError_t launch_gemv_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, uint32_t pro,
                                      hipStream_t st);
 int64_t gemv_fused_max_k();
 uint32_t gemv_grouped_rows_per_block();

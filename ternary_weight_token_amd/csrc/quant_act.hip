@@ -93,6 +93,59 @@ __global__ __launch_bounds__(kQThreads) void rmsnorm_quant_kernel(const uint16_t
         qv[v] = mz > 0.0 ? rms_code8(xv[v], gv[2 * v], gv[2 * v + 1], c, mz) : make_uint2(0u, 0u);
 }
 
+// SwiGLU of the fp32 gate and up rows, then the quantization of the result
+// (device_common.h, swiglu_*): pass 1 forms a and takes max|a| (an integer max of
+// the magnitude bits, exact and order-free), pass 2 writes the codes.  The values a
+// of each thread's first kHold vectors of 8 stay in registers between the passes;
+// later vectors (K > 8 kQThreads kHold) are formed again.  K % 8 == 0; g, u and q
+// 16-byte aligned.
+__global__ __launch_bounds__(kQThreads) void swiglu_quant_kernel(const float *__restrict__ g,
+                                                                 const float *__restrict__ u, int K,
+                                                                 int8_t *__restrict__ q,
+                                                                 float *__restrict__ s_x) {
+    constexpr int kHold = 4;
+    __shared__ uint32_t red[kQThreads / 64];
+    const size_t m = blockIdx.x;
+    const int tid = threadIdx.x, nv = K >> 3;
+    const float4 *gv = reinterpret_cast<const float4 *>(g + m * K);
+    const float4 *uv = reinterpret_cast<const float4 *>(u + m * K);
+    float a[kHold][8];
+    uint32_t mx = 0;
+    #pragma unroll
+    for (int j = 0; j < kHold; ++j) {
+        const int v = tid + kQThreads * j;
+        if (v < nv) mx = max(mx, swiglu8(gv[2 * v], gv[2 * v + 1], uv[2 * v], uv[2 * v + 1], a[j]));
+    }
+    for (int v = tid + kQThreads * kHold; v < nv; v += kQThreads) {
+        float t[8];
+        mx = max(mx, swiglu8(gv[2 * v], gv[2 * v + 1], uv[2 * v], uv[2 * v + 1], t));
+    }
+    mx = wave_max_u32(mx);
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    mx = max(max(red[0], red[1]), max(red[2], red[3]));
+    const float s = __uint_as_float(mx);
+    const float inv = 1.0f / s;
+    if (tid == 0) s_x[m] = s;
+    uint2 *qv = reinterpret_cast<uint2 *>(q + m * K);
+    #pragma unroll
+    for (int j = 0; j < kHold; ++j) {
+        const int v = tid + kQThreads * j;
+        if (v < nv) qv[v] = mx != 0 ? qcode8_f32(a[j], s, inv) : make_uint2(0u, 0u);
+    }
+    for (int v = tid + kQThreads * kHold; v < nv; v += kQThreads) {
+        float t[8];
+        swiglu8(gv[2 * v], gv[2 * v + 1], uv[2 * v], uv[2 * v + 1], t);
+        qv[v] = mx != 0 ? qcode8_f32(t, s, inv) : make_uint2(0u, 0u);
+    }
+}
+
+hipError_t launch_swiglu_quant(const float *g, const float *u, int64_t M, int64_t K, int8_t *q, float *s_x,
+                               hipStream_t st) {
+    swiglu_quant_kernel<<<dim3((unsigned)M), dim3(kQThreads), 0, st>>>(g, u, (int)K, q, s_x);
+    return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm_quant(const uint16_t *x, const float *g, float eps, int64_t M, int64_t K, int8_t *q,
                                 float *s_x, hipStream_t st) {
     rmsnorm_quant_kernel<<<dim3((unsigned)M), dim3(kQThreads), 0, st>>>(x, g, eps, (int)K, q, s_x);

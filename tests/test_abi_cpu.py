@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -232,6 +232,54 @@ def test_fused_plan_norm_checks_and_variant(L):
                     (F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, a16, n(-1.0)), ARG)):
         one = (F * 1)(d)
         assert L.bitnet_grouped_plan_fused(one, 1, buf, nb) == want
+
+
+def test_swiglu_quant_rejects_bad_arguments(L):
+    p = ctypes.c_void_p(256)  # never dereferenced: every call below fails its checks
+    z = None
+    assert L.bitnet_swiglu_quant_act(p, z, 1, 64, p, p, z) == NULL
+    assert L.bitnet_swiglu_quant_act(p, p, 1, 60, p, p, z) == SHAPE     # K % 8
+    assert L.bitnet_swiglu_quant_act(ctypes.c_void_p(264), p, 1, 64, p, p, z) == ALIGN
+    assert L.bitnet_swiglu_quant_act(p, ctypes.c_void_p(260), 1, 64, p, p, z) == ALIGN
+    assert L.bitnet_swiglu_quant_act(p, p, 1, 64, ctypes.c_void_p(264), p, z) == ALIGN
+    assert L.bitnet_swiglu_quant_act(p, p, -1, 64, p, p, z) == SHAPE
+    assert L.bitnet_swiglu_quant_act(z, z, 0, 64, z, z, z) == OK
+
+
+def test_fused_plan_swiglu_checks_and_variant(L):
+    F = tw._FusedDesc
+    a16 = 4096
+    n = ctypes.c_float
+
+    def plan(*descs):
+        arr = (F * len(descs))(*descs)
+        nb = L.bitnet_grouped_plan_fused_bytes(len(descs), arr)
+        buf = ctypes.create_string_buffer(nb)
+        assert L.bitnet_grouped_plan_fused(arr, len(descs), buf, nb) == OK
+        return (ctypes.c_uint32 * 8).from_buffer_copy(buf.raw[:32])
+
+    plain = F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, 0, n(0.0), 0, 0, 0)
+    norm = F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, a16, n(1e-6), 0, 0, 0)
+    f32 = F(0, a16, a16, a16, 0, 0, 0, 1, 2560, 6912, 0, n(0.0), a16, 0, 0)
+    pair = F(a16, a16, a16, a16, 0, 0, 0, 1, 6912, 2560, a16, n(1e-6), 0, a16, a16)
+    assert plan(plain)[7] == 0 and plan(norm)[7] == 1 and plan(f32)[7] == 2 and plan(pair)[7] == 3
+    assert plan(plain, f32)[7] == 2 and plan(norm, plain, f32)[7] == 3
+    # blocks: R rows per block, R / 2 for a pair (each row of both matrices)
+    R = plan(f32)[5]
+    assert plan(f32)[3] == -(-2560 // R) and plan(pair)[3] == -(-6912 // (R // 2))
+    assert plan(pair, f32)[3] == -(-6912 // (R // 2)) - (-2560 // R)
+    buf = ctypes.create_string_buffer(4096)
+    for d, want in ((F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 6912, 0, n(0.0), a16, 0, 0), ARG),   # x and x_f32
+                    (F(0, a16, a16, a16, 0, 0, 0, 1, 300, 6912, a16, n(0.0), a16, 0, 0), ARG),   # x_f32 and a norm
+                    (F(0, a16, a16, a16, 0, 0, 0, 1, 300, 6912, 0, n(0.0), a16 + 4, 0, 0), ALIGN),
+                    (F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, 0, n(0.0), 0, a16, 0), NULL),  # s_w_up missing
+                    (F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, 0, n(0.0), 0, 0, a16), NULL),  # packed_up missing
+                    (F(a16, a16, a16, a16, a16, 0, 0, 1, 300, 2560, 0, n(0.0), 0, a16, a16), ARG),  # pair with acc
+                    (F(0, a16, a16, a16, 0, 0, 0, 1, 300, 2560, 0, n(0.0), a16, a16, a16), ARG),  # pair on fp32 x
+                    (F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, 0, n(0.0), 0, a16 + 8, a16), ALIGN),
+                    (F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, 0, n(0.0), 0, a16, a16 + 2), ALIGN)):
+        one = (F * 1)(d)
+        assert L.bitnet_grouped_plan_fused(one, 1, buf, 4096) == want
 
 
 def test_linear_plan_weight_groups(L):

@@ -424,6 +424,166 @@ def test_fused_rmsnorm_linear_grouped(with_outputs):
                 assert_scale(pr[6].cpu().numpy(), sx_ref)
 
 
+# ----------------------------------------------------------------- SwiGLU + quantization
+
+def _gate_up(key, M, K, outliers=False):
+    """Gate and up outputs: normal rows (gate wider, so that silu's bend and both
+    tails are hit), a few large values when asked."""
+    g = (3.0 * synth.normal(synth.stream_key(key, 1), M * K).float().numpy()).astype(np.float32).reshape(M, K)
+    u = synth.normal(synth.stream_key(key, 2), M * K).float().numpy().astype(np.float32).reshape(M, K)
+    if outliers:
+        g[:, ::997] *= 8.0
+        u[:, 5::1009] *= 20.0
+    return g, u
+
+
+@pytest.mark.parametrize("M,K,outliers", [(1, 6912, False), (4, 6912, True), (3, 64, False), (2, 8, False),
+                                          (5, 27648, True), (1, 52224, False), (33, 2560, False)])
+def test_swiglu_quant_parity(M, K, outliers):
+    key = synth.stream_key(340, M, K)
+    g, u = _gate_up(key, M, K, outliers)
+    if M > 2:
+        u[1] = 0.0          # a row of zeros after SwiGLU
+    _, q_ref, s_ref = oracle.swiglu_quant(g, u)
+    q, s = tw.swiglu_quant(torch.from_numpy(g).to(DEV), torch.from_numpy(u).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+def _near_tie_row(K, key):
+    """fp32 row whose values sit within an fp32 rounding of code boundaries for the
+    row scale 1 (x = fl((2j + 1) / 254)), mixed with normal values below it."""
+    x = (0.3 * synth.normal(key, K).float().numpy()).astype(np.float32)
+    x = np.clip(x, -0.99, 0.99)
+    j = np.arange(K) % 127
+    x[::3] = (((2 * j + 1) / 254.0) * np.where(j % 2, 1.0, -1.0)).astype(np.float32)[::3]
+    x[K // 2] = 1.0
+    return x.reshape(1, K)
+
+
+def _fused_case(kind, N, K, key):
+    """Inputs and the oracle's expected outputs of one fused problem of a kind:
+    'plain' / 'norm' (bf16 row), 'f32' / 'f32tie' / 'f32zero' (fp32 row), 'pair' /
+    'pairnorm' (gate / up pair)."""
+    pk = lambda k: synth.random_bytes(synth.stream_key(key, k), N * K // 4).numpy().reshape(N, K // 4)
+    s_w = np.float32(0.0037 + 0.001 * (key % 7))
+    gain = None
+    if kind.startswith("f32"):
+        if kind == "f32tie":
+            x = _near_tie_row(K, synth.stream_key(key, 5))
+        elif kind == "f32zero":
+            x = np.zeros((1, K), np.float32)
+        else:
+            x = (synth.normal(synth.stream_key(key, 5), K).float().numpy() * 0.7).astype(np.float32).reshape(1, K)
+            x[0, ::501] *= 30.0
+        q_ref, sx_ref = oracle.quant_act_f32(x)
+        xin = torch.from_numpy(x).to(DEV)
+    else:
+        x = synth.activations(synth.stream_key(key, 6), 1, K, outlier_frac=0.002)
+        if kind in ("norm", "pairnorm"):
+            gn = _gain(key, K)
+            q_ref, sx_ref = oracle.rmsnorm_quant(bits_np(x), gn, 1e-6)
+            gain = torch.from_numpy(gn).to(DEV)
+        else:
+            q_ref, sx_ref = oracle.quant_act(bits_np(x))
+        xin = x.to(DEV)
+    packed = pk(1)
+    if kind.startswith("pair"):
+        packed_up = pk(2)
+        s_up = np.float32(s_w * 1.7)
+        _, y_g = oracle.linear(q_ref, sx_ref, packed, s_w)
+        _, y_u = oracle.linear(q_ref, sx_ref, packed_up, s_up)
+        a_ref = oracle.swiglu_quant(y_g, y_u)[0]
+        exp = dict(q=q_ref, s=sx_ref, y=a_ref, acc=None)
+        pw = (torch.from_numpy(packed).to(DEV), torch.from_numpy(packed_up).to(DEV))
+        sw = (torch.tensor([s_w], device=DEV), torch.tensor([s_up], device=DEV))
+    else:
+        acc_ref, y_ref = oracle.linear(q_ref, sx_ref, packed, s_w)
+        exp = dict(q=q_ref, s=sx_ref, y=y_ref, acc=acc_ref)
+        pw, sw = torch.from_numpy(packed).to(DEV), torch.tensor([s_w], device=DEV)
+    return xin, pw, sw, gain, exp
+
+
+def _check_fused(kind, exp, y, acc, q, sx):
+    if kind.startswith("pair"):
+        # y_gate and y_up match the oracle's bit for bit (one rounding of the same
+        # float64 product), so does a = fp32(silu(y_gate) y_up)
+        assert np.array_equal(y, exp["y"]), kind
+    else:
+        assert np.array_equal(acc, exp["acc"]), kind
+        tol = 2.0 ** -22 if kind == "norm" else 2.0 ** -23
+        yd = np.abs(y.astype(np.float64) - exp["y"].astype(np.float64))
+        assert np.all(yd <= tol * np.abs(exp["y"].astype(np.float64))), kind
+    if q is not None:
+        assert np.array_equal(q, exp["q"]), kind
+        if kind in ("norm", "pairnorm"):
+            assert_scale(sx, exp["s"])
+        else:
+            assert np.array_equal(sx, exp["s"]), kind
+
+
+FUSED_SWIGLU_SHAPES = [("pairnorm", 6912, 2560), ("pair", 300, 2560), ("pair", 65, 64), ("pairnorm", 1, 12288),
+                       ("f32", 2560, 6912), ("f32tie", 97, 12288), ("f32", 129, 52224), ("f32", 64, 64),
+                       ("f32zero", 33, 6912), ("norm", 300, 2560), ("plain", 200, 2560)]
+
+
+@pytest.mark.parametrize("with_outputs", [True, False])
+def test_fused_swiglu_ends(with_outputs):
+    """One fused launch with gate / up pairs (SwiGLU epilogue) and fp32 input rows
+    (the down projections) next to plain and RMSNorm rows; then the same problems
+    without the RMSNorm ones (the kernel without that path)."""
+    probs, cases = [], []
+    for i, (kind, N, K) in enumerate(FUSED_SWIGLU_SHAPES):
+        xin, pw, sw, gain, exp = _fused_case(kind, N, K, synth.stream_key(342, i))
+        y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+        acc = None if kind.startswith("pair") else torch.empty((1, N), dtype=torch.int32, device=DEV)
+        q = torch.full((1, K), 99, dtype=torch.int8, device=DEV) if with_outputs else None
+        sx = torch.full((1,), -1.0, dtype=torch.float32, device=DEV) if with_outputs else None
+        probs.append((xin, pw, sw, y, acc, q, sx, gain, 1e-6))
+        cases.append((kind, exp))
+    for sel in (range(len(probs)), [i for i, c in enumerate(cases) if "norm" not in c[0]]):
+        sub = [probs[i] for i in sel]
+        plan = tw.bitnet_grouped_plan_fused(sub)
+        for rep in range(2):
+            for pr in sub:
+                pr[3].fill_(float("nan"))
+                if pr[4] is not None:
+                    pr[4].fill_(-1)
+            plan.launch()
+            torch.cuda.synchronize()
+            for i in sel:
+                pr = probs[i]
+                kind, exp = cases[i]
+                _check_fused(kind, exp, pr[3].cpu().numpy(), None if pr[4] is None else pr[4].cpu().numpy(),
+                             None if pr[5] is None else pr[5].cpu().numpy(),
+                             None if pr[6] is None else pr[6].cpu().numpy())
+
+
+def test_fused_pair_matches_swiglu_then_linear():
+    """The pair's output fed back as an fp32 row gives the codes that
+    bitnet_swiglu_quant_act gives from the two projections' outputs."""
+    N, K, Nd = 6912, 2560, 2560
+    key = synth.stream_key(343)
+    x = synth.activations(key, 1, K).to(DEV)
+    pg = torch.from_numpy(synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)).to(DEV)
+    pu = torch.from_numpy(synth.random_bytes(synth.stream_key(key, 2), N * K // 4).numpy().reshape(N, K // 4)).to(DEV)
+    sg, su = torch.tensor([0.011], device=DEV), torch.tensor([0.017], device=DEV)
+    a = torch.empty((1, N), dtype=torch.float32, device=DEV)
+    tw.bitnet_grouped_plan_fused([(x, (pg, pu), (sg, su), a, None, None, None)]).launch()
+    q, s = tw.quant_act(x)
+    yg = tw.linear(q, s, pg, sg)
+    yu = tw.linear(q, s, pu, su)
+    q2, s2 = tw.swiglu_quant(yg, yu)
+    pd = torch.from_numpy(synth.random_bytes(synth.stream_key(key, 3), Nd * N // 4).numpy().reshape(Nd, N // 4)).to(DEV)
+    yd = torch.empty((1, Nd), dtype=torch.float32, device=DEV)
+    qa = torch.empty((1, N), dtype=torch.int8, device=DEV)
+    sa = torch.empty((1,), dtype=torch.float32, device=DEV)
+    tw.bitnet_grouped_plan_fused([(a, pd, sg, yd, None, qa, sa)]).launch()
+    torch.cuda.synchronize()
+    assert torch.equal(qa, q2) and torch.equal(sa, s2)
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 200, 53312), (2, 70, 26176), (3, 200, 16704), (8, 200, 16704),
                                    (13, 130, 8192), (16, 65, 28672)])
 def test_gemv_parity_k_segments(M, N, K):
