@@ -52,6 +52,10 @@ def lib():
         L.oracle_pack_grouped.argtypes = [P, I64, I64, I64, ctypes.c_float, P, P]
         L.oracle_swiglu_quant.argtypes = [P, P, I64, I64, P, P, P]
         L.oracle_quant_act_f32.argtypes = [P, I64, I64, P, P]
+        L.oracle_pack_binary.argtypes = [P, I64, I64, P]
+        L.oracle_linear_binary.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, P, P]
+        L.oracle_pack_bitplanes.argtypes = [P, I64, I64, P]
+        L.oracle_linear_bitplanes.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, P, P]
         L.oracle_linear_grouped.argtypes = [P, P, P, P, I64, P, I64, I64, I64, P, P]
         L.oracle_set_threads.argtypes = [ctypes.c_int]
         L.oracle_get_threads.restype = ctypes.c_int
@@ -151,6 +155,53 @@ def rmsnorm_quant(x_bits: np.ndarray, gain: np.ndarray, eps: float) -> tuple[np.
     s = np.empty(M, dtype=np.float32)
     lib().oracle_rmsnorm_quant(_p(x_bits), _p(gain), ctypes.c_float(eps), M, K, _p(q), _p(s))
     return q, s
+
+
+def pack_binary(w: np.ndarray) -> tuple[np.ndarray, np.float32]:
+    """b1.0 binary weights: fp32 [N][K] -> (bits uint8 [N][K/8], s_w) with the
+    absmean scale of the ternary path."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    assert K % 8 == 0
+    bits = np.empty((N, K // 8), dtype=np.uint8)
+    lib().oracle_pack_binary(_p(w), N, K, _p(bits))
+    return bits, weight_scale(w)[0]
+
+
+def linear_binary(q, s_x, bits, s_w, K: int | None = None):
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s_x = np.ascontiguousarray(s_x, dtype=np.float32)
+    bits = np.ascontiguousarray(bits, dtype=np.uint8)
+    M, K = q.shape
+    N = bits.shape[0]
+    acc = np.empty((M, N), dtype=np.int32)
+    y = np.empty((M, N), dtype=np.float32)
+    lib().oracle_linear_binary(_p(q), _p(s_x), _p(bits), ctypes.c_float(float(np.float32(s_w))), M, N, K,
+                               _p(acc), _p(y))
+    return acc, y
+
+
+def pack_bitplanes(packed: np.ndarray, K: int) -> np.ndarray:
+    """2-bit codes [N][K/4] -> sign / mask bitplanes uint8 [N][K/32][8]."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    N = packed.shape[0]
+    assert K % 32 == 0 and packed.shape[1] == K // 4
+    planes = np.empty((N, K // 32, 8), dtype=np.uint8)
+    lib().oracle_pack_bitplanes(_p(packed), N, K, _p(planes))
+    return planes
+
+
+def linear_bitplanes(q, s_x, planes, s_w):
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s_x = np.ascontiguousarray(s_x, dtype=np.float32)
+    planes = np.ascontiguousarray(planes, dtype=np.uint8)
+    M, K = q.shape
+    N = planes.shape[0]
+    acc = np.empty((M, N), dtype=np.int32)
+    y = np.empty((M, N), dtype=np.float32)
+    lib().oracle_linear_bitplanes(_p(q), _p(s_x), _p(planes), ctypes.c_float(float(np.float32(s_w))), M, N, K,
+                                  _p(acc), _p(y))
+    return acc, y
 
 
 def quant_act_f32(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:

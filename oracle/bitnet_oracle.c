@@ -144,7 +144,7 @@ void oracle_pack_grouped(const float *w, int64_t N, int64_t K, int64_t G, float 
     }
 }
 
-/* Decode one weight from the packed layout (code - 1; code 3 -> +2). *//* Decode one weight from the packed layout (code - 1; code 3 -> +2). */
+/* Decode one weight from the packed layout (code - 1; code 3 -> +2). */
 static int weight_at(const uint8_t *packed, int64_t KB, int64_t n, int64_t k) {
     unsigned byte = packed[n * KB + k / 4];
     unsigned code = (byte >> (2 * (k % 4))) & 3u;
@@ -356,6 +356,95 @@ void oracle_linear(const int8_t *q, const float *s_x, const uint8_t *packed,
                    float s_w, int64_t M, int64_t N, int64_t K,
                    int32_t *acc, float *y) {
     oracle_linear_bias(q, s_x, packed, s_w, NULL, M, N, K, acc, y);
+}
+
+/* --- other weight encodings: b1.0 binary weights, sign / mask bitplanes --- */
+
+/* Binary weights ([P1] 1 and its b1.0 paragraph: the first BitNet's weights are
+ * {-1, +1}, no zero).  The pages give no binarization rule; here t = +1 for
+ * w >= 0 (either zero) and -1 for w < 0, with the same absmean scale s_w as the
+ * ternary weights (oracle_weight_scale; mean |w| is also the scale that best fits
+ * sign(W) in the least-squares sense).  Layout: row n holds K / 8 bytes, weight k
+ * in byte k / 8, bit k % 8 (LSB first), set for +1.  K % 8 == 0. */
+void oracle_pack_binary(const float *w, int64_t N, int64_t K, uint8_t *bits) {
+    const int64_t KB = K / 8;
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < KB; ++j) {
+            unsigned byte = 0;
+            for (int i = 0; i < 8; ++i)
+                if (w[n * K + 8 * j + i] >= 0.0f) byte |= 1u << i;
+            bits[n * KB + j] = (uint8_t)byte;
+        }
+    }
+}
+
+static int binary_at(const uint8_t *bits, int64_t K, int64_t n, int64_t k) {
+    return ((bits[n * (K / 8) + k / 8] >> (k % 8)) & 1u) ? 1 : -1;
+}
+
+/* acc = sum_k q t (exact), y = fp32(acc s_x s_w / 127) in float64, as oracle_linear. */
+void oracle_linear_binary(const int8_t *q, const float *s_x, const uint8_t *bits, float s_w, int64_t M,
+                          int64_t N, int64_t K, int32_t *acc, float *y) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            int64_t a = 0;
+            for (int64_t k = 0; k < K; ++k) a += (int64_t)q[m * K + k] * binary_at(bits, K, n, k);
+            if (acc) acc[m * N + n] = (int32_t)a;
+            y[m * N + n] = (float)((((double)a * (double)s_x[m]) * (double)s_w) / 127.0);
+        }
+    }
+}
+
+/* Sign / mask bitplanes ([P3], bitnet_linear with weight_sign and weight_mask: a
+ * weight is a nonzero mask bit and a sign, the product adds x where the mask is
+ * set, negated where the sign is negative).  The same ternary weights as the
+ * 2-bit codes, in another layout: row n is cut into chunks of 32 weights; chunk c
+ * holds two little-endian 32-bit words, the mask (bit i set when weight 32 c + i
+ * is nonzero) then the sign (bit i set when it is -1; clear for zero weights).
+ * K % 32 == 0.  Converted from the 2-bit codes: code 0 -> -1, 1 -> 0, 2 -> +1;
+ * a code 3 (which the packer never writes) becomes +1, the nearest value the
+ * planes can hold. */
+void oracle_pack_bitplanes(const uint8_t *packed, int64_t N, int64_t K, uint8_t *planes) {
+    const int64_t KB = K / 4, C = K / 32;
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t c = 0; c < C; ++c) {
+            uint32_t mask = 0, sign = 0;
+            for (int i = 0; i < 32; ++i) {
+                const int t = weight_at(packed, KB, n, 32 * c + i);
+                if (t != 0) mask |= 1u << i;
+                if (t < 0) sign |= 1u << i;
+            }
+            uint8_t *out = planes + (n * C + c) * 8;
+            for (int b = 0; b < 4; ++b) {
+                out[b] = (uint8_t)(mask >> (8 * b));
+                out[4 + b] = (uint8_t)(sign >> (8 * b));
+            }
+        }
+    }
+}
+
+static int bitplane_at(const uint8_t *planes, int64_t K, int64_t n, int64_t k) {
+    const uint8_t *ch = planes + (n * (K / 32) + k / 32) * 8;
+    const int i = (int)(k % 32);
+    const int m = (ch[i / 8] >> (i % 8)) & 1, sg = (ch[4 + i / 8] >> (i % 8)) & 1;
+    return m ? (sg ? -1 : 1) : 0;
+}
+
+/* acc = sum_k q t over the bitplane weights (exact); y as oracle_linear. */
+void oracle_linear_bitplanes(const int8_t *q, const float *s_x, const uint8_t *planes, float s_w, int64_t M,
+                             int64_t N, int64_t K, int32_t *acc, float *y) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            int64_t a = 0;
+            for (int64_t k = 0; k < K; ++k) a += (int64_t)q[m * K + k] * bitplane_at(planes, K, n, k);
+            if (acc) acc[m * N + n] = (int32_t)a;
+            y[m * N + n] = (float)((((double)a * (double)s_x[m]) * (double)s_w) / 127.0);
+        }
+    }
 }
 
 /* --- bf16 output ---------------------------------------------------------- */

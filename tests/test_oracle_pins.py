@@ -724,3 +724,88 @@ def test_swiglu_quant_codes_are_those_of_its_fp32_row():
     a, q, s = oracle.swiglu_quant(g, u)
     q2, s2 = oracle.quant_act_f32(a)
     assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+# ----------------------------------------------------------------- binary (b1.0) weights
+
+def test_pack_binary_hand_case():
+    """w = [0.5, -0.25, 0, -0, 1, -2, 3, -4]: +1 for the first, third, fourth (both
+    zeros), fifth and seventh -> bits 0, 2, 3, 4, 6 -> 0x5D; mean |w| = 10.75 / 8."""
+    w = np.array([[0.5, -0.25, 0.0, -0.0, 1.0, -2.0, 3.0, -4.0]], np.float32)
+    bits, s_w = oracle.pack_binary(w)
+    assert bits.tolist() == [[0x5D]] and s_w == np.float32(10.75 / 8)
+
+
+def _decode_binary(bits, K):
+    b = np.unpackbits(bits.reshape(-1, 1), axis=1, bitorder="little").reshape(bits.shape[0], K)
+    return (2 * b.astype(np.int64) - 1)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 8), (2, 3, 16), (3, 5, 256)])
+def test_linear_binary_brute_force(M, N, K):
+    key = synth.stream_key(31, M, N, K)
+    q = synth.random_bytes(key, M * K).numpy().view(np.int8).reshape(M, K).copy()
+    q[q == -128] = -127
+    bits = synth.random_bytes(synth.stream_key(key, 1), N * K // 8).numpy().reshape(N, K // 8)
+    s = np.linspace(0.5, 2.0, M).astype(np.float32)
+    acc, y = oracle.linear_binary(q, s, bits, np.float32(0.03))
+    t = _decode_binary(bits, K)
+    for m in range(M):
+        for n in range(N):
+            a = sum(int(q[m, k]) * int(t[n, k]) for k in range(K))
+            assert acc[m, n] == a
+            assert y[m, n] == np.float32(round_fraction_to_f32(
+                Fraction(a) * Fraction(float(s[m])) * Fraction(float(np.float32(0.03))) / 127))
+
+
+def test_binary_of_weights_is_their_sign():
+    """Packing then decoding gives sign(w) with zeros as +1; the linear of binary
+    weights equals the ternary linear of the same +-1 values (codes 0 / 2)."""
+    key = synth.stream_key(32)
+    N, K = 6, 256
+    w = synth.latent_weights(key, N, K, 0.02).numpy()
+    w[0, :5] = 0.0
+    bits, s_w = oracle.pack_binary(w)
+    t = _decode_binary(bits, K)
+    assert np.array_equal(t, np.where(w >= 0, 1, -1))
+    codes = (t + 1).astype(np.uint8).reshape(N, K // 4, 4)
+    packed = (codes[..., 0] | codes[..., 1] << 2 | codes[..., 2] << 4 | codes[..., 3] << 6).astype(np.uint8)
+    x = synth.activations(synth.stream_key(key, 1), 3, K)
+    q, s = oracle.quant_act(synth.bf16_bits(x).numpy().view(np.uint16))
+    acc_b, y_b = oracle.linear_binary(q, s, bits, s_w)
+    acc_t, y_t = oracle.linear(q, s, packed, s_w)
+    assert np.array_equal(acc_b, acc_t) and np.array_equal(y_b, y_t)
+
+
+# ----------------------------------------------------------------- sign / mask bitplanes
+
+def test_bitplanes_hand_case():
+    """Byte 0xA4 holds t = [-1, 0, +1, +1] (codes 0, 1, 2, 2); the rest of the 32
+    weights are zero (byte 0x55): mask word 0b1101 = 0x0D, sign word 0b0001."""
+    packed = np.array([[0xA4] + [0x55] * 7], np.uint8)
+    planes = oracle.pack_bitplanes(packed, 32)
+    assert planes.tolist() == [[[0x0D, 0, 0, 0, 0x01, 0, 0, 0]]]
+
+
+def test_bitplanes_decode_and_linear_match_codes():
+    key = synth.stream_key(33)
+    N, K = 7, 640
+    w = synth.latent_weights(key, N, K, 0.02).numpy()
+    packed, s_w = oracle.pack(w)
+    planes = oracle.pack_bitplanes(packed, K)
+    # independent decode of the planes (numpy bit order) against the codes
+    pb = np.unpackbits(planes.reshape(N, K // 32, 2, 4), axis=3, bitorder="little").reshape(N, K // 32, 2, 32)
+    t = (pb[:, :, 0, :].astype(np.int64) * (1 - 2 * pb[:, :, 1, :].astype(np.int64))).reshape(N, K)
+    assert np.array_equal(t, decode_unpackbits(packed, K))
+    assert not np.any(pb[:, :, 1, :] & (1 - pb[:, :, 0, :]))      # no sign without the mask
+    x = synth.activations(synth.stream_key(key, 1), 4, K)
+    q, s = oracle.quant_act(synth.bf16_bits(x).numpy().view(np.uint16))
+    acc_p, y_p = oracle.linear_bitplanes(q, s, planes, s_w)
+    acc_t, y_t = oracle.linear(q, s, packed, s_w)
+    assert np.array_equal(acc_p, acc_t) and np.array_equal(y_p, y_t)
+
+
+def test_bitplanes_code3_becomes_plus_one():
+    packed = np.array([[0xFF] * 8], np.uint8)                 # every code 3
+    planes = oracle.pack_bitplanes(packed, 32)
+    assert planes.tolist() == [[[0xFF, 0xFF, 0xFF, 0xFF, 0, 0, 0, 0]]]
