@@ -90,7 +90,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--legs", default="two_launch,rmsnorm,prefill,sweep,decode_m8,ffn100b,scales",
+    ap.add_argument("--legs", default="two_launch,rmsnorm,prefill,sweep,decode_m8,ffn100b,scales,encodings",
                     help="secondary legs to run (comma-separated subset of the default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -420,6 +420,64 @@ def main() -> int:
             us = graph_us(torch, lambda: tw.bitnet_linear(q1, s1, shard, fsw[0], y1), reps=50)
             sec["colsplit8_gate_shard_M1"] = {"us": round(us, 2), "weight_GBs": round(shard.numel() / (us * 1e-6) / 1e9, 1)}
             del fpacked
+        if "encodings" in legs:
+            # the same 100B-scale FFN stream (M = 1, 24 GEMV launches in one graph) with
+            # the weights as 2-bit codes, as sign / mask bitplanes (same bytes, another
+            # contraction) and as b1.0 binary bits (half the bytes)
+            fmats = W.ffn_100b(8)
+            enc = {"two_bit_codes": [], "bitplanes": [], "binary": []}
+            for m in fmats:
+                w = W.weights(m, dev)
+                p_, s_ = tw.pack_weights(w, 1e-5)
+                enc["two_bit_codes"].append((p_, s_))
+                enc["bitplanes"].append((tw.pack_bitplanes(p_, m.K), s_))
+                enc["binary"].append(tw.pack_weights_binary(w))
+                del w
+            xq = [[tw.quant_act(x) for x in W.ffn_100b_activations(l, 1, dev)] for l in range(8)]
+            fys = [torch.empty((1, m.N), dtype=torch.float32, device=dev) for m in fmats]
+            nweights = sum(m.N * m.K for m in fmats)
+            res = {}
+            for v in enc:
+                def stream_fn(v=v):
+                    for i, m in enumerate(fmats):
+                        q_, s_ = xq[m.layer][m.slot]
+                        wb, sw_ = enc[v][i]
+                        if v == "two_bit_codes":
+                            tw.bitnet_linear(q_, s_, wb, sw_, fys[i])
+                        else:
+                            tw.bitnet_linear_bits(q_, s_, wb, tw.FMT_BINARY if v == "binary" else tw.FMT_BITPLANES,
+                                                  sw_, fys[i], None, 2)
+                us = graph_us(torch, stream_fn, reps=2, replays=5)
+                wbytes = sum(e[0].numel() for e in enc[v])
+                res[v] = {"us": round(us, 1), "weight_bytes": wbytes,
+                          "weight_GBs": round(wbytes / (us * 1e-6) / 1e9, 1),
+                          "gweights_per_s": round(nweights / (us * 1e-6) / 1e9, 1), "launches": len(fmats)}
+                log(f"ffn100b M=1 encoding {v}: {us:.1f} us, {res[v]['weight_GBs']} GB/s, "
+                    f"{res[v]['gweights_per_s']} G weights/s")
+            # one launch over the 8 gate matrices stacked (N = 229376, K = 8192): the
+            # per-launch ramp and drain no longer weigh on the comparison
+            big_w = {}
+            for v in enc:
+                big_w[v] = torch.cat([enc[v][i][0] for i, m in enumerate(fmats) if m.name == "gate"], 0)
+            q0, s0 = xq[0][0]
+            yb = torch.empty((1, big_w["binary"].shape[0]), dtype=torch.float32, device=dev)
+            one = {}
+            for v in enc:
+                sw_ = enc[v][0][1]
+                if v == "two_bit_codes":
+                    fn = lambda: tw.bitnet_linear(q0, s0, big_w[v], sw_, yb)
+                else:
+                    f_ = tw.FMT_BINARY if v == "binary" else tw.FMT_BITPLANES
+                    fn = lambda v=v, f_=f_, sw_=sw_: tw.bitnet_linear_bits(q0, s0, big_w[v], f_, sw_, yb, None, 2)
+                us = graph_us(torch, fn, reps=10, replays=5)
+                wbytes = big_w[v].numel()
+                one[v] = {"us": round(us, 1), "weight_GBs": round(wbytes / (us * 1e-6) / 1e9, 1),
+                          "gweights_per_s": round(229376 * 8192 / (us * 1e-6) / 1e9, 1)}
+                log(f"stacked gate 229376x8192 M=1 encoding {v}: {us:.1f} us, {one[v]['weight_GBs']} GB/s, "
+                    f"{one[v]['gweights_per_s']} G weights/s")
+            res["one_launch_229376x8192"] = one
+            sec["ffn100b_8layers_M1_encodings"] = res
+            del enc, big_w
         if "scales" in legs:
             # weight-scale granularity on the 100B-scale FFN stream at M = 1 (HBM-bound):
             # one scale per tensor, per output channel, per group of 128 weights; 24

@@ -307,6 +307,42 @@ BITNET_API int bitnet_linear_grouped(const void *plan_host, const void *plan_dev
 BITNET_API int bitnet_quant_act_grouped(const void *plan_host, const void *plan_dev, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Other weight encodings of the same product.
+ *
+ * BITNET_FMT_BINARY: b1.0 binary weights {-1, +1} (page chenxutan.com sec. 1: the
+ * first BitNet's weights are binary, no zero).  bits (device) uint8 [N][K/8]:
+ * weight k of row n is bit k % 8 of byte k / 8 (LSB first), set for +1.
+ * BITNET_FMT_BITPLANES: the ternary weights as sign / mask bitplanes (page
+ * sns.style "1-bit LLM ..." sec. on ternary weights: bitnet_linear over
+ * weight_sign and weight_mask).  planes (device) uint8 [N][K/32][8]: per 32
+ * weights a little-endian mask word (bit i set: weight 32 c + i nonzero) then a
+ * sign word (bit i set: -1; clear for zero weights).
+ * ------------------------------------------------------------------------- */
+#define BITNET_FMT_BINARY 1
+#define BITNET_FMT_BITPLANES 2
+
+/* Binary packing of w (device fp32 [N][K], 16-byte aligned, K % 32 == 0): t = +1
+ * for w >= 0 (either zero), -1 below, and s_w = mean|w| over the tensor exactly as
+ * bitnet_pack_weights forms it (float64 row sums in the workspace, same size rule).
+ * NaN weights give -1.  bits (device) [N][K/8], 4-byte aligned. */
+BITNET_API int bitnet_pack_weights_binary(const float *w, int64_t N, int64_t K, uint8_t *bits, float *s_w,
+                                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Sign / mask bitplanes of 2-bit packed weights (bitnet_pack_weights' layout),
+ * K % 32 == 0, packed 8-byte aligned, planes (device) [N][K/32][8] 8-byte aligned.
+ * Codes 0, 1, 2 become -1, 0, +1; a code 3 (never written by the packer) +1. */
+BITNET_API int bitnet_pack_bitplanes(const uint8_t *packed, int64_t N, int64_t K, uint8_t *planes, void *stream);
+
+/* acc[m][n] = sum_k q[m][k] t[n][k] (exact int32) and y = fp32(acc s_x[m] s_w / 127)
+ * (formed as in bitnet_linear) for weights in format fmt.  K % 32 == 0.  kernel: 0
+ * picks, 1 the general kernel (any M, any alignment), 2 the bit-serial GEMV (M == 1,
+ * K % 128 == 0 for binary or K % 64 == 0 for bitplanes, K at most 57344 / 51584,
+ * q and wbits 16-byte aligned; BITNET_ERR_ARG otherwise).  acc may be NULL. */
+BITNET_API int bitnet_linear_bits(const int8_t *q, const float *s_x, const uint8_t *wbits, int fmt,
+                                  const float *s_w, int64_t M, int64_t N, int64_t K, float *y, int32_t *acc,
+                                  int kernel, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Fused decode step: activation quantization and linear in one grouped launch
  * (pages: chenxutan.com sec. 2.2 absmax_quantize and sec. 3.1 BitLinear.forward,
  * whose forward quantizes the input on entry; sec. 5.3 item 4 on fusing the

@@ -65,6 +65,9 @@ def lib() -> ctypes.CDLL:
         L.bitnet_linear_select.argtypes = [P, P, P, P, I64, I64, I64, P, P, I, P]
         L.bitnet_linear_ex.argtypes = [P, P, P, P, I64, I64, I64, I64, P, P, I, P, I, P]
         L.bitnet_pack_weights_grouped.argtypes = [P, I64, I64, I64, ctypes.c_float, P, P, P]
+        L.bitnet_pack_weights_binary.argtypes = [P, I64, I64, P, P, P, ctypes.c_size_t, P]
+        L.bitnet_pack_bitplanes.argtypes = [P, I64, I64, P, P]
+        L.bitnet_linear_bits.argtypes = [P, P, P, I, P, I64, I64, I64, P, P, I, P]
         L.bitnet_grouped_plan_bytes.argtypes = [I, I, P]
         L.bitnet_grouped_plan_bytes.restype = ctypes.c_size_t
         L.bitnet_grouped_plan_linear.argtypes = [P, I, P, ctypes.c_size_t]
@@ -75,7 +78,7 @@ def lib() -> ctypes.CDLL:
         L.bitnet_grouped_plan_fused_bytes.restype = ctypes.c_size_t
         L.bitnet_grouped_plan_fused.argtypes = [P, I, P, ctypes.c_size_t]
         L.bitnet_linear_fused_grouped.argtypes = [P, P, P]
-        for f in ("bitnet_pack_weights", "bitnet_pack_weights_grouped", "bitnet_quant_act", "bitnet_rmsnorm_quant_act", "bitnet_swiglu_quant_act", "bitnet_linear", "bitnet_linear_select", "bitnet_linear_ex",
+        for f in ("bitnet_pack_weights", "bitnet_pack_weights_grouped", "bitnet_quant_act", "bitnet_rmsnorm_quant_act", "bitnet_swiglu_quant_act", "bitnet_pack_weights_binary", "bitnet_pack_bitplanes", "bitnet_linear_bits", "bitnet_linear", "bitnet_linear_select", "bitnet_linear_ex",
                   "bitnet_grouped_plan_linear", "bitnet_grouped_plan_quant", "bitnet_grouped_plan_fused",
                   "bitnet_linear_grouped", "bitnet_quant_act_grouped", "bitnet_linear_fused_grouped"):
             getattr(L, f).restype = I
@@ -350,6 +353,57 @@ def swiglu_quant(gate: torch.Tensor, up: torch.Tensor, stream=None):
     s_x = torch.empty(M, dtype=torch.float32, device=gate.device)
     bitnet_swiglu_quant_act(gate, up, q, s_x, stream)
     return q, s_x
+
+
+FMT_BINARY, FMT_BITPLANES = 1, 2
+
+
+def pack_weights_binary(w: torch.Tensor, stream=None):
+    """b1.0 binary packing -> (bits uint8 [N][K/8], s_w fp32 [1])."""
+    _dev(w, torch.float32, "w")
+    N, K = w.shape
+    bits = torch.empty((N, K // 8), dtype=torch.uint8, device=w.device)
+    s_w = torch.empty(1, dtype=torch.float32, device=w.device)
+    ws = torch.empty(max(1, bitnet_pack_workspace_bytes(N, K) // 8), dtype=torch.float64, device=w.device)
+    _check(lib().bitnet_pack_weights_binary(_ptr(w), N, K, _ptr(bits), _ptr(s_w), _ptr(ws), ws.numel() * 8,
+                                            _stream(stream)))
+    return bits, s_w
+
+
+def pack_bitplanes(packed: torch.Tensor, K: int, stream=None) -> torch.Tensor:
+    """2-bit packed [N][K/4] -> sign / mask bitplanes uint8 [N][K/32][8]."""
+    _dev(packed, torch.uint8, "packed")
+    N = packed.shape[0]
+    if packed.shape != (N, K // 4):
+        raise ValueError("packed must be [N][K/4]")
+    planes = torch.empty((N, K // 32, 8), dtype=torch.uint8, device=packed.device)
+    _check(lib().bitnet_pack_bitplanes(_ptr(packed), N, K, _ptr(planes), _stream(stream)))
+    return planes
+
+
+def bitnet_linear_bits(q, s_x, wbits, fmt: int, s_w, y, acc=None, kernel: int = 0, stream=None) -> None:
+    """q int8 [M][K] against binary bits [N][K/8] or bitplanes [N][K/32][8] -> y fp32
+    [M][N] (and acc int32 [M][N])."""
+    _dev(q, torch.int8, "q"); _dev(s_x, torch.float32, "s_x"); _dev(wbits, torch.uint8, "wbits")
+    _dev(s_w, torch.float32, "s_w"); _dev(y, torch.float32, "y")
+    M, K = q.shape
+    N = wbits.shape[0]
+    if wbits.numel() != N * K // (8 if fmt == FMT_BINARY else 4) or y.shape != (M, N):
+        raise ValueError("weights do not match K, or y is not [M][N]")
+    if acc is not None:
+        _dev(acc, torch.int32, "acc")
+    _check(lib().bitnet_linear_bits(_ptr(q), _ptr(s_x), _ptr(wbits), int(fmt), _ptr(s_w), M, N, K, _ptr(y),
+                                    _ptr(acc), int(kernel), _stream(stream)))
+
+
+def linear_bits(q, s_x, wbits, fmt: int, s_w, want_acc: bool = False, kernel: int = 0, stream=None):
+    """y (and acc) of q against binary bits [N][K/8] or bitplanes [N][K/32][8]."""
+    M, K = q.shape
+    N = wbits.shape[0]
+    y = torch.empty((M, N), dtype=torch.float32, device=q.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=q.device) if want_acc else None
+    bitnet_linear_bits(q, s_x, wbits, fmt, s_w, y, acc, kernel, stream)
+    return (y, acc) if want_acc else y
 
 
 def pack_weights_grouped(w: torch.Tensor, group: int, eps: float = 1e-5, stream=None):

@@ -94,6 +94,49 @@ BITNET_API int bitnet_pack_weights(const float *w, int64_t N, int64_t K, float e
     return hip_status(launch_pack(w, N, K, eps, packed, s_w, (double *)workspace, (hipStream_t)stream));
 }
 
+BITNET_API int bitnet_pack_weights_binary(const float *w, int64_t N, int64_t K, uint8_t *bits, float *s_w,
+                                          void *workspace, size_t workspace_bytes, void *stream) {
+    int st = check_dims(0, N, K);
+    if (st) return st;
+    if (K % 32 != 0) return fail(BITNET_ERR_SHAPE, "K must be a multiple of 32");
+    if (!s_w) return fail(BITNET_ERR_NULL, "s_w is NULL");
+    if (N > 0 && (!w || !bits || !workspace)) return fail(BITNET_ERR_NULL, "null pointer");
+    if (!aligned(s_w, 4) || (w && !aligned(w, 16)) || (bits && !aligned(bits, 4)) ||
+        (workspace && !aligned(workspace, 8)))
+        return fail(BITNET_ERR_ALIGN, "w must be 16-byte, bits and s_w 4-byte, workspace 8-byte aligned");
+    if (workspace_bytes < bitnet_pack_workspace_bytes(N, K)) return fail(BITNET_ERR_ARG, "workspace too small");
+    hipError_t e = launch_weight_scale(w, N, K, s_w, (double *)workspace, (hipStream_t)stream);
+    if (e == hipSuccess) e = launch_pack_binary(w, N, K, bits, (hipStream_t)stream);
+    return hip_status(e);
+}
+
+BITNET_API int bitnet_pack_bitplanes(const uint8_t *packed, int64_t N, int64_t K, uint8_t *planes, void *stream) {
+    int st = check_dims(0, N, K);
+    if (st) return st;
+    if (K % 32 != 0) return fail(BITNET_ERR_SHAPE, "K must be a multiple of 32");
+    if (N == 0) return BITNET_OK;
+    if (!packed || !planes) return fail(BITNET_ERR_NULL, "null pointer");
+    if (!aligned(packed, 8) || !aligned(planes, 8)) return fail(BITNET_ERR_ALIGN, "packed and planes must be 8-byte aligned");
+    return hip_status(launch_pack_bitplanes(packed, N, K, planes, (hipStream_t)stream));
+}
+
+BITNET_API int bitnet_linear_bits(const int8_t *q, const float *s_x, const uint8_t *wbits, int fmt, const float *s_w,
+                                  int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, int kernel, void *stream) {
+    if (fmt != BITNET_FMT_BINARY && fmt != BITNET_FMT_BITPLANES) return fail(BITNET_ERR_ARG, "unknown weight format");
+    if (kernel < 0 || kernel > 2) return fail(BITNET_ERR_ARG, "unknown kernel id");
+    int st = check_dims(M, N, K);
+    if (st) return st;
+    if (K % 32 != 0) return fail(BITNET_ERR_SHAPE, "K must be a multiple of 32");
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!q || !s_x || !wbits || !s_w || !y) return fail(BITNET_ERR_NULL, "null pointer");
+    if (!aligned(s_x, 4) || !aligned(s_w, 4) || !aligned(y, 4) || (acc && !aligned(acc, 4)))
+        return fail(BITNET_ERR_ALIGN, "s_x, s_w, y and acc must be 4-byte aligned");
+    if (kernel == 2 && !bits_fast_ok(fmt, M, K, q, wbits))
+        return fail(BITNET_ERR_ARG, "the bit-serial GEMV needs M == 1, K % 128 (binary) or % 64 (bitplanes), "
+                                    "K within its LDS limit, 16-byte aligned q and weights");
+    return hip_status(launch_linear_bits(q, s_x, wbits, fmt, s_w, M, N, K, y, acc, kernel, (hipStream_t)stream));
+}
+
 BITNET_API int bitnet_pack_weights_grouped(const float *w, int64_t N, int64_t K, int64_t group, float eps,
                                            uint8_t *packed, float *s_w, void *stream) {
     int st = check_dims(0, N, K);

@@ -76,6 +76,15 @@ hipError_t launch_swiglu_quant(const float *g, const float *u, int64_t M, int64_
                                hipStream_t st);
 hipError_t launch_rmsnorm_quant(const uint16_t *x, const float *g, float eps, int64_t M, int64_t K, int8_t *q,
                                 float *s_x, hipStream_t st);
+// s_w = mean |w| of the whole tensor (the row sums in rowsum, float64)
+hipError_t launch_weight_scale(const float *w, int64_t N, int64_t K, float *s_w, double *rowsum, hipStream_t st);
+// other weight encodings (bits.hip): b1.0 binary bits, sign / mask bitplanes
+hipError_t launch_pack_binary(const float *w, int64_t N, int64_t K, uint8_t *bits, hipStream_t st);
+hipError_t launch_pack_bitplanes(const uint8_t *packed, int64_t N, int64_t K, uint8_t *planes, hipStream_t st);
+int64_t bits_max_k(int fmt);
+bool bits_fast_ok(int fmt, int64_t M, int64_t K, const void *q, const void *wbits);
+hipError_t launch_linear_bits(const int8_t *q, const float *s_x, const uint8_t *wbits, int fmt, const float *s_w,
+                              int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, int kernel, hipStream_t st);
 hipError_t launch_pack(const float *w, int64_t N, int64_t K, float eps, uint8_t *packed,
                        float *s_w, double *rowsum, hipStream_t st);
 hipError_t launch_pack_grouped(const float *w, int64_t N, int64_t K, int64_t G, float eps, uint8_t *packed,

@@ -99,15 +99,19 @@ hipError_t launch_pack_grouped(const float *w, int64_t N, int64_t K, int64_t G, 
     return hipGetLastError();
 }
 
-hipError_t launch_pack(const float *w, int64_t N, int64_t K, float eps, uint8_t *packed, float *s_w,
-                       double *rowsum, hipStream_t st) {
+hipError_t launch_weight_scale(const float *w, int64_t N, int64_t K, float *s_w, double *rowsum, hipStream_t st) {
     if (N > 0) {
         rowsum_kernel<<<dim3((unsigned)((N + 63) / 64)), dim3(64), 0, st>>>(w, N, K, rowsum);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     combine_kernel<<<dim3(1), dim3(64), 0, st>>>(rowsum, N, K, s_w);
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+hipError_t launch_pack(const float *w, int64_t N, int64_t K, float eps, uint8_t *packed, float *s_w,
+                       double *rowsum, hipStream_t st) {
+    hipError_t e = launch_weight_scale(w, N, K, s_w, rowsum, st);
     if (e != hipSuccess || N == 0) return e;
     const int64_t nbytes = N * K / 4;
     const int64_t threads = (nbytes + 3) / 4;

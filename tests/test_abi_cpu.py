@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -280,6 +280,31 @@ def test_fused_plan_swiglu_checks_and_variant(L):
                     (F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, 0, n(0.0), 0, a16, a16 + 2), ALIGN)):
         one = (F * 1)(d)
         assert L.bitnet_grouped_plan_fused(one, 1, buf, 4096) == want
+
+
+def test_bit_encodings_reject_bad_arguments(L):
+    p = ctypes.c_void_p(4096)  # never dereferenced: every call below fails its checks
+    z = None
+    ws = ctypes.c_size_t(1 << 20)
+    assert L.bitnet_pack_weights_binary(p, 4, 48, p, p, p, ws, z) == SHAPE        # K % 32
+    assert L.bitnet_pack_weights_binary(p, 4, 64, p, z, p, ws, z) == NULL
+    assert L.bitnet_pack_weights_binary(ctypes.c_void_p(4100), 4, 64, p, p, p, ws, z) == ALIGN
+    assert L.bitnet_pack_weights_binary(p, 4, 64, p, p, p, ctypes.c_size_t(8), z) == ARG  # workspace
+    assert L.bitnet_pack_bitplanes(p, 4, 48, p, z) == SHAPE
+    assert L.bitnet_pack_bitplanes(ctypes.c_void_p(4100), 4, 64, p, z) == ALIGN
+    assert L.bitnet_pack_bitplanes(z, 4, 64, p, z) == NULL
+    assert L.bitnet_pack_bitplanes(z, 0, 64, z, z) == OK
+    lb = L.bitnet_linear_bits
+    assert lb(p, p, p, 3, p, 1, 8, 128, p, z, 0, z) == ARG                        # format
+    assert lb(p, p, p, 1, p, 1, 8, 128, p, z, 3, z) == ARG                        # kernel id
+    assert lb(p, p, p, 1, p, 1, 8, 100, p, z, 0, z) == SHAPE                      # K % 32
+    assert lb(p, p, z, 1, p, 1, 8, 128, p, z, 0, z) == NULL
+    assert lb(p, p, p, 1, p, 2, 8, 128, p, z, 2, z) == ARG                        # GEMV: M == 1
+    assert lb(p, p, p, 1, p, 1, 8, 96, p, z, 2, z) == ARG                         # binary GEMV: K % 128
+    assert lb(p, p, p, 2, p, 1, 8, 96, p, z, 2, z) == ARG                         # bitplanes GEMV: K % 64
+    assert lb(p, p, p, 1, p, 1, 8, 57344 + 128, p, z, 2, z) == ARG                # LDS limit
+    assert lb(ctypes.c_void_p(4097), p, p, 1, p, 1, 8, 128, p, z, 2, z) == ARG    # alignment
+    assert lb(p, p, p, 1, p, 0, 8, 128, p, z, 0, z) == OK
 
 
 def test_linear_plan_weight_groups(L):

@@ -584,6 +584,94 @@ def test_fused_pair_matches_swiglu_then_linear():
     assert torch.equal(qa, q2) and torch.equal(sa, s2)
 
 
+# ----------------------------------------------------------------- binary weights, sign / mask bitplanes
+
+@pytest.mark.parametrize("N,K", [(300, 2560), (33, 6912), (5, 32), (70, 640)])
+def test_pack_binary_parity(N, K):
+    w = synth.latent_weights(synth.stream_key(350, N, K), N, K, 0.02)
+    w[0, :7] = 0.0
+    w[1, :3] = -0.0
+    b_ref, s_ref = oracle.pack_binary(w.numpy())
+    bits, s_w = tw.pack_weights_binary(w.to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits.cpu().numpy(), b_ref) and s_w.item() == s_ref
+
+
+@pytest.mark.parametrize("N,K", [(300, 2560), (7, 32), (129, 6912)])
+def test_pack_bitplanes_parity(N, K):
+    packed = synth.random_bytes(synth.stream_key(351, N, K), N * K // 4).numpy().reshape(N, K // 4)  # codes 0-3
+    ref = oracle.pack_bitplanes(packed, K)
+    planes = tw.pack_bitplanes(torch.from_numpy(packed).to(DEV), K)
+    torch.cuda.synchronize()
+    assert np.array_equal(planes.cpu().numpy(), ref)
+
+
+def _bits_case(fmt, N, K, key):
+    if fmt == tw.FMT_BINARY:
+        wb = synth.random_bytes(synth.stream_key(key, 1), N * K // 8).numpy().reshape(N, K // 8)
+        return wb, lambda q, s, sw: oracle.linear_binary(q, s, wb, sw)
+    w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02).numpy()
+    packed, _ = oracle.pack(w)
+    wb = oracle.pack_bitplanes(packed, K)
+    return wb, lambda q, s, sw: oracle.linear_bitplanes(q, s, wb, sw)
+
+
+BITS_SHAPES = [(1, 300, 2560), (1, 2560, 6912), (1, 65, 128), (1, 1, 256), (1, 700, 8192), (1, 129, 28672),
+               (3, 70, 640), (8, 33, 2560)]
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("M,N,K", BITS_SHAPES)
+def test_linear_bits_parity(fmt, M, N, K):
+    key = synth.stream_key(352, fmt, M, N, K)
+    x, q, s = quantized_inputs(key, M, K, outlier_frac=0.002)
+    wb, ref = _bits_case(fmt, N, K, key)
+    s_w = np.float32(0.0123)
+    acc_ref, y_ref = ref(q, s, s_w)
+    qd, sd = torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV)
+    wd, swd = torch.from_numpy(wb).to(DEV), torch.tensor([s_w], device=DEV)
+    kernels = (0, 1, 2) if M == 1 else (0, 1)
+    for kern in kernels:
+        y, acc = tw.linear_bits(qd, sd, wd, fmt, swd, want_acc=True, kernel=kern)
+        torch.cuda.synchronize()
+        assert np.array_equal(acc.cpu().numpy(), acc_ref), kern
+        assert_y(y.cpu().numpy(), y_ref)
+
+
+@pytest.mark.parametrize("fmt,K", [(1, 57344), (2, 51584)])
+def test_linear_bits_longest_k(fmt, K):
+    """The longest K whose staged planes fit LDS, with extreme codes (+-127, -127 on
+    every value of one row) so that every plane and the sign plane count."""
+    N = 97
+    key = synth.stream_key(353, fmt, K)
+    q = np.full((1, K), -127, np.int8)
+    q[0, ::3] = 127
+    q[0, 5::7] = 0
+    s = np.array([0.75], np.float32)
+    wb, ref = _bits_case(fmt, N, K, key)
+    acc_ref, y_ref = ref(q, s, np.float32(0.01))
+    y, acc = tw.linear_bits(torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV), torch.from_numpy(wb).to(DEV),
+                            fmt, torch.tensor([0.01], device=DEV), want_acc=True, kernel=2)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    assert_y(y.cpu().numpy(), y_ref)
+
+
+def test_bitplanes_equal_two_bit_codes_on_gpu():
+    """The same ternary weights through the 2-bit GEMV and the bitplane GEMV."""
+    N, K = 2560, 6912
+    key = synth.stream_key(354)
+    x, q, s = quantized_inputs(key, 1, K)
+    w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02)
+    packed, s_w = tw.pack_weights(w.to(DEV))
+    planes = tw.pack_bitplanes(packed, K)
+    qd, sd = torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV)
+    y2, a2 = tw.linear(qd, sd, packed, s_w, want_acc=True)
+    yb, ab = tw.linear_bits(qd, sd, planes, tw.FMT_BITPLANES, s_w, want_acc=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a2, ab) and torch.equal(y2, yb)
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 200, 53312), (2, 70, 26176), (3, 200, 16704), (8, 200, 16704),
                                    (13, 130, 8192), (16, 65, 28672)])
 def test_gemv_parity_k_segments(M, N, K):
