@@ -13,10 +13,14 @@
 // two's-complement bit planes (plane j of 32 values: bit i = bit j of q_i), and a
 // 32-weight word w contributes popcount(plane_j & w) to counter j; at the end
 // sum_k q_k [bit k of w] = sum_j 2^j cnt_j with the weight of plane 7 being -128.
-// Binary: sum q t = 2 sum_{bit set} q - sum q.  Bitplanes: sum q t =
-// sum_{mask} q - 2 sum_{mask & sign} q.  Per 32 weights and row that is 16 VALU
-// operations (binary) or 33 (bitplanes), no unpacking into bytes.
+// Binary: sum q t = 2 sum_{bit set} q - sum q.  Bitplanes: a negative weight adds
+// -q = ~q + 1 (two's complement), so with pos = mask & ~sign each plane word
+// becomes bfi(p_j, pos, sign) = (p_j & pos) | (~p_j & sign) -- q's bit where the
+// weight is +1, its complement where it is -1, 0 where it is 0 -- and sum q t =
+// sum_j 2^j cnt_j + popcount(sign).  Per 32 weights and row that is 16 VALU
+// operations (binary) or 19 (bitplanes), no unpacking into bytes.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -131,16 +135,20 @@ struct BitsFmt {
     static constexpr int RowDiv = FMT == 1 ? 8 : 4;    // weights per byte
 };
 
-constexpr int kBitsRG = 2;
+// rows per octet: 4 for tall matrices (fewer LDS plane reads and less loop overhead
+// per weight), 2 otherwise (twice the workgroups for a small N)
+constexpr int64_t kBitsTallN = 16384;
 
-template <int FMT>
-__global__ __launch_bounds__(256) void gemv_bits_kernel(const int8_t *__restrict__ q, const float *__restrict__ s_x,
+// Binary with 4 rows per octet is held at 4 waves per SIMD (it would settle just
+// above 128 registers otherwise); the bitplane kernels run faster as compiled.
+template <int FMT, int RG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FMT == 1 && RG == 4 ? 4 : 1)))
+void gemv_bits_kernel(const int8_t *__restrict__ q, const float *__restrict__ s_x,
                                                         const uint8_t *__restrict__ wbits,
                                                         const float *__restrict__ s_w, int N, int K,
                                                         float *__restrict__ y, int32_t *__restrict__ acc_out,
                                                         int ks) {
     using F = BitsFmt<FMT>;
-    constexpr int RG = kBitsRG;
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
     __shared__ int sq;
     __shared__ int red[4 * 8 * RG];
@@ -196,17 +204,21 @@ __global__ __launch_bounds__(256) void gemv_bits_kernel(const int8_t *__restrict
     if (FMT == 1 && part != 0) atomicAdd(&sq, part);
     __syncthreads();
 
-    // counters per row and plane (bitplanes: of mask, then of mask & sign)
-    int cnt[RG][8], cnt2[RG][8];
+    // counters per row and plane (bitplanes: and of the sign bits)
+    int cnt[RG][8], cns[RG];
     #pragma unroll
     for (int g = 0; g < RG; ++g) {
+        cns[g] = 0;
         #pragma unroll
-        for (int j = 0; j < 8; ++j) { cnt[g][j] = 0; cnt2[g][j] = 0; }
+        for (int j = 0; j < 8; ++j) cnt[g][j] = 0;
     }
-    auto consume = [&](const uint4 (&b)[RG], int t) {
+    // CHECK: the step may hold slots past the slice (only the last one does); they
+    // count as all-zero words
+    auto consume = [&](const uint4 (&b)[RG], int t, auto check) {
+        constexpr bool CHECK = decltype(check)::value;
         const int sl = sb + l8 + 8 * t;
-        const bool valid = sl < se;
-        const uint32_t *src = lds + min(sl, slast) * F::SD;
+        const bool valid = !CHECK || sl < se;
+        const uint32_t *src = lds + (CHECK ? min(sl, slast) : sl) * F::SD;
         #pragma unroll
         for (int i = 0; i < F::GC; ++i) {
             const uint4 p0 = *reinterpret_cast<const uint4 *>(src + 8 * i);
@@ -221,35 +233,39 @@ __global__ __launch_bounds__(256) void gemv_bits_kernel(const int8_t *__restrict
                     for (int j = 0; j < 8; ++j) cnt[g][j] += __builtin_popcount(p[j] & w);
                 } else {
                     const uint32_t m = valid ? wv[2 * i] : 0u;
-                    const uint32_t ms = m & wv[2 * i + 1];
+                    const uint32_t sg = m & wv[2 * i + 1];   // a sign bit counts only under the mask
+                    const uint32_t pos = m ^ sg;
                     #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        cnt[g][j] += __builtin_popcount(p[j] & m);
-                        cnt2[g][j] += __builtin_popcount(p[j] & ms);
-                    }
+                    for (int j = 0; j < 8; ++j) cnt[g][j] += __builtin_popcount((p[j] & pos) | (~p[j] & sg));
+                    cns[g] += __builtin_popcount(sg);
                 }
             }
         }
     };
-    // two register buffers: the loads of step t + 1 are in flight during step t
+    using Checked = std::true_type;
+    using Unchecked = std::false_type;
+    // two register buffers: the loads of step t + 1 are in flight during step t;
+    // every slot of steps 0 .. T - 2 lies inside the slice
     if (T > 0) {
         int t = 0;
-        for (; t + 2 <= T; t += 2) {
+        for (; t + 2 <= T - 1; t += 2) {
             issue(bufB, t + 1);
-            consume(bufA, t);
+            consume(bufA, t, Unchecked{});
             issue(bufA, t + 2);
-            consume(bufB, t + 1);
+            consume(bufB, t + 1, Unchecked{});
         }
-        if (t < T) consume(bufA, t);
+        if (t == T - 2) {
+            issue(bufB, t + 1);
+            consume(bufA, t, Unchecked{});
+            consume(bufB, t + 1, Checked{});
+        } else {
+            consume(bufA, t, Checked{});
+        }
     }
 
     int a[RG];
     #pragma unroll
-    for (int g = 0; g < RG; ++g) {
-        int v = plane_sum(cnt[g]);
-        if (FMT == 2) v -= 2 * plane_sum(cnt2[g]);
-        a[g] = octet_sum(v);
-    }
+    for (int g = 0; g < RG; ++g) a[g] = octet_sum(plane_sum(cnt[g]) + cns[g]);
     const double c = rescale_factor(*s_x, *s_w);
     auto finish = [&](int r, int v) {
         const int acc = FMT == 1 ? 2 * v - sq : v;
@@ -294,18 +310,27 @@ bool bits_fast_ok(int fmt, int64_t M, int64_t K, const void *q, const void *wbit
            (uintptr_t)wbits % 16 == 0;
 }
 
+template <int FMT, int RG>
+static hipError_t launch_gemv_bits_rg(const int8_t *q, const float *s_x, const uint8_t *wbits, const float *s_w,
+                                      int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
+    using F = BitsFmt<FMT>;
+    const int S = (int)(K / F::V);
+    auto blocks = [&](int k) { return (N + (4 / k) * 8 * RG - 1) / ((4 / k) * 8 * RG); };
+    // more K slices while the launch has fewer than 2 workgroups per CU and each
+    // slice would keep at least 1024 weights of its rows
+    int ks = 1;
+    while (ks < 4 && blocks(ks) < 512 && K / (2 * ks) >= 1024) ks *= 2;
+    const size_t lds = (size_t)S * F::SD * 4;
+    gemv_bits_kernel<FMT, RG><<<dim3((unsigned)blocks(ks)), dim3(256), lds, st>>>(q, s_x, wbits, s_w, (int)N, (int)K,
+                                                                                  y, acc, ks);
+    return hipGetLastError();
+}
+
 template <int FMT>
 static hipError_t launch_gemv_bits(const int8_t *q, const float *s_x, const uint8_t *wbits, const float *s_w,
                                    int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
-    using F = BitsFmt<FMT>;
-    const int S = (int)(K / F::V);
-    auto blocks = [&](int k) { return (N + (4 / k) * 8 * kBitsRG - 1) / ((4 / k) * 8 * kBitsRG); };
-    int ks = 1;
-    while (ks < 4 && blocks(ks) < 512 && S / (8 * ks * 2) >= 2) ks *= 2;
-    const size_t lds = (size_t)S * F::SD * 4;
-    gemv_bits_kernel<FMT><<<dim3((unsigned)blocks(ks)), dim3(256), lds, st>>>(q, s_x, wbits, s_w, (int)N, (int)K, y,
-                                                                              acc, ks);
-    return hipGetLastError();
+    return N >= kBitsTallN ? launch_gemv_bits_rg<FMT, 4>(q, s_x, wbits, s_w, N, K, y, acc, st)
+                           : launch_gemv_bits_rg<FMT, 2>(q, s_x, wbits, s_w, N, K, y, acc, st);
 }
 
 // ---- any M: one thread per output, plain loops (any alignment)

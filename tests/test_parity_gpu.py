@@ -617,7 +617,7 @@ def _bits_case(fmt, N, K, key):
 
 
 BITS_SHAPES = [(1, 300, 2560), (1, 2560, 6912), (1, 65, 128), (1, 1, 256), (1, 700, 8192), (1, 129, 28672),
-               (3, 70, 640), (8, 33, 2560)]
+               (1, 16400, 640), (1, 16384, 8192), (3, 70, 640), (8, 33, 2560)]
 
 
 @pytest.mark.parametrize("fmt", [1, 2])
@@ -638,11 +638,12 @@ def test_linear_bits_parity(fmt, M, N, K):
         assert_y(y.cpu().numpy(), y_ref)
 
 
+@pytest.mark.parametrize("N", [97, 16400])
 @pytest.mark.parametrize("fmt,K", [(1, 57344), (2, 51584)])
-def test_linear_bits_longest_k(fmt, K):
+def test_linear_bits_longest_k(fmt, K, N):
     """The longest K whose staged planes fit LDS, with extreme codes (+-127, -127 on
-    every value of one row) so that every plane and the sign plane count."""
-    N = 97
+    every value of one row) so that every plane and the sign plane count; N below
+    and above the row count where the kernel takes 4 rows per octet."""
     key = synth.stream_key(353, fmt, K)
     q = np.full((1, K), -127, np.int8)
     q[0, ::3] = 127
