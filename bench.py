@@ -421,6 +421,30 @@ def main() -> int:
             sec["colsplit8_gate_shard_M1"] = {"us": round(us, 2), "weight_GBs": round(shard.numel() / (us * 1e-6) / 1e9, 1)}
             del fpacked
         if "encodings" in legs:
+            # the decode step with its weights as sign / mask bitplanes (the same 2 bits
+            # per weight, converted from the packed codes): one fused launch of the
+            # bit-serial kernel, quantization inside the workgroups as in the timed step
+            planes = [tw.pack_bitplanes(p_, m.K) for p_, m in zip(packed, mats)]
+            bys = [torch.empty_like(y) for y in ys]
+            bplan = tw.bitnet_grouped_plan_fused(
+                [(xs[m.layer][m.slot], planes[i], sws[i], bys[i], None, None, None) for i, m in enumerate(mats)])
+            for _ in range(300):
+                bplan.launch(stream)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(500):
+                bplan.launch(stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            b_us = a.elapsed_time(b) * 1e3 / 500
+            for y_, yb_ in zip(ys, bys):
+                assert torch.isfinite(yb_).all()
+            sec["decode_step_2p4b_bitplanes_fused"] = {
+                "us": round(b_us, 1), "weight_GBs": round(weight_bytes / (b_us * 1e-6) / 1e9, 1),
+                "kernel": "gemv_bits_fused_grouped_kernel", "vs_codes_fused_us": round(b_us - kern_ms * 1e3, 1)}
+            log(f"fused step over bitplanes: {b_us:.1f} us ({b_us - kern_ms * 1e3:+.1f} us vs the 2-bit codes)")
+            del planes, bys, bplan
             # the same 100B-scale FFN stream (M = 1, 24 GEMV launches in one graph) with
             # the weights as 2-bit codes, as sign / mask bitplanes (same bytes, another
             # contraction) and as b1.0 binary bits (half the bytes)

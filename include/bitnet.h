@@ -391,6 +391,10 @@ typedef struct bitnet_fused_desc {
                                the problem is the gate (packed, s_w) / up (packed_up,
                                s_w_up) pair of a SwiGLU feed-forward part; acc must be NULL */
     const float *s_w_up;    /* (device) [1] */
+    int32_t weight_fmt;     /* 0: packed holds 2-bit codes; BITNET_FMT_BITPLANES: packed holds
+                               the sign / mask bitplanes [N][K/32][8] of the same weights (plain
+                               rows only: no norm_gain, x_f32 or packed_up; K <= 51584).  Every
+                               descriptor of a plan has the same format. */
 } bitnet_fused_desc;
 
 BITNET_API size_t bitnet_grouped_plan_fused_bytes(int count, const bitnet_fused_desc *descs);

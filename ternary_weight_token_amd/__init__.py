@@ -34,7 +34,8 @@ class _FusedDesc(ctypes.Structure):
                 ("y", ctypes.c_void_p), ("acc", ctypes.c_void_p), ("q", ctypes.c_void_p),
                 ("s_x", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("norm_gain", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
-                ("x_f32", ctypes.c_void_p), ("packed_up", ctypes.c_void_p), ("s_w_up", ctypes.c_void_p)]
+                ("x_f32", ctypes.c_void_p), ("packed_up", ctypes.c_void_p), ("s_w_up", ctypes.c_void_p),
+                ("weight_fmt", ctypes.c_int32)]
 
 
 class _QuantDesc(ctypes.Structure):
@@ -289,7 +290,8 @@ def bitnet_grouped_plan_fused(problems, device=None) -> GroupedPlan:
     after an RMSNorm with the fp32 gain [K] when one is given) or an fp32 [1][K] row
     (quantized the same way, no norm).  packed and s_w are one matrix, or the pairs
     (packed_gate, packed_up) and (s_w_gate, s_w_up) of a SwiGLU feed-forward part,
-    whose y gets fp32(silu(y_gate) y_up)."""
+    whose y gets fp32(silu(y_gate) y_up).  Weights as sign / mask bitplanes are given
+    as [N][K/32][8] tensors (pack_bitplanes), every problem of the plan alike."""
     arr = (_FusedDesc * len(problems))()
     refs = []
     for i, prob in enumerate(problems):
@@ -313,10 +315,11 @@ def bitnet_grouped_plan_fused(problems, device=None) -> GroupedPlan:
             _dev(gain, torch.float32, "norm_gain")
             if gain.shape != (K,):
                 raise ValueError("norm_gain must be [K]")
+        fmt = FMT_BITPLANES if packed.dim() == 3 else 0
         arr[i] = _FusedDesc(xp, packed.data_ptr(), s_w.data_ptr(), y.data_ptr(),
                             0 if acc is None else acc.data_ptr(), 0 if q is None else q.data_ptr(),
                             0 if s_x is None else s_x.data_ptr(), M, packed.shape[0], K,
-                            0 if gain is None else gain.data_ptr(), eps, xf, pu, su)
+                            0 if gain is None else gain.data_ptr(), eps, xf, pu, su, fmt)
         refs.append((x, packed, s_w, y, acc, q, s_x, gain))
     n = lib().bitnet_grouped_plan_fused_bytes(len(problems), ctypes.cast(arr, ctypes.c_void_p))
     buf = ctypes.create_string_buffer(n)

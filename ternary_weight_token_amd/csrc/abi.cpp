@@ -277,6 +277,12 @@ static int check_fused_desc(const bitnet_fused_desc &d) {
     int st = check_dims(d.M, d.N, d.K);
     if (st) return st;
     if (d.M != 1 || d.N < 1) return fail(BITNET_ERR_SHAPE, "fused linear needs M == 1, N >= 1");
+    if (d.weight_fmt != 0 && d.weight_fmt != BITNET_FMT_BITPLANES) return fail(BITNET_ERR_ARG, "unknown weight format");
+    if (d.weight_fmt == BITNET_FMT_BITPLANES) {
+        if (d.norm_gain || d.x_f32 || d.packed_up)
+            return fail(BITNET_ERR_ARG, "bitplane weights take plain rows only (no norm_gain, x_f32 or packed_up)");
+        if (d.K > bits_max_k(BITNET_FMT_BITPLANES)) return fail(BITNET_ERR_SHAPE, "bitplane rows need K <= 51584");
+    }
     if (d.x_f32) {
         if (d.x || d.norm_gain) return fail(BITNET_ERR_ARG, "an fp32 row takes no x and no norm_gain");
         if (!aligned(d.x_f32, 16)) return fail(BITNET_ERR_ALIGN, "x_f32 must be 16-byte aligned");
@@ -419,7 +425,9 @@ BITNET_API int bitnet_grouped_plan_quant(const bitnet_quant_desc *descs, int cou
 
 static uint64_t fused_blocks(const bitnet_fused_desc &d) {
     // a gate / up pair takes both matrices' rows in each block: half the rows of each
-    const uint64_t rows = gemv_fused_rows_per_block() / (d.packed_up ? 2 : 1);
+    const uint64_t rows = (d.weight_fmt == BITNET_FMT_BITPLANES ? bits_fused_rows_per_block()
+                                                                 : gemv_fused_rows_per_block()) /
+                          (d.packed_up ? 2 : 1);
     return ((uint64_t)d.N + rows - 1) / rows;
 }
 
@@ -438,6 +446,8 @@ BITNET_API int bitnet_grouped_plan_fused(const bitnet_fused_desc *descs, int cou
     for (int i = 0; i < count; ++i) {
         int st = check_fused_desc(descs[i]);
         if (st) return st;
+        if (descs[i].weight_fmt != descs[0].weight_fmt)
+            return fail(BITNET_ERR_ARG, "every descriptor of a plan needs the same weight format");
         blocks += fused_blocks(descs[i]);
     }
     if (blocks >= ((uint64_t)1 << 31)) return fail(BITNET_ERR_SHAPE, "too many blocks");
@@ -453,12 +463,18 @@ BITNET_API int bitnet_grouped_plan_fused(const bitnet_fused_desc *descs, int cou
     h->total_blocks = (uint32_t)blocks;
     h->block_threads = gemv_fused_threads();
     h->rows_per_block = gemv_fused_rows_per_block();
+    const bool planes = descs[0].weight_fmt == BITNET_FMT_BITPLANES;
     h->variant = 0;   // mask of the prologues in use
     for (int i = 0; i < count; ++i) {
         if (descs[i].norm_gain) h->variant |= kFusedProNorm;
         if (descs[i].x_f32 || descs[i].packed_up) h->variant |= kFusedProSwiglu;
     }
-    for (int i = 0; i < count; ++i) h->lds_bytes = std::max(h->lds_bytes, gemv_grouped_lds_bytes(descs[i].K));
+    if (planes) {
+        h->variant = kFusedBitplanes;
+        h->rows_per_block = bits_fused_rows_per_block();
+    }
+    for (int i = 0; i < count; ++i)
+        h->lds_bytes = std::max(h->lds_bytes, planes ? bits_fused_lds_bytes(descs[i].K) : gemv_grouped_lds_bytes(descs[i].K));
     h->desc_offset = doff;
     h->table_offset = toff;
     h->total_bytes = need;
@@ -506,6 +522,8 @@ BITNET_API int bitnet_linear_fused_grouped(const void *plan_host, const void *pl
     if (st) return st;
     const PlanHeader *h = (const PlanHeader *)plan_host;
     if (h->total_blocks == 0) return BITNET_OK;
+    if (h->variant == kFusedBitplanes)
+        return hip_status(launch_bits_fused_grouped(plan_dev, h->total_blocks, h->lds_bytes, (hipStream_t)stream));
     if (h->variant > kFusedProMask) return fail(BITNET_ERR_ARG, "not a plan of this kind");
     return hip_status(launch_gemv_fused_grouped(plan_dev, h->total_blocks, h->lds_bytes, h->variant,
                                                 (hipStream_t)stream));

@@ -139,24 +139,128 @@ struct BitsFmt {
 // per weight), 2 otherwise (twice the workgroups for a small N)
 constexpr int64_t kBitsTallN = 16384;
 
-// Binary with 4 rows per octet is held at 4 waves per SIMD (it would settle just
-// above 128 registers otherwise); the bitplane kernels run faster as compiled.
-template <int FMT, int RG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FMT == 1 && RG == 4 ? 4 : 1)))
-void gemv_bits_kernel(const int8_t *__restrict__ q, const float *__restrict__ s_x,
-                                                        const uint8_t *__restrict__ wbits,
-                                                        const float *__restrict__ s_w, int N, int K,
-                                                        float *__restrict__ y, int32_t *__restrict__ acc_out,
-                                                        int ks) {
+// Stagers put the bit planes of the token row into LDS (slot layout of BitsFmt):
+// load() issues the global loads the staging needs, before the first weight loads
+// (so that waiting for them does not wait for the weights); operator() forms the
+// planes and, for binary weights, adds the row's sum of q to *sq.
+
+// From int8 q in memory.
+template <int FMT>
+struct StagePlanesQ {
+    const int8_t *q;
+    int K;
+    struct Pre { uint4 a, b; };
+    __device__ __forceinline__ Pre load() const {
+        const int c0 = min((int)threadIdx.x, (K >> 5) - 1);
+        return Pre{gload16(q + 32 * c0), gload16(q + 32 * c0 + 16)};
+    }
+    __device__ __forceinline__ void operator()(const Pre &pre, uint32_t *lds, int *sq) const {
+        using F = BitsFmt<FMT>;
+        const int tid = threadIdx.x, C32 = K >> 5;
+        int part = 0;
+        auto put = [&](int c, uint4 a, uint4 b) {
+            uint32_t p[8];
+            q_planes(a, b, p);
+            uint32_t *dst = lds + (c / F::GC) * F::SD + 8 * (c % F::GC);
+            *reinterpret_cast<uint4 *>(dst) = make_uint4(p[0], p[1], p[2], p[3]);
+            *reinterpret_cast<uint4 *>(dst + 4) = make_uint4(p[4], p[5], p[6], p[7]);
+            if (FMT == 1) {
+                int s = dot4(a.x, 0x01010101u, 0);
+                s = dot4(a.y, 0x01010101u, s);
+                s = dot4(a.z, 0x01010101u, s);
+                s = dot4(a.w, 0x01010101u, s);
+                s = dot4(b.x, 0x01010101u, s);
+                s = dot4(b.y, 0x01010101u, s);
+                s = dot4(b.z, 0x01010101u, s);
+                part += dot4(b.w, 0x01010101u, s);
+            }
+        };
+        if (tid < C32) put(tid, pre.a, pre.b);
+        for (int c = tid + 256; c < C32; c += 256) put(c, gload16(q + 32 * c), gload16(q + 32 * c + 16));
+        if (FMT == 1 && part != 0) atomicAdd(sq, part);
+    }
+};
+
+// From the bf16 token row (bitplane weights): the absmax quantization of
+// bitnet_quant_act done in the workgroup (page chenxutan.com sec. 2.2: s = max|x| as
+// an integer max of the bf16 magnitudes, codes rint((127 x) / s), all zero for a zero
+// row), then the planes of the codes.  s goes to *s_lds; q and s are also written out
+// when q_out / s_out are set.  Each thread holds its first 32 values from load().
+template <int FMT>
+struct StagePlanesQuant {
+    const uint16_t *x;
+    int K;
+    int8_t *q_out;
+    float *s_out;
+    float *s_lds;
+    uint32_t *red;       // LDS, one word per wavefront
+    struct Pre { uint4 v[4]; };
+    __device__ __forceinline__ Pre load() const {
+        const int c0 = min((int)threadIdx.x, (K >> 5) - 1);   // a clamped duplicate leaves the max as it is
+        Pre p;
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) p.v[i] = gload16(x + 32 * c0 + 8 * i);
+        return p;
+    }
+    __device__ __forceinline__ void operator()(const Pre &pre, uint32_t *lds, int *) const {
+        using F = BitsFmt<FMT>;
+        static_assert(FMT == 2, "the row sum of q is not formed here");
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, C32 = K >> 5;
+        uint32_t mx = max(max(absmax8(pre.v[0]), absmax8(pre.v[1])), max(absmax8(pre.v[2]), absmax8(pre.v[3])));
+        for (int c = tid + 256; c < C32; c += 256) {
+            #pragma unroll
+            for (int i = 0; i < 4; ++i) mx = max(mx, absmax8(gload16(x + 32 * c + 8 * i)));
+        }
+        mx = wave_max_u32(mx);
+        if (lane == 0) red[wave] = mx;
+        __syncthreads();
+        mx = max(max(red[0], red[1]), max(red[2], red[3]));
+        const float s = bf16f(mx);
+        const float inv = 1.0f / s;
+        if (tid == 0) {
+            *s_lds = s;
+            if (s_out) *s_out = s;
+        }
+        auto put = [&](int c, const uint4 (&v)[4]) {
+            uint2 w[4] = {make_uint2(0u, 0u), make_uint2(0u, 0u), make_uint2(0u, 0u), make_uint2(0u, 0u)};
+            if (mx != 0) {
+                #pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = qcode8(v[i], s, inv);
+            }
+            const uint4 a = make_uint4(w[0].x, w[0].y, w[1].x, w[1].y), b = make_uint4(w[2].x, w[2].y, w[3].x, w[3].y);
+            if (q_out) {
+                *reinterpret_cast<uint4 *>(q_out + 32 * c) = a;
+                *reinterpret_cast<uint4 *>(q_out + 32 * c + 16) = b;
+            }
+            uint32_t p[8];
+            q_planes(a, b, p);
+            uint32_t *dst = lds + (c / F::GC) * F::SD + 8 * (c % F::GC);
+            *reinterpret_cast<uint4 *>(dst) = make_uint4(p[0], p[1], p[2], p[3]);
+            *reinterpret_cast<uint4 *>(dst + 4) = make_uint4(p[4], p[5], p[6], p[7]);
+        };
+        if (tid < C32) put(tid, pre.v);
+        for (int c = tid + 256; c < C32; c += 256) {
+            const uint4 v[4] = {gload16(x + 32 * c), gload16(x + 32 * c + 8), gload16(x + 32 * c + 16),
+                                gload16(x + 32 * c + 24)};
+            put(c, v);
+        }
+    }
+};
+
+// One token row against rows [row_base, row_base + (4 / ks) 8 RG) of the weights.
+// sxp is read after the staging (it may be the LDS word the stager writes).
+template <int FMT, int RG, class Stage>
+__device__ __forceinline__ void bits_tile(const Stage &stage, const float *sxp, const uint8_t *__restrict__ wbits,
+                                          const float *__restrict__ s_w, int N, int K, int row_base, int ks,
+                                          float *__restrict__ y, int32_t *__restrict__ acc_out, uint32_t *lds,
+                                          int *sq_ptr, int *red) {
     using F = BitsFmt<FMT>;
-    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-    __shared__ int sq;
-    __shared__ int red[4 * 8 * RG];
+    int &sq = *sq_ptr;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l8 = lane & 7, rs = lane >> 3;
-    const int C32 = K >> 5, S = K / F::V;
+    const int S = K / F::V;
     const int rowsets = 4 / ks, rowset = wave / ks, slice = wave - rowset * ks;
-    const int row0 = (int)blockIdx.x * (rowsets * 8 * RG) + rowset * 8 * RG;
+    const int row0 = row_base + rowset * 8 * RG;
     const int sb = (int)((int64_t)S * slice / ks), se = (int)((int64_t)S * (slice + 1) / ks);
     const int64_t row_bytes = K / F::RowDiv;
 
@@ -175,33 +279,12 @@ void gemv_bits_kernel(const int8_t *__restrict__ q, const float *__restrict__ s_
         for (int g = 0; g < RG; ++g) b[g] = load_weights<true>(prow[g] + 16 * (size_t)sl);
     };
 
-    // q's first chunk of this thread, then the first weights, then the staging
-    const int c0 = min(tid, C32 - 1);
-    const uint4 qa = gload16(q + 32 * c0), qb = gload16(q + 32 * c0 + 16);
+    // the stager's loads, then the first weights, then the staging
+    const typename Stage::Pre pre = stage.load();
     issue(bufA, 0);
     if (tid == 0) sq = 0;
-    int part = 0;
-    auto stage = [&](int c, uint4 a, uint4 b) {
-        uint32_t p[8];
-        q_planes(a, b, p);
-        uint32_t *dst = lds + (c / F::GC) * F::SD + 8 * (c % F::GC);
-        *reinterpret_cast<uint4 *>(dst) = make_uint4(p[0], p[1], p[2], p[3]);
-        *reinterpret_cast<uint4 *>(dst + 4) = make_uint4(p[4], p[5], p[6], p[7]);
-        if (FMT == 1) {
-            int s = dot4(a.x, 0x01010101u, 0);
-            s = dot4(a.y, 0x01010101u, s);
-            s = dot4(a.z, 0x01010101u, s);
-            s = dot4(a.w, 0x01010101u, s);
-            s = dot4(b.x, 0x01010101u, s);
-            s = dot4(b.y, 0x01010101u, s);
-            s = dot4(b.z, 0x01010101u, s);
-            part += dot4(b.w, 0x01010101u, s);
-        }
-    };
     __syncthreads();   // sq initialised
-    if (tid < C32) stage(tid, qa, qb);
-    for (int c = tid + 256; c < C32; c += 256) stage(c, gload16(q + 32 * c), gload16(q + 32 * c + 16));
-    if (FMT == 1 && part != 0) atomicAdd(&sq, part);
+    stage(pre, lds, &sq);
     __syncthreads();
 
     // counters per row and plane (bitplanes: and of the sign bits)
@@ -266,7 +349,7 @@ void gemv_bits_kernel(const int8_t *__restrict__ q, const float *__restrict__ s_
     int a[RG];
     #pragma unroll
     for (int g = 0; g < RG; ++g) a[g] = octet_sum(plane_sum(cnt[g]) + cns[g]);
-    const double c = rescale_factor(*s_x, *s_w);
+    const double c = rescale_factor(*sxp, *s_w);
     auto finish = [&](int r, int v) {
         const int acc = FMT == 1 ? 2 * v - sq : v;
         y[r] = rescale(acc, c);
@@ -288,13 +371,56 @@ void gemv_bits_kernel(const int8_t *__restrict__ q, const float *__restrict__ s_
     __syncthreads();
     if (tid < rowsets * R) {
         const int rsi = tid / R, rr = tid - rsi * R;
-        const int r = (int)blockIdx.x * (rowsets * R) + rsi * R + rr;
+        const int r = row_base + rsi * R + rr;
         if (r < N) {
             int v = 0;
             for (int w = 0; w < ks; ++w) v += red[(rsi * ks + w) * R + rr];
             finish(r, v);
         }
     }
+}
+
+// Binary with 4 rows per octet is held at 4 waves per SIMD (it would settle just
+// above 128 registers otherwise); the bitplane kernels run faster as compiled.
+template <int FMT, int RG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FMT == 1 && RG == 4 ? 4 : 1)))
+void gemv_bits_kernel(const int8_t *__restrict__ q, const float *__restrict__ s_x, const uint8_t *__restrict__ wbits,
+                      const float *__restrict__ s_w, int N, int K, float *__restrict__ y,
+                      int32_t *__restrict__ acc_out, int ks) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+    __shared__ int sq;
+    __shared__ int red[4 * 8 * RG];
+    bits_tile<FMT, RG>(StagePlanesQ<FMT>{q, K}, s_x, wbits, s_w, N, K, (int)blockIdx.x * ((4 / ks) * 8 * RG), ks, y,
+                       acc_out, lds, &sq, red);
+}
+
+// Fused decode step over bitplane weights: the block table and descriptors of the
+// fused grouped plan (one token row per problem, 4 rows per octet, no K split), the
+// row quantized in every workgroup of its problem while staging its planes.
+constexpr int kBitsFusedRG = 4;
+
+__global__ __launch_bounds__(256) void gemv_bits_fused_grouped_kernel(const uint8_t *__restrict__ plan) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+    __shared__ int sq;
+    __shared__ int red[4 * 8 * kBitsFusedRG];
+    __shared__ uint32_t qred[4];
+    __shared__ float s_lds;
+    const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
+    const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[blockIdx.x];
+    const FusedDescDev d = reinterpret_cast<const FusedDescDev *>(plan + h->desc_offset)[e.desc];
+    const bool first = e.local == 0;
+    bits_tile<2, kBitsFusedRG>(
+        StagePlanesQuant<2>{d.x, d.K, first ? d.q : nullptr, first ? d.s_x : nullptr, &s_lds, qred}, &s_lds,
+        d.packed, d.s_w, d.N, d.K, (int)e.local * (4 * 8 * kBitsFusedRG), 1, d.y, d.acc, lds, &sq, red);
+}
+
+uint32_t bits_fused_rows_per_block() { return 4 * 8 * kBitsFusedRG; }
+uint32_t bits_fused_lds_bytes(int64_t K) { return (uint32_t)((K / BitsFmt<2>::V) * BitsFmt<2>::SD * 4); }
+
+hipError_t launch_bits_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st) {
+    gemv_bits_fused_grouped_kernel<<<dim3(blocks), dim3(256), lds_bytes, st>>>(
+        reinterpret_cast<const uint8_t *>(plan_dev));
+    return hipGetLastError();
 }
 
 // Longest K whose staged planes fit 63 KiB of LDS (the kernel's own arrays beside them).

@@ -836,10 +836,17 @@ static hipError_t launch_lds(const int8_t *q, const float *s_x, const uint8_t *p
     return hipGetLastError();
 }
 
+constexpr int64_t kGemvTallN = 16384;
+
 template <bool GRP>
 static hipError_t launch_gemv_mt(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                                  int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st) {
     const bool d8 = BITNET_GROUPED_DOT8 != 0;
+    // one token: 4 rows per octet for tall matrices (fewer LDS reads and less loop
+    // work per weight), BITNET_GEMV1_RG otherwise (more workgroups for a small N) and
+    // with group scales (whose tile needs more registers per row)
+    if (!GRP && M == 1 && N >= kGemvTallN)
+        return launch_lds<1, 4, d8, GRP>(q, s_x, packed, s_w, M, N, K, y, acc, st);
     if (M == 1) return launch_lds<1, BITNET_GEMV1_RG, d8, GRP>(q, s_x, packed, s_w, M, N, K, y, acc, st);
     if (M == 2) return launch_lds<2, 2, d8, GRP>(q, s_x, packed, s_w, M, N, K, y, acc, st);
     if (M <= 4) return launch_lds<4, 2, d8, GRP>(q, s_x, packed, s_w, M, N, K, y, acc, st);

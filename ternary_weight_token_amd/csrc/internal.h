@@ -38,6 +38,8 @@ constexpr uint32_t kVariantGemvGroups = 2;
 // RMSNorm; fp32 input rows or gate / up pairs, the two ends of SwiGLU); each mask
 // has its own kernel, so a plan without them takes the kernel without that code.
 constexpr uint32_t kFusedProNorm = 1, kFusedProSwiglu = 2, kFusedProMask = 3;
+// a fused plan over bitplane weights (plain rows only) has this variant instead
+constexpr uint32_t kFusedBitplanes = 4;
 
 struct PlanHeader {            // 64 bytes
     uint32_t magic, kind, count, total_blocks;
@@ -82,6 +84,9 @@ hipError_t launch_weight_scale(const float *w, int64_t N, int64_t K, float *s_w,
 hipError_t launch_pack_binary(const float *w, int64_t N, int64_t K, uint8_t *bits, hipStream_t st);
 hipError_t launch_pack_bitplanes(const uint8_t *packed, int64_t N, int64_t K, uint8_t *planes, hipStream_t st);
 int64_t bits_max_k(int fmt);
+uint32_t bits_fused_rows_per_block();
+uint32_t bits_fused_lds_bytes(int64_t K);
+hipError_t launch_bits_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st);
 bool bits_fast_ok(int fmt, int64_t M, int64_t K, const void *q, const void *wbits);
 hipError_t launch_linear_bits(const int8_t *q, const float *s_x, const uint8_t *wbits, int fmt, const float *s_w,
                               int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, int kernel, hipStream_t st);

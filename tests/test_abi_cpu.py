@@ -307,6 +307,32 @@ def test_bit_encodings_reject_bad_arguments(L):
     assert lb(p, p, p, 1, p, 0, 8, 128, p, z, 0, z) == OK
 
 
+def test_fused_plan_bitplanes(L):
+    F = tw._FusedDesc
+    a16 = 4096
+    n = ctypes.c_float
+    arr = (F * 2)(F(a16, a16, a16, a16, 0, 0, 0, 1, 2560, 6912, 0, n(0.0), 0, 0, 0, 2),
+                  F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, 0, n(0.0), 0, 0, 0, 2))
+    nb = L.bitnet_grouped_plan_fused_bytes(2, arr)
+    buf = ctypes.create_string_buffer(nb)
+    assert L.bitnet_grouped_plan_fused(arr, 2, buf, nb) == OK
+    hdr = (ctypes.c_uint32 * 8).from_buffer_copy(buf.raw[:32])
+    assert hdr[7] == 4 and hdr[3] == -(-2560 // hdr[5]) - (-300 // hdr[5])
+    bad = [
+        (F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, 0, n(0.0), 0, 0, 0, 1), ARG),          # binary: not here
+        (F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, a16, n(1e-6), 0, 0, 0, 2), ARG),       # no norm
+        (F(0, a16, a16, a16, 0, 0, 0, 1, 300, 2560, 0, n(0.0), a16, 0, 0, 2), ARG),          # no fp32 row
+        (F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, 0, n(0.0), 0, a16, a16, 2), ARG),      # no pair
+        (F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 51584 + 64, 0, n(0.0), 0, 0, 0, 2), SHAPE),  # LDS limit
+    ]
+    for d, want in bad:
+        one = (F * 1)(d)
+        assert L.bitnet_grouped_plan_fused(one, 1, buf, nb) == want
+    mixed = (F * 2)(F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, 0, n(0.0), 0, 0, 0, 2),
+                    F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, 0, n(0.0), 0, 0, 0, 0))
+    assert L.bitnet_grouped_plan_fused(mixed, 2, buf, nb) == ARG
+
+
 def test_linear_plan_weight_groups(L):
     D = tw._LinearDesc
     a16 = 4096

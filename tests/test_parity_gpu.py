@@ -189,7 +189,8 @@ def test_gemv_parity_all_m(M):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 6912), (1, 33, 28672), (4, 640, 2560), (16, 1000, 8192),
-                                   (1, 1, 64), (2, 7, 128)])
+                                   (1, 1, 64), (2, 7, 128),
+                                   (1, 16400, 2560), (1, 16384, 8192)])   # tall: 4 rows per octet
 def test_gemv_parity_shapes(M, N, K):
     key = synth.stream_key(301, M, N, K)
     x, q, s = quantized_inputs(key, M, K)
@@ -282,6 +283,7 @@ def _grouped_bound(q, s_x, packed, s_w, G, K):
     (1, 1, 300, 2560, 128), (1, 3, 70, 6912, 128), (1, 9, 33, 640, 64), (0, 1, 640, 2560, 128),
     (0, 20, 129, 2560, 256), (3, 4, 33, 132, 44), (0, 2, 50, 2560 + 4, 4),             # group-wise
     (1, 1, 200, 53312, 64), (1, 2, 100, 53248, 128),                                   # K in segments
+    (1, 1, 16400, 640, 128), (0, 1, 16400, 640, 640),                                  # tall, one token
 ])
 @pytest.mark.parametrize("opts", ["plain", "bias_bf16"])
 def test_linear_weight_scale_groups(kernel, M, N, K, G, opts):
@@ -656,6 +658,43 @@ def test_linear_bits_longest_k(fmt, K, N):
     torch.cuda.synchronize()
     assert np.array_equal(acc.cpu().numpy(), acc_ref)
     assert_y(y.cpu().numpy(), y_ref)
+
+
+@pytest.mark.parametrize("with_outputs", [True, False])
+def test_fused_bitplanes_grouped(with_outputs):
+    """The fused decode plan over bitplane weights against the oracle's quant_act +
+    linear of the same 2-bit codes: ragged N, K from one slot to the longest bitplane
+    K, an all-zero row, outliers."""
+    shapes = [(2560, 6912, {}), (300, 2560, {"outlier_frac": 0.01}), (129, 51584, {}), (64, 64, {}),
+              (700, 8192, {"row_scale": (1e-3, 1e-3)}), (33, 2560, "zero"), (1, 128, {})]
+    probs, refs = [], []
+    for i, (N, K, kw) in enumerate(shapes):
+        key = synth.stream_key(355, i)
+        x = torch.zeros((1, K), dtype=torch.bfloat16) if kw == "zero" else synth.activations(key, 1, K, **kw)
+        w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02).numpy()
+        packed, s_w = oracle.pack(w)
+        q_ref, sx_ref = oracle.quant_act(bits_np(x))
+        acc_ref, y_ref = oracle.linear(q_ref, sx_ref, packed, s_w)
+        refs.append((q_ref, sx_ref, acc_ref, y_ref))
+        planes = torch.from_numpy(oracle.pack_bitplanes(packed, K)).to(DEV)
+        y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+        acc = torch.empty((1, N), dtype=torch.int32, device=DEV)
+        q = torch.full((1, K), 99, dtype=torch.int8, device=DEV) if with_outputs else None
+        sx = torch.full((1,), -1.0, dtype=torch.float32, device=DEV) if with_outputs else None
+        probs.append((x.to(DEV), planes, torch.tensor([s_w], device=DEV), y, acc, q, sx))
+    plan = tw.bitnet_grouped_plan_fused(probs)
+    for _ in range(2):
+        for pr in probs:
+            pr[3].fill_(float("nan"))
+            pr[4].fill_(-1)
+        plan.launch()
+        torch.cuda.synchronize()
+        for (q_ref, sx_ref, acc_ref, y_ref), pr in zip(refs, probs):
+            assert np.array_equal(pr[4].cpu().numpy(), acc_ref)
+            assert_y(pr[3].cpu().numpy(), y_ref)
+            if with_outputs:
+                assert np.array_equal(pr[5].cpu().numpy(), q_ref)
+                assert np.array_equal(pr[6].cpu().numpy(), sx_ref)
 
 
 def test_bitplanes_equal_two_bit_codes_on_gpu():
