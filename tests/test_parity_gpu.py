@@ -910,7 +910,20 @@ def test_empty_problems_are_noops():
     y2 = torch.full((3, 0), 1.0, device=DEV)
     tw.bitnet_linear(torch.zeros((3, 64), dtype=torch.int8, device=DEV), torch.zeros(3, device=DEV),
                      torch.zeros((0, 16), dtype=torch.uint8, device=DEV), torch.zeros(1, device=DEV), y2)
+    # the same for the other entry points: nothing is launched, nothing is written
+    q, s = tw.swiglu_quant(torch.empty((0, 64), device=DEV), torch.empty((0, 64), device=DEV))
+    assert q.shape == (0, 64) and s.shape == (0,)
+    q, s = tw.rmsnorm_quant(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV), torch.ones(64, device=DEV), 1e-6)
+    for fmt, wb in ((tw.FMT_BINARY, torch.zeros((5, 16), dtype=torch.uint8, device=DEV)),
+                    (tw.FMT_BITPLANES, torch.zeros((5, 4, 8), dtype=torch.uint8, device=DEV))):
+        y3 = tw.linear_bits(torch.empty((0, 128), dtype=torch.int8, device=DEV), torch.empty(0, device=DEV), wb, fmt,
+                            torch.zeros(1, device=DEV))
+        assert y3.shape == (0, 5)
+    planes = tw.pack_bitplanes(torch.zeros((0, 32), dtype=torch.uint8, device=DEV), 128)
+    assert planes.shape == (0, 4, 8)
+    bits, s_w = tw.pack_weights_binary(torch.empty((0, 128), device=DEV))
     torch.cuda.synchronize()
+    assert bits.shape == (0, 16) and s_w.item() == 0.0
 
 
 def test_determinism():
