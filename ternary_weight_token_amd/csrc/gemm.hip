@@ -6,12 +6,10 @@
 // so the block tile is BM = 16 WM TM rows by BN = 16 WN TN columns, chosen per
 // shape so that the tile count matches the 256 compute units (e.g. 256 x 224 for
 // N = 6912, 256 x 80 for N = 2560).  K advances 64 per step:
-//  * the A (q) tile BM x 64 int8 is staged in LDS with each 16-byte piece
-//    byte-transposed into the order the code expansion produces;
+//  * the A (q) tile BM x 64 int8 is copied to LDS as it is;
 //  * the B tile is loaded packed (16 bytes per row and step) and expanded once per
-//    workgroup to int8 codes c = t + 1 in LDS (shift + mask, 7 VALU ops per 16
-//    weights); sum_k q t = sum_k q c - sum_k q, where sum_k q is accumulated per
-//    row while staging A;
+//    workgroup to the signed ternary weights t = c - 1 as int8, in k order, in LDS
+//    (ternary4: 5 VALU ops per 4 weights);
 //  * LDS is double-buffered: the global loads of step s + 1 are in flight while
 //    the MFMAs of step s run; one barrier per step;
 //  * both operands assign the same k to the same (lane, byte) position, which is
@@ -52,6 +50,21 @@ __device__ __forceinline__ void store_y_stream(const OutSpec &out, size_t o, dou
     else __builtin_nontemporal_store((float)v, reinterpret_cast<float *>(out.y) + o);
 }
 
+// The 4 weights of one packed byte (k = 4j + i in bits 2i..2i+1) as 4 signed int8
+// t = c - 1 in k order: spread the byte so that byte i of a dword holds code i in
+// its low two bits, then map each code through a 4-entry byte table with one byte
+// permute (0 -> -1, 1 -> 0, 2 -> +1, 3 -> +2).
+__device__ __forceinline__ uint32_t ternary4(uint32_t byte) {
+    uint32_t sp = byte | (byte << 6);
+    sp = (sp | (sp << 12)) & 0x03030303u;
+    return __builtin_amdgcn_perm(0u, 0x020100FFu, sp);
+}
+
+// 16 packed weights (one dword) as 16 int8 weights in k order.
+__device__ __forceinline__ uint4 ternary16(uint32_t w) {
+    return make_uint4(ternary4(w & 0xFFu), ternary4((w >> 8) & 0xFFu), ternary4((w >> 16) & 0xFFu), ternary4(w >> 24));
+}
+
 __device__ __forceinline__ uint4 gld16(const void *p) {
     const v4u_g v = *(gv4u_g *)p;
     return make_uint4(v.x, v.y, v.z, v.w);
@@ -79,7 +92,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
     constexpr int RSB = BPACK ? 16 * KS + 4 : RS;
     __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * RS];
     __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * RSB];
-    __shared__ int rowsum[BM];
     __shared__ double rowscale[BM];
 
     // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; give each
@@ -104,9 +116,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
 
     // staging: A piece p = tid + NT * i -> row p / CPR, piece p % CPR (CPR
     // consecutive threads cover a row's BK bytes); B piece p -> row p / KS, part p % KS.
-    int a_sum[A_PER_T];
-    #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) a_sum[i] = 0;
 
     uint4 ra[A_PER_T], rb[B_PER_T];
     auto load_step = [&](int s) {
@@ -133,14 +142,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
             const int p = tid + NT * i;
             if (p < A_PIECES) {
                 const int row = p / CPR, ch = p % CPR;
-                const uint4 v = ra[i];
-                uint4 o;
-                transpose4x4(v.x, v.y, v.z, v.w, o.x, o.y, o.z, o.w);
-                *reinterpret_cast<uint4 *>(&As[buf][row * RS + 16 * ch]) = o;
-                int sm = dot4(v.x, 0x01010101u, a_sum[i]);
-                sm = dot4(v.y, 0x01010101u, sm);
-                sm = dot4(v.z, 0x01010101u, sm);
-                a_sum[i] = dot4(v.w, 0x01010101u, sm);
+                *reinterpret_cast<uint4 *>(&As[buf][row * RS + 16 * ch]) = ra[i];
             }
         }
         #pragma unroll
@@ -154,11 +156,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
                     dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2]; dst[3] = w[3];
                 } else {
                     #pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        const uint4 o = make_uint4(codes_i(w[d], 0), codes_i(w[d], 1), codes_i(w[d], 2),
-                                                   codes_i(w[d], 3));
-                        *reinterpret_cast<uint4 *>(&Bs[buf][r * RS + 64 * part + 16 * d]) = o;
-                    }
+                    for (int d = 0; d < 4; ++d)
+                        *reinterpret_cast<uint4 *>(&Bs[buf][r * RS + 64 * part + 16 * d]) = ternary16(w[d]);
                 }
             }
         }
@@ -188,7 +187,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
                 if (BPACK) {
                     const uint32_t w = *reinterpret_cast<const uint32_t *>(
                         &Bs[buf][(wn * TN * 16 + j * 16 + l16) * RSB + 16 * u + 4 * g]);
-                    b[j] = v4i{(int)codes_i(w, 0), (int)codes_i(w, 1), (int)codes_i(w, 2), (int)codes_i(w, 3)};
+                    const uint4 e = ternary16(w);
+                    b[j] = v4i{(int)e.x, (int)e.y, (int)e.z, (int)e.w};
                 } else {
                     b[j] = *reinterpret_cast<const v4i *>(&Bs[buf][(wn * TN * 16 + j * 16 + l16) * RS + 64 * u + 16 * g]);
                 }
@@ -203,20 +203,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
         __syncthreads();
     }
 
-    // row sums of q (CPR threads per row) and per-row rescale factors
+    // per-row rescale factors
     const float sw = *s_w;
-    #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-        int v = a_sum[i];
-        #pragma unroll
-        for (int o = 1; o < CPR; o <<= 1) v += __shfl_xor(v, o, 64);
-        const int p = tid + NT * i;
-        if (p < A_PIECES && (p % CPR) == 0) {
-            const int row = p / CPR;
-            rowsum[row] = v;
-            const int gm = m_base + row;
-            rowscale[row] = gm < M ? rescale_factor(s_x[gm], sw) : 0.0;
-        }
+    for (int row = tid; row < BM; row += NT) {
+        const int gm = m_base + row;
+        rowscale[row] = gm < M ? rescale_factor(s_x[gm], sw) : 0.0;
     }
     __syncthreads();
 
@@ -235,7 +226,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
             const int lr = wm * TM * 16 + i * 16 + 4 * g + r;
             const int row = m_base + lr;
             if (row >= M) continue;
-            const int sq = rowsum[lr];
             const double cm = rowscale[lr];
             const float sxr = out.w_group ? s_x[row] : 0.0f;
             #pragma unroll
@@ -243,7 +233,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
                 const int col = n_base + wn * TN * 16 + j * 16 + l16;
                 if (col < N) {
                     const size_t o = (size_t)row * N + col;
-                    const int v = acc[i][j][r] - sq;
+                    const int v = acc[i][j][r];
                     double yv = (double)v * col_factor(out, s_w, col, sxr, cm);
                     if (out.bias) yv += (double)bcol[j];
                     store_y_stream(out, o, yv);
