@@ -309,12 +309,12 @@ BITNET_API int bitnet_quant_act_grouped(const void *plan_host, const void *plan_
 /* ---------------------------------------------------------------------------
  * Other weight encodings of the same product.
  *
- * BITNET_FMT_BINARY: b1.0 binary weights {-1, +1} (page chenxutan.com sec. 1: the
- * first BitNet's weights are binary, no zero).  bits (device) uint8 [N][K/8]:
+ * BITNET_FMT_BINARY: b1.0 binary weights {-1, +1} (page chenxutan.com sec. 1 and
+ * the b1.0 paragraph of sec. 2.1: the first BitNet's weights are binary, no zero).  bits (device) uint8 [N][K/8]:
  * weight k of row n is bit k % 8 of byte k / 8 (LSB first), set for +1.
- * BITNET_FMT_BITPLANES: the ternary weights as sign / mask bitplanes (page
- * sns.style "1-bit LLM ..." sec. on ternary weights: bitnet_linear over
- * weight_sign and weight_mask).  planes (device) uint8 [N][K/32][8]: per 32
+ * BITNET_FMT_BITPLANES: the ternary weights as sign / mask bitplanes (the
+ * untitled devpress.csdn.net summary on Microsoft's open BitNet framework, sec.
+ * "三值量化：把乘法变成加减法": bitnet_linear over weight_sign and weight_mask).  planes (device) uint8 [N][K/32][8]: per 32
  * weights a little-endian mask word (bit i set: weight 32 c + i nonzero) then a
  * sign word (bit i set: -1; clear for zero weights).
  * ------------------------------------------------------------------------- */

@@ -17,6 +17,9 @@
  *       sec. 2.2 (absmean / absmax quantization), sec. 2.3 (rescale with the
  *       two scale factors), sec. 3.1 (BitLinear.forward), sec. 3.3 (INT2
  *       packing, 4 weights per byte, code = w + 1, LSB first).
+ *  [P3] untitled summary of Microsoft's open BitNet framework (devpress.csdn.net),
+ *       sec. "三值量化：把乘法变成加减法" (bitnet_linear over weight_sign and
+ *       weight_mask: the sign / mask bitplanes).
  *  [P5] "1-bit推理框架bitnet.cpp实测……" (0539edu.com), sec. 2.1
  *       (RoundClip(w / scale, -1, 1), scale = mean|w|).
  *
@@ -360,7 +363,7 @@ void oracle_linear(const int8_t *q, const float *s_x, const uint8_t *packed,
 
 /* --- other weight encodings: b1.0 binary weights, sign / mask bitplanes --- */
 
-/* Binary weights ([P1] 1 and its b1.0 paragraph: the first BitNet's weights are
+/* Binary weights ([P1] 1 and the b1.0 paragraph of 2.1: the first BitNet's weights are
  * {-1, +1}, no zero).  The pages give no binarization rule; here t = +1 for
  * w >= 0 (either zero) and -1 for w < 0, with the same absmean scale s_w as the
  * ternary weights (oracle_weight_scale; mean |w| is also the scale that best fits

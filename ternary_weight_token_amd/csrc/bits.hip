@@ -1,9 +1,9 @@
 // Other encodings of the weights of the same product, each with its own packer and
 // contraction:
-//  - b1.0 binary weights {-1, +1} (page chenxutan.com sec. 1: the first BitNet,
-//    no zero), one bit per weight, bit set for +1, LSB first; the scale is the same
+//  - b1.0 binary weights {-1, +1} (page chenxutan.com sec. 1 and the b1.0 paragraph
+//    of sec. 2.1: the first BitNet, no zero), one bit per weight, bit set for +1, LSB first; the scale is the same
 //    absmean s_w as for ternary weights;
-//  - sign / mask bitplanes (page sns.style "1-bit LLM ..." sec. on ternary weights:
+//  - sign / mask bitplanes (page devpress.csdn.net, sec. "三值量化：把乘法变成加减法":
 //    bitnet_linear over weight_sign and weight_mask): per 32 weights a mask word
 //    (bit set: nonzero) and a sign word (bit set: -1), converted from the 2-bit
 //    codes.
