@@ -106,6 +106,8 @@ uint32_t gemv_grouped_rows_per_block();
 uint32_t gemv_fused_rows_per_block();
 uint32_t gemv_fused_threads();
 uint32_t gemv_grouped_threads();
+double skinny_estimate_us(int64_t M, int64_t N, int64_t K);
+double gemm_estimate_us(int64_t M, int64_t N, int64_t K);
 hipError_t launch_skinny(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                          int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st);
 hipError_t launch_skinny_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st);

@@ -212,6 +212,16 @@ static void launch_rg(const int8_t *q, const float *s_x, const uint8_t *packed, 
                                                                           (int)K, y, acc, ks);
 }
 
+// Estimated time (us) of launch_skinny: the first 16 tokens stream the weights at
+// about 3.5 TB/s plus 5 us; each further 16-token tile (a concurrent re-read of the
+// weights) adds about W / 4 TB/s + 1.8 us (measured on M = 16 .. 256 against six
+// shapes from 2560 x 2560 to 8192 x 28672).
+double skinny_estimate_us(int64_t M, int64_t N, int64_t K) {
+    const double w = (double)N * (double)K / 4.0;   // packed bytes
+    const int64_t tiles = (M + 15) / 16;
+    return w / 3.5e6 + 5.0 + (double)(tiles - 1) * (w / 4.0e6 + 1.8);
+}
+
 hipError_t launch_skinny(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                          int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st) {
     // Rows per wavefront (16 RG) against parallelism: the largest RG whose launch,

@@ -761,10 +761,30 @@ def test_grouped_linear_mixed_k(shapes):
 @pytest.mark.parametrize("M,N,K", [(17, 129, 256), (32, 300, 2560), (64, 6912, 2560), (130, 257, 640),
                                    (200, 96, 6912), (2048, 384, 2560)])
 def test_gemm_parity(M, N, K):
+    """The MFMA GEMM, forced (the automatic choice takes the MFMA decode kernel for
+    some of these shapes)."""
     key = synth.stream_key(302, M, N, K)
     x, q, s = quantized_inputs(key, M, K, row_scale=(0.1, 10.0))
     packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
-    check_linear(q, s, packed, np.float32(0.0071))
+    acc_ref, y_ref = oracle.linear(q, s, packed, np.float32(0.0071))
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    tw.bitnet_linear_select(torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV),
+                            torch.from_numpy(packed).to(DEV), torch.tensor([0.0071], device=DEV), y, acc, 2)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    assert_y(y.cpu().numpy(), y_ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 2560, 2560), (48, 640, 6912), (96, 300, 2560), (130, 257, 640),
+                                   (256, 2560, 6912), (256, 6912, 2560)])
+def test_linear_auto_dispatch_beyond_16_tokens(M, N, K):
+    """bitnet_linear's own choice between the MFMA decode kernel and the GEMM for
+    M > 16 (an estimate of each): parity whichever it takes."""
+    key = synth.stream_key(309, M, N, K)
+    x, q, s = quantized_inputs(key, M, K, row_scale=(0.1, 10.0))
+    packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
+    check_linear(q, s, packed, np.float32(0.0093))
 
 
 @pytest.mark.parametrize("cfg", range(5))
@@ -956,7 +976,7 @@ def test_end_to_end_single_gemv():
 
 @pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 32, 64])
 def test_batched_decode_sweep(M):
-    """K = 2560, N = 6912 with M tokens (GEMV up to 16, MFMA GEMM beyond)."""
+    """K = 2560, N = 6912 with M tokens, through the automatic kernel choice."""
     x = W.sweep_activations(M)
     w = W.sweep_weights()
     p_ref, sw_ref = oracle.pack(w.numpy(), 1e-5)
