@@ -343,11 +343,11 @@ def main() -> int:
             # per call, device time (graph-captured)
             p, s = tw.pack_weights(W.sweep_weights(dev), 1e-5)
             sweep = {}
-            for M in (1, 2, 4, 8, 16, 32, 64):
+            for M in (1, 2, 4, 8, 16, 32, 64, 128, 256):
                 q, sx = tw.quant_act(W.sweep_activations(M, dev))
                 y = torch.empty((M, p.shape[0]), dtype=torch.float32, device=dev)
                 row = {}
-                for kname, kid in (("gemv", 1), ("mfma_decode", 4), ("gemm", 2)):
+                for kname, kid in (("gemv", 1), ("mfma_decode", 4), ("gemm", 2), ("auto", 0)):
                     us = graph_us(torch, lambda: tw.bitnet_linear_select(q, sx, p, s, y, None, kid))
                     row[kname] = {"us": round(us, 2), "weight_GBs": round(p.numel() / (us * 1e-6) / 1e9, 1)}
                 sweep[f"M{M}"] = row
