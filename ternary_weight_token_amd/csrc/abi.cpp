@@ -212,12 +212,18 @@ BITNET_API int bitnet_linear_ex(const int8_t *q, const float *s_x, const uint8_t
         return hip_status(launch_linear_generic(q, s_x, packed, s_w, M, N, K, out, acc, s));
     if (!fast)
         return fail(BITNET_ERR_ALIGN, "kernel needs K % 64 == 0, 16-byte aligned q/packed (and w_group % 64 == 0)");
-    // one token: the GEMV; up to 16: the MFMA decode kernel; beyond, whichever of the
-    // MFMA decode kernel (one 16-token tile per pass over the weights) and the GEMM
-    // (few tiles, each walking all of K, when M and N are small) is estimated faster
-    if (kernel == 0)
-        kernel = (M == 1 || groups) ? 1
-                 : (M <= kGemvMaxM || skinny_estimate_us(M, N, K) <= gemm_estimate_us(M, N, K)) ? 4 : 2;
+    // one token: the GEMV, except below 32 MB of packed weights, where the MFMA decode
+    // kernel's shorter critical path wins (0.4 .. 17 MB: 4.3 .. 6.2 us against 5.6 ..
+    // 7.3 us; from 58.7 MB on the GEMV streams faster); up to 16 tokens: the MFMA decode
+    // kernel; beyond, whichever of the MFMA decode kernel (one 16-token tile per pass
+    // over the weights) and the GEMM (few tiles, each walking all of K, when M and N are
+    // small) is estimated faster; group-wise scales: the GEMV
+    if (kernel == 0) {
+        const bool small = N * (K / 4) < ((int64_t)32 << 20);
+        if (groups || (M == 1 && !small)) kernel = 1;
+        else if (M <= kGemvMaxM || skinny_estimate_us(M, N, K) <= gemm_estimate_us(M, N, K)) kernel = 4;
+        else kernel = 2;
+    }
     if (kernel == 1) return hip_status(launch_gemv(q, s_x, packed, s_w, M, N, K, out, acc, s));
     if (kernel == 4) return hip_status(launch_skinny(q, s_x, packed, s_w, M, N, K, out, acc, s));
     if (forced_tile) return hip_status(launch_gemm_cfg(kernel - 16, q, s_x, packed, s_w, M, N, K, out, acc, s));

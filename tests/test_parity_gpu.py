@@ -52,20 +52,27 @@ def gpu_quant(x_cpu):
     return q.cpu().numpy(), s.cpu().numpy()
 
 
-def gpu_linear(q_np, s_np, packed_np, s_w, want_acc=True):
+def gpu_linear(q_np, s_np, packed_np, s_w, want_acc=True, kernel=0):
+    """kernel 0: bitnet_linear's own choice; else forced (1 GEMV, 2 GEMM, 4 MFMA decode)."""
     q = torch.from_numpy(q_np).to(DEV)
     s = torch.from_numpy(s_np).to(DEV)
     p = torch.from_numpy(packed_np).to(DEV)
     sw = torch.tensor([s_w], dtype=torch.float32, device=DEV)
-    y, acc = tw.linear(q, s, p, sw, want_acc=True)
+    if kernel == 0:
+        y, acc = tw.linear(q, s, p, sw, want_acc=True)
+    else:
+        y = torch.empty((q.shape[0], p.shape[0]), dtype=torch.float32, device=DEV)
+        acc = torch.empty((q.shape[0], p.shape[0]), dtype=torch.int32, device=DEV)
+        tw.bitnet_linear_select(q, s, p, sw, y, acc, kernel)
     return y.cpu().numpy(), acc.cpu().numpy()
 
 
-def check_linear(q_np, s_np, packed_np, s_w):
+def check_linear(q_np, s_np, packed_np, s_w, kernels=(0,)):
     acc_ref, y_ref = oracle.linear(q_np, s_np, packed_np, s_w)
-    y, acc = gpu_linear(q_np, s_np, packed_np, s_w)
-    assert np.array_equal(acc, acc_ref)
-    assert_y(y, y_ref)
+    for kern in kernels:
+        y, acc = gpu_linear(q_np, s_np, packed_np, s_w, kernel=kern)
+        assert np.array_equal(acc, acc_ref), kern
+        assert_y(y, y_ref)
     return acc, y
 
 
@@ -185,7 +192,7 @@ def test_gemv_parity_all_m(M):
     key = synth.stream_key(300, M)
     x, q, s = quantized_inputs(key, M, K, outlier_frac=0.001)
     packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
-    check_linear(q, s, packed, np.float32(0.0113))
+    check_linear(q, s, packed, np.float32(0.0113), kernels=(0, 1))
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 6912), (1, 33, 28672), (4, 640, 2560), (16, 1000, 8192),
@@ -196,7 +203,7 @@ def test_gemv_parity_shapes(M, N, K):
     x, q, s = quantized_inputs(key, M, K)
     w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02)
     packed, s_w = oracle.pack(w.numpy())
-    check_linear(q, s, packed, s_w)
+    check_linear(q, s, packed, s_w, kernels=(0, 1))
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 300, 2624), (2, 70, 26176), (3, 200, 64), (5, 33, 8192),
@@ -721,7 +728,7 @@ def test_gemv_parity_k_segments(M, N, K):
     x, q, s = quantized_inputs(key, M, K)
     w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02)
     packed, s_w = oracle.pack(w.numpy())
-    check_linear(q, s, packed, s_w)
+    check_linear(q, s, packed, s_w, kernels=(0, 1))
 
 
 @pytest.mark.parametrize("shapes", [
