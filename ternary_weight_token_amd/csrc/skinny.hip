@@ -256,10 +256,15 @@ hipError_t launch_skinny(const int8_t *q, const float *s_x, const uint8_t *packe
 // decode-step shape up to 12 tokens; one barrier pair per segment.
 constexpr int kSkLdsBudget = 64 * 1024;
 
+// A staged chunk takes 64 M bytes of q plus 16 bytes of padding: the threads that
+// stage consecutive chunks (and the lane groups that read them) then fall 4 banks
+// apart instead of on the same banks.
+__host__ __device__ __forceinline__ int sk_chunk_dw(int M) { return 16 * M + 4; }
+
 // Segment length in 64-weight chunks for M tokens: all of K if its staged q fits the
 // budget, else the fewest equal segments, each a multiple of 8 chunks (one step).
 __host__ __device__ __forceinline__ int sk_segment_chunks(int C, int M) {
-    const int max_seg = (kSkLdsBudget / (64 * M)) & ~7;
+    const int max_seg = (kSkLdsBudget / (4 * sk_chunk_dw(M))) & ~7;
     if (C <= max_seg) return C;
     const int nseg = (C + max_seg - 1) / max_seg;
     return (((C + nseg - 1) / nseg) + 7) & ~7;
@@ -312,7 +317,7 @@ __device__ __forceinline__ void skinny_lds_tile(const int8_t *__restrict__ q, co
             for (int u = 0; u < UN; ++u) {
                 const int cl = 4 * UN * t + 4 * u + g;
                 const bool valid = cl < sc;
-                const uint32_t *src = qs + ((min(cl, sc - 1) * 4) * M + tok) * 4;
+                const uint32_t *src = qs + min(cl, sc - 1) * sk_chunk_dw(M) + tok * 4;
                 uint32_t wm[RG][4];
                 #pragma unroll
                 for (int rg = 0; rg < RG; ++rg) {
@@ -356,7 +361,8 @@ __device__ __forceinline__ void skinny_lds_tile(const int8_t *__restrict__ q, co
             }
             #pragma unroll
             for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<uint4 *>(qs + ((c * 4 + i) * M + m) * 4) = make_uint4(P[i][0], P[i][1], P[i][2], P[i][3]);
+                *reinterpret_cast<uint4 *>(qs + c * sk_chunk_dw(M) + (i * M + m) * 4) =
+                    make_uint4(P[i][0], P[i][1], P[i][2], P[i][3]);
             if (sm != 0) atomicAdd(&sq[m], sm);
         }
         __syncthreads();
@@ -415,7 +421,7 @@ __global__ __launch_bounds__(64 * kGroupedSkNW) void skinny_grouped_kernel(const
 
 uint32_t skinny_grouped_rows_per_block() { return kGroupedSkNW * 16 * kGroupedSkRG; }
 uint32_t skinny_grouped_lds_bytes(int64_t M, int64_t K) {
-    return (uint32_t)(sk_segment_chunks((int)(K / 64), (int)M) * 64 * M);
+    return (uint32_t)(sk_segment_chunks((int)(K / 64), (int)M) * sk_chunk_dw((int)M) * 4);
 }
 
 hipError_t launch_skinny_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st) {
