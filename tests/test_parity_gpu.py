@@ -823,6 +823,44 @@ def _epilogue_tolerance(acc_ref, s, s_w, bias):
     return 2.0 ** -45 * (P + b)
 
 
+@pytest.mark.parametrize("cfg", [2, 16, 17, 18, 19, 20])
+@pytest.mark.parametrize("M,N,K,with_bias", [(257, 225, 640, False), (300, 500, 640, True),
+                                             (130, 258, 6912 - 64, True), (2048, 384, 2560, False)])
+def test_gemm_output_without_acc(cfg, M, N, K, with_bias):
+    """The GEMM's output written without the int32 accumulators (the output rows are
+    then staged through LDS and stored as whole row segments): fp32 bit-identical to
+    the same call that also returns acc and within the bound of the oracle; bf16 equal
+    to that fp32 result rounded to nearest even; N not a multiple of 4, or y only
+    4-byte aligned, takes the element-wise stores."""
+    key = synth.stream_key(313, cfg, M, N, K)
+    x, q, s = quantized_inputs(key, M, K, row_scale=(0.1, 10.0))
+    packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
+    s_w = np.float32(0.0081)
+    bias = None
+    if with_bias:
+        bias = synth.activations(synth.stream_key(key, 2), 1, N).float().numpy()[0] * np.float32(3.0)
+    acc_ref, y_ref = oracle.linear(q, s, packed, s_w, bias=bias)
+    args = (torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV), torch.from_numpy(packed).to(DEV),
+            torch.tensor([s_w], device=DEV), None if bias is None else torch.from_numpy(bias).to(DEV))
+    y_acc = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    tw.bitnet_linear_ex(*args, y_acc, acc, cfg)
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    want32 = y_acc.cpu()
+    d = np.abs(want32.numpy().astype(np.float64) - y_ref.astype(np.float64))
+    bad = d > REL * np.abs(y_ref.astype(np.float64)) + _epilogue_tolerance(acc_ref, s, s_w, bias)
+    assert not bad.any(), f"{bad.sum()} fp32 outputs outside the bound"
+    for dtype in (torch.float32, torch.bfloat16):
+        for offset in (0, 4 // dtype.itemsize):     # y 4 bytes past an aligned address
+            buf = torch.full((M * N + offset,), float("nan"), dtype=dtype, device=DEV)
+            y = buf[offset:].view(M, N)
+            tw.bitnet_linear_ex(*args, y, None, cfg)
+            got = y.cpu()
+            want = want32 if dtype == torch.float32 else want32.to(torch.bfloat16)
+            assert torch.equal(got.view(torch.int16 if dtype == torch.bfloat16 else torch.int32),
+                               want.view(torch.int16 if dtype == torch.bfloat16 else torch.int32)), (dtype, offset)
+
+
 @pytest.mark.parametrize("kernel,M,N,K", [
     (1, 1, 300, 2560), (1, 3, 70, 6912), (1, 9, 33, 640),             # decode GEMV
     (4, 2, 300, 2624), (4, 16, 129, 2560), (4, 20, 70, 640),           # MFMA decode
