@@ -27,6 +27,15 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u_g __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const v4u_g gv4u_g;
 
+#ifndef BITNET_GEMM_SCHED
+#define BITNET_GEMM_SCHED 1
+#endif
+#ifndef BITNET_GEMM_SCHED_VALU
+#define BITNET_GEMM_SCHED_VALU 2
+#endif
+#ifndef BITNET_GEMM_SCHED_WR
+#define BITNET_GEMM_SCHED_WR 2
+#endif
 #ifndef BITNET_GEMM_GROUP_M
 #define BITNET_GEMM_GROUP_M 8
 #endif
@@ -90,6 +99,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
     constexpr int A_PER_T = (A_PIECES + NT - 1) / NT;
     constexpr int B_PIECES = BN * KS;         // 16-byte packed pieces per step
     constexpr int B_PER_T = (B_PIECES + NT - 1) / NT;
+    // Clamped, branch-free staging (see load_step) only where nearly every thread has
+    // a B piece: elsewhere the repeated pieces cost more VALU and LDS time than the
+    // interleaving gains (256 x 80 tile: 65 -> 70 us on the down shape).
+    constexpr bool CLAMP = (B_PIECES % NT == 0) || 8 * (B_PIECES % NT) >= 7 * NT;
     // B in LDS: expanded int8 codes (row stride RS) or packed 2-bit codes (row
     // stride 16 KS + 4 bytes: 16 lanes reading one dword each hit distinct banks)
     constexpr int RSB = BPACK ? 16 * KS + 4 : RS;
@@ -127,38 +140,46 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
     // staging: A piece p = tid + NT * i -> row p / CPR, piece p % CPR (CPR
     // consecutive threads cover a row's BK bytes); B piece p -> row p / KS, part p % KS.
 
+    // With CLAMP, piece indices and rows are clamped instead of guarded, so that the
+    // loop body is one basic block the scheduler can interleave: threads past the
+    // last piece repeat it (same bytes to the same LDS address), A rows past M repeat
+    // row M - 1 and B rows past N repeat row N - 1 (they only feed outputs that are
+    // never stored).  Without it, missing pieces are skipped and rows past the end
+    // load zeros.
     uint4 ra[A_PER_T], rb[B_PER_T];
     auto load_step = [&](int s) {
         const int k0 = s * BK;
         #pragma unroll
         for (int i = 0; i < A_PER_T; ++i) {
-            const int p = tid + NT * i;
+            const int p = CLAMP ? min(tid + NT * i, A_PIECES - 1) : tid + NT * i;
             const int row = p / CPR, ch = p % CPR;
             const int gm = m_base + row;
-            ra[i] = (p < A_PIECES && gm < M) ? gld16(q + (size_t)gm * K + k0 + 16 * ch) : make_uint4(0u, 0u, 0u, 0u);
+            if (CLAMP) ra[i] = gld16(q + (size_t)min(gm, M - 1) * K + k0 + 16 * ch);
+            else ra[i] = (p < A_PIECES && gm < M) ? gld16(q + (size_t)gm * K + k0 + 16 * ch) : make_uint4(0u, 0u, 0u, 0u);
         }
         #pragma unroll
         for (int i = 0; i < B_PER_T; ++i) {
-            const int p = tid + NT * i;
+            const int p = CLAMP ? min(tid + NT * i, B_PIECES - 1) : tid + NT * i;
             const int r = p / KS, part = p % KS;
             const int gn = n_base + r;
-            rb[i] = (p < B_PIECES && gn < N) ? gld16(packed + (size_t)gn * KB + (k0 >> 2) + 16 * part)
-                                             : make_uint4(0u, 0u, 0u, 0u);
+            if (CLAMP) rb[i] = gld16(packed + (size_t)min(gn, N - 1) * KB + (k0 >> 2) + 16 * part);
+            else rb[i] = (p < B_PIECES && gn < N) ? gld16(packed + (size_t)gn * KB + (k0 >> 2) + 16 * part)
+                                                  : make_uint4(0u, 0u, 0u, 0u);
         }
     };
     auto store_step = [&](int buf) {
         #pragma unroll
         for (int i = 0; i < A_PER_T; ++i) {
-            const int p = tid + NT * i;
-            if (p < A_PIECES) {
+            const int p = CLAMP ? min(tid + NT * i, A_PIECES - 1) : tid + NT * i;
+            if (CLAMP || p < A_PIECES) {
                 const int row = p / CPR, ch = p % CPR;
                 *reinterpret_cast<uint4 *>(&As[buf][row * RS + 16 * ch]) = ra[i];
             }
         }
         #pragma unroll
         for (int i = 0; i < B_PER_T; ++i) {
-            const int p = tid + NT * i;
-            if (p < B_PIECES) {
+            const int p = CLAMP ? min(tid + NT * i, B_PIECES - 1) : tid + NT * i;
+            if (CLAMP || p < B_PIECES) {
                 const int r = p / KS, part = p % KS;
                 const uint32_t w[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
                 if (BPACK) {
@@ -185,7 +206,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
     __syncthreads();
     for (int s = 0; s < steps; ++s) {
         const int buf = s & 1;
-        if (s + 1 < steps) load_step(s + 1);
+        // with CLAMP the last step reloads and restages its own tile into the idle
+        // buffer (never read), which keeps the body free of branches
+        if (CLAMP) load_step(min(s + 1, steps - 1));
+        else if (s + 1 < steps) load_step(s + 1);
         #pragma unroll
         for (int u = 0; u < KS; ++u) {
             v4i a[TM], b[TN];
@@ -209,7 +233,32 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
         }
-        if (s + 1 < steps) store_step(buf ^ 1);
+        if (CLAMP || s + 1 < steps) store_step(buf ^ 1);
+#if BITNET_GEMM_SCHED
+        // Instruction order within the step: the global loads first, the first
+        // substep's fragment reads, then the MFMAs with the next substep's fragment
+        // reads between them, and in the last substep the B expansion (VALU) and the
+        // LDS stores of the next step between the MFMAs.
+        if (CLAMP) {
+            constexpr int NMF = TM * TN, NRD = TM + TN, NWR = A_PER_T + 4 * B_PER_T;
+            __builtin_amdgcn_sched_group_barrier(0x020, A_PER_T + B_PER_T, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+            #pragma unroll
+            for (int u = 0; u < KS; ++u) {
+                #pragma unroll
+                for (int m = 0; m < NMF; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (u + 1 < KS) {
+                        if (m < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    } else {
+                        __builtin_amdgcn_sched_group_barrier(0x002, BITNET_GEMM_SCHED_VALU, 0);
+                        if (m % BITNET_GEMM_SCHED_WR == BITNET_GEMM_SCHED_WR - 1 && m / BITNET_GEMM_SCHED_WR < NWR)
+                            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                    }
+                }
+            }
+        }
+#endif
         __syncthreads();
     }
 
