@@ -37,7 +37,7 @@ typedef __attribute__((address_space(1))) const v4u_g gv4u_g;
 #define BITNET_GEMM_SCHED_WR 2
 #endif
 #ifndef BITNET_GEMM_GROUP_M
-#define BITNET_GEMM_GROUP_M 8
+#define BITNET_GEMM_GROUP_M 2
 #endif
 // tile configurations 0 (256 x 224) and 1 (256 x 80): waves M, waves N, MFMA
 // tiles per wave in M and N, 64-k substeps per barrier step

@@ -2,8 +2,10 @@
 checked against the CPU oracle on sampled matrices / rows / columns.
 
 * decode step: 30 layers x {q, k, v, o, gate, up, down} of the 2.4B shape,
-  M = 1, one grouped quant launch + one grouped GEMV launch (layers 0 and 29
-  compared in full, every matrix's y checked for finiteness);
+  M = 1, one grouped quant launch + one grouped GEMV launch, the one fused
+  launch, and the fused launch with RMSNorm and SwiGLU at both ends of the
+  feed-forward part (layers 0 and 29 compared in full, every output checked
+  for finiteness);
 * prefill: M = 2048 on up (2560 -> 6912) and down (6912 -> 2560), natural
   density and 30 / 50 / 70 % nonzero codes, 160 sampled output columns;
 * 100B-scale FFN: gate (8192 -> 28672) and down (28672 -> 8192) of layer 0 at
@@ -129,6 +131,77 @@ def test_decode_step_fused():
         assert np.array_equal(q.cpu().numpy(), q_ref) and np.array_equal(sx.cpu().numpy(), sx_ref)
         assert np.array_equal(acc.cpu().numpy(), acc_ref), (m.layer, m.name)
         assert_y(y.cpu().numpy(), y_ref)
+
+
+def test_decode_step_fused_rmsnorm_swiglu():
+    """The 30-layer decode step as the one fused launch with RMSNorm before q / k / v
+    and gate / up, each layer's gate / up as one pair problem whose epilogue writes
+    a = fp32(silu(y_gate) y_up), and down taking an fp32 row: layers 0 and 29
+    compared in full against the oracle (pairs bit for bit, codes and acc exactly,
+    normed y within 2^-22 |y|), every output finite."""
+    mats = W.decode_step_2p4b(30)
+    sample = {0, 29}
+    xs = [W.decode_step_activations(l, DEV) for l in range(30)]
+    gains = [W.decode_step_gains(l, DEV) for l in range(30)]
+    hidden = [W.decode_step_ffn_hidden(l, DEV) for l in range(30)]
+    packed, sws, host = [], [], {}
+    for i, m in enumerate(mats):
+        w = W.weights(m, DEV)
+        p, s = tw.pack_weights(w, 1e-5)
+        packed.append(p)
+        sws.append(s)
+        if m.layer in sample:
+            host[i] = w.cpu()
+        del w
+    probs, cases = [], []
+    for i, m in enumerate(mats):
+        if m.name == "up":
+            continue
+        if m.name == "gate":
+            iu = next(j for j, o in enumerate(mats) if o.layer == m.layer and o.name == "up")
+            y = torch.full((1, m.N), float("nan"), dtype=torch.float32, device=DEV)
+            probs.append((xs[m.layer][m.slot], (packed[i], packed[iu]), (sws[i], sws[iu]), y, None, None, None,
+                          gains[m.layer].get(m.slot), 1e-6))
+            cases.append((m, "pair", (i, iu)))
+            continue
+        acc = torch.empty((1, m.N), dtype=torch.int32, device=DEV) if m.layer in sample else None
+        y = torch.full((1, m.N), float("nan"), dtype=torch.float32, device=DEV)
+        if m.slot == W.SWIGLU_SLOT_2P4B:
+            probs.append((hidden[m.layer], packed[i], sws[i], y, acc, None, None))
+            cases.append((m, "f32", (i,)))
+        else:
+            gn = gains[m.layer].get(m.slot)
+            probs.append((xs[m.layer][m.slot], packed[i], sws[i], y, acc, None, None, gn, 1e-6))
+            cases.append((m, "plain" if gn is None else "norm", (i,)))
+    plan = tw.bitnet_grouped_plan_fused(probs)
+    plan.launch()
+    torch.cuda.synchronize()
+    for pr in probs:
+        assert torch.isfinite(pr[3]).all()
+    for pr, (m, kind, idx) in zip(probs, cases):
+        if m.layer not in sample:
+            continue
+        refs = [oracle.pack(host[j].numpy(), 1e-5) for j in idx]
+        if kind == "f32":
+            q_ref, sx_ref = oracle.quant_act_f32(hidden[m.layer].cpu().numpy())
+        elif kind == "plain":
+            q_ref, sx_ref = oracle.quant_act(bits_np(xs[m.layer][m.slot]))
+        else:
+            gn = gains[m.layer][m.slot].cpu().numpy()
+            q_ref, sx_ref = oracle.rmsnorm_quant(bits_np(xs[m.layer][m.slot]), gn, 1e-6)
+        y = pr[3].cpu().numpy()
+        if kind == "pair":
+            (pg, sg), (pu, su) = refs
+            _, y_g = oracle.linear(q_ref, sx_ref, pg, sg)
+            _, y_u = oracle.linear(q_ref, sx_ref, pu, su)
+            assert np.array_equal(y, oracle.swiglu_quant(y_g, y_u)[0]), (m.layer, m.name)
+            continue
+        (p_ref, sw_ref), = refs
+        acc_ref, y_ref = oracle.linear(q_ref, sx_ref, p_ref, sw_ref)
+        assert np.array_equal(pr[4].cpu().numpy(), acc_ref), (m.layer, m.name)
+        tol = 2.0 ** -22 if kind == "norm" else REL
+        d = np.abs(y.astype(np.float64) - y_ref.astype(np.float64))
+        assert np.all(d <= tol * np.abs(y_ref.astype(np.float64))), (m.layer, m.name)
 
 
 @pytest.mark.parametrize("name", ["up", "down"])
