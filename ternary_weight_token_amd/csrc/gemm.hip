@@ -82,7 +82,7 @@ __device__ __forceinline__ uint4 gld16(const void *p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int WM, int WN, int TM, int TN, int KS, bool BPACK>
+template <int WM, int WN, int TM, int TN, int KS>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__restrict__ q,
                                                            const float *__restrict__ s_x,
                                                            const uint8_t *__restrict__ packed,
@@ -103,18 +103,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
     // a B piece: elsewhere the repeated pieces cost more VALU and LDS time than the
     // interleaving gains (256 x 80 tile: 65 -> 70 us on the down shape).
     constexpr bool CLAMP = (B_PIECES % NT == 0) || 8 * (B_PIECES % NT) >= 7 * NT;
-    // B in LDS: expanded int8 codes (row stride RS) or packed 2-bit codes (row
-    // stride 16 KS + 4 bytes: 16 lanes reading one dword each hit distinct banks)
-    constexpr int RSB = BPACK ? 16 * KS + 4 : RS;
     // A and B staging share one allocation, reused after the k loop to stage the
     // fp32 output rows (row stride CWP floats: +4 spreads a lane group's 4 rows over
     // distinct banks)
-    constexpr int A_BYTES = 2 * BM * RS, B_BYTES = 2 * BN * RSB;
+    constexpr int A_BYTES = 2 * BM * RS, B_BYTES = 2 * BN * RS;
     constexpr int CW = 16 * TN, CWP = CW + 4;
     static_assert(WM * WN * 16 * CWP * 4 <= A_BYTES + B_BYTES, "output staging exceeds LDS");
     __shared__ __attribute__((aligned(16))) uint8_t smem[A_BYTES + B_BYTES];
     uint8_t (*As)[BM * RS] = reinterpret_cast<uint8_t (*)[BM * RS]>(smem);
-    uint8_t (*Bs)[BN * RSB] = reinterpret_cast<uint8_t (*)[BN * RSB]>(smem + A_BYTES);
+    uint8_t (*Bs)[BN * RS] = reinterpret_cast<uint8_t (*)[BN * RS]>(smem + A_BYTES);
     __shared__ double rowscale[BM];
 
     // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; give each
@@ -182,14 +179,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
             if (CLAMP || p < B_PIECES) {
                 const int r = p / KS, part = p % KS;
                 const uint32_t w[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
-                if (BPACK) {
-                    uint32_t *dst = reinterpret_cast<uint32_t *>(&Bs[buf][r * RSB + 16 * part]);
-                    dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2]; dst[3] = w[3];
-                } else {
-                    #pragma unroll
-                    for (int d = 0; d < 4; ++d)
-                        *reinterpret_cast<uint4 *>(&Bs[buf][r * RS + 64 * part + 16 * d]) = ternary16(w[d]);
-                }
+                #pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    *reinterpret_cast<uint4 *>(&Bs[buf][r * RS + 64 * part + 16 * d]) = ternary16(w[d]);
             }
         }
     };
@@ -217,16 +209,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
             for (int i = 0; i < TM; ++i)
                 a[i] = *reinterpret_cast<const v4i *>(&As[buf][(wm * TM * 16 + i * 16 + l16) * RS + 64 * u + 16 * g]);
             #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                if (BPACK) {
-                    const uint32_t w = *reinterpret_cast<const uint32_t *>(
-                        &Bs[buf][(wn * TN * 16 + j * 16 + l16) * RSB + 16 * u + 4 * g]);
-                    const uint4 e = ternary16(w);
-                    b[j] = v4i{(int)e.x, (int)e.y, (int)e.z, (int)e.w};
-                } else {
-                    b[j] = *reinterpret_cast<const v4i *>(&Bs[buf][(wn * TN * 16 + j * 16 + l16) * RS + 64 * u + 16 * g]);
-                }
-            }
+            for (int j = 0; j < TN; ++j)
+                b[j] = *reinterpret_cast<const v4i *>(&Bs[buf][(wn * TN * 16 + j * 16 + l16) * RS + 64 * u + 16 * g]);
             #pragma unroll
             for (int i = 0; i < TM; ++i)
                 #pragma unroll
@@ -366,12 +350,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
 
 struct GemmCfg { int wm, wn, tm, tn; };
 
-template <int WM, int WN, int TM, int TN, int KS, bool BPACK = false>
+template <int WM, int WN, int TM, int TN, int KS>
 static hipError_t launch_cfg(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                              int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st) {
     constexpr int BM = 16 * WM * TM, BN = 16 * WN * TN;
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-    gemm_kernel<WM, WN, TM, TN, KS, BPACK><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * WM * WN), 0, st>>>(
+    gemm_kernel<WM, WN, TM, TN, KS><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * WM * WN), 0, st>>>(
         q, s_x, packed, s_w, (int)M, (int)N, (int)K, y, acc, tiles_m, tiles_n);
     return hipGetLastError();
 }
