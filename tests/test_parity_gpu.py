@@ -795,9 +795,11 @@ def test_linear_auto_dispatch_beyond_16_tokens(M, N, K):
 
 
 @pytest.mark.parametrize("cfg", range(5))
-@pytest.mark.parametrize("M,N,K", [(300, 500, 640), (17, 33, 64), (257, 225, 6912 - 64)])
+@pytest.mark.parametrize("M,N,K", [(300, 500, 640), (17, 33, 64), (257, 225, 6912 - 64), (5, 230, 256),
+                                   (1, 1, 128)])
 def test_gemm_tile_configs(cfg, M, N, K):
-    """Every MFMA tile configuration, forced, on ragged M and N."""
+    """Every MFMA tile configuration, forced, on ragged M and N, down to a single row
+    and column (the tiles whose staging repeats the last row past M or N)."""
     key = synth.stream_key(307, M, N, K)
     x, q, s = quantized_inputs(key, M, K, row_scale=(0.1, 10.0))
     packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
