@@ -9,7 +9,8 @@ checked against the CPU oracle on sampled matrices / rows / columns.
 * prefill: M = 2048 on up (2560 -> 6912) and down (6912 -> 2560), natural
   density and 30 / 50 / 70 % nonzero codes, 160 sampled output columns;
 * 100B-scale FFN: gate (8192 -> 28672) and down (28672 -> 8192) of layer 0 at
-  M = 1 and M = 8, compared in full.
+  M = 1 and M = 8, compared in full;
+* sign / mask bitplanes at the stacked 229376 x 8192 shape, 3 sampled row slices.
 """
 from __future__ import annotations
 
@@ -242,3 +243,30 @@ def test_ffn_100b_layer0(which):
         acc_ref, y_ref = oracle.linear(q_ref, sx_ref, p_ref, sw_ref)
         assert np.array_equal(acc.cpu().numpy(), acc_ref)
         assert_y(y.cpu().numpy(), y_ref)
+
+
+def test_bitplanes_stacked_100b_gate():
+    """Sign / mask bitplanes at the encodings leg's one-launch shape (the 8 gate
+    matrices of the 100B-scale FFN stacked: N = 229376, K = 8192, M = 1, the 4-row
+    tile of the bit-serial GEMV): planes packed on the GPU and y / acc of three
+    sampled 512-row slices (first, middle, last) against the oracle, every y finite."""
+    N, K = 229376, 8192
+    key = synth.stream_key(361, N, K)
+    packed = synth.random_bytes(key, N * K // 4, DEV).view(N, K // 4)
+    planes = tw.pack_bitplanes(packed, K)
+    x = synth.activations(synth.stream_key(key, 1), 1, K, outlier_frac=0.001)
+    q_ref, s_ref = oracle.quant_act(bits_np(x))
+    q, sx = torch.from_numpy(q_ref).to(DEV), torch.from_numpy(s_ref).to(DEV)
+    s_w = np.float32(0.0117)
+    y, acc = tw.linear_bits(q, sx, planes, tw.FMT_BITPLANES, torch.tensor([s_w], device=DEV), want_acc=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all()
+    for r0 in (0, N // 2 - 256, N - 512):
+        rows = slice(r0, r0 + 512)
+        p_np = packed[rows].cpu().numpy()
+        pl_ref = oracle.pack_bitplanes(p_np, K)
+        assert np.array_equal(planes[rows].cpu().numpy(), pl_ref), r0
+        acc_ref, y_ref = oracle.linear_bitplanes(q_ref, s_ref, pl_ref, s_w)
+        assert np.array_equal(acc[:, rows].cpu().numpy(), acc_ref), r0
+        assert_y(y[:, rows].cpu().numpy(), y_ref)
+
