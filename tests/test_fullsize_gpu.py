@@ -10,7 +10,8 @@ checked against the CPU oracle on sampled matrices / rows / columns.
   density and 30 / 50 / 70 % nonzero codes, 160 sampled output columns;
 * 100B-scale FFN: gate (8192 -> 28672) and down (28672 -> 8192) of layer 0 at
   M = 1 and M = 8, compared in full;
-* sign / mask bitplanes at the stacked 229376 x 8192 shape, 3 sampled row slices.
+* sign / mask bitplanes and binary weights at the stacked 229376 x 8192 shape,
+  3 sampled row slices.
 """
 from __future__ import annotations
 
@@ -267,6 +268,27 @@ def test_bitplanes_stacked_100b_gate():
         pl_ref = oracle.pack_bitplanes(p_np, K)
         assert np.array_equal(planes[rows].cpu().numpy(), pl_ref), r0
         acc_ref, y_ref = oracle.linear_bitplanes(q_ref, s_ref, pl_ref, s_w)
+        assert np.array_equal(acc[:, rows].cpu().numpy(), acc_ref), r0
+        assert_y(y[:, rows].cpu().numpy(), y_ref)
+
+
+def test_binary_stacked_100b_gate():
+    """b1.0 binary weights at the same stacked shape (N = 229376, K = 8192, M = 1):
+    random weight bits (every pattern is a valid set of +1 / -1 weights), y / acc of
+    three sampled 512-row slices against the oracle, every y finite."""
+    N, K = 229376, 8192
+    key = synth.stream_key(362, N, K)
+    bits = synth.random_bytes(key, N * K // 8, DEV).view(N, K // 8)
+    x = synth.activations(synth.stream_key(key, 1), 1, K, outlier_frac=0.001)
+    q_ref, s_ref = oracle.quant_act(bits_np(x))
+    q, sx = torch.from_numpy(q_ref).to(DEV), torch.from_numpy(s_ref).to(DEV)
+    s_w = np.float32(0.0093)
+    y, acc = tw.linear_bits(q, sx, bits, tw.FMT_BINARY, torch.tensor([s_w], device=DEV), want_acc=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all()
+    for r0 in (0, N // 2 - 256, N - 512):
+        rows = slice(r0, r0 + 512)
+        acc_ref, y_ref = oracle.linear_binary(q_ref, s_ref, bits[rows].cpu().numpy(), s_w, K)
         assert np.array_equal(acc[:, rows].cpu().numpy(), acc_ref), r0
         assert_y(y[:, rows].cpu().numpy(), y_ref)
 
