@@ -1,11 +1,11 @@
 """Full-size workloads on the GPU, in the launch configuration the bench times,
 checked against the CPU oracle on sampled matrices / rows / columns.
 
-* decode step: 30 layers x {q, k, v, o, gate, up, down} of the 2.4B shape,
-  M = 1, one grouped quant launch + one grouped GEMV launch, the one fused
-  launch, and the fused launch with RMSNorm and SwiGLU at both ends of the
-  feed-forward part (layers 0 and 29 compared in full, every output checked
-  for finiteness);
+* decode step: 30 layers x {q, k, v, o, gate, up, down} of the 2.4B shape:
+  one grouped quant launch + one grouped linear launch at M = 1 and M = 8, the
+  one fused launch at M = 1, and the fused launch with RMSNorm, without and with
+  SwiGLU at both ends of the feed-forward part (layers 0 and 29 compared in
+  full, every output checked for finiteness);
 * prefill: M = 2048 on up (2560 -> 6912) and down (6912 -> 2560), natural
   density and 30 / 50 / 70 % nonzero codes, 160 sampled output columns;
 * 100B-scale FFN: gate (8192 -> 28672) and down (28672 -> 8192) of layer 0 at
@@ -48,7 +48,11 @@ def assert_y(y, y_ref):
     assert np.all(d <= REL * np.abs(y_ref.astype(np.float64)))
 
 
-def test_decode_step_grouped():
+@pytest.mark.parametrize("M", [1, 8])
+def test_decode_step_grouped(M):
+    """The 30-layer decode step as one grouped quant launch and one grouped linear
+    launch (the GEMV at M = 1, the MFMA decode kernel at M = 8): layers 0 and 29
+    compared in full, every output finite."""
     mats = W.decode_step_2p4b(30)
     sample = {0, 29}
     packed, sws, host_w = [], [], {}
@@ -60,15 +64,15 @@ def test_decode_step_grouped():
         if m.layer in sample:
             host_w[i] = w.cpu()
         del w
-    xs = [W.decode_step_activations(l, DEV) for l in range(30)]
-    qs = [[torch.empty((1, x.shape[1]), dtype=torch.int8, device=DEV) for x in xl] for xl in xs]
-    sxs = [[torch.empty(1, dtype=torch.float32, device=DEV) for _ in xl] for xl in xs]
+    xs = [W.decode_step_activations(l, DEV, M) for l in range(30)]
+    qs = [[torch.empty((M, x.shape[1]), dtype=torch.int8, device=DEV) for x in xl] for xl in xs]
+    sxs = [[torch.empty(M, dtype=torch.float32, device=DEV) for _ in xl] for xl in xs]
     qplan = tw.bitnet_grouped_plan_quant(
         [(xs[l][s], qs[l][s], sxs[l][s]) for l in range(30) for s in range(4)])
     ys, accs, probs = [], [], []
     for i, m in enumerate(mats):
-        y = torch.full((1, m.N), float("nan"), dtype=torch.float32, device=DEV)
-        acc = torch.empty((1, m.N), dtype=torch.int32, device=DEV) if m.layer in sample else None
+        y = torch.full((M, m.N), float("nan"), dtype=torch.float32, device=DEV)
+        acc = torch.empty((M, m.N), dtype=torch.int32, device=DEV) if m.layer in sample else None
         ys.append(y)
         accs.append(acc)
         probs.append((qs[m.layer][m.slot], sxs[m.layer][m.slot], packed[i], sws[i], y, acc))
@@ -135,12 +139,13 @@ def test_decode_step_fused():
         assert_y(y.cpu().numpy(), y_ref)
 
 
-def test_decode_step_fused_rmsnorm_swiglu():
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_decode_step_fused_rmsnorm_swiglu(swiglu):
     """The 30-layer decode step as the one fused launch with RMSNorm before q / k / v
-    and gate / up, each layer's gate / up as one pair problem whose epilogue writes
-    a = fp32(silu(y_gate) y_up), and down taking an fp32 row: layers 0 and 29
-    compared in full against the oracle (pairs bit for bit, codes and acc exactly,
-    normed y within 2^-22 |y|), every output finite."""
+    and gate / up; with swiglu, each layer's gate / up as one pair problem whose
+    epilogue writes a = fp32(silu(y_gate) y_up) and down taking an fp32 row: layers
+    0 and 29 compared in full against the oracle (pairs bit for bit, codes and acc
+    exactly, normed y within 2^-22 |y|), every output finite."""
     mats = W.decode_step_2p4b(30)
     sample = {0, 29}
     xs = [W.decode_step_activations(l, DEV) for l in range(30)]
@@ -157,9 +162,9 @@ def test_decode_step_fused_rmsnorm_swiglu():
         del w
     probs, cases = [], []
     for i, m in enumerate(mats):
-        if m.name == "up":
+        if swiglu and m.name == "up":
             continue
-        if m.name == "gate":
+        if swiglu and m.name == "gate":
             iu = next(j for j, o in enumerate(mats) if o.layer == m.layer and o.name == "up")
             y = torch.full((1, m.N), float("nan"), dtype=torch.float32, device=DEV)
             probs.append((xs[m.layer][m.slot], (packed[i], packed[iu]), (sws[i], sws[iu]), y, None, None, None,
@@ -168,7 +173,7 @@ def test_decode_step_fused_rmsnorm_swiglu():
             continue
         acc = torch.empty((1, m.N), dtype=torch.int32, device=DEV) if m.layer in sample else None
         y = torch.full((1, m.N), float("nan"), dtype=torch.float32, device=DEV)
-        if m.slot == W.SWIGLU_SLOT_2P4B:
+        if swiglu and m.slot == W.SWIGLU_SLOT_2P4B:
             probs.append((hidden[m.layer], packed[i], sws[i], y, acc, None, None))
             cases.append((m, "f32", (i,)))
         else:
