@@ -11,7 +11,8 @@ checked against the CPU oracle on sampled matrices / rows / columns.
 * 100B-scale FFN: gate (8192 -> 28672) and down (28672 -> 8192) of layer 0 at
   M = 1 and M = 8, compared in full;
 * sign / mask bitplanes and binary weights at the stacked 229376 x 8192 shape,
-  3 sampled row slices.
+  3 sampled row slices;
+* the decode step with group-128 weight scales (grouped quant + grouped GEMV).
 """
 from __future__ import annotations
 
@@ -296,4 +297,54 @@ def test_binary_stacked_100b_gate():
         acc_ref, y_ref = oracle.linear_binary(q_ref, s_ref, bits[rows].cpu().numpy(), s_w, K)
         assert np.array_equal(acc[:, rows].cpu().numpy(), acc_ref), r0
         assert_y(y[:, rows].cpu().numpy(), y_ref)
+
+
+def _grouped_bound(q, s_x, packed, s_w, G, K):
+    """2^-44 (s_x / 127) sum_g |acc_g s_g| per output: the library sums the groups'
+    float64 terms in another order than the oracle."""
+    t = oracle.unpack(packed, K).astype(np.float64)
+    sg = np.repeat(s_w.astype(np.float64), G, axis=1)
+    mag = np.abs(q.astype(np.float64)) @ (np.abs(t) * sg).T
+    return 2.0 ** -44 * mag * (s_x.astype(np.float64)[:, None] / 127.0)
+
+
+def test_decode_step_grouped_group128_scales():
+    """The 30-layer decode step with a weight scale per group of 128 weights, as
+    one grouped quant launch and one grouped linear launch: layers 0 and 29 (packed
+    bytes, scales, acc and y) against the oracle, every output finite."""
+    G = 128
+    mats = W.decode_step_2p4b(30)
+    sample = {0, 29}
+    xs = [W.decode_step_activations(l, DEV) for l in range(30)]
+    qs = [[torch.empty((1, x.shape[1]), dtype=torch.int8, device=DEV) for x in xl] for xl in xs]
+    sxs = [[torch.empty(1, dtype=torch.float32, device=DEV) for _ in xl] for xl in xs]
+    qplan = tw.bitnet_grouped_plan_quant([(xs[l][j], qs[l][j], sxs[l][j]) for l in range(30) for j in range(4)])
+    probs, host = [], {}
+    for i, m in enumerate(mats):
+        w = W.weights(m, DEV)
+        p, sw = tw.pack_weights_grouped(w, G, 1e-5)
+        if m.layer in sample:
+            host[i] = w.cpu()
+        del w
+        y = torch.full((1, m.N), float("nan"), dtype=torch.float32, device=DEV)
+        acc = torch.empty((1, m.N), dtype=torch.int32, device=DEV) if m.layer in sample else None
+        probs.append((qs[m.layer][m.slot], sxs[m.layer][m.slot], p, sw, y, acc, G))
+    plan = tw.bitnet_grouped_plan_linear(probs)
+    qplan.launch()
+    plan.launch()
+    torch.cuda.synchronize()
+    for pr in probs:
+        assert torch.isfinite(pr[4]).all()
+    for i, m in enumerate(mats):
+        if m.layer not in sample:
+            continue
+        p_ref, s_ref = oracle.pack_grouped(host[i].numpy(), G, 1e-5)
+        _, _, p, sw, y, acc, _ = probs[i]
+        assert np.array_equal(p.cpu().numpy(), p_ref) and np.array_equal(sw.cpu().numpy(), s_ref), (m.layer, m.name)
+        q_ref, sx_ref = oracle.quant_act(bits_np(xs[m.layer][m.slot]))
+        acc_ref, y_ref = oracle.linear_grouped(q_ref, sx_ref, p_ref, s_ref, G)
+        assert np.array_equal(acc.cpu().numpy(), acc_ref), (m.layer, m.name)
+        d = np.abs(y.cpu().numpy().astype(np.float64) - y_ref.astype(np.float64))
+        bound = REL * np.abs(y_ref.astype(np.float64)) + _grouped_bound(q_ref, sx_ref, p_ref, s_ref, G, m.K)
+        assert np.all(d <= bound), (m.layer, m.name)
 
