@@ -33,8 +33,10 @@
  *  - activation code: q = clamp(RNE(127 * x / max|x_row|), -127, 127) where the
  *    quotient is the exact real number (computed in float64, which is exact
  *    for bf16 inputs, see the tests); an all-zero row gives q = 0, s_x = 0;
- *  - output y = acc * (s_x / 127) * s_w, the real number rounded once to fp32
- *    (formed in float64); the /127 undoes the *127 of the activation code;
+ *  - output y = acc * c with one rescale factor per token row and weight scale,
+ *    c = (s_x * s_w) / 127 formed in float64 ([P1] 2.3 applies the two scale
+ *    factors to the integer product; the /127 undoes the *127 of the activation
+ *    code), then acc * c in float64 and one rounding to fp32;
  *  - a 2-bit field holding 3 (never written by the packer) decodes to +2;
  *  - the optional bias ([P1] 3.1 adds it after the rescale) joins the float64
  *    value before its one rounding to fp32; a bf16 output is that fp32 value
@@ -302,10 +304,15 @@ void oracle_swiglu_quant(const float *g, const float *u, int64_t M, int64_t K, f
 /* --- contraction and rescale ([P1] 2.3, 3.1 BitLinear.forward) ---------- */
 
 /* acc[m][n] = sum_k q[m][k] * t[n][k]  (exact integer sum)
- * y[m][n]   = fp32( acc * s_x[m] * s_w / 127 + bias[n] )   formed in float64;
+ * c_m       = (s_x[m] * s_w) / 127                       in float64 (s_x s_w is exact),
+ * y[m][n]   = fp32( acc * c_m + bias[n] )                  in float64;
  * the bias is the layer's own bias, added after the rescale ([P1] 3.1, where
  * BitLinear.forward adds self.bias to the dequantized product).
  * acc and bias may be NULL (no bias: the sum has no second term). */
+static double row_factor(float s_x, float s_w) {
+    return ((double)s_x * (double)s_w) / 127.0;
+}
+
 void oracle_linear_bias(const int8_t *q, const float *s_x, const uint8_t *packed,
                         float s_w, const float *bias, int64_t M, int64_t N, int64_t K,
                         int32_t *acc, float *y) {
@@ -317,9 +324,7 @@ void oracle_linear_bias(const int8_t *q, const float *s_x, const uint8_t *packed
             for (int64_t k = 0; k < K; ++k)
                 a += (int64_t)q[m * K + k] * (int64_t)weight_at(packed, KB, n, k);
             if (acc) acc[m * N + n] = (int32_t)a;
-            double v = (double)a * (double)s_x[m];
-            v = v * (double)s_w;
-            v = v / 127.0;
+            double v = (double)a * row_factor(s_x[m], s_w);
             if (bias) v = v + (double)bias[n];
             y[m * N + n] = (float)v;
         }
@@ -329,7 +334,9 @@ void oracle_linear_bias(const int8_t *q, const float *s_x, const uint8_t *packed
 /* Group-wise scales: acc_g[m][n] = sum over group g of q t (exact integer), and
  * y[m][n] = fp32( (sum_g acc_g s_w[n][g]) * s_x[m] / 127 (+ bias[n]) ), the sum
  * over g ascending, all in float64; acc[m][n] = sum_g acc_g (the whole-row
- * integer sum, for inspection).  acc and bias may be NULL. */
+ * integer sum, for inspection).  acc and bias may be NULL.  A single group per
+ * row (G = K: one scale per output channel) is the per-tensor rescale with the
+ * row's own scale: y = fp32(acc * c + bias), c = (s_x[m] * s_w[n]) / 127. */
 void oracle_linear_grouped(const int8_t *q, const float *s_x, const uint8_t *packed,
                            const float *s_w, int64_t G, const float *bias, int64_t M, int64_t N,
                            int64_t K, int32_t *acc, float *y) {
@@ -347,8 +354,12 @@ void oracle_linear_grouped(const int8_t *q, const float *s_x, const uint8_t *pac
                 v += (double)a * (double)s_w[n * ng + g];
             }
             if (acc) acc[m * N + n] = (int32_t)total;
-            v = v * (double)s_x[m];
-            v = v / 127.0;
+            if (ng == 1) {
+                v = (double)total * row_factor(s_x[m], s_w[n]);
+            } else {
+                v = v * (double)s_x[m];
+                v = v / 127.0;
+            }
             if (bias) v = v + (double)bias[n];
             y[m * N + n] = (float)v;
         }
@@ -386,7 +397,7 @@ static int binary_at(const uint8_t *bits, int64_t K, int64_t n, int64_t k) {
     return ((bits[n * (K / 8) + k / 8] >> (k % 8)) & 1u) ? 1 : -1;
 }
 
-/* acc = sum_k q t (exact), y = fp32(acc s_x s_w / 127) in float64, as oracle_linear. */
+/* acc = sum_k q t (exact), y = fp32(acc c_m), c_m = (s_x s_w) / 127, as oracle_linear. */
 void oracle_linear_binary(const int8_t *q, const float *s_x, const uint8_t *bits, float s_w, int64_t M,
                           int64_t N, int64_t K, int32_t *acc, float *y) {
     #pragma omp parallel for schedule(static)
@@ -395,7 +406,7 @@ void oracle_linear_binary(const int8_t *q, const float *s_x, const uint8_t *bits
             int64_t a = 0;
             for (int64_t k = 0; k < K; ++k) a += (int64_t)q[m * K + k] * binary_at(bits, K, n, k);
             if (acc) acc[m * N + n] = (int32_t)a;
-            y[m * N + n] = (float)((((double)a * (double)s_x[m]) * (double)s_w) / 127.0);
+            y[m * N + n] = (float)((double)a * row_factor(s_x[m], s_w));
         }
     }
 }
@@ -445,7 +456,7 @@ void oracle_linear_bitplanes(const int8_t *q, const float *s_x, const uint8_t *p
             int64_t a = 0;
             for (int64_t k = 0; k < K; ++k) a += (int64_t)q[m * K + k] * bitplane_at(planes, K, n, k);
             if (acc) acc[m * N + n] = (int32_t)a;
-            y[m * N + n] = (float)((((double)a * (double)s_x[m]) * (double)s_w) / 127.0);
+            y[m * N + n] = (float)((double)a * row_factor(s_x[m], s_w));
         }
     }
 }

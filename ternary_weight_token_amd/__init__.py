@@ -113,6 +113,21 @@ def _dev(t: torch.Tensor, dtype, name: str) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _arg(t: torch.Tensor, dtype, shape, name: str) -> None:
+    """A device tensor of this dtype and shape (the kernels trust the sizes they are given)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    _dev(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _same_device(name: str, *ts) -> None:
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"{name}: every tensor of a problem must be on one device")
+
+
 def bitnet_pack_workspace_bytes(N: int, K: int) -> int:
     return int(lib().bitnet_pack_workspace_bytes(N, K))
 
@@ -254,7 +269,22 @@ def bitnet_grouped_plan_linear(problems, device=None) -> GroupedPlan:
     for i, prob in enumerate(problems):
         q, s_x, packed, s_w, y, acc = prob[:6]
         w_group = int(prob[6]) if len(prob) > 6 else 0
+        if not isinstance(q, torch.Tensor) or q.dim() != 2 or not isinstance(packed, torch.Tensor) or packed.dim() != 2:
+            raise ValueError(f"problem {i}: q must be [M][K] and packed [N][K/4]")
         M, K = q.shape
+        N = packed.shape[0]
+        _arg(q, torch.int8, (M, K), f"problem {i}: q")
+        _arg(s_x, torch.float32, (M,), f"problem {i}: s_x")
+        _arg(packed, torch.uint8, (N, K // 4), f"problem {i}: packed")
+        if w_group < 0 or (w_group and K % w_group):
+            raise ValueError(f"problem {i}: w_group must be 0 or divide K")
+        _dev(s_w, torch.float32, f"problem {i}: s_w")
+        if s_w.numel() != (N * (K // w_group) if w_group else 1):
+            raise ValueError(f"problem {i}: s_w must hold {'N * K / w_group' if w_group else 'one'} scale(s)")
+        _arg(y, torch.float32, (M, N), f"problem {i}: y")
+        if acc is not None:
+            _arg(acc, torch.int32, (M, N), f"problem {i}: acc")
+        _same_device(f"problem {i}", q, s_x, packed, s_w, y, acc)
         arr[i] = _LinearDesc(q.data_ptr(), s_x.data_ptr(), packed.data_ptr(), s_w.data_ptr(),
                              y.data_ptr(), 0 if acc is None else acc.data_ptr(), M, packed.shape[0], K, w_group)
         refs.append((q, s_x, packed, s_w, y, acc))
@@ -272,7 +302,13 @@ def bitnet_grouped_plan_quant(problems, device=None) -> GroupedPlan:
     arr = (_QuantDesc * len(problems))()
     refs = []
     for i, (x, q, s_x) in enumerate(problems):
+        if not isinstance(x, torch.Tensor) or x.dim() != 2:
+            raise ValueError(f"problem {i}: x must be [M][K]")
         M, K = x.shape
+        _arg(x, torch.bfloat16, (M, K), f"problem {i}: x")
+        _arg(q, torch.int8, (M, K), f"problem {i}: q")
+        _arg(s_x, torch.float32, (M,), f"problem {i}: s_x")
+        _same_device(f"problem {i}", x, q, s_x)
         arr[i] = _QuantDesc(x.data_ptr(), q.data_ptr(), s_x.data_ptr(), M, K)
         refs.append((x, q, s_x))
     n = lib().bitnet_grouped_plan_bytes(len(problems), 0, ctypes.cast(arr, ctypes.c_void_p))
@@ -299,23 +335,37 @@ def bitnet_grouped_plan_fused(problems, device=None) -> GroupedPlan:
         gain, eps = (prob[7], float(prob[8])) if len(prob) > 7 and prob[7] is not None else (None, 0.0)
         if not isinstance(x, torch.Tensor) or x.dtype not in (torch.bfloat16, torch.float32):
             raise TypeError("x must be a bf16 or fp32 tensor")
-        _dev(x, x.dtype, "x")
+        if x.dim() != 2:
+            raise ValueError(f"problem {i}: x must be [M][K]")
         M, K = x.shape
+        _arg(x, x.dtype, (M, K), f"problem {i}: x")
         xp, xf = (x.data_ptr(), 0) if x.dtype == torch.bfloat16 else (0, x.data_ptr())
         pu = su = 0
+        packed_up = s_w_up = None
         if isinstance(packed, (tuple, list)):
             packed, packed_up = packed
             s_w, s_w_up = s_w
-            _dev(packed_up, torch.uint8, "packed_up"); _dev(s_w_up, torch.float32, "s_w_up")
-            if packed_up.shape != packed.shape:
-                raise ValueError("gate and up weights must have one shape")
+        if not isinstance(packed, torch.Tensor) or packed.dim() not in (2, 3):
+            raise ValueError(f"problem {i}: packed must be [N][K/4] (or bitplanes [N][K/32][8])")
+        N = packed.shape[0]
+        fmt = FMT_BITPLANES if packed.dim() == 3 else 0
+        _arg(packed, torch.uint8, (N, K // 32, 8) if fmt else (N, K // 4), f"problem {i}: packed")
+        _arg(s_w, torch.float32, (1,), f"problem {i}: s_w")
+        if packed_up is not None:
+            _arg(packed_up, torch.uint8, tuple(packed.shape), f"problem {i}: packed_up")
+            _arg(s_w_up, torch.float32, (1,), f"problem {i}: s_w_up")
             pu, su = packed_up.data_ptr(), s_w_up.data_ptr()
             refs.append((packed_up, s_w_up))
+        _arg(y, torch.float32, (M, N), f"problem {i}: y")
+        if acc is not None:
+            _arg(acc, torch.int32, (M, N), f"problem {i}: acc")
+        if q is not None:
+            _arg(q, torch.int8, (M, K), f"problem {i}: q")
+        if s_x is not None:
+            _arg(s_x, torch.float32, (M,), f"problem {i}: s_x")
         if gain is not None:
-            _dev(gain, torch.float32, "norm_gain")
-            if gain.shape != (K,):
-                raise ValueError("norm_gain must be [K]")
-        fmt = FMT_BITPLANES if packed.dim() == 3 else 0
+            _arg(gain, torch.float32, (K,), f"problem {i}: norm_gain")
+        _same_device(f"problem {i}", x, packed, s_w, y, acc, q, s_x, gain, packed_up, s_w_up)
         arr[i] = _FusedDesc(xp, packed.data_ptr(), s_w.data_ptr(), y.data_ptr(),
                             0 if acc is None else acc.data_ptr(), 0 if q is None else q.data_ptr(),
                             0 if s_x is None else s_x.data_ptr(), M, packed.shape[0], K,
@@ -394,7 +444,9 @@ def bitnet_linear_bits(q, s_x, wbits, fmt: int, s_w, y, acc=None, kernel: int = 
     if wbits.numel() != N * K // (8 if fmt == FMT_BINARY else 4) or y.shape != (M, N):
         raise ValueError("weights do not match K, or y is not [M][N]")
     if acc is not None:
-        _dev(acc, torch.int32, "acc")
+        _arg(acc, torch.int32, (M, N), "acc")
+    if s_x.shape != (M,) or s_w.numel() != 1:
+        raise ValueError("s_x must be [M] and s_w [1]")
     _check(lib().bitnet_linear_bits(_ptr(q), _ptr(s_x), _ptr(wbits), int(fmt), _ptr(s_w), M, N, K, _ptr(y),
                                     _ptr(acc), int(kernel), _stream(stream)))
 

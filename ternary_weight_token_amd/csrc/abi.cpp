@@ -372,8 +372,10 @@ BITNET_API int bitnet_grouped_plan_linear(const bitnet_linear_desc *descs, int c
         for (int i = 0; i < count; ++i) h->lds_bytes = std::max(h->lds_bytes, skinny_grouped_lds_bytes(descs[i].M, descs[i].K));
     } else {
         h->rows_per_block = gemv_grouped_rows_per_block();
+        // each descriptor is staged by the path its own scales take (group-wise
+        // descriptors keep one more dword per chunk, so they segment K sooner)
         for (int i = 0; i < count; ++i)
-            h->lds_bytes = std::max(h->lds_bytes, gemv_grouped_lds_bytes(descs[i].K, variant == kVariantGemvGroups));
+            h->lds_bytes = std::max(h->lds_bytes, gemv_grouped_lds_bytes(descs[i].K, desc_groups(descs[i])));
     }
     h->desc_offset = doff;
     h->table_offset = toff;

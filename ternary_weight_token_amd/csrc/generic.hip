@@ -27,8 +27,9 @@ __global__ __launch_bounds__(256) void linear_generic_kernel(
         if (acc_out) acc_out[idx] = s;
         return;
     }
-    // weight scales per group of G = w_group weights of the row (G = K: per output
-    // channel): y = fp32((sum_g acc_g s_w[n][g]) s_x / 127), the sum in float64
+    // weight scales per group of G = w_group weights of the row: y = fp32((sum_g
+    // acc_g s_w[n][g]) s_x / 127), the sum in float64; G = K (one scale per output
+    // channel) is the per-tensor rescale with the row's own scale
     const int64_t G = out.w_group, ng = K / G;
     int total = 0;
     double v = 0.0;
@@ -42,7 +43,8 @@ __global__ __launch_bounds__(256) void linear_generic_kernel(
         total += a;
         v += (double)a * (double)s_w[n * ng + g];
     }
-    v = (v * (double)s_x[m]) / 127.0;
+    if (ng == 1) v = (double)total * rescale_factor(s_x[m], s_w[n]);
+    else v = (v * (double)s_x[m]) / 127.0;
     if (out.bias) v += (double)out.bias[n];
     store_y(out, idx, v);
     if (acc_out) acc_out[idx] = total;

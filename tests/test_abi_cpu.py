@@ -170,6 +170,21 @@ def test_python_binding_fails_loudly_without_gpu_tensors():
                          torch.zeros(1), torch.zeros((1, 4)))
 
 
+def test_grouped_plan_builders_reject_host_tensors():
+    """The plan builders check every tensor before anything reaches the C planner."""
+    import torch
+    q = torch.zeros((1, 64), dtype=torch.int8)
+    s = torch.zeros(1)
+    p = torch.zeros((4, 16), dtype=torch.uint8)
+    y = torch.zeros((1, 4))
+    with pytest.raises(ValueError):
+        tw.bitnet_grouped_plan_linear([(q, s, p, s, y, None)])
+    with pytest.raises(ValueError):
+        tw.bitnet_grouped_plan_quant([(torch.zeros((1, 64), dtype=torch.bfloat16), q, s)])
+    with pytest.raises(ValueError):
+        tw.bitnet_grouped_plan_fused([(torch.zeros((1, 64), dtype=torch.bfloat16), p, s, y, None, None, None)])
+
+
 def test_fused_plan_checks(L):
     F = tw._FusedDesc
     a16 = 4096
@@ -349,3 +364,21 @@ def test_linear_plan_weight_groups(L):
     ok = (D * 1)(D(a16, a16, a16, a16, a16, 0, 2, 300, 2560, 2560))     # per channel: MFMA variant stays
     assert L.bitnet_grouped_plan_linear(ok, 1, buf, nb) == OK
     assert (ctypes.c_uint32 * 8).from_buffer_copy(buf.raw[:32])[7] == 1
+
+
+def test_linear_plan_lds_covers_every_descriptor(L):
+    """The plan's dynamic LDS size covers each descriptor's own staging: a plain
+    K = 51200 row stages all 800 chunks at 20 dwords (64000 bytes) in one segment,
+    while group-wise descriptors keep 21 dwords per chunk and split such a K."""
+    D = tw._LinearDesc
+    a16 = 4096
+    mixed = (D * 2)(D(a16, a16, a16, a16, a16, 0, 1, 64, 51200, 0), D(a16, a16, a16, a16, a16, 0, 1, 64, 2560, 128))
+    nb = L.bitnet_grouped_plan_bytes(2, 1, mixed)
+    buf = ctypes.create_string_buffer(nb)
+    assert L.bitnet_grouped_plan_linear(mixed, 2, buf, nb) == OK
+    hdr = (ctypes.c_uint32 * 8).from_buffer_copy(buf.raw[:32])
+    assert hdr[7] == 2 and hdr[6] >= 800 * 20 * 4
+    alone = (D * 1)(D(a16, a16, a16, a16, a16, 0, 1, 64, 51200, 128))
+    assert L.bitnet_grouped_plan_linear(alone, 1, buf, nb) == OK
+    hdr = (ctypes.c_uint32 * 8).from_buffer_copy(buf.raw[:32])
+    assert 0 < hdr[6] <= 64 * 1024

@@ -45,8 +45,21 @@ def bits_np(x):
 
 
 def assert_y(y, y_ref):
-    d = np.abs(y.astype(np.float64) - y_ref.astype(np.float64))
-    assert np.all(d <= REL * np.abs(y_ref.astype(np.float64)))
+    """fp32 y bit for bit: library and oracle both form acc * ((s_x s_w) / 127) in
+    float64 and round once."""
+    assert np.array_equal(np.ascontiguousarray(y, dtype=np.float32).view(np.uint32),
+                          np.ascontiguousarray(y_ref, dtype=np.float32).view(np.uint32))
+
+
+def swiglu_pair_bound(y_g, y_u, rel):
+    """How far a = silu(g) u can move when g and u each move by rel of themselves,
+    plus one fp32 rounding of a."""
+    g = y_g.astype(np.float64)
+    u = y_u.astype(np.float64)
+    sg = 1.0 / (1.0 + np.exp(-g))
+    dsilu = sg * (1.0 + g * (1.0 - sg))
+    a = g * sg * u
+    return 2 * rel * (np.abs(dsilu * g * u) + np.abs(a)) + 2.0 ** -23 * np.abs(a)
 
 
 @pytest.mark.parametrize("M", [1, 8])
@@ -202,14 +215,22 @@ def test_decode_step_fused_rmsnorm_swiglu(swiglu):
             (pg, sg), (pu, su) = refs
             _, y_g = oracle.linear(q_ref, sx_ref, pg, sg)
             _, y_u = oracle.linear(q_ref, sx_ref, pu, su)
-            assert np.array_equal(y, oracle.swiglu_quant(y_g, y_u)[0]), (m.layer, m.name)
+            a_ref = oracle.swiglu_quant(y_g, y_u)[0]
+            if gains[m.layer].get(m.slot) is None:
+                assert np.array_equal(y, a_ref), (m.layer, m.name)
+            else:
+                # RMSNorm rows: s_x within one fp32 unit of the oracle's
+                bound = swiglu_pair_bound(y_g, y_u, 2.0 ** -22)
+                assert np.all(np.abs(y.astype(np.float64) - a_ref.astype(np.float64)) <= bound), (m.layer, m.name)
             continue
         (p_ref, sw_ref), = refs
         acc_ref, y_ref = oracle.linear(q_ref, sx_ref, p_ref, sw_ref)
         assert np.array_equal(pr[4].cpu().numpy(), acc_ref), (m.layer, m.name)
-        tol = 2.0 ** -22 if kind == "norm" else REL
-        d = np.abs(y.astype(np.float64) - y_ref.astype(np.float64))
-        assert np.all(d <= tol * np.abs(y_ref.astype(np.float64))), (m.layer, m.name)
+        if kind == "norm":
+            d = np.abs(y.astype(np.float64) - y_ref.astype(np.float64))
+            assert np.all(d <= 2.0 ** -22 * np.abs(y_ref.astype(np.float64))), (m.layer, m.name)
+        else:
+            assert_y(y, y_ref)
 
 
 @pytest.mark.parametrize("name", ["up", "down"])

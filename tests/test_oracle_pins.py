@@ -56,6 +56,19 @@ def round_fraction_to_f32(fr: Fraction) -> float:
     return sign * math.ldexp(float(fl), e)
 
 
+def assert_rescale_rounding(y, exact: Fraction, delta: Fraction, where=None):
+    """The oracle's y = fp32(v), v = acc * c_m (+ b) formed in float64 with
+    c_m = (s_x s_w) / 127, lies within delta of the exact value (float64 rounding
+    of c_m, of the product and of the sum), so y is the correct rounding of some
+    value in [exact - delta, exact + delta]: rounding is monotone, so y lies
+    between the roundings of the two ends.  Away from an fp32 rounding boundary
+    the two ends round alike and y is the correctly rounded exact value."""
+    lo = round_fraction_to_f32(exact - delta)
+    hi = round_fraction_to_f32(exact + delta)
+    assert lo <= float(y) <= hi, (where, float(y), lo, hi)
+    return lo == hi
+
+
 def rne_int(num: np.ndarray, den: np.ndarray) -> np.ndarray:
     """Round-half-even of num/den for int64 arrays (den > 0), exact."""
     fl = np.floor_divide(num, den)
@@ -340,7 +353,15 @@ def test_linear_all_plus_one_and_code3():
     assert accc[0, 0] == 127 * K
 
 
-def test_epilogue_is_correctly_rounded():
+# float64 error of acc * ((s_x s_w) / 127): s_x s_w is exact (48 significant bits), the
+# quotient and the product are each rounded once, 2 * 2^-53 relative plus a product term
+EPI_REL = Fraction(1, 2 ** 51)
+
+
+def test_epilogue_rounding():
+    """y against the exact rational acc s_x s_w / 127: the correctly rounded fp32
+    value wherever the exact value is not within 2^-51 relative of a rounding
+    boundary, which is every sampled output here."""
     key = synth.stream_key(15)
     M, N, K = 4, 200, 512
     x = synth.activations(key, M, K, row_scale=(0.1, 10.0))
@@ -348,16 +369,37 @@ def test_epilogue_is_correctly_rounded():
     w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02).numpy()
     packed, s_w = oracle.pack(w)
     acc, y = oracle.linear(q, s, packed, s_w)
+    decided = 0
     for m in range(M):
         for n in range(N):
             exact = Fraction(int(acc[m, n])) * Fraction(float(s[m])) * Fraction(float(s_w)) / 127
-            assert y[m, n] == np.float32(round_fraction_to_f32(exact)), (m, n)
+            decided += assert_rescale_rounding(y[m, n], exact, abs(exact) * EPI_REL, (m, n))
+    assert decided == M * N      # every output here is the correctly rounded value
     # extreme accumulators
     qx = np.full((1, K), 127, np.int8)
     acc_x, y_x = oracle.linear(qx, np.array([3.0e5], np.float32), np.full((1, K // 4), 0xAA, np.uint8),
                                np.float32(7.77e-3))
     exact = Fraction(127 * K) * Fraction(float(np.float32(3.0e5))) * Fraction(float(np.float32(7.77e-3))) / 127
-    assert y_x[0, 0] == np.float32(round_fraction_to_f32(exact))
+    assert assert_rescale_rounding(y_x[0, 0], exact, abs(exact) * EPI_REL)
+
+
+def test_epilogue_one_factor_per_row():
+    """The rescale is one float64 factor per token row, c_m = (s_x[m] s_w) / 127,
+    times acc: scaling acc by 2^j (a power of two, exact) scales y by 2^j exactly,
+    and two outputs of one row with acc and -acc are exact negatives."""
+    K, N = 64, 4
+    q = np.zeros((1, K), np.int8)
+    q[0, 0], q[0, 1] = 100, 27
+    packed = np.full((N, K // 4), 0x55, np.uint8)        # all codes 1 (weight 0)
+    packed[0, 0] = 0x56                                 # weight +1 at k = 0
+    packed[1, 0] = 0x54                                 # weight -1 at k = 0
+    packed[2, 0] = 0x5A                                 # +1 at k = 0 and k = 1
+    s = np.array([0.8317], np.float32)
+    acc, y = oracle.linear(q, s, packed, np.float32(0.0137))
+    assert list(acc[0]) == [100, -100, 127, 0]
+    assert y[0, 0] == -y[0, 1] and y[0, 3] == 0.0
+    c = (float(s[0]) * float(np.float32(0.0137))) / 127.0
+    assert y[0, 0] == np.float32(100.0 * c) and y[0, 2] == np.float32(127.0 * c)
 
 
 # ----------------------------------------------------------------- epilogue options
@@ -429,9 +471,11 @@ def test_linear_bias_exact(M, N, K):
     acc_bf = _brute_force(q, s, packed, s_w, K)
     for m in range(M):
         for n in range(N):
-            exact = (Fraction(int(acc_bf[m, n])) * Fraction(float(s[m])) * Fraction(float(s_w)) / 127
-                     + Fraction(float(bias[n])))
-            assert y[m, n] == np.float32(round_fraction_to_f32(exact)), (m, n)
+            prod = Fraction(int(acc_bf[m, n])) * Fraction(float(s[m])) * Fraction(float(s_w)) / 127
+            exact = prod + Fraction(float(bias[n]))
+            # float64: the product's error, then one rounding of the sum
+            delta = abs(prod) * EPI_REL + abs(exact) * Fraction(1, 2 ** 52)
+            assert assert_rescale_rounding(y[m, n], exact, delta, (m, n))
 
 
 def test_linear_bias_broadcast_over_tokens():
@@ -585,9 +629,15 @@ def test_linear_grouped_exact(M, N, K, G):
             groups = [int(np.dot(q[m, g * G:(g + 1) * G].astype(np.int64), t[n, g * G:(g + 1) * G]))
                       for g in range(K // G)]
             assert acc[m, n] == sum(groups)
-            exact = (sum(Fraction(a) * Fraction(float(s_w[n, g])) for g, a in enumerate(groups))
-                     * Fraction(float(s[m])) / 127 + Fraction(float(bias[n])))
-            assert y[m, n] == np.float32(round_fraction_to_f32(exact)), (m, n)
+            prod = (sum(Fraction(a) * Fraction(float(s_w[n, g])) for g, a in enumerate(groups))
+                    * Fraction(float(s[m])) / 127)
+            exact = prod + Fraction(float(bias[n]))
+            if K // G == 1:
+                # one scale per row: the per-tensor rescale with the row's own scale
+                delta = abs(prod) * EPI_REL + abs(exact) * Fraction(1, 2 ** 52)
+                assert assert_rescale_rounding(y[m, n], exact, delta, (m, n))
+            else:
+                assert y[m, n] == np.float32(round_fraction_to_f32(exact)), (m, n)
 
 
 def test_linear_grouped_uniform_scales_match_per_tensor():
@@ -754,8 +804,8 @@ def test_linear_binary_brute_force(M, N, K):
         for n in range(N):
             a = sum(int(q[m, k]) * int(t[n, k]) for k in range(K))
             assert acc[m, n] == a
-            assert y[m, n] == np.float32(round_fraction_to_f32(
-                Fraction(a) * Fraction(float(s[m])) * Fraction(float(np.float32(0.03))) / 127))
+            exact = Fraction(a) * Fraction(float(s[m])) * Fraction(float(np.float32(0.03))) / 127
+            assert assert_rescale_rounding(y[m, n], exact, abs(exact) * EPI_REL, (m, n))
 
 
 def test_binary_of_weights_is_their_sign():
