@@ -104,6 +104,28 @@ BITNET_API int bitnet_pack_weights(const float *w, int64_t N, int64_t K, float e
                                    void *stream);
 
 /* ---------------------------------------------------------------------------
+ * The same packing for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops, harnesses that forbid hipMalloc): the
+ * float64 row sums go to a scratch array the library holds, one copy per GPU,
+ * allocated when the library is loaded and kept until the process ends; the
+ * call itself allocates nothing.
+ *
+ *   w, eps, packed, s_w   as bitnet_pack_weights; results are bit-identical
+ *   N                     at most BITNET_PACK_NOALLOC_MAX_ROWS (262144 rows,
+ *                         2 MiB of scratch per GPU), else BITNET_ERR_SHAPE
+ *                         before anything is enqueued
+ *   stream                a stream of the current device (hipSetDevice)
+ *
+ * Every call on one GPU uses that GPU's one scratch array: calls that overlap
+ * in time on one GPU (different streams, or threads without ordering) race and
+ * may give wrong s_w.  Calls ordered on one stream are safe.  The row sums are
+ * fully written before they are read, so nothing needs clearing between calls.
+ * ------------------------------------------------------------------------- */
+#define BITNET_PACK_NOALLOC_MAX_ROWS 262144
+BITNET_API int bitnet_pack_weights_noalloc(const float *w, int64_t N, int64_t K, float eps,
+                                           uint8_t *packed, float *s_w, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Per-token absmax int8 activation quantization.
  * Page: chenxutan.com sec. 2.2 (absmax_quantize, 8 bits -> qmax 127).
  *

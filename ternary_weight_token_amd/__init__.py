@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
         L.bitnet_pack_workspace_bytes.argtypes = [I64, I64]
         L.bitnet_pack_workspace_bytes.restype = ctypes.c_size_t
         L.bitnet_pack_weights.argtypes = [P, I64, I64, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
+        L.bitnet_pack_weights_noalloc.argtypes = [P, I64, I64, ctypes.c_float, P, P, P]
         L.bitnet_quant_act.argtypes = [P, I64, I64, P, P, P]
         L.bitnet_rmsnorm_quant_act.argtypes = [P, P, ctypes.c_float, I64, I64, P, P, P]
         L.bitnet_swiglu_quant_act.argtypes = [P, P, I64, I64, P, P, P]
@@ -79,7 +80,7 @@ def lib() -> ctypes.CDLL:
         L.bitnet_grouped_plan_fused_bytes.restype = ctypes.c_size_t
         L.bitnet_grouped_plan_fused.argtypes = [P, I, P, ctypes.c_size_t]
         L.bitnet_linear_fused_grouped.argtypes = [P, P, P]
-        for f in ("bitnet_pack_weights", "bitnet_pack_weights_grouped", "bitnet_quant_act", "bitnet_rmsnorm_quant_act", "bitnet_swiglu_quant_act", "bitnet_pack_weights_binary", "bitnet_pack_bitplanes", "bitnet_linear_bits", "bitnet_linear", "bitnet_linear_select", "bitnet_linear_ex",
+        for f in ("bitnet_pack_weights", "bitnet_pack_weights_noalloc", "bitnet_pack_weights_grouped", "bitnet_quant_act", "bitnet_rmsnorm_quant_act", "bitnet_swiglu_quant_act", "bitnet_pack_weights_binary", "bitnet_pack_bitplanes", "bitnet_linear_bits", "bitnet_linear", "bitnet_linear_select", "bitnet_linear_ex",
                   "bitnet_grouped_plan_linear", "bitnet_grouped_plan_quant", "bitnet_grouped_plan_fused",
                   "bitnet_linear_grouped", "bitnet_quant_act_grouped", "bitnet_linear_fused_grouped"):
             getattr(L, f).restype = I
@@ -142,6 +143,21 @@ def bitnet_pack_weights(w: torch.Tensor, eps: float, packed: torch.Tensor, s_w: 
     _check(lib().bitnet_pack_weights(_ptr(w), N, K, ctypes.c_float(eps), _ptr(packed), _ptr(s_w),
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(stream)))
+
+
+PACK_NOALLOC_MAX_ROWS = 262144
+
+
+def bitnet_pack_weights_noalloc(w: torch.Tensor, eps: float, packed: torch.Tensor, s_w: torch.Tensor,
+                                stream=None) -> None:
+    """bitnet_pack_weights with the library's own per-GPU scratch (no workspace, no
+    allocation); N <= PACK_NOALLOC_MAX_ROWS; calls overlapping on one GPU race."""
+    _dev(w, torch.float32, "w"); _dev(packed, torch.uint8, "packed"); _dev(s_w, torch.float32, "s_w")
+    N, K = w.shape
+    if packed.shape != (N, K // 4) or s_w.numel() != 1:
+        raise ValueError("packed must be [N][K/4] and s_w [1]")
+    _check(lib().bitnet_pack_weights_noalloc(_ptr(w), N, K, ctypes.c_float(eps), _ptr(packed), _ptr(s_w),
+                                             _stream(stream)))
 
 
 def bitnet_quant_act(x: torch.Tensor, q: torch.Tensor, s_x: torch.Tensor, stream=None) -> None:

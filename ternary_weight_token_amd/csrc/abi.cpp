@@ -94,6 +94,21 @@ BITNET_API int bitnet_pack_weights(const float *w, int64_t N, int64_t K, float e
     return hip_status(launch_pack(w, N, K, eps, packed, s_w, (double *)workspace, (hipStream_t)stream));
 }
 
+BITNET_API int bitnet_pack_weights_noalloc(const float *w, int64_t N, int64_t K, float eps, uint8_t *packed,
+                                           float *s_w, void *stream) {
+    static_assert(BITNET_PACK_NOALLOC_MAX_ROWS == kPackScratchRows, "header and library disagree");
+    int st = check_dims(0, N, K);
+    if (st) return st;
+    if (N > BITNET_PACK_NOALLOC_MAX_ROWS) return fail(BITNET_ERR_SHAPE, "N exceeds the library's scratch rows");
+    if (!s_w) return fail(BITNET_ERR_NULL, "s_w is NULL");
+    if (N > 0 && (!w || !packed)) return fail(BITNET_ERR_NULL, "null pointer");
+    if (!aligned(s_w, 4) || (w && !aligned(w, 4))) return fail(BITNET_ERR_ALIGN, "w and s_w must be 4-byte aligned");
+    double *rowsum = nullptr;
+    hipError_t e = pack_scratch(&rowsum);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(launch_pack(w, N, K, eps, packed, s_w, rowsum, (hipStream_t)stream));
+}
+
 BITNET_API int bitnet_pack_weights_binary(const float *w, int64_t N, int64_t K, uint8_t *bits, float *s_w,
                                           void *workspace, size_t workspace_bytes, void *stream) {
     int st = check_dims(0, N, K);

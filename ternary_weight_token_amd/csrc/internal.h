@@ -92,6 +92,11 @@ hipError_t launch_linear_bits(const int8_t *q, const float *s_x, const uint8_t *
                               int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, int kernel, hipStream_t st);
 hipError_t launch_pack(const float *w, int64_t N, int64_t K, float eps, uint8_t *packed,
                        float *s_w, double *rowsum, hipStream_t st);
+// Library-held row-sum scratch of the pack step (one copy per GPU, rows up to
+// kPackScratchRows): its device address on the current device.
+constexpr int64_t kPackScratchRows = (int64_t)1 << 18;
+constexpr int kMaxScratchDevices = 64;
+hipError_t pack_scratch(double **out);
 hipError_t launch_pack_grouped(const float *w, int64_t N, int64_t K, int64_t G, float eps, uint8_t *packed,
                                float *s_w, hipStream_t st);
 hipError_t launch_gemv(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,

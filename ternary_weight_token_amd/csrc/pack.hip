@@ -9,6 +9,8 @@
 //  3. code_kernel     : t = clamp(rint(w / (s_w + eps)), -1, 1) with binary32
 //                       ops, code t + 1, four codes per byte, LSB first; works on
 //                       the flat array (K % 4 == 0 keeps bytes inside rows).
+#include <mutex>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -107,6 +109,35 @@ hipError_t launch_weight_scale(const float *w, int64_t N, int64_t K, float *s_w,
     }
     combine_kernel<<<dim3(1), dim3(64), 0, st>>>(rowsum, N, K, s_w);
     return hipGetLastError();
+}
+
+// Scratch for callers that cannot allocate: the float64 row sums of one pack call
+// live in this array instead of a caller workspace.  Each GPU holds its own copy
+// for the life of the process; host code must use the address hipGetSymbolAddress
+// reports for the current device (the array's name on the host is only a stand-in,
+// and a kernel handed it would fault).
+static __device__ __align__(256) double scratch[kPackScratchRows];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t pack_scratch(double **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_dev[dev] = p;
+    }
+    *out = static_cast<double *>(g_scratch_dev[dev]);
+    return hipSuccess;
 }
 
 hipError_t launch_pack(const float *w, int64_t N, int64_t K, float eps, uint8_t *packed, float *s_w,
