@@ -396,7 +396,9 @@ hipError_t launch_gemm(const int8_t *q, const float *s_x, const uint8_t *packed,
     return launch_gemm_cfg(gemm_pick(M, N, nullptr), q, s_x, packed, s_w, M, N, K, y, acc, st);
 }
 
-int gemm_config_count() { return 5; }
+// configurations 0..4: this file's tiles; 5, 6: the pipelined kernel with 128 x 224
+// and 128 x 160 tiles
+int gemm_config_count() { return 7; }
 
 hipError_t launch_gemm_cfg(int cfg, const int8_t *q, const float *s_x, const uint8_t *packed,
                            const float *s_w, int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc,
@@ -408,6 +410,12 @@ hipError_t launch_gemm_cfg(int cfg, const int8_t *q, const float *s_x, const uin
                             : launch_cfg<BITNET_GEMM_CFG0_K64>(q, s_x, packed, s_w, M, N, K, y, acc, st);
         case 1: return k128 ? launch_cfg<BITNET_GEMM_CFG1>(q, s_x, packed, s_w, M, N, K, y, acc, st)
                             : launch_cfg<BITNET_GEMM_CFG1_K64>(q, s_x, packed, s_w, M, N, K, y, acc, st);
+        case 5:
+        case 6:
+            // the pipelined kernel where its whole 128-weight steps fit, else the
+            // matching tile of this file
+            if (gemm_pipe_ok(M, N, K)) return launch_gemm_pipe(cfg == 5 ? 7 : 5, q, s_x, packed, s_w, M, N, K, y, acc, st);
+            return launch_gemm_cfg(cfg - 5, q, s_x, packed, s_w, M, N, K, y, acc, st);
         case 2: return launch_cfg<2, 2, 8, 4, 1>(q, s_x, packed, s_w, M, N, K, y, acc, st);
         case 3: return launch_cfg<2, 2, 4, 4, 1>(q, s_x, packed, s_w, M, N, K, y, acc, st);
         default: return launch_cfg<1, 4, 4, 2, 1>(q, s_x, packed, s_w, M, N, K, y, acc, st);

@@ -843,7 +843,29 @@ def test_linear_auto_dispatch_beyond_16_tokens(M, N, K):
     check_linear(q, s, packed, np.float32(0.0093))
 
 
-@pytest.mark.parametrize("cfg", range(5))
+@pytest.mark.parametrize("cfg,M,N,K", [(5, 1100, 6912, 128), (6, 1300, 4000, 256), (5, 520, 7000, 128),
+                                       (6, 2048, 2560 + 16, 128), (5, 300, 500, 6912 - 128)])
+def test_gemm_pipelined_several_tiles_per_workgroup(cfg, M, N, K):
+    """The pipelined GEMM with more tiles than workgroups: each workgroup walks its
+    tiles in one step sequence, loads of the next tile overlapping the current one,
+    ragged last M and N tiles, K of one to three steps."""
+    key = synth.stream_key(315, cfg, M, N, K)
+    x, q, s = quantized_inputs(key, M, K, row_scale=(0.1, 10.0))
+    packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
+    acc_ref, y_ref = oracle.linear(q, s, packed, np.float32(0.0077))
+    args = (torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV), torch.from_numpy(packed).to(DEV),
+            torch.tensor([0.0077], device=DEV))
+    for rep in range(2):
+        y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+        acc = torch.full((M, N), -1, dtype=torch.int32, device=DEV)
+        tw.bitnet_linear_select(*args, y, acc if rep == 0 else None, 16 + cfg)
+        torch.cuda.synchronize()
+        if rep == 0:
+            assert np.array_equal(acc.cpu().numpy(), acc_ref)
+        assert_y(y.cpu().numpy(), y_ref)
+
+
+@pytest.mark.parametrize("cfg", range(7))
 @pytest.mark.parametrize("M,N,K", [(300, 500, 640), (17, 33, 64), (257, 225, 6912 - 64), (5, 230, 256),
                                    (1, 1, 128)])
 def test_gemm_tile_configs(cfg, M, N, K):
@@ -864,7 +886,7 @@ def test_gemm_tile_configs(cfg, M, N, K):
 
 # ----------------------------------------------------------------- epilogue options
 
-@pytest.mark.parametrize("cfg", [2, 16, 17, 18, 19, 20])
+@pytest.mark.parametrize("cfg", [2, 16, 17, 18, 19, 20, 21, 22])
 @pytest.mark.parametrize("M,N,K,with_bias", [(257, 225, 640, False), (300, 500, 640, True),
                                              (130, 258, 6912 - 64, True), (2048, 384, 2560, False)])
 def test_gemm_output_without_acc(cfg, M, N, K, with_bias):
@@ -904,7 +926,7 @@ def test_gemm_output_without_acc(cfg, M, N, K, with_bias):
     (4, 2, 300, 2624), (4, 16, 129, 2560), (4, 20, 70, 640),           # MFMA decode
     (2, 17, 129, 256), (2, 130, 257, 640),                             # MFMA GEMM, automatic tile
     (16, 257, 225, 640), (17, 257, 225, 640), (18, 257, 225, 640),     # each forced tile
-    (19, 257, 225, 640), (20, 257, 225, 640),
+    (19, 257, 225, 640), (20, 257, 225, 640), (21, 257, 225, 640), (22, 257, 225, 640),
     (3, 3, 9, 68), (3, 20, 33, 132),                                   # general kernel
     (0, 1, 640, 2560), (0, 8, 300, 2560), (0, 40, 300, 2560),          # automatic choice
 ])
