@@ -382,10 +382,24 @@ static int gemm_pick(int64_t M, int64_t N, int64_t *tiles_out) {
     return best;
 }
 
-// Estimated time (us) of launch_gemm: rounds of tiles over the 256 CUs x K / 64 steps
-// of about 0.55 us, plus about 6 us of launch, prologue and epilogue (measured on
-// M = 16 .. 256 against six shapes from 2560 x 2560 to 8192 x 28672).
+// The pipelined kernel (gemm_pipe.hip) where its whole 128-weight steps fit, except
+// where this file's 256 x 224 tile covers the problem in one round and the pipelined
+// kernel needs two or more (M = 2048, N = 6912, K = 2560: 47.6 against 50.0 us;
+// M = 1024, N = 13824: 49.8 against 53.3 us).  Elsewhere it measured faster at every
+// M = 512 .. 4096, N = 640 .. 13824, K = 2560 .. 8192 tried (by 1.03 .. 1.9x).
+static bool gemm_use_pipe(int64_t M, int64_t N, int64_t K) {
+    if (!gemm_pipe_ok(M, N, K)) return false;
+    int64_t tiles = 0;
+    const int cfg = gemm_pick(M, N, &tiles);
+    return !(cfg == 0 && tiles <= 256 && gemm_pipe_rounds(M, N) >= 2);
+}
+
+// Estimated time (us) of launch_gemm.  This file's kernel: rounds of tiles over the
+// 256 CUs x K / 64 steps of about 0.55 us, plus about 6 us of launch, prologue and
+// epilogue (measured on M = 16 .. 256 against six shapes from 2560 x 2560 to
+// 8192 x 28672).
 double gemm_estimate_us(int64_t M, int64_t N, int64_t K) {
+    if (gemm_use_pipe(M, N, K)) return gemm_pipe_estimate_us(M, N, K);
     int64_t tiles = 0;
     gemm_pick(M, N, &tiles);
     return (double)((tiles + 255) / 256) * (double)(K / 64) * 0.55 + 6.0;
@@ -393,6 +407,7 @@ double gemm_estimate_us(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_gemm(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                        int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st) {
+    if (gemm_use_pipe(M, N, K)) return launch_gemm_pipe(0, q, s_x, packed, s_w, M, N, K, y, acc, st);
     return launch_gemm_cfg(gemm_pick(M, N, nullptr), q, s_x, packed, s_w, M, N, K, y, acc, st);
 }
 

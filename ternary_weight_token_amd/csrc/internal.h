@@ -126,6 +126,7 @@ hipError_t launch_gemm_cfg(int cfg, const int8_t *q, const float *s_x, const uin
 int gemm_config_count();
 // pipelined persistent GEMM (gemm_pipe.hip); tn_force 0 = by its cost model, else 5 or 7
 bool gemm_pipe_ok(int64_t M, int64_t N, int64_t K);
+int64_t gemm_pipe_rounds(int64_t M, int64_t N);   // tiles per busiest workgroup on 256 CUs
 double gemm_pipe_estimate_us(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_pipe(int tn_force, const int8_t *q, const float *s_x, const uint8_t *packed,
                             const float *s_w, int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc,
