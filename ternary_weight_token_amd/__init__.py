@@ -80,7 +80,12 @@ def lib() -> ctypes.CDLL:
         L.bitnet_grouped_plan_fused_bytes.restype = ctypes.c_size_t
         L.bitnet_grouped_plan_fused.argtypes = [P, I, P, ctypes.c_size_t]
         L.bitnet_linear_fused_grouped.argtypes = [P, P, P]
-        for f in ("bitnet_pack_weights", "bitnet_pack_weights_noalloc", "bitnet_pack_weights_grouped", "bitnet_quant_act", "bitnet_rmsnorm_quant_act", "bitnet_swiglu_quant_act", "bitnet_pack_weights_binary", "bitnet_pack_bitplanes", "bitnet_linear_bits", "bitnet_linear", "bitnet_linear_select", "bitnet_linear_ex",
+        L.bitnet_probe_stream_read.argtypes = [P, ctypes.c_size_t, I64, ctypes.c_uint32, P, P]
+        L.bitnet_probe_mfma_i8.argtypes = [I64, I64, ctypes.c_uint32, P, P]
+        L.bitnet_probe_mfma_i8_ops.argtypes = [I64, I64]
+        L.bitnet_probe_mfma_i8_ops.restype = ctypes.c_double
+        for f in ("bitnet_probe_stream_read", "bitnet_probe_mfma_i8",
+                  "bitnet_pack_weights", "bitnet_pack_weights_noalloc", "bitnet_pack_weights_grouped", "bitnet_quant_act", "bitnet_rmsnorm_quant_act", "bitnet_swiglu_quant_act", "bitnet_pack_weights_binary", "bitnet_pack_bitplanes", "bitnet_linear_bits", "bitnet_linear", "bitnet_linear_select", "bitnet_linear_ex",
                   "bitnet_grouped_plan_linear", "bitnet_grouped_plan_quant", "bitnet_grouped_plan_fused",
                   "bitnet_linear_grouped", "bitnet_quant_act_grouped", "bitnet_linear_fused_grouped"):
             getattr(L, f).restype = I
@@ -507,3 +512,25 @@ def linear(q, s_x, packed, s_w, want_acc: bool = False, stream=None, bias=None,
     else:
         bitnet_linear_ex(q, s_x, packed, s_w, bias, y, acc, kernel, stream, w_group)
     return (y, acc) if want_acc else y
+
+
+# ------------------------------------------------------------------ measurement probes
+PROBE_KEY = 0x9E3779B9
+
+
+def probe_stream_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int = 2048, stream=None) -> None:
+    """Read every byte of buf once (bitnet_probe_stream_read): the HBM streaming
+    ceiling next to which the decode kernels are measured."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    _arg(sink, torch.int32, (1,), "sink")
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().bitnet_probe_stream_read(_ptr(buf), nbytes, int(blocks), PROBE_KEY, _ptr(sink), _stream(stream)))
+
+
+def probe_mfma_i8(sink: torch.Tensor, blocks: int, iters: int, stream=None) -> float:
+    """int8 MFMAs from registers only (bitnet_probe_mfma_i8); returns the int8
+    operations of the launch."""
+    _arg(sink, torch.int32, (1,), "sink")
+    _check(lib().bitnet_probe_mfma_i8(int(blocks), int(iters), PROBE_KEY, _ptr(sink), _stream(stream)))
+    return float(lib().bitnet_probe_mfma_i8_ops(int(blocks), int(iters)))

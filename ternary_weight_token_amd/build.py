@@ -10,7 +10,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libbitnet.so")
 
-SOURCES = ["abi.cpp", "quant_act.hip", "pack.hip", "gemv.hip", "skinny.hip", "gemm.hip", "gemm_pipe.hip", "generic.hip", "bits.hip"]
+SOURCES = ["abi.cpp", "quant_act.hip", "pack.hip", "gemv.hip", "skinny.hip", "gemm.hip", "gemm_pipe.hip", "generic.hip", "bits.hip", "probe.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

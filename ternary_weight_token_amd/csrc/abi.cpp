@@ -2,6 +2,7 @@
 // kernels.  Checks never touch the GPU, so a failed check enqueues nothing.
 #define BITNET_BUILD 1
 #include "bitnet.h"
+#include "bitnet_probe.h"
 
 #include <string.h>
 
@@ -75,6 +76,27 @@ BITNET_API const char *bitnet_status_str(int s) {
 BITNET_API const char *bitnet_last_error(void) { return g_last_error.c_str(); }
 
 BITNET_API int bitnet_version(void) { return 100; }
+
+// ----------------------------------------------------------------- probes
+
+BITNET_API int bitnet_probe_stream_read(const void *buf, size_t bytes, int64_t blocks, uint32_t key,
+                                        uint32_t *sink, void *stream) {
+    if (!buf || !sink) return fail(BITNET_ERR_NULL, "null pointer");
+    if (bytes == 0 || bytes % 16 != 0 || bytes >= ((size_t)1 << 40) || blocks < 1 || blocks > 65536)
+        return fail(BITNET_ERR_SHAPE, "bytes must be a nonzero multiple of 16 below 2^40, blocks 1 .. 65536");
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(BITNET_ERR_ALIGN, "buf 16-byte, sink 4-byte aligned");
+    return hip_status(launch_probe_stream_read(buf, (int64_t)bytes, blocks, key, sink, (hipStream_t)stream));
+}
+
+BITNET_API int bitnet_probe_mfma_i8(int64_t blocks, int64_t iters, uint32_t key, uint32_t *sink, void *stream) {
+    if (!sink) return fail(BITNET_ERR_NULL, "null pointer");
+    if (blocks < 1 || blocks > 65536 || iters < 1 || iters > ((int64_t)1 << 24))
+        return fail(BITNET_ERR_SHAPE, "blocks 1 .. 65536, iters 1 .. 2^24");
+    if (!aligned(sink, 4)) return fail(BITNET_ERR_ALIGN, "sink 4-byte aligned");
+    return hip_status(launch_probe_mfma_i8(blocks, iters, key, sink, (hipStream_t)stream));
+}
+
+BITNET_API double bitnet_probe_mfma_i8_ops(int64_t blocks, int64_t iters) { return probe_mfma_i8_ops(blocks, iters); }
 
 BITNET_API size_t bitnet_pack_workspace_bytes(int64_t N, int64_t K) {
     (void)K;

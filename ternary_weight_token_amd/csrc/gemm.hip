@@ -87,7 +87,7 @@ __device__ __forceinline__ uint4 gld16(const void *p) {
 }
 
 template <int WM, int WN, int TM, int TN, int KS>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__restrict__ q,
+__global__ __launch_bounds__(64 * WM * WN, WM * WN <= 4 ? 2 : 1) void gemm_kernel(const int8_t *__restrict__ q,
                                                            const float *__restrict__ s_x,
                                                            const uint8_t *__restrict__ packed,
                                                            const float *__restrict__ s_w, int M, int N,

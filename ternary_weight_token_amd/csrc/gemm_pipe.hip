@@ -6,7 +6,7 @@
 // Workgroup: 8 wavefronts, two per SIMD, with two roles; output tile 128 x BN,
 // BN = 32 TN weight rows; one k-step is 128 weights.
 //  * 4 producer waves load the step's q rows (whole 128-byte lines) and packed
-//    weight rows (32 bytes each) into registers two steps ahead, and write them
+//    weight rows (32 bytes each) into registers three steps ahead, and write them
 //    to one of three LDS stages: the q bytes of each 16-byte chunk in the
 //    transposed order k = 4d + i -> byte 4i + d (four byte permutes per dword),
 //    chunks XOR-swizzled so that fragment reads are free of bank conflicts.
@@ -82,7 +82,6 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
 
     if (wave >= 4) {
         // ------------------------------------------------------------ producer
-        const int p = wave - 4;
         const int tp = tid - 256;
         constexpr int NB = (2 * BN + 255) / 256;          // packed chunks per thread (1 or 2)
         // chunks of this thread: q chunk tp + 256 h -> row (tp >> 3) + 32 h, 16-byte
@@ -109,7 +108,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
         };
         set_tile(0);
         // loads of step d_s (clamped to the last step) into register set R
-        pv4u ra[3][4], rb[3][2];
+        pv4u ra[4][4], rb[4][2];
         auto issue = [&](int R) {
             #pragma unroll
             for (int h = 0; h < 4; ++h) ra[R][h] = gload(arow[h] + (size_t)d_kr * kPipeKS);
@@ -166,29 +165,33 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
                 ++t_ti;
             }
         };
+        // register set of step x: x % 4
         issue(0);
         issue(1);
         issue(2);
+        issue(3);
         store(0, 0);
         issue(0);
         store(1, 1);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        // iteration s: loads of step s + 4 into the set of step s + 1 (stored in the
+        // iteration s: loads of step s + 5 into the set of step s + 1 (stored in the
         // last iteration), step s + 2 from its set into the stage of step s - 1 (read
-        // up to the last barrier)
+        // up to the last barrier); three steps of loads stay in flight
         auto body = [&](int s, int Ri, int Rs) {
             issue(Ri);
             store(s + 2, Rs);
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         };
         int s = 0;
-        for (; s + 3 <= total; s += 3) {
+        for (; s + 4 <= total; s += 4) {
             body(s, 1, 2);
-            body(s + 1, 2, 0);
-            body(s + 2, 0, 1);
+            body(s + 1, 2, 3);
+            body(s + 2, 3, 0);
+            body(s + 3, 0, 1);
         }
         if (s < total) body(s, 1, 2);
-        if (s + 1 < total) body(s + 1, 2, 0);
+        if (s + 1 < total) body(s + 1, 2, 3);
+        if (s + 2 < total) body(s + 2, 3, 0);
         return;
     }
 

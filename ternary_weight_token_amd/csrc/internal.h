@@ -131,6 +131,11 @@ double gemm_pipe_estimate_us(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_pipe(int tn_force, const int8_t *q, const float *s_x, const uint8_t *packed,
                             const float *s_w, int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc,
                             hipStream_t st);
+// measurement probes (probe.hip)
+hipError_t launch_probe_stream_read(const void *buf, int64_t bytes, int64_t blocks, uint32_t key, uint32_t *sink,
+                                    hipStream_t st);
+hipError_t launch_probe_mfma_i8(int64_t blocks, int64_t iters, uint32_t key, uint32_t *sink, hipStream_t st);
+double probe_mfma_i8_ops(int64_t blocks, int64_t iters);
 hipError_t launch_linear_generic(const int8_t *q, const float *s_x, const uint8_t *packed,
                                  const float *s_w, int64_t M, int64_t N, int64_t K, const OutSpec &y,
                                  int32_t *acc, hipStream_t st);

@@ -12,13 +12,13 @@ import pytest
 import ternary_weight_token_amd as tw
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "bitnet.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("bitnet.h", "bitnet_probe.h")]
 
 OK, NULL, SHAPE, ALIGN, HIP, ARG = range(6)
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    src = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"BITNET_API\s+[\w\s\*]+?\b(bitnet_\w+)\s*\(", src)))
 
 
@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 27, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -41,6 +41,24 @@ def test_status_strings(L):
     for s in range(6):
         assert L.bitnet_status_str(s).decode().startswith("BITNET_")
     assert L.bitnet_version() == 100
+
+
+def test_probes_reject_bad_arguments(L):
+    p = ctypes.c_void_p(4096)  # never dereferenced: every call below fails its checks
+    z = None
+    sr, mf = L.bitnet_probe_stream_read, L.bitnet_probe_mfma_i8
+    assert sr(z, 1024, 8, 1, p, z) == NULL
+    assert sr(p, 1024, 8, 1, z, z) == NULL
+    assert sr(p, 1000, 8, 1, p, z) == SHAPE          # bytes % 16
+    assert sr(p, 0, 8, 1, p, z) == SHAPE
+    assert sr(p, 1024, 0, 1, p, z) == SHAPE          # blocks
+    assert sr(p, 1024, 65537, 1, p, z) == SHAPE
+    assert sr(ctypes.c_void_p(4100), 1024, 8, 1, p, z) == ALIGN
+    assert mf(8, 10, 1, z, z) == NULL
+    assert mf(0, 10, 1, p, z) == SHAPE
+    assert mf(8, (1 << 24) + 1, 1, p, z) == SHAPE
+    assert mf(8, 10, 1, ctypes.c_void_p(4098), z) == ALIGN
+    assert L.bitnet_probe_mfma_i8_ops(2, 3) == 2 * 8 * 8 * 3 * 2 * 16 * 16 * 64
 
 
 def test_linear_rejects_bad_arguments(L):

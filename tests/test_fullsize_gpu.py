@@ -8,8 +8,10 @@ checked against the CPU oracle on sampled matrices / rows / columns.
   full, every output checked for finiteness);
 * prefill: M = 2048 on up (2560 -> 6912) and down (6912 -> 2560), natural
   density and 30 / 50 / 70 % nonzero codes, 160 sampled output columns;
+* prefill as timed (y only, and bias + bf16 y) on 96 sampled token rows;
 * 100B-scale FFN: gate (8192 -> 28672) and down (28672 -> 8192) of layer 0 at
-  M = 1 and M = 8, compared in full;
+  M = 1 and M = 8, compared in full; the 8-layer grouped launch as timed, its
+  last layer compared in full;
 * sign / mask bitplanes and binary weights at the stacked 229376 x 8192 shape,
   3 sampled row slices;
 * the decode step with group-128 weight scales (grouped quant + grouped GEMV).
@@ -251,6 +253,74 @@ def test_prefill_sampled(name, density):
     acc_ref, y_ref = oracle.linear(q_ref, sx_ref, np.ascontiguousarray(p_ref[cols]), sw_ref)
     assert np.array_equal(acc.cpu().numpy()[:, cols], acc_ref)
     assert_y(y.cpu().numpy()[:, cols], y_ref)
+
+
+@pytest.mark.parametrize("name", ["up", "down"])
+def test_prefill_timed_form(name):
+    """The prefill GEMM exactly as timed: y only (no int32 accumulators requested,
+    so the kernel takes its y-only store path), and the bias + bf16 form, at
+    M = 2048 on the full N = 6912 / 2560; 96 sampled token rows (the first and
+    last, and rows in every 128-row tile) compared over all N columns."""
+    x, w = W.prefill_inputs(name, None)
+    N, K = w.shape
+    p_ref, sw_ref = oracle.pack(w.numpy(), 1e-5)
+    q_ref, sx_ref = oracle.quant_act(bits_np(x))
+    p, sw = tw.pack_weights(w.to(DEV), 1e-5)
+    q, sx = tw.quant_act(x.to(DEV))
+    y = torch.full((2048, N), float("nan"), dtype=torch.float32, device=DEV)
+    tw.bitnet_linear(q, sx, p, sw, y)
+    bias = torch.linspace(-1.0, 1.0, N, dtype=torch.float32)
+    yb = tw.linear(q, sx, p, sw, bias=bias.to(DEV), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 2047], np.arange(16) * 128 + rng.integers(0, 128, 16),
+                                     rng.choice(2048, 78, replace=False)]))
+    qs = np.ascontiguousarray(q_ref[rows])
+    _, y_ref = oracle.linear(qs, np.ascontiguousarray(sx_ref[rows]), p_ref, sw_ref)
+    assert_y(y.cpu().numpy()[rows], y_ref)
+    _, yb_ref = oracle.linear(qs, np.ascontiguousarray(sx_ref[rows]), p_ref, sw_ref, bias=bias.numpy())
+    got = yb.cpu().view(torch.int16).numpy().view(np.uint16)[rows]
+    assert np.array_equal(got, oracle.to_bf16(yb_ref))
+    assert torch.isfinite(y).all()
+
+
+def test_ffn_100b_grouped_timed_form():
+    """The 100B-scale FFN stream exactly as timed: 8 layers x {gate, up, down} in one
+    grouped launch at M = 1 (the decode GEMV) and M = 8 (the MFMA decode kernel);
+    the last layer's three matrices compared in full, every output finite."""
+    mats = W.ffn_100b(8)
+    sample = 7
+    packed, sws, host_w = [], [], {}
+    for i, m in enumerate(mats):
+        w = W.weights(m, DEV)
+        p, s = tw.pack_weights(w, 1e-5)
+        packed.append(p)
+        sws.append(s)
+        if m.layer == sample:
+            host_w[i] = w.cpu().numpy()
+        del w
+    refs = {i: oracle.pack(wh, 1e-5) for i, wh in host_w.items()}
+    host_w.clear()
+    for M in (1, 8):
+        xs = [W.ffn_100b_activations(l, M, DEV) for l in range(8)]
+        qx = [[tw.quant_act(x) for x in xl] for xl in xs]
+        ys = [torch.full((M, m.N), float("nan"), dtype=torch.float32, device=DEV) for m in mats]
+        accs = [torch.empty((M, m.N), dtype=torch.int32, device=DEV) if m.layer == sample else None for m in mats]
+        plan = tw.bitnet_grouped_plan_linear(
+            [(qx[m.layer][m.slot][0], qx[m.layer][m.slot][1], packed[i], sws[i], ys[i], accs[i])
+             for i, m in enumerate(mats)])
+        plan.launch()
+        torch.cuda.synchronize()
+        for y in ys:
+            assert torch.isfinite(y).all()
+        for i, (p_ref, sw_ref) in refs.items():
+            m = mats[i]
+            assert sws[i].item() == sw_ref
+            q_ref, sx_ref = oracle.quant_act(bits_np(xs[m.layer][m.slot]))
+            acc_ref, y_ref = oracle.linear(q_ref, sx_ref, p_ref, sw_ref)
+            assert np.array_equal(accs[i].cpu().numpy(), acc_ref), (M, m.name)
+            assert_y(ys[i].cpu().numpy(), y_ref)
+        del xs, qx, ys, accs, plan
 
 
 @pytest.mark.parametrize("which", [0, 2])  # gate (8192 -> 28672), down (28672 -> 8192)
