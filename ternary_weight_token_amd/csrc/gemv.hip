@@ -26,7 +26,10 @@
 #include "internal.h"
 
 #ifndef BITNET_GROUPED_RG
-#define BITNET_GROUPED_RG 4
+#define BITNET_GROUPED_RG 2      // row groups of 8 per wavefront, grouped launch (q staged)
+#endif
+#ifndef BITNET_FUSED_RG
+#define BITNET_FUSED_RG 4        // row groups of 8 per wavefront, fused launch
 #endif
 #ifndef BITNET_GROUPED_DOT8
 #define BITNET_GROUPED_DOT8 1
@@ -721,6 +724,7 @@ __global__ __launch_bounds__(256) void gemv_grouped_kernel(const uint8_t *__rest
 // staging step (one segment, so the row max covers the whole row).  The workgroup of
 // row block 0 also writes q and s_x out when the descriptor asks for them.
 constexpr int kFusedNW = BITNET_FUSED_NW;
+constexpr int kFusedRG = BITNET_FUSED_RG;
 
 // PRO: the mask of paths the plan's problems use (kFusedProNorm: an RMSNorm;
 // kFusedProSwiglu: fp32 input rows and gate / up pairs with the SwiGLU epilogue);
@@ -735,16 +739,16 @@ __global__ __launch_bounds__(64 * kFusedNW) __attribute__((amdgpu_waves_per_eu(P
 void gemv_fused_grouped_kernel(const uint8_t *__restrict__ plan) {
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
     __shared__ int sq[1];
-    __shared__ int red[kFusedNW * 8 * kGroupedRG];
+    __shared__ int red[kFusedNW * 8 * kFusedRG];
     __shared__ uint32_t qred[kFusedNW];
     __shared__ double dred[2 * kFusedNW];
     __shared__ float s_lds;
-    __shared__ float ypair[(PRO & kFusedProSwiglu) ? kFusedNW * 8 * kGroupedRG : 1];
+    __shared__ float ypair[(PRO & kFusedProSwiglu) ? kFusedNW * 8 * kFusedRG : 1];
     const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
     auto entry = [&](uint32_t b) {
         const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[b];
         const FusedDescDev d = reinterpret_cast<const FusedDescDev *>(plan + h->desc_offset)[e.desc];
-        const int rows = kFusedNW * 8 * kGroupedRG;
+        const int rows = kFusedNW * 8 * kFusedRG;
         const bool first = e.local == 0;
         constexpr bool D8 = BITNET_GROUPED_DOT8 != 0, NTL = BITNET_GEMV_NT != 0;
         // a gate / up pair covers half the rows per workgroup (each row twice)
@@ -754,11 +758,11 @@ void gemv_fused_grouped_kernel(const uint8_t *__restrict__ plan) {
         auto tile = [&](const auto &stage, bool as_pair) {
             using S = std::decay_t<decltype(stage)>;
             if ((PRO & kFusedProSwiglu) && as_pair)
-                gemv_lds_tile<1, kGroupedRG, D8, NTL, kFusedNW, S, false, true>(
+                gemv_lds_tile<1, kFusedRG, D8, NTL, kFusedNW, S, false, true>(
                     stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K, OutSpec{d.y, nullptr, 0}, nullptr, row_base, 0, 1,
                     d.K >> 6, dyn, sq, red, nullptr, d.packed2, d.s_w2, ypair);
             else
-                gemv_lds_tile<1, kGroupedRG, D8, NTL, kFusedNW>(stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K,
+                gemv_lds_tile<1, kFusedRG, D8, NTL, kFusedNW>(stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K,
                                                                  OutSpec{d.y, nullptr, 0}, d.acc, row_base, 0, 1,
                                                                  d.K >> 6, dyn, sq, red);
         };
@@ -804,7 +808,7 @@ hipError_t launch_gemv_fused_grouped(const void *plan_dev, uint32_t blocks, uint
 }
 
 uint32_t gemv_grouped_rows_per_block() { return 4 * 8 * kGroupedRG; }
-uint32_t gemv_fused_rows_per_block() { return kFusedNW * 8 * kGroupedRG; }
+uint32_t gemv_fused_rows_per_block() { return kFusedNW * 8 * kFusedRG; }
 uint32_t gemv_fused_threads() { return 64 * kFusedNW; }
 uint32_t gemv_grouped_threads() { return 256; }
 uint32_t gemv_grouped_lds_bytes(int64_t K, bool grp) {

@@ -375,7 +375,8 @@ def test_linear_plan_weight_groups(L):
     assert L.bitnet_grouped_plan_linear(arr, 2, buf, nb) == OK
     hdr = (ctypes.c_uint32 * 8).from_buffer_copy(buf.raw[:32])
     assert hdr[7] == 2                          # GEMV with the group-wise path, even with M = 3
-    assert hdr[3] == 3 + 2 * 3                  # GEMV blocks: one per 128 rows and token
+    R = hdr[5]                                  # GEMV blocks: one per R rows and token
+    assert R > 0 and hdr[3] == -(-300 // R) + 3 * -(-200 // R)
     for w_group in (96, 32, -64):               # not dividing K / not a multiple of 64
         bad = (D * 1)(D(a16, a16, a16, a16, a16, 0, 1, 300, 2560, w_group))
         assert L.bitnet_grouped_plan_linear(bad, 1, buf, nb) == SHAPE
