@@ -301,12 +301,18 @@ typedef struct bitnet_linear_desc {
     const float *s_x;       /* (device) [M]      */
     const uint8_t *packed;  /* (device) [N][K/4] */
     const float *s_w;       /* (device) [1], or [N][K/w_group] */
-    float *y;               /* (device) [M][N]   */
+    void *y;                /* (device) [M][N], fp32 or bf16 (y_dtype), 4- / 2-byte aligned */
     int32_t *acc;           /* (device) [M][N] or NULL */
     int64_t M, N, K;
     int64_t w_group;        /* weight-scale granularity as in bitnet_linear_ex: 0, K, or
                                a multiple of 64 dividing K (a plan holding any of the
                                latter runs the decode GEMV for all its problems) */
+    const float *bias;      /* (device) [N] fp32, 4-byte aligned, or NULL: added after the
+                               rescale, as in bitnet_linear_ex (page chenxutan.com sec. 3.1,
+                               the bias of BitLinear) */
+    int32_t y_dtype;        /* BITNET_F32 (0) or BITNET_BF16: y rounded once to fp32, then
+                               to bf16 nearest-even, as in bitnet_linear_ex */
+    int32_t reserved;       /* 0 */
 } bitnet_linear_desc;
 
 typedef struct bitnet_quant_desc {
@@ -417,6 +423,11 @@ typedef struct bitnet_fused_desc {
                                the sign / mask bitplanes [N][K/32][8] of the same weights (plain
                                rows only: no norm_gain, x_f32 or packed_up; K <= 51584).  Every
                                descriptor of a plan has the same format. */
+    int32_t y_dtype;        /* BITNET_F32 (0) or BITNET_BF16 for y (2-byte aligned for bf16):
+                               rounded once to fp32, then to bf16 nearest-even; 2-bit codes only */
+    const float *bias;      /* (device) [N] fp32, 4-byte aligned, or NULL: added after the
+                               rescale (page chenxutan.com sec. 3.1, the bias of BitLinear);
+                               2-bit codes only, and not on a gate / up pair */
 } bitnet_fused_desc;
 
 BITNET_API size_t bitnet_grouped_plan_fused_bytes(int count, const bitnet_fused_desc *descs);

@@ -26,7 +26,8 @@ class BitnetError(RuntimeError):
 class _LinearDesc(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("s_x", ctypes.c_void_p), ("packed", ctypes.c_void_p),
                 ("s_w", ctypes.c_void_p), ("y", ctypes.c_void_p), ("acc", ctypes.c_void_p),
-                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("w_group", ctypes.c_int64)]
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("w_group", ctypes.c_int64),
+                ("bias", ctypes.c_void_p), ("y_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class _FusedDesc(ctypes.Structure):
@@ -35,7 +36,7 @@ class _FusedDesc(ctypes.Structure):
                 ("s_x", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("norm_gain", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
                 ("x_f32", ctypes.c_void_p), ("packed_up", ctypes.c_void_p), ("s_w_up", ctypes.c_void_p),
-                ("weight_fmt", ctypes.c_int32)]
+                ("weight_fmt", ctypes.c_int32), ("y_dtype", ctypes.c_int32), ("bias", ctypes.c_void_p)]
 
 
 class _QuantDesc(ctypes.Structure):
@@ -282,14 +283,26 @@ class GroupedPlan:
         _check(f(ctypes.cast(self.host, ctypes.c_void_p), _ptr(self.dev), _stream(stream)))
 
 
+def _out_args(y, bias, M, N, where):
+    """y: fp32 or bf16 [M][N]; bias: fp32 [N] or None -> (y_dtype, bias pointer)."""
+    if not isinstance(y, torch.Tensor) or y.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"{where}: y must be an fp32 or bf16 tensor")
+    _arg(y, y.dtype, (M, N), f"{where}: y")
+    if bias is not None:
+        _arg(bias, torch.float32, (N,), f"{where}: bias")
+    return (1 if y.dtype == torch.bfloat16 else 0), (0 if bias is None else bias.data_ptr())
+
+
 def bitnet_grouped_plan_linear(problems, device=None) -> GroupedPlan:
-    """problems: list of (q, s_x, packed, s_w, y, acc_or_None[, w_group]); w_group as
-    in bitnet_linear_ex (s_w [N][K / w_group] when it is nonzero)."""
+    """problems: list of (q, s_x, packed, s_w, y, acc_or_None[, w_group[, bias]]); w_group
+    as in bitnet_linear_ex (s_w [N][K / w_group] when it is nonzero); y fp32 or bf16;
+    bias an fp32 [N] added after the rescale, or None."""
     arr = (_LinearDesc * len(problems))()
     refs = []
     for i, prob in enumerate(problems):
         q, s_x, packed, s_w, y, acc = prob[:6]
-        w_group = int(prob[6]) if len(prob) > 6 else 0
+        w_group = int(prob[6]) if len(prob) > 6 and prob[6] is not None else 0
+        bias = prob[7] if len(prob) > 7 else None
         if not isinstance(q, torch.Tensor) or q.dim() != 2 or not isinstance(packed, torch.Tensor) or packed.dim() != 2:
             raise ValueError(f"problem {i}: q must be [M][K] and packed [N][K/4]")
         M, K = q.shape
@@ -302,13 +315,14 @@ def bitnet_grouped_plan_linear(problems, device=None) -> GroupedPlan:
         _dev(s_w, torch.float32, f"problem {i}: s_w")
         if s_w.numel() != (N * (K // w_group) if w_group else 1):
             raise ValueError(f"problem {i}: s_w must hold {'N * K / w_group' if w_group else 'one'} scale(s)")
-        _arg(y, torch.float32, (M, N), f"problem {i}: y")
+        y_dtype, bias_p = _out_args(y, bias, M, N, f"problem {i}")
         if acc is not None:
             _arg(acc, torch.int32, (M, N), f"problem {i}: acc")
-        _same_device(f"problem {i}", q, s_x, packed, s_w, y, acc)
+        _same_device(f"problem {i}", q, s_x, packed, s_w, y, acc, bias)
         arr[i] = _LinearDesc(q.data_ptr(), s_x.data_ptr(), packed.data_ptr(), s_w.data_ptr(),
-                             y.data_ptr(), 0 if acc is None else acc.data_ptr(), M, packed.shape[0], K, w_group)
-        refs.append((q, s_x, packed, s_w, y, acc))
+                             y.data_ptr(), 0 if acc is None else acc.data_ptr(), M, packed.shape[0], K, w_group,
+                             bias_p, y_dtype, 0)
+        refs.append((q, s_x, packed, s_w, y, acc, bias))
     n = lib().bitnet_grouped_plan_bytes(len(problems), 1, ctypes.cast(arr, ctypes.c_void_p))
     buf = ctypes.create_string_buffer(n)
     _check(lib().bitnet_grouped_plan_linear(ctypes.cast(arr, ctypes.c_void_p), len(problems),
@@ -343,17 +357,20 @@ def bitnet_grouped_plan_quant(problems, device=None) -> GroupedPlan:
 
 def bitnet_grouped_plan_fused(problems, device=None) -> GroupedPlan:
     """problems: list of (x, packed, s_w, y, acc_or_None, q_or_None, s_x_or_None
-    [, norm_gain, norm_eps]).  x is a bf16 [1][K] row (quantized inside the launch,
-    after an RMSNorm with the fp32 gain [K] when one is given) or an fp32 [1][K] row
-    (quantized the same way, no norm).  packed and s_w are one matrix, or the pairs
+    [, norm_gain, norm_eps[, bias]]).  x is a bf16 [1][K] row (quantized inside the
+    launch, after an RMSNorm with the fp32 gain [K] when one is given) or an fp32 [1][K]
+    row (quantized the same way, no norm).  packed and s_w are one matrix, or the pairs
     (packed_gate, packed_up) and (s_w_gate, s_w_up) of a SwiGLU feed-forward part,
     whose y gets fp32(silu(y_gate) y_up).  Weights as sign / mask bitplanes are given
-    as [N][K/32][8] tensors (pack_bitplanes), every problem of the plan alike."""
+    as [N][K/32][8] tensors (pack_bitplanes), every problem of the plan alike.  y is
+    fp32 or bf16; bias an fp32 [N] added after the rescale (not on pairs) or None;
+    bitplane plans take fp32 y and no bias."""
     arr = (_FusedDesc * len(problems))()
     refs = []
     for i, prob in enumerate(problems):
         x, packed, s_w, y, acc, q, s_x = prob[:7]
         gain, eps = (prob[7], float(prob[8])) if len(prob) > 7 and prob[7] is not None else (None, 0.0)
+        bias = prob[9] if len(prob) > 9 else None
         if not isinstance(x, torch.Tensor) or x.dtype not in (torch.bfloat16, torch.float32):
             raise TypeError("x must be a bf16 or fp32 tensor")
         if x.dim() != 2:
@@ -377,7 +394,7 @@ def bitnet_grouped_plan_fused(problems, device=None) -> GroupedPlan:
             _arg(s_w_up, torch.float32, (1,), f"problem {i}: s_w_up")
             pu, su = packed_up.data_ptr(), s_w_up.data_ptr()
             refs.append((packed_up, s_w_up))
-        _arg(y, torch.float32, (M, N), f"problem {i}: y")
+        y_dtype, bias_p = _out_args(y, bias, M, N, f"problem {i}")
         if acc is not None:
             _arg(acc, torch.int32, (M, N), f"problem {i}: acc")
         if q is not None:
@@ -386,12 +403,12 @@ def bitnet_grouped_plan_fused(problems, device=None) -> GroupedPlan:
             _arg(s_x, torch.float32, (M,), f"problem {i}: s_x")
         if gain is not None:
             _arg(gain, torch.float32, (K,), f"problem {i}: norm_gain")
-        _same_device(f"problem {i}", x, packed, s_w, y, acc, q, s_x, gain, packed_up, s_w_up)
+        _same_device(f"problem {i}", x, packed, s_w, y, acc, q, s_x, gain, packed_up, s_w_up, bias)
         arr[i] = _FusedDesc(xp, packed.data_ptr(), s_w.data_ptr(), y.data_ptr(),
                             0 if acc is None else acc.data_ptr(), 0 if q is None else q.data_ptr(),
                             0 if s_x is None else s_x.data_ptr(), M, packed.shape[0], K,
-                            0 if gain is None else gain.data_ptr(), eps, xf, pu, su, fmt)
-        refs.append((x, packed, s_w, y, acc, q, s_x, gain))
+                            0 if gain is None else gain.data_ptr(), eps, xf, pu, su, fmt, y_dtype, bias_p)
+        refs.append((x, packed, s_w, y, acc, q, s_x, gain, bias))
     n = lib().bitnet_grouped_plan_fused_bytes(len(problems), ctypes.cast(arr, ctypes.c_void_p))
     buf = ctypes.create_string_buffer(n)
     _check(lib().bitnet_grouped_plan_fused(ctypes.cast(arr, ctypes.c_void_p), len(problems),

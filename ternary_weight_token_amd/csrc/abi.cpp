@@ -311,8 +311,21 @@ static uint64_t linear_blocks(const bitnet_linear_desc &d, uint32_t variant) {
     return ((uint64_t)d.N + rows - 1) / rows * (uint64_t)d.M;
 }
 
+// The output options of a descriptor: y's dtype and alignment, the bias.
+static int check_desc_output(const void *y, int32_t y_dtype, const float *bias) {
+    if (y_dtype != BITNET_F32 && y_dtype != BITNET_BF16) return fail(BITNET_ERR_ARG, "unknown output dtype");
+    if (!aligned(y, y_dtype == BITNET_BF16 ? 2 : 4)) return fail(BITNET_ERR_ALIGN, "y must be aligned to its element size");
+    if (bias && !aligned(bias, 4)) return fail(BITNET_ERR_ALIGN, "bias must be 4-byte aligned");
+    return BITNET_OK;
+}
+
 static int check_linear_desc(const bitnet_linear_desc &d) {
-    int st = check_linear(d.q, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, d.y, d.acc);
+    int st = check_dims(d.M, d.N, d.K);
+    if (st) return st;
+    if (!d.q || !d.s_x || !d.packed || !d.s_w || !d.y) return fail(BITNET_ERR_NULL, "null pointer");
+    if (!aligned(d.s_x, 4) || !aligned(d.s_w, 4) || (d.acc && !aligned(d.acc, 4)))
+        return fail(BITNET_ERR_ALIGN, "s_x, s_w and acc must be 4-byte aligned");
+    st = check_desc_output(d.y, d.y_dtype, d.bias);
     if (st) return st;
     if (d.M < 1 || d.M > kGemvMaxM || d.N < 1) return fail(BITNET_ERR_SHAPE, "grouped linear needs 1 <= M <= 16, N >= 1");
     if (!linear_fast(d.q, d.packed, d.K)) return fail(BITNET_ERR_ALIGN, "grouped linear needs K % 64 == 0 and 16-byte aligned q/packed");
@@ -347,8 +360,13 @@ static int check_fused_desc(const bitnet_fused_desc &d) {
     if (d.K > gemv_fused_max_k()) return fail(BITNET_ERR_SHAPE, "fused linear needs K <= 52224");
     if (d.K % 64 != 0 || !aligned(d.x, 16) || !aligned(d.packed, 16) || (d.q && !aligned(d.q, 16)))
         return fail(BITNET_ERR_ALIGN, "fused linear needs K % 64 == 0 and 16-byte aligned x, packed and q");
-    if (!aligned(d.s_w, 4) || !aligned(d.y, 4) || (d.acc && !aligned(d.acc, 4)) || (d.s_x && !aligned(d.s_x, 4)))
-        return fail(BITNET_ERR_ALIGN, "s_w, y, acc and s_x must be 4-byte aligned");
+    if (!aligned(d.s_w, 4) || (d.acc && !aligned(d.acc, 4)) || (d.s_x && !aligned(d.s_x, 4)))
+        return fail(BITNET_ERR_ALIGN, "s_w, acc and s_x must be 4-byte aligned");
+    st = check_desc_output(d.y, d.y_dtype, d.bias);
+    if (st) return st;
+    if (d.weight_fmt == BITNET_FMT_BITPLANES && (d.bias || d.y_dtype != BITNET_F32))
+        return fail(BITNET_ERR_ARG, "bitplane weights take no bias and an fp32 y");
+    if (d.packed_up && d.bias) return fail(BITNET_ERR_ARG, "a gate / up pair takes no bias");
     if (d.norm_gain) {
         if (!aligned(d.norm_gain, 16)) return fail(BITNET_ERR_ALIGN, "norm_gain must be 16-byte aligned");
         if (!(d.norm_eps >= 0.0f) || d.norm_eps > 3.4e38f) return fail(BITNET_ERR_ARG, "norm_eps must be finite and >= 0");
@@ -422,7 +440,7 @@ BITNET_API int bitnet_grouped_plan_linear(const bitnet_linear_desc *descs, int c
     for (int i = 0; i < count; ++i) {
         const bitnet_linear_desc &d = descs[i];
         dd[i] = LinearDescDev{d.q, d.s_x, d.packed, d.s_w, d.y, d.acc, (int32_t)d.M, (int32_t)d.N, (int32_t)d.K,
-                              (int32_t)d.w_group};
+                              (int32_t)d.w_group, d.bias, d.y_dtype == BITNET_BF16 ? 1 : 0, 0};
     }
     // Workgroups are dispatched roughly in table order: put the longest ones (largest
     // K, i.e. most bytes per row) first so that the short ones fill the tail.
@@ -533,7 +551,8 @@ BITNET_API int bitnet_grouped_plan_fused(const bitnet_fused_desc *descs, int cou
     for (int i = 0; i < count; ++i) {
         const bitnet_fused_desc &d = descs[i];
         dd[i] = FusedDescDev{d.x, d.packed, d.s_w, d.y, d.acc, d.q, d.s_x, (int32_t)d.M, (int32_t)d.N, (int32_t)d.K, 0,
-                             d.norm_gain, d.norm_gain ? d.norm_eps : 0.0f, 0, d.x_f32, d.packed_up, d.s_w_up};
+                             d.norm_gain, d.norm_gain ? d.norm_eps : 0.0f, 0, d.x_f32, d.packed_up, d.s_w_up,
+                             d.bias, d.y_dtype == BITNET_BF16 ? 1 : 0, 0};
     }
     // longest rows first, as for linear plans
     std::vector<int> order(count);

@@ -411,7 +411,8 @@ __global__ __launch_bounds__(256) void gemv_bits_fused_grouped_kernel(const uint
     const bool first = e.local == 0;
     bits_tile<2, kBitsFusedRG>(
         StagePlanesQuant<2>{d.x, d.K, first ? d.q : nullptr, first ? d.s_x : nullptr, &s_lds, qred}, &s_lds,
-        d.packed, d.s_w, d.N, d.K, (int)e.local * (4 * 8 * kBitsFusedRG), 1, d.y, d.acc, lds, &sq, red);
+        d.packed, d.s_w, d.N, d.K, (int)e.local * (4 * 8 * kBitsFusedRG), 1, static_cast<float *>(d.y), d.acc, lds, &sq,
+        red);
 }
 
 uint32_t bits_fused_rows_per_block() { return 4 * 8 * kBitsFusedRG; }

@@ -704,7 +704,7 @@ __global__ __launch_bounds__(256) void gemv_grouped_kernel(const uint8_t *__rest
     const int rows = 4 * 8 * kGroupedRG;
     const int rowblocks = (d.N + rows - 1) / rows;
     const int rb = (int)(e.local % rowblocks), mt = (int)(e.local / rowblocks);
-    const OutSpec out{d.y, nullptr, 0, d.w_group};
+    const OutSpec out = d.out();
     constexpr bool D8 = BITNET_GROUPED_DOT8 != 0, NTL = BITNET_GEMV_NT != 0;
     if (GRP && d.w_group > 0 && d.w_group < d.K) {
         const int seg = segment_chunks(d.K >> 6, kGroupedMT, kLdsChunkDw + 1);
@@ -759,11 +759,11 @@ void gemv_fused_grouped_kernel(const uint8_t *__restrict__ plan) {
             using S = std::decay_t<decltype(stage)>;
             if ((PRO & kFusedProSwiglu) && as_pair)
                 gemv_lds_tile<1, kFusedRG, D8, NTL, kFusedNW, S, false, true>(
-                    stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K, OutSpec{d.y, nullptr, 0}, nullptr, row_base, 0, 1,
+                    stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K, OutSpec{d.y, nullptr, d.bf16, 0}, nullptr, row_base, 0, 1,
                     d.K >> 6, dyn, sq, red, nullptr, d.packed2, d.s_w2, ypair);
             else
                 gemv_lds_tile<1, kFusedRG, D8, NTL, kFusedNW>(stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K,
-                                                                 OutSpec{d.y, nullptr, 0}, d.acc, row_base, 0, 1,
+                                                                 OutSpec{d.y, d.bias, d.bf16, 0}, d.acc, row_base, 0, 1,
                                                                  d.K >> 6, dyn, sq, red);
         };
         int8_t *q_out = first ? d.q : nullptr;

@@ -47,10 +47,13 @@ struct PlanHeader {            // 64 bytes
     uint64_t desc_offset, table_offset, total_bytes, reserved2;
 };
 
-struct LinearDescDev {         // 64 bytes, device layout
+struct LinearDescDev {         // 80 bytes, device layout
     const int8_t *q; const float *s_x; const uint8_t *packed; const float *s_w;
-    float *y; int32_t *acc;
+    void *y; int32_t *acc;
     int32_t M, N, K, w_group;  // w_group as OutSpec::w_group
+    const float *bias;         // [N] or null
+    int32_t bf16, pad;         // y as bf16 when set
+    __host__ __device__ OutSpec out() const { return OutSpec{y, bias, bf16, w_group}; }
 };
 
 struct QuantDescDev {          // 32 bytes
@@ -58,14 +61,16 @@ struct QuantDescDev {          // 32 bytes
     int32_t M, K;
 };
 
-struct FusedDescDev {          // 112 bytes: (RMSNorm +) quantization + linear of one token row
+struct FusedDescDev {          // 128 bytes: (RMSNorm +) quantization + linear of one token row
     const uint16_t *x; const uint8_t *packed; const float *s_w;
-    float *y; int32_t *acc; int8_t *q; float *s_x;
+    void *y; int32_t *acc; int8_t *q; float *s_x;
     int32_t M, N, K, pad;
     const float *gain; float eps; int32_t pad2;
     const float *xf;           // fp32 input row instead of x, or null
     const uint8_t *packed2;    // up projection of a gate / up pair (SwiGLU epilogue), or null
     const float *s_w2;
+    const float *bias;         // [N] or null (not on pairs)
+    int32_t bf16, pad3;        // y as bf16 when set
 };
 
 struct BlockEntry { uint32_t desc, local; };

@@ -415,7 +415,7 @@ __global__ __launch_bounds__(64 * kGroupedSkNW) void skinny_grouped_kernel(const
     const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
     const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[blockIdx.x];
     const LinearDescDev d = reinterpret_cast<const LinearDescDev *>(plan + h->desc_offset)[e.desc];
-    skinny_lds_tile<kGroupedSkRG, kGroupedSkUN, BITNET_GROUPED_SK_NT != 0>(d.q, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, OutSpec{d.y, nullptr, 0, d.w_group}, d.acc,
+    skinny_lds_tile<kGroupedSkRG, kGroupedSkUN, BITNET_GROUPED_SK_NT != 0>(d.q, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, d.out(), d.acc,
                                                          (int)e.local * kGroupedSkNW * 16 * kGroupedSkRG, qs, sq);
 }
 

@@ -401,3 +401,50 @@ def test_linear_plan_lds_covers_every_descriptor(L):
     assert L.bitnet_grouped_plan_linear(alone, 1, buf, nb) == OK
     hdr = (ctypes.c_uint32 * 8).from_buffer_copy(buf.raw[:32])
     assert 0 < hdr[6] <= 64 * 1024
+
+
+def test_plan_output_options_checks(L):
+    """Bias and bf16 y per descriptor: dtype and alignment checks, and the forms that
+    take neither (a gate / up pair takes no bias; bitplane plans take fp32 y, no bias)."""
+    D, F = tw._LinearDesc, tw._FusedDesc
+    a16 = 4096
+    n = ctypes.c_float
+    buf = ctypes.create_string_buffer(8192)
+
+    def lin(**kw):
+        d = D(a16, a16, a16, a16, a16, 0, 1, 100, 2560, 0)
+        for k, v in kw.items():
+            setattr(d, k, v)
+        return L.bitnet_grouped_plan_linear((D * 1)(d), 1, buf, 8192)
+
+    assert lin() == OK
+    assert lin(bias=a16, y_dtype=1) == OK
+    assert lin(y_dtype=2) == ARG
+    assert lin(y=a16 + 2) == ALIGN                 # fp32 y: 4-byte aligned
+    assert lin(y=a16 + 2, y_dtype=1) == OK         # bf16 y: 2-byte aligned
+    assert lin(bias=a16 + 2) == ALIGN
+
+    def fused(**kw):
+        d = F(a16, a16, a16, a16, 0, 0, 0, 1, 300, 2560, 0, n(0.0), 0, 0, 0, 0)
+        for k, v in kw.items():
+            setattr(d, k, v)
+        return L.bitnet_grouped_plan_fused((F * 1)(d), 1, buf, 8192)
+
+    assert fused() == OK
+    assert fused(bias=a16, y_dtype=1) == OK
+    assert fused(y_dtype=3) == ARG
+    assert fused(y=a16 + 1, y_dtype=1) == ALIGN
+    assert fused(bias=a16 + 1) == ALIGN
+    assert fused(packed_up=a16, s_w_up=a16, y_dtype=1) == OK
+    assert fused(packed_up=a16, s_w_up=a16, bias=a16) == ARG      # no bias on a pair
+    assert fused(weight_fmt=2, bias=a16) == ARG                   # bitplanes: no bias
+    assert fused(weight_fmt=2, y_dtype=1) == ARG                  # bitplanes: fp32 y
+
+
+def test_plan_builders_check_output_options():
+    import torch
+    q = torch.zeros((1, 64), dtype=torch.int8)
+    with pytest.raises(ValueError):
+        # a host tensor is refused before anything else
+        tw.bitnet_grouped_plan_linear([(q, torch.zeros(1), torch.zeros((4, 16), dtype=torch.uint8), torch.zeros(1),
+                                        torch.zeros((1, 4), dtype=torch.float16), None)])

@@ -388,6 +388,96 @@ def test_grouped_plan_weight_scales(mixed_m):
                 assert_y_within(pr[4].cpu().numpy(), y_ref, REL, slack)
 
 
+# ----------------------------------------------------------------- bias and bf16 y in plans
+
+def _bias(key, N):
+    return (synth.normal(synth.stream_key(key, 21), N).float().numpy() * 0.3).astype(np.float32)
+
+
+@pytest.mark.parametrize("variant", ["gemv", "groups", "mfma"])
+def test_grouped_plan_bias_bf16(variant):
+    """Grouped linear plans whose problems carry a bias and / or a bf16 y (each
+    combination), on the plan's three kernels: the decode GEMV (M = 1), the GEMV with
+    group-wise scales, the MFMA decode kernel (some M > 1).  y is the oracle's
+    fp32(acc c_m + bias), bf16 rounded from it."""
+    shapes = [(300, 2560, 0), (129, 6912, 0), (64, 64, 0), (700, 640, 0)]
+    if variant == "groups":
+        shapes += [(200, 2560, 128), (70, 640, 64)]
+    opts = [(False, False), (True, False), (False, True), (True, True)]
+    probs, refs = [], []
+    for i, (N, K, G) in enumerate(shapes):
+        M = 1 + (i % 3) if variant == "mfma" else (1 + i % 2 if variant == "groups" else 1)
+        with_bias, bf16 = opts[i % 4]
+        key = synth.stream_key(335, i, M)
+        x, q, s = quantized_inputs(key, M, K)
+        b = _bias(key, N) if with_bias else None
+        if G:
+            w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02).numpy()
+            packed, s_w = oracle.pack_grouped(w, G, 1e-5)
+            acc_ref, y_ref = oracle.linear_grouped(q, s, packed, s_w, G, bias=b)
+            slack = _grouped_bound(q, s, packed, s_w, G, K)
+        else:
+            packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
+            s_w = np.array([0.0043 * (i + 1)], np.float32)
+            acc_ref, y_ref = oracle.linear(q, s, packed, s_w[0], bias=b)
+            slack = None
+        refs.append((acc_ref, y_ref, slack, bf16))
+        y = torch.full((M, N), float("nan"), dtype=torch.bfloat16 if bf16 else torch.float32, device=DEV)
+        acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+        probs.append((torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV), torch.from_numpy(packed).to(DEV),
+                      torch.from_numpy(s_w).to(DEV), y, acc, G, None if b is None else torch.from_numpy(b).to(DEV)))
+    plan = tw.bitnet_grouped_plan_linear(probs)
+    for _ in range(2):
+        for pr in probs:
+            pr[4].fill_(float("nan"))
+        plan.launch()
+        torch.cuda.synchronize()
+        for (acc_ref, y_ref, slack, bf16), pr in zip(refs, probs):
+            assert np.array_equal(pr[5].cpu().numpy(), acc_ref)
+            y = pr[4].cpu()
+            if slack is not None:
+                got = y.float().numpy()
+                extra = 2.0 ** -8 * np.abs(y_ref.astype(np.float64)) if bf16 else 0.0
+                assert_y_within(got, y_ref, REL, slack + extra)
+            elif bf16:
+                assert_bf16(y.view(torch.int16).numpy(), y_ref)
+            else:
+                assert_y(y.numpy(), y_ref)
+
+
+def test_fused_plan_bias_bf16():
+    """A fused plan whose rows carry a bias and / or a bf16 y: plain bf16 rows, fp32
+    rows and gate / up pairs (bf16 only: a pair takes no bias)."""
+    cases = [("plain", 300, 2560, True, False), ("plain", 129, 6912, False, True), ("plain", 64, 64, True, True),
+             ("f32", 2560, 6912, True, True), ("f32", 97, 640, True, False), ("pair", 300, 2560, False, True),
+             ("plain", 700, 2560, False, False)]
+    probs, exps = [], []
+    for i, (kind, N, K, with_bias, bf16) in enumerate(cases):
+        key = synth.stream_key(344, i)
+        xin, pw, sw, gain, exp = _fused_case(kind, N, K, key)
+        b = _bias(key, N) if with_bias else None
+        if b is not None:
+            _, exp["y"] = oracle.linear(exp["q"], exp["s"], pw.cpu().numpy(), sw.item(), bias=b)
+        y = torch.full((1, N), float("nan"), dtype=torch.bfloat16 if bf16 else torch.float32, device=DEV)
+        acc = None if kind == "pair" else torch.empty((1, N), dtype=torch.int32, device=DEV)
+        probs.append((xin, pw, sw, y, acc, None, None, None, 0.0, None if b is None else torch.from_numpy(b).to(DEV)))
+        exps.append((kind, exp, bf16))
+    plan = tw.bitnet_grouped_plan_fused(probs)
+    for _ in range(2):
+        for pr in probs:
+            pr[3].fill_(float("nan"))
+        plan.launch()
+        torch.cuda.synchronize()
+        for (kind, exp, bf16), pr in zip(exps, probs):
+            y = pr[3].cpu()
+            if kind != "pair":
+                assert np.array_equal(pr[4].cpu().numpy(), exp["acc"]), kind
+            if bf16:
+                assert_bf16(y.view(torch.int16).numpy(), exp["y"])
+            else:
+                assert_y(y.numpy(), exp["y"])
+
+
 # ----------------------------------------------------------------- RMSNorm + quantization
 
 def _gain(key, K):
@@ -1094,13 +1184,16 @@ def test_grouped_plan_builders_check_tensors():
                             z((1,), torch.float32), z((M, N), torch.float32), z((M, N), torch.int32))
     good = (q, sx, p, sw, y, acc)
     tw.bitnet_grouped_plan_linear([good])
+    tw.bitnet_grouped_plan_linear([(q, sx, p, sw, z((M, N), torch.bfloat16), acc, 0, z((N,), torch.float32))])
     bad_linear = [
         (z((M, K), torch.uint8), sx, p, sw, y, acc),           # q dtype
         (q, z((2,), torch.float32), p, sw, y, acc),             # s_x shape
         (q, sx, z((N, K // 8), torch.uint8), sw, y, acc),       # packed shape
         (q, sx, p, z((2,), torch.float32), y, acc),             # s_w count
         (q, sx, p, sw, z((M, N + 1), torch.float32), acc),      # y shape
-        (q, sx, p, sw, z((M, N), torch.bfloat16), acc),         # y dtype
+        (q, sx, p, sw, z((M, N), torch.float16), acc),          # y dtype (fp32 or bf16 only)
+        (q, sx, p, sw, y, acc, 0, z((N + 1,), torch.float32)),  # bias shape
+        (q, sx, p, sw, y, acc, 0, z((N,), torch.bfloat16)),     # bias dtype
         (q, sx, p, sw, y, z((M, N - 1), torch.int32)),          # acc shape
         (q, sx, p, sw, y, acc, 128),                            # w_group without N * K / 128 scales
     ]
@@ -1121,6 +1214,8 @@ def test_grouped_plan_builders_check_tensors():
                  (x, p, sw, y, None, None, z((M + 1,), torch.float32)),
                  (x, z((N, K // 4 - 1), torch.uint8), sw, y, None, None, None),
                  (x, (p, z((N + 1, K // 4), torch.uint8)), (sw, sw), y, None, None, None),
-                 (x, p, sw, y, None, None, None, z((K + 1,), torch.float32), 1e-6)]:
+                 (x, p, sw, y, None, None, None, z((K + 1,), torch.float32), 1e-6),
+                 (x, p, sw, z((M, N), torch.float16), None, None, None),
+                 (x, p, sw, y, None, None, None, None, 0.0, z((N - 1,), torch.float32))]:
         with pytest.raises(ValueError):
             tw.bitnet_grouped_plan_fused([prob])
