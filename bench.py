@@ -679,7 +679,64 @@ def main() -> int:
                            "scale_bytes": (4 if v == "per_tensor" else sum(p_[1].numel() * 4 for p_ in gpk))}
                 log(f"decode step two launches, scales {v}: {us:.1f} us")
             sec["decode_step_2p4b_weight_scales"] = dres
-            del gpk
+            # the same at 8 tokens (grouped quant + grouped linear): one scale per tensor
+            # runs the MFMA decode kernel; group-128 scales the GEMV (one token per workgroup)
+            xs8 = [W.decode_step_activations(l, dev, 8) for l in range(30)]
+            qs8 = [[torch.empty((8, x.shape[1]), dtype=torch.int8, device=dev) for x in xl] for xl in xs8]
+            sx8 = [[torch.empty(8, dtype=torch.float32, device=dev) for _ in xl] for xl in xs8]
+            ys8 = [torch.empty((8, m.N), dtype=torch.float32, device=dev) for m in mats]
+            qplan8 = tw.bitnet_grouped_plan_quant([(xs8[l][j], qs8[l][j], sx8[l][j]) for l in range(30) for j in range(4)])
+            dres8 = {}
+            for v, plan_probs in (
+                    ("per_tensor", [(qs8[m.layer][m.slot], sx8[m.layer][m.slot], packed[i], sws[i], ys8[i], None)
+                                    for i, m in enumerate(mats)]),
+                    ("group128", [(qs8[m.layer][m.slot], sx8[m.layer][m.slot], gpk[i][0], gpk[i][1], ys8[i], None, 128)
+                                  for i, m in enumerate(mats)])):
+                lp = tw.bitnet_grouped_plan_linear(plan_probs)
+                for _ in range(10):
+                    qplan8.launch(stream)
+                    lp.launch(stream)
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(30):
+                    qplan8.launch(stream)
+                    lp.launch(stream)
+                b.record(stream)
+                torch.cuda.synchronize()
+                us = a.elapsed_time(b) * 1e3 / 30
+                dres8[v] = {"us": round(us, 1), "weight_GBs": round(weight_bytes / (us * 1e-6) / 1e9, 1),
+                            "kernel": "skinny_grouped_kernel" if v == "per_tensor" else "gemv_grouped_kernel<true>"}
+                log(f"decode step M=8 two launches, scales {v}: {us:.1f} us")
+            sec["decode_step_2p4b_M8_weight_scales"] = dres8
+            del gpk, xs8, qs8, sx8, ys8
+            # prefill M = 2048 with one scale per tensor and per group of 128 weights (the
+            # pipelined GEMM's group-wise path: fp32 accumulators per group)
+            pres = {}
+            for name in ("up", "down"):
+                x, w = W.prefill_inputs(name, None, dev)
+                q, sx = tw.quant_act(x)
+                N, K = w.shape
+                y = torch.empty((2048, N), dtype=torch.float32, device=dev)
+                row = {}
+                for v, g in (("per_tensor", 0), ("group128", 128)):
+                    p_, s_ = tw.pack_weights(w, 1e-5) if g == 0 else tw.pack_weights_grouped(w, g, 1e-5)
+                    fn = lambda: tw.bitnet_linear_ex(q, sx, p_, s_, None, y, None, 0, w_group=g)
+                    for _ in range(5):
+                        fn()
+                    a.record(stream)
+                    for _ in range(30):
+                        fn()
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    us = a.elapsed_time(b) * 1e3 / 30
+                    tops = 2.0 * 2048 * N * K / (us * 1e-6) / 1e12
+                    row[v] = {"us": round(us, 2), "int8_tops": round(tops, 1),
+                              "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+                    log(f"prefill {name} M=2048 scales {v}: {us:.1f} us")
+                pres[name] = row
+                del w, x
+            sec["prefill_M2048_weight_scales"] = pres
         line["secondary"] = sec
 
     # ------------------------------------------------------------ CPU baseline

@@ -261,10 +261,14 @@ BITNET_API int bitnet_pack_weights_grouped(const float *w, int64_t N, int64_t K,
  * groups in float64 (any order; the result is within 2^-23 |y| plus 2^-45 times
  * the sum of the terms' magnitudes of the ordered sum); acc is then sum_g acc_g.
  * Group-wise scales (G < K) run on the decode GEMV (kernel 1; needs G % 64 == 0
- * besides its usual conditions) or the general kernel (3); kernel 0 picks the
- * GEMV when it can, at any M (it re-reads the weights once per 8 rows of q);
- * other kernel ids give BITNET_ERR_ARG.  A w_group that is not 0 or a multiple of
- * 4 dividing K gives BITNET_ERR_SHAPE.
+ * besides its usual conditions), the general kernel (3), or the pipelined GEMM
+ * (kernel 2, or tiles 21 / 22) when acc is NULL, K % 128 == 0 and G is 64 or a
+ * multiple of 128: there each group's exact integer sums are scaled into fp32
+ * accumulators (y within 2^-23 |y| plus (K / G + 1) 2^-24 s_x / 127 times the sum
+ * over groups of |acc_g s_w[n][g]|).  Kernel 0 picks the GEMM for M > 16 when it
+ * can, else the GEMV (which re-reads the weights once per 8 rows of q); other
+ * kernel ids, or the GEMM outside its conditions, give BITNET_ERR_ARG.  A w_group
+ * that is not 0 or a multiple of 4 dividing K gives BITNET_ERR_SHAPE.
  *
  * y[m][n] = fp32(acc * c_m + bias[n]) with c_m = (s_x[m] * s_w) / 127, the
  * product and the sum taken in float64 and rounded once to fp32; a bf16 y is

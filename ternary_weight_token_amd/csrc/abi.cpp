@@ -232,10 +232,15 @@ BITNET_API int bitnet_linear_ex(const int8_t *q, const float *s_x, const uint8_t
     if (st) return st;
     if (w_group < 0 || (w_group > 0 && (K % w_group != 0 || w_group % 4 != 0)))
         return fail(BITNET_ERR_SHAPE, "w_group must be 0 or a multiple of 4 dividing K");
-    // group-wise scales below the row length: decode GEMV or general kernel only
+    // group-wise scales below the row length: the decode GEMV, the general kernel, or
+    // the pipelined GEMM (kernel 2, tiles 21 / 22) without acc
     const bool groups = w_group > 0 && w_group < K;
-    if (groups && kernel != 0 && kernel != 1 && kernel != 3)
-        return fail(BITNET_ERR_ARG, "group-wise weight scales need kernel 0, 1 or 3");
+    const bool pipe_tile = kernel == 16 + 5 || kernel == 16 + 6;
+    if (groups && kernel != 0 && kernel != 1 && kernel != 3) {
+        if ((kernel != 2 && !pipe_tile) || acc || !gemm_pipe_groups_ok(M, N, K, w_group))
+            return fail(BITNET_ERR_ARG, "group-wise weight scales need kernel 0, 1 or 3, or the GEMM (2, 21, 22) "
+                                        "with no acc, K % 128 == 0 and w_group 64 or a multiple of 128");
+    }
     if (M == 0 || N == 0) return BITNET_OK;
     if (!q || !s_x || !packed || !s_w || !y) return fail(BITNET_ERR_NULL, "null pointer");
     if (!aligned(s_x, 4) || !aligned(s_w, 4) || (acc && !aligned(acc, 4)) || (bias && !aligned(bias, 4)))
@@ -257,7 +262,8 @@ BITNET_API int bitnet_linear_ex(const int8_t *q, const float *s_x, const uint8_t
     // small) is estimated faster; group-wise scales: the GEMV
     if (kernel == 0) {
         const bool small = N * (K / 4) < ((int64_t)32 << 20);
-        if (groups || (M == 1 && !small)) kernel = 1;
+        if (groups) kernel = (M > kGemvMaxM && !acc && gemm_pipe_groups_ok(M, N, K, w_group)) ? 2 : 1;
+        else if (M == 1 && !small) kernel = 1;
         else if (M <= kGemvMaxM || skinny_estimate_us(M, N, K) <= gemm_estimate_us(M, N, K)) kernel = 4;
         else kernel = 2;
     }

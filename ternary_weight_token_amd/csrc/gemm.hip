@@ -407,7 +407,8 @@ double gemm_estimate_us(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_gemm(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                        int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st) {
-    if (gemm_use_pipe(M, N, K)) return launch_gemm_pipe(0, q, s_x, packed, s_w, M, N, K, y, acc, st);
+    // group-wise scales: the pipelined kernel only
+    if (gemm_use_pipe(M, N, K) || (y.w_group > 0 && y.w_group < K)) return launch_gemm_pipe(0, q, s_x, packed, s_w, M, N, K, y, acc, st);
     return launch_gemm_cfg(gemm_pick(M, N, nullptr), q, s_x, packed, s_w, M, N, K, y, acc, st);
 }
 

@@ -60,7 +60,10 @@ __device__ __forceinline__ int qslot(int r, int c) { return c ^ (r & 7) ^ ((r >>
 // TN: 16-row weight blocks per consumer wave (tile BN = 32 TN).
 // OPT: the epilogue options (bias, bf16 output, one weight scale per output
 // channel) are compiled in; without them the store path is fp32 y (and acc).
-template <int TN, bool OPT>
+// GRP: group-wise weight scales (out.w_group = G < K, G = 64 or a multiple of 128):
+// the int32 products of each group are scaled into fp32 accumulators when the
+// group's last half step is done (see the consumer); OPT is set as well.
+template <int TN, bool OPT, bool GRP = false>
 __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s_x, const uint8_t *__restrict__ packed,
     const float *__restrict__ s_w, int M, int N, int K, const OutSpec out, int32_t *__restrict__ acc_out,
@@ -71,6 +74,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t smem[D * kPipeStage];
     // per tile (4 slots, tile index % 4): sum over k of q for each of the 128 rows
     __shared__ int sqbuf[4][kPipeBM];
+    // GRP, per stage: sum of q over each half step (64 weights) of the 128 rows, and
+    // the weight scale of each half step's group for the BN rows
+    __shared__ int sqh[GRP ? D : 1][2][kPipeBM];
+    __shared__ __attribute__((aligned(16))) float scs[GRP ? D : 1][2][BN];
 
     // the wave index is the same in every lane: keep it (and what derives from it) scalar
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -79,6 +86,17 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
     const int KS = K / kPipeKS;
     const int total = my_tiles * KS;
     const size_t KB = (size_t)(K >> 2);
+    // k order rotated per workgroup: workgroups that share q rows (one XCD, one M
+    // tile) or weight rows (one N tile) start at different k; GRP: at a group start,
+    // so that every group's half steps follow one another
+    const int gh = GRP ? out.w_group / 64 : 1;    // half steps per group
+    const int ng = GRP ? K / out.w_group : 1;
+    int kr0;
+    {
+        const int kx = wg & 7, kj = wg >> 3, kjn = (G + 7) >> 3;
+        kr0 = (int)(((int64_t)kj * KS / kjn + 3 * kx) % KS);
+        if (GRP && gh > 2) kr0 -= kr0 % (gh / 2);
+    }
 
     if (wave >= 4) {
         // ------------------------------------------------------------ producer
@@ -92,15 +110,14 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
         // second slot (a wave-uniform condition)
         const bool b2 = NB > 1 && 256 + tp < 2 * BN;
         int d_s = 0, d_ti = 0, d_kk = 0;
-        // k order rotated per workgroup: workgroups that share q rows (one XCD,
-        // one M tile) or weight rows (one N tile) start at different k
-        const int kx = wg & 7, kj = wg >> 3, kjn = (G + 7) >> 3;
-        int d_kr = (int)(((int64_t)kj * KS / kjn + 3 * kx) % KS);
+        int d_kr = kr0;
         const int8_t *arow[4];
         const uint8_t *brow[2];
+        int bn0 = 0;   // first weight row of the tile being loaded
         auto set_tile = [&](int ti) {
             const int t = wg + ti * G;
             const int m0 = (t % tiles_m) * kPipeBM, n0 = (t / tiles_m) * BN;
+            bn0 = n0;
             #pragma unroll
             for (int h = 0; h < 4; ++h) arow[h] = q + (size_t)min(m0 + ar + 32 * h, M - 1) * K + 16 * ac;
             #pragma unroll
@@ -109,11 +126,23 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
         set_tile(0);
         // loads of step d_s (clamped to the last step) into register set R
         pv4u ra[4][4], rb[4][2];
+        // GRP: scale entries tp and tp + 256 of the step's 2 x BN (half, row) pairs
+        float rsc[GRP ? 4 : 1][2];
         auto issue = [&](int R) {
             #pragma unroll
             for (int h = 0; h < 4; ++h) ra[R][h] = gload(arow[h] + (size_t)d_kr * kPipeKS);
             rb[R][0] = gload(brow[0] + (size_t)d_kr * (kPipeKS / 4));
             if (b2) rb[R][1] = gload(brow[1] + (size_t)d_kr * (kPipeKS / 4));
+            if (GRP) {
+                #pragma unroll
+                for (int e2 = 0; e2 < 2; ++e2) {
+                    const int e = tp + 256 * e2;   // e2 = 1: whole waves with or without an entry
+                    if (e < 2 * BN) {
+                        const int u = e >= BN ? 1 : 0, c = e - u * BN;
+                        rsc[R][e2] = s_w[(size_t)min(bn0 + c, N - 1) * ng + (2 * d_kr + u) / gh];
+                    }
+                }
+            }
             ++d_s;
             if (d_s < total) {
                 if (++d_kr == KS) d_kr = 0;
@@ -133,10 +162,18 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
             #pragma unroll
             for (int h = 0; h < 4; ++h) {
                 const int r = ar + 32 * h;
-                int t = __builtin_amdgcn_sdot4((int)ra[R][h].x, 0x01010101, psq[h], false);
+                int t = __builtin_amdgcn_sdot4((int)ra[R][h].x, 0x01010101, GRP ? 0 : psq[h], false);
                 t = __builtin_amdgcn_sdot4((int)ra[R][h].y, 0x01010101, t, false);
                 t = __builtin_amdgcn_sdot4((int)ra[R][h].z, 0x01010101, t, false);
-                psq[h] = __builtin_amdgcn_sdot4((int)ra[R][h].w, 0x01010101, t, false);
+                t = __builtin_amdgcn_sdot4((int)ra[R][h].w, 0x01010101, t, false);
+                if (GRP) {
+                    // the half step's sum of q for row r: chunks ac & ~3 .. + 3
+                    t += __shfl_xor(t, 1, 64);
+                    t += __shfl_xor(t, 2, 64);
+                    if ((ac & 3) == 0) sqh[x % D][ac >> 2][r] = t;
+                } else {
+                    psq[h] = t;
+                }
                 uint32_t p0, p1, p2, p3;
                 transpose4x4(ra[R][h].x, ra[R][h].y, ra[R][h].z, ra[R][h].w, p0, p1, p2, p3);
                 *reinterpret_cast<uint4 *>(st + 1024 * (r >> 3) + 128 * (r & 7) + 16 * qslot(r, ac)) =
@@ -149,9 +186,16 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
                     *reinterpret_cast<pv4u *>(st + kPipeA + 32 * r + 16 * (bh ^ ((r >> 3) & 1))) = rb[R][h];
                 }
             }
+            if (GRP) {
+                #pragma unroll
+                for (int e2 = 0; e2 < 2; ++e2) {
+                    const int e = tp + 256 * e2;
+                    if (e < 2 * BN) (&scs[x % D][0][0])[e] = rsc[R][e2];
+                }
+            }
             // the tile's last step: each row's sum over its eight chunk lanes, into
             // the tile's slot (read by the consumers after two more barriers)
-            if (x < total && ++t_kk == KS) {
+            if (!GRP && x < total && ++t_kk == KS) {
                 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
                     int v = psq[h];
@@ -203,6 +247,17 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
     for (int i = 0; i < 4; ++i)
         #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = pv4i{0, 0, 0, 0};
+    // GRP: sum over groups of (acc_g - sum_g q) s_g in fp32, the running sum of q of
+    // the current group per row, and the half steps of the group done so far
+    pv4f facc[GRP ? 4 : 1][GRP ? TN : 1];
+    int sqrun[4] = {0, 0, 0, 0};
+    int c_h = 0;
+    if (GRP) {
+        #pragma unroll
+        for (int i = 0; i < 4; ++i)
+            #pragma unroll
+            for (int j = 0; j < TN; ++j) facc[i][j] = pv4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
     // per-lane offsets: the q fragment of half u (local row r = 64 wm + 16 i + l16
     // lies in 1 KB block r / 8 at position r % 8 = lane % 8, chunk 4u + g at its
     // slot) and the packed dword 4u + g of weight row r (halves swapped on rows with
@@ -233,7 +288,29 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
             for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, fa[u][i], acc[i][j], 0, 0, 0);
         }
     };
-    const float sw = *s_w;
+    // GRP, after half u of step x: at the group's last half, its products (codes c,
+    // less the group's sum of q) times the group scale of each column into facc
+    auto fold_half = [&](int x, int u) {
+        const int st = x % D;
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) sqrun[i] += sqh[st][u][64 * wm + 16 * i + l16];
+        if (++c_h == gh) {
+            c_h = 0;
+            #pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const pv4f s4 = *reinterpret_cast<const pv4f *>(&scs[st][u][16 * TN * wn + 16 * j + 4 * g]);
+                #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    #pragma unroll
+                    for (int r = 0; r < 4; ++r) facc[i][j][r] += (float)(acc[i][j][r] - sqrun[i]) * s4[r];
+                    acc[i][j] = pv4i{0, 0, 0, 0};
+                }
+            }
+            #pragma unroll
+            for (int i = 0; i < 4; ++i) sqrun[i] = 0;
+        }
+    };
+    const float sw = GRP ? 0.0f : *s_w;
     int c_ti = 0, c_kk = 0;
     float sxr[4];
     auto load_sx = [&](int ti) {
@@ -281,7 +358,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
                 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int n = min(n0 + r, N - 1);
-                    double yv = (double)acc[i][j][r] * ((OPT && out.w_group) ? rescale_factor(sxr[i], s_w[n]) : cm);
+                    double yv;
+                    if (GRP) yv = ((double)facc[i][j][r] * (double)sxr[i]) / 127.0;
+                    else yv = (double)acc[i][j][r] * ((OPT && out.w_group) ? rescale_factor(sxr[i], s_w[n]) : cm);
                     if (OPT && out.bias) yv += (double)out.bias[n];
                     v[r] = (float)yv;
                 }
@@ -318,22 +397,29 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
     for (int s = 0; s < total; ++s) {
         read(s, 1);
         half(0);
+        if (GRP) fold_half(s, 0);
         read(s + 1, 0);
         half(1);
+        if (GRP) fold_half(s, 1);
         if (++c_kk == KS) {
             // products ran on the codes c: acc = sum q c - sum q, the row sums of q
-            // formed by the producers while staging this tile
-            #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = sqbuf[c_ti & 3][64 * wm + 16 * i + l16];
+            // formed by the producers while staging this tile (GRP: group by group)
+            if (!GRP) {
                 #pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] -= pv4i{t, t, t, t};
+                for (int i = 0; i < 4; ++i) {
+                    const int t = sqbuf[c_ti & 3][64 * wm + 16 * i + l16];
+                    #pragma unroll
+                    for (int j = 0; j < TN; ++j) acc[i][j] -= pv4i{t, t, t, t};
+                }
             }
             epilogue(c_ti);
             #pragma unroll
             for (int i = 0; i < 4; ++i)
                 #pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = pv4i{0, 0, 0, 0};
+                for (int j = 0; j < TN; ++j) {
+                    acc[i][j] = pv4i{0, 0, 0, 0};
+                    if (GRP) facc[i][j] = pv4f{0.0f, 0.0f, 0.0f, 0.0f};
+                }
             c_kk = 0;
             if (++c_ti < my_tiles) load_sx(c_ti);
         }
@@ -381,6 +467,12 @@ bool gemm_pipe_ok(int64_t M, int64_t N, int64_t K) {
     return K % kPipeKS == 0 && M > 0 && N > 0 && (int64_t)kPipeBM * K < ((int64_t)1 << 31);
 }
 
+bool gemm_pipe_groups_ok(int64_t M, int64_t N, int64_t K, int64_t w_group) {
+    // group-wise scales: whole groups of half steps (64) or of steps (multiples of 128)
+    return gemm_pipe_ok(M, N, K) && w_group > 0 && w_group < K && K % w_group == 0 &&
+           (w_group == 64 || w_group % kPipeKS == 0);
+}
+
 int64_t gemm_pipe_rounds(int64_t M, int64_t N) {
     int64_t tiles = 0, rounds = 0;
     pipe_pick_tn(M, N, 256, &tiles, &rounds);
@@ -409,6 +501,18 @@ hipError_t launch_gemm_pipe(int tn_force, const int8_t *q, const float *s_x, con
                             const float *s_w, int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc,
                             hipStream_t st) {
     const int cus = device_cus();
+    const bool grp = y.w_group > 0 && y.w_group < K;
+    if (grp) {
+        // group-wise scales: 128 x 160 tiles (their fp32 group accumulators fit beside
+        // the int32 ones), no int32 output
+        if (acc || !gemm_pipe_groups_ok(M, N, K, y.w_group)) return hipErrorInvalidValue;
+        const int tiles_m = (int)((M + kPipeBM - 1) / kPipeBM);
+        const int64_t tiles = (int64_t)tiles_m * ((N + 159) / 160);
+        const dim3 g((unsigned)std::min<int64_t>(tiles, cus));
+        gemm_pipe_kernel<5, true, true><<<g, dim3(kPipeThreads), 0, st>>>(q, s_x, packed, s_w, (int)M, (int)N, (int)K, y,
+                                                                          nullptr, tiles_m, (int)tiles);
+        return hipGetLastError();
+    }
     const int tn = tn_force ? tn_force : pipe_pick_tn(M, N, cus, nullptr, nullptr);
     const int64_t bn = 32 * tn;
     const int tiles_m = (int)((M + kPipeBM - 1) / kPipeBM);

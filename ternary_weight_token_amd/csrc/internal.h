@@ -131,6 +131,8 @@ hipError_t launch_gemm_cfg(int cfg, const int8_t *q, const float *s_x, const uin
 int gemm_config_count();
 // pipelined persistent GEMM (gemm_pipe.hip); tn_force 0 = by its cost model, else 5 or 7
 bool gemm_pipe_ok(int64_t M, int64_t N, int64_t K);
+// group-wise scales (w_group < K) on the pipelined kernel: G = 64 or a multiple of 128
+bool gemm_pipe_groups_ok(int64_t M, int64_t N, int64_t K, int64_t w_group);
 int64_t gemm_pipe_rounds(int64_t M, int64_t N);   // tiles per busiest workgroup on 256 CUs
 double gemm_pipe_estimate_us(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_pipe(int tn_force, const int8_t *q, const float *s_x, const uint8_t *packed,

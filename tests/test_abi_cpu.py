@@ -101,8 +101,14 @@ def test_linear_ex_rejects_bad_arguments(L):
     assert L.bitnet_linear_ex(p, p, p, p, 6, 1, 1, 64, z, p, F32, z, 0, z) == SHAPE
     assert L.bitnet_linear_ex(p, p, p, p, 48, 1, 1, 128, z, p, F32, z, 0, z) == SHAPE
     assert L.bitnet_linear_ex(p, p, p, p, -4, 1, 1, 64, z, p, F32, z, 0, z) == SHAPE
-    for kern in (2, 4, 16):
+    # group-wise scales: not on the MFMA decode kernel or the older GEMM tiles; on the
+    # pipelined GEMM only without acc, K % 128 == 0 and G = 64 or a multiple of 128
+    for kern in (4, 16, 20):
         assert L.bitnet_linear_ex(p, p, p, p, 64, 1, 1, 128, z, p, F32, z, kern, z) == ARG
+    for kern in (2, 21, 22):
+        assert L.bitnet_linear_ex(p, p, p, p, 64, 1, 1, 128, z, p, F32, p, kern, z) == ARG     # with acc
+        assert L.bitnet_linear_ex(p, p, p, p, 192, 1, 1, 384, z, p, F32, z, kern, z) == ARG    # G = 192
+        assert L.bitnet_linear_ex(p, p, p, p, 64, 1, 1, 192, z, p, F32, z, kern, z) == ARG     # K % 128
     assert L.bitnet_linear_ex(p, p, p, p, 32, 1, 1, 128, z, p, F32, z, 1, z) == ALIGN
 
 

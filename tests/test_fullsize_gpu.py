@@ -8,7 +8,8 @@ checked against the CPU oracle on sampled matrices / rows / columns.
   full, every output checked for finiteness);
 * prefill: M = 2048 on up (2560 -> 6912) and down (6912 -> 2560), natural
   density and 30 / 50 / 70 % nonzero codes, 160 sampled output columns;
-* prefill as timed (y only, and bias + bf16 y) on 96 sampled token rows;
+* prefill as timed (y only, and bias + bf16 y) on 96 sampled token rows, and
+  with group-128 weight scales on 64 sampled rows;
 * 100B-scale FFN: gate (8192 -> 28672) and down (28672 -> 8192) of layer 0 at
   M = 1 and M = 8, compared in full; the 8-layer grouped launch as timed, its
   last layer compared in full;
@@ -281,6 +282,42 @@ def test_prefill_timed_form(name):
     _, yb_ref = oracle.linear(qs, np.ascontiguousarray(sx_ref[rows]), p_ref, sw_ref, bias=bias.numpy())
     got = yb.cpu().view(torch.int16).numpy().view(np.uint16)[rows]
     assert np.array_equal(got, oracle.to_bf16(yb_ref))
+    assert torch.isfinite(y).all()
+
+
+def _gemm_group_bound(q, s_x, packed, s_w, G, K):
+    """(K / G + 1) 2^-24 (s_x / 127) sum_g |acc_g s_g|: one rounding of each scaled
+    group sum and of each running fp32 sum."""
+    t = oracle.unpack(packed, K).astype(np.float64)
+    qf = q.astype(np.float64)
+    mag = np.zeros((q.shape[0], t.shape[0]))
+    for g in range(K // G):
+        sl = slice(g * G, (g + 1) * G)
+        mag += np.abs(qf[:, sl] @ t[:, sl].T) * s_w[:, g].astype(np.float64)[None, :]
+    return (K // G + 1) * 2.0 ** -24 * mag * (s_x.astype(np.float64)[:, None] / 127.0)
+
+
+@pytest.mark.parametrize("name", ["up", "down"])
+def test_prefill_group128_scales(name):
+    """Prefill at M = 2048 with one weight scale per 128 weights (the pipelined GEMM's
+    group-wise path, y only, as timed): 64 sampled token rows over all N columns,
+    within the bound of its fp32 group accumulation."""
+    x, w = W.prefill_inputs(name, None)
+    N, K = w.shape
+    p_ref, sw_ref = oracle.pack_grouped(w.numpy(), 128, 1e-5)
+    q_ref, sx_ref = oracle.quant_act(bits_np(x))
+    p, sw = tw.pack_weights_grouped(w.to(DEV), 128, 1e-5)
+    q, sx = tw.quant_act(x.to(DEV))
+    y = torch.full((2048, N), float("nan"), dtype=torch.float32, device=DEV)
+    tw.bitnet_linear_ex(q, sx, p, sw, None, y, None, 0, w_group=128)
+    torch.cuda.synchronize()
+    assert np.array_equal(p.cpu().numpy(), p_ref) and np.array_equal(sw.cpu().numpy(), sw_ref)
+    rows = np.unique(np.concatenate([[0, 2047], np.random.default_rng(13).choice(2048, 62, replace=False)]))
+    qs, ss = np.ascontiguousarray(q_ref[rows]), np.ascontiguousarray(sx_ref[rows])
+    _, y_ref = oracle.linear_grouped(qs, ss, p_ref, sw_ref, 128)
+    slack = _gemm_group_bound(qs, ss, p_ref, sw_ref, 128, K)
+    d = np.abs(y.cpu().numpy()[rows].astype(np.float64) - y_ref.astype(np.float64))
+    assert not (d > REL * np.abs(y_ref.astype(np.float64)) + slack).any()
     assert torch.isfinite(y).all()
 
 

@@ -303,6 +303,52 @@ def _grouped_bound(q, s_x, packed, s_w, G, K):
     return 2.0 ** -44 * mag * (s_x.astype(np.float64)[:, None] / 127.0)
 
 
+def _gemm_group_bound(q, s_x, packed, s_w, G, K):
+    """The pipelined GEMM scales each group's exact integer sum acc_g into an fp32
+    accumulator: one rounding of acc_g s_g and one of each running sum, so |error| <=
+    (K / G + 1) 2^-24 (s_x / 127) sum_g |acc_g s_g| before the final rounding."""
+    t = oracle.unpack(packed, K).astype(np.float64)
+    qf = q.astype(np.float64)
+    mag = np.zeros((q.shape[0], t.shape[0]))
+    for g in range(K // G):
+        sl = slice(g * G, (g + 1) * G)
+        mag += np.abs(qf[:, sl] @ t[:, sl].T) * s_w[:, g].astype(np.float64)[None, :]
+    return (K // G + 1) * 2.0 ** -24 * mag * (s_x.astype(np.float64)[:, None] / 127.0)
+
+
+@pytest.mark.parametrize("kernel,M,N,K,G", [
+    (2, 257, 225, 640, 128), (21, 300, 500, 2560, 128), (22, 200, 333, 2560, 64), (0, 40, 129, 2560, 128),
+    (2, 130, 96, 1024, 256), (22, 520, 1000, 1024, 512), (2, 17, 300, 6912, 128), (0, 300, 700, 2560, 640),
+])
+@pytest.mark.parametrize("opts", ["plain", "bias_bf16"])
+def test_gemm_weight_scale_groups(kernel, M, N, K, G, opts):
+    """Group-wise scales on the pipelined GEMM (no int32 output): several tiles per
+    workgroup, ragged M and N, G = 64 (a group per half step) up to several steps."""
+    key = synth.stream_key(337, kernel, M, N, K, G)
+    x, q, s = quantized_inputs(key, M, K, row_scale=(0.1, 10.0))
+    w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02).numpy()
+    w[: N // 2, :G] *= 6.0
+    packed, s_w = oracle.pack_grouped(w, G, 1e-5)
+    bias = (np.linspace(-2, 2, N).astype(np.float32) if opts == "bias_bf16" else None)
+    _, y_ref = oracle.linear_grouped(q, s, packed, s_w, G, bias=bias)
+    out_dtype = torch.bfloat16 if opts == "bias_bf16" else torch.float32
+    y = torch.full((M, N), float("nan"), dtype=out_dtype, device=DEV)
+    tw.bitnet_linear_ex(torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV),
+                        torch.from_numpy(packed).to(DEV), torch.from_numpy(s_w).to(DEV),
+                        None if bias is None else torch.from_numpy(bias).to(DEV), y, None, kernel, w_group=G)
+    torch.cuda.synchronize()
+    slack = _gemm_group_bound(q, s, packed, s_w, G, K)
+    if out_dtype == torch.float32:
+        d = np.abs(y.cpu().numpy().astype(np.float64) - y_ref.astype(np.float64))
+        bad = d > REL * np.abs(y_ref.astype(np.float64)) + slack
+    else:
+        got = (y.cpu().view(torch.int16).numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+        want = (oracle.to_bf16(y_ref).astype(np.uint32) << 16).view(np.float32)
+        d = np.abs(got.astype(np.float64) - want.astype(np.float64))
+        bad = d > 2.0 ** -7 * np.abs(want.astype(np.float64)) + slack
+    assert not bad.any(), f"{bad.sum()} outputs outside the bound; first at {np.argwhere(bad)[0]}"
+
+
 @pytest.mark.parametrize("kernel,M,N,K,G", [
     (1, 1, 300, 2560, 2560), (4, 8, 300, 2560, 2560), (2, 40, 257, 640, 640), (3, 3, 33, 132, 132),
     (16, 257, 225, 640, 640), (17, 257, 225, 640, 640), (18, 257, 225, 640, 640), (19, 257, 225, 640, 640),
