@@ -369,7 +369,12 @@ BITNET_API int bitnet_pack_bitplanes(const uint8_t *packed, int64_t N, int64_t K
  * (formed as in bitnet_linear) for weights in format fmt.  K % 32 == 0.  kernel: 0
  * picks, 1 the general kernel (any M, any alignment), 2 the bit-serial GEMV (M == 1,
  * K % 128 == 0 for binary or K % 64 == 0 for bitplanes, K at most 57344 / 51584,
- * q and wbits 16-byte aligned; BITNET_ERR_ARG otherwise).  acc may be NULL. */
+ * q and wbits 16-byte aligned; BITNET_ERR_ARG otherwise), 3 the bit-serial kernel for
+ * several tokens (any M up to 65535: the weights are read once per 4 tokens for
+ * binary, per 2 for bitplanes, fewer when one token's planes exceed 16 KiB; same K
+ * divisibility and alignment, one token's planes within 64 KiB; BITNET_ERR_ARG
+ * otherwise).  Kernel 0 takes 2 for one token and 3 for more when they apply.  acc
+ * may be NULL. */
 BITNET_API int bitnet_linear_bits(const int8_t *q, const float *s_x, const uint8_t *wbits, int fmt,
                                   const float *s_w, int64_t M, int64_t N, int64_t K, float *y, int32_t *acc,
                                   int kernel, void *stream);

@@ -460,6 +460,188 @@ static hipError_t launch_gemv_bits(const int8_t *q, const float *s_x, const uint
                            : launch_gemv_bits_rg<FMT, 2>(q, s_x, wbits, s_w, N, K, y, acc, st);
 }
 
+// ---- several tokens per pass over the weights
+
+// MT tokens against 64 weight rows per workgroup (4 wavefronts x 8 octets x 2 rows):
+// the weights are read once per MT tokens.  The planes of the MT token rows are
+// staged in LDS, token after token (slot layout of BitsFmt); each 32-weight word is
+// then counted against every token's planes (one and / bit-field select and one
+// accumulating popcount per plane), so the vector work per weight grows with MT
+// while the weight bytes do not.  blockIdx.y: the token tile (tokens MT y ..).
+constexpr int kBitsMtRG = 2;
+
+template <int FMT, int MT>
+__global__ __launch_bounds__(256) void bits_mt_kernel(const int8_t *__restrict__ q, const float *__restrict__ s_x,
+                                                      const uint8_t *__restrict__ wbits,
+                                                      const float *__restrict__ s_w, int M, int N, int K,
+                                                      float *__restrict__ y, int32_t *__restrict__ acc_out) {
+    using F = BitsFmt<FMT>;
+    constexpr int RG = kBitsMtRG;
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+    __shared__ int sq[MT];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l8 = lane & 7, rs = lane >> 3;
+    const int S = K / F::V, C32 = K >> 5;
+    const int m0 = (int)blockIdx.y * MT, mcount = min(MT, M - m0);
+    const int row0 = (int)blockIdx.x * (4 * 8 * RG) + wave * 8 * RG;
+    const int64_t row_bytes = K / F::RowDiv;
+
+    const uint8_t *prow[RG];
+    #pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        const int r = row0 + 8 * g + rs;
+        prow[g] = wbits + (size_t)(r < N ? r : 0) * row_bytes;   // rows past N read row 0, discarded
+    }
+    const int T = row0 < N ? (S + 7) >> 3 : 0;
+    uint4 bufA[RG], bufB[RG];
+    auto issue = [&](uint4 (&b)[RG], int t) {
+        const int sl = min(l8 + 8 * t, S - 1);
+        #pragma unroll
+        for (int g = 0; g < RG; ++g) b[g] = load_weights<true>(prow[g] + 16 * (size_t)sl);
+    };
+    if (T > 0) issue(bufA, 0);
+
+    // ---- stage the planes of the tile's tokens (and, binary, their sums of q)
+    if (tid < MT) sq[tid] = 0;
+    __syncthreads();
+    for (int idx = tid; idx < mcount * C32; idx += 256) {
+        const int m = idx / C32, c = idx - m * C32;
+        const int8_t *src = q + (size_t)(m0 + m) * K + 32 * c;
+        const uint4 a = gload16(src), b = gload16(src + 16);
+        uint32_t p[8];
+        q_planes(a, b, p);
+        uint32_t *dst = lds + (size_t)m * S * F::SD + (c / F::GC) * F::SD + 8 * (c % F::GC);
+        *reinterpret_cast<uint4 *>(dst) = make_uint4(p[0], p[1], p[2], p[3]);
+        *reinterpret_cast<uint4 *>(dst + 4) = make_uint4(p[4], p[5], p[6], p[7]);
+        if (FMT == 1) {
+            int sm = dot4(a.x, 0x01010101u, 0);
+            sm = dot4(a.y, 0x01010101u, sm);
+            sm = dot4(a.z, 0x01010101u, sm);
+            sm = dot4(a.w, 0x01010101u, sm);
+            sm = dot4(b.x, 0x01010101u, sm);
+            sm = dot4(b.y, 0x01010101u, sm);
+            sm = dot4(b.z, 0x01010101u, sm);
+            sm = dot4(b.w, 0x01010101u, sm);
+            if (sm != 0) atomicAdd(&sq[m], sm);
+        }
+    }
+    __syncthreads();
+
+    int cnt[RG][MT][8], cns[RG];
+    #pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        cns[g] = 0;
+        #pragma unroll
+        for (int m = 0; m < MT; ++m)
+            #pragma unroll
+            for (int j = 0; j < 8; ++j) cnt[g][m][j] = 0;
+    }
+    // slot l8 + 8 t of every row: tokens past mcount read token 0's planes (their
+    // counts are never stored); slots past S count as all-zero words
+    auto consume = [&](const uint4 (&b)[RG], int t) {
+        const int sl = l8 + 8 * t;
+        const bool valid = sl < S;
+        #pragma unroll
+        for (int i = 0; i < F::GC; ++i) {
+            uint32_t pos[RG], sg[RG];
+            #pragma unroll
+            for (int g = 0; g < RG; ++g) {
+                const uint32_t wv[4] = {b[g].x, b[g].y, b[g].z, b[g].w};
+                if (FMT == 1) {
+                    pos[g] = valid ? wv[i] : 0u;
+                    sg[g] = 0u;
+                } else {
+                    const uint32_t mk = valid ? wv[2 * i] : 0u;
+                    sg[g] = mk & wv[2 * i + 1];   // a sign bit counts only under the mask
+                    pos[g] = mk ^ sg[g];
+                    cns[g] += __builtin_popcount(sg[g]);
+                }
+            }
+            #pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const uint32_t *src = lds + (size_t)(m < mcount ? m : 0) * S * F::SD + min(sl, S - 1) * F::SD + 8 * i;
+                const uint4 p0 = *reinterpret_cast<const uint4 *>(src);
+                const uint4 p1 = *reinterpret_cast<const uint4 *>(src + 4);
+                const uint32_t p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+                #pragma unroll
+                for (int g = 0; g < RG; ++g) {
+                    #pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const uint32_t v = FMT == 1 ? (p[j] & pos[g]) : ((p[j] & pos[g]) | (~p[j] & sg[g]));
+                        cnt[g][m][j] += __builtin_popcount(v);
+                    }
+                }
+            }
+        }
+    };
+    if (T > 0) {
+        int t = 0;
+        for (; t + 2 <= T - 1; t += 2) {
+            issue(bufB, t + 1);
+            consume(bufA, t);
+            issue(bufA, t + 2);
+            consume(bufB, t + 1);
+        }
+        if (t == T - 2) {
+            issue(bufB, t + 1);
+            consume(bufA, t);
+            consume(bufB, t + 1);
+        } else {
+            consume(bufA, t);
+        }
+    }
+
+    const float sw = *s_w;
+    #pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        const int r = row0 + 8 * g + rs;
+        const int sgn = FMT == 2 ? octet_sum(cns[g]) : 0;
+        #pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int a = octet_sum(plane_sum(cnt[g][m])) + sgn;
+            if (l8 == 0 && r < N && m < mcount) {
+                const int acc = FMT == 1 ? 2 * a - sq[m] : a;
+                const size_t o = (size_t)(m0 + m) * N + r;
+                y[o] = rescale(acc, rescale_factor(s_x[m0 + m], sw));
+                if (acc_out) acc_out[o] = acc;
+            }
+        }
+    }
+}
+
+// Tokens per pass: binary 4 while their planes fit 64 KiB of LDS, else 2, else 1;
+// bitplanes at most 2 (its counters for 4 tokens take all 256 registers).
+static int bits_mt_tokens(int fmt, int64_t K) {
+    const int64_t per_token = fmt == 1 ? (K / BitsFmt<1>::V) * BitsFmt<1>::SD * 4 : (K / BitsFmt<2>::V) * BitsFmt<2>::SD * 4;
+    for (int mt : {4, 2, 1})
+        if ((fmt == 1 || mt <= 2) && mt * per_token <= 64 * 1024) return mt;
+    return 0;
+}
+
+bool bits_mt_ok(int fmt, int64_t K, const void *q, const void *wbits) {
+    const int64_t v = fmt == 1 ? BitsFmt<1>::V : BitsFmt<2>::V;
+    return K > 0 && K % v == 0 && bits_mt_tokens(fmt, K) > 0 && (uintptr_t)q % 16 == 0 && (uintptr_t)wbits % 16 == 0;
+}
+
+template <int FMT, int MT>
+static hipError_t launch_bits_mt_t(const int8_t *q, const float *s_x, const uint8_t *wbits, const float *s_w,
+                                   int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
+    using F = BitsFmt<FMT>;
+    const size_t lds = (size_t)MT * (K / F::V) * F::SD * 4;
+    const dim3 grid((unsigned)((N + 4 * 8 * kBitsMtRG - 1) / (4 * 8 * kBitsMtRG)), (unsigned)((M + MT - 1) / MT));
+    bits_mt_kernel<FMT, MT><<<grid, dim3(256), lds, st>>>(q, s_x, wbits, s_w, (int)M, (int)N, (int)K, y, acc);
+    return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_bits_mt(const int8_t *q, const float *s_x, const uint8_t *wbits, const float *s_w,
+                                 int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
+    const int mt = bits_mt_tokens(FMT, K);
+    if (FMT == 1 && mt == 4) return launch_bits_mt_t<FMT, FMT == 1 ? 4 : 2>(q, s_x, wbits, s_w, M, N, K, y, acc, st);
+    if (mt == 2) return launch_bits_mt_t<FMT, 2>(q, s_x, wbits, s_w, M, N, K, y, acc, st);
+    return launch_bits_mt_t<FMT, 1>(q, s_x, wbits, s_w, M, N, K, y, acc, st);
+}
+
 // ---- any M: one thread per output, plain loops (any alignment)
 
 template <int FMT>
@@ -497,6 +679,11 @@ hipError_t launch_linear_bits(const int8_t *q, const float *s_x, const uint8_t *
     if (fast) {
         return fmt == 1 ? launch_gemv_bits<1>(q, s_x, wbits, s_w, N, K, y, acc, st)
                         : launch_gemv_bits<2>(q, s_x, wbits, s_w, N, K, y, acc, st);
+    }
+    // (token tiles on the grid's y: at most 65535 of them)
+    if (kernel == 3 || (kernel == 0 && bits_mt_ok(fmt, K, q, wbits) && M <= 65535)) {
+        return fmt == 1 ? launch_bits_mt<1>(q, s_x, wbits, s_w, M, N, K, y, acc, st)
+                        : launch_bits_mt<2>(q, s_x, wbits, s_w, M, N, K, y, acc, st);
     }
     const int64_t total = M * N;
     const dim3 grid((unsigned)((total + 255) / 256));

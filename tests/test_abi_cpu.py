@@ -335,7 +335,11 @@ def test_bit_encodings_reject_bad_arguments(L):
     assert L.bitnet_pack_bitplanes(z, 0, 64, z, z) == OK
     lb = L.bitnet_linear_bits
     assert lb(p, p, p, 3, p, 1, 8, 128, p, z, 0, z) == ARG                        # format
-    assert lb(p, p, p, 1, p, 1, 8, 128, p, z, 3, z) == ARG                        # kernel id
+    assert lb(p, p, p, 1, p, 1, 8, 128, p, z, 4, z) == ARG                        # kernel id
+    assert lb(p, p, p, 1, p, 2, 8, 96, p, z, 3, z) == ARG                         # multi-token binary: K % 128
+    assert lb(p, p, p, 2, p, 2, 8, 96, p, z, 3, z) == ARG                         # multi-token bitplanes: K % 64
+    assert lb(p, p, p, 1, p, 65536, 8, 128, p, z, 3, z) == ARG                    # token tiles on the grid's y
+    assert lb(ctypes.c_void_p(4097), p, p, 1, p, 2, 8, 128, p, z, 3, z) == ARG    # alignment
     assert lb(p, p, p, 1, p, 1, 8, 100, p, z, 0, z) == SHAPE                      # K % 32
     assert lb(p, p, z, 1, p, 1, 8, 128, p, z, 0, z) == NULL
     assert lb(p, p, p, 1, p, 2, 8, 128, p, z, 2, z) == ARG                        # GEMV: M == 1

@@ -811,7 +811,9 @@ def _bits_case(fmt, N, K, key):
 
 
 BITS_SHAPES = [(1, 300, 2560), (1, 2560, 6912), (1, 65, 128), (1, 1, 256), (1, 700, 8192), (1, 129, 28672),
-               (1, 16400, 640), (1, 16384, 8192), (3, 70, 640), (8, 33, 2560)]
+               (1, 16400, 640), (1, 16384, 8192), (3, 70, 640), (8, 33, 2560),
+               # several tokens per pass (4 / 2 / 1 by K and format), ragged token tiles
+               (2, 300, 2560), (5, 129, 6912), (16, 1000, 8192), (4, 64, 28672), (9, 70, 640), (7, 65, 128)]
 
 
 @pytest.mark.parametrize("fmt", [1, 2])
@@ -824,7 +826,7 @@ def test_linear_bits_parity(fmt, M, N, K):
     acc_ref, y_ref = ref(q, s, s_w)
     qd, sd = torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV)
     wd, swd = torch.from_numpy(wb).to(DEV), torch.tensor([s_w], device=DEV)
-    kernels = (0, 1, 2) if M == 1 else (0, 1)
+    kernels = (0, 1, 2, 3) if M == 1 else (0, 1, 3)
     for kern in kernels:
         y, acc = tw.linear_bits(qd, sd, wd, fmt, swd, want_acc=True, kernel=kern)
         torch.cuda.synchronize()
