@@ -300,12 +300,18 @@ static size_t plan_layout(int count, size_t desc_size, uint64_t blocks, uint64_t
 // A plan whose problems all have M == 1 runs the GEMV (q staged in LDS); any M > 1
 // makes it run the MFMA decode kernel, which reads each weight once for all M tokens.
 // Problems with group-wise weight scales (w_group below K) make the whole plan run
-// the GEMV with its grouped path (the MFMA decode kernel has one).
+// the GEMV with its grouped path (the MFMA decode kernel has none): one token per
+// workgroup, or kGemvGroupsMT tokens per workgroup when any problem has M > 1.
 static bool desc_groups(const bitnet_linear_desc &d) { return d.w_group > 0 && d.w_group < d.K; }
 
 static uint32_t linear_variant(const bitnet_linear_desc *d, int count) {
-    for (int i = 0; i < count; ++i)
-        if (desc_groups(d[i])) return kVariantGemvGroups;
+    for (int i = 0; i < count; ++i) {
+        if (desc_groups(d[i])) {
+            for (int j = 0; j < count; ++j)
+                if (d[j].M > 1) return kVariantGemvGroupsMT;
+            return kVariantGemvGroups;
+        }
+    }
     for (int i = 0; i < count; ++i)
         if (d[i].M > 1) return kVariantMfma;
     return kVariantGemv;
@@ -317,7 +323,8 @@ static uint64_t linear_blocks(const bitnet_linear_desc &d, uint32_t variant) {
         return ((uint64_t)d.N + rows - 1) / rows;
     }
     const uint64_t rows = gemv_grouped_rows_per_block();
-    return ((uint64_t)d.N + rows - 1) / rows * (uint64_t)d.M;
+    const uint64_t mt = variant == kVariantGemvGroupsMT ? kGemvGroupsMT : 1;
+    return ((uint64_t)d.N + rows - 1) / rows * (((uint64_t)d.M + mt - 1) / mt);
 }
 
 // The output options of a descriptor: y's dtype and alignment, the bias.
@@ -438,8 +445,9 @@ BITNET_API int bitnet_grouped_plan_linear(const bitnet_linear_desc *descs, int c
         h->rows_per_block = gemv_grouped_rows_per_block();
         // each descriptor is staged by the path its own scales take (group-wise
         // descriptors keep one more dword per chunk, so they segment K sooner)
+        const int mt = variant == kVariantGemvGroupsMT ? kGemvGroupsMT : 1;
         for (int i = 0; i < count; ++i)
-            h->lds_bytes = std::max(h->lds_bytes, gemv_grouped_lds_bytes(descs[i].K, desc_groups(descs[i])));
+            h->lds_bytes = std::max(h->lds_bytes, gemv_grouped_lds_bytes(descs[i].K, desc_groups(descs[i]), mt));
     }
     h->desc_offset = doff;
     h->table_offset = toff;
@@ -590,8 +598,9 @@ BITNET_API int bitnet_linear_grouped(const void *plan_host, const void *plan_dev
     if (h->total_blocks == 0) return BITNET_OK;
     if (h->variant == kVariantMfma)
         return hip_status(launch_skinny_grouped(plan_dev, h->total_blocks, h->lds_bytes, (hipStream_t)stream));
-    if (h->variant != kVariantGemv && h->variant != kVariantGemvGroups) return fail(BITNET_ERR_ARG, "not a plan of this kind");
-    return hip_status(launch_gemv_grouped(plan_dev, h->total_blocks, h->lds_bytes, h->variant == kVariantGemvGroups,
+    if (h->variant != kVariantGemv && h->variant != kVariantGemvGroups && h->variant != kVariantGemvGroupsMT)
+        return fail(BITNET_ERR_ARG, "not a plan of this kind");
+    return hip_status(launch_gemv_grouped(plan_dev, h->total_blocks, h->lds_bytes, h->variant,
                                           (hipStream_t)stream));
 }
 

@@ -689,15 +689,15 @@ __host__ __device__ __forceinline__ int segment_chunks(int C, int mt, int dw = k
 // Grouped decode: 4 wavefronts per block, block -> (descriptor, row block, M tile)
 // through the plan's block table; staged-q LDS size comes from the plan header.
 constexpr int kGroupedRG = BITNET_GROUPED_RG;
-constexpr int kGroupedMT = 1;
+constexpr int kGroupedMT = 1;   // tokens per workgroup of the plain grouped GEMV
 
 // GRP: the plan has problems with group-wise weight scales (descriptor w_group below
 // K), which take the grouped tile; plans without them use the kernel without it.
-template <bool GRP>
+template <bool GRP, int MT>
 __global__ __launch_bounds__(256) void gemv_grouped_kernel(const uint8_t *__restrict__ plan) {
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
-    __shared__ int sq[kGroupedMT];
-    __shared__ int red[4 * 8 * kGroupedRG * kGroupedMT];
+    __shared__ int sq[MT];
+    __shared__ int red[4 * 8 * kGroupedRG * MT];
     const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
     const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[blockIdx.x];
     const LinearDescDev d = reinterpret_cast<const LinearDescDev *>(plan + h->desc_offset)[e.desc];
@@ -707,15 +707,15 @@ __global__ __launch_bounds__(256) void gemv_grouped_kernel(const uint8_t *__rest
     const OutSpec out = d.out();
     constexpr bool D8 = BITNET_GROUPED_DOT8 != 0, NTL = BITNET_GEMV_NT != 0;
     if (GRP && d.w_group > 0 && d.w_group < d.K) {
-        const int seg = segment_chunks(d.K >> 6, kGroupedMT, kLdsChunkDw + 1);
-        int *sqc = reinterpret_cast<int *>(dyn + kGroupedMT * seg * kLdsChunkDw);
-        gemv_lds_tile<kGroupedMT, kGroupedRG, D8, NTL, 4, StageQChunks<kGroupedMT, D8>, true>(
-            StageQChunks<kGroupedMT, D8>{d.q, d.K, sqc}, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, out, d.acc, rb * rows,
-            mt * kGroupedMT, 1, seg, dyn, sq, red, sqc);
+        const int seg = segment_chunks(d.K >> 6, MT, kLdsChunkDw + 1);
+        int *sqc = reinterpret_cast<int *>(dyn + MT * seg * kLdsChunkDw);
+        gemv_lds_tile<MT, kGroupedRG, D8, NTL, 4, StageQChunks<MT, D8>, true>(
+            StageQChunks<MT, D8>{d.q, d.K, sqc}, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, out, d.acc, rb * rows,
+            mt * MT, 1, seg, dyn, sq, red, sqc);
     } else {
-        gemv_lds_tile<kGroupedMT, kGroupedRG, D8, NTL, 4>(
-            StageQ<kGroupedMT, D8>{d.q, d.K}, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, out, d.acc, rb * rows,
-            mt * kGroupedMT, 1, segment_chunks(d.K >> 6, kGroupedMT), dyn, sq, red);
+        gemv_lds_tile<MT, kGroupedRG, D8, NTL, 4>(
+            StageQ<MT, D8>{d.q, d.K}, d.s_x, d.packed, d.s_w, d.M, d.N, d.K, out, d.acc, rb * rows,
+            mt * MT, 1, segment_chunks(d.K >> 6, MT), dyn, sq, red);
     }
 }
 
@@ -811,9 +811,9 @@ uint32_t gemv_grouped_rows_per_block() { return 4 * 8 * kGroupedRG; }
 uint32_t gemv_fused_rows_per_block() { return kFusedNW * 8 * kFusedRG; }
 uint32_t gemv_fused_threads() { return 64 * kFusedNW; }
 uint32_t gemv_grouped_threads() { return 256; }
-uint32_t gemv_grouped_lds_bytes(int64_t K, bool grp) {
+uint32_t gemv_grouped_lds_bytes(int64_t K, bool grp, int mt) {
     const int dw = kLdsChunkDw + (grp ? 1 : 0);
-    return (uint32_t)(kGroupedMT * segment_chunks((int)(K / 64), kGroupedMT, dw) * dw * 4);
+    return (uint32_t)(mt * segment_chunks((int)(K / 64), mt, dw) * dw * 4);
 }
 
 template <int MT, int RG, bool DOT8, bool GRP>
@@ -866,13 +866,15 @@ hipError_t launch_gemv(const int8_t *q, const float *s_x, const uint8_t *packed,
     return launch_gemv_mt<false>(q, s_x, packed, s_w, M, N, K, y, acc, st);
 }
 
-hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, bool grp,
+hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, uint32_t variant,
                                hipStream_t st) {
     const uint8_t *p = reinterpret_cast<const uint8_t *>(plan_dev);
-    if (grp)
-        gemv_grouped_kernel<true><<<dim3(blocks), dim3(256), lds_bytes, st>>>(p);
+    if (variant == kVariantGemvGroupsMT)
+        gemv_grouped_kernel<true, kGemvGroupsMT><<<dim3(blocks), dim3(256), lds_bytes, st>>>(p);
+    else if (variant == kVariantGemvGroups)
+        gemv_grouped_kernel<true, kGroupedMT><<<dim3(blocks), dim3(256), lds_bytes, st>>>(p);
     else
-        gemv_grouped_kernel<false><<<dim3(blocks), dim3(256), lds_bytes, st>>>(p);
+        gemv_grouped_kernel<false, kGroupedMT><<<dim3(blocks), dim3(256), lds_bytes, st>>>(p);
     return hipGetLastError();
 }
 

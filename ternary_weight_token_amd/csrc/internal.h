@@ -32,8 +32,11 @@ constexpr uint32_t kPlanLinear = 1, kPlanQuant = 2, kPlanFused = 3;
 // Linear plan variants: one block per (row block, token) running the GEMV, or one
 // block per row block running the MFMA decode kernel for all tokens at once.
 constexpr uint32_t kVariantGemv = 0, kVariantMfma = 1;
-// ... and the GEMV with the group-wise-scale path, for plans with such weights.
-constexpr uint32_t kVariantGemvGroups = 2;
+// ... and the GEMV with the group-wise-scale path, for plans with such weights: one
+// token per workgroup, or (any M > 1 among them) up to kGemvGroupsMT tokens per
+// workgroup, so that the weights are read once per kGemvGroupsMT tokens.
+constexpr uint32_t kVariantGemvGroups = 2, kVariantGemvGroupsMT = 3;
+constexpr int kGemvGroupsMT = 4;
 // Fused plan variants: a mask of what its problems use beyond the plain path (an
 // RMSNorm; fp32 input rows or gate / up pairs, the two ends of SwiGLU); each mask
 // has its own kernel, so a plan without them takes the kernel without that code.
@@ -107,9 +110,9 @@ hipError_t launch_pack_grouped(const float *w, int64_t N, int64_t K, int64_t G, 
                                float *s_w, hipStream_t st);
 hipError_t launch_gemv(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                        int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st);
-hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, bool grp,
+hipError_t launch_gemv_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, uint32_t variant,
                                hipStream_t st);
-uint32_t gemv_grouped_lds_bytes(int64_t K, bool grp = false);
+uint32_t gemv_grouped_lds_bytes(int64_t K, bool grp = false, int mt = 1);
 hipError_t launch_gemv_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, uint32_t pro,
                                      hipStream_t st);
 int64_t gemv_fused_max_k();

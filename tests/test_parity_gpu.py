@@ -395,7 +395,7 @@ def test_linear_weight_scale_groups(kernel, M, N, K, G, opts):
     assert not bad.any(), f"{bad.sum()} outputs outside the bound"
 
 
-@pytest.mark.parametrize("mixed_m", [False, True])
+@pytest.mark.parametrize("mixed_m", [False, True, "wide"])
 def test_grouped_plan_weight_scales(mixed_m):
     """One grouped linear launch over problems with one scale per tensor, per output
     channel and per group of 128 / 64 weights (and, mixed_m, M up to 5)."""
@@ -403,7 +403,7 @@ def test_grouped_plan_weight_scales(mixed_m):
     shapes = [(300, 2560, 0), (129, 2560, 2560), (200, 6912, 128), (70, 640, 64), (640, 2560, 128), (64, 51200, 0)]
     probs, refs = [], []
     for i, (N, K, G) in enumerate(shapes):
-        M = (1 + i % 5) if mixed_m else 1
+        M = ([8, 16, 3, 9, 1, 12][i] if mixed_m == "wide" else (1 + i % 5)) if mixed_m else 1
         key = synth.stream_key(332, i, M)
         x, q, s = quantized_inputs(key, M, K)
         w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02).numpy()
