@@ -116,10 +116,15 @@ static void linear_plans(void) {
     plan = plan_linear(d, ND, &st);
     CHECK(st == BITNET_OK && hdr_word(plan, 7) == 1);
     free(plan);
-    for (int i = 0; i < ND; ++i) d[i].w_group = (i % 3) ? 0 : 64;   /* group-wise variant */
+    for (int i = 0; i < ND; ++i) d[i].w_group = (i % 3) ? 0 : 64;   /* group-wise, several tokens */
+    plan = plan_linear(d, ND, &st);
+    CHECK(st == BITNET_OK && hdr_word(plan, 7) == 3);
+    free(plan);
+    for (int i = 0; i < ND; ++i) d[i].M = 1;                /* group-wise, one token each */
     plan = plan_linear(d, ND, &st);
     CHECK(st == BITNET_OK && hdr_word(plan, 7) == 2);
     free(plan);
+    for (int i = 0; i < ND; ++i) d[i].M = 1 + i % 16;
     d[5].M = 17;
     plan = plan_linear(d, ND, &st);
     CHECK(st == BITNET_ERR_SHAPE);
