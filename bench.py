@@ -67,6 +67,19 @@ def committed_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def settle(torch, fn, seconds: float = 0.1) -> None:
+    """Untimed calls of fn() for a fixed wall time before a leg is timed: after the
+    host-side set-up between legs the GPU's clocks have dropped, and they take tens
+    of milliseconds of load to come back."""
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+
+
 def graph_us(torch, fn, reps: int = 20, replays: int = 5) -> float:
     """Device time per call of fn(): reps calls captured in one HIP graph, replayed
     (removes the host cost of one launch per call from the figure)."""
@@ -100,6 +113,8 @@ def main() -> int:
     ap.add_argument("--legs", default="achievable,config0,two_launch,deporder,rmsnorm,prefill,sweep,decode_m8,"
                                       "ffn100b,scales,encodings",
                     help="secondary legs to run (comma-separated subset of the default)")
+    ap.add_argument("--clock-ramp-ms", type=float, default=300.0,
+                    help="untimed launches of the step for this wall time before the warmup steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling PMC byte counters)")
@@ -152,6 +167,15 @@ def main() -> int:
     # around the timed region divided by the step count is the launch's average
     # duration (inter-launch gaps included).  Events around every launch would add
     # their own dispatch overhead to both the wall time and the launch (~5 us here).
+    # Before the warmup steps the step runs untimed for a fixed wall time: an idle GPU
+    # takes tens of milliseconds of load to leave its low clocks, longer than a few
+    # warmup steps last.
+    ramp_s = max(args.clock_ramp_ms, 0.0) * 1e-3
+    r0 = time.perf_counter()
+    while time.perf_counter() - r0 < ramp_s:
+        for _ in range(64):
+            fplan.launch(stream)
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         fplan.launch(stream)
     torch.cuda.synchronize()
@@ -180,6 +204,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_ramp_ms": args.clock_ramp_ms,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -287,10 +312,7 @@ def main() -> int:
             lplan = tw.bitnet_grouped_plan_linear(
                 [(qs[m.layer][m.slot], sxs[m.layer][m.slot], packed[i], sws[i], ys[i], None) for i, m in enumerate(mats)])
             gemv_bytes = weight_bytes + sum(m.K + 4 * m.N + 8 for m in mats)
-            for _ in range(10):
-                qplan.launch(stream)
-                lplan.launch(stream)
-            torch.cuda.synchronize()
+            settle(torch, lambda: (qplan.launch(stream), lplan.launch(stream)))
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             for i in range(100):
@@ -407,8 +429,7 @@ def main() -> int:
                     q, sx = tw.quant_act(x)
                     N, K = p.shape[0], q.shape[1]
                     y = torch.empty((2048, N), dtype=torch.float32, device=dev)
-                    for _ in range(5):
-                        tw.bitnet_linear(q, sx, p, s, y)
+                    settle(torch, lambda: tw.bitnet_linear(q, sx, p, s, y))
                     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     a.record(stream)
                     for _ in range(reps):
@@ -480,9 +501,7 @@ def main() -> int:
             lplan8 = tw.bitnet_grouped_plan_linear(
                 [(qs8[m.layer][m.slot], sxs8[m.layer][m.slot], packed[i], sws[i], ys8[i], None)
                  for i, m in enumerate(mats)])
-            for _ in range(10):
-                qplan8.launch(stream)
-                lplan8.launch(stream)
+            settle(torch, lambda: (qplan8.launch(stream), lplan8.launch(stream)))
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             for _ in range(100):
@@ -514,8 +533,7 @@ def main() -> int:
                     [(qx[m.layer][m.slot][0], qx[m.layer][m.slot][1], fpacked[i], fsw[i], fys[i], None)
                      for i, m in enumerate(fmats)])
                 run = lambda: plan.launch(stream)
-                for _ in range(3):
-                    run()
+                settle(torch, run)
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
                 for _ in range(20):
@@ -525,7 +543,7 @@ def main() -> int:
                 us = a.elapsed_time(b) * 1e3 / 20
                 key = f"ffn100b_8layers_M{M}"
                 sec[key] = {"us": round(us, 1), "weight_GBs": round(fbytes / (us * 1e-6) / 1e9, 1),
-                            "launches": 1, "kernel": "gemv_grouped_kernel" if M == 1 else "skinny_grouped_kernel"}
+                            "launches": 1, "kernel": "gemv_grouped_kernel" if M == 1 else "skinny2_grouped_kernel"}
                 log(f"{key}: {us:.1f} us, {sec[key]['weight_GBs']} GB/s")
             # one GPU's share of an 8-way column split of the 100B gate matrix (K=8192, N=3584)
             shard = fpacked[0][:3584].contiguous()
@@ -725,7 +743,7 @@ def main() -> int:
                 torch.cuda.synchronize()
                 us = a.elapsed_time(b) * 1e3 / 30
                 dres8[v] = {"us": round(us, 1), "weight_GBs": round(weight_bytes / (us * 1e-6) / 1e9, 1),
-                            "kernel": "skinny_grouped_kernel" if v == "per_tensor" else "gemv_grouped_kernel<true>"}
+                            "kernel": "skinny2_grouped_kernel" if v == "per_tensor" else "gemv_grouped_kernel<true>"}
                 log(f"decode step M=8 two launches, scales {v}: {us:.1f} us")
             sec["decode_step_2p4b_M8_weight_scales"] = dres8
             del gpk, xs8, qs8, sx8, ys8

@@ -407,8 +407,233 @@ __device__ __forceinline__ void skinny_lds_tile(const int8_t *__restrict__ q, co
     }
 }
 
-// Grouped decode on the matrix cores: block -> (descriptor, row block of NW x 16 RG
-// rows) through the plan's block table; every descriptor has M <= 16.
+// ---------------------------------------------------------------------------
+// Line-granular grouped variant (the one grouped launches use).  The weights are
+// read in whole 128-byte lines: the 8 lanes of an octet take the 8 16-byte pieces of
+// one line of one row, so one load instruction covers 8 rows x 128 bytes, and the
+// loads are nontemporal.  A wavefront then regroups each step (one line of each of
+// its rows) into MFMA operands through a small LDS buffer of its own: lane
+// (row i, piece p) writes its 16 bytes, lane (row r16, lane group g) reads pieces 2g
+// and 2g + 1 of row r16 back (one LDS write and one read per 16 bytes, no barrier:
+// a wavefront's LDS accesses are carried out in order).
+//  * MFMA f (0..7) of a step takes, in lane (r16, g), dword f of those 32 bytes:
+//    16 codes of row r16 at k = 16 D + 4b + i (D = the dword's 16-weight block, byte
+//    b), spread by shift + mask into four dwords (dword i, byte b = code of
+//    k = 16 D + 4b + i) as the A operand.  The B operand, lane (token, g), holds the
+//    16 q values of the same block in the same order (a 4x4 byte transpose made once
+//    while staging q), so the k of every (lane group, byte) position agrees.
+//  * Rows whose packed rows start mid-line (K = 6912: every other row starts 64 bytes
+//    into a line) are loaded line-aligned, and a step's window of 8 pieces is shifted
+//    by the rows' offset.  The rows of one 16-row block share their offset: block beta
+//    holds rows 16 P (beta / P) + beta % P + P i, P = the period of the offsets (1, 2,
+//    4 or 8 rows), and a wavefront takes blocks w and w + 8 (one offset).  Pieces
+//    outside the row (or the staged K segment) are written as zero codes.
+//  * The codes are c = t + 1: sum q t = sum q c - sum q, sum q formed while staging.
+//  * The results of the workgroup's 256 rows go through LDS and are stored as whole
+//    row segments per token.
+constexpr int kSk2NW = 8;       // wavefronts per workgroup
+constexpr int kSk2RB = 2;       // 16-row blocks per wavefront
+constexpr int kSk2TDw = 36;     // dwords per row of a wavefront's regrouping buffer (32 + 4 pad)
+constexpr int kSk2Rows = kSk2NW * kSk2RB * 16;
+#ifndef SK2_PRE
+#define SK2_PRE 1       // steps of weight loads issued before the q staging (1 or 2)
+#endif
+#ifndef SK2_WAVES
+#define SK2_WAVES 4     // wavefronts per SIMD the register allocation aims at
+#endif
+
+template <bool NT>
+__device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_base, uint32_t *qs, uint32_t *tb,
+                                             int *sq, double *cms) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g = lane >> 4, o = lane >> 3, l8 = lane & 7;
+    const int M = d.M, N = d.N, K = d.K;
+    const int C = K >> 6, KB = K >> 2;
+    // rows whose packed rows start at the same position within a 128-byte line recur
+    // every P rows (KB is a multiple of 16)
+    const int kbm = KB & 127;
+    const int P = kbm == 0 ? 1 : 128 / (kbm & -kbm);
+    int rb0[kSk2RB];
+    #pragma unroll
+    for (int b = 0; b < kSk2RB; ++b) {
+        const int beta = wave + kSk2NW * b;
+        rb0[b] = row_base + 16 * P * (beta / P) + beta % P;
+    }
+    // pieces (16 bytes) between the start of the line and the rows' first byte
+    const int off = (int)(((uintptr_t)(d.packed + (size_t)rb0[0] * KB) & 127) >> 4);
+    const uint8_t *prow[kSk2RB][2];
+    #pragma unroll
+    for (int b = 0; b < kSk2RB; ++b)
+        #pragma unroll
+        for (int h = 0; h < 2; ++h)
+            prow[b][h] = d.packed + (size_t)min(rb0[b] + P * (8 * h + o), N - 1) * KB;   // rows past N: dropped
+
+    v4i_sk acc[kSk2RB];
+    #pragma unroll
+    for (int b = 0; b < kSk2RB; ++b) acc[b] = v4i_sk{0, 0, 0, 0};
+    if (tid < 16) sq[tid] = 0;
+    const int tokc = min(l16, M - 1);   // tokens past M repeat the last one (outputs dropped)
+    uint32_t *tw = tb + wave * 16 * kSk2TDw;
+    const int seg_chunks = sk_segment_chunks(C, M);
+    const int cdw = sk_chunk_dw(M);
+
+    for (int s0 = 0; s0 < C; s0 += seg_chunks) {
+        const int sc = min(seg_chunks, C - s0), s1 = s0 + sc;
+        // step t: piece l8 of line t (from the rows' line start) is chunk 8t + l8 - off;
+        // the steps whose window [8t - off, 8t + 8 - off) meets [s0, s1)
+        const int t0 = (s0 + off) >> 3, T = ((s1 + off + 7) >> 3) - t0;
+        uint4 wA[kSk2RB][2], wB[kSk2RB][2];
+        auto issue = [&](uint4 (&w)[kSk2RB][2], int t) {
+            const int c = min(max(8 * (t0 + t) + l8 - off, s0), s1 - 1);
+            #pragma unroll
+            for (int b = 0; b < kSk2RB; ++b)
+                #pragma unroll
+                for (int h = 0; h < 2; ++h) w[b][h] = load_weights<NT>(prow[b][h] + 16 * c);
+        };
+        auto consume = [&](const uint4 (&w)[kSk2RB][2], int t) {
+            const int cw = 8 * (t0 + t) - off;        // first chunk of the window
+            const bool valid = cw + l8 >= s0 && cw + l8 < s1;
+            // regroup both blocks through the wavefront's buffer (block 1 written after
+            // block 0 is read back): pw[b][f] = dword f of pieces 2g, 2g + 1 of row l16
+            uint32_t pw[kSk2RB][8];
+            #pragma unroll
+            for (int b = 0; b < kSk2RB; ++b) {
+                #pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    *reinterpret_cast<uint4 *>(tw + (8 * h + o) * kSk2TDw + 4 * l8) =
+                        valid ? w[b][h] : make_uint4(0u, 0u, 0u, 0u);
+                const uint4 a0 = *reinterpret_cast<const uint4 *>(tw + l16 * kSk2TDw + 8 * g);
+                const uint4 a1 = *reinterpret_cast<const uint4 *>(tw + l16 * kSk2TDw + 8 * g + 4);
+                pw[b][0] = a0.x; pw[b][1] = a0.y; pw[b][2] = a0.z; pw[b][3] = a0.w;
+                pw[b][4] = a1.x; pw[b][5] = a1.y; pw[b][6] = a1.z; pw[b][7] = a1.w;
+            }
+            #pragma unroll
+            for (int f = 0; f < 8; ++f) {
+                // B operand: chunk cw + 2g + f / 4, block f % 4 (clamped into the segment
+                // where the codes are zero)
+                const int cl = min(max(cw + 2 * g + (f >> 2) - s0, 0), sc - 1);
+                const v4i_sk bq = *reinterpret_cast<const v4i_sk *>(qs + cl * cdw + ((f & 3) * M + tokc) * 4);
+                #pragma unroll
+                for (int b = 0; b < kSk2RB; ++b) {
+                    const uint32_t x = pw[b][f];
+                    const v4i_sk a = v4i_sk{(int)codes_i(x, 0), (int)codes_i(x, 1), (int)codes_i(x, 2), (int)codes_i(x, 3)};
+                    acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bq, acc[b], 0, 0, 0);
+                }
+            }
+        };
+        // the segment's first SK2_PRE steps of weight loads go out before the staging of q
+        issue(wA, 0);
+        if (SK2_PRE > 1) issue(wB, 1);
+
+        // ---- stage the segment's q: (token m, chunk c) per thread; block D of the chunk
+        // (16 values) transposed as the B operand of the blocks' MFMAs
+        __syncthreads();   // previous segment's LDS reads done; sq initialised
+        // two (token, chunk) items per thread and pass, their loads issued together
+        auto stage_item = [&](int idx, const uint4 (&v)[4]) {
+            const int m = idx / sc, c = idx - m * sc;
+            int sm = 0;
+            #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t p0, p1, p2, p3;
+                transpose4x4(v[j].x, v[j].y, v[j].z, v[j].w, p0, p1, p2, p3);
+                *reinterpret_cast<uint4 *>(qs + c * cdw + (j * M + m) * 4) = make_uint4(p0, p1, p2, p3);
+                sm = dot4(v[j].x, 0x01010101u, sm);
+                sm = dot4(v[j].y, 0x01010101u, sm);
+                sm = dot4(v[j].z, 0x01010101u, sm);
+                sm = dot4(v[j].w, 0x01010101u, sm);
+            }
+            if (sm != 0) atomicAdd(&sq[m], sm);
+        };
+        auto item_src = [&](int idx) {
+            const int m = idx / sc, c = idx - m * sc;
+            return d.q + (size_t)m * K + 64 * (s0 + c);
+        };
+        const int items = M * sc, nth = (int)blockDim.x;
+        for (int idx = tid; idx < items; idx += 2 * nth) {
+            const int idx2 = min(idx + nth, items - 1);   // a clamped duplicate is loaded, not staged
+            const int8_t *src = item_src(idx), *src2 = item_src(idx2);
+            uint4 v[4], v2[4];
+            #pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = gload16(src + 16 * j);
+            #pragma unroll
+            for (int j = 0; j < 4; ++j) v2[j] = gload16(src2 + 16 * j);
+            stage_item(idx, v);
+            if (idx + nth < items) stage_item(idx2, v2);
+        }
+        __syncthreads();
+
+        // pairs of steps, no branch in the loop body; the last one to three peeled
+        if (SK2_PRE > 1) {
+            // steps t and t + 1 are in flight at the top of every iteration
+            int t = 0;
+            for (; t + 3 < T; t += 2) {
+                consume(wA, t);
+                issue(wA, t + 2);
+                consume(wB, t + 1);
+                issue(wB, t + 3);
+            }
+            if (T - t == 3) {
+                consume(wA, t);
+                issue(wA, t + 2);
+                consume(wB, t + 1);
+                consume(wA, t + 2);
+            } else if (T - t == 2) {
+                consume(wA, t);
+                consume(wB, t + 1);
+            } else {
+                consume(wA, t);
+            }
+        } else {
+            const int T2 = (T + 1) & ~1;
+            for (int t = 0; t < T2 - 2; t += 2) {
+                issue(wB, t + 1);
+                consume(wA, t);
+                issue(wA, t + 2);
+                consume(wB, t + 1);
+            }
+            if (T2 == T) {
+                issue(wB, T - 1);
+                consume(wA, T - 2);
+                consume(wB, T - 1);
+            } else {
+                consume(wA, T - 1);
+            }
+        }
+    }
+
+    // ---- epilogue: acc (16 x 16 layout: lane -> token l16, register r -> row 4g + r of
+    // the block) less sum q into LDS as [token][row of the workgroup], then whole row
+    // segments per token, rescaled
+    __syncthreads();   // every wavefront done with the staged q
+    int *ys = reinterpret_cast<int *>(qs);
+    if (l16 < M) {
+        const int sqm = sq[l16];
+        #pragma unroll
+        for (int b = 0; b < kSk2RB; ++b)
+            #pragma unroll
+            for (int r = 0; r < 4; ++r) ys[l16 * kSk2Rows + rb0[b] - row_base + P * (4 * g + r)] = acc[b][r] - sqm;
+    }
+    if (tid < M) cms[tid] = rescale_factor(d.s_x[tid], *d.s_w);
+    __syncthreads();
+    const OutSpec out = d.out();
+    for (int idx = tid; idx < M * kSk2Rows; idx += blockDim.x) {
+        const int m = idx / kSk2Rows, row = row_base + (idx - m * kSk2Rows);
+        if (row < N) {
+            const size_t o2 = (size_t)m * N + row;
+            const int v = ys[idx];
+            put_y(out, o2, row, v, col_factor(out, d.s_w, row, d.s_x[m], cms[m]));
+            if (d.acc) d.acc[o2] = v;
+        }
+    }
+}
+
+#ifndef BITNET_SKINNY_V2
+#define BITNET_SKINNY_V2 1
+#endif
+
+// Grouped decode on the matrix cores: block -> (descriptor, row block of 256 rows)
+// through the plan's block table; every descriptor has M <= 16.
 __global__ __launch_bounds__(64 * kGroupedSkNW) void skinny_grouped_kernel(const uint8_t *__restrict__ plan) {
     extern __shared__ __attribute__((aligned(16))) uint32_t qs[];   // staged q of one segment
     __shared__ int sq[16];
@@ -419,13 +644,30 @@ __global__ __launch_bounds__(64 * kGroupedSkNW) void skinny_grouped_kernel(const
                                                          (int)e.local * kGroupedSkNW * 16 * kGroupedSkRG, qs, sq);
 }
 
+__global__ __launch_bounds__(64 * kSk2NW) __attribute__((amdgpu_waves_per_eu(SK2_WAVES))) void skinny2_grouped_kernel(const uint8_t *__restrict__ plan) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t qs[];   // staged q of one segment; results
+    __shared__ __attribute__((aligned(16))) uint32_t tb[kSk2NW * 16 * kSk2TDw];
+    __shared__ int sq[16];
+    __shared__ double cms[16];
+    const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
+    const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[blockIdx.x];
+    const LinearDescDev d = reinterpret_cast<const LinearDescDev *>(plan + h->desc_offset)[e.desc];
+    skinny2_tile<true>(d, (int)e.local * kSk2Rows, qs, tb, sq, cms);
+}
+
+static_assert(kSk2Rows == kGroupedSkNW * 16 * kGroupedSkRG, "both grouped variants take 256-row blocks");
+
 uint32_t skinny_grouped_rows_per_block() { return kGroupedSkNW * 16 * kGroupedSkRG; }
 uint32_t skinny_grouped_lds_bytes(int64_t M, int64_t K) {
-    return (uint32_t)(sk_segment_chunks((int)(K / 64), (int)M) * sk_chunk_dw((int)M) * 4);
+    const uint32_t stage = (uint32_t)(sk_segment_chunks((int)(K / 64), (int)M) * sk_chunk_dw((int)M) * 4);
+    // the line-granular variant also keeps the results of its 256 rows there (16 tokens)
+    return BITNET_SKINNY_V2 ? std::max<uint32_t>(stage, 16u * kSk2Rows * 4u) : stage;
 }
 
 hipError_t launch_skinny_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st) {
-    skinny_grouped_kernel<<<dim3(blocks), dim3(64 * kGroupedSkNW), lds_bytes, st>>>(reinterpret_cast<const uint8_t *>(plan_dev));
+    const uint8_t *p = reinterpret_cast<const uint8_t *>(plan_dev);
+    if (BITNET_SKINNY_V2) skinny2_grouped_kernel<<<dim3(blocks), dim3(64 * kSk2NW), lds_bytes, st>>>(p);
+    else skinny_grouped_kernel<<<dim3(blocks), dim3(64 * kGroupedSkNW), lds_bytes, st>>>(p);
     return hipGetLastError();
 }
 
