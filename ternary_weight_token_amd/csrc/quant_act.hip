@@ -20,9 +20,19 @@ __device__ __forceinline__ void quant_row(const uint16_t *__restrict__ x, int K,
     __shared__ uint32_t red[kQThreads / 64];
     const int tid = threadIdx.x;
     uint32_t mx = 0;
+    // VEC: the first kHold pieces of 8 values of each thread stay in registers from the
+    // max to the codes (all of K <= 8192); later pieces are read again
+    constexpr int kHold = 4;
+    uint4 held[kHold];
     if (VEC) {
         const uint4 *xv = reinterpret_cast<const uint4 *>(x);
-        for (int v = tid; v < (K >> 3); v += kQThreads) mx = max(mx, absmax8(xv[v]));
+        #pragma unroll
+        for (int j = 0; j < kHold; ++j) {
+            const int v = tid + kQThreads * j;
+            held[j] = v < (K >> 3) ? xv[v] : make_uint4(0u, 0u, 0u, 0u);
+            mx = max(mx, absmax8(held[j]));
+        }
+        for (int v = tid + kQThreads * kHold; v < (K >> 3); v += kQThreads) mx = max(mx, absmax8(xv[v]));
     } else {
         for (int k = tid; k < K; k += kQThreads) mx = max(mx, (uint32_t)(x[k] & 0x7FFFu));
     }
@@ -36,7 +46,12 @@ __device__ __forceinline__ void quant_row(const uint16_t *__restrict__ x, int K,
     if (VEC) {
         const uint4 *xv = reinterpret_cast<const uint4 *>(x);
         uint2 *qv = reinterpret_cast<uint2 *>(q);
-        for (int v = tid; v < (K >> 3); v += kQThreads) {
+        #pragma unroll
+        for (int j = 0; j < kHold; ++j) {
+            const int v = tid + kQThreads * j;
+            if (v < (K >> 3)) qv[v] = mx != 0 ? qcode8(held[j], s, inv) : make_uint2(0u, 0u);
+        }
+        for (int v = tid + kQThreads * kHold; v < (K >> 3); v += kQThreads) {
             qv[v] = mx != 0 ? qcode8(xv[v], s, inv) : make_uint2(0u, 0u);
         }
     } else {

@@ -475,6 +475,7 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
     if (tid < 16) sq[tid] = 0;
     const int tokc = min(l16, M - 1);   // tokens past M repeat the last one (outputs dropped)
     uint32_t *tw = tb + wave * 16 * kSk2TDw;
+    static_assert(kSk2NW * 64 * 2 * 4 * (16 * 16 + 4) >= 16 * 65536, "one staging pass covers a segment");
     const int seg_chunks = sk_segment_chunks(C, M);
     const int cdw = sk_chunk_dw(M);
 
@@ -522,14 +523,10 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
                 }
             }
         };
-        // the segment's first SK2_PRE steps of weight loads go out before the staging of q
-        issue(wA, 0);
-        if (SK2_PRE > 1) issue(wB, 1);
-
-        // ---- stage the segment's q: (token m, chunk c) per thread; block D of the chunk
-        // (16 values) transposed as the B operand of the blocks' MFMAs
-        __syncthreads();   // previous segment's LDS reads done; sq initialised
-        // two (token, chunk) items per thread and pass, their loads issued together
+        // ---- stage the segment's q: (token m, chunk c) items, two per thread and pass; block
+        // D of a chunk (16 values) transposed as the B operand of the blocks' MFMAs.  The
+        // first pass's q loads go out before the segment's first weight loads, so that the
+        // staging waits for its own (L2-resident) data only, not for the weights.
         auto stage_item = [&](int idx, const uint4 (&v)[4]) {
             const int m = idx / sc, c = idx - m * sc;
             int sm = 0;
@@ -545,23 +542,28 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
             }
             if (sm != 0) atomicAdd(&sq[m], sm);
         };
-        auto item_src = [&](int idx) {
-            const int m = idx / sc, c = idx - m * sc;
-            return d.q + (size_t)m * K + 64 * (s0 + c);
-        };
         const int items = M * sc, nth = (int)blockDim.x;
-        for (int idx = tid; idx < items; idx += 2 * nth) {
-            const int idx2 = min(idx + nth, items - 1);   // a clamped duplicate is loaded, not staged
-            const int8_t *src = item_src(idx), *src2 = item_src(idx2);
-            uint4 v[4], v2[4];
+        // item idx (clamped: a duplicate is loaded, not staged) into v
+        auto load_item = [&](int idx, uint4 (&v)[4]) {
+            const int i = min(idx, items - 1);
+            const int m = i / sc, c = i - m * sc;
+            const int8_t *src = d.q + (size_t)m * K + 64 * (s0 + c);
             #pragma unroll
             for (int j = 0; j < 4; ++j) v[j] = gload16(src + 16 * j);
-            #pragma unroll
-            for (int j = 0; j < 4; ++j) v2[j] = gload16(src2 + 16 * j);
-            stage_item(idx, v);
-            if (idx + nth < items) stage_item(idx2, v2);
-        }
-        __syncthreads();
+        };
+        // A segment holds at most 2 nth items (64 KiB of 16 M + 4 dwords per chunk is under
+        // 1024 / M chunks), so one pass stages it.  The barriers wait for the LDS accesses
+        // only (an s_barrier after lgkmcnt(0)): __syncthreads() would also wait for the
+        // weight loads in flight.
+        uint4 v[4], v2[4];
+        load_item(tid, v);
+        load_item(tid + nth, v2);
+        issue(wA, 0);
+        if (SK2_PRE > 1) issue(wB, 1);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // previous segment's LDS reads done
+        if (tid < items) stage_item(tid, v);
+        if (tid + nth < items) stage_item(tid + nth, v2);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
         // pairs of steps, no branch in the loop body; the last one to three peeled
         if (SK2_PRE > 1) {
