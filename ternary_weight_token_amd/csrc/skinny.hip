@@ -435,6 +435,7 @@ constexpr int kSk2NW = 8;       // wavefronts per workgroup
 constexpr int kSk2RB = 2;       // 16-row blocks per wavefront
 constexpr int kSk2TDw = 36;     // dwords per row of a wavefront's regrouping buffer (32 + 4 pad)
 constexpr int kSk2Rows = kSk2NW * kSk2RB * 16;
+constexpr int kSk2YStride = kSk2Rows + 1;   // ints per token row of the staged results
 #ifndef SK2_PRE
 #define SK2_PRE 1       // steps of weight loads issued before the q staging (1 or 2)
 #endif
@@ -608,22 +609,23 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
     // the block) less sum q into LDS as [token][row of the workgroup], then whole row
     // segments per token, rescaled
     __syncthreads();   // every wavefront done with the staged q
+    // rows of kSk2YStride ints: the 16 tokens of one row fall on 16 different banks
     int *ys = reinterpret_cast<int *>(qs);
     if (l16 < M) {
         const int sqm = sq[l16];
         #pragma unroll
         for (int b = 0; b < kSk2RB; ++b)
             #pragma unroll
-            for (int r = 0; r < 4; ++r) ys[l16 * kSk2Rows + rb0[b] - row_base + P * (4 * g + r)] = acc[b][r] - sqm;
+            for (int r = 0; r < 4; ++r) ys[l16 * kSk2YStride + rb0[b] - row_base + P * (4 * g + r)] = acc[b][r] - sqm;
     }
     if (tid < M) cms[tid] = rescale_factor(d.s_x[tid], *d.s_w);
     __syncthreads();
     const OutSpec out = d.out();
     for (int idx = tid; idx < M * kSk2Rows; idx += blockDim.x) {
-        const int m = idx / kSk2Rows, row = row_base + (idx - m * kSk2Rows);
+        const int m = idx / kSk2Rows, rr = idx - m * kSk2Rows, row = row_base + rr;
         if (row < N) {
             const size_t o2 = (size_t)m * N + row;
-            const int v = ys[idx];
+            const int v = ys[m * kSk2YStride + rr];
             put_y(out, o2, row, v, col_factor(out, d.s_w, row, d.s_x[m], cms[m]));
             if (d.acc) d.acc[o2] = v;
         }
@@ -663,7 +665,7 @@ uint32_t skinny_grouped_rows_per_block() { return kGroupedSkNW * 16 * kGroupedSk
 uint32_t skinny_grouped_lds_bytes(int64_t M, int64_t K) {
     const uint32_t stage = (uint32_t)(sk_segment_chunks((int)(K / 64), (int)M) * sk_chunk_dw((int)M) * 4);
     // the line-granular variant also keeps the results of its 256 rows there (16 tokens)
-    return BITNET_SKINNY_V2 ? std::max<uint32_t>(stage, 16u * kSk2Rows * 4u) : stage;
+    return BITNET_SKINNY_V2 ? std::max<uint32_t>(stage, 16u * kSk2YStride * 4u) : stage;
 }
 
 hipError_t launch_skinny_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st) {
