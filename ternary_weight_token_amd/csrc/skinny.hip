@@ -254,7 +254,10 @@ hipError_t launch_skinny(const int8_t *q, const float *s_x, const uint8_t *packe
 // reads its B operands from LDS; sum_k q is formed while staging.  A segment is as
 // long as the LDS budget allows for the problem's M tokens: the whole K for every
 // decode-step shape up to 12 tokens; one barrier pair per segment.
-constexpr int kSkLdsBudget = 64 * 1024;
+#ifndef BITNET_SK_LDS_KB
+#define BITNET_SK_LDS_KB 64
+#endif
+constexpr int kSkLdsBudget = BITNET_SK_LDS_KB * 1024;
 
 // A staged chunk takes 64 M bytes of q plus 16 bytes of padding: the threads that
 // stage consecutive chunks (and the lane groups that read them) then fall 4 banks
@@ -436,6 +439,7 @@ constexpr int kSk2RB = 2;       // 16-row blocks per wavefront
 constexpr int kSk2TDw = 36;     // dwords per row of a wavefront's regrouping buffer (32 + 4 pad)
 constexpr int kSk2Rows = kSk2NW * kSk2RB * 16;
 constexpr int kSk2YStride = kSk2Rows + 1;   // ints per token row of the staged results
+constexpr int kSk2Items = (kSkLdsBudget / 64 + 64 * kSk2NW - 1) / (64 * kSk2NW);   // staged items per thread
 #ifndef SK2_PRE
 #define SK2_PRE 1       // steps of weight loads issued before the q staging (1 or 2)
 #endif
@@ -476,7 +480,7 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
     if (tid < 16) sq[tid] = 0;
     const int tokc = min(l16, M - 1);   // tokens past M repeat the last one (outputs dropped)
     uint32_t *tw = tb + wave * 16 * kSk2TDw;
-    static_assert(kSk2NW * 64 * 2 * 4 * (16 * 16 + 4) >= 16 * 65536, "one staging pass covers a segment");
+    static_assert(kSk2Items * kSk2NW * 64 * 64 >= kSkLdsBudget, "one staging pass covers a segment");
     const int seg_chunks = sk_segment_chunks(C, M);
     const int cdw = sk_chunk_dw(M);
 
@@ -552,18 +556,19 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
             #pragma unroll
             for (int j = 0; j < 4; ++j) v[j] = gload16(src + 16 * j);
         };
-        // A segment holds at most 2 nth items (64 KiB of 16 M + 4 dwords per chunk is under
-        // 1024 / M chunks), so one pass stages it.  The barriers wait for the LDS accesses
-        // only (an s_barrier after lgkmcnt(0)): __syncthreads() would also wait for the
-        // weight loads in flight.
-        uint4 v[4], v2[4];
-        load_item(tid, v);
-        load_item(tid + nth, v2);
+        // A segment holds fewer than kSk2Items nth items (the LDS budget over 16 M + 4
+        // dwords per chunk is under budget / 64 / M chunks), so one pass stages it.  The
+        // barriers wait for the LDS accesses only (an s_barrier after lgkmcnt(0)):
+        // __syncthreads() would also wait for the weight loads in flight.
+        uint4 v[kSk2Items][4];
+        #pragma unroll
+        for (int u = 0; u < kSk2Items; ++u) load_item(tid + u * nth, v[u]);
         issue(wA, 0);
         if (SK2_PRE > 1) issue(wB, 1);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // previous segment's LDS reads done
-        if (tid < items) stage_item(tid, v);
-        if (tid + nth < items) stage_item(tid + nth, v2);
+        #pragma unroll
+        for (int u = 0; u < kSk2Items; ++u)
+            if (tid + u * nth < items) stage_item(tid + u * nth, v[u]);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
         // pairs of steps, no branch in the loop body; the last one to three peeled
