@@ -1267,3 +1267,34 @@ def test_grouped_plan_builders_check_tensors():
                  (x, p, sw, y, None, None, None, None, 0.0, z((N - 1,), torch.float32))]:
         with pytest.raises(ValueError):
             tw.bitnet_grouped_plan_fused([prob])
+
+
+@pytest.mark.parametrize("M", [2, 5, 8, 16])
+def test_grouped_mfma_decode_packed_at_line_offsets(M):
+    """Grouped MFMA decode with each matrix's packed rows starting 16 .. 112 bytes into a
+    128-byte line (views into one buffer at those byte offsets): the kernel loads whole
+    lines and shifts each 16-row block's window by the rows' offset, whose period is 1, 2,
+    4 or 8 rows for these K (K / 4 = 640, 1728, 160, 16 bytes per row).  acc bit for bit,
+    y to the bound."""
+    shapes = [(300, 2560, 16), (257, 6912, 48), (70, 640, 64), (33, 64, 112), (129, 6912, 80)]
+    probs, refs = [], []
+    for i, (N, K, off) in enumerate(shapes):
+        key = synth.stream_key(331, M, i)
+        x, q, s = quantized_inputs(key, M, K)
+        packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
+        s_w = np.float32(0.0057 * (i + 1))
+        refs.append(oracle.linear(q, s, packed, s_w))
+        buf = torch.zeros(N * K // 4 + 256, dtype=torch.uint8, device=DEV)
+        assert buf.data_ptr() % 128 == 0
+        view = buf[off:off + N * K // 4].view(N, K // 4)
+        view.copy_(torch.from_numpy(packed))
+        y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+        acc = torch.full((M, N), -1, dtype=torch.int32, device=DEV)
+        probs.append((torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV), view,
+                      torch.tensor([s_w], dtype=torch.float32, device=DEV), y, acc))
+    plan = tw.bitnet_grouped_plan_linear(probs)
+    plan.launch()
+    torch.cuda.synchronize()
+    for (acc_ref, y_ref), pr in zip(refs, probs):
+        assert np.array_equal(pr[5].cpu().numpy(), acc_ref)
+        assert_y(pr[4].cpu().numpy(), y_ref)
