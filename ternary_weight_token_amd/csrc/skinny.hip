@@ -222,8 +222,15 @@ double skinny_estimate_us(int64_t M, int64_t N, int64_t K) {
     return w / 3.5e6 + 5.0 + (double)(tiles - 1) * (w / 4.0e6 + 1.8);
 }
 
+static bool skinny2_single_ok(const int8_t *q, const uint8_t *packed, int64_t M, int64_t N, int64_t K, const OutSpec &y);
+static hipError_t launch_skinny2_single(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
+                                        int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st);
+
 hipError_t launch_skinny(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                          int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st) {
+    // Many rows (at least two 256-row workgroups per CU): the line-granular kernel of the
+    // grouped launches, one 256-row block per workgroup, all tokens at once.
+    if (skinny2_single_ok(q, packed, M, N, K, y)) return launch_skinny2_single(q, s_x, packed, s_w, M, N, K, y, acc, st);
     // Rows per wavefront (16 RG) against parallelism: the largest RG whose launch,
     // with K split over up to 8 wavefronts of a workgroup (at least 8 chunks per
     // slice), still reaches 2048 wavefronts (one workgroup per CU); more row groups
@@ -665,6 +672,38 @@ __global__ __launch_bounds__(64 * kSk2NW) __attribute__((amdgpu_waves_per_eu(SK2
 }
 
 static_assert(kSk2Rows == kGroupedSkNW * 16 * kGroupedSkRG, "both grouped variants take 256-row blocks");
+
+// The same kernel for one matrix (bitnet_linear with 2..16 tokens and many rows):
+// workgroup b takes rows 256 b .. 256 b + 255.
+__global__ __launch_bounds__(64 * kSk2NW) __attribute__((amdgpu_waves_per_eu(SK2_WAVES))) void skinny2_kernel(
+    const int8_t *__restrict__ q, const float *__restrict__ s_x, const uint8_t *__restrict__ packed,
+    const float *__restrict__ s_w, int M, int N, int K, const OutSpec out, int32_t *__restrict__ acc) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t qs[];
+    __shared__ __attribute__((aligned(16))) uint32_t tb[kSk2NW * 16 * kSk2TDw];
+    __shared__ int sq[16];
+    __shared__ double cms[16];
+    const LinearDescDev d{q, s_x, packed, s_w, out.y, acc, M, N, K, out.w_group, out.bias, out.bf16, 0};
+    skinny2_tile<true>(d, (int)blockIdx.x * kSk2Rows, qs, tb, sq, cms);
+}
+
+// At least 2 workgroups per CU of a 256-CU part, up to 16 tokens, whole 64-weight
+// chunks and 16-byte aligned q / packed rows (the grouped launches' preconditions);
+// group-wise weight scales take the GEMV.
+constexpr int64_t kSk2SingleMinRows = 512 * (int64_t)kSk2Rows;
+
+static bool skinny2_single_ok(const int8_t *q, const uint8_t *packed, int64_t M, int64_t N, int64_t K, const OutSpec &y) {
+    return BITNET_SKINNY_V2 && M >= 1 && M <= 16 && N >= kSk2SingleMinRows && N < ((int64_t)1 << 31) && K % 64 == 0 &&
+           K < ((int64_t)1 << 30) && reinterpret_cast<uintptr_t>(q) % 16 == 0 && reinterpret_cast<uintptr_t>(packed) % 16 == 0 &&
+           (y.w_group == 0 || y.w_group == K);
+}
+
+static hipError_t launch_skinny2_single(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
+                                        int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st) {
+    const unsigned blocks = (unsigned)((N + kSk2Rows - 1) / kSk2Rows);
+    skinny2_kernel<<<dim3(blocks), dim3(64 * kSk2NW), skinny_grouped_lds_bytes(M, K), st>>>(
+        q, s_x, packed, s_w, (int)M, (int)N, (int)K, y, acc);
+    return hipGetLastError();
+}
 
 uint32_t skinny_grouped_rows_per_block() { return kGroupedSkNW * 16 * kGroupedSkRG; }
 uint32_t skinny_grouped_lds_bytes(int64_t M, int64_t K) {

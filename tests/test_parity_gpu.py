@@ -1298,3 +1298,14 @@ def test_grouped_mfma_decode_packed_at_line_offsets(M):
     for (acc_ref, y_ref), pr in zip(refs, probs):
         assert np.array_equal(pr[5].cpu().numpy(), acc_ref)
         assert_y(pr[4].cpu().numpy(), y_ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(2, 131072 + 300, 128), (8, 131072 + 17, 704), (16, 131072, 256), (5, 140000, 6912 // 4)])
+def test_linear_many_rows_line_granular(M, N, K):
+    """bitnet_linear with 2..16 tokens on a matrix of 131072 rows or more runs the
+    line-granular MFMA decode kernel (one 256-row block per workgroup); ragged last
+    block, rows starting mid-line (K / 4 = 32, 176, 64, 432 bytes per row)."""
+    key = synth.stream_key(332, M, N, K)
+    x, q, s = quantized_inputs(key, M, K)
+    packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
+    check_linear(q, s, packed, np.float32(0.0043), kernels=(0, 4))
