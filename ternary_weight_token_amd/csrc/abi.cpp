@@ -299,16 +299,20 @@ static size_t plan_layout(int count, size_t desc_size, uint64_t blocks, uint64_t
 
 // A plan whose problems all have M == 1 runs the GEMV (q staged in LDS); any M > 1
 // makes it run the MFMA decode kernel, which reads each weight once for all M tokens.
-// Problems with group-wise weight scales (w_group below K) make the whole plan run
-// the GEMV with its grouped path (the MFMA decode kernel has none): one token per
-// workgroup, or kGemvGroupsMT tokens per workgroup when any problem has M > 1.
+// Problems with group-wise weight scales (w_group below K) make the whole plan run the
+// kernels' group-wise paths: the GEMV's (one token per workgroup) when every M is 1,
+// else the MFMA decode kernel's (BITNET_GROUPS_MFMA = 0: the GEMV's with kGemvGroupsMT
+// tokens per workgroup, which reads the weights once per kGemvGroupsMT tokens).
+#ifndef BITNET_GROUPS_MFMA
+#define BITNET_GROUPS_MFMA 1
+#endif
 static bool desc_groups(const bitnet_linear_desc &d) { return d.w_group > 0 && d.w_group < d.K; }
 
 static uint32_t linear_variant(const bitnet_linear_desc *d, int count) {
     for (int i = 0; i < count; ++i) {
         if (desc_groups(d[i])) {
             for (int j = 0; j < count; ++j)
-                if (d[j].M > 1) return kVariantGemvGroupsMT;
+                if (d[j].M > 1) return BITNET_GROUPS_MFMA ? kVariantMfmaGroups : kVariantGemvGroupsMT;
             return kVariantGemvGroups;
         }
     }
@@ -318,7 +322,7 @@ static uint32_t linear_variant(const bitnet_linear_desc *d, int count) {
 }
 
 static uint64_t linear_blocks(const bitnet_linear_desc &d, uint32_t variant) {
-    if (variant == kVariantMfma) {
+    if (variant == kVariantMfma || variant == kVariantMfmaGroups) {
         const uint64_t rows = skinny_grouped_rows_per_block();
         return ((uint64_t)d.N + rows - 1) / rows;
     }
@@ -438,9 +442,10 @@ BITNET_API int bitnet_grouped_plan_linear(const bitnet_linear_desc *descs, int c
     h->total_blocks = (uint32_t)blocks;
     h->block_threads = gemv_grouped_threads();
     h->variant = variant;
-    if (variant == kVariantMfma) {
+    if (variant == kVariantMfma || variant == kVariantMfmaGroups) {
         h->rows_per_block = skinny_grouped_rows_per_block();
-        for (int i = 0; i < count; ++i) h->lds_bytes = std::max(h->lds_bytes, skinny_grouped_lds_bytes(descs[i].M, descs[i].K));
+        for (int i = 0; i < count; ++i)
+            h->lds_bytes = std::max(h->lds_bytes, skinny_grouped_lds_bytes(descs[i].M, descs[i].K, desc_groups(descs[i])));
     } else {
         h->rows_per_block = gemv_grouped_rows_per_block();
         // each descriptor is staged by the path its own scales take (group-wise
@@ -596,8 +601,9 @@ BITNET_API int bitnet_linear_grouped(const void *plan_host, const void *plan_dev
     if (st) return st;
     const PlanHeader *h = (const PlanHeader *)plan_host;
     if (h->total_blocks == 0) return BITNET_OK;
-    if (h->variant == kVariantMfma)
-        return hip_status(launch_skinny_grouped(plan_dev, h->total_blocks, h->lds_bytes, (hipStream_t)stream));
+    if (h->variant == kVariantMfma || h->variant == kVariantMfmaGroups)
+        return hip_status(launch_skinny_grouped(plan_dev, h->total_blocks, h->lds_bytes, h->variant == kVariantMfmaGroups,
+                                                (hipStream_t)stream));
     if (h->variant != kVariantGemv && h->variant != kVariantGemvGroups && h->variant != kVariantGemvGroupsMT)
         return fail(BITNET_ERR_ARG, "not a plan of this kind");
     return hip_status(launch_gemv_grouped(plan_dev, h->total_blocks, h->lds_bytes, h->variant,

@@ -37,6 +37,9 @@ constexpr uint32_t kVariantGemv = 0, kVariantMfma = 1;
 // workgroup, so that the weights are read once per kGemvGroupsMT tokens.
 constexpr uint32_t kVariantGemvGroups = 2, kVariantGemvGroupsMT = 3;
 constexpr int kGemvGroupsMT = 4;
+// ... and the MFMA decode kernel with its group-wise path, for plans with such weights
+// and any M > 1 (every problem once over its weights, all tokens at once).
+constexpr uint32_t kVariantMfmaGroups = 4;
 // Fused plan variants: a mask of what its problems use beyond the plain path (an
 // RMSNorm; fp32 input rows or gate / up pairs, the two ends of SwiGLU); each mask
 // has its own kernel, so a plan without them takes the kernel without that code.
@@ -124,9 +127,9 @@ double skinny_estimate_us(int64_t M, int64_t N, int64_t K);
 double gemm_estimate_us(int64_t M, int64_t N, int64_t K);
 hipError_t launch_skinny(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                          int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st);
-hipError_t launch_skinny_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st);
+hipError_t launch_skinny_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, bool grp, hipStream_t st);
 uint32_t skinny_grouped_rows_per_block();
-uint32_t skinny_grouped_lds_bytes(int64_t M, int64_t K);
+uint32_t skinny_grouped_lds_bytes(int64_t M, int64_t K, bool grp = false);
 hipError_t launch_gemm(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                        int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st);
 hipError_t launch_gemm_cfg(int cfg, const int8_t *q, const float *s_x, const uint8_t *packed,

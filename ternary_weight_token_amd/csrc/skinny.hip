@@ -454,9 +454,16 @@ constexpr int kSk2Items = (kSkLdsBudget / 64 + 64 * kSk2NW - 1) / (64 * kSk2NW);
 #define SK2_WAVES 4     // wavefronts per SIMD the register allocation aims at
 #endif
 
-template <bool NT>
+// GRP: group-wise weight scales (d.w_group = G below K, a multiple of 64; s_w is
+// [N][K / G]).  Then MFMA f of a step takes piece f (one 64-weight chunk, a single
+// group's) in every lane group: lane (row r16, group g) holds dword g of piece f, and
+// the B operand block g of that chunk.  After the MFMA of a group's last chunk its
+// products, less the group's sum of q (per-chunk sums kept while staging), are scaled
+// by the rows' group scales into float64 accumulators; the scales travel with the
+// weights (loaded beside each piece, regrouped through LDS with them).
+template <bool NT, bool GRP>
 __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_base, uint32_t *qs, uint32_t *tb,
-                                             int *sq, double *cms) {
+                                             float *tsc, int *sq, double *cms) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g = lane >> 4, o = lane >> 3, l8 = lane & 7;
@@ -475,6 +482,8 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
     // pieces (16 bytes) between the start of the line and the rows' first byte
     const int off = (int)(((uintptr_t)(d.packed + (size_t)rb0[0] * KB) & 127) >> 4);
     const uint8_t *prow[kSk2RB][2];
+    // GRP: chunks per scale group, groups per row
+    const int gc = GRP ? d.w_group >> 6 : 1, ng = GRP ? K / d.w_group : 1;
     #pragma unroll
     for (int b = 0; b < kSk2RB; ++b)
         #pragma unroll
@@ -484,38 +493,64 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
     v4i_sk acc[kSk2RB];
     #pragma unroll
     for (int b = 0; b < kSk2RB; ++b) acc[b] = v4i_sk{0, 0, 0, 0};
+    // GRP: sum over the groups done of (products - sum q) s_g and of (products - sum q)
+    double facc[GRP ? kSk2RB : 1][4];
+    int itot[GRP ? kSk2RB : 1][4];
+    int sqrun = 0;   // GRP: sum of q over the current group's chunks so far (lane's token)
+    if (GRP) {
+        #pragma unroll
+        for (int b = 0; b < kSk2RB; ++b)
+            #pragma unroll
+            for (int r = 0; r < 4; ++r) { facc[b][r] = 0.0; itot[b][r] = 0; }
+    }
     if (tid < 16) sq[tid] = 0;
     const int tokc = min(l16, M - 1);   // tokens past M repeat the last one (outputs dropped)
     uint32_t *tw = tb + wave * 16 * kSk2TDw;
+    float *ts = GRP ? tsc + wave * kSk2RB * 8 * 16 : nullptr;   // GRP: [block][piece][row] scales of a step
     static_assert(kSk2Items * kSk2NW * 64 * 64 >= kSkLdsBudget, "one staging pass covers a segment");
     const int seg_chunks = sk_segment_chunks(C, M);
     const int cdw = sk_chunk_dw(M);
+    int *sqc = reinterpret_cast<int *>(qs + seg_chunks * cdw);   // GRP: [token][chunk] sums of q
 
     for (int s0 = 0; s0 < C; s0 += seg_chunks) {
         const int sc = min(seg_chunks, C - s0), s1 = s0 + sc;
         // step t: piece l8 of line t (from the rows' line start) is chunk 8t + l8 - off;
         // the steps whose window [8t - off, 8t + 8 - off) meets [s0, s1)
         const int t0 = (s0 + off) >> 3, T = ((s1 + off + 7) >> 3) - t0;
-        uint4 wA[kSk2RB][2], wB[kSk2RB][2];
-        auto issue = [&](uint4 (&w)[kSk2RB][2], int t) {
+        struct WBuf { uint4 w[kSk2RB][2]; float s[GRP ? kSk2RB : 1][2]; };
+        WBuf wA, wB;
+        auto issue = [&](WBuf &w, int t) {
             const int c = min(max(8 * (t0 + t) + l8 - off, s0), s1 - 1);
+            const int grp = GRP ? c / gc : 0;
             #pragma unroll
             for (int b = 0; b < kSk2RB; ++b)
                 #pragma unroll
-                for (int h = 0; h < 2; ++h) w[b][h] = load_weights<NT>(prow[b][h] + 16 * c);
+                for (int h = 0; h < 2; ++h) {
+                    w.w[b][h] = load_weights<NT>(prow[b][h] + 16 * c);
+                    // GRP: the loading lane's row's scale of the chunk's group
+                    if (GRP) w.s[b][h] = d.s_w[(size_t)min(rb0[b] + P * (8 * h + o), N - 1) * ng + grp];
+                }
         };
-        auto consume = [&](const uint4 (&w)[kSk2RB][2], int t) {
+        auto consume = [&](const WBuf &w, int t) {
             const int cw = 8 * (t0 + t) - off;        // first chunk of the window
             const bool valid = cw + l8 >= s0 && cw + l8 < s1;
             // regroup both blocks through the wavefront's buffer (block 1 written after
-            // block 0 is read back): pw[b][f] = dword f of pieces 2g, 2g + 1 of row l16
+            // block 0 is read back).  Plain: pw[b][f] = dword f of pieces 2g, 2g + 1 of
+            // row l16; GRP: dword g of piece f (pieces stored dword-major)
             uint32_t pw[kSk2RB][8];
             #pragma unroll
             for (int b = 0; b < kSk2RB; ++b) {
                 #pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    *reinterpret_cast<uint4 *>(tw + (8 * h + o) * kSk2TDw + 4 * l8) =
-                        valid ? w[b][h] : make_uint4(0u, 0u, 0u, 0u);
+                for (int h = 0; h < 2; ++h) {
+                    const uint4 v = valid ? w.w[b][h] : make_uint4(0u, 0u, 0u, 0u);
+                    if (GRP) {
+                        uint32_t *dst = tw + (8 * h + o) * kSk2TDw + l8;
+                        dst[0] = v.x; dst[8] = v.y; dst[16] = v.z; dst[24] = v.w;
+                        ts[(b * 8 + l8) * 16 + 8 * h + o] = w.s[b][h];
+                    } else {
+                        *reinterpret_cast<uint4 *>(tw + (8 * h + o) * kSk2TDw + 4 * l8) = v;
+                    }
+                }
                 const uint4 a0 = *reinterpret_cast<const uint4 *>(tw + l16 * kSk2TDw + 8 * g);
                 const uint4 a1 = *reinterpret_cast<const uint4 *>(tw + l16 * kSk2TDw + 8 * g + 4);
                 pw[b][0] = a0.x; pw[b][1] = a0.y; pw[b][2] = a0.z; pw[b][3] = a0.w;
@@ -523,22 +558,43 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
             }
             #pragma unroll
             for (int f = 0; f < 8; ++f) {
-                // B operand: chunk cw + 2g + f / 4, block f % 4 (clamped into the segment
-                // where the codes are zero)
-                const int cl = min(max(cw + 2 * g + (f >> 2) - s0, 0), sc - 1);
-                const v4i_sk bq = *reinterpret_cast<const v4i_sk *>(qs + cl * cdw + ((f & 3) * M + tokc) * 4);
+                // B operand.  Plain: chunk cw + 2g + f / 4, block f % 4; GRP: chunk cw + f,
+                // block g (clamped into the segment where the codes are zero)
+                const int craw = GRP ? cw + f : cw + 2 * g + (f >> 2);
+                const int cl = min(max(craw - s0, 0), sc - 1);
+                const v4i_sk bq = *reinterpret_cast<const v4i_sk *>(qs + cl * cdw + ((GRP ? g : (f & 3)) * M + tokc) * 4);
                 #pragma unroll
                 for (int b = 0; b < kSk2RB; ++b) {
                     const uint32_t x = pw[b][f];
                     const v4i_sk a = v4i_sk{(int)codes_i(x, 0), (int)codes_i(x, 1), (int)codes_i(x, 2), (int)codes_i(x, 3)};
                     acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bq, acc[b], 0, 0, 0);
                 }
+                if (GRP && craw >= s0 && craw < s1) {
+                    sqrun += sqc[tokc * seg_chunks + cl];
+                    if ((craw + 1) % gc == 0) {
+                        // the group's last chunk: fold its products into the accumulators
+                        #pragma unroll
+                        for (int b = 0; b < kSk2RB; ++b) {
+                            const float4 s4 = *reinterpret_cast<const float4 *>(ts + (b * 8 + f) * 16 + 4 * g);
+                            const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+                            #pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int pr = acc[b][r] - sqrun;   // |pr| <= 127 G
+                                facc[b][r] += (double)pr * (double)sv[r];
+                                itot[b][r] += pr;
+                            }
+                            acc[b] = v4i_sk{0, 0, 0, 0};
+                        }
+                        sqrun = 0;
+                    }
+                }
             }
         };
-        // ---- stage the segment's q: (token m, chunk c) items, two per thread and pass; block
-        // D of a chunk (16 values) transposed as the B operand of the blocks' MFMAs.  The
-        // first pass's q loads go out before the segment's first weight loads, so that the
-        // staging waits for its own (L2-resident) data only, not for the weights.
+        // ---- stage the segment's q: (token m, chunk c) items, several per thread and
+        // pass; block D of a chunk (16 values) transposed as the B operand of the blocks'
+        // MFMAs (GRP: and each item's sum of q kept per chunk).  The first pass's q loads
+        // go out before the segment's first weight loads, so that the staging waits for
+        // its own (L2-resident) data only, not for the weights.
         auto stage_item = [&](int idx, const uint4 (&v)[4]) {
             const int m = idx / sc, c = idx - m * sc;
             int sm = 0;
@@ -552,6 +608,7 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
                 sm = dot4(v[j].z, 0x01010101u, sm);
                 sm = dot4(v[j].w, 0x01010101u, sm);
             }
+            if (GRP) sqc[m * seg_chunks + c] = sm;
             if (sm != 0) atomicAdd(&sq[m], sm);
         };
         const int items = M * sc, nth = (int)blockDim.x;
@@ -617,29 +674,50 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
         }
     }
 
-    // ---- epilogue: acc (16 x 16 layout: lane -> token l16, register r -> row 4g + r of
-    // the block) less sum q into LDS as [token][row of the workgroup], then whole row
-    // segments per token, rescaled
+    // ---- epilogue.  Plain: acc (16 x 16 layout: lane -> token l16, register r -> row
+    // 4g + r of the block) less sum q into LDS as [token][row of the workgroup], then whole
+    // row segments per token, rescaled.  GRP: the lane forms y itself, y = fp32((sum_g
+    // (acc_g - sum_g q) s_g) s_x / 127 (+ bias)), and stages its bits beside the exact
+    // integer sums.
     __syncthreads();   // every wavefront done with the staged q
     // rows of kSk2YStride ints: the 16 tokens of one row fall on 16 different banks
     int *ys = reinterpret_cast<int *>(qs);
+    int *ys2 = ys + 16 * kSk2YStride;   // GRP: the integer sums
     if (l16 < M) {
         const int sqm = sq[l16];
         #pragma unroll
         for (int b = 0; b < kSk2RB; ++b)
             #pragma unroll
-            for (int r = 0; r < 4; ++r) ys[l16 * kSk2YStride + rb0[b] - row_base + P * (4 * g + r)] = acc[b][r] - sqm;
+            for (int r = 0; r < 4; ++r) {
+                const int rl = rb0[b] - row_base + P * (4 * g + r);
+                if (GRP) {
+                    const int row = min(row_base + rl, N - 1);
+                    double yv = (facc[b][r] * (double)d.s_x[l16]) / 127.0;
+                    if (d.bias) yv += (double)d.bias[row];
+                    ys[l16 * kSk2YStride + rl] = (int)__float_as_uint((float)yv);
+                    ys2[l16 * kSk2YStride + rl] = itot[b][r];
+                } else {
+                    ys[l16 * kSk2YStride + rl] = acc[b][r] - sqm;
+                }
+            }
     }
-    if (tid < M) cms[tid] = rescale_factor(d.s_x[tid], *d.s_w);
+    if (!GRP && tid < M) cms[tid] = rescale_factor(d.s_x[tid], *d.s_w);
     __syncthreads();
     const OutSpec out = d.out();
     for (int idx = tid; idx < M * kSk2Rows; idx += blockDim.x) {
         const int m = idx / kSk2Rows, rr = idx - m * kSk2Rows, row = row_base + rr;
         if (row < N) {
             const size_t o2 = (size_t)m * N + row;
-            const int v = ys[m * kSk2YStride + rr];
-            put_y(out, o2, row, v, col_factor(out, d.s_w, row, d.s_x[m], cms[m]));
-            if (d.acc) d.acc[o2] = v;
+            if (GRP) {
+                const float yf = __uint_as_float((uint32_t)ys[m * kSk2YStride + rr]);
+                if (out.bf16) reinterpret_cast<uint16_t *>(out.y)[o2] = bf16_rne(yf);
+                else reinterpret_cast<float *>(out.y)[o2] = yf;
+                if (d.acc) d.acc[o2] = ys2[m * kSk2YStride + rr];
+            } else {
+                const int v = ys[m * kSk2YStride + rr];
+                put_y(out, o2, row, v, col_factor(out, d.s_w, row, d.s_x[m], cms[m]));
+                if (d.acc) d.acc[o2] = v;
+            }
         }
     }
 }
@@ -660,15 +738,22 @@ __global__ __launch_bounds__(64 * kGroupedSkNW) void skinny_grouped_kernel(const
                                                          (int)e.local * kGroupedSkNW * 16 * kGroupedSkRG, qs, sq);
 }
 
-__global__ __launch_bounds__(64 * kSk2NW) __attribute__((amdgpu_waves_per_eu(SK2_WAVES))) void skinny2_grouped_kernel(const uint8_t *__restrict__ plan) {
+// GRP: the plan has problems with group-wise weight scales, which take the group-wise
+// tile; plans without them use the kernel without it.
+template <bool GRP>
+__global__ __launch_bounds__(64 * kSk2NW) __attribute__((amdgpu_waves_per_eu(GRP ? 3 : SK2_WAVES))) void skinny2_grouped_kernel(const uint8_t *__restrict__ plan) {
     extern __shared__ __attribute__((aligned(16))) uint32_t qs[];   // staged q of one segment; results
     __shared__ __attribute__((aligned(16))) uint32_t tb[kSk2NW * 16 * kSk2TDw];
+    __shared__ __attribute__((aligned(16))) float tsc[GRP ? kSk2NW * kSk2RB * 8 * 16 : 4];
     __shared__ int sq[16];
     __shared__ double cms[16];
     const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
     const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[blockIdx.x];
     const LinearDescDev d = reinterpret_cast<const LinearDescDev *>(plan + h->desc_offset)[e.desc];
-    skinny2_tile<true>(d, (int)e.local * kSk2Rows, qs, tb, sq, cms);
+    if (GRP && d.w_group > 0 && d.w_group < d.K)
+        skinny2_tile<true, true>(d, (int)e.local * kSk2Rows, qs, tb, tsc, sq, cms);
+    else
+        skinny2_tile<true, false>(d, (int)e.local * kSk2Rows, qs, tb, tsc, sq, cms);
 }
 
 static_assert(kSk2Rows == kGroupedSkNW * 16 * kGroupedSkRG, "both grouped variants take 256-row blocks");
@@ -683,7 +768,7 @@ __global__ __launch_bounds__(64 * kSk2NW) __attribute__((amdgpu_waves_per_eu(SK2
     __shared__ int sq[16];
     __shared__ double cms[16];
     const LinearDescDev d{q, s_x, packed, s_w, out.y, acc, M, N, K, out.w_group, out.bias, out.bf16, 0};
-    skinny2_tile<true>(d, (int)blockIdx.x * kSk2Rows, qs, tb, sq, cms);
+    skinny2_tile<true, false>(d, (int)blockIdx.x * kSk2Rows, qs, tb, nullptr, sq, cms);
 }
 
 // At least 2 workgroups per CU of a 256-CU part, up to 16 tokens, whole 64-weight
@@ -706,15 +791,19 @@ static hipError_t launch_skinny2_single(const int8_t *q, const float *s_x, const
 }
 
 uint32_t skinny_grouped_rows_per_block() { return kGroupedSkNW * 16 * kGroupedSkRG; }
-uint32_t skinny_grouped_lds_bytes(int64_t M, int64_t K) {
-    const uint32_t stage = (uint32_t)(sk_segment_chunks((int)(K / 64), (int)M) * sk_chunk_dw((int)M) * 4);
-    // the line-granular variant also keeps the results of its 256 rows there (16 tokens)
-    return BITNET_SKINNY_V2 ? std::max<uint32_t>(stage, 16u * kSk2YStride * 4u) : stage;
+uint32_t skinny_grouped_lds_bytes(int64_t M, int64_t K, bool grp) {
+    const int seg = sk_segment_chunks((int)(K / 64), (int)M);
+    // group-wise problems also keep each (token, chunk) sum of q after the staged chunks
+    const uint32_t stage = (uint32_t)(seg * sk_chunk_dw((int)M) * 4 + (grp ? (int)M * seg * 4 : 0));
+    // the line-granular variant also keeps the results of its 256 rows there (16 tokens;
+    // group-wise: the fp32 y and the integer sums)
+    return BITNET_SKINNY_V2 ? std::max<uint32_t>(stage, (grp ? 2u : 1u) * 16u * kSk2YStride * 4u) : stage;
 }
 
-hipError_t launch_skinny_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st) {
+hipError_t launch_skinny_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, bool grp, hipStream_t st) {
     const uint8_t *p = reinterpret_cast<const uint8_t *>(plan_dev);
-    if (BITNET_SKINNY_V2) skinny2_grouped_kernel<<<dim3(blocks), dim3(64 * kSk2NW), lds_bytes, st>>>(p);
+    if (grp) skinny2_grouped_kernel<true><<<dim3(blocks), dim3(64 * kSk2NW), lds_bytes, st>>>(p);
+    else if (BITNET_SKINNY_V2) skinny2_grouped_kernel<false><<<dim3(blocks), dim3(64 * kSk2NW), lds_bytes, st>>>(p);
     else skinny_grouped_kernel<<<dim3(blocks), dim3(64 * kGroupedSkNW), lds_bytes, st>>>(p);
     return hipGetLastError();
 }

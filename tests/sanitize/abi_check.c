@@ -116,9 +116,9 @@ static void linear_plans(void) {
     plan = plan_linear(d, ND, &st);
     CHECK(st == BITNET_OK && hdr_word(plan, 7) == 1);
     free(plan);
-    for (int i = 0; i < ND; ++i) d[i].w_group = (i % 3) ? 0 : 64;   /* group-wise, several tokens */
+    for (int i = 0; i < ND; ++i) d[i].w_group = (i % 3) ? 0 : 64;   /* group-wise, several tokens: MFMA decode */
     plan = plan_linear(d, ND, &st);
-    CHECK(st == BITNET_OK && hdr_word(plan, 7) == 3);
+    CHECK(st == BITNET_OK && hdr_word(plan, 7) == 4);
     free(plan);
     for (int i = 0; i < ND; ++i) d[i].M = 1;                /* group-wise, one token each */
     plan = plan_linear(d, ND, &st);

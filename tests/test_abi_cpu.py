@@ -384,13 +384,15 @@ def test_linear_plan_weight_groups(L):
     buf = ctypes.create_string_buffer(nb)
     assert L.bitnet_grouped_plan_linear(arr, 2, buf, nb) == OK
     hdr = (ctypes.c_uint32 * 8).from_buffer_copy(buf.raw[:32])
-    assert hdr[7] == 3                          # GEMV with the group-wise path, 4 tokens per workgroup
-    R = hdr[5]                                  # GEMV blocks: one per R rows and 4 tokens
-    assert R > 0 and hdr[3] == -(-300 // R) + -(-200 // R)
-    one = (D * 1)(D(a16, a16, a16, a16, a16, 0, 1, 200, 2560, 128))    # every M = 1: one token each
-    assert L.bitnet_grouped_plan_linear(one, 1, buf, nb) == OK
+    assert hdr[7] == 4                          # MFMA decode kernel with its group-wise path
+    R = hdr[5]                                  # one block per R rows, all tokens at once
+    assert R == 256 and hdr[3] == -(-300 // R) + -(-200 // R)
+    one = (D * 1)(D(a16, a16, a16, a16, a16, 0, 1, 200, 2560, 128))    # every M = 1: the GEMV, one token each
+    nb1 = L.bitnet_grouped_plan_bytes(1, 1, one)
+    assert L.bitnet_grouped_plan_linear(one, 1, buf, nb1) == OK
     hdr = (ctypes.c_uint32 * 8).from_buffer_copy(buf.raw[:32])
-    assert hdr[7] == 2 and hdr[3] == -(-200 // R)
+    R1 = hdr[5]
+    assert hdr[7] == 2 and R1 > 0 and hdr[3] == -(-200 // R1)
     for w_group in (96, 32, -64):               # not dividing K / not a multiple of 64
         bad = (D * 1)(D(a16, a16, a16, a16, a16, 0, 1, 300, 2560, w_group))
         assert L.bitnet_grouped_plan_linear(bad, 1, buf, nb) == SHAPE
