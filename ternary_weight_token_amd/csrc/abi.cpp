@@ -445,7 +445,7 @@ BITNET_API int bitnet_grouped_plan_linear(const bitnet_linear_desc *descs, int c
     if (variant == kVariantMfma || variant == kVariantMfmaGroups) {
         h->rows_per_block = skinny_grouped_rows_per_block();
         for (int i = 0; i < count; ++i)
-            h->lds_bytes = std::max(h->lds_bytes, skinny_grouped_lds_bytes(descs[i].M, descs[i].K, desc_groups(descs[i])));
+            h->lds_bytes = std::max(h->lds_bytes, skinny_grouped_lds_bytes(descs[i].M, descs[i].K, variant == kVariantMfmaGroups));
     } else {
         h->rows_per_block = gemv_grouped_rows_per_block();
         // each descriptor is staged by the path its own scales take (group-wise

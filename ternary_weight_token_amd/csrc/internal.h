@@ -38,7 +38,8 @@ constexpr uint32_t kVariantGemv = 0, kVariantMfma = 1;
 constexpr uint32_t kVariantGemvGroups = 2, kVariantGemvGroupsMT = 3;
 constexpr int kGemvGroupsMT = 4;
 // ... and the MFMA decode kernel with its group-wise path, for plans with such weights
-// and any M > 1 (every problem once over its weights, all tokens at once).
+// and any M > 1 (every problem once over its weights, all tokens at once; the plan's
+// other problems take that path too, with one group of all of K).
 constexpr uint32_t kVariantMfmaGroups = 4;
 // Fused plan variants: a mask of what its problems use beyond the plain path (an
 // RMSNorm; fp32 input rows or gate / up pairs, the two ends of SwiGLU); each mask

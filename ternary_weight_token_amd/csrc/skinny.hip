@@ -273,8 +273,11 @@ __host__ __device__ __forceinline__ int sk_chunk_dw(int M) { return 16 * M + 4; 
 
 // Segment length in 64-weight chunks for M tokens: all of K if its staged q fits the
 // budget, else the fewest equal segments, each a multiple of 8 chunks (one step).
-__host__ __device__ __forceinline__ int sk_segment_chunks(int C, int M) {
-    const int max_seg = (kSkLdsBudget / (4 * sk_chunk_dw(M))) & ~7;
+// grp: the group-wise path of the line-granular kernel, which keeps less staged q
+// (kSkLdsBudgetGrp) so that two of its workgroups fit a CU beside their larger static LDS.
+constexpr int kSkLdsBudgetGrp = 48 * 1024;
+__host__ __device__ __forceinline__ int sk_segment_chunks(int C, int M, bool grp = false) {
+    const int max_seg = ((grp ? kSkLdsBudgetGrp : kSkLdsBudget) / (4 * sk_chunk_dw(M))) & ~7;
     if (C <= max_seg) return C;
     const int nseg = (C + max_seg - 1) / max_seg;
     return (((C + nseg - 1) / nseg) + 7) & ~7;
@@ -482,8 +485,11 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
     // pieces (16 bytes) between the start of the line and the rows' first byte
     const int off = (int)(((uintptr_t)(d.packed + (size_t)rb0[0] * KB) & 127) >> 4);
     const uint8_t *prow[kSk2RB][2];
-    // GRP: chunks per scale group, groups per row
-    const int gc = GRP ? d.w_group >> 6 : 1, ng = GRP ? K / d.w_group : 1;
+    // GRP: chunks per scale group, groups per row.  A problem without group-wise scales
+    // (dg false: one scale per tensor or per output channel) runs the same path with one
+    // group of all of K and its own rescale at the end.
+    const bool dg = GRP && d.w_group > 0 && d.w_group < K;
+    const int gc = dg ? d.w_group >> 6 : C, ng = dg ? K / d.w_group : 1;
     #pragma unroll
     for (int b = 0; b < kSk2RB; ++b)
         #pragma unroll
@@ -508,7 +514,7 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
     uint32_t *tw = tb + wave * 16 * kSk2TDw;
     float *ts = GRP ? tsc + wave * kSk2RB * 8 * 16 : nullptr;   // GRP: [block][piece][row] scales of a step
     static_assert(kSk2Items * kSk2NW * 64 * 64 >= kSkLdsBudget, "one staging pass covers a segment");
-    const int seg_chunks = sk_segment_chunks(C, M);
+    const int seg_chunks = sk_segment_chunks(C, M, GRP);
     const int cdw = sk_chunk_dw(M);
     int *sqc = reinterpret_cast<int *>(qs + seg_chunks * cdw);   // GRP: [token][chunk] sums of q
 
@@ -528,7 +534,7 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
                 for (int h = 0; h < 2; ++h) {
                     w.w[b][h] = load_weights<NT>(prow[b][h] + 16 * c);
                     // GRP: the loading lane's row's scale of the chunk's group
-                    if (GRP) w.s[b][h] = d.s_w[(size_t)min(rb0[b] + P * (8 * h + o), N - 1) * ng + grp];
+                    if (GRP) w.s[b][h] = dg ? d.s_w[(size_t)min(rb0[b] + P * (8 * h + o), N - 1) * ng + grp] : 1.0f;
                 }
         };
         auto consume = [&](const WBuf &w, int t) {
@@ -682,7 +688,7 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
     __syncthreads();   // every wavefront done with the staged q
     // rows of kSk2YStride ints: the 16 tokens of one row fall on 16 different banks
     int *ys = reinterpret_cast<int *>(qs);
-    int *ys2 = ys + 16 * kSk2YStride;   // GRP: the integer sums
+    int *ys2 = ys + 16 * kSk2YStride;   // dg: the integer sums
     if (l16 < M) {
         const int sqm = sq[l16];
         #pragma unroll
@@ -690,25 +696,25 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
             #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int rl = rb0[b] - row_base + P * (4 * g + r);
-                if (GRP) {
+                if (dg) {
                     const int row = min(row_base + rl, N - 1);
                     double yv = (facc[b][r] * (double)d.s_x[l16]) / 127.0;
                     if (d.bias) yv += (double)d.bias[row];
                     ys[l16 * kSk2YStride + rl] = (int)__float_as_uint((float)yv);
                     ys2[l16 * kSk2YStride + rl] = itot[b][r];
                 } else {
-                    ys[l16 * kSk2YStride + rl] = acc[b][r] - sqm;
+                    ys[l16 * kSk2YStride + rl] = GRP ? itot[b][r] : acc[b][r] - sqm;
                 }
             }
     }
-    if (!GRP && tid < M) cms[tid] = rescale_factor(d.s_x[tid], *d.s_w);
+    if (!dg && tid < M) cms[tid] = rescale_factor(d.s_x[tid], *d.s_w);
     __syncthreads();
     const OutSpec out = d.out();
     for (int idx = tid; idx < M * kSk2Rows; idx += blockDim.x) {
         const int m = idx / kSk2Rows, rr = idx - m * kSk2Rows, row = row_base + rr;
         if (row < N) {
             const size_t o2 = (size_t)m * N + row;
-            if (GRP) {
+            if (dg) {
                 const float yf = __uint_as_float((uint32_t)ys[m * kSk2YStride + rr]);
                 if (out.bf16) reinterpret_cast<uint16_t *>(out.y)[o2] = bf16_rne(yf);
                 else reinterpret_cast<float *>(out.y)[o2] = yf;
@@ -741,7 +747,7 @@ __global__ __launch_bounds__(64 * kGroupedSkNW) void skinny_grouped_kernel(const
 // GRP: the plan has problems with group-wise weight scales, which take the group-wise
 // tile; plans without them use the kernel without it.
 template <bool GRP>
-__global__ __launch_bounds__(64 * kSk2NW) __attribute__((amdgpu_waves_per_eu(GRP ? 3 : SK2_WAVES))) void skinny2_grouped_kernel(const uint8_t *__restrict__ plan) {
+__global__ __launch_bounds__(64 * kSk2NW) __attribute__((amdgpu_waves_per_eu(SK2_WAVES))) void skinny2_grouped_kernel(const uint8_t *__restrict__ plan) {
     extern __shared__ __attribute__((aligned(16))) uint32_t qs[];   // staged q of one segment; results
     __shared__ __attribute__((aligned(16))) uint32_t tb[kSk2NW * 16 * kSk2TDw];
     __shared__ __attribute__((aligned(16))) float tsc[GRP ? kSk2NW * kSk2RB * 8 * 16 : 4];
@@ -750,10 +756,7 @@ __global__ __launch_bounds__(64 * kSk2NW) __attribute__((amdgpu_waves_per_eu(GRP
     const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
     const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[blockIdx.x];
     const LinearDescDev d = reinterpret_cast<const LinearDescDev *>(plan + h->desc_offset)[e.desc];
-    if (GRP && d.w_group > 0 && d.w_group < d.K)
-        skinny2_tile<true, true>(d, (int)e.local * kSk2Rows, qs, tb, tsc, sq, cms);
-    else
-        skinny2_tile<true, false>(d, (int)e.local * kSk2Rows, qs, tb, tsc, sq, cms);
+    skinny2_tile<true, GRP>(d, (int)e.local * kSk2Rows, qs, tb, tsc, sq, cms);
 }
 
 static_assert(kSk2Rows == kGroupedSkNW * 16 * kGroupedSkRG, "both grouped variants take 256-row blocks");
@@ -792,7 +795,7 @@ static hipError_t launch_skinny2_single(const int8_t *q, const float *s_x, const
 
 uint32_t skinny_grouped_rows_per_block() { return kGroupedSkNW * 16 * kGroupedSkRG; }
 uint32_t skinny_grouped_lds_bytes(int64_t M, int64_t K, bool grp) {
-    const int seg = sk_segment_chunks((int)(K / 64), (int)M);
+    const int seg = sk_segment_chunks((int)(K / 64), (int)M, grp);
     // group-wise problems also keep each (token, chunk) sum of q after the staged chunks
     const uint32_t stage = (uint32_t)(seg * sk_chunk_dw((int)M) * 4 + (grp ? (int)M * seg * 4 : 0));
     // the line-granular variant also keeps the results of its 256 rows there (16 tokens;
