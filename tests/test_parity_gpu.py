@@ -1309,3 +1309,34 @@ def test_linear_many_rows_line_granular(M, N, K):
     x, q, s = quantized_inputs(key, M, K)
     packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
     check_linear(q, s, packed, np.float32(0.0043), kernels=(0, 4))
+
+
+@pytest.mark.parametrize("M", [2, 7, 16])
+def test_grouped_mfma_decode_groups_across_windows(M):
+    """Group-wise scales on the line-granular MFMA decode kernel with groups longer than a
+    step's 8 chunks (G = 640 and 1728: 10 and 27 chunks), K long enough for several staged
+    segments (K = 30720, G = 3840), rows starting mid-line (K = 6912), a bias on some
+    problems: acc bit for bit, y within the group-wise bound."""
+    shapes = [(300, 2560, 640, False), (257, 6912, 1728, True), (70, 30720, 3840, False), (129, 6912, 64, True)]
+    probs, refs = [], []
+    for i, (N, K, G, with_bias) in enumerate(shapes):
+        key = synth.stream_key(333, M, i)
+        x, q, s = quantized_inputs(key, M, K)
+        w = synth.latent_weights(synth.stream_key(key, 1), N, K, 0.02).numpy()
+        w[:, :G] *= 3.0
+        packed, s_w = oracle.pack_grouped(w, G, 1e-5)
+        bias = _bias(key, N) if with_bias else None
+        acc_ref, y_ref = oracle.linear_grouped(q, s, packed, s_w, G, bias)
+        refs.append((acc_ref, y_ref, _grouped_bound(q, s, packed, s_w, G, K)))
+        y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+        acc = torch.full((M, N), -1, dtype=torch.int32, device=DEV)
+        probs.append((torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV), torch.from_numpy(packed).to(DEV),
+                      torch.from_numpy(s_w).to(DEV), y, acc, G,
+                      None if bias is None else torch.from_numpy(bias).to(DEV)))
+    plan = tw.bitnet_grouped_plan_linear(probs)
+    for _ in range(2):
+        plan.launch()
+        torch.cuda.synchronize()
+        for i, ((acc_ref, y_ref, slack), pr) in enumerate(zip(refs, probs)):
+            assert np.array_equal(pr[5].cpu().numpy(), acc_ref), i
+            assert_y_within(pr[4].cpu().numpy(), y_ref, REL, slack)
