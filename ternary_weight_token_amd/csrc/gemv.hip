@@ -46,6 +46,9 @@
 #ifndef BITNET_FUSED_PERSIST
 #define BITNET_FUSED_PERSIST 0   // > 0: the fused grouped launch uses at most this many workgroups
 #endif
+#ifndef BITNET_GEMV_WG_STORE
+#define BITNET_GEMV_WG_STORE 1     // one token: wavefront 0 stores the outputs of the whole workgroup
+#endif
 #ifndef BITNET_GEMV_PREISSUE
 #define BITNET_GEMV_PREISSUE 1   // weight steps issued before the q staging (1 or 2)
 #endif
@@ -441,6 +444,9 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s
         for (int m = 0; m < MT; ++m) { hi[g][m] = 0; lo[g][m] = 0u; facc[g][m] = 0.0; }
     }
     if (tid < MT) sq[tid] = 0;
+    // the per-tensor weight scale, read before the weight stream so that its latency
+    // is not paid after the last chunk
+    const float sw = *(const __attribute__((address_space(4))) float *)s_w;   // read-only here: scalar load
     // chunk offset of this lane's rows within their 128-byte line (the same for all
     // RG groups: their rows differ by multiples of 8)
     const int line_off = (int)((((uint32_t)(row0 + rs) & 7u) * ((uint32_t)(KB >> 4) & 7u)) & 7u);
@@ -596,7 +602,6 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s
             acc[g][m] = octet_sum(DOT8 ? 16 * hi[g][m] + (int)lo[g][m] : hi[g][m]);
     }
 
-    const float sw = *s_w;
     if (PAIR) {
         constexpr int kHalfRows = (NW / 2) * 8 * RG;
         const double cm = rescale_factor(s_x[m0], sw);
@@ -608,6 +613,30 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s
         __syncthreads();
         const int r = row_base + tid;
         if (tid < kHalfRows && r < N) store_y(out, (size_t)m0 * N + r, (double)swiglu_value(ypair[tid], ypair[kHalfRows + tid]));
+        return;
+    }
+    if (BITNET_GEMV_WG_STORE && MT == 1 && kslices == 1) {
+        // one token: the row sums of all wavefronts meet in red (LDS) and wavefront 0
+        // stores the workgroup's rows, consecutive lanes on consecutive rows; the other
+        // wavefronts end without stores of their own to wait for
+        if (l8 == 0) {
+            #pragma unroll
+            for (int g = 0; g < RG; ++g) red[wave * 8 * RG + 8 * g + rs] = acc[g][0];
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (wave != 0 || mcount <= 0) return;
+        const double cm = rescale_factor(s_x[m0], sw);
+        #pragma unroll
+        for (int i = 0; i < (NW * 8 * RG + 63) / 64; ++i) {
+            const int j = 64 * i + lane;
+            const int r = row_base + j;
+            if (j < NW * 8 * RG && r < N) {
+                const size_t o = (size_t)m0 * N + r;
+                const int a = red[j] - sq[0];
+                put_y(out, o, r, a, col_factor(out, s_w, r, s_x[m0], cm));
+                if (acc_out) acc_out[o] = a;
+            }
+        }
         return;
     }
     if (kslices == 1) {
