@@ -50,7 +50,10 @@
 #define BITNET_GEMV_WG_STORE 1     // one token: wavefront 0 stores the outputs of the whole workgroup
 #endif
 #ifndef BITNET_GEMV_PREISSUE
-#define BITNET_GEMV_PREISSUE 1   // weight steps issued before the q staging (1 or 2)
+#define BITNET_GEMV_PREISSUE 1   // weight steps issued before the q staging (1 or 2), GEMV launches
+#endif
+#ifndef BITNET_FUSED_PREISSUE
+#define BITNET_FUSED_PREISSUE 2  // the same for the fused grouped launch
 #endif
 
 namespace bitnet {
@@ -403,7 +406,8 @@ struct StageQuantizeF32 {
 // 4 NW RG) of gate, the others the same rows of up; the epilogue meets the two fp32
 // outputs of each row in LDS (ypair, 8 NW RG floats) and writes
 // a = fp32(silu(y_gate) y_up) (device_common.h, swiglu_value) to out.y.
-template <int MT, int RG, bool DOT8, bool NT, int NW, class Stage, bool GRP = false, bool PAIR = false>
+template <int MT, int RG, bool DOT8, bool NT, int NW, class Stage, bool GRP = false, bool PAIR = false,
+          int PI = BITNET_GEMV_PREISSUE>
 __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s_x,
                                               const uint8_t *__restrict__ packed,
                                               const float *__restrict__ s_w, int M, int N, int K,
@@ -523,7 +527,7 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s
         // for the stager's data also wait for these loads.
         const typename Stage::Pre pre = stage.load(s0, sc);
         issue(bufA, 0);
-        if (BITNET_GEMV_PREISSUE > 1) issue(bufB, 1);
+        if (PI > 1) issue(bufB, 1);
 
         // ---- stage the segment of the M tile of q, rearranged, and its row sums
         __syncthreads();   // previous segment's LDS reads done; sq initialised
@@ -535,7 +539,7 @@ __device__ __forceinline__ void gemv_lds_tile(const Stage &stage, const float *s
         // peeled (a uniform branch outside the loop).
         if (T > 0) {
             const int T2 = (T + 1) & ~1;
-            if (BITNET_GEMV_PREISSUE > 1) {
+            if (PI > 1) {
                 // steps t and t + 1 are in flight at the top of every iteration
                 int t = 0;
                 for (; t + 3 < T; t += 2) {
@@ -754,17 +758,20 @@ __global__ __launch_bounds__(256) void gemv_grouped_kernel(const uint8_t *__rest
 // row block 0 also writes q and s_x out when the descriptor asks for them.
 constexpr int kFusedNW = BITNET_FUSED_NW;
 constexpr int kFusedRG = BITNET_FUSED_RG;
+constexpr int kFusedPI = BITNET_FUSED_PREISSUE;
 
 // PRO: the mask of paths the plan's problems use (kFusedProNorm: an RMSNorm;
 // kFusedProSwiglu: fp32 input rows and gate / up pairs with the SwiGLU epilogue);
 // each problem takes the stager and epilogue its descriptor asks for, and a kernel
-// holds only the paths of its mask (fewer registers without them).  Waves per SIMD:
-// at least 6 for the plain kernel (80 registers, no spills; 0.3 us faster per decode
-// step than at 5), at least 4 for the others, which would otherwise settle just
-// above 128 registers.  (The output spec is built in each call, not kept in a named
-// local, which costs registers here.)
+// holds only the paths of its mask (fewer registers without them).  Every wavefront
+// keeps two steps of weight loads in flight, the first two issued before the q
+// staging.  Waves per SIMD: at least 5 for the plain kernel (no spills; fewer bytes in
+// flight per CU than at 6 with one step pre-issued, so the x row waits less behind
+// the weight stream: 82.0 -> 80.7 us per decode step), at least 4 for the others.
+// (The output spec is built in each call, not kept in a named local, which costs
+// registers here.)
 template <int PRO>
-__global__ __launch_bounds__(64 * kFusedNW) __attribute__((amdgpu_waves_per_eu(PRO == 0 ? 6 : 4)))
+__global__ __launch_bounds__(64 * kFusedNW) __attribute__((amdgpu_waves_per_eu(PRO == 0 ? 5 : 4)))
 void gemv_fused_grouped_kernel(const uint8_t *__restrict__ plan) {
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
     __shared__ int sq[1];
@@ -787,11 +794,11 @@ void gemv_fused_grouped_kernel(const uint8_t *__restrict__ plan) {
         auto tile = [&](const auto &stage, bool as_pair) {
             using S = std::decay_t<decltype(stage)>;
             if ((PRO & kFusedProSwiglu) && as_pair)
-                gemv_lds_tile<1, kFusedRG, D8, NTL, kFusedNW, S, false, true>(
+                gemv_lds_tile<1, kFusedRG, D8, NTL, kFusedNW, S, false, true, kFusedPI>(
                     stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K, OutSpec{d.y, nullptr, d.bf16, 0}, nullptr, row_base, 0, 1,
                     d.K >> 6, dyn, sq, red, nullptr, d.packed2, d.s_w2, ypair);
             else
-                gemv_lds_tile<1, kFusedRG, D8, NTL, kFusedNW>(stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K,
+                gemv_lds_tile<1, kFusedRG, D8, NTL, kFusedNW, S, false, false, kFusedPI>(stage, &s_lds, d.packed, d.s_w, 1, d.N, d.K,
                                                                  OutSpec{d.y, d.bias, d.bf16, 0}, d.acc, row_base, 0, 1,
                                                                  d.K >> 6, dyn, sq, red);
         };
