@@ -511,6 +511,12 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
     }
     if (tid < 16) sq[tid] = 0;
     const int tokc = min(l16, M - 1);   // tokens past M repeat the last one (outputs dropped)
+    // plain kernel: the epilogue's scales (the lane's token's s_x; the per-tensor s_w
+    // through the scalar path), read before the weight stream so that their latency is
+    // not paid after the last step (1.9 us per 8-token decode step).  The group-wise
+    // kernel reads them at the end: holding them costs it spills.
+    const float sx_early = GRP ? 0.0f : d.s_x[tokc];
+    const float sw_early = GRP ? 0.0f : *(const __attribute__((address_space(4))) float *)d.s_w;
     uint32_t *tw = tb + wave * 16 * kSk2TDw;
     float *ts = GRP ? tsc + wave * kSk2RB * 8 * 16 : nullptr;   // GRP: [block][piece][row] scales of a step
     static_assert(kSk2Items * kSk2NW * 64 * 64 >= kSkLdsBudget, "one staging pass covers a segment");
@@ -707,7 +713,11 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
                 }
             }
     }
-    if (!dg && tid < M) cms[tid] = rescale_factor(d.s_x[tid], *d.s_w);
+    if (!dg && tid < M) {
+        const float sxm = GRP ? d.s_x[tid] : sx_early;   // tid < 16: token tid
+        cms[tid] = rescale_factor(sxm, GRP ? *d.s_w : sw_early);
+        cms[16 + tid] = (double)sxm;
+    }
     __syncthreads();
     const OutSpec out = d.out();
     for (int idx = tid; idx < M * kSk2Rows; idx += blockDim.x) {
@@ -721,7 +731,7 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
                 if (d.acc) d.acc[o2] = ys2[m * kSk2YStride + rr];
             } else {
                 const int v = ys[m * kSk2YStride + rr];
-                put_y(out, o2, row, v, col_factor(out, d.s_w, row, d.s_x[m], cms[m]));
+                put_y(out, o2, row, v, col_factor(out, d.s_w, row, (float)cms[16 + m], cms[m]));
                 if (d.acc) d.acc[o2] = v;
             }
         }
@@ -752,7 +762,7 @@ __global__ __launch_bounds__(64 * kSk2NW) __attribute__((amdgpu_waves_per_eu(SK2
     __shared__ __attribute__((aligned(16))) uint32_t tb[kSk2NW * 16 * kSk2TDw];
     __shared__ __attribute__((aligned(16))) float tsc[GRP ? kSk2NW * kSk2RB * 8 * 16 : 4];
     __shared__ int sq[16];
-    __shared__ double cms[16];
+    __shared__ double cms[32];   // per token: c_m, then s_x
     const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
     const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[blockIdx.x];
     const LinearDescDev d = reinterpret_cast<const LinearDescDev *>(plan + h->desc_offset)[e.desc];
@@ -769,7 +779,7 @@ __global__ __launch_bounds__(64 * kSk2NW) __attribute__((amdgpu_waves_per_eu(SK2
     extern __shared__ __attribute__((aligned(16))) uint32_t qs[];
     __shared__ __attribute__((aligned(16))) uint32_t tb[kSk2NW * 16 * kSk2TDw];
     __shared__ int sq[16];
-    __shared__ double cms[16];
+    __shared__ double cms[32];   // per token: c_m, then s_x
     const LinearDescDev d{q, s_x, packed, s_w, out.y, acc, M, N, K, out.w_group, out.bias, out.bf16, 0};
     skinny2_tile<true, false>(d, (int)blockIdx.x * kSk2Rows, qs, tb, nullptr, sq, cms);
 }
