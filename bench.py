@@ -716,8 +716,8 @@ def main() -> int:
                            "scale_bytes": (4 if v == "per_tensor" else sum(p_[1].numel() * 4 for p_ in gpk))}
                 log(f"decode step two launches, scales {v}: {us:.1f} us")
             sec["decode_step_2p4b_weight_scales"] = dres
-            # the same at 8 tokens (grouped quant + grouped linear): one scale per tensor
-            # runs the MFMA decode kernel; group-128 scales the GEMV (one token per workgroup)
+            # the same at 8 tokens (grouped quant + grouped linear): the line-granular MFMA
+            # decode kernel, with its group-wise path for group-128 scales
             xs8 = [W.decode_step_activations(l, dev, 8) for l in range(30)]
             qs8 = [[torch.empty((8, x.shape[1]), dtype=torch.int8, device=dev) for x in xl] for xl in xs8]
             sx8 = [[torch.empty(8, dtype=torch.float32, device=dev) for _ in xl] for xl in xs8]
@@ -730,10 +730,7 @@ def main() -> int:
                     ("group128", [(qs8[m.layer][m.slot], sx8[m.layer][m.slot], gpk[i][0], gpk[i][1], ys8[i], None, 128)
                                   for i, m in enumerate(mats)])):
                 lp = tw.bitnet_grouped_plan_linear(plan_probs)
-                for _ in range(10):
-                    qplan8.launch(stream)
-                    lp.launch(stream)
-                torch.cuda.synchronize()
+                settle(torch, lambda: (qplan8.launch(stream), lp.launch(stream)))
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
                 for _ in range(30):
@@ -742,8 +739,9 @@ def main() -> int:
                 b.record(stream)
                 torch.cuda.synchronize()
                 us = a.elapsed_time(b) * 1e3 / 30
-                dres8[v] = {"us": round(us, 1), "weight_GBs": round(weight_bytes / (us * 1e-6) / 1e9, 1),
-                            "kernel": "skinny2_grouped_kernel" if v == "per_tensor" else "gemv_grouped_kernel<true>"}
+                kern = {1: "skinny2_grouped_kernel<false>", 4: "skinny2_grouped_kernel<true>"}.get(
+                    lp.variant, f"gemv_grouped_kernel (plan variant {lp.variant})")
+                dres8[v] = {"us": round(us, 1), "weight_GBs": round(weight_bytes / (us * 1e-6) / 1e9, 1), "kernel": kern}
                 log(f"decode step M=8 two launches, scales {v}: {us:.1f} us")
             sec["decode_step_2p4b_M8_weight_scales"] = dres8
             del gpk, xs8, qs8, sx8, ys8
@@ -759,8 +757,7 @@ def main() -> int:
                 for v, g in (("per_tensor", 0), ("group128", 128)):
                     p_, s_ = tw.pack_weights(w, 1e-5) if g == 0 else tw.pack_weights_grouped(w, g, 1e-5)
                     fn = lambda: tw.bitnet_linear_ex(q, sx, p_, s_, None, y, None, 0, w_group=g)
-                    for _ in range(5):
-                        fn()
+                    settle(torch, fn)
                     a.record(stream)
                     for _ in range(30):
                         fn()

@@ -277,6 +277,12 @@ class GroupedPlan:
         self.kind = kind
         self._refs = refs  # keep the described tensors alive
 
+    @property
+    def variant(self) -> int:
+        """The plan header's kernel variant (the sixth 32-bit field after magic, kind,
+        count, total_blocks, block_threads, rows_per_block and lds_bytes)."""
+        return int.from_bytes(self.host.raw[28:32], "little")
+
     def launch(self, stream=None) -> None:
         f = {"linear": lib().bitnet_linear_grouped, "quant": lib().bitnet_quant_act_grouped,
              "fused": lib().bitnet_linear_fused_grouped}[self.kind]

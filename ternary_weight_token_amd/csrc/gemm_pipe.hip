@@ -344,6 +344,42 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
             }
             return;
         }
+        if (OPT && !GRP && vec && m_base + 64 <= M && n_base + 16 * TN <= N && !out.w_group &&
+            (reinterpret_cast<uintptr_t>(out.bias) & 15) == 0) {
+            // whole block inside with a bias and / or bf16 y (one scale per tensor): the
+            // bias of the lane's 4 columns per block read once, before the stores
+            pv4f b4[TN];
+            #pragma unroll
+            for (int j = 0; j < TN; ++j)
+                b4[j] = out.bias ? *reinterpret_cast<const pv4f *>(out.bias + n_base + 16 * j + 4 * g)
+                                 : pv4f{0.0f, 0.0f, 0.0f, 0.0f};
+            #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = m_base + 16 * i + l16;
+                const double cm = rescale_factor(sxr[i], sw);
+                #pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const size_t o = (size_t)m * N + n_base + 16 * j + 4 * g;
+                    float v[4];
+                    #pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        double yv = (double)acc[i][j][r] * cm;
+                        if (out.bias) yv += (double)b4[j][r];
+                        v[r] = (float)yv;
+                    }
+                    if (out.bf16) {
+                        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out.y) + o) =
+                            make_uint2((uint32_t)bf16_rne(v[0]) | ((uint32_t)bf16_rne(v[1]) << 16),
+                                       (uint32_t)bf16_rne(v[2]) | ((uint32_t)bf16_rne(v[3]) << 16));
+                    } else {
+                        __builtin_nontemporal_store(pv4f{v[0], v[1], v[2], v[3]},
+                                                    reinterpret_cast<pv4f *>(reinterpret_cast<float *>(out.y) + o));
+                    }
+                    if (acc_out) *reinterpret_cast<pv4i *>(acc_out + o) = acc[i][j];
+                }
+            }
+            return;
+        }
         #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = m_base + 16 * i + l16;

@@ -1340,3 +1340,20 @@ def test_grouped_mfma_decode_groups_across_windows(M):
         for i, ((acc_ref, y_ref, slack), pr) in enumerate(zip(refs, probs)):
             assert np.array_equal(pr[5].cpu().numpy(), acc_ref), i
             assert_y_within(pr[4].cpu().numpy(), y_ref, REL, slack)
+
+
+def test_grouped_plan_variant_reported():
+    """GroupedPlan.variant reads the kernel choice from the plan header: the GEMV for
+    one token, the line-granular MFMA decode kernel for several, its group-wise path
+    when a problem has group-wise weight scales (nothing is launched)."""
+    def plan(M, group):
+        K, N = 256, 64
+        q = torch.zeros((M, K), dtype=torch.int8, device=DEV)
+        sx = torch.ones(M, dtype=torch.float32, device=DEV)
+        p = torch.zeros((N, K // 4), dtype=torch.uint8, device=DEV)
+        sw = torch.ones((N, K // group) if group else 1, dtype=torch.float32, device=DEV)
+        y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        return tw.bitnet_grouped_plan_linear([(q, sx, p, sw, y, None, group)])
+    assert plan(1, 0).variant == 0
+    assert plan(8, 0).variant == 1
+    assert plan(8, 128).variant == 4
