@@ -6,8 +6,9 @@
 // Workgroup: 8 wavefronts, two per SIMD, with two roles; output tile 128 x BN,
 // BN = 32 TN weight rows; one k-step is 128 weights.
 //  * 4 producer waves load the step's q rows (whole 128-byte lines) and packed
-//    weight rows (32 bytes each) into registers three steps ahead, and write them
-//    to one of three LDS stages: the q bytes of each 16-byte chunk in the
+//    weight rows (32 bytes each; 64 bytes per pair of steps where K is a multiple
+//    of 256) into registers three steps ahead, and write them to one of three LDS
+//    stages: the q bytes of each 16-byte chunk in the
 //    transposed order k = 4d + i -> byte 4i + d (four byte permutes per dword),
 //    chunks XOR-swizzled so that fragment reads are free of bank conflicts.
 //  * 4 consumer waves (2 x 2), each 64 token rows x 16 TN weight rows: read the
@@ -44,7 +45,7 @@ constexpr int kPipeBM = 128;                    // token rows per tile (2 consum
 constexpr int kPipeKS = 128;                    // weights per k-step (one 128-byte line of q per row)
 constexpr int kPipeA = kPipeBM * kPipeKS;       // q bytes per stage
 constexpr int kPipeBp = 256 * 32;               // packed weight bytes per stage (up to 256 rows)
-constexpr int kPipeStage = kPipeA + kPipeBp;
+constexpr int kPipeBp2 = 256 * 64;              // the same for a pair of steps (PW)
 constexpr int kPipeD = 3;                       // stages
 constexpr int kPipeThreads = 512;
 
@@ -63,7 +64,12 @@ __device__ __forceinline__ int qslot(int r, int c) { return c ^ (r & 7) ^ ((r >>
 // GRP: group-wise weight scales (out.w_group = G < K, G = 64 or a multiple of 128):
 // the int32 products of each group are scaled into fp32 accumulators when the
 // group's last half step is done (see the consumer); OPT is set as well.
-template <int TN, bool OPT, bool GRP = false>
+// PW (K a multiple of 256): the packed weights of a pair of steps (k-steps 2j and
+// 2j + 1) are loaded together as 64-byte row pieces on the even step and staged in
+// its stage; the odd step reads them from there.  A load instruction then covers 16
+// rows in 64-byte pieces instead of 32 rows in 32-byte pieces: half the cache lines
+// per staged byte.
+template <int TN, bool OPT, bool GRP = false, bool PW = false>
 __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s_x, const uint8_t *__restrict__ packed,
     const float *__restrict__ s_w, int M, int N, int K, const OutSpec out, int32_t *__restrict__ acc_out,
@@ -71,7 +77,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
     constexpr int BN = 32 * TN;
     static_assert(BN <= 256, "packed stage holds 256 rows");
     constexpr int D = kPipeD;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[D * kPipeStage];
+    constexpr int Stage = kPipeA + (PW ? kPipeBp2 : kPipeBp);
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[D * Stage];
     // per tile (4 slots, tile index % 4): sum over k of q for each of the 128 rows
     __shared__ int sqbuf[4][kPipeBM];
     // GRP, per stage: sum of q over each half step (64 weights) of the 128 rows, and
@@ -91,11 +98,14 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
     // so that every group's half steps follow one another
     const int gh = GRP ? out.w_group / 64 : 1;    // half steps per group
     const int ng = GRP ? K / out.w_group : 1;
+    // (PW: at an even step, so that the pairs are k-steps 2j, 2j + 1)
     int kr0;
     {
         const int kx = wg & 7, kj = wg >> 3, kjn = (G + 7) >> 3;
         kr0 = (int)(((int64_t)kj * KS / kjn + 3 * kx) % KS);
-        if (GRP && gh > 2) kr0 -= kr0 % (gh / 2);
+        int al = (GRP && gh > 2) ? gh / 2 : 1;
+        if (PW && (al & 1)) al *= 2;
+        kr0 -= kr0 % al;
     }
 
     if (wave >= 4) {
@@ -109,10 +119,14 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
         // packed chunks past the tile's rows: the last waves have none in the
         // second slot (a wave-uniform condition)
         const bool b2 = NB > 1 && 256 + tp < 2 * BN;
+        // PW: piece wc of the pair's 64 bytes of rows wr + 64 h; the rows past the
+        // tile's BN (a multiple of 32) fall on whole waves
+        constexpr int NW = PW ? (BN + 63) / 64 : 2;
+        const int wr = tp >> 2, wc = tp & 3;
         int d_s = 0, d_ti = 0, d_kk = 0;
         int d_kr = kr0;
         const int8_t *arow[4];
-        const uint8_t *brow[2];
+        const uint8_t *brow[NW];
         int bn0 = 0;   // first weight row of the tile being loaded
         auto set_tile = [&](int ti) {
             const int t = wg + ti * G;
@@ -120,19 +134,35 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
             bn0 = n0;
             #pragma unroll
             for (int h = 0; h < 4; ++h) arow[h] = q + (size_t)min(m0 + ar + 32 * h, M - 1) * K + 16 * ac;
-            #pragma unroll
-            for (int h = 0; h < 2; ++h) brow[h] = packed + (size_t)min(n0 + br + 128 * h, N - 1) * KB + 16 * bh;
+            if (PW) {
+                #pragma unroll
+                for (int h = 0; h < NW; ++h) brow[h] = packed + (size_t)min(n0 + wr + 64 * h, N - 1) * KB + 16 * wc;
+            } else {
+                #pragma unroll
+                for (int h = 0; h < 2; ++h) brow[h] = packed + (size_t)min(n0 + br + 128 * h, N - 1) * KB + 16 * bh;
+            }
         };
         set_tile(0);
         // loads of step d_s (clamped to the last step) into register set R
-        pv4u ra[4][4], rb[4][2];
+        // (PW: only the even sets hold weights, the pair's pieces)
+        pv4u ra[4][4], rb[4][NW];
         // GRP: scale entries tp and tp + 256 of the step's 2 x BN (half, row) pairs
         float rsc[GRP ? 4 : 1][2];
         auto issue = [&](int R) {
             #pragma unroll
             for (int h = 0; h < 4; ++h) ra[R][h] = gload(arow[h] + (size_t)d_kr * kPipeKS);
-            rb[R][0] = gload(brow[0] + (size_t)d_kr * (kPipeKS / 4));
-            if (b2) rb[R][1] = gload(brow[1] + (size_t)d_kr * (kPipeKS / 4));
+            if (PW) {
+                // the set's parity is the step's; past the last step d_kr stays at
+                // an odd k-step, whose pair starts one step earlier
+                if ((R & 1) == 0) {
+                    #pragma unroll
+                    for (int h = 0; h < NW; ++h)
+                        if (64 * h + wr < BN) rb[R][h] = gload(brow[h] + (size_t)(d_kr & ~1) * (kPipeKS / 4));
+                }
+            } else {
+                rb[R][0] = gload(brow[0] + (size_t)d_kr * (kPipeKS / 4));
+                if (b2) rb[R][1] = gload(brow[1] + (size_t)d_kr * (kPipeKS / 4));
+            }
             if (GRP) {
                 #pragma unroll
                 for (int e2 = 0; e2 < 2; ++e2) {
@@ -158,7 +188,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
         // register set R (step x) into stage x % 3: q chunks transposed and
         // swizzled, packed halves swapped on rows with bit 3 set
         auto store = [&](int x, int R) {
-            uint8_t *st = smem + (x % D) * kPipeStage;
+            uint8_t *st = smem + (x % D) * Stage;
             #pragma unroll
             for (int h = 0; h < 4; ++h) {
                 const int r = ar + 32 * h;
@@ -179,11 +209,23 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
                 *reinterpret_cast<uint4 *>(st + 1024 * (r >> 3) + 128 * (r & 7) + 16 * qslot(r, ac)) =
                     make_uint4(p0, p1, p2, p3);
             }
-            #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                if (h == 0 || b2) {
-                    const int r = br + 128 * h;
-                    *reinterpret_cast<pv4u *>(st + kPipeA + 32 * r + 16 * (bh ^ ((r >> 3) & 1))) = rb[R][h];
+            if (PW) {
+                // 64 bytes per row, the 16-byte pieces XOR-swizzled by bits 2..3 of
+                // the row: the consumers' 16 rows of a fragment read hit distinct banks
+                if ((R & 1) == 0) {
+                    #pragma unroll
+                    for (int h = 0; h < NW; ++h) {
+                        const int r = wr + 64 * h;
+                        if (r < BN) *reinterpret_cast<pv4u *>(st + kPipeA + 64 * r + 16 * (wc ^ ((r >> 2) & 3))) = rb[R][h];
+                    }
+                }
+            } else {
+                #pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    if (h == 0 || b2) {
+                        const int r = br + 128 * h;
+                        *reinterpret_cast<pv4u *>(st + kPipeA + 32 * r + 16 * (bh ^ ((r >> 3) & 1))) = rb[R][h];
+                    }
                 }
             }
             if (GRP) {
@@ -262,20 +304,28 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
     // lies in 1 KB block r / 8 at position r % 8 = lane % 8, chunk 4u + g at its
     // slot) and the packed dword 4u + g of weight row r (halves swapped on rows with
     // bit 3 set: dword 4u + g sits at (4u + g) ^ 4)
+    // (PW: dword g of piece 2 (x & 1) + u of the pair's 64 bytes, swizzled as stored)
     int aoff[2], boff[2];
     #pragma unroll
     for (int u = 0; u < 2; ++u) {
         aoff[u] = 1024 * (8 * wm + ((lane >> 3) & 1)) + 128 * (lane & 7) + 16 * qslot(lane & 15, 4 * u + g);
         boff[u] = kPipeA + 32 * (16 * TN * wn + l16) + 4 * ((4 * u + g) ^ (4 * ((l16 >> 3) & 1)));
     }
+    const int pwoff = kPipeA + 64 * (16 * TN * wn + l16) + 4 * g, pwsw = (l16 >> 2) & 3;
     pv4i fa[2][4];
     uint32_t fb[2][TN];
     auto read = [&](int x, int u) {
-        const uint8_t *st = smem + (x % D) * kPipeStage;
+        const uint8_t *st = smem + (x % D) * Stage;
         #pragma unroll
         for (int i = 0; i < 4; ++i) fa[u][i] = *reinterpret_cast<const pv4i *>(st + aoff[u] + 2048 * i);
-        #pragma unroll
-        for (int j = 0; j < TN; ++j) fb[u][j] = *reinterpret_cast<const uint32_t *>(st + boff[u] + 512 * j);
+        if (PW) {
+            const uint8_t *sb = smem + ((x & ~1) % D) * Stage + pwoff + 16 * ((2 * (x & 1) + u) ^ pwsw);
+            #pragma unroll
+            for (int j = 0; j < TN; ++j) fb[u][j] = *reinterpret_cast<const uint32_t *>(sb + 1024 * j);
+        } else {
+            #pragma unroll
+            for (int j = 0; j < TN; ++j) fb[u][j] = *reinterpret_cast<const uint32_t *>(st + boff[u] + 512 * j);
+        }
     };
     auto half = [&](int u) {
         #pragma unroll
@@ -526,11 +576,26 @@ double gemm_pipe_estimate_us(int64_t M, int64_t N, int64_t K) {
     return (double)rounds * (double)(K / kPipeKS) * step + 5.0;
 }
 
+// paired weight loads where the steps of a tile pair up (K a multiple of 256)
+static bool pipe_pairs(int64_t K) { return K % (2 * kPipeKS) == 0; }
+
+template <int TN, bool PW>
+static void launch_pipe_pw(bool opt, dim3 g, hipStream_t st, const int8_t *q, const float *s_x,
+                           const uint8_t *packed, const float *s_w, int m, int n, int k, const OutSpec &y,
+                           int32_t *acc, int tiles_m, int nt) {
+    if (opt)
+        gemm_pipe_kernel<TN, true, false, PW><<<g, dim3(kPipeThreads), 0, st>>>(q, s_x, packed, s_w, m, n, k, y, acc,
+                                                                             tiles_m, nt);
+    else
+        gemm_pipe_kernel<TN, false, false, PW><<<g, dim3(kPipeThreads), 0, st>>>(q, s_x, packed, s_w, m, n, k, y, acc,
+                                                                              tiles_m, nt);
+}
+
 template <int TN>
 static void launch_pipe(bool opt, dim3 g, hipStream_t st, const int8_t *q, const float *s_x, const uint8_t *packed,
                         const float *s_w, int m, int n, int k, const OutSpec &y, int32_t *acc, int tiles_m, int nt) {
-    if (opt) gemm_pipe_kernel<TN, true><<<g, dim3(kPipeThreads), 0, st>>>(q, s_x, packed, s_w, m, n, k, y, acc, tiles_m, nt);
-    else gemm_pipe_kernel<TN, false><<<g, dim3(kPipeThreads), 0, st>>>(q, s_x, packed, s_w, m, n, k, y, acc, tiles_m, nt);
+    if (pipe_pairs(k)) launch_pipe_pw<TN, true>(opt, g, st, q, s_x, packed, s_w, m, n, k, y, acc, tiles_m, nt);
+    else launch_pipe_pw<TN, false>(opt, g, st, q, s_x, packed, s_w, m, n, k, y, acc, tiles_m, nt);
 }
 
 hipError_t launch_gemm_pipe(int tn_force, const int8_t *q, const float *s_x, const uint8_t *packed,
@@ -545,8 +610,12 @@ hipError_t launch_gemm_pipe(int tn_force, const int8_t *q, const float *s_x, con
         const int tiles_m = (int)((M + kPipeBM - 1) / kPipeBM);
         const int64_t tiles = (int64_t)tiles_m * ((N + 159) / 160);
         const dim3 g((unsigned)std::min<int64_t>(tiles, cus));
-        gemm_pipe_kernel<5, true, true><<<g, dim3(kPipeThreads), 0, st>>>(q, s_x, packed, s_w, (int)M, (int)N, (int)K, y,
-                                                                          nullptr, tiles_m, (int)tiles);
+        if (pipe_pairs(K))
+            gemm_pipe_kernel<5, true, true, true><<<g, dim3(kPipeThreads), 0, st>>>(q, s_x, packed, s_w, (int)M, (int)N,
+                                                                                (int)K, y, nullptr, tiles_m, (int)tiles);
+        else
+            gemm_pipe_kernel<5, true, true, false><<<g, dim3(kPipeThreads), 0, st>>>(q, s_x, packed, s_w, (int)M, (int)N,
+                                                                                 (int)K, y, nullptr, tiles_m, (int)tiles);
         return hipGetLastError();
     }
     const int tn = tn_force ? tn_force : pipe_pick_tn(M, N, cus, nullptr, nullptr);
