@@ -632,9 +632,10 @@ def main() -> int:
                 log(f"stacked gate 229376x8192 M=1 encoding {v}: {us:.1f} us, {one[v]['weight_GBs']} GB/s, "
                     f"{one[v]['gweights_per_s']} G weights/s")
             res["one_launch_229376x8192"] = one
-            # the same stacked matrix with 8 tokens: the MFMA decode kernel on the codes, the
-            # multi-token bit-serial kernel on the planes and the binary bits (weights read
-            # once per 2 / 4 tokens)
+            # the same stacked matrix with 8 tokens, the library's choice for each format: the
+            # MFMA decode kernel on the codes, the matrix-core kernel on the planes (weights
+            # read once), the multi-token bit-serial kernel on the binary bits (once per 4
+            # tokens); and, for comparison, the bit-serial kernel on the planes (once per 2)
             q8, s8 = tw.quant_act(W.ffn_100b_activations(0, 8, dev)[0])
             y8 = torch.empty((8, big_w["binary"].shape[0]), dtype=torch.float32, device=dev)
             one8 = {}
@@ -644,12 +645,21 @@ def main() -> int:
                     fn = lambda: tw.bitnet_linear(q8, s8, big_w[v], sw_, y8)
                 else:
                     f_ = tw.FMT_BINARY if v == "binary" else tw.FMT_BITPLANES
-                    fn = lambda v=v, f_=f_, sw_=sw_: tw.bitnet_linear_bits(q8, s8, big_w[v], f_, sw_, y8, None, 3)
+                    fn = lambda v=v, f_=f_, sw_=sw_: tw.bitnet_linear_bits(q8, s8, big_w[v], f_, sw_, y8, None, 0)
                 us = graph_us(torch, fn, reps=5, replays=3)
                 wbytes = big_w[v].numel()
                 one8[v] = {"us": round(us, 1), "weight_GBs": round(wbytes / (us * 1e-6) / 1e9, 1),
-                           "gweights_per_s": round(229376 * 8192 / (us * 1e-6) / 1e9, 1)}
+                           "gweights_per_s": round(229376 * 8192 / (us * 1e-6) / 1e9, 1),
+                           "kernel": {"two_bit_codes": "skinny2_kernel", "bitplanes": "bits_mfma_kernel",
+                                      "binary": "bits_mt_kernel"}[v]}
                 log(f"stacked gate 229376x8192 M=8 encoding {v}: {us:.1f} us, {one8[v]['weight_GBs']} GB/s")
+                if v == "bitplanes":
+                    fn3 = lambda sw_=sw_: tw.bitnet_linear_bits(q8, s8, big_w[v], tw.FMT_BITPLANES, sw_, y8, None, 3)
+                    us3 = graph_us(torch, fn3, reps=5, replays=3)
+                    one8["bitplanes_bit_serial"] = {"us": round(us3, 1),
+                                                    "weight_GBs": round(wbytes / (us3 * 1e-6) / 1e9, 1),
+                                                    "kernel": "bits_mt_kernel"}
+                    log(f"stacked gate 229376x8192 M=8 bitplanes, bit-serial kernel: {us3:.1f} us")
             res["one_launch_229376x8192_M8"] = one8
             sec["ffn100b_8layers_M1_encodings"] = res
             del enc, big_w

@@ -160,7 +160,7 @@ BITNET_API int bitnet_pack_bitplanes(const uint8_t *packed, int64_t N, int64_t K
 BITNET_API int bitnet_linear_bits(const int8_t *q, const float *s_x, const uint8_t *wbits, int fmt, const float *s_w,
                                   int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, int kernel, void *stream) {
     if (fmt != BITNET_FMT_BINARY && fmt != BITNET_FMT_BITPLANES) return fail(BITNET_ERR_ARG, "unknown weight format");
-    if (kernel < 0 || kernel > 3) return fail(BITNET_ERR_ARG, "unknown kernel id");
+    if (kernel < 0 || kernel > 4) return fail(BITNET_ERR_ARG, "unknown kernel id");
     int st = check_dims(M, N, K);
     if (st) return st;
     if (K % 32 != 0) return fail(BITNET_ERR_SHAPE, "K must be a multiple of 32");
@@ -174,6 +174,9 @@ BITNET_API int bitnet_linear_bits(const int8_t *q, const float *s_x, const uint8
     if (kernel == 3 && (!bits_mt_ok(fmt, K, q, wbits) || M > 65535))
         return fail(BITNET_ERR_ARG, "the multi-token bit-serial kernel needs K % 128 (binary) or % 64 (bitplanes), "
                                     "one token's planes within 64 KiB of LDS, M <= 65535, 16-byte aligned q and weights");
+    if (kernel == 4 && !bits_mfma_ok(fmt, M, K, q, wbits))
+        return fail(BITNET_ERR_ARG, "the MFMA kernel for bitplanes needs the bitplane format, K % 64 == 0, "
+                                    "at most 65535 tiles of 16 tokens, 16-byte aligned q and weights");
     return hip_status(launch_linear_bits(q, s_x, wbits, fmt, s_w, M, N, K, y, acc, kernel, (hipStream_t)stream));
 }
 

@@ -642,6 +642,197 @@ static hipError_t launch_bits_mt(const int8_t *q, const float *s_x, const uint8_
     return launch_bits_mt_t<FMT, 1>(q, s_x, wbits, s_w, M, N, K, y, acc, st);
 }
 
+// ---- bitplanes, several tokens: the matrix cores
+//
+// sum q t = sum q pos - sum q neg, pos = mask ^ sign (the +1 weights) and neg = sign
+// (the -1 weights; the sign bit is set only under the mask), each a plane of 0 / 1
+// bytes multiplied with q on v_mfma_i32_16x16x64_i8 (16 weight rows x 16 tokens, 64
+// k per instruction).  The weights are read once for up to 16 tokens.
+//  * Lane (row r16, lane group g) loads the 16 bytes of 64-weight chunk c of its row
+//    (mask and sign of weights 32 G + i, G = 0, 1) and its token's 64 q values of the
+//    same chunk; the four lane groups take four consecutive chunks.
+//  * MFMA j (0..3) of a chunk holds in dword u, byte b the weight
+//    k = 32 (u >> 1) + 2 j + (u & 1) + 8 b: (plane_G >> s) & 0x01010101 with
+//    s = 2 j + (u & 1), one shift and one mask per 4 weights.  The q operand holds the
+//    same k at the same place: four 4x4 byte transposes of the 64 q bytes (dwords
+//    8 G + 2 b + h, h = s >> 2, give the bytes p = s & 3).
+//  * K is split over the wavefronts of a workgroup when there are few row groups
+//    (summed through LDS), as in the MFMA decode kernel for 2-bit codes.
+constexpr int kBitsMfmaNW = 8;   // wavefronts per workgroup
+
+__device__ __forceinline__ uint32_t plane_bytes(uint32_t w, int s) { return (w >> s) & 0x01010101u; }
+
+template <int RG>
+__global__ __launch_bounds__(64 * kBitsMfmaNW) void bits_mfma_kernel(
+    const int8_t *__restrict__ q, const float *__restrict__ s_x, const uint8_t *__restrict__ planes,
+    const float *__restrict__ s_w, int M, int N, int K, float *__restrict__ y, int32_t *__restrict__ acc_out,
+    int kslices) {
+    typedef int v4i_b __attribute__((ext_vector_type(4)));
+    constexpr int NW = kBitsMfmaNW;
+    __shared__ int red[NW * RG * 256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int m0 = (int)blockIdx.y * 16, mt = min(16, M - m0);   // this workgroup's token tile
+    const int C = K >> 6;
+    const size_t KB = (size_t)(K >> 2);   // plane bytes per row
+    const int rowset = wave / kslices, slice = wave - rowset * kslices;
+    const int row_base = (int)blockIdx.x * ((NW / kslices) * 16 * RG);
+    const int row0 = row_base + rowset * 16 * RG;
+    const int cb = (int)(((int64_t)C * slice) / kslices);
+    const int ce = (int)(((int64_t)C * (slice + 1)) / kslices);
+    const int8_t *qrow = q + (size_t)(m0 + min(l16, mt - 1)) * K;   // tokens past the tile repeat its last
+    const uint8_t *prow[RG];
+    #pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+        const int r = row0 + 16 * rg + l16;
+        prow[rg] = planes + (size_t)(r < N ? r : 0) * KB;   // rows past N read row 0, dropped
+    }
+    v4i_b accp[RG], accn[RG];
+    #pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+        accp[rg] = v4i_b{0, 0, 0, 0};
+        accn[rg] = v4i_b{0, 0, 0, 0};
+    }
+    // step t: lane group g takes chunk cb + 4 t + g; past the slice end the chunk is
+    // clamped (an in-range load) and its planes are zeroed
+    const int T = (ce - cb + 3) >> 2;
+    const int clast = max(ce - 1, cb);
+    uint4 wA[RG], wB[RG], qA[4], qB[4];
+    auto issue = [&](uint4 (&w)[RG], uint4 (&qq)[4], int t) {
+        const int cc = min(cb + 4 * t + g, clast);
+        #pragma unroll
+        for (int rg = 0; rg < RG; ++rg) w[rg] = gload16(prow[rg] + 16 * cc);
+        #pragma unroll
+        for (int d = 0; d < 4; ++d) qq[d] = gload16(qrow + 64 * cc + 16 * d);
+    };
+    auto consume = [&](const uint4 (&w)[RG], const uint4 (&qq)[4], int t) {
+        const bool valid = cb + 4 * t + g < ce;
+        // O[G][h][p], byte b: q of k = 32 G + 8 b + 4 h + p
+        uint32_t O[2][2][4];
+        transpose4x4(qq[0].x, qq[0].z, qq[1].x, qq[1].z, O[0][0][0], O[0][0][1], O[0][0][2], O[0][0][3]);
+        transpose4x4(qq[0].y, qq[0].w, qq[1].y, qq[1].w, O[0][1][0], O[0][1][1], O[0][1][2], O[0][1][3]);
+        transpose4x4(qq[2].x, qq[2].z, qq[3].x, qq[3].z, O[1][0][0], O[1][0][1], O[1][0][2], O[1][0][3]);
+        transpose4x4(qq[2].y, qq[2].w, qq[3].y, qq[3].w, O[1][1][0], O[1][1][1], O[1][1][2], O[1][1][3]);
+        uint32_t pos[RG][2], neg[RG][2];
+        #pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+            pos[rg][0] = valid ? (w[rg].x ^ w[rg].y) : 0u;
+            neg[rg][0] = valid ? w[rg].y : 0u;
+            pos[rg][1] = valid ? (w[rg].z ^ w[rg].w) : 0u;
+            neg[rg][1] = valid ? w[rg].w : 0u;
+        }
+        #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int h = j >> 1, p = 2 * (j & 1);
+            const v4i_b b = v4i_b{(int)O[0][h][p], (int)O[0][h][p + 1], (int)O[1][h][p], (int)O[1][h][p + 1]};
+            #pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                const v4i_b ap = v4i_b{(int)plane_bytes(pos[rg][0], 2 * j), (int)plane_bytes(pos[rg][0], 2 * j + 1),
+                                       (int)plane_bytes(pos[rg][1], 2 * j), (int)plane_bytes(pos[rg][1], 2 * j + 1)};
+                const v4i_b an = v4i_b{(int)plane_bytes(neg[rg][0], 2 * j), (int)plane_bytes(neg[rg][0], 2 * j + 1),
+                                       (int)plane_bytes(neg[rg][1], 2 * j), (int)plane_bytes(neg[rg][1], 2 * j + 1)};
+                accp[rg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap, b, accp[rg], 0, 0, 0);
+                accn[rg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(an, b, accn[rg], 0, 0, 0);
+            }
+        }
+    };
+    if (T > 0) {
+        issue(wA, qA, 0);
+        const int T2 = (T + 1) & ~1;
+        for (int t = 0; t < T2 - 2; t += 2) {
+            issue(wB, qB, t + 1);
+            consume(wA, qA, t);
+            issue(wA, qA, t + 2);
+            consume(wB, qB, t + 1);
+        }
+        if (T2 == T) {
+            issue(wB, qB, T - 1);
+            consume(wA, qA, T - 2);
+            consume(wB, qB, T - 1);
+        } else {
+            consume(wA, qA, T - 1);
+        }
+    }
+    // 16 x 16 accumulator layout: lane -> token l16 of the tile; register r -> row
+    // 4 g + r of the row group
+    const float sw = *s_w;
+    if (kslices == 1) {
+        if (l16 < mt) {
+            const int m = m0 + l16;
+            const double cm = rescale_factor(s_x[m], sw);
+            #pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = row0 + 16 * rg + 4 * g + r;
+                    if (row < N) {
+                        const size_t o = (size_t)m * N + row;
+                        const int v = accp[rg][r] - accn[rg][r];
+                        y[o] = rescale(v, cm);
+                        if (acc_out) acc_out[o] = v;
+                    }
+                }
+            }
+        }
+        return;
+    }
+    #pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+        #pragma unroll
+        for (int r = 0; r < 4; ++r) red[((wave * RG + rg) * 4 + r) * 64 + lane] = accp[rg][r] - accn[rg][r];
+    }
+    __syncthreads();
+    const int rowsets = NW / kslices;
+    for (int idx = tid; idx < rowsets * RG * 256; idx += NW * 64) {
+        const int rsi = idx / (RG * 256), rem = idx - rsi * RG * 256;
+        const int rg = rem >> 8, r = (rem >> 6) & 3, ln = rem & 63;
+        const int tok = ln & 15;
+        const int row = row_base + rsi * 16 * RG + 16 * rg + 4 * (ln >> 4) + r;
+        if (tok >= mt || row >= N) continue;
+        int sum = 0;
+        for (int w = 0; w < kslices; ++w) sum += red[(((rsi * kslices + w) * RG + rg) * 4 + r) * 64 + ln];
+        const size_t o = (size_t)(m0 + tok) * N + row;
+        y[o] = rescale(sum, rescale_factor(s_x[m0 + tok], sw));
+        if (acc_out) acc_out[o] = sum;
+    }
+}
+
+// Bitplanes, K % 64 == 0, 16-byte aligned q and planes; any M (16-token tiles on the
+// grid's y, at most 65535 of them).
+bool bits_mfma_ok(int fmt, int64_t M, int64_t K, const void *q, const void *wbits) {
+    return fmt == 2 && M >= 1 && (M + 15) / 16 <= 65535 && K > 0 && K % 64 == 0 && K < ((int64_t)1 << 30) &&
+           (uintptr_t)q % 16 == 0 && (uintptr_t)wbits % 16 == 0;
+}
+
+template <int RG>
+static void launch_bits_mfma_rg(const int8_t *q, const float *s_x, const uint8_t *wbits, const float *s_w, int64_t M,
+                                int64_t N, int64_t K, float *y, int32_t *acc, int ks, hipStream_t st) {
+    constexpr int NW = kBitsMfmaNW;
+    const int64_t rows_per_block = (NW / ks) * 16 * RG;
+    const dim3 grid((unsigned)((N + rows_per_block - 1) / rows_per_block), (unsigned)((M + 15) / 16));
+    bits_mfma_kernel<RG><<<grid, dim3(64 * NW), 0, st>>>(q, s_x, wbits, s_w, (int)M, (int)N, (int)K, y, acc, ks);
+}
+
+// Rows per wavefront (16 RG) against parallelism, as for the 2-bit codes: the largest
+// RG whose launch, with K split over up to 8 wavefronts (at least 8 chunks per
+// slice), still reaches 4096 wavefronts.
+static hipError_t launch_bits_mfma(const int8_t *q, const float *s_x, const uint8_t *wbits, const float *s_w,
+                                   int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
+    const int64_t C = K / 64;
+    int rg = 1, ks = 1;
+    for (int r = 2; r >= 1; r >>= 1) {
+        const int64_t groups = (N + 16 * r - 1) / (16 * r);
+        int k = 1;
+        while (k < kBitsMfmaNW && groups * k < 4096 && C / (2 * k) >= 8) k *= 2;
+        rg = r;
+        ks = k;
+        if (groups * k >= 4096) break;
+    }
+    if (rg == 2) launch_bits_mfma_rg<2>(q, s_x, wbits, s_w, M, N, K, y, acc, ks, st);
+    else launch_bits_mfma_rg<1>(q, s_x, wbits, s_w, M, N, K, y, acc, ks, st);
+    return hipGetLastError();
+}
+
 // ---- any M: one thread per output, plain loops (any alignment)
 
 template <int FMT>
@@ -680,6 +871,9 @@ hipError_t launch_linear_bits(const int8_t *q, const float *s_x, const uint8_t *
         return fmt == 1 ? launch_gemv_bits<1>(q, s_x, wbits, s_w, N, K, y, acc, st)
                         : launch_gemv_bits<2>(q, s_x, wbits, s_w, N, K, y, acc, st);
     }
+    // bitplanes, several tokens: the matrix cores
+    if (kernel == 4 || (kernel == 0 && M > 1 && bits_mfma_ok(fmt, M, K, q, wbits)))
+        return launch_bits_mfma(q, s_x, wbits, s_w, M, N, K, y, acc, st);
     // (token tiles on the grid's y: at most 65535 of them)
     if (kernel == 3 || (kernel == 0 && bits_mt_ok(fmt, K, q, wbits) && M <= 65535)) {
         return fmt == 1 ? launch_bits_mt<1>(q, s_x, wbits, s_w, M, N, K, y, acc, st)

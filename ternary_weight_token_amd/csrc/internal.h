@@ -101,6 +101,7 @@ uint32_t bits_fused_lds_bytes(int64_t K);
 hipError_t launch_bits_fused_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, hipStream_t st);
 bool bits_fast_ok(int fmt, int64_t M, int64_t K, const void *q, const void *wbits);
 bool bits_mt_ok(int fmt, int64_t K, const void *q, const void *wbits);   // several tokens per pass
+bool bits_mfma_ok(int fmt, int64_t M, int64_t K, const void *q, const void *wbits);   // bitplanes on MFMA
 hipError_t launch_linear_bits(const int8_t *q, const float *s_x, const uint8_t *wbits, int fmt, const float *s_w,
                               int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, int kernel, hipStream_t st);
 hipError_t launch_pack(const float *w, int64_t N, int64_t K, float eps, uint8_t *packed,
