@@ -633,9 +633,9 @@ def main() -> int:
                     f"{one[v]['gweights_per_s']} G weights/s")
             res["one_launch_229376x8192"] = one
             # the same stacked matrix with 8 tokens, the library's choice for each format: the
-            # MFMA decode kernel on the codes, the matrix-core kernel on the planes (weights
-            # read once), the multi-token bit-serial kernel on the binary bits (once per 4
-            # tokens); and, for comparison, the bit-serial kernel on the planes (once per 2)
+            # MFMA decode kernel on the codes, the matrix-core kernel on the planes and on the
+            # binary bits (weights read once); and, for comparison, the multi-token bit-serial
+            # kernel on both (weights read once per 2 / 4 tokens)
             q8, s8 = tw.quant_act(W.ffn_100b_activations(0, 8, dev)[0])
             y8 = torch.empty((8, big_w["binary"].shape[0]), dtype=torch.float32, device=dev)
             one8 = {}
@@ -650,16 +650,15 @@ def main() -> int:
                 wbytes = big_w[v].numel()
                 one8[v] = {"us": round(us, 1), "weight_GBs": round(wbytes / (us * 1e-6) / 1e9, 1),
                            "gweights_per_s": round(229376 * 8192 / (us * 1e-6) / 1e9, 1),
-                           "kernel": {"two_bit_codes": "skinny2_kernel", "bitplanes": "bits_mfma_kernel",
-                                      "binary": "bits_mt_kernel"}[v]}
+                           "kernel": "skinny2_kernel" if v == "two_bit_codes" else "bits_mfma_kernel"}
                 log(f"stacked gate 229376x8192 M=8 encoding {v}: {us:.1f} us, {one8[v]['weight_GBs']} GB/s")
-                if v == "bitplanes":
-                    fn3 = lambda sw_=sw_: tw.bitnet_linear_bits(q8, s8, big_w[v], tw.FMT_BITPLANES, sw_, y8, None, 3)
+                if v != "two_bit_codes":
+                    fn3 = lambda v=v, f_=f_, sw_=sw_: tw.bitnet_linear_bits(q8, s8, big_w[v], f_, sw_, y8, None, 3)
                     us3 = graph_us(torch, fn3, reps=5, replays=3)
-                    one8["bitplanes_bit_serial"] = {"us": round(us3, 1),
-                                                    "weight_GBs": round(wbytes / (us3 * 1e-6) / 1e9, 1),
-                                                    "kernel": "bits_mt_kernel"}
-                    log(f"stacked gate 229376x8192 M=8 bitplanes, bit-serial kernel: {us3:.1f} us")
+                    one8[f"{v}_bit_serial"] = {"us": round(us3, 1),
+                                               "weight_GBs": round(wbytes / (us3 * 1e-6) / 1e9, 1),
+                                               "kernel": "bits_mt_kernel"}
+                    log(f"stacked gate 229376x8192 M=8 {v}, bit-serial kernel: {us3:.1f} us")
             res["one_launch_229376x8192_M8"] = one8
             sec["ffn100b_8layers_M1_encodings"] = res
             del enc, big_w

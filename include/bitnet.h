@@ -373,11 +373,11 @@ BITNET_API int bitnet_pack_bitplanes(const uint8_t *packed, int64_t N, int64_t K
  * several tokens (any M up to 65535: the weights are read once per 4 tokens for
  * binary, per 2 for bitplanes, fewer when one token's planes exceed 16 KiB; same K
  * divisibility and alignment, one token's planes within 64 KiB; BITNET_ERR_ARG
- * otherwise), 4 the matrix-core kernel for bitplanes (fmt BITNET_FMT_BITPLANES only,
- * any M, the weights read once per 16 tokens: the +1 and -1 planes as 0 / 1 bytes
- * multiplied with q by int8 MFMAs; K % 64 == 0, q and wbits 16-byte aligned;
- * BITNET_ERR_ARG otherwise).  Kernel 0 takes 2 for one token, and for more takes 4
- * (bitplanes) or 3 when they apply.  acc may be NULL. */
+ * otherwise), 4 the matrix-core kernel (any M, the weights read once per 16 tokens:
+ * bitplanes as their +1 and -1 planes, binary weights as their bits, each a set of
+ * 0 / 1 bytes multiplied with q by int8 MFMAs; K % 64 == 0, q and wbits 16-byte
+ * aligned; BITNET_ERR_ARG otherwise).  Kernel 0 takes 2 for one token and 4 for
+ * more, else 3 when they apply.  acc may be NULL. */
 BITNET_API int bitnet_linear_bits(const int8_t *q, const float *s_x, const uint8_t *wbits, int fmt,
                                   const float *s_w, int64_t M, int64_t N, int64_t K, float *y, int32_t *acc,
                                   int kernel, void *stream);

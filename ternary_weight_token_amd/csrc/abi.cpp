@@ -175,8 +175,8 @@ BITNET_API int bitnet_linear_bits(const int8_t *q, const float *s_x, const uint8
         return fail(BITNET_ERR_ARG, "the multi-token bit-serial kernel needs K % 128 (binary) or % 64 (bitplanes), "
                                     "one token's planes within 64 KiB of LDS, M <= 65535, 16-byte aligned q and weights");
     if (kernel == 4 && !bits_mfma_ok(fmt, M, K, q, wbits))
-        return fail(BITNET_ERR_ARG, "the MFMA kernel for bitplanes needs the bitplane format, K % 64 == 0, "
-                                    "at most 65535 tiles of 16 tokens, 16-byte aligned q and weights");
+        return fail(BITNET_ERR_ARG, "the matrix-core kernel needs K % 64 == 0, at most 65535 tiles of 16 tokens, "
+                                    "16-byte aligned q and weights");
     return hip_status(launch_linear_bits(q, s_x, wbits, fmt, s_w, M, N, K, y, acc, kernel, (hipStream_t)stream));
 }
 

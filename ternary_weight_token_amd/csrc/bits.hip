@@ -642,15 +642,18 @@ static hipError_t launch_bits_mt(const int8_t *q, const float *s_x, const uint8_
     return launch_bits_mt_t<FMT, 1>(q, s_x, wbits, s_w, M, N, K, y, acc, st);
 }
 
-// ---- bitplanes, several tokens: the matrix cores
+// ---- several tokens: the matrix cores
 //
-// sum q t = sum q pos - sum q neg, pos = mask ^ sign (the +1 weights) and neg = sign
-// (the -1 weights; the sign bit is set only under the mask), each a plane of 0 / 1
-// bytes multiplied with q on v_mfma_i32_16x16x64_i8 (16 weight rows x 16 tokens, 64
-// k per instruction).  The weights are read once for up to 16 tokens.
-//  * Lane (row r16, lane group g) loads the 16 bytes of 64-weight chunk c of its row
-//    (mask and sign of weights 32 G + i, G = 0, 1) and its token's 64 q values of the
-//    same chunk; the four lane groups take four consecutive chunks.
+// Bitplanes (FMT 2): sum q t = sum q pos - sum q neg, pos = mask ^ sign (the +1
+// weights) and neg = sign (the -1 weights; the sign bit is set only under the mask).
+// Binary (FMT 1): sum q t = 2 sum q bit - sum q, the row sums of q from one more
+// MFMA with an all-ones operand.  Each plane is a set of 0 / 1 bytes multiplied with q
+// on v_mfma_i32_16x16x64_i8 (16 weight rows x 16 tokens, 64 k per instruction), so
+// the weights are read once for up to 16 tokens.
+//  * Lane (row r16, lane group g) loads the bytes of 64-weight chunk c of its row
+//    (bitplanes: mask and sign of weights 32 G + i, G = 0, 1, 16 bytes; binary: the
+//    two 32-weight words, 8 bytes) and its token's 64 q values of the same chunk; the
+//    four lane groups take four consecutive chunks.
 //  * MFMA j (0..3) of a chunk holds in dword u, byte b the weight
 //    k = 32 (u >> 1) + 2 j + (u & 1) + 8 b: (plane_G >> s) & 0x01010101 with
 //    s = 2 j + (u & 1), one shift and one mask per 4 weights.  The q operand holds the
@@ -662,7 +665,7 @@ constexpr int kBitsMfmaNW = 8;   // wavefronts per workgroup
 
 __device__ __forceinline__ uint32_t plane_bytes(uint32_t w, int s) { return (w >> s) & 0x01010101u; }
 
-template <int RG>
+template <int FMT, int RG>
 __global__ __launch_bounds__(64 * kBitsMfmaNW) void bits_mfma_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s_x, const uint8_t *__restrict__ planes,
     const float *__restrict__ s_w, int M, int N, int K, float *__restrict__ y, int32_t *__restrict__ acc_out,
@@ -674,7 +677,7 @@ __global__ __launch_bounds__(64 * kBitsMfmaNW) void bits_mfma_kernel(
     const int l16 = lane & 15, g = lane >> 4;
     const int m0 = (int)blockIdx.y * 16, mt = min(16, M - m0);   // this workgroup's token tile
     const int C = K >> 6;
-    const size_t KB = (size_t)(K >> 2);   // plane bytes per row
+    const size_t KB = (size_t)(FMT == 2 ? K >> 2 : K >> 3);   // weight bytes per row
     const int rowset = wave / kslices, slice = wave - rowset * kslices;
     const int row_base = (int)blockIdx.x * ((NW / kslices) * 16 * RG);
     const int row0 = row_base + rowset * 16 * RG;
@@ -687,12 +690,12 @@ __global__ __launch_bounds__(64 * kBitsMfmaNW) void bits_mfma_kernel(
         const int r = row0 + 16 * rg + l16;
         prow[rg] = planes + (size_t)(r < N ? r : 0) * KB;   // rows past N read row 0, dropped
     }
-    v4i_b accp[RG], accn[RG];
+    // accp: the +1 plane (binary: the bits); accn: the -1 plane (binary: the sums of q)
+    v4i_b accp[RG], accn[FMT == 2 ? RG : 1];
     #pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-        accp[rg] = v4i_b{0, 0, 0, 0};
-        accn[rg] = v4i_b{0, 0, 0, 0};
-    }
+    for (int rg = 0; rg < RG; ++rg) accp[rg] = v4i_b{0, 0, 0, 0};
+    #pragma unroll
+    for (int rg = 0; rg < (FMT == 2 ? RG : 1); ++rg) accn[rg] = v4i_b{0, 0, 0, 0};
     // step t: lane group g takes chunk cb + 4 t + g; past the slice end the chunk is
     // clamped (an in-range load) and its planes are zeroed
     const int T = (ce - cb + 3) >> 2;
@@ -701,7 +704,15 @@ __global__ __launch_bounds__(64 * kBitsMfmaNW) void bits_mfma_kernel(
     auto issue = [&](uint4 (&w)[RG], uint4 (&qq)[4], int t) {
         const int cc = min(cb + 4 * t + g, clast);
         #pragma unroll
-        for (int rg = 0; rg < RG; ++rg) w[rg] = gload16(prow[rg] + 16 * cc);
+        for (int rg = 0; rg < RG; ++rg) {
+            if (FMT == 2) {
+                w[rg] = gload16(prow[rg] + 16 * cc);
+            } else {
+                typedef unsigned int v2u_b __attribute__((ext_vector_type(2)));
+                const v2u_b v = *(__attribute__((address_space(1))) const v2u_b *)(prow[rg] + 8 * cc);
+                w[rg] = make_uint4(v.x, v.y, 0u, 0u);
+            }
+        }
         #pragma unroll
         for (int d = 0; d < 4; ++d) qq[d] = gload16(qrow + 64 * cc + 16 * d);
     };
@@ -716,23 +727,33 @@ __global__ __launch_bounds__(64 * kBitsMfmaNW) void bits_mfma_kernel(
         uint32_t pos[RG][2], neg[RG][2];
         #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
-            pos[rg][0] = valid ? (w[rg].x ^ w[rg].y) : 0u;
-            neg[rg][0] = valid ? w[rg].y : 0u;
-            pos[rg][1] = valid ? (w[rg].z ^ w[rg].w) : 0u;
-            neg[rg][1] = valid ? w[rg].w : 0u;
+            if (FMT == 2) {
+                pos[rg][0] = valid ? (w[rg].x ^ w[rg].y) : 0u;
+                neg[rg][0] = valid ? w[rg].y : 0u;
+                pos[rg][1] = valid ? (w[rg].z ^ w[rg].w) : 0u;
+                neg[rg][1] = valid ? w[rg].w : 0u;
+            } else {
+                pos[rg][0] = valid ? w[rg].x : 0u;
+                pos[rg][1] = valid ? w[rg].y : 0u;
+            }
         }
+        const int one = valid ? 0x01010101 : 0;
+        const v4i_b ones = v4i_b{one, one, one, one};
         #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int h = j >> 1, p = 2 * (j & 1);
             const v4i_b b = v4i_b{(int)O[0][h][p], (int)O[0][h][p + 1], (int)O[1][h][p], (int)O[1][h][p + 1]};
+            if (FMT == 1) accn[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, b, accn[0], 0, 0, 0);
             #pragma unroll
             for (int rg = 0; rg < RG; ++rg) {
                 const v4i_b ap = v4i_b{(int)plane_bytes(pos[rg][0], 2 * j), (int)plane_bytes(pos[rg][0], 2 * j + 1),
                                        (int)plane_bytes(pos[rg][1], 2 * j), (int)plane_bytes(pos[rg][1], 2 * j + 1)};
-                const v4i_b an = v4i_b{(int)plane_bytes(neg[rg][0], 2 * j), (int)plane_bytes(neg[rg][0], 2 * j + 1),
-                                       (int)plane_bytes(neg[rg][1], 2 * j), (int)plane_bytes(neg[rg][1], 2 * j + 1)};
                 accp[rg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap, b, accp[rg], 0, 0, 0);
-                accn[rg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(an, b, accn[rg], 0, 0, 0);
+                if (FMT == 2) {
+                    const v4i_b an = v4i_b{(int)plane_bytes(neg[rg][0], 2 * j), (int)plane_bytes(neg[rg][0], 2 * j + 1),
+                                           (int)plane_bytes(neg[rg][1], 2 * j), (int)plane_bytes(neg[rg][1], 2 * j + 1)};
+                    accn[rg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(an, b, accn[rg], 0, 0, 0);
+                }
             }
         }
     };
@@ -767,7 +788,7 @@ __global__ __launch_bounds__(64 * kBitsMfmaNW) void bits_mfma_kernel(
                     const int row = row0 + 16 * rg + 4 * g + r;
                     if (row < N) {
                         const size_t o = (size_t)m * N + row;
-                        const int v = accp[rg][r] - accn[rg][r];
+                        const int v = FMT == 2 ? accp[rg][r] - accn[rg][r] : 2 * accp[rg][r] - accn[0][r];
                         y[o] = rescale(v, cm);
                         if (acc_out) acc_out[o] = v;
                     }
@@ -779,7 +800,9 @@ __global__ __launch_bounds__(64 * kBitsMfmaNW) void bits_mfma_kernel(
     #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
         #pragma unroll
-        for (int r = 0; r < 4; ++r) red[((wave * RG + rg) * 4 + r) * 64 + lane] = accp[rg][r] - accn[rg][r];
+        for (int r = 0; r < 4; ++r)
+            red[((wave * RG + rg) * 4 + r) * 64 + lane] =
+                FMT == 2 ? accp[rg][r] - accn[rg][r] : 2 * accp[rg][r] - accn[0][r];
     }
     __syncthreads();
     const int rowsets = NW / kslices;
@@ -797,25 +820,26 @@ __global__ __launch_bounds__(64 * kBitsMfmaNW) void bits_mfma_kernel(
     }
 }
 
-// Bitplanes, K % 64 == 0, 16-byte aligned q and planes; any M (16-token tiles on the
-// grid's y, at most 65535 of them).
+// K % 64 == 0, 16-byte aligned q and weights; any M (16-token tiles on the grid's y,
+// at most 65535 of them).
 bool bits_mfma_ok(int fmt, int64_t M, int64_t K, const void *q, const void *wbits) {
-    return fmt == 2 && M >= 1 && (M + 15) / 16 <= 65535 && K > 0 && K % 64 == 0 && K < ((int64_t)1 << 30) &&
+    return (fmt == 1 || fmt == 2) && M >= 1 && (M + 15) / 16 <= 65535 && K > 0 && K % 64 == 0 && K < ((int64_t)1 << 30) &&
            (uintptr_t)q % 16 == 0 && (uintptr_t)wbits % 16 == 0;
 }
 
-template <int RG>
+template <int FMT, int RG>
 static void launch_bits_mfma_rg(const int8_t *q, const float *s_x, const uint8_t *wbits, const float *s_w, int64_t M,
                                 int64_t N, int64_t K, float *y, int32_t *acc, int ks, hipStream_t st) {
     constexpr int NW = kBitsMfmaNW;
     const int64_t rows_per_block = (NW / ks) * 16 * RG;
     const dim3 grid((unsigned)((N + rows_per_block - 1) / rows_per_block), (unsigned)((M + 15) / 16));
-    bits_mfma_kernel<RG><<<grid, dim3(64 * NW), 0, st>>>(q, s_x, wbits, s_w, (int)M, (int)N, (int)K, y, acc, ks);
+    bits_mfma_kernel<FMT, RG><<<grid, dim3(64 * NW), 0, st>>>(q, s_x, wbits, s_w, (int)M, (int)N, (int)K, y, acc, ks);
 }
 
 // Rows per wavefront (16 RG) against parallelism, as for the 2-bit codes: the largest
 // RG whose launch, with K split over up to 8 wavefronts (at least 8 chunks per
 // slice), still reaches 4096 wavefronts.
+template <int FMT>
 static hipError_t launch_bits_mfma(const int8_t *q, const float *s_x, const uint8_t *wbits, const float *s_w,
                                    int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
     const int64_t C = K / 64;
@@ -828,8 +852,8 @@ static hipError_t launch_bits_mfma(const int8_t *q, const float *s_x, const uint
         ks = k;
         if (groups * k >= 4096) break;
     }
-    if (rg == 2) launch_bits_mfma_rg<2>(q, s_x, wbits, s_w, M, N, K, y, acc, ks, st);
-    else launch_bits_mfma_rg<1>(q, s_x, wbits, s_w, M, N, K, y, acc, ks, st);
+    if (rg == 2) launch_bits_mfma_rg<FMT, 2>(q, s_x, wbits, s_w, M, N, K, y, acc, ks, st);
+    else launch_bits_mfma_rg<FMT, 1>(q, s_x, wbits, s_w, M, N, K, y, acc, ks, st);
     return hipGetLastError();
 }
 
@@ -871,9 +895,10 @@ hipError_t launch_linear_bits(const int8_t *q, const float *s_x, const uint8_t *
         return fmt == 1 ? launch_gemv_bits<1>(q, s_x, wbits, s_w, N, K, y, acc, st)
                         : launch_gemv_bits<2>(q, s_x, wbits, s_w, N, K, y, acc, st);
     }
-    // bitplanes, several tokens: the matrix cores
+    // several tokens: the matrix cores
     if (kernel == 4 || (kernel == 0 && M > 1 && bits_mfma_ok(fmt, M, K, q, wbits)))
-        return launch_bits_mfma(q, s_x, wbits, s_w, M, N, K, y, acc, st);
+        return fmt == 1 ? launch_bits_mfma<1>(q, s_x, wbits, s_w, M, N, K, y, acc, st)
+                        : launch_bits_mfma<2>(q, s_x, wbits, s_w, M, N, K, y, acc, st);
     // (token tiles on the grid's y: at most 65535 of them)
     if (kernel == 3 || (kernel == 0 && bits_mt_ok(fmt, K, q, wbits) && M <= 65535)) {
         return fmt == 1 ? launch_bits_mt<1>(q, s_x, wbits, s_w, M, N, K, y, acc, st)

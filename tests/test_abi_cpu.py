@@ -336,7 +336,7 @@ def test_bit_encodings_reject_bad_arguments(L):
     lb = L.bitnet_linear_bits
     assert lb(p, p, p, 3, p, 1, 8, 128, p, z, 0, z) == ARG                        # format
     assert lb(p, p, p, 1, p, 1, 8, 128, p, z, 5, z) == ARG                        # kernel id
-    assert lb(p, p, p, 1, p, 2, 8, 128, p, z, 4, z) == ARG                        # MFMA kernel: bitplanes only
+    assert lb(p, p, p, 1, p, 2, 8, 96, p, z, 4, z) == ARG                         # MFMA kernel, binary: K % 64
     assert lb(p, p, p, 2, p, 2, 8, 96, p, z, 4, z) == ARG                         # MFMA kernel: K % 64
     assert lb(p, p, p, 2, p, 16 * 65536, 8, 128, p, z, 4, z) == ARG               # MFMA kernel: token tiles
     assert lb(p, p, ctypes.c_void_p(4104), 2, p, 2, 8, 128, p, z, 4, z) == ARG    # MFMA kernel: alignment

@@ -826,7 +826,7 @@ def test_linear_bits_parity(fmt, M, N, K):
     acc_ref, y_ref = ref(q, s, s_w)
     qd, sd = torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV)
     wd, swd = torch.from_numpy(wb).to(DEV), torch.tensor([s_w], device=DEV)
-    kernels = ((0, 1, 2, 3) if M == 1 else (0, 1, 3)) + ((4,) if fmt == tw.FMT_BITPLANES else ())
+    kernels = ((0, 1, 2, 3) if M == 1 else (0, 1, 3)) + ((4,) if K % 64 == 0 else ())
     for kern in kernels:
         y, acc = tw.linear_bits(qd, sd, wd, fmt, swd, want_acc=True, kernel=kern)
         torch.cuda.synchronize()
@@ -834,25 +834,31 @@ def test_linear_bits_parity(fmt, M, N, K):
         assert_y(y.cpu().numpy(), y_ref)
 
 
+@pytest.mark.parametrize("fmt", [1, 2])
 @pytest.mark.parametrize("M,N,K", [(2, 1, 64), (16, 5000, 2560), (17, 300, 6912), (40, 129, 1024), (8, 6000, 8192),
                                    (3, 7, 28672), (33, 4096, 128), (8, 65, 57344), (4, 131112, 128)])
-def test_linear_bitplanes_mfma(M, N, K):
-    """The matrix-core kernel for bitplanes (kernel 4): one to three 16-token tiles,
-    ragged rows, K split over 1 to 8 wavefronts, one or two 16-row groups per
-    wavefront, K from one chunk to 57344, planes of random 2-bit codes (code 3 as +1),
-    and a token row of +-127 so that every byte of the products counts; acc bit-exact
-    and y against the oracle's product over the same planes."""
-    key = synth.stream_key(354, M, N, K)
+def test_linear_bits_mfma(fmt, M, N, K):
+    """The matrix-core kernel for binary weights and bitplanes (kernel 4): one to three
+    16-token tiles, ragged rows, K split over 1 to 8 wavefronts, one or two 16-row
+    groups per wavefront, K from one chunk to 57344, random weight bits (binary) or
+    planes of random 2-bit codes (code 3 as +1), and a token row of +-127 so that every
+    byte of the products counts; acc bit-exact and y against the oracle's product over
+    the same weights."""
+    key = synth.stream_key(354, fmt, M, N, K)
     x, q, s = quantized_inputs(key, M, K, outlier_frac=0.002)
     q[0, ::2] = 127
     q[0, 1::2] = -127
     s[0] = np.float32(1.5)
-    packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
-    wb = oracle.pack_bitplanes(packed, K)
     s_w = np.float32(0.0109)
-    acc_ref, y_ref = oracle.linear_bitplanes(q, s, wb, s_w)
+    if fmt == tw.FMT_BINARY:
+        wb = synth.random_bytes(synth.stream_key(key, 1), N * K // 8).numpy().reshape(N, K // 8)
+        acc_ref, y_ref = oracle.linear_binary(q, s, wb, s_w)
+    else:
+        packed = synth.random_bytes(synth.stream_key(key, 1), N * K // 4).numpy().reshape(N, K // 4)
+        wb = oracle.pack_bitplanes(packed, K)
+        acc_ref, y_ref = oracle.linear_bitplanes(q, s, wb, s_w)
     y, acc = tw.linear_bits(torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV), torch.from_numpy(wb).to(DEV),
-                            tw.FMT_BITPLANES, torch.tensor([s_w], device=DEV), want_acc=True, kernel=4)
+                            fmt, torch.tensor([s_w], device=DEV), want_acc=True, kernel=4)
     torch.cuda.synchronize()
     assert np.array_equal(acc.cpu().numpy(), acc_ref)
     assert_y(y.cpu().numpy(), y_ref)
