@@ -662,6 +662,9 @@ static hipError_t launch_bits_mt(const int8_t *q, const float *s_x, const uint8_
 //  * K is split over the wavefronts of a workgroup when there are few row groups
 //    (summed through LDS), as in the MFMA decode kernel for 2-bit codes.
 constexpr int kBitsMfmaNW = 8;   // wavefronts per workgroup
+#ifndef BITNET_BITS_MFMA_RG
+#define BITNET_BITS_MFMA_RG 4     // most 16-row groups per wavefront
+#endif
 
 __device__ __forceinline__ uint32_t plane_bytes(uint32_t w, int s) { return (w >> s) & 0x01010101u; }
 
@@ -838,13 +841,16 @@ static void launch_bits_mfma_rg(const int8_t *q, const float *s_x, const uint8_t
 
 // Rows per wavefront (16 RG) against parallelism, as for the 2-bit codes: the largest
 // RG whose launch, with K split over up to 8 wavefronts (at least 8 chunks per
-// slice), still reaches 4096 wavefronts.
+// slice), still reaches 4096 wavefronts.  Every wavefront loads its tokens' q for
+// each chunk, so more rows per wavefront mean fewer q loads per weight byte: the
+// stacked 229376 x 8192 matrix at M = 8 took 150 / 132 us (bitplanes / binary) with
+// at most 2 row groups, 134 / 105 us with 4 and 147 / 106 us with 8 (2 waves per SIMD).
 template <int FMT>
 static hipError_t launch_bits_mfma(const int8_t *q, const float *s_x, const uint8_t *wbits, const float *s_w,
                                    int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
     const int64_t C = K / 64;
     int rg = 1, ks = 1;
-    for (int r = 2; r >= 1; r >>= 1) {
+    for (int r = BITNET_BITS_MFMA_RG; r >= 1; r >>= 1) {
         const int64_t groups = (N + 16 * r - 1) / (16 * r);
         int k = 1;
         while (k < kBitsMfmaNW && groups * k < 4096 && C / (2 * k) >= 8) k *= 2;
@@ -852,7 +858,8 @@ static hipError_t launch_bits_mfma(const int8_t *q, const float *s_x, const uint
         ks = k;
         if (groups * k >= 4096) break;
     }
-    if (rg == 2) launch_bits_mfma_rg<FMT, 2>(q, s_x, wbits, s_w, M, N, K, y, acc, ks, st);
+    if (rg == 4) launch_bits_mfma_rg<FMT, 4>(q, s_x, wbits, s_w, M, N, K, y, acc, ks, st);
+    else if (rg == 2) launch_bits_mfma_rg<FMT, 2>(q, s_x, wbits, s_w, M, N, K, y, acc, ks, st);
     else launch_bits_mfma_rg<FMT, 1>(q, s_x, wbits, s_w, M, N, K, y, acc, ks, st);
     return hipGetLastError();
 }
