@@ -650,7 +650,7 @@ def main() -> int:
                 wbytes = big_w[v].numel()
                 one8[v] = {"us": round(us, 1), "weight_GBs": round(wbytes / (us * 1e-6) / 1e9, 1),
                            "gweights_per_s": round(229376 * 8192 / (us * 1e-6) / 1e9, 1),
-                           "kernel": "skinny2_kernel" if v == "two_bit_codes" else "bits_mfma_kernel"}
+                           "kernel": "skinny2_kernel" if v == "two_bit_codes" else "bits_lds_kernel"}
                 log(f"stacked gate 229376x8192 M=8 encoding {v}: {us:.1f} us, {one8[v]['weight_GBs']} GB/s")
                 if v != "two_bit_codes":
                     fn3 = lambda v=v, f_=f_, sw_=sw_: tw.bitnet_linear_bits(q8, s8, big_w[v], f_, sw_, y8, None, 3)

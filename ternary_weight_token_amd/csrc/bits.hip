@@ -665,6 +665,15 @@ constexpr int kBitsMfmaNW = 8;   // wavefronts per workgroup
 #ifndef BITNET_BITS_MFMA_RG
 #define BITNET_BITS_MFMA_RG 4     // most 16-row groups per wavefront
 #endif
+#ifndef BITNET_BITS_LDS_RG
+#define BITNET_BITS_LDS_RG 2      // 16-row groups per wavefront of the LDS-staged form
+#endif
+#ifndef BITNET_BITS_LDS_UN
+#define BITNET_BITS_LDS_UN 2      // chunks per lane and step of the LDS-staged form (binary: twice)
+#endif
+#ifndef BITNET_BITS_LDS
+#define BITNET_BITS_LDS 1         // tall matrices take the LDS-staged form
+#endif
 
 __device__ __forceinline__ uint32_t plane_bytes(uint32_t w, int s) { return (w >> s) & 0x01010101u; }
 
@@ -823,6 +832,203 @@ __global__ __launch_bounds__(64 * kBitsMfmaNW) void bits_mfma_kernel(
     }
 }
 
+// The same products for tall matrices, q staged once per workgroup: a workgroup of 8
+// wavefronts takes 16 RG rows per wavefront and the whole K, in segments whose q (all
+// tokens of the tile) fits 64 KiB of LDS.  Each (token, chunk) item is loaded once,
+// transposed into the four MFMA operands (the k order above) and stored as
+// [chunk][operand j][token], 16 bytes each, a 16-byte pad per chunk (the threads that
+// stage consecutive chunks then fall on different banks); binary also sums q per token
+// while staging, in place of the all-ones MFMA.  The wavefronts read their B operands
+// from LDS instead of loading q themselves.  Lane group g takes chunks 4 UN t + 4 u + g
+// (u < UN) of step t, so that the UN loads of a row group are back to back: 128
+// contiguous bytes of each row per step (UN = 2 for bitplanes, 4 for binary).
+constexpr int kBitsLdsBudget = 64 * 1024;
+constexpr int64_t kBitsLdsMinRows = 131072;   // at least two 256-row workgroups per CU
+
+__host__ __device__ __forceinline__ int bits_chunk_dw(int M) { return 16 * M + 4; }
+static int bits_segment_chunks(int C, int M) {
+    const int max_seg = (kBitsLdsBudget / (4 * bits_chunk_dw(M))) & ~3;
+    if (C <= max_seg) return C;
+    const int nseg = (C + max_seg - 1) / max_seg;
+    return (((C + nseg - 1) / nseg) + 3) & ~3;
+}
+
+template <int FMT, int RG, int UN>
+__global__ __launch_bounds__(64 * kBitsMfmaNW) void bits_lds_kernel(
+    const int8_t *__restrict__ q, const float *__restrict__ s_x, const uint8_t *__restrict__ planes,
+    const float *__restrict__ s_w, int M, int N, int K, float *__restrict__ y, int32_t *__restrict__ acc_out,
+    int seg_chunks) {
+    typedef int v4i_b __attribute__((ext_vector_type(4)));
+    extern __shared__ __attribute__((aligned(16))) uint32_t qs[];   // staged q of one segment
+    __shared__ int sq[16];                                            // binary: sum of q per token
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int m0 = (int)blockIdx.y * 16, mt = min(16, M - m0);
+    const int C = K >> 6;
+    constexpr int CB = FMT == 2 ? 16 : 8;   // weight bytes per 64-weight chunk of a row
+    const size_t KB = (size_t)C * CB;
+    const int row0 = (int)blockIdx.x * (kBitsMfmaNW * 16 * RG) + wave * 16 * RG;
+    const int tok = min(l16, mt - 1);
+    const int cdw = bits_chunk_dw(mt);
+    const uint8_t *prow[RG];
+    #pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+        const int r = row0 + 16 * rg + l16;
+        prow[rg] = planes + (size_t)(r < N ? r : 0) * KB;   // rows past N read row 0, dropped
+    }
+    v4i_b accp[RG], accn[FMT == 2 ? RG : 1];
+    #pragma unroll
+    for (int rg = 0; rg < RG; ++rg) accp[rg] = v4i_b{0, 0, 0, 0};
+    #pragma unroll
+    for (int rg = 0; rg < (FMT == 2 ? RG : 1); ++rg) accn[rg] = v4i_b{0, 0, 0, 0};
+    if (tid < 16) sq[tid] = 0;
+
+    for (int s0 = 0; s0 < C; s0 += seg_chunks) {
+        const int sc = min(seg_chunks, C - s0);
+        // step t: lane group g takes local chunks 4 UN t + 4 u + g; past the segment a
+        // chunk is clamped (an in-range load) and its planes are zeroed
+        const int T = (sc + 4 * UN - 1) / (4 * UN);
+        uint4 wA[UN][RG], wB[UN][RG];
+        auto issue = [&](uint4 (&w)[UN][RG], int t) {
+            #pragma unroll
+            for (int u = 0; u < UN; ++u) {
+                const int cc = s0 + min(4 * UN * t + 4 * u + g, sc - 1);
+                #pragma unroll
+                for (int rg = 0; rg < RG; ++rg) {
+                    if (FMT == 2) {
+                        w[u][rg] = gload16(prow[rg] + 16 * cc);
+                    } else {
+                        typedef unsigned int v2u_b __attribute__((ext_vector_type(2)));
+                        const v2u_b v = *(__attribute__((address_space(1))) const v2u_b *)(prow[rg] + 8 * cc);
+                        w[u][rg] = make_uint4(v.x, v.y, 0u, 0u);
+                    }
+                }
+            }
+        };
+        auto consume = [&](const uint4 (&w)[UN][RG], int t) {
+            #pragma unroll
+            for (int u = 0; u < UN; ++u) {
+                const int cl = 4 * UN * t + 4 * u + g;
+                const bool valid = cl < sc;
+                const uint32_t *src = qs + min(cl, sc - 1) * cdw + tok * 4;
+                uint32_t pos[RG][2], neg[RG][2];
+                #pragma unroll
+                for (int rg = 0; rg < RG; ++rg) {
+                    if (FMT == 2) {
+                        pos[rg][0] = valid ? (w[u][rg].x ^ w[u][rg].y) : 0u;
+                        neg[rg][0] = valid ? w[u][rg].y : 0u;
+                        pos[rg][1] = valid ? (w[u][rg].z ^ w[u][rg].w) : 0u;
+                        neg[rg][1] = valid ? w[u][rg].w : 0u;
+                    } else {
+                        pos[rg][0] = valid ? w[u][rg].x : 0u;
+                        pos[rg][1] = valid ? w[u][rg].y : 0u;
+                    }
+                }
+                #pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const v4i_b b = *reinterpret_cast<const v4i_b *>(src + j * mt * 4);
+                    #pragma unroll
+                    for (int rg = 0; rg < RG; ++rg) {
+                        const v4i_b ap = v4i_b{(int)plane_bytes(pos[rg][0], 2 * j), (int)plane_bytes(pos[rg][0], 2 * j + 1),
+                                               (int)plane_bytes(pos[rg][1], 2 * j), (int)plane_bytes(pos[rg][1], 2 * j + 1)};
+                        accp[rg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap, b, accp[rg], 0, 0, 0);
+                        if (FMT == 2) {
+                            const v4i_b an = v4i_b{(int)plane_bytes(neg[rg][0], 2 * j), (int)plane_bytes(neg[rg][0], 2 * j + 1),
+                                                   (int)plane_bytes(neg[rg][1], 2 * j), (int)plane_bytes(neg[rg][1], 2 * j + 1)};
+                            accn[rg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(an, b, accn[rg], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+        };
+        // the segment's first weight loads go out before the staging of q
+        if (T > 0) issue(wA, 0);
+        __syncthreads();   // previous segment's LDS reads done; sq initialised
+        for (int idx = tid; idx < mt * sc; idx += (int)blockDim.x) {
+            const int m = idx / sc, c = idx - m * sc;
+            const int8_t *src = q + (size_t)(m0 + m) * K + 64 * (s0 + c);
+            uint4 v[4];
+            #pragma unroll
+            for (int d = 0; d < 4; ++d) v[d] = gload16(src + 16 * d);
+            // O[G][h][p], byte b: q of k = 32 G + 8 b + 4 h + p
+            uint32_t O[2][2][4];
+            transpose4x4(v[0].x, v[0].z, v[1].x, v[1].z, O[0][0][0], O[0][0][1], O[0][0][2], O[0][0][3]);
+            transpose4x4(v[0].y, v[0].w, v[1].y, v[1].w, O[0][1][0], O[0][1][1], O[0][1][2], O[0][1][3]);
+            transpose4x4(v[2].x, v[2].z, v[3].x, v[3].z, O[1][0][0], O[1][0][1], O[1][0][2], O[1][0][3]);
+            transpose4x4(v[2].y, v[2].w, v[3].y, v[3].w, O[1][1][0], O[1][1][1], O[1][1][2], O[1][1][3]);
+            #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int h = j >> 1, p = 2 * (j & 1);
+                *reinterpret_cast<uint4 *>(qs + c * cdw + (j * mt + m) * 4) =
+                    make_uint4(O[0][h][p], O[0][h][p + 1], O[1][h][p], O[1][h][p + 1]);
+            }
+            if (FMT == 1) {
+                int sm = 0;
+                #pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    sm = dot4(v[d].x, 0x01010101u, sm);
+                    sm = dot4(v[d].y, 0x01010101u, sm);
+                    sm = dot4(v[d].z, 0x01010101u, sm);
+                    sm = dot4(v[d].w, 0x01010101u, sm);
+                }
+                if (sm != 0) atomicAdd(&sq[m], sm);
+            }
+        }
+        __syncthreads();
+        if (T > 0) {
+            const int T2 = (T + 1) & ~1;
+            for (int t = 0; t < T2 - 2; t += 2) {
+                issue(wB, t + 1);
+                consume(wA, t);
+                issue(wA, t + 2);
+                consume(wB, t + 1);
+            }
+            if (T2 == T) {
+                issue(wB, T - 1);
+                consume(wA, T - 2);
+                consume(wB, T - 1);
+            } else {
+                consume(wA, T - 1);
+            }
+        }
+    }
+    // 16 x 16 accumulator layout: lane -> token l16 of the tile; register r -> row
+    // 4 g + r of the row group
+    if (l16 < mt) {
+        const int m = m0 + l16;
+        const double cm = rescale_factor(s_x[m], *s_w);
+        const int sqm = FMT == 1 ? sq[l16] : 0;
+        #pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+            #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = row0 + 16 * rg + 4 * g + r;
+                if (row < N) {
+                    const size_t o = (size_t)m * N + row;
+                    const int v = FMT == 2 ? accp[rg][r] - accn[rg][r] : 2 * accp[rg][r] - sqm;
+                    y[o] = rescale(v, cm);
+                    if (acc_out) acc_out[o] = v;
+                }
+            }
+        }
+    }
+}
+
+template <int FMT>
+static hipError_t launch_bits_lds(const int8_t *q, const float *s_x, const uint8_t *wbits, const float *s_w,
+                                  int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
+    constexpr int RG = BITNET_BITS_LDS_RG;
+    constexpr int UN = FMT == 2 ? BITNET_BITS_LDS_UN : 2 * BITNET_BITS_LDS_UN;
+    const int64_t rows = (int64_t)kBitsMfmaNW * 16 * RG;
+    const int mt = (int)std::min<int64_t>(M, 16);
+    const int seg = bits_segment_chunks((int)(K / 64), mt);
+    const size_t lds = (size_t)seg * bits_chunk_dw(mt) * 4;
+    const dim3 grid((unsigned)((N + rows - 1) / rows), (unsigned)((M + 15) / 16));
+    bits_lds_kernel<FMT, RG, UN><<<grid, dim3(64 * kBitsMfmaNW), lds, st>>>(q, s_x, wbits, s_w, (int)M, (int)N, (int)K,
+                                                                             y, acc, seg);
+    return hipGetLastError();
+}
+
 // K % 64 == 0, 16-byte aligned q and weights; any M (16-token tiles on the grid's y,
 // at most 65535 of them).
 bool bits_mfma_ok(int fmt, int64_t M, int64_t K, const void *q, const void *wbits) {
@@ -848,6 +1054,7 @@ static void launch_bits_mfma_rg(const int8_t *q, const float *s_x, const uint8_t
 template <int FMT>
 static hipError_t launch_bits_mfma(const int8_t *q, const float *s_x, const uint8_t *wbits, const float *s_w,
                                    int64_t M, int64_t N, int64_t K, float *y, int32_t *acc, hipStream_t st) {
+    if (BITNET_BITS_LDS && N >= kBitsLdsMinRows) return launch_bits_lds<FMT>(q, s_x, wbits, s_w, M, N, K, y, acc, st);
     const int64_t C = K / 64;
     int rg = 1, ks = 1;
     for (int r = BITNET_BITS_MFMA_RG; r >= 1; r >>= 1) {

@@ -837,11 +837,13 @@ def test_linear_bits_parity(fmt, M, N, K):
 @pytest.mark.parametrize("fmt", [1, 2])
 @pytest.mark.parametrize("M,N,K", [(2, 1, 64), (16, 5000, 2560), (17, 300, 6912), (40, 129, 1024), (8, 6000, 8192),
                                    (3, 7, 28672), (33, 4096, 128), (8, 65, 57344), (4, 131112, 128),
-                                   (3, 262200, 64), (8, 40000, 8192)])
+                                   (3, 262200, 64), (8, 40000, 8192), (20, 131080, 256), (8, 131072, 6912)])
 def test_linear_bits_mfma(fmt, M, N, K):
     """The matrix-core kernel for binary weights and bitplanes (kernel 4): one to three
     16-token tiles, ragged rows, K split over 1 to 8 wavefronts, one, two or four
-    16-row groups per wavefront, K from one chunk to 57344, random weight bits (binary) or
+    16-row groups per wavefront, from 131072 rows the form with q staged once per
+    workgroup (K in segments, a ragged second token tile), K from one chunk to 57344,
+    random weight bits (binary) or
     planes of random 2-bit codes (code 3 as +1), and a token row of +-127 so that every
     byte of the products counts; acc bit-exact and y against the oracle's product over
     the same weights."""
