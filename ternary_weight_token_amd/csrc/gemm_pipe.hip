@@ -32,6 +32,10 @@
 #include "device_common.h"
 #include "internal.h"
 
+#ifndef BITNET_PIPE_SGN
+#define BITNET_PIPE_SGN 1   // group-wise scales, groups up to 128: signed operands
+#endif
+
 namespace bitnet {
 
 namespace {
@@ -64,12 +68,16 @@ __device__ __forceinline__ int qslot(int r, int c) { return c ^ (r & 7) ^ ((r >>
 // GRP: group-wise weight scales (out.w_group = G < K, G = 64 or a multiple of 128):
 // the int32 products of each group are scaled into fp32 accumulators when the
 // group's last half step is done (see the consumer); OPT is set as well.
+// SGN (GRP with groups of at most 128 weights, a fold every step or half step): the
+// codes are expanded to the signed weights t = c - 1 (one byte permute per dword,
+// code 3 as +2), so that each group's products are sum q t itself and the fold has no
+// sum of q to subtract; the same integers, so the same results.
 // PW (K a multiple of 256): the packed weights of a pair of steps (k-steps 2j and
 // 2j + 1) are loaded together as 64-byte row pieces on the even step and staged in
 // its stage; the odd step reads them from there.  A load instruction then covers 16
 // rows in 64-byte pieces instead of 32 rows in 32-byte pieces: half the cache lines
 // per staged byte.
-template <int TN, bool OPT, bool GRP = false, bool PW = false>
+template <int TN, bool OPT, bool GRP = false, bool PW = false, bool SGN = false>
 __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s_x, const uint8_t *__restrict__ packed,
     const float *__restrict__ s_w, int M, int N, int K, const OutSpec out, int32_t *__restrict__ acc_out,
@@ -332,18 +340,25 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
         for (int j = 0; j < TN; ++j) {
             // dword i of the operand: code i of each packed byte (k = 4d + i at byte 4i + d)
             const uint32_t w = fb[u][j];
-            const pv4i b{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
-                         (int)((w >> 6) & 0x03030303u)};
+            pv4i b{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
+                   (int)((w >> 6) & 0x03030303u)};
+            if (SGN) {
+                #pragma unroll
+                for (int d = 0; d < 4; ++d) b[d] = (int)__builtin_amdgcn_perm(0u, 0x020100FFu, (uint32_t)b[d]);
+            }
             #pragma unroll
             for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, fa[u][i], acc[i][j], 0, 0, 0);
         }
     };
     // GRP, after half u of step x: at the group's last half, its products (codes c,
-    // less the group's sum of q) times the group scale of each column into facc
+    // less the group's sum of q; SGN: the signed weights) times the group scale of
+    // each column into facc
     auto fold_half = [&](int x, int u) {
         const int st = x % D;
-        #pragma unroll
-        for (int i = 0; i < 4; ++i) sqrun[i] += sqh[st][u][64 * wm + 16 * i + l16];
+        if (!SGN) {
+            #pragma unroll
+            for (int i = 0; i < 4; ++i) sqrun[i] += sqh[st][u][64 * wm + 16 * i + l16];
+        }
         if (++c_h == gh) {
             c_h = 0;
             #pragma unroll
@@ -352,7 +367,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void gemm_pipe_kernel(
                 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     #pragma unroll
-                    for (int r = 0; r < 4; ++r) facc[i][j][r] += (float)(acc[i][j][r] - sqrun[i]) * s4[r];
+                    for (int r = 0; r < 4; ++r) facc[i][j][r] += (float)(SGN ? acc[i][j][r] : acc[i][j][r] - sqrun[i]) * s4[r];
                     acc[i][j] = pv4i{0, 0, 0, 0};
                 }
             }
@@ -610,9 +625,17 @@ hipError_t launch_gemm_pipe(int tn_force, const int8_t *q, const float *s_x, con
         const int tiles_m = (int)((M + kPipeBM - 1) / kPipeBM);
         const int64_t tiles = (int64_t)tiles_m * ((N + 159) / 160);
         const dim3 g((unsigned)std::min<int64_t>(tiles, cus));
-        if (pipe_pairs(K))
+        const bool sgn = BITNET_PIPE_SGN && y.w_group <= 128;
+        if (pipe_pairs(K) && sgn)
+            gemm_pipe_kernel<5, true, true, true, true><<<g, dim3(kPipeThreads), 0, st>>>(q, s_x, packed, s_w, (int)M, (int)N,
+                                                                                      (int)K, y, nullptr, tiles_m, (int)tiles);
+        else if (pipe_pairs(K))
             gemm_pipe_kernel<5, true, true, true><<<g, dim3(kPipeThreads), 0, st>>>(q, s_x, packed, s_w, (int)M, (int)N,
                                                                                 (int)K, y, nullptr, tiles_m, (int)tiles);
+        else if (sgn)
+            gemm_pipe_kernel<5, true, true, false, true><<<g, dim3(kPipeThreads), 0, st>>>(q, s_x, packed, s_w, (int)M,
+                                                                                       (int)N, (int)K, y, nullptr,
+                                                                                       tiles_m, (int)tiles);
         else
             gemm_pipe_kernel<5, true, true, false><<<g, dim3(kPipeThreads), 0, st>>>(q, s_x, packed, s_w, (int)M, (int)N,
                                                                                  (int)K, y, nullptr, tiles_m, (int)tiles);
