@@ -460,6 +460,8 @@ BITNET_API int bitnet_grouped_plan_linear(const bitnet_linear_desc *descs, int c
     h->desc_offset = doff;
     h->table_offset = toff;
     h->total_bytes = need;
+    for (int i = 0; i < count; ++i)
+        if (desc_groups(descs[i]) && descs[i].acc) h->flags |= kPlanFlagGroupAcc;
     LinearDescDev *dd = (LinearDescDev *)(p + doff);
     BlockEntry *tb = (BlockEntry *)(p + toff);
     for (int i = 0; i < count; ++i) {
@@ -606,7 +608,7 @@ BITNET_API int bitnet_linear_grouped(const void *plan_host, const void *plan_dev
     if (h->total_blocks == 0) return BITNET_OK;
     if (h->variant == kVariantMfma || h->variant == kVariantMfmaGroups)
         return hip_status(launch_skinny_grouped(plan_dev, h->total_blocks, h->lds_bytes, h->variant == kVariantMfmaGroups,
-                                                (hipStream_t)stream));
+                                                (h->flags & kPlanFlagGroupAcc) != 0, (hipStream_t)stream));
     if (h->variant != kVariantGemv && h->variant != kVariantGemvGroups && h->variant != kVariantGemvGroupsMT)
         return fail(BITNET_ERR_ARG, "not a plan of this kind");
     return hip_status(launch_gemv_grouped(plan_dev, h->total_blocks, h->lds_bytes, h->variant,

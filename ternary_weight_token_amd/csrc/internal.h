@@ -51,8 +51,10 @@ constexpr uint32_t kFusedBitplanes = 4;
 struct PlanHeader {            // 64 bytes
     uint32_t magic, kind, count, total_blocks;
     uint32_t block_threads, rows_per_block, lds_bytes, variant;
-    uint64_t desc_offset, table_offset, total_bytes, reserved2;
+    uint64_t desc_offset, table_offset, total_bytes, flags;   // flags: kPlanFlag*
 };
+// a linear plan with group-wise scales where some such descriptor asks for int32 acc
+constexpr uint64_t kPlanFlagGroupAcc = 1;
 
 struct LinearDescDev {         // 80 bytes, device layout
     const int8_t *q; const float *s_x; const uint8_t *packed; const float *s_w;
@@ -129,7 +131,8 @@ double skinny_estimate_us(int64_t M, int64_t N, int64_t K);
 double gemm_estimate_us(int64_t M, int64_t N, int64_t K);
 hipError_t launch_skinny(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,
                          int64_t M, int64_t N, int64_t K, const OutSpec &y, int32_t *acc, hipStream_t st);
-hipError_t launch_skinny_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, bool grp, hipStream_t st);
+hipError_t launch_skinny_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, bool grp, bool grp_acc,
+                                 hipStream_t st);
 uint32_t skinny_grouped_rows_per_block();
 uint32_t skinny_grouped_lds_bytes(int64_t M, int64_t K, bool grp = false);
 hipError_t launch_gemm(const int8_t *q, const float *s_x, const uint8_t *packed, const float *s_w,

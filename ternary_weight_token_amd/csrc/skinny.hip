@@ -464,7 +464,10 @@ constexpr int kSk2Items = (kSkLdsBudget / 64 + 64 * kSk2NW - 1) / (64 * kSk2NW);
 // products, less the group's sum of q (per-chunk sums kept while staging), are scaled
 // by the rows' group scales into float64 accumulators; the scales travel with the
 // weights (loaded beside each piece, regrouped through LDS with them).
-template <bool NT, bool GRP>
+// IT (with GRP): also keep each row's exact integer sum of the group-wise problems,
+// for their int32 acc output; without it only the problems with one group (whose
+// float64 sum is that integer exactly) have acc.
+template <bool NT, bool GRP, bool IT = true>
 __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_base, uint32_t *qs, uint32_t *tb,
                                              float *tsc, int *sq, double *cms) {
     const int tid = threadIdx.x;
@@ -501,13 +504,16 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
     for (int b = 0; b < kSk2RB; ++b) acc[b] = v4i_sk{0, 0, 0, 0};
     // GRP: sum over the groups done of (products - sum q) s_g and of (products - sum q)
     double facc[GRP ? kSk2RB : 1][4];
-    int itot[GRP ? kSk2RB : 1][4];
+    int itot[GRP && IT ? kSk2RB : 1][4];
     int sqrun = 0;   // GRP: sum of q over the current group's chunks so far (lane's token)
     if (GRP) {
         #pragma unroll
         for (int b = 0; b < kSk2RB; ++b)
             #pragma unroll
-            for (int r = 0; r < 4; ++r) { facc[b][r] = 0.0; itot[b][r] = 0; }
+            for (int r = 0; r < 4; ++r) {
+                facc[b][r] = 0.0;
+                if (IT) itot[b][r] = 0;
+            }
     }
     if (tid < 16) sq[tid] = 0;
     const int tokc = min(l16, M - 1);   // tokens past M repeat the last one (outputs dropped)
@@ -593,7 +599,7 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
                             for (int r = 0; r < 4; ++r) {
                                 const int pr = acc[b][r] - sqrun;   // |pr| <= 127 G
                                 facc[b][r] += (double)pr * (double)sv[r];
-                                itot[b][r] += pr;
+                                if (IT) itot[b][r] += pr;
                             }
                             acc[b] = v4i_sk{0, 0, 0, 0};
                         }
@@ -707,9 +713,10 @@ __device__ __forceinline__ void skinny2_tile(const LinearDescDev &d, int row_bas
                     double yv = (facc[b][r] * (double)d.s_x[l16]) / 127.0;
                     if (d.bias) yv += (double)d.bias[row];
                     ys[l16 * kSk2YStride + rl] = (int)__float_as_uint((float)yv);
-                    ys2[l16 * kSk2YStride + rl] = itot[b][r];
+                    ys2[l16 * kSk2YStride + rl] = IT ? itot[b][r] : 0;
                 } else {
-                    ys[l16 * kSk2YStride + rl] = GRP ? itot[b][r] : acc[b][r] - sqm;
+                    // GRP: one group of all of K with scale 1, its float64 sum exact
+                    ys[l16 * kSk2YStride + rl] = GRP ? (IT ? itot[b][r] : (int)facc[b][r]) : acc[b][r] - sqm;
                 }
             }
     }
@@ -756,7 +763,7 @@ __global__ __launch_bounds__(64 * kGroupedSkNW) void skinny_grouped_kernel(const
 
 // GRP: the plan has problems with group-wise weight scales, which take the group-wise
 // tile; plans without them use the kernel without it.
-template <bool GRP>
+template <bool GRP, bool IT = true>
 __global__ __launch_bounds__(64 * kSk2NW) __attribute__((amdgpu_waves_per_eu(SK2_WAVES))) void skinny2_grouped_kernel(const uint8_t *__restrict__ plan) {
     extern __shared__ __attribute__((aligned(16))) uint32_t qs[];   // staged q of one segment; results
     __shared__ __attribute__((aligned(16))) uint32_t tb[kSk2NW * 16 * kSk2TDw];
@@ -766,7 +773,7 @@ __global__ __launch_bounds__(64 * kSk2NW) __attribute__((amdgpu_waves_per_eu(SK2
     const PlanHeader *h = reinterpret_cast<const PlanHeader *>(plan);
     const BlockEntry e = reinterpret_cast<const BlockEntry *>(plan + h->table_offset)[blockIdx.x];
     const LinearDescDev d = reinterpret_cast<const LinearDescDev *>(plan + h->desc_offset)[e.desc];
-    skinny2_tile<true, GRP>(d, (int)e.local * kSk2Rows, qs, tb, tsc, sq, cms);
+    skinny2_tile<true, GRP, IT>(d, (int)e.local * kSk2Rows, qs, tb, tsc, sq, cms);
 }
 
 static_assert(kSk2Rows == kGroupedSkNW * 16 * kGroupedSkRG, "both grouped variants take 256-row blocks");
@@ -813,9 +820,14 @@ uint32_t skinny_grouped_lds_bytes(int64_t M, int64_t K, bool grp) {
     return BITNET_SKINNY_V2 ? std::max<uint32_t>(stage, (grp ? 2u : 1u) * 16u * kSk2YStride * 4u) : stage;
 }
 
-hipError_t launch_skinny_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, bool grp, hipStream_t st) {
+hipError_t launch_skinny_grouped(const void *plan_dev, uint32_t blocks, uint32_t lds_bytes, bool grp, bool grp_acc,
+                                 hipStream_t st) {
     const uint8_t *p = reinterpret_cast<const uint8_t *>(plan_dev);
-    if (grp) skinny2_grouped_kernel<true><<<dim3(blocks), dim3(64 * kSk2NW), lds_bytes, st>>>(p);
+    // group-wise plans: the integer sums only when a group-wise problem asks for acc
+    // (8 registers fewer, no spills at 4 waves per SIMD: 8-token decode step with
+    // group-128 scales 188.5 -> 178.8 us)
+    if (grp && grp_acc) skinny2_grouped_kernel<true, true><<<dim3(blocks), dim3(64 * kSk2NW), lds_bytes, st>>>(p);
+    else if (grp) skinny2_grouped_kernel<true, false><<<dim3(blocks), dim3(64 * kSk2NW), lds_bytes, st>>>(p);
     else if (BITNET_SKINNY_V2) skinny2_grouped_kernel<false><<<dim3(blocks), dim3(64 * kSk2NW), lds_bytes, st>>>(p);
     else skinny_grouped_kernel<<<dim3(blocks), dim3(64 * kGroupedSkNW), lds_bytes, st>>>(p);
     return hipGetLastError();

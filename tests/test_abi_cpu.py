@@ -403,6 +403,16 @@ def test_linear_plan_weight_groups(L):
     ok = (D * 1)(D(a16, a16, a16, a16, a16, 0, 2, 300, 2560, 2560))     # per channel: MFMA variant stays
     assert L.bitnet_grouped_plan_linear(ok, 1, buf, nb) == OK
     assert (ctypes.c_uint32 * 8).from_buffer_copy(buf.raw[:32])[7] == 1
+    # header flags (the last 8 header bytes): bit 0 set only when a group-wise problem
+    # asks for its int32 acc (the several-token kernel then keeps the integer sums)
+    assert L.bitnet_grouped_plan_linear(arr, 2, buf, nb) == OK
+    assert ctypes.c_uint64.from_buffer_copy(buf.raw[56:64]).value == 0
+    acc_plain = (D * 2)(D(a16, a16, a16, a16, a16, a16, 1, 300, 2560, 0), D(a16, a16, a16, a16, a16, 0, 3, 200, 2560, 128))
+    assert L.bitnet_grouped_plan_linear(acc_plain, 2, buf, nb) == OK
+    assert ctypes.c_uint64.from_buffer_copy(buf.raw[56:64]).value == 0
+    acc_group = (D * 2)(D(a16, a16, a16, a16, a16, 0, 1, 300, 2560, 0), D(a16, a16, a16, a16, a16, a16, 3, 200, 2560, 128))
+    assert L.bitnet_grouped_plan_linear(acc_group, 2, buf, nb) == OK
+    assert ctypes.c_uint64.from_buffer_copy(buf.raw[56:64]).value == 1
 
 
 def test_linear_plan_lds_covers_every_descriptor(L):

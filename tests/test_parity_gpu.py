@@ -395,10 +395,14 @@ def test_linear_weight_scale_groups(kernel, M, N, K, G, opts):
     assert not bad.any(), f"{bad.sum()} outputs outside the bound"
 
 
+@pytest.mark.parametrize("group_acc", [True, False])
 @pytest.mark.parametrize("mixed_m", [False, True, "wide"])
-def test_grouped_plan_weight_scales(mixed_m):
+def test_grouped_plan_weight_scales(mixed_m, group_acc):
     """One grouped linear launch over problems with one scale per tensor, per output
-    channel and per group of 128 / 64 weights (and, mixed_m, M up to 5)."""
+    channel and per group of 128 / 64 weights (and, mixed_m, M up to 5).  group_acc
+    False: the group-wise problems ask for y only, which lets the several-token kernel
+    drop their integer sums; the other problems still return acc (their float64 sum is
+    the integer itself)."""
     # a plain K = 51200 row (one segment of 20-dword chunks) next to group-wise rows
     shapes = [(300, 2560, 0), (129, 2560, 2560), (200, 6912, 128), (70, 640, 64), (640, 2560, 128), (64, 51200, 0)]
     probs, refs = [], []
@@ -419,7 +423,7 @@ def test_grouped_plan_weight_scales(mixed_m):
             slack = None
         refs.append((acc_ref, y_ref, slack))
         y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
-        acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+        acc = torch.empty((M, N), dtype=torch.int32, device=DEV) if group_acc or not 0 < G < K else None
         probs.append((torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV), torch.from_numpy(packed).to(DEV),
                       torch.from_numpy(s_w).to(DEV), y, acc, G))
     plan = tw.bitnet_grouped_plan_linear(probs)
@@ -427,7 +431,8 @@ def test_grouped_plan_weight_scales(mixed_m):
         plan.launch()
         torch.cuda.synchronize()
         for (acc_ref, y_ref, slack), pr in zip(refs, probs):
-            assert np.array_equal(pr[5].cpu().numpy(), acc_ref)
+            if pr[5] is not None:
+                assert np.array_equal(pr[5].cpu().numpy(), acc_ref)
             if slack is None:
                 assert_y(pr[4].cpu().numpy(), y_ref)
             else:
