@@ -748,7 +748,8 @@ def main() -> int:
                 b.record(stream)
                 torch.cuda.synchronize()
                 us = a.elapsed_time(b) * 1e3 / 30
-                kern = {1: "skinny2_grouped_kernel<false>", 4: "skinny2_grouped_kernel<true>"}.get(
+                kern = {1: "skinny2_grouped_kernel<false, true>",
+                        4: f"skinny2_grouped_kernel<true, {'true' if lp.flags & 1 else 'false'}>"}.get(
                     lp.variant, f"gemv_grouped_kernel (plan variant {lp.variant})")
                 dres8[v] = {"us": round(us, 1), "weight_GBs": round(weight_bytes / (us * 1e-6) / 1e9, 1), "kernel": kern}
                 log(f"decode step M=8 two launches, scales {v}: {us:.1f} us")

@@ -283,6 +283,12 @@ class GroupedPlan:
         count, total_blocks, block_threads, rows_per_block and lds_bytes)."""
         return int.from_bytes(self.host.raw[28:32], "little")
 
+    @property
+    def flags(self) -> int:
+        """The plan header's flags (its last 8 bytes); bit 0: a problem with group-wise
+        weight scales asks for its int32 acc."""
+        return int.from_bytes(self.host.raw[56:64], "little")
+
     def launch(self, stream=None) -> None:
         f = {"linear": lib().bitnet_linear_grouped, "quant": lib().bitnet_quant_act_grouped,
              "fused": lib().bitnet_linear_fused_grouped}[self.kind]
