@@ -123,6 +123,29 @@ def test_quant_act_parity(M, K, kw):
     assert np.array_equal(s, s_ref)
 
 
+def test_quant_act_grouped_rows():
+    """The grouped quantization plan (one wavefront per row): rows of 8 .. 16392 values
+    (up to two passes over a row), an all-zero row, outliers, several tokens per
+    problem and problems of different K in one launch; q and s_x bit for bit."""
+    shapes = [(1, 8), (3, 64), (8, 2560), (2, 6912), (5, 8192), (1, 8200), (4, 16392), (9, 640)]
+    probs, refs = [], []
+    for i, (M, K) in enumerate(shapes):
+        x = synth.activations(synth.stream_key(104, i, M, K), M, K, outlier_frac=0.002)
+        if i == 2:
+            x[1].zero_()
+        refs.append(oracle.quant_act(bits_np(x)))
+        xd = x.to(DEV)
+        probs.append((xd, torch.full((M, K), 99, dtype=torch.int8, device=DEV),
+                      torch.full((M,), -1.0, dtype=torch.float32, device=DEV)))
+    plan = tw.bitnet_grouped_plan_quant(probs)
+    for _ in range(2):
+        plan.launch()
+        torch.cuda.synchronize()
+        for (q_ref, s_ref), (xd, q, s) in zip(refs, probs):
+            assert np.array_equal(q.cpu().numpy(), q_ref)
+            assert np.array_equal(s.cpu().numpy(), s_ref)
+
+
 @pytest.mark.parametrize("fused", [False, True])
 def test_quant_act_exhaustive_bf16(fused):
     """Every finite bf16 value x with |x| <= s, for scales s across the whole range
